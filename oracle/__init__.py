@@ -1,0 +1,194 @@
+"""CPU oracle for the sparse-MoE FFN layer forward -- TEST INFRASTRUCTURE.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  The GPU library never uses it, and
+it uses nothing from the GPU library.
+
+Thin numpy/ctypes wrapper over ``moe_oracle.c``; the arithmetic lives in
+the C file (fp32 storage, fp64 sequential sums).  Each function states the
+passage of the page "Mixture of experts" (rayaq.ca) it follows.
+
+Integer codes used here are the oracle's own:
+  gate: "renorm" (softmax over the k chosen logits) | "switch" (full-softmax p)
+  act:  "relu" | "gelu" | "swiglu"
+"""
+import ctypes
+import os
+
+import numpy as np
+
+from . import build as _build
+
+_GATE = {"renorm": 0, "switch": 1}
+_ACT = {"relu": 0, "gelu": 1, "swiglu": 2}
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = os.environ.get("MOE_ORACLE_LIB")   # a planted-mistake build, in the mutation test
+    if path is None:
+        path = _build.LIB
+        if not os.path.exists(path):
+            _build.build()
+    lib = ctypes.CDLL(path)
+    i64, ip, fp, dp = ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p
+    lib.orc_router_logits.argtypes = [i64, i64, i64, fp, fp, fp, fp, fp]
+    lib.orc_router_logits.restype = None
+    lib.orc_gate.argtypes = [i64, i64, i64, ctypes.c_int, fp, ip, dp, dp, dp]
+    lib.orc_gate.restype = ctypes.c_int
+    lib.orc_capacity.argtypes = [i64, i64, i64, ctypes.c_double]
+    lib.orc_capacity.restype = i64
+    lib.orc_dispatch.argtypes = [i64, i64, i64, i64, ip, ip, ip, ip, ip, ip, ip]
+    lib.orc_dispatch.restype = None
+    lib.orc_expert_ffn.argtypes = [i64, ip, ip, i64, i64, ctypes.c_int, fp, fp, fp, fp, fp]
+    lib.orc_expert_ffn.restype = None
+    lib.orc_combine.argtypes = [i64, i64, i64, dp, ip, fp, fp]
+    lib.orc_combine.restype = None
+    lib.orc_stats.argtypes = [i64, i64, i64, ip, dp, dp, dp, dp, dp, dp]
+    lib.orc_stats.restype = None
+    _lib = lib
+    return lib
+
+
+def _p(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _f32(a):
+    return None if a is None else np.ascontiguousarray(a, dtype=np.float32)
+
+
+def router_logits(x, Wr, bias=None, noise=None):
+    """h = W_r x (+ b + n), fp32 ("Replacing the feed-forward block"; noise per
+    "Top-k gating"; float32 router per "Implementation")."""
+    x, Wr, bias, noise = _f32(x), _f32(Wr), _f32(bias), _f32(noise)
+    T, d = x.shape
+    E = Wr.shape[0]
+    assert Wr.shape == (E, d)
+    assert bias is None or bias.shape == (E,)
+    assert noise is None or noise.shape == (T, E)
+    h = np.empty((T, E), np.float32)
+    _load().orc_router_logits(T, d, E, _p(x), _p(Wr), _p(bias), _p(noise), _p(h))
+    return h
+
+
+def gate(h, k, mode):
+    """Softmax, top-k (largest first, ties to the lower index) and gates
+    ("Top-k gating").  Returns idx int32 [T,k], gates f64 [T,k],
+    p f64 [T,E], lse f64 [T]."""
+    h = _f32(h)
+    T, E = h.shape
+    idx = np.empty((T, k), np.int32)
+    g = np.empty((T, k), np.float64)
+    p = np.empty((T, E), np.float64)
+    lse = np.empty((T,), np.float64)
+    rc = _load().orc_gate(T, E, k, _GATE[mode], _p(h), _p(idx), _p(g), _p(p), _p(lse))
+    if rc != 0:
+        raise ValueError("orc_gate: bad arguments")
+    return idx, g, p, lse
+
+
+def capacity(T, E, k, cf):
+    """ceil(cf*T*k/E), or None for no limit ("Capacity and dropped tokens")."""
+    c = _load().orc_capacity(T, E, k, float(cf))
+    return None if c < 0 else int(c)
+
+
+def dispatch(idx, E, C):
+    """Token-ordered per-expert lists cut at capacity C (None = no limit)
+    ("Capacity and dropped tokens"; the listing's nonzero + [:capacity])."""
+    idx = np.ascontiguousarray(idx, dtype=np.int32)
+    T, k = idx.shape
+    out = dict(
+        routed=np.empty(E, np.int32), kept=np.empty(E, np.int32),
+        offsets=np.empty(E + 1, np.int32), row_of_slot=np.empty((T, k), np.int32),
+        token_of_row=np.empty(T * k, np.int32), dropped=np.empty((T, k), np.uint8))
+    _load().orc_dispatch(T, E, k, -1 if C is None else int(C), _p(idx),
+                         _p(out["routed"]), _p(out["kept"]), _p(out["offsets"]),
+                         _p(out["row_of_slot"]), _p(out["token_of_row"]), _p(out["dropped"]))
+    return out
+
+
+def expert_ffn(tok, ex, x, W1, W3, W2, act):
+    """E_e(x_t) for each (t, e) pair ("Implementation": SwiGLU expert; ReLU/GELU
+    experts d -> d_ff -> d).  Weights: W1, W3 [E][d_ff][d], W2 [E][d][d_ff]."""
+    tok = np.ascontiguousarray(tok, dtype=np.int32)
+    ex = np.ascontiguousarray(ex, dtype=np.int32)
+    x, W1, W2 = _f32(x), _f32(W1), _f32(W2)
+    W3 = _f32(W3) if act == "swiglu" else None
+    if act == "swiglu" and W3 is None:
+        raise ValueError("swiglu needs W3")
+    n = tok.shape[0]
+    d = x.shape[1]
+    d_ff = W1.shape[1]
+    assert W1.shape[2] == d and W2.shape[1:] == (d, d_ff)
+    out = np.empty((n, d), np.float32)
+    _load().orc_expert_ffn(n, _p(tok), _p(ex), d, d_ff, _ACT[act], _p(x), _p(W1),
+                           _p(W3), _p(W2), _p(out))
+    return out
+
+
+def combine(gates, rows, ys):
+    """y_t = sum over kept slots, in slot order, of g_s * ys[row] (Eq. for y in
+    "Replacing the feed-forward block"; fully dropped tokens give 0)."""
+    gates = np.ascontiguousarray(gates, dtype=np.float64)
+    rows = np.ascontiguousarray(rows, dtype=np.int32)
+    ys = _f32(ys)
+    n, k = gates.shape
+    d = ys.shape[1]
+    y = np.empty((n, d), np.float32)
+    _load().orc_combine(n, k, d, _p(gates), _p(rows), _p(ys), _p(y))
+    return y
+
+
+def stats(idx, p, lse):
+    """f, P, aux = E*sum f P, z = mean lse^2 ("The load-balancing loss")."""
+    idx = np.ascontiguousarray(idx, dtype=np.int32)
+    p = np.ascontiguousarray(p, dtype=np.float64)
+    lse = np.ascontiguousarray(lse, dtype=np.float64)
+    T, k = idx.shape
+    E = p.shape[1]
+    f = np.empty(E, np.float64)
+    P = np.empty(E, np.float64)
+    aux = np.zeros(1, np.float64)
+    z = np.zeros(1, np.float64)
+    _load().orc_stats(T, E, k, _p(idx), _p(p), _p(lse), _p(f), _p(P), _p(aux), _p(z))
+    return f, P, float(aux[0]), float(z[0])
+
+
+def route(x, Wr, k, mode, bias=None, noise=None):
+    """Router + gate + statistics for all tokens."""
+    h = router_logits(x, Wr, bias, noise)
+    idx, g, p, lse = gate(h, k, mode)
+    f, P, aux, z = stats(idx, p, lse)
+    return dict(h=h, idx=idx, gates=g, p=p, lse=lse, f=f, P=P, aux=aux, z=z)
+
+
+def forward(x, Wr, W1, W3, W2, k, mode, cf, act, bias=None, noise=None, tokens=None):
+    """Whole layer forward.  Routing, dispatch and statistics always cover
+    every token (capacity couples tokens through their order); the expert
+    FFN and the combine run for ``tokens`` only (all tokens if None), and
+    ``y`` then holds those tokens' rows in the order given."""
+    x = _f32(x)
+    T, d = x.shape
+    E = Wr.shape[0]
+    r = route(x, Wr, k, mode, bias, noise)
+    C = capacity(T, E, k, cf)
+    disp = dispatch(r["idx"], E, C)
+    sel = np.arange(T, dtype=np.int64) if tokens is None else np.asarray(tokens, np.int64)
+    kept = disp["row_of_slot"][sel] >= 0                       # [n, k]
+    pair_t = np.repeat(sel, k).reshape(len(sel), k)[kept]
+    pair_e = r["idx"][sel][kept]
+    ys = expert_ffn(pair_t, pair_e, x, W1, W3, W2, act) if len(pair_t) else \
+        np.zeros((0, d), np.float32)
+    rows = np.full((len(sel), k), -1, np.int32)
+    rows[kept] = np.arange(int(kept.sum()), dtype=np.int32)
+    y = combine(r["gates"][sel], rows, ys)
+    out = dict(r)
+    out.update(disp)
+    out.update(C=C, y=y, tokens=sel)
+    return out

@@ -1,0 +1,50 @@
+"""Rejection of near-tied router logits -- TEST INFRASTRUCTURE.
+
+The GPU accumulates the fp32 router in a different order from the oracle,
+so a token whose deciding logits are closer than the rounding difference
+could be routed differently.  Inputs are therefore filtered on the oracle's
+fp32 logits: a token is redrawn (row t of x and of the noise, from the
+generator's per-row retry stream) until every gap between consecutive
+logits among its top k+1 (top k when k = E) is at least ``margin``.  The
+gaps checked include those inside the top k, because slot order is part of
+the routing that must match exactly.
+"""
+import numpy as np
+
+from . import router_logits
+
+
+def tight_tokens(h: np.ndarray, k: int, margin: float) -> np.ndarray:
+    """Indices of tokens whose deciding logit gaps are below ``margin``."""
+    E = h.shape[1]
+    m = k if k == E else k + 1
+    if m < 2:
+        return np.zeros(0, np.int64)
+    s = -np.sort(-h.astype(np.float64), axis=1)[:, :m]
+    gaps = s[:, :-1] - s[:, 1:]
+    return np.nonzero((gaps < margin).any(axis=1))[0]
+
+
+def reject_near_ties(w, weights, tokens, seed=0, step=0, margin=1e-4, max_attempts=64):
+    """Redraw, in place, every token of ``tokens`` (from synth.make_tokens)
+    whose deciding logit gaps are below ``margin``.  Returns the number of
+    redrawn rows.  ``w`` is a synth.Workload and ``weights`` its weights."""
+    from sparse_mixture_experts_03_amd import synth
+
+    Wr, bias = weights["Wr"], weights["bias"]
+    x, noise = tokens["x"], tokens["noise"]
+    h = router_logits(synth.widen(x), Wr, bias, noise)
+    bad = tight_tokens(h, w.k, margin)
+    redrawn = 0
+    for attempt in range(1, max_attempts + 1):
+        if len(bad) == 0:
+            return redrawn
+        for t in bad:
+            xr, nr = synth.redraw_token(w, seed, step, int(t), attempt)
+            x[t] = xr
+            if noise is not None:
+                noise[t] = nr
+        redrawn += len(bad)
+        hb = router_logits(synth.widen(x[bad]), Wr, bias, None if noise is None else noise[bad])
+        bad = bad[tight_tokens(hb, w.k, margin)]
+    raise RuntimeError("margin rejection did not converge")

@@ -1,0 +1,369 @@
+/*
+ * moe_oracle.c -- CPU oracle for the forward pass of a sparse
+ * Mixture-of-Experts FFN layer.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg may load this library.  The GPU library
+ * never links, includes or calls it, and this file includes nothing from
+ * the GPU side: the two share no code.
+ *
+ * What it computes follows the page "Mixture of experts" (rayaq.ca,
+ * ml-models/mixture-of-experts), section Mechanics:
+ *   - "Replacing the feed-forward block": h = W_r x, p = softmax(h),
+ *     y = sum over i in TopK(h) of g_i(x) * E_i(x);
+ *   - "Top-k gating": the Switch gate (g = full-softmax p of the argmax
+ *     expert) and the renormalised top-k gate (softmax over the k chosen
+ *     logits); noise, when used, is added to the logits before the top-k;
+ *   - "The load-balancing loss": f_i, P_i, E * sum f_i P_i, and the ST-MoE
+ *     z statistic mean_t (log sum_j exp h_tj)^2;
+ *   - "Capacity and dropped tokens": capacity from the capacity factor,
+ *     slots filled in token (position) order, overflow tokens skip the
+ *     expert and contribute nothing to the layer output;
+ * and section Implementation (the SwiGLU expert, bias-free Linears, the
+ * float32 router, the token-ordered per-expert lists).
+ *
+ * Precision: every input is fp32 (bf16 inputs are widened exactly by the
+ * caller).  Every sum is accumulated in double, sequentially, in index
+ * order, and rounded to fp32 once where a stored fp32 tensor is produced
+ * (logits, expert hidden H, expert output rows, layer output).  Threads
+ * split tokens or rows only, never a sum, so results do not depend on the
+ * thread count.  The one blocking used (several independent output
+ * elements updated in the same inner loop) keeps each element's own sum
+ * strictly sequential; it only lets the compiler vectorise across
+ * independent elements.
+ *
+ * Readings of points the page leaves open (each is also listed in the
+ * design notes of the repository):
+ *   - noise and bias are added to the logits, and the noisy logits are
+ *     used everywhere downstream (p, top-k, gates, statistics);
+ *   - top-k order: descending logit, ties to the lower expert index;
+ *   - capacity C = ceil(cf * T * k / E) evaluated in double in exactly
+ *     that order; cf <= 0 means no limit;
+ *   - drop priority is token order within each expert, whatever the slot;
+ *   - gates are not renormalised after drops;
+ *   - f_i counts top (slot-0) choices before any drop;
+ *   - GELU is the exact erf form.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORC_GATE_RENORM 0 /* softmax over the k selected logits */
+#define ORC_GATE_SWITCH 1 /* full-softmax probability of each selected expert */
+
+#define ORC_ACT_RELU 0
+#define ORC_ACT_GELU 1
+#define ORC_ACT_SWIGLU 2
+
+/* Number of independent output elements updated together in one inner loop. */
+#define ORC_BLK 8
+
+/*
+ * Router logits ("Replacing the feed-forward block": h = W_r x; the
+ * router is one bias-free Linear with E rows, computed in float32 per the
+ * Implementation section's closing advice).
+ *   x     [T][d]   fp32
+ *   Wr    [E][d]   fp32
+ *   bias  [E]      fp32 or NULL
+ *   noise [T][E]   fp32 or NULL ("Top-k gating": noise added to the logits
+ *                  before the top-k)
+ *   h     [T][E]   fp32 out: h[t][i] = fl32(sum_j x[t][j] Wr[i][j] + b[i] + n[t][i])
+ */
+void orc_router_logits(int64_t T, int64_t d, int64_t E, const float *x,
+                       const float *Wr, const float *bias, const float *noise,
+                       float *h)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < T; ++t) {
+        const float *xt = x + t * d;
+        for (int64_t i = 0; i < E; ++i) {
+            const float *wi = Wr + i * d;
+            double acc = 0.0;
+            for (int64_t j = 0; j < d; ++j)
+                acc += (double)xt[j] * (double)wi[j];
+            if (bias)
+                acc += (double)bias[i];
+            if (noise)
+                acc += (double)noise[t * E + i];
+            h[t * E + i] = (float)acc;
+        }
+    }
+}
+
+/*
+ * Softmax, log-sum-exp, top-k and gates for every token.
+ *   h      [T][E] fp32 logits
+ *   idx    [T][k] int32 out: the k largest logits, largest first, ties to
+ *                 the lower expert index ("Top-k gating": keep the k
+ *                 largest logits)
+ *   gates  [T][k] double out:
+ *                 RENORM: softmax over the k selected logits
+ *                 SWITCH: full-softmax probability p of each selected expert
+ *   p      [T][E] double out (may be NULL): p = softmax(h)
+ *   lse    [T]    double out (may be NULL): log sum_j exp h_j
+ * Returns 0, or -1 on bad arguments.
+ */
+int orc_gate(int64_t T, int64_t E, int64_t k, int mode, const float *h,
+             int32_t *idx, double *gates, double *p, double *lse)
+{
+    if (k < 1 || k > E || (mode != ORC_GATE_RENORM && mode != ORC_GATE_SWITCH))
+        return -1;
+    int bad = 0;
+#pragma omp parallel for schedule(static) reduction(| : bad)
+    for (int64_t t = 0; t < T; ++t) {
+        const float *ht = h + t * E;
+        /* full softmax in double */
+        double m = (double)ht[0];
+        for (int64_t i = 1; i < E; ++i)
+            if ((double)ht[i] > m)
+                m = (double)ht[i];
+        double s = 0.0;
+        for (int64_t i = 0; i < E; ++i)
+            s += exp((double)ht[i] - m);
+        if (p)
+            for (int64_t i = 0; i < E; ++i)
+                p[t * E + i] = exp((double)ht[i] - m) / s;
+        if (lse)
+            lse[t] = m + log(s);
+
+        /* top-k by k successive scans for the best expert not yet taken;
+         * the strict '>' on an ascending scan keeps the lower index on a tie */
+        char *taken = (char *)calloc((size_t)E, 1);
+        if (!taken) {
+            bad = 1;
+            continue;
+        }
+        int32_t *it = idx + t * k;
+        for (int64_t sl = 0; sl < k; ++sl) {
+            int64_t best = -1;
+            for (int64_t i = 0; i < E; ++i)
+                if (!taken[i] && (best < 0 || ht[i] > ht[best]))
+                    best = i;
+            taken[best] = 1;
+            it[sl] = (int32_t)best;
+        }
+        free(taken);
+
+        double *gt = gates + t * k;
+        if (mode == ORC_GATE_RENORM) {
+            /* softmax over the selected logits, shifted by the largest one */
+            double top = (double)ht[it[0]];
+            double den = 0.0;
+            for (int64_t sl = 0; sl < k; ++sl)
+                den += exp((double)ht[it[sl]] - top);
+            for (int64_t sl = 0; sl < k; ++sl)
+                gt[sl] = exp((double)ht[it[sl]] - top) / den;
+        } else {
+            for (int64_t sl = 0; sl < k; ++sl)
+                gt[sl] = exp((double)ht[it[sl]] - m) / s;
+        }
+    }
+    return bad ? -1 : 0;
+}
+
+/*
+ * Expert capacity ("Capacity and dropped tokens": tokens per batch over
+ * number of experts, times the capacity factor).  With k slots per token
+ * the assignments per batch are T*k, which is what a factor of 1 must
+ * balance exactly; the result is rounded up.  cf <= 0 means no limit
+ * (dropless), returned as -1.
+ */
+int64_t orc_capacity(int64_t T, int64_t E, int64_t k, double cf)
+{
+    if (!(cf > 0.0))
+        return -1;
+    return (int64_t)ceil(cf * (double)T * (double)k / (double)E);
+}
+
+/*
+ * Dispatch with capacity ("Capacity and dropped tokens"; the Implementation
+ * listing's per-expert token lists, which are in token order and cut at
+ * the capacity).  For each expert e, its assignments (t, s) with
+ * idx[t][s] == e are ranked in token order; rank < C is kept, the rest
+ * are dropped.  Kept rows are laid out expert after expert.
+ *   idx          [T][k] int32 in
+ *   C            capacity, or < 0 for no limit
+ *   routed       [E]    out: assignments per expert before dropping
+ *   kept         [E]    out: min(routed, C)
+ *   offsets      [E+1]  out: exclusive prefix sum of kept
+ *   row_of_slot  [T][k] out: row of the kept assignment, -1 if dropped
+ *   token_of_row [T*k]  out: token of each kept row (first offsets[E] valid;
+ *                       the rest are set to -1)
+ *   dropped      [T][k] out: 1 if dropped, else 0
+ */
+void orc_dispatch(int64_t T, int64_t E, int64_t k, int64_t C,
+                  const int32_t *idx, int32_t *routed, int32_t *kept,
+                  int32_t *offsets, int32_t *row_of_slot,
+                  int32_t *token_of_row, uint8_t *dropped)
+{
+    for (int64_t e = 0; e < E; ++e) {
+        int64_t n = 0;
+        for (int64_t t = 0; t < T; ++t)
+            for (int64_t s = 0; s < k; ++s)
+                if (idx[t * k + s] == e)
+                    ++n;
+        routed[e] = (int32_t)n;
+        kept[e] = (int32_t)((C >= 0 && n > C) ? C : n);
+    }
+    offsets[0] = 0;
+    for (int64_t e = 0; e < E; ++e)
+        offsets[e + 1] = offsets[e] + kept[e];
+    for (int64_t r = 0; r < T * k; ++r)
+        token_of_row[r] = -1;
+    for (int64_t e = 0; e < E; ++e) {
+        int64_t rank = 0;
+        for (int64_t t = 0; t < T; ++t)
+            for (int64_t s = 0; s < k; ++s) {
+                if (idx[t * k + s] != e)
+                    continue;
+                if (C < 0 || rank < C) {
+                    int32_t row = offsets[e] + (int32_t)rank;
+                    token_of_row[row] = (int32_t)t;
+                    row_of_slot[t * k + s] = row;
+                    dropped[t * k + s] = 0;
+                } else {
+                    row_of_slot[t * k + s] = -1;
+                    dropped[t * k + s] = 1;
+                }
+                ++rank;
+            }
+    }
+}
+
+static double orc_act(int act, double a1, double a3)
+{
+    switch (act) {
+    case ORC_ACT_RELU:
+        return a1 > 0.0 ? a1 : 0.0;
+    case ORC_ACT_GELU:
+        /* exact GELU: a * Phi(a), Phi the standard normal CDF */
+        return 0.5 * a1 * (1.0 + erf(a1 / sqrt(2.0)));
+    default:
+        /* SwiGLU ("Implementation": w2(silu(w1 x) * w3 x)), silu(z) = z / (1 + e^-z) */
+        return (a1 / (1.0 + exp(-a1))) * a3;
+    }
+}
+
+/*
+ * Expert FFN on n (token, expert) pairs ("Implementation": the SwiGLU
+ * expert w2(silu(w1 x) * w3 x) with bias-free Linears; ReLU and GELU
+ * experts are d -> d_ff -> d with the activation between).
+ *   tok, ex  [n]            token and expert of each pair
+ *   x        [T][d]         fp32
+ *   W1, W3   [E][d_ff][d]   fp32 (W3 only for SwiGLU, else may be NULL)
+ *   W2       [E][d][d_ff]   fp32
+ *   out      [n][d]         fp32: out[r] = fl32(W2_e fl32(act(W1_e x, W3_e x)))
+ */
+void orc_expert_ffn(int64_t n, const int32_t *tok, const int32_t *ex,
+                    int64_t d, int64_t d_ff, int act, const float *x,
+                    const float *W1, const float *W3, const float *W2,
+                    float *out)
+{
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t r = 0; r < n; ++r) {
+        const float *xr = x + (int64_t)tok[r] * d;
+        const int64_t e = ex[r];
+        const float *w1 = W1 + e * d_ff * d;
+        const float *w3 = (act == ORC_ACT_SWIGLU) ? W3 + e * d_ff * d : NULL;
+        const float *w2 = W2 + e * d * d_ff;
+        float *H = (float *)malloc((size_t)d_ff * sizeof(float));
+        double *xd = (double *)malloc((size_t)(d > d_ff ? d : d_ff) * sizeof(double));
+        if (!H || !xd) {
+            free(H);
+            free(xd);
+            continue;
+        }
+        for (int64_t j = 0; j < d; ++j)
+            xd[j] = (double)xr[j];
+        /* hidden: H_f = fl32(act(sum_j x_j W1[f][j], sum_j x_j W3[f][j])) */
+        for (int64_t f0 = 0; f0 < d_ff; f0 += ORC_BLK) {
+            int64_t nb = d_ff - f0 < ORC_BLK ? d_ff - f0 : ORC_BLK;
+            double a1[ORC_BLK] = {0}, a3[ORC_BLK] = {0};
+            for (int64_t j = 0; j < d; ++j)
+                for (int64_t u = 0; u < nb; ++u)
+                    a1[u] += xd[j] * (double)w1[(f0 + u) * d + j];
+            if (w3)
+                for (int64_t j = 0; j < d; ++j)
+                    for (int64_t u = 0; u < nb; ++u)
+                        a3[u] += xd[j] * (double)w3[(f0 + u) * d + j];
+            for (int64_t u = 0; u < nb; ++u)
+                H[f0 + u] = (float)orc_act(act, a1[u], a3[u]);
+        }
+        /* output: out_o = fl32(sum_f H_f W2[o][f]) */
+        for (int64_t f = 0; f < d_ff; ++f)
+            xd[f] = (double)H[f];
+        for (int64_t o0 = 0; o0 < d; o0 += ORC_BLK) {
+            int64_t nb = d - o0 < ORC_BLK ? d - o0 : ORC_BLK;
+            double acc[ORC_BLK] = {0};
+            for (int64_t f = 0; f < d_ff; ++f)
+                for (int64_t u = 0; u < nb; ++u)
+                    acc[u] += xd[f] * (double)w2[(o0 + u) * d_ff + f];
+            for (int64_t u = 0; u < nb; ++u)
+                out[r * d + o0 + u] = (float)acc[u];
+        }
+        free(H);
+        free(xd);
+    }
+}
+
+/*
+ * Gate-weighted combine ("Replacing the feed-forward block":
+ * y = sum over the selected experts of g_i E_i(x); the Implementation
+ * listing's index_add_ of the gated expert outputs).  Slots are summed in
+ * slot order; a dropped slot contributes nothing, so a token whose every
+ * slot was dropped gets 0 ("Capacity and dropped tokens": the residual,
+ * outside the layer, carries it).
+ *   gates [n][k] double
+ *   rows  [n][k] int32: row of ys holding E_{idx[t][s]}(x_t), or -1 if dropped
+ *   ys    [*][d] fp32 expert outputs
+ *   y     [n][d] fp32 out
+ */
+void orc_combine(int64_t n, int64_t k, int64_t d, const double *gates,
+                 const int32_t *rows, const float *ys, float *y)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < n; ++t)
+        for (int64_t o = 0; o < d; ++o) {
+            double acc = 0.0;
+            for (int64_t s = 0; s < k; ++s) {
+                int32_t r = rows[t * k + s];
+                if (r >= 0)
+                    acc += gates[t * k + s] * (double)ys[(int64_t)r * d + o];
+            }
+            y[t * d + o] = (float)acc;
+        }
+}
+
+/*
+ * Load-balancing statistics ("The load-balancing loss"; the listing's
+ * f, aux and z).  Means run over all T tokens, dropped ones included.
+ *   f[i]  = #{t : idx[t][0] == i} / T   (top choice, before any drop)
+ *   P[i]  = sum_t p[t][i] / T
+ *   aux   = E * sum_i f[i] P[i]         (unweighted; alpha is applied by the caller)
+ *   z     = sum_t lse[t]^2 / T          (unweighted)
+ */
+void orc_stats(int64_t T, int64_t E, int64_t k, const int32_t *idx,
+               const double *p, const double *lse, double *f, double *P,
+               double *aux, double *z)
+{
+    for (int64_t i = 0; i < E; ++i) {
+        f[i] = 0.0;
+        P[i] = 0.0;
+    }
+    for (int64_t t = 0; t < T; ++t)
+        f[idx[t * k]] += 1.0;
+    for (int64_t t = 0; t < T; ++t)
+        for (int64_t i = 0; i < E; ++i)
+            P[i] += p[t * E + i];
+    double a = 0.0, zz = 0.0;
+    for (int64_t i = 0; i < E; ++i) {
+        f[i] /= (double)T;
+        P[i] /= (double)T;
+        a += f[i] * P[i];
+    }
+    for (int64_t t = 0; t < T; ++t)
+        zz += lse[t] * lse[t];
+    *aux = (double)E * a;
+    *z = zz / (double)T;
+}
