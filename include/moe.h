@@ -1,0 +1,220 @@
+/*
+ * moe.h -- C ABI of libmoe: the forward pass of a sparse Mixture-of-Experts
+ * FFN layer on one AMD Instinct MI355X (gfx950).
+ *
+ * The layer follows the page "Mixture of experts" (rayaq.ca,
+ * ml-models/mixture-of-experts), section Mechanics:
+ *   h = W_r x,  p = softmax(h),  y = sum_{i in TopK(h)} g_i(x) E_i(x)
+ * ("Replacing the feed-forward block"), with the gate conventions of
+ * "Top-k gating", the statistics of "The load-balancing loss" and the
+ * capacity rule of "Capacity and dropped tokens"; the expert is the
+ * bias-free SwiGLU (or a ReLU/GELU FFN) of the Implementation section,
+ * whose loop over experts is replaced here by a sort of tokens by expert
+ * and a grouped matrix multiply, as that section describes.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - All tensor arguments are DEVICE pointers to row-major arrays, owned by
+ *    the caller, aligned to 16 bytes.  The library never allocates or frees
+ *    device memory and keeps no per-call state.
+ *  - "act dtype" below means fp32 when desc->dtype == MOE_DTYPE_F32 and
+ *    bf16 (uint16 bit patterns) when desc->dtype == MOE_DTYPE_BF16.  The
+ *    router (W_r, bias, noise, logits) is always fp32.
+ *  - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream)
+ *    and runs asynchronously; no call synchronises with the host.  Results
+ *    are valid once the caller has synchronised the stream.  Calls on
+ *    distinct streams with distinct buffers may run concurrently.
+ *  - Every argument is validated before anything is enqueued: a call that
+ *    returns an error has launched nothing.  Errors are returned as status
+ *    codes (below); nothing is thrown across the ABI.  A fault inside a
+ *    kernel (e.g. a pointer to too small a buffer) cannot be detected by
+ *    the call and surfaces at the caller's next synchronisation.
+ *  - `ws` is a device workspace of at least moe_workspace_size() bytes,
+ *    `ws_bytes` its size.  Its contents on entry do not matter.
+ *  - Given the same inputs, every output is bitwise reproducible: no
+ *    floating-point atomics are used, and every sum runs in a fixed order.
+ *
+ * Shapes (T tokens, d model width, d_ff expert hidden width, E experts,
+ * k experts per token):
+ *   x            [T][d]        act dtype    tokens, batch and sequence flattened
+ *   W_r          [E][d]        fp32         router rows
+ *   bias         [E]           fp32         optional router bias (NULL = none)
+ *   noise        [T][E]        fp32         optional logit noise (NULL = none)
+ *   W1, W3       [E][d_ff][d]  act dtype    up projections (W3 only for SwiGLU)
+ *   W2           [E][d][d_ff]  act dtype    down projection
+ *   topk_idx     [T][k]        int32        chosen experts, largest logit first
+ *   gates        [T][k]        fp32         gate of each chosen expert
+ *   routed_counts[E]           int32        assignments per expert before drops
+ *   kept_counts  [E]           int32        min(routed, C)
+ *   offsets      [E+1]         int32        exclusive prefix sum of kept_counts
+ *   row_of_slot  [T][k]        int32        permuted row of (t, s), -1 if dropped
+ *   token_of_row [T*k]         int32        token of each permuted row; entries
+ *                                           at and after offsets[E] are -1
+ *   dropped      [T][k]        uint8        1 if (t, s) was dropped by capacity
+ *   x_perm       [T*k][d]      act dtype    x rows in expert order (first
+ *                                           offsets[E] rows written)
+ *   y_perm       [T*k][d]      fp32         expert outputs in the same order
+ *   y            [T][d]        act dtype    layer output
+ *   stats        [2E+2]        fp32         f[E], P[E], aux, z (see moe_route)
+ */
+#ifndef MOE_H_
+#define MOE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ------------------------------------------------------ */
+#define MOE_OK 0
+#define MOE_ERR_INVALID_ARG (-1) /* bad size, null required pointer, bad enum */
+#define MOE_ERR_UNSUPPORTED (-2) /* valid but outside what the kernels handle */
+#define MOE_ERR_HIP (-3)         /* the HIP runtime reported an error        */
+#define MOE_ERR_WORKSPACE (-4)   /* ws_bytes below moe_workspace_size()       */
+
+/* ---- gate conventions ("Top-k gating") ---------------------------------- */
+/* Renormalised top-k (Mixtral): softmax over the k selected logits. */
+#define MOE_GATE_RENORM 0
+/* Switch: the full-softmax probability p of each selected expert (k = 1 is
+ * the Switch Transformer gate; k > 1 keeps p for every selected expert). */
+#define MOE_GATE_SWITCH 1
+
+/* ---- expert activation --------------------------------------------------- */
+#define MOE_ACT_RELU 0   /* W2 relu(W1 x)                                   */
+#define MOE_ACT_GELU 1   /* W2 gelu(W1 x), exact erf form                   */
+#define MOE_ACT_SWIGLU 2 /* W2 (silu(W1 x) * W3 x)  ("Implementation")      */
+
+/* ---- storage type of x, expert weights, x_perm and y --------------------- */
+#define MOE_DTYPE_F32 0
+#define MOE_DTYPE_BF16 1
+
+/* Router logits of one token live in registers: E is at most this. */
+#define MOE_MAX_EXPERTS 128
+
+/* Number of kernel stages of moe_forward, for the optional stage events. */
+#define MOE_FORWARD_STAGES 7
+
+/*
+ * Problem description: the page's MoE(d, d_ff, num_experts, k, capacity)
+ * plus the batch size T, the gate convention, the activation and the
+ * storage type.
+ *
+ * capacity_factor: 0 means no capacity limit (dropless).  Otherwise the
+ * capacity of every expert is C = ceil(capacity_factor * T * k / E),
+ * evaluated in double precision in exactly that order ("Capacity and
+ * dropped tokens": tokens per batch over experts, times the factor; with k
+ * slots per token the batch holds T*k assignments).  Each expert keeps its
+ * first C assignments in token order and drops the rest.
+ *
+ * stage_events / n_stage_events: optional profiling hook.  When non-NULL,
+ * stage_events points to n_stage_events hipEvent_t handles; moe_forward
+ * records event j after its j-th kernel stage (event 0 before the first),
+ * for j < n_stage_events, on `stream`; MOE_FORWARD_STAGES + 1 events
+ * bracket every stage.  NULL disables it.  The stages, in order: route,
+ * route-finalize, dispatch, gather, expert-up, expert-down, combine.
+ * The other entry points ignore it.
+ */
+typedef struct moe_desc {
+    int32_t T, d, d_ff, E, k;
+    int32_t gate;  /* MOE_GATE_*  */
+    int32_t act;   /* MOE_ACT_*   */
+    int32_t dtype; /* MOE_DTYPE_* */
+    double capacity_factor;
+    void *const *stage_events;
+    int32_t n_stage_events;
+} moe_desc;
+
+/*
+ * Workspace bytes needed by any entry point for this description.
+ * Returns MOE_OK, MOE_ERR_INVALID_ARG or MOE_ERR_UNSUPPORTED (the same
+ * validation as the compute calls).  Host only; enqueues nothing.
+ */
+int moe_workspace_size(const moe_desc *desc, size_t *bytes);
+
+/*
+ * The capacity C for this description, or -1 when there is no limit.
+ * Host only.
+ */
+int moe_capacity(const moe_desc *desc, int64_t *capacity);
+
+/*
+ * Router, gate and load-balancing statistics ("Replacing the feed-forward
+ * block", "Top-k gating", "The load-balancing loss").
+ *   h[t][i]  = sum_j x[t][j] W_r[i][j] + bias[i] + noise[t][i]   (fp32)
+ *   p[t]     = softmax(h[t]),  lse[t] = log sum_i exp h[t][i]
+ *   topk_idx = the k largest logits, largest first, ties to the lower index
+ *   gates    = RENORM: softmax over the k selected logits
+ *              SWITCH: p of each selected expert
+ *   stats    = f[E]  : share of tokens whose top choice (slot 0) is i,
+ *                      counted before any capacity drop
+ *              P[E]  : mean over tokens of p[t][i]
+ *              aux   : E * sum_i f[i] P[i]   (unweighted; 1 when balanced)
+ *              z     : mean over tokens of lse[t]^2   (unweighted)
+ * Inputs x, W_r, bias?, noise?; outputs topk_idx, gates, stats.
+ */
+int moe_route(const moe_desc *desc, const void *x, const float *W_r, const float *bias,
+              const float *noise, int32_t *topk_idx, float *gates, float *stats, void *ws,
+              size_t ws_bytes, void *stream);
+
+/*
+ * Capacity and dispatch ("Capacity and dropped tokens"; the
+ * Implementation section's sort of tokens by expert).  For each expert,
+ * its assignments (t, s) are ranked in token order; the first C are kept
+ * and laid out expert after expert (expert e owns rows
+ * [offsets[e], offsets[e+1]) in token order), the rest are dropped.
+ * Then x_perm[r] = x[token_of_row[r]] for r < offsets[E].
+ * Input x, topk_idx; outputs routed_counts, kept_counts, offsets,
+ * row_of_slot, token_of_row, dropped, x_perm.
+ */
+int moe_dispatch(const moe_desc *desc, const void *x, const int32_t *topk_idx,
+                 int32_t *routed_counts, int32_t *kept_counts, int32_t *offsets,
+                 int32_t *row_of_slot, int32_t *token_of_row, uint8_t *dropped, void *x_perm,
+                 void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Expert FFNs as a grouped matrix multiply over the ragged per-expert row
+ * blocks given by offsets (read on the device; the host never learns the
+ * counts).  For every row r of expert e (offsets[e] <= r < offsets[e+1]):
+ *   H      = act(x_perm[r] W1_e^T) [* (x_perm[r] W3_e^T) for SwiGLU]
+ *   y_perm[r] = H W2_e^T
+ * H is kept in the workspace in the act dtype; accumulation is fp32.
+ * Experts with no rows read none of their weights.  W3 must be NULL
+ * unless act is SwiGLU (then it is required).
+ */
+int moe_expert_ffn(const moe_desc *desc, const void *x_perm, const int32_t *offsets,
+                   const void *W1, const void *W3, const void *W2, float *y_perm, void *ws,
+                   size_t ws_bytes, void *stream);
+
+/*
+ * Gate-weighted combine (the equation for y): for every token t,
+ *   y[t] = sum_{s = 0..k-1, row_of_slot[t][s] >= 0} gates[t][s] * y_perm[row_of_slot[t][s]]
+ * summed in fp32 in slot order and stored in the act dtype.  A token whose
+ * every slot was dropped gets 0 (the residual outside the layer carries
+ * it).  Gates are not renormalised after drops.
+ */
+int moe_combine(const moe_desc *desc, const float *y_perm, const int32_t *row_of_slot,
+                const float *gates, void *y, void *stream);
+
+/*
+ * The whole layer: moe_route, moe_dispatch, moe_expert_ffn and moe_combine
+ * in sequence on `stream`, with x_perm and y_perm held in the workspace.
+ * Required: x, W_r, W1, W2 (W3 for SwiGLU), y, ws.  Every other output
+ * pointer may be NULL, in which case that tensor lives in the workspace
+ * and is not returned.
+ */
+int moe_forward(const moe_desc *desc, const void *x, const float *W_r, const float *bias,
+                const float *noise, const void *W1, const void *W3, const void *W2, void *y,
+                int32_t *topk_idx, float *gates, int32_t *routed_counts, int32_t *kept_counts,
+                int32_t *offsets, int32_t *row_of_slot, int32_t *token_of_row,
+                uint8_t *dropped, float *stats, void *ws, size_t ws_bytes, void *stream);
+
+/* A static, human-readable name for a status code. */
+const char *moe_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H_ */

@@ -50,6 +50,8 @@ def _load():
     lib.orc_combine.restype = None
     lib.orc_stats.argtypes = [i64, i64, i64, ip, dp, dp, dp, dp, dp, dp]
     lib.orc_stats.restype = None
+    lib.orc_threads.argtypes = []
+    lib.orc_threads.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -158,6 +160,11 @@ def stats(idx, p, lse):
     z = np.zeros(1, np.float64)
     _load().orc_stats(T, E, k, _p(idx), _p(p), _p(lse), _p(f), _p(P), _p(aux), _p(z))
     return f, P, float(aux[0]), float(z[0])
+
+
+def threads():
+    """Host threads the oracle's parallel loops use."""
+    return int(_load().orc_threads())
 
 
 def route(x, Wr, k, mode, bias=None, noise=None):

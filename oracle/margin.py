@@ -14,8 +14,13 @@ import numpy as np
 from . import router_logits
 
 
-def tight_tokens(h: np.ndarray, k: int, margin: float) -> np.ndarray:
-    """Indices of tokens whose deciding logit gaps are below ``margin``."""
+def tight_tokens(h: np.ndarray, k: int, margin: float, ignore=()) -> np.ndarray:
+    """Indices of tokens whose deciding logit gaps are below ``margin``.
+    Columns in ``ignore`` are left out (an expert whose router row
+    duplicates another's ties with it exactly, and that tie is decided by
+    index on both sides)."""
+    if len(ignore):
+        h = np.delete(h, list(ignore), axis=1)
     E = h.shape[1]
     m = k if k == E else k + 1
     if m < 2:
@@ -25,7 +30,7 @@ def tight_tokens(h: np.ndarray, k: int, margin: float) -> np.ndarray:
     return np.nonzero((gaps < margin).any(axis=1))[0]
 
 
-def reject_near_ties(w, weights, tokens, seed=0, step=0, margin=1e-4, max_attempts=64):
+def reject_near_ties(w, weights, tokens, seed=0, step=0, margin=1e-4, max_attempts=64, ignore=()):
     """Redraw, in place, every token of ``tokens`` (from synth.make_tokens)
     whose deciding logit gaps are below ``margin``.  Returns the number of
     redrawn rows.  ``w`` is a synth.Workload and ``weights`` its weights."""
@@ -34,7 +39,7 @@ def reject_near_ties(w, weights, tokens, seed=0, step=0, margin=1e-4, max_attemp
     Wr, bias = weights["Wr"], weights["bias"]
     x, noise = tokens["x"], tokens["noise"]
     h = router_logits(synth.widen(x), Wr, bias, noise)
-    bad = tight_tokens(h, w.k, margin)
+    bad = tight_tokens(h, w.k, margin, ignore)
     redrawn = 0
     for attempt in range(1, max_attempts + 1):
         if len(bad) == 0:
@@ -46,5 +51,5 @@ def reject_near_ties(w, weights, tokens, seed=0, step=0, margin=1e-4, max_attemp
                 noise[t] = nr
         redrawn += len(bad)
         hb = router_logits(synth.widen(x[bad]), Wr, bias, None if noise is None else noise[bad])
-        bad = bad[tight_tokens(hb, w.k, margin)]
+        bad = bad[tight_tokens(hb, w.k, margin, ignore)]
     raise RuntimeError("margin rejection did not converge")

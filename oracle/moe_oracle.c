@@ -367,3 +367,17 @@ void orc_stats(int64_t T, int64_t E, int64_t k, const int32_t *idx,
     *aux = (double)E * a;
     *z = zz / (double)T;
 }
+
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* Number of host threads the oracle's parallel loops use. */
+int orc_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}

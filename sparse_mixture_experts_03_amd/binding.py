@@ -1,0 +1,245 @@
+"""Python binding of libmoe's C ABI (``include/moe.h``).
+
+Argument marshalling only: every function checks that the torch tensors it
+is given have the dtype, shape and device the ABI expects, then passes raw
+device pointers and the current HIP stream to the library.  Every step of
+the layer runs in the library's HIP kernels; there is no fallback path, and
+loading fails loudly when the library cannot be found or built.
+
+Names match the ABI: moe_workspace_size, moe_capacity, moe_route,
+moe_dispatch, moe_expert_ffn, moe_combine, moe_forward.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmoe.so")
+
+GATE = {"renorm": 0, "switch": 1}
+ACT = {"relu": 0, "gelu": 1, "swiglu": 2}
+DTYPE = {"f32": 0, "bf16": 1}
+TORCH_DTYPE = {"f32": torch.float32, "bf16": torch.bfloat16}
+FORWARD_STAGES = 7
+STAGE_NAMES = ("route", "route_finalize", "dispatch", "gather", "expert_up", "expert_down", "combine")
+
+MOE_OK = 0
+STATUS = {0: "MOE_OK", -1: "MOE_ERR_INVALID_ARG", -2: "MOE_ERR_UNSUPPORTED", -3: "MOE_ERR_HIP",
+          -4: "MOE_ERR_WORKSPACE"}
+
+
+class MoeError(RuntimeError):
+    def __init__(self, fn, code):
+        self.code = code
+        super().__init__(f"{fn} returned {code} ({STATUS.get(code, 'unknown')})")
+
+
+class MoeDesc(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int32), ("d", ctypes.c_int32), ("d_ff", ctypes.c_int32),
+                ("E", ctypes.c_int32), ("k", ctypes.c_int32), ("gate", ctypes.c_int32),
+                ("act", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("capacity_factor", ctypes.c_double),
+                ("stage_events", ctypes.POINTER(ctypes.c_void_p)),
+                ("n_stage_events", ctypes.c_int32)]
+
+
+def make_desc(T, d, d_ff, E, k, gate="renorm", act="swiglu", dtype="bf16", cf=0.0) -> MoeDesc:
+    return MoeDesc(int(T), int(d), int(d_ff), int(E), int(k), GATE[gate], ACT[act], DTYPE[dtype],
+                   float(cf), None, 0)
+
+
+def desc_for(w, T=None) -> MoeDesc:
+    """Description of a synth.Workload (optionally with another T)."""
+    return make_desc(w.T if T is None else T, w.d, w.d_ff, w.E, w.k, w.gate, w.act, w.dtype, w.cf)
+
+
+_lib = None
+
+
+def load(build_if_missing: bool = True):
+    """Load libmoe.so; build it first if it is not there."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        if not build_if_missing:
+            raise RuntimeError(f"libmoe not built: {LIB_PATH} is missing")
+        from . import build as _build
+        _build.build()
+    lib = ctypes.CDLL(LIB_PATH)
+    P = ctypes.c_void_p
+    D = ctypes.POINTER(MoeDesc)
+    sz = ctypes.c_size_t
+    lib.moe_workspace_size.argtypes = [D, ctypes.POINTER(ctypes.c_size_t)]
+    lib.moe_capacity.argtypes = [D, ctypes.POINTER(ctypes.c_int64)]
+    lib.moe_route.argtypes = [D, P, P, P, P, P, P, P, P, sz, P]
+    lib.moe_dispatch.argtypes = [D, P, P, P, P, P, P, P, P, P, P, sz, P]
+    lib.moe_expert_ffn.argtypes = [D, P, P, P, P, P, P, P, sz, P]
+    lib.moe_combine.argtypes = [D, P, P, P, P, P]
+    lib.moe_forward.argtypes = [D, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, sz, P]
+    lib.moe_status_string.argtypes = [ctypes.c_int]
+    lib.moe_status_string.restype = ctypes.c_char_p
+    for fn in ("moe_workspace_size", "moe_capacity", "moe_route", "moe_dispatch",
+               "moe_expert_ffn", "moe_combine", "moe_forward"):
+        getattr(lib, fn).restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def _check(fn, rc):
+    if rc != MOE_OK:
+        raise MoeError(fn, rc)
+
+
+def _ptr(t, dtype=None, shape=None, name="tensor", optional=False):
+    if t is None:
+        if optional:
+            return None
+        raise ValueError(f"{name} is required")
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _act_dtype(desc):
+    return torch.float32 if desc.dtype == DTYPE["f32"] else torch.bfloat16
+
+
+def moe_workspace_size(desc: MoeDesc) -> int:
+    n = ctypes.c_size_t(0)
+    _check("moe_workspace_size", load().moe_workspace_size(ctypes.byref(desc), ctypes.byref(n)))
+    return n.value
+
+
+def moe_capacity(desc: MoeDesc):
+    c = ctypes.c_int64(0)
+    _check("moe_capacity", load().moe_capacity(ctypes.byref(desc), ctypes.byref(c)))
+    return None if c.value < 0 else c.value
+
+
+def workspace(desc: MoeDesc, device="cuda") -> torch.Tensor:
+    return torch.empty(max(moe_workspace_size(desc), 1), dtype=torch.uint8, device=device)
+
+
+def moe_route(desc, x, W_r, bias, noise, topk_idx, gates, stats, ws, stream=None):
+    T, d, E, k = desc.T, desc.d, desc.E, desc.k
+    rc = load().moe_route(
+        ctypes.byref(desc), _ptr(x, _act_dtype(desc), (T, d), "x"),
+        _ptr(W_r, torch.float32, (E, d), "W_r"), _ptr(bias, torch.float32, (E,), "bias", True),
+        _ptr(noise, torch.float32, (T, E), "noise", True),
+        _ptr(topk_idx, torch.int32, (T, k), "topk_idx"), _ptr(gates, torch.float32, (T, k), "gates"),
+        _ptr(stats, torch.float32, (2 * E + 2,), "stats"), _ptr(ws, torch.uint8, None, "ws"),
+        ws.numel(), _stream(stream))
+    _check("moe_route", rc)
+
+
+def moe_dispatch(desc, x, topk_idx, routed_counts, kept_counts, offsets, row_of_slot, token_of_row,
+                 dropped, x_perm, ws, stream=None):
+    T, d, E, k = desc.T, desc.d, desc.E, desc.k
+    rc = load().moe_dispatch(
+        ctypes.byref(desc), _ptr(x, _act_dtype(desc), (T, d), "x"),
+        _ptr(topk_idx, torch.int32, (T, k), "topk_idx"),
+        _ptr(routed_counts, torch.int32, (E,), "routed_counts"),
+        _ptr(kept_counts, torch.int32, (E,), "kept_counts"),
+        _ptr(offsets, torch.int32, (E + 1,), "offsets"),
+        _ptr(row_of_slot, torch.int32, (T, k), "row_of_slot"),
+        _ptr(token_of_row, torch.int32, (T * k,), "token_of_row"),
+        _ptr(dropped, torch.uint8, (T, k), "dropped"),
+        _ptr(x_perm, _act_dtype(desc), (T * k, d), "x_perm"),
+        _ptr(ws, torch.uint8, None, "ws"), ws.numel(), _stream(stream))
+    _check("moe_dispatch", rc)
+
+
+def moe_expert_ffn(desc, x_perm, offsets, W1, W3, W2, y_perm, ws, stream=None):
+    T, d, d_ff, E, k = desc.T, desc.d, desc.d_ff, desc.E, desc.k
+    dt = _act_dtype(desc)
+    rc = load().moe_expert_ffn(
+        ctypes.byref(desc), _ptr(x_perm, dt, (T * k, d), "x_perm"),
+        _ptr(offsets, torch.int32, (E + 1,), "offsets"), _ptr(W1, dt, (E, d_ff, d), "W1"),
+        _ptr(W3, dt, (E, d_ff, d), "W3", True), _ptr(W2, dt, (E, d, d_ff), "W2"),
+        _ptr(y_perm, torch.float32, (T * k, d), "y_perm"), _ptr(ws, torch.uint8, None, "ws"),
+        ws.numel(), _stream(stream))
+    _check("moe_expert_ffn", rc)
+
+
+def moe_combine(desc, y_perm, row_of_slot, gates, y, stream=None):
+    T, d, k = desc.T, desc.d, desc.k
+    rc = load().moe_combine(
+        ctypes.byref(desc), _ptr(y_perm, torch.float32, (T * k, d), "y_perm"),
+        _ptr(row_of_slot, torch.int32, (T, k), "row_of_slot"),
+        _ptr(gates, torch.float32, (T, k), "gates"), _ptr(y, _act_dtype(desc), (T, d), "y"),
+        _stream(stream))
+    _check("moe_combine", rc)
+
+
+def moe_forward(desc, x, W_r, bias, noise, W1, W3, W2, y, ws, topk_idx=None, gates=None,
+                routed_counts=None, kept_counts=None, offsets=None, row_of_slot=None,
+                token_of_row=None, dropped=None, stats=None, stream=None):
+    T, d, d_ff, E, k = desc.T, desc.d, desc.d_ff, desc.E, desc.k
+    dt = _act_dtype(desc)
+    rc = load().moe_forward(
+        ctypes.byref(desc), _ptr(x, dt, (T, d), "x"), _ptr(W_r, torch.float32, (E, d), "W_r"),
+        _ptr(bias, torch.float32, (E,), "bias", True),
+        _ptr(noise, torch.float32, (T, E), "noise", True),
+        _ptr(W1, dt, (E, d_ff, d), "W1"), _ptr(W3, dt, (E, d_ff, d), "W3", True),
+        _ptr(W2, dt, (E, d, d_ff), "W2"), _ptr(y, dt, (T, d), "y"),
+        _ptr(topk_idx, torch.int32, (T, k), "topk_idx", True),
+        _ptr(gates, torch.float32, (T, k), "gates", True),
+        _ptr(routed_counts, torch.int32, (E,), "routed_counts", True),
+        _ptr(kept_counts, torch.int32, (E,), "kept_counts", True),
+        _ptr(offsets, torch.int32, (E + 1,), "offsets", True),
+        _ptr(row_of_slot, torch.int32, (T, k), "row_of_slot", True),
+        _ptr(token_of_row, torch.int32, (T * k,), "token_of_row", True),
+        _ptr(dropped, torch.uint8, (T, k), "dropped", True),
+        _ptr(stats, torch.float32, (2 * E + 2,), "stats", True),
+        _ptr(ws, torch.uint8, None, "ws"), ws.numel(), _stream(stream))
+    _check("moe_forward", rc)
+
+
+def status_string(code: int) -> str:
+    return load().moe_status_string(int(code)).decode()
+
+
+# ---- helpers for callers holding synth inputs (host numpy arrays) ----------
+
+def to_device(a, dtype_name, device="cuda"):
+    """A synth array (uint16 bf16 bits or float32) as a device tensor of the
+    matching torch dtype (bf16 bits are reinterpreted, not converted)."""
+    import numpy as np
+    if a is None:
+        return None
+    if a.dtype == np.uint16:
+        t = torch.from_numpy(a.view(np.int16)).view(torch.bfloat16)
+    else:
+        t = torch.from_numpy(np.ascontiguousarray(a))
+    return t.to(device)
+
+
+def alloc_outputs(desc, device="cuda") -> dict:
+    T, d, E, k = desc.T, desc.d, desc.E, desc.k
+    dt = _act_dtype(desc)
+    i32 = dict(dtype=torch.int32, device=device)
+    return dict(
+        y=torch.empty((T, d), dtype=dt, device=device),
+        topk_idx=torch.empty((T, k), **i32), gates=torch.empty((T, k), dtype=torch.float32, device=device),
+        routed_counts=torch.empty((E,), **i32), kept_counts=torch.empty((E,), **i32),
+        offsets=torch.empty((E + 1,), **i32), row_of_slot=torch.empty((T, k), **i32),
+        token_of_row=torch.empty((T * k,), **i32),
+        dropped=torch.empty((T, k), dtype=torch.uint8, device=device),
+        stats=torch.empty((2 * E + 2,), dtype=torch.float32, device=device))

@@ -1,0 +1,84 @@
+// combine.hip -- gate-weighted combine of the expert outputs.
+//
+// Page "Mixture of experts" (rayaq.ca), Mechanics, "Replacing the
+// feed-forward block": y = sum over the selected experts of g_i E_i(x);
+// Implementation: the gated expert outputs are added back per token (the
+// listing's index_add_), so a token with two experts gets both; "Capacity
+// and dropped tokens": a dropped assignment skips the expert, so it adds
+// nothing here, and a token dropped from every expert gets 0 (its residual,
+// outside the layer, carries it).
+//
+// combine_kernel: one wave per token, grid-stride over tokens.  Each lane
+// owns 4 consecutive columns and sums the k slots in slot order in fp32,
+// then stores fp32 or bf16.  Every output element is written exactly once,
+// so no memset and no atomics are needed.
+#include "moe_internal.h"
+
+namespace moe {
+
+namespace {
+
+template <bool BF16, bool VEC4>
+__global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ y_perm,
+                                                      const int32_t *__restrict__ row_of_slot,
+                                                      const float *__restrict__ gates, int T,
+                                                      int d, int k, void *__restrict__ y) {
+    const int lane = threadIdx.x & 63;
+    for (int t = blockIdx.x * 4 + (threadIdx.x >> 6); t < T; t += gridDim.x * 4) {
+        const int32_t *rs = row_of_slot + (int64_t)t * k;
+        const float *gs = gates + (int64_t)t * k;
+        if (VEC4) {
+            for (int c = lane * 4; c < d; c += 256) {
+                float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
+                for (int s = 0; s < k; ++s) {
+                    const int r = rs[s];
+                    if (r < 0) continue;
+                    const float g = gs[s];
+                    const float4 v = *(const float4 *)(y_perm + (int64_t)r * d + c);
+                    a.x = fmaf(g, v.x, a.x);
+                    a.y = fmaf(g, v.y, a.y);
+                    a.z = fmaf(g, v.z, a.z);
+                    a.w = fmaf(g, v.w, a.w);
+                }
+                if (BF16) {
+                    uint2 o;
+                    o.x = (uint32_t)f32_to_bf16(a.x) | ((uint32_t)f32_to_bf16(a.y) << 16);
+                    o.y = (uint32_t)f32_to_bf16(a.z) | ((uint32_t)f32_to_bf16(a.w) << 16);
+                    *(uint2 *)((uint16_t *)y + (int64_t)t * d + c) = o;
+                } else {
+                    *(float4 *)((float *)y + (int64_t)t * d + c) = a;
+                }
+            }
+        } else {
+            for (int c = lane; c < d; c += 64) {
+                float a = 0.f;
+                for (int s = 0; s < k; ++s) {
+                    const int r = rs[s];
+                    if (r < 0) continue;
+                    a = fmaf(gs[s], y_perm[(int64_t)r * d + c], a);
+                }
+                if (BF16)
+                    ((uint16_t *)y)[(int64_t)t * d + c] = f32_to_bf16(a);
+                else
+                    ((float *)y)[(int64_t)t * d + c] = a;
+            }
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_combine(const Shape &s, const float *y_perm, const int32_t *row_of_slot,
+                          const float *gates, void *y, hipStream_t st) {
+    int blocks = (s.T + 3) / 4;
+    if (blocks > 8192) blocks = 8192;
+    const bool v4 = (s.d % 4) == 0;
+    const bool bf = s.dtype == 1;
+    auto kern = bf ? (v4 ? combine_kernel<true, true> : combine_kernel<true, false>)
+                   : (v4 ? combine_kernel<false, true> : combine_kernel<false, false>);
+    hipLaunchKernelGGL(kern, dim3(blocks), dim3(256), 0, st, y_perm, row_of_slot, gates, s.T, s.d,
+                       s.k, y);
+    return hipGetLastError();
+}
+
+}  // namespace moe

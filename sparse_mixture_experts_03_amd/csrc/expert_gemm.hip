@@ -1,0 +1,331 @@
+// expert_gemm.hip -- the expert FFNs as grouped matrix multiplies over the
+// ragged per-expert row blocks of the permuted tokens.
+//
+// Page "Mixture of experts" (rayaq.ca), Implementation: the SwiGLU expert
+// w2(silu(w1 x) * w3 x) with bias-free Linears, and the remark that
+// production kernels replace the loop over experts by a sort of tokens by
+// expert plus a grouped matrix multiply with the same arithmetic.
+//
+// Layouts (all K-contiguous, so both MFMA operands are read K-major with no
+// repacking):  A = x_perm [rows][K=d] or H [rows][K=d_ff];
+//              W1, W3 [E][N=d_ff][K=d];  W2 [E][N=d][K=d_ff].
+// Expert e owns rows [offsets[e], offsets[e+1]), read on the device.
+//
+// gemm_bf16_kernel: one 256-thread block per (expert, BM-row tile, BN-col
+// tile).  blockIdx.y walks the concatenation of every expert's row tiles;
+// the block finds its expert from offsets (surplus blocks exit at once,
+// and an expert with no rows has no tiles, so its weights are never read).
+// The K loop stages BM x 64 of A and BN x 64 of each weight matrix through
+// LDS (double buffered, rows padded by 16 bytes against bank conflicts,
+// the next tile prefetched into registers while the current one feeds the
+// MFMAs).  Four waves split the tile 2 x 2 (or 1 x 4); each wave issues
+// v_mfma_f32_32x32x16_bf16 with fp32 accumulators.  For SwiGLU the block
+// loads the same BN rows of W1 and W3 and keeps both accumulators, so the
+// epilogue forms silu(a1) * a3 in registers and writes H once in bf16.
+// The down projection writes y_perm in fp32.
+//
+// MFMA 32x32x16 operand layout (lane l of 64): A supplies row l % 32 and
+// the 8 consecutive k at 8 * (l / 32); B supplies column l % 32 and the
+// same k; accumulator register r of lane l holds row
+// 8 * (r / 4) + 4 * (l / 32) + r % 4, column l % 32.
+//
+// gemm_f32 kernels: a plain fp32 path (one block per row, one thread per
+// output column, sequential fp32 FMA over K) for fp32 layers.
+#include "moe_internal.h"
+
+namespace moe {
+
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+constexpr int ACT_RELU = 0, ACT_GELU = 1, ACT_SWIGLU = 2, ACT_NONE = 3;
+
+__device__ __forceinline__ float apply_act(int act, float a1, float a3) {
+    if (act == ACT_SWIGLU) return a1 / (1.f + expf(-a1)) * a3;
+    if (act == ACT_GELU) return 0.5f * a1 * (1.f + erff(a1 * 0.70710678118654752f));
+    if (act == ACT_RELU) return fmaxf(a1, 0.f);
+    return a1;
+}
+
+// Find the expert and first row of row tile `tile` of height BM.
+// Returns false if the tile index is past the last expert's last tile.
+template <int BM>
+__device__ __forceinline__ bool find_tile(const int32_t *__restrict__ offsets, int E, int tile,
+                                          int &e, int &row0, int &nrows) {
+    int acc = 0;
+    for (int i = 0; i < E; ++i) {
+        const int lo = offsets[i], hi = offsets[i + 1];
+        const int nt = (hi - lo + BM - 1) / BM;
+        if (tile < acc + nt) {
+            e = i;
+            const int m0 = (tile - acc) * BM;
+            row0 = lo + m0;
+            nrows = min(BM, hi - lo - m0);
+            return true;
+        }
+        acc += nt;
+    }
+    return false;
+}
+
+template <int BM, int BN, int WAVES_M, int WAVES_N, bool DUAL, int ACT, bool OUT_BF16>
+__global__ __launch_bounds__(256) void gemm_bf16_kernel(
+    const uint16_t *__restrict__ A, const int32_t *__restrict__ offsets, int E,
+    const uint16_t *__restrict__ B1, const uint16_t *__restrict__ B3, void *__restrict__ C,
+    int N, int K) {
+    constexpr int BK = 64;
+    constexpr int LDK = BK + 8;
+    constexpr int NB = DUAL ? 2 : 1;
+    constexpr int BROWS = NB * BN;
+    constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
+    constexpr int TM = WM / 32, TN = WN / 32;
+    constexpr int CPR = BK / 8;                      // 16-byte chunks per row
+    constexpr int A_CH = BM * CPR / 256;             // chunks per thread
+    constexpr int B_CH = BROWS * CPR / 256;
+    static_assert(WAVES_M * WAVES_N == 4, "four waves");
+    static_assert(TM >= 1 && TN >= 1 && WM % 32 == 0 && WN % 32 == 0, "wave tile");
+    static_assert(A_CH >= 1 && (BM * CPR) % 256 == 0 && (BROWS * CPR) % 256 == 0, "loads");
+
+    __shared__ __attribute__((aligned(16))) uint16_t As[2][BM][LDK];
+    __shared__ __attribute__((aligned(16))) uint16_t Bs[2][BROWS][LDK];
+
+    int e, row0, nrows;
+    if (!find_tile<BM>(offsets, E, blockIdx.y, e, row0, nrows)) return;
+    const int n0 = blockIdx.x * BN;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int wm = wave / WAVES_N, wn = wave % WAVES_N;
+
+    // global source of each 16-byte chunk this thread stages
+    const uint16_t *a_src[A_CH];
+    int a_row[A_CH], a_kc[A_CH];
+#pragma unroll
+    for (int i = 0; i < A_CH; ++i) {
+        const int c = tid + i * 256;
+        a_row[i] = c / CPR;
+        a_kc[i] = (c % CPR) * 8;
+        const int r = min(a_row[i], nrows - 1);  // rows past the expert's last repeat it
+        a_src[i] = A + (int64_t)(row0 + r) * K + a_kc[i];
+    }
+    const uint16_t *b_src[B_CH];
+    int b_row[B_CH], b_kc[B_CH];
+    bool b_ok[B_CH];
+#pragma unroll
+    for (int i = 0; i < B_CH; ++i) {
+        const int c = tid + i * 256;
+        b_row[i] = c / CPR;
+        b_kc[i] = (c % CPR) * 8;
+        const int which = b_row[i] / BN;
+        const int n = n0 + b_row[i] % BN;
+        b_ok[i] = n < N;
+        const uint16_t *base = (DUAL && which) ? B3 : B1;
+        b_src[i] = base + ((int64_t)e * N + (b_ok[i] ? n : 0)) * K + b_kc[i];
+    }
+
+    uint4 ra[A_CH], rb[B_CH];
+    auto gload = [&](int k0) {
+#pragma unroll
+        for (int i = 0; i < A_CH; ++i)
+            ra[i] = (k0 + a_kc[i] < K) ? *(const uint4 *)(a_src[i] + k0) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+        for (int i = 0; i < B_CH; ++i)
+            rb[i] = (b_ok[i] && k0 + b_kc[i] < K) ? *(const uint4 *)(b_src[i] + k0)
+                                                  : make_uint4(0, 0, 0, 0);
+    };
+    auto lstore = [&](int buf) {
+#pragma unroll
+        for (int i = 0; i < A_CH; ++i) *(uint4 *)&As[buf][a_row[i]][a_kc[i]] = ra[i];
+#pragma unroll
+        for (int i = 0; i < B_CH; ++i) *(uint4 *)&Bs[buf][b_row[i]][b_kc[i]] = rb[i];
+    };
+
+    f32x16_t acc[NB][TM][TN];
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[b][i][j][r] = 0.f;
+
+    const int KT = (K + BK - 1) / BK;
+    gload(0);
+    lstore(0);
+    __syncthreads();
+    const int lrow = lane & 31, lk = (lane >> 5) * 8;
+    for (int kt = 0; kt < KT; ++kt) {
+        const int cur = kt & 1;
+        if (kt + 1 < KT) gload((kt + 1) * BK);
+#pragma unroll
+        for (int kk = 0; kk < BK; kk += 16) {
+            bf16x8_t af[TM], bfr[NB][TN];
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+                af[i] = *(const bf16x8_t *)&As[cur][wm * WM + i * 32 + lrow][kk + lk];
+#pragma unroll
+            for (int b = 0; b < NB; ++b)
+#pragma unroll
+                for (int j = 0; j < TN; ++j)
+                    bfr[b][j] = *(const bf16x8_t *)&Bs[cur][b * BN + wn * WN + j * 32 + lrow][kk + lk];
+#pragma unroll
+            for (int b = 0; b < NB; ++b)
+#pragma unroll
+                for (int i = 0; i < TM; ++i)
+#pragma unroll
+                    for (int j = 0; j < TN; ++j)
+                        acc[b][i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[b][j],
+                                                                              acc[b][i][j], 0, 0, 0);
+        }
+        if (kt + 1 < KT) lstore(cur ^ 1);
+        __syncthreads();
+    }
+
+    // epilogue: activation (up) or plain store (down)
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+            const int col = n0 + wn * WN + j * 32 + lrow;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int row = wm * WM + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+                if (row < nrows && col < N) {
+                    const float a1 = acc[0][i][j][r];
+                    const float a3 = DUAL ? acc[NB - 1][i][j][r] : 0.f;
+                    const float v = apply_act(ACT, a1, a3);
+                    const int64_t o = (int64_t)(row0 + row) * N + col;
+                    if (OUT_BF16)
+                        ((uint16_t *)C)[o] = f32_to_bf16(v);
+                    else
+                        ((float *)C)[o] = v;
+                }
+            }
+        }
+}
+
+// ---- fp32 path -----------------------------------------------------------
+
+__device__ __forceinline__ int expert_of_row(const int32_t *__restrict__ offsets, int E, int r) {
+    int e = 0;
+    while (e < E - 1 && r >= offsets[e + 1]) ++e;
+    return e;
+}
+
+__global__ __launch_bounds__(256) void up_f32_kernel(const float *__restrict__ A,
+                                                     const int32_t *__restrict__ offsets, int E,
+                                                     const float *__restrict__ W1,
+                                                     const float *__restrict__ W3, int act,
+                                                     float *__restrict__ H, int d, int d_ff) {
+    const int n = offsets[E];
+    for (int r = blockIdx.x; r < n; r += gridDim.x) {
+        const int e = expert_of_row(offsets, E, r);
+        const float *a = A + (int64_t)r * d;
+        for (int f = threadIdx.x; f < d_ff; f += blockDim.x) {
+            const float *w1 = W1 + ((int64_t)e * d_ff + f) * d;
+            float a1 = 0.f, a3 = 0.f;
+            for (int j = 0; j < d; ++j) a1 = fmaf(a[j], w1[j], a1);
+            if (act == ACT_SWIGLU) {
+                const float *w3 = W3 + ((int64_t)e * d_ff + f) * d;
+                for (int j = 0; j < d; ++j) a3 = fmaf(a[j], w3[j], a3);
+            }
+            H[(int64_t)r * d_ff + f] = apply_act(act, a1, a3);
+        }
+    }
+}
+
+__global__ __launch_bounds__(256) void down_f32_kernel(const float *__restrict__ H,
+                                                       const int32_t *__restrict__ offsets, int E,
+                                                       const float *__restrict__ W2,
+                                                       float *__restrict__ Y, int d, int d_ff) {
+    const int n = offsets[E];
+    for (int r = blockIdx.x; r < n; r += gridDim.x) {
+        const int e = expert_of_row(offsets, E, r);
+        const float *h = H + (int64_t)r * d_ff;
+        for (int o = threadIdx.x; o < d; o += blockDim.x) {
+            const float *w2 = W2 + ((int64_t)e * d + o) * d_ff;
+            float a = 0.f;
+            for (int f = 0; f < d_ff; ++f) a = fmaf(h[f], w2[f], a);
+            Y[(int64_t)r * d + o] = a;
+        }
+    }
+}
+
+// ---- launch configuration ------------------------------------------------
+
+// Upper bound on row tiles: sum_e ceil(kept_e / BM) <= rows / BM + E.
+inline unsigned row_tile_bound(const Shape &s, int BM) {
+    int64_t rows = s.Tk();
+    if (s.C >= 0 && (int64_t)s.E * s.C < rows) rows = (int64_t)s.E * s.C;
+    return (unsigned)((rows + BM - 1) / BM + s.E);
+}
+
+// Row-tile height from the mean rows per expert (the counts themselves
+// stay on the device).
+inline int pick_bm(const Shape &s) {
+    int64_t rows = s.Tk();
+    if (s.C >= 0 && (int64_t)s.E * s.C < rows) rows = (int64_t)s.E * s.C;
+    const int64_t mean = rows / s.E;
+    if (mean >= 96) return 128;
+    if (mean >= 24) return 64;
+    return 32;
+}
+
+template <int BM, int BN, int WM_, int WN_, bool DUAL, int ACT, bool OUT_BF16>
+hipError_t launch_gemm(const Shape &s, const void *A, const int32_t *offsets, const void *B1,
+                       const void *B3, void *C, int N, int K, hipStream_t st) {
+    dim3 grid((unsigned)((N + BN - 1) / BN), row_tile_bound(s, BM));
+    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM_, WN_, DUAL, ACT, OUT_BF16>), grid, dim3(256),
+                       0, st, (const uint16_t *)A, offsets, s.E, (const uint16_t *)B1,
+                       (const uint16_t *)B3, C, N, K);
+    return hipGetLastError();
+}
+
+template <int ACT, bool DUAL>
+hipError_t launch_up_bf16(const Shape &s, const void *A, const int32_t *offsets, const void *W1,
+                          const void *W3, void *H, hipStream_t st) {
+    switch (pick_bm(s)) {
+    case 128: return launch_gemm<128, 128, 2, 2, DUAL, ACT, true>(s, A, offsets, W1, W3, H, s.d_ff, s.d, st);
+    case 64:  return launch_gemm<64, 128, 2, 2, DUAL, ACT, true>(s, A, offsets, W1, W3, H, s.d_ff, s.d, st);
+    default:  return launch_gemm<32, 128, 1, 4, DUAL, ACT, true>(s, A, offsets, W1, W3, H, s.d_ff, s.d, st);
+    }
+}
+
+}  // namespace
+
+hipError_t launch_expert_up(const Shape &s, const void *x_perm, const int32_t *offsets,
+                            const void *W1, const void *W3, void *H, hipStream_t st) {
+    if (s.dtype == 0) {
+        int64_t blocks = s.Tk() < 16384 ? s.Tk() : 16384;
+        hipLaunchKernelGGL(up_f32_kernel, dim3((unsigned)(blocks > 0 ? blocks : 1)), dim3(256), 0,
+                           st, (const float *)x_perm, offsets, s.E, (const float *)W1,
+                           (const float *)W3, s.act, (float *)H, s.d, s.d_ff);
+        return hipGetLastError();
+    }
+    switch (s.act) {
+    case ACT_SWIGLU: return launch_up_bf16<ACT_SWIGLU, true>(s, x_perm, offsets, W1, W3, H, st);
+    case ACT_GELU:   return launch_up_bf16<ACT_GELU, false>(s, x_perm, offsets, W1, nullptr, H, st);
+    default:         return launch_up_bf16<ACT_RELU, false>(s, x_perm, offsets, W1, nullptr, H, st);
+    }
+}
+
+hipError_t launch_expert_down(const Shape &s, const void *H, const int32_t *offsets,
+                              const void *W2, float *y_perm, hipStream_t st) {
+    if (s.dtype == 0) {
+        int64_t blocks = s.Tk() < 16384 ? s.Tk() : 16384;
+        hipLaunchKernelGGL(down_f32_kernel, dim3((unsigned)(blocks > 0 ? blocks : 1)), dim3(256), 0,
+                           st, (const float *)H, offsets, s.E, (const float *)W2, y_perm, s.d,
+                           s.d_ff);
+        return hipGetLastError();
+    }
+    switch (pick_bm(s)) {
+    case 128: return launch_gemm<128, 128, 2, 2, false, ACT_NONE, false>(s, H, offsets, W2, nullptr, y_perm, s.d, s.d_ff, st);
+    case 64:  return launch_gemm<64, 128, 2, 2, false, ACT_NONE, false>(s, H, offsets, W2, nullptr, y_perm, s.d, s.d_ff, st);
+    default:  return launch_gemm<32, 128, 1, 4, false, ACT_NONE, false>(s, H, offsets, W2, nullptr, y_perm, s.d, s.d_ff, st);
+    }
+}
+
+}  // namespace moe

@@ -1,0 +1,268 @@
+// moe_api.cpp -- the C ABI declared in include/moe.h.
+//
+// Validates every argument before enqueuing anything, carves the caller's
+// workspace, and enqueues the kernel stages on the caller's stream.  Holds
+// no state between calls, allocates nothing and never synchronises.
+#include "moe.h"
+
+#include <cmath>
+#include <cstdint>
+
+#include "moe_internal.h"
+
+namespace {
+
+using moe::Shape;
+
+constexpr size_t kAlign = 256;
+
+inline size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+// Validates a description and fills the derived shape.
+int check_desc(const moe_desc *desc, Shape *s) {
+    if (!desc) return MOE_ERR_INVALID_ARG;
+    const moe_desc &d = *desc;
+    if (d.T < 1 || d.d < 1 || d.d_ff < 1 || d.E < 1 || d.k < 1 || d.k > d.E)
+        return MOE_ERR_INVALID_ARG;
+    if (d.gate != MOE_GATE_RENORM && d.gate != MOE_GATE_SWITCH) return MOE_ERR_INVALID_ARG;
+    if (d.act != MOE_ACT_RELU && d.act != MOE_ACT_GELU && d.act != MOE_ACT_SWIGLU)
+        return MOE_ERR_INVALID_ARG;
+    if (d.dtype != MOE_DTYPE_F32 && d.dtype != MOE_DTYPE_BF16) return MOE_ERR_INVALID_ARG;
+    if (!std::isfinite(d.capacity_factor) || d.capacity_factor < 0.0) return MOE_ERR_INVALID_ARG;
+    if (d.stage_events == nullptr && d.n_stage_events != 0) return MOE_ERR_INVALID_ARG;
+    if (d.n_stage_events < 0) return MOE_ERR_INVALID_ARG;
+    if (d.E > MOE_MAX_EXPERTS) return MOE_ERR_UNSUPPORTED;
+    if (d.dtype == MOE_DTYPE_BF16 && (d.d % 8 != 0 || d.d_ff % 8 != 0)) return MOE_ERR_UNSUPPORTED;
+    // permuted row indices are int32
+    if ((int64_t)d.T * d.k >= ((int64_t)1 << 31)) return MOE_ERR_UNSUPPORTED;
+    s->T = d.T;
+    s->d = d.d;
+    s->d_ff = d.d_ff;
+    s->E = d.E;
+    s->k = d.k;
+    s->gate = d.gate;
+    s->act = d.act;
+    s->dtype = d.dtype;
+    if (d.capacity_factor > 0.0)
+        s->C = (int64_t)std::ceil(d.capacity_factor * (double)d.T * (double)d.k / (double)d.E);
+    else
+        s->C = -1;
+    return MOE_OK;
+}
+
+// Workspace layout; every region starts on a 256-byte boundary.
+struct Layout {
+    size_t part_P, part_lse2;                       // router partial sums
+    size_t topk_idx, gates, routed, kept, offsets;  // moe_forward's optional outputs
+    size_t row_of_slot, token_of_row, dropped, stats;
+    size_t x_perm, H, y_perm;
+    size_t total;
+};
+
+Layout layout(const Shape &s) {
+    Layout L{};
+    const size_t elem = s.dtype == MOE_DTYPE_BF16 ? 2 : 4;
+    const size_t Tk = (size_t)s.Tk();
+    size_t rows = Tk;
+    if (s.C >= 0 && (size_t)s.E * (size_t)s.C < rows) rows = (size_t)s.E * (size_t)s.C;
+    const size_t nblk = (size_t)moe::route_blocks(s);
+    size_t o = 0;
+    auto take = [&](size_t bytes) {
+        size_t at = o;
+        o = align_up(o + bytes);
+        return at;
+    };
+    L.part_P = take(nblk * s.E * sizeof(float));
+    L.part_lse2 = take(nblk * sizeof(float));
+    L.topk_idx = take(Tk * 4);
+    L.gates = take(Tk * 4);
+    L.routed = take((size_t)s.E * 4);
+    L.kept = take((size_t)s.E * 4);
+    L.offsets = take(((size_t)s.E + 1) * 4);
+    L.row_of_slot = take(Tk * 4);
+    L.token_of_row = take(Tk * 4);
+    L.dropped = take(Tk);
+    L.stats = take((2 * (size_t)s.E + 2) * 4);
+    L.x_perm = take(rows * (size_t)s.d * elem);
+    L.H = take(rows * (size_t)s.d_ff * elem);
+    L.y_perm = take(rows * (size_t)s.d * 4);
+    L.total = o;
+    return L;
+}
+
+template <typename T>
+T *at(void *ws, size_t off) {
+    return reinterpret_cast<T *>(static_cast<char *>(ws) + off);
+}
+
+int check_ws(const Shape &s, const void *ws, size_t ws_bytes) {
+    if (!ws) return MOE_ERR_INVALID_ARG;
+    if (ws_bytes < layout(s).total) return MOE_ERR_WORKSPACE;
+    return MOE_OK;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+#define MOE_TRY(expr)                            \
+    do {                                         \
+        int rc_ = hip_status(expr);              \
+        if (rc_ != MOE_OK) return rc_;           \
+    } while (0)
+
+struct StageEvents {
+    void *const *ev;
+    int n;
+    int next = 0;
+    hipError_t record(hipStream_t st) {
+        hipError_t e = hipSuccess;
+        if (ev && next < n) e = hipEventRecord((hipEvent_t)ev[next], st);
+        ++next;
+        return e;
+    }
+};
+
+}  // namespace
+
+extern "C" {
+
+int moe_workspace_size(const moe_desc *desc, size_t *bytes) {
+    Shape s;
+    int rc = check_desc(desc, &s);
+    if (rc != MOE_OK) return rc;
+    if (!bytes) return MOE_ERR_INVALID_ARG;
+    *bytes = layout(s).total;
+    return MOE_OK;
+}
+
+int moe_capacity(const moe_desc *desc, int64_t *capacity) {
+    Shape s;
+    int rc = check_desc(desc, &s);
+    if (rc != MOE_OK) return rc;
+    if (!capacity) return MOE_ERR_INVALID_ARG;
+    *capacity = s.C;
+    return MOE_OK;
+}
+
+int moe_route(const moe_desc *desc, const void *x, const float *W_r, const float *bias,
+              const float *noise, int32_t *topk_idx, float *gates, float *stats, void *ws,
+              size_t ws_bytes, void *stream) {
+    Shape s;
+    int rc = check_desc(desc, &s);
+    if (rc != MOE_OK) return rc;
+    if (!x || !W_r || !topk_idx || !gates || !stats) return MOE_ERR_INVALID_ARG;
+    if ((rc = check_ws(s, ws, ws_bytes)) != MOE_OK) return rc;
+    const Layout L = layout(s);
+    hipStream_t st = (hipStream_t)stream;
+    MOE_TRY(moe::launch_route(s, x, W_r, bias, noise, topk_idx, gates, at<float>(ws, L.part_P),
+                              at<float>(ws, L.part_lse2), st));
+    MOE_TRY(moe::launch_route_finalize(s, topk_idx, at<float>(ws, L.part_P),
+                                       at<float>(ws, L.part_lse2), stats, st));
+    return MOE_OK;
+}
+
+int moe_dispatch(const moe_desc *desc, const void *x, const int32_t *topk_idx,
+                 int32_t *routed_counts, int32_t *kept_counts, int32_t *offsets,
+                 int32_t *row_of_slot, int32_t *token_of_row, uint8_t *dropped, void *x_perm,
+                 void *ws, size_t ws_bytes, void *stream) {
+    Shape s;
+    int rc = check_desc(desc, &s);
+    if (rc != MOE_OK) return rc;
+    if (!x || !topk_idx || !routed_counts || !kept_counts || !offsets || !row_of_slot ||
+        !token_of_row || !dropped || !x_perm)
+        return MOE_ERR_INVALID_ARG;
+    (void)ws;
+    (void)ws_bytes;  // no scratch needed
+    hipStream_t st = (hipStream_t)stream;
+    MOE_TRY(moe::launch_dispatch(s, topk_idx, routed_counts, kept_counts, offsets, row_of_slot,
+                                 token_of_row, dropped, st));
+    MOE_TRY(moe::launch_gather(s, x, token_of_row, offsets, x_perm, st));
+    return MOE_OK;
+}
+
+int moe_expert_ffn(const moe_desc *desc, const void *x_perm, const int32_t *offsets,
+                   const void *W1, const void *W3, const void *W2, float *y_perm, void *ws,
+                   size_t ws_bytes, void *stream) {
+    Shape s;
+    int rc = check_desc(desc, &s);
+    if (rc != MOE_OK) return rc;
+    if (!x_perm || !offsets || !W1 || !W2 || !y_perm) return MOE_ERR_INVALID_ARG;
+    if ((s.act == MOE_ACT_SWIGLU) != (W3 != nullptr)) return MOE_ERR_INVALID_ARG;
+    if ((rc = check_ws(s, ws, ws_bytes)) != MOE_OK) return rc;
+    const Layout L = layout(s);
+    hipStream_t st = (hipStream_t)stream;
+    void *H = at<char>(ws, L.H);
+    MOE_TRY(moe::launch_expert_up(s, x_perm, offsets, W1, W3, H, st));
+    MOE_TRY(moe::launch_expert_down(s, H, offsets, W2, y_perm, st));
+    return MOE_OK;
+}
+
+int moe_combine(const moe_desc *desc, const float *y_perm, const int32_t *row_of_slot,
+                const float *gates, void *y, void *stream) {
+    Shape s;
+    int rc = check_desc(desc, &s);
+    if (rc != MOE_OK) return rc;
+    if (!y_perm || !row_of_slot || !gates || !y) return MOE_ERR_INVALID_ARG;
+    MOE_TRY(moe::launch_combine(s, y_perm, row_of_slot, gates, y, (hipStream_t)stream));
+    return MOE_OK;
+}
+
+int moe_forward(const moe_desc *desc, const void *x, const float *W_r, const float *bias,
+                const float *noise, const void *W1, const void *W3, const void *W2, void *y,
+                int32_t *topk_idx, float *gates, int32_t *routed_counts, int32_t *kept_counts,
+                int32_t *offsets, int32_t *row_of_slot, int32_t *token_of_row,
+                uint8_t *dropped, float *stats, void *ws, size_t ws_bytes, void *stream) {
+    Shape s;
+    int rc = check_desc(desc, &s);
+    if (rc != MOE_OK) return rc;
+    if (!x || !W_r || !W1 || !W2 || !y) return MOE_ERR_INVALID_ARG;
+    if ((s.act == MOE_ACT_SWIGLU) != (W3 != nullptr)) return MOE_ERR_INVALID_ARG;
+    if ((rc = check_ws(s, ws, ws_bytes)) != MOE_OK) return rc;
+    const Layout L = layout(s);
+    if (!topk_idx) topk_idx = at<int32_t>(ws, L.topk_idx);
+    if (!gates) gates = at<float>(ws, L.gates);
+    if (!routed_counts) routed_counts = at<int32_t>(ws, L.routed);
+    if (!kept_counts) kept_counts = at<int32_t>(ws, L.kept);
+    if (!offsets) offsets = at<int32_t>(ws, L.offsets);
+    if (!row_of_slot) row_of_slot = at<int32_t>(ws, L.row_of_slot);
+    if (!token_of_row) token_of_row = at<int32_t>(ws, L.token_of_row);
+    if (!dropped) dropped = at<uint8_t>(ws, L.dropped);
+    if (!stats) stats = at<float>(ws, L.stats);
+    void *x_perm = at<char>(ws, L.x_perm);
+    void *H = at<char>(ws, L.H);
+    float *y_perm = at<float>(ws, L.y_perm);
+
+    hipStream_t st = (hipStream_t)stream;
+    StageEvents ev{desc->stage_events, desc->n_stage_events};
+    MOE_TRY(ev.record(st));
+    MOE_TRY(moe::launch_route(s, x, W_r, bias, noise, topk_idx, gates, at<float>(ws, L.part_P),
+                              at<float>(ws, L.part_lse2), st));
+    MOE_TRY(ev.record(st));
+    MOE_TRY(moe::launch_route_finalize(s, topk_idx, at<float>(ws, L.part_P),
+                                       at<float>(ws, L.part_lse2), stats, st));
+    MOE_TRY(ev.record(st));
+    MOE_TRY(moe::launch_dispatch(s, topk_idx, routed_counts, kept_counts, offsets, row_of_slot,
+                                 token_of_row, dropped, st));
+    MOE_TRY(ev.record(st));
+    MOE_TRY(moe::launch_gather(s, x, token_of_row, offsets, x_perm, st));
+    MOE_TRY(ev.record(st));
+    MOE_TRY(moe::launch_expert_up(s, x_perm, offsets, W1, W3, H, st));
+    MOE_TRY(ev.record(st));
+    MOE_TRY(moe::launch_expert_down(s, H, offsets, W2, y_perm, st));
+    MOE_TRY(ev.record(st));
+    MOE_TRY(moe::launch_combine(s, y_perm, row_of_slot, gates, y, st));
+    MOE_TRY(ev.record(st));
+    return MOE_OK;
+}
+
+const char *moe_status_string(int status) {
+    switch (status) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_INVALID_ARG: return "MOE_ERR_INVALID_ARG: invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED: valid but not supported by the kernels";
+    case MOE_ERR_HIP: return "MOE_ERR_HIP: the HIP runtime reported an error";
+    case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE: workspace smaller than moe_workspace_size()";
+    default: return "unknown moe status";
+    }
+}
+
+}  // extern "C"

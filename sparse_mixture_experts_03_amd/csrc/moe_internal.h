@@ -1,0 +1,67 @@
+// moe_internal.h -- internal declarations of libmoe (not part of the ABI).
+//
+// Each kernel family lives in its own .hip file and exports a host-side
+// launcher declared here; moe_api.cpp validates arguments, carves the
+// workspace and calls the launchers in order on the caller's stream.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+// Problem sizes plus the derived capacity (C < 0: no limit).
+struct Shape {
+    int T, d, d_ff, E, k;
+    int gate, act, dtype;
+    int64_t C;
+    int64_t Tk() const { return (int64_t)T * k; }
+};
+
+// ---- router: one block per ROUTE_TOKENS tokens -------------------------
+constexpr int ROUTE_TOKENS = 32;
+inline int route_blocks(const Shape &s) { return (s.T + ROUTE_TOKENS - 1) / ROUTE_TOKENS; }
+
+hipError_t launch_route(const Shape &s, const void *x, const float *Wr, const float *bias,
+                        const float *noise, int32_t *topk_idx, float *gates, float *part_P,
+                        float *part_lse2, hipStream_t st);
+hipError_t launch_route_finalize(const Shape &s, const int32_t *topk_idx, const float *part_P,
+                                 const float *part_lse2, float *stats, hipStream_t st);
+
+// ---- dispatch: capacity, stable permutation, gather ----------------------
+hipError_t launch_dispatch(const Shape &s, const int32_t *topk_idx, int32_t *routed,
+                           int32_t *kept, int32_t *offsets, int32_t *row_of_slot,
+                           int32_t *token_of_row, uint8_t *dropped, hipStream_t st);
+hipError_t launch_gather(const Shape &s, const void *x, const int32_t *token_of_row,
+                         const int32_t *offsets, void *x_perm, hipStream_t st);
+
+// ---- expert FFN: grouped GEMMs over ragged per-expert row blocks --------
+hipError_t launch_expert_up(const Shape &s, const void *x_perm, const int32_t *offsets,
+                            const void *W1, const void *W3, void *H, hipStream_t st);
+hipError_t launch_expert_down(const Shape &s, const void *H, const int32_t *offsets,
+                              const void *W2, float *y_perm, hipStream_t st);
+
+// ---- combine -------------------------------------------------------------
+hipError_t launch_combine(const Shape &s, const float *y_perm, const int32_t *row_of_slot,
+                          const float *gates, void *y, hipStream_t st);
+
+}  // namespace moe
+
+// ---- device helpers shared by the kernels --------------------------------
+#if defined(__HIPCC__)
+namespace moe {
+
+// fp32 -> bf16 bits, round to nearest even (NaN becomes a quiet NaN).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+    return __uint_as_float((uint32_t)b << 16);
+}
+
+}  // namespace moe
+#endif
