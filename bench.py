@@ -1,0 +1,286 @@
+"""Benchmark of the sparse-MoE layer forward on one MI355X.
+
+One step = one moe_forward call (router, top-k, dispatch with capacity,
+gather, grouped expert GEMMs, combine, statistics) over one batch of
+seeded synthetic tokens, inputs resident in HBM before the timed region.
+
+Default workload: the Mixtral-8x7B-shape layer in prefill (T=4096, d=4096,
+d_ff=14336, E=8, top-2, SwiGLU, bf16 experts, fp32 router); the same layer
+in decode (T=32, 100 steps with fresh tokens each step) is measured in the
+same run and reported in the "decode" object.  Prints one JSON line.
+
+Timing: W untimed warm-up steps, then exactly K steps between two device
+synchronisations.  Per-kernel durations come from HIP events that the
+library records on the launch stream around each stage (the descriptor's
+stage-event hook), over the same timed steps.
+
+Roofline of the dominant kernel (the expert up-projection, a grouped GEMM
+on bf16 MFMA): algorithmic FLOPs per launch = N_kept * 2 * n_up * d * d_ff
+(n_up = 2 matrices for SwiGLU) over its mean event-timed duration, against
+the 2.5 PFLOP/s dense bf16 peak.  Decode is bound by HBM: algorithmic bytes
+per launch = the touched experts' W1 and W3 (2 * d * d_ff * 2 bytes each)
+plus the permuted activations in and H out, against 8 TB/s.
+
+CPU baseline: the CPU oracle (test infrastructure; fp64 sums) timed on this
+host on a bounded sample: routing, dispatch and statistics over all T
+tokens plus the expert FFN and combine on S sampled tokens; tokens/s is
+1 / (t_route / T + t_ffn / S).
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                       [--no-cpu] [--no-decode]
+"""
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE layer tokens/s + % bf16 MFMA peak (prefill) / % HBM BW (decode), Mixtral-shape"
+PEAK_BF16_TFLOPS = 2500.0
+PEAK_HBM_GBS = 8000.0
+STAGES = ("route", "route_finalize", "dispatch", "gather", "expert_up", "expert_down", "combine")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
+GEMM_SRC = os.path.join(ROOT, "sparse_mixture_experts_03_amd", "csrc", "expert_gemm.hip")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+class HipEvents:
+    """hipEvent_t handles from the HIP runtime (the library records them)."""
+
+    def __init__(self):
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self, n):
+        arr = (ctypes.c_void_p * n)()
+        for i in range(n):
+            e = ctypes.c_void_p()
+            rc = self.hip.hipEventCreate(ctypes.byref(e))
+            if rc != 0:
+                raise RuntimeError(f"hipEventCreate failed: {rc}")
+            arr[i] = e
+        return arr
+
+    def elapsed_ms(self, a, b):
+        ms = ctypes.c_float()
+        rc = self.hip.hipEventElapsedTime(ctypes.byref(ms), a, b)
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed: {rc}")
+        return ms.value
+
+    def destroy(self, arr):
+        for e in arr:
+            self.hip.hipEventDestroy(e)
+
+
+def source_sha():
+    with open(GEMM_SRC, "rb") as fh:
+        return hashlib.sha256(fh.read()).hexdigest()[:16]
+
+
+def traffic_for(workload, kernel, launches_per_step=1):
+    """HBM bytes per launch of ``kernel`` from the committed rocprofv3 counter
+    summary, or None when absent or taken on a different kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            rec = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if rec.get("gemm_source_sha") != source_sha():
+        return None
+    ent = rec.get("kernels", {}).get(f"{workload}/{kernel}")
+    if not ent:
+        return None
+    return ent["hbm_bytes_per_launch"]
+
+
+def run_workload(w, steps, warmup, fresh_x_steps=0, seed=0):
+    """Times ``steps`` forward steps of workload w. Returns a result dict."""
+    import torch
+    from sparse_mixture_experts_03_amd import binding as B
+    from sparse_mixture_experts_03_amd import synth
+
+    t0 = time.time()
+    wt = synth.make_weights(w, seed)
+    dw = {k: B.to_device(v, w.dtype) for k, v in wt.items()}
+    del wt
+    n_x = max(1, fresh_x_steps)
+    xs, noises = [], []
+    for s in range(n_x):
+        tk = synth.make_tokens(w, seed, s)
+        xs.append(B.to_device(tk["x"], w.dtype))
+        noises.append(B.to_device(tk["noise"], w.dtype))
+    log(f"[bench] {w.name}: inputs ready in {time.time() - t0:.1f}s")
+
+    desc = B.desc_for(w)
+    ws = B.workspace(desc)
+    out = B.alloc_outputs(desc)
+    ev = HipEvents()
+    nev = len(STAGES) + 1
+    stream = torch.cuda.current_stream()
+
+    def step(i, events=None):
+        j = i % n_x
+        if events is not None:
+            desc.stage_events = ctypes.cast(events, ctypes.POINTER(ctypes.c_void_p))
+            desc.n_stage_events = nev
+        else:
+            desc.stage_events = None
+            desc.n_stage_events = 0
+        B.moe_forward(desc, xs[j], dw["Wr"], dw["bias"], noises[j], dw["W1"], dw["W3"], dw["W2"],
+                      out["y"], ws, kept_counts=out["kept_counts"], stats=out["stats"],
+                      stream=stream)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    evsets = [ev.create(nev) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for i in range(steps):
+        step(warmup + i, evsets[i])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t_start
+
+    stage_ms = np.array([[ev.elapsed_ms(es[j], es[j + 1]) for j in range(nev - 1)] for es in evsets])
+    for es in evsets:
+        ev.destroy(es)
+    kept = out["kept_counts"].cpu().numpy().astype(np.int64)
+    n_kept = int(kept.sum())
+    touched = int((kept > 0).sum())
+    return dict(elapsed=elapsed, steps=steps, stage_ms=stage_ms.mean(0), stage_ms_all=stage_ms,
+                n_kept=n_kept, touched=touched)
+
+
+def cpu_baseline(w, seed=0, target_s=12.0):
+    """The oracle on this host's cores on a bounded sample of workload w."""
+    import oracle
+    from oracle.margin import reject_near_ties  # noqa: F401  (inputs are used unfiltered here)
+    from sparse_mixture_experts_03_amd import synth
+
+    wt = synth.make_weights(w, seed)
+    tk = synth.make_tokens(w, seed, 0)
+    x = synth.widen(tk["x"])
+    W1 = synth.widen(wt["W1"])
+    W3 = None if wt["W3"] is None else synth.widen(wt["W3"])
+    W2 = synth.widen(wt["W2"])
+    t0 = time.perf_counter()
+    r = oracle.forward(x, wt["Wr"], W1, W3, W2, w.k, w.gate, w.cf, w.act, wt["bias"], tk["noise"],
+                       tokens=np.zeros(0, np.int64))
+    t_route = time.perf_counter() - t0
+    rng = np.random.default_rng(1)
+
+    def ffn_time(S):
+        sel = np.sort(rng.choice(w.T, size=S, replace=False))
+        t1 = time.perf_counter()
+        oracle.forward(x, wt["Wr"], W1, W3, W2, w.k, w.gate, w.cf, w.act, wt["bias"], tk["noise"],
+                       tokens=sel)
+        return time.perf_counter() - t1 - t_route  # the call re-routes every token
+
+    S = 4
+    t_ffn = max(ffn_time(S), 1e-6)
+    S = int(min(w.T, max(S, round(S * target_s / t_ffn))))
+    t_ffn = max(ffn_time(S), 1e-6)
+    per_token = t_route / w.T + t_ffn / S
+    return {"value": 1.0 / per_token, "unit": "tokens/s", "cores": oracle.threads(),
+            "kind": "oracle",
+            "sample": (f"{w.name}: router, gate, dispatch and statistics on all {w.T} tokens "
+                       f"({t_route:.2f}s); expert FFN and combine on {S} sampled tokens "
+                       f"({t_ffn:.2f}s); fp64 sums")}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="mixtral_prefill")
+    ap.add_argument("--decode-steps", type=int, default=100)
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the layer runs on a single MI355X with every expert "
+              "resident in its HBM (no expert parallelism, no collectives). Use --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from sparse_mixture_experts_03_amd import binding as B
+    from sparse_mixture_experts_03_amd import synth
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    B.load(build_if_missing=False)
+    w = synth.WORKLOADS[args.workload]
+    res = run_workload(w, args.steps, args.warmup)
+    ms_step = res["elapsed"] * 1e3 / res["steps"]
+    tokens_s = w.T * res["steps"] / res["elapsed"]
+    n_up = 2 if w.act == "swiglu" else 1
+    n_mat = n_up + 1
+    flops_step = 2.0 * w.T * w.E * w.d + res["n_kept"] * 2.0 * n_mat * w.d * w.d_ff
+    up = STAGES.index("expert_up")
+    up_ms = float(res["stage_ms"][up])
+    up_flops = res["n_kept"] * 2.0 * n_up * w.d * w.d_ff
+    achieved = up_flops / (up_ms * 1e-3) / 1e12
+    stages = {n: round(float(v), 4) for n, v in zip(STAGES, res["stage_ms"])}
+    log(f"[bench] {w.name}: {ms_step:.3f} ms/step, stages(ms) {stages}")
+    line = {
+        "metric": METRIC, "value": round(tokens_s, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "T": w.T, "d": w.d, "d_ff": w.d_ff, "E": w.E, "k": w.k,
+                   "gate": w.gate, "act": w.act, "capacity_factor": w.cf, "router": "fp32",
+                   "parallelism": "single_gpu"},
+        "tflops_per_step": round(flops_step / (ms_step * 1e-3) / 1e12, 2),
+        "stage_ms": stages,
+        "roofline": {"bound": "mfma", "kernel": "expert_up (grouped GEMM, SwiGLU epilogue)",
+                     "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic_for(w.name, "expert_up"),
+                     "algorithmic_per_launch": up_flops, "mean_launch_ms": round(up_ms, 4)},
+    }
+    if not args.no_decode and w.name == "mixtral_prefill":
+        wd = synth.WORKLOADS["mixtral_decode"]
+        rd = run_workload(wd, args.decode_steps, 10, fresh_x_steps=args.decode_steps)
+        ms_d = rd["elapsed"] * 1e3 / rd["steps"]
+        up_ms_d = float(rd["stage_ms"][up])
+        dn_ms_d = float(rd["stage_ms"][STAGES.index("expert_down")])
+        # algorithmic bytes: touched experts' weights + permuted activations + H
+        up_bytes = rd["touched"] * 2 * wd.d * wd.d_ff * 2 + rd["n_kept"] * (wd.d + wd.d_ff) * 2
+        step_bytes = rd["touched"] * 3 * wd.d * wd.d_ff * 2 + wd.T * wd.d * 4 + wd.E * wd.d * 4
+        gbs = up_bytes / (up_ms_d * 1e-3) / 1e9
+        line["decode"] = {
+            "workload": wd.name, "value": round(wd.T * rd["steps"] / rd["elapsed"], 1),
+            "unit": "tokens/s", "steps": rd["steps"], "ms_per_step": round(ms_d, 4),
+            "step_hbm_gbs": round(step_bytes / (ms_d * 1e-3) / 1e9, 1),
+            "step_hbm_frac": round(step_bytes / (ms_d * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+            "stage_ms": {n: round(float(v), 4) for n, v in zip(STAGES, rd["stage_ms"])},
+            "roofline": {"bound": "hbm", "kernel": "expert_up", "achieved": round(gbs, 1),
+                         "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+                         "traffic": traffic_for(wd.name, "expert_up"),
+                         "algorithmic_per_launch": up_bytes, "mean_launch_ms": round(up_ms_d, 4),
+                         "down_mean_launch_ms": round(dn_ms_d, 4)},
+        }
+        log(f"[bench] {wd.name}: {ms_d:.3f} ms/step")
+    if not args.no_cpu:
+        log("[bench] CPU oracle baseline ...")
+        line["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
