@@ -12,9 +12,9 @@
 // Expert e owns rows [offsets[e], offsets[e+1]), read on the device.
 //
 // gemm_bf16_kernel: one 256-thread block per (expert, BM-row tile, BN-col
-// tile).  blockIdx.y walks the concatenation of every expert's row tiles;
-// the block finds its expert from offsets (surplus blocks exit at once,
-// and an expert with no rows has no tiles, so its weights are never read).
+// tile), scheduled XCD-aware (see find_tile); the block finds its expert
+// from offsets (surplus blocks exit at once, and an expert with no rows has
+// no tiles, so its weights are never read).
 // The K loop stages BM x 64 of A and BN x 64 of each weight matrix through
 // LDS (double buffered, rows padded by 16 bytes against bank conflicts,
 // the next tile prefetched into registers while the current one feeds the
@@ -49,23 +49,42 @@ __device__ __forceinline__ float apply_act(int act, float a1, float a3) {
     return a1;
 }
 
-// Find the expert and first row of row tile `tile` of height BM.
-// Returns false if the tile index is past the last expert's last tile.
+// Tile schedule.  The work is the set of (expert e, column tile n, row tile
+// m) with m < ceil(rows_e / BM), ordered e-major, then n, then m.  The 1-D
+// grid is an upper bound; block b is mapped XCD-aware: blocks are
+// dispatched round-robin over the 8 XCDs (b % 8), so XCD x is given the
+// contiguous run [x * per, (x + 1) * per) of the ordered tiles (per = the
+// real tile count / 8, rounded up).  The blocks resident on one XCD at a
+// time then cover all row tiles of a few column tiles of one expert: each
+// weight panel is fetched into that XCD's L2 once and shared, and every XCD
+// gets the same amount of real work.  Surplus blocks return at once.
+constexpr int NUM_XCD = 8;
+
 template <int BM>
-__device__ __forceinline__ bool find_tile(const int32_t *__restrict__ offsets, int E, int tile,
-                                          int &e, int &row0, int &nrows) {
-    int acc = 0;
+__device__ __forceinline__ bool find_tile(const int32_t *__restrict__ offsets, int E, int ntiles_n,
+                                          int &e, int &row0, int &nrows, int &ntile) {
+    int total = 0;
+    for (int i = 0; i < E; ++i) total += (offsets[i + 1] - offsets[i] + BM - 1) / BM;
+    total *= ntiles_n;
+    const int per = (total + NUM_XCD - 1) / NUM_XCD;
+    const int b = blockIdx.x;
+    const int slot = b / NUM_XCD;
+    if (slot >= per) return false;
+    int L = (b % NUM_XCD) * per + slot;
+    if (L >= total) return false;
     for (int i = 0; i < E; ++i) {
         const int lo = offsets[i], hi = offsets[i + 1];
-        const int nt = (hi - lo + BM - 1) / BM;
-        if (tile < acc + nt) {
+        const int mt = (hi - lo + BM - 1) / BM;
+        const int cnt = mt * ntiles_n;
+        if (L < cnt) {
             e = i;
-            const int m0 = (tile - acc) * BM;
+            ntile = L / mt;
+            const int m0 = (L % mt) * BM;
             row0 = lo + m0;
             nrows = min(BM, hi - lo - m0);
             return true;
         }
-        acc += nt;
+        L -= cnt;
     }
     return false;
 }
@@ -91,9 +110,9 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(
     __shared__ __attribute__((aligned(16))) uint16_t As[2][BM][LDK];
     __shared__ __attribute__((aligned(16))) uint16_t Bs[2][BROWS][LDK];
 
-    int e, row0, nrows;
-    if (!find_tile<BM>(offsets, E, blockIdx.y, e, row0, nrows)) return;
-    const int n0 = blockIdx.x * BN;
+    int e, row0, nrows, ntile;
+    if (!find_tile<BM>(offsets, E, (N + BN - 1) / BN, e, row0, nrows, ntile)) return;
+    const int n0 = ntile * BN;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
@@ -207,6 +226,156 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(
         }
 }
 
+// ---- large row tiles: direct-to-LDS loads, 256 x 256 tiles ----------------
+//
+// gemm_bf16_big_kernel, for experts with many rows and K a multiple of 64.
+// A block computes 256 rows x 256 weight rows (SwiGLU: 128 rows of W1 and
+// the same 128 rows of W3, i.e. 128 columns of H), four waves of 128 x 128.
+// Operands go from global memory straight into LDS with
+// global_load_lds_dwordx4 (no register staging): instruction j of wave w
+// fills LDS rows 8*(8w + j) .. +8, lane l writing the 16 bytes at
+// (row 8*(8w + j) + l/8, slot l%8).  The slot holds k-chunk
+// (l % 8) ^ (row % 8) of that row -- an XOR swizzle, so that the 32 rows a
+// fragment read touches fall on distinct banks.  Two LDS stages (2 x 64 KB):
+// the loads for stage k+1 are issued right after the barrier that opens
+// stage k, and run under stage k's 64 MFMAs per wave.  Fragments for the
+// next 16-wide k step are read from LDS while the current step's MFMAs run.
+constexpr int BIG_BM = 256;
+
+template <bool DUAL, int ACT, bool OUT_BF16>
+__global__ __launch_bounds__(256) void gemm_bf16_big_kernel(
+    const uint16_t *__restrict__ A, const int32_t *__restrict__ offsets, int E,
+    const uint16_t *__restrict__ B1, const uint16_t *__restrict__ B3, void *__restrict__ C,
+    int N, int K) {
+    constexpr int BK = 64;
+    constexpr int BN = DUAL ? 128 : 256;   // output columns per block
+    constexpr int ROWB = BK * 2;           // bytes per LDS row (8 slots of 16 bytes)
+    constexpr int OPB = 256 * ROWB;        // bytes per operand per stage
+    __shared__ __attribute__((aligned(1024))) char lds[2][2][OPB];
+
+    int e, row0, nrows, ntile;
+    if (!find_tile<BIG_BM>(offsets, E, (N + BN - 1) / BN, e, row0, nrows, ntile)) return;
+    const int n0 = ntile * BN;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+
+    // element offsets (from the operand base, at k = 0) of the 16 chunks this
+    // lane loads per stage: 8 of A, 8 of the weights
+    const int sub = lane >> 3;                  // row within an 8-row group
+    const int kchunk = ((lane & 7) ^ sub) * 8;  // swizzled k-chunk, in elements
+    uint32_t a_off[8], b_off[8];
+    const uint16_t *bbase;
+    {
+        const int wrow0 = wave * 64;  // first LDS row this wave fills
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int r = wrow0 + j * 8 + sub;
+            a_off[j] = (uint32_t)(row0 + min(r, nrows - 1)) * (uint32_t)K + kchunk;
+        }
+        if (DUAL) {
+            // waves 0,1 fill W1 rows 0..127; waves 2,3 fill W3 rows 0..127
+            bbase = (wave < 2 ? B1 : B3) + (int64_t)e * N * K;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int r = (wrow0 & 127) + j * 8 + sub;
+                b_off[j] = (uint32_t)min(n0 + r, N - 1) * (uint32_t)K + kchunk;
+            }
+        } else {
+            bbase = B1 + (int64_t)e * N * K;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int r = wrow0 + j * 8 + sub;
+                b_off[j] = (uint32_t)min(n0 + r, N - 1) * (uint32_t)K + kchunk;
+            }
+        }
+    }
+    auto issue = [&](int stage, int k0) {
+        char *la = lds[stage][0] + wave * 64 * ROWB;
+        char *lb = lds[stage][1] + wave * 64 * ROWB;
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            __builtin_amdgcn_global_load_lds((const void *)(A + a_off[j] + k0),
+                                             (__attribute__((address_space(3))) void *)(la + j * 8 * ROWB),
+                                             16, 0, 0);
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            __builtin_amdgcn_global_load_lds((const void *)(bbase + b_off[j] + k0),
+                                             (__attribute__((address_space(3))) void *)(lb + j * 8 * ROWB),
+                                             16, 0, 0);
+    };
+
+    f32x16_t acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+    // fragment rows in LDS: A rows wm*128 + i*32 + lane%32; weight rows of
+    // column group j (DUAL: j < 2 -> W1 rows wn*64 + j*32, j >= 2 -> W3)
+    const int lr = lane & 31;
+    int brow[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+        brow[j] = DUAL ? ((j >> 1) * 128 + wn * 64 + (j & 1) * 32 + lr) : (wn * 128 + j * 32 + lr);
+
+    auto read_frags = [&](int stage, int kk, bf16x8_t (&a)[4], bf16x8_t (&b)[4]) {
+        const int slot = ((kk * 2 + (lane >> 5)) ^ (lane & 7)) * 16;
+        const char *la = lds[stage][0];
+        const char *lb = lds[stage][1];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            a[i] = *(const bf16x8_t *)(la + (wm * 128 + i * 32 + lr) * ROWB + slot);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) b[j] = *(const bf16x8_t *)(lb + brow[j] * ROWB + slot);
+    };
+
+    const int KT = K / BK;
+    issue(0, 0);
+    for (int kt = 0; kt < KT; ++kt) {
+        const int cur = kt & 1;
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        if (kt + 1 < KT) issue(cur ^ 1, (kt + 1) * BK);
+        bf16x8_t fa[2][4], fb[2][4];
+        read_frags(cur, 0, fa[0], fb[0]);
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            if (kk < 3) read_frags(cur, kk + 1, fa[(kk + 1) & 1], fb[(kk + 1) & 1]);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[kk & 1][i], fb[kk & 1][j],
+                                                                        acc[i][j], 0, 0, 0);
+        }
+    }
+
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int jj = 0; jj < (DUAL ? 2 : 4); ++jj) {
+            // one 32 x 32 tile at a time: keeps the activation's temporaries
+            // from piling up across tiles
+            __builtin_amdgcn_sched_barrier(0);
+            const int col = n0 + (DUAL ? wn * 64 + jj * 32 : wn * 128 + jj * 32) + lr;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int row = wm * 128 + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+                if (row < nrows && col < N) {
+                    const float v = DUAL ? apply_act(ACT, acc[i][jj][r], acc[i][jj + 2][r])
+                                         : apply_act(ACT, acc[i][jj][r], 0.f);
+                    const int64_t o = (int64_t)(row0 + row) * N + col;
+                    if (OUT_BF16)
+                        ((uint16_t *)C)[o] = f32_to_bf16(v);
+                    else
+                        ((float *)C)[o] = v;
+                }
+            }
+        }
+}
+
 // ---- fp32 path -----------------------------------------------------------
 
 __device__ __forceinline__ int expert_of_row(const int32_t *__restrict__ offsets, int E, int r) {
@@ -265,10 +434,11 @@ inline unsigned row_tile_bound(const Shape &s, int BM) {
 
 // Row-tile height from the mean rows per expert (the counts themselves
 // stay on the device).
-inline int pick_bm(const Shape &s) {
+inline int pick_bm(const Shape &s, int K) {
     int64_t rows = s.Tk();
     if (s.C >= 0 && (int64_t)s.E * s.C < rows) rows = (int64_t)s.E * s.C;
     const int64_t mean = rows / s.E;
+    if (mean >= 192 && K % 64 == 0) return BIG_BM;
     if (mean >= 96) return 128;
     if (mean >= 24) return 64;
     return 32;
@@ -277,9 +447,25 @@ inline int pick_bm(const Shape &s) {
 template <int BM, int BN, int WM_, int WN_, bool DUAL, int ACT, bool OUT_BF16>
 hipError_t launch_gemm(const Shape &s, const void *A, const int32_t *offsets, const void *B1,
                        const void *B3, void *C, int N, int K, hipStream_t st) {
-    dim3 grid((unsigned)((N + BN - 1) / BN), row_tile_bound(s, BM));
+    const unsigned nt = (unsigned)((N + BN - 1) / BN);
+    unsigned blocks = nt * row_tile_bound(s, BM);
+    blocks = (blocks + NUM_XCD - 1) / NUM_XCD * NUM_XCD;
+    dim3 grid(blocks);
     hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM_, WN_, DUAL, ACT, OUT_BF16>), grid, dim3(256),
                        0, st, (const uint16_t *)A, offsets, s.E, (const uint16_t *)B1,
+                       (const uint16_t *)B3, C, N, K);
+    return hipGetLastError();
+}
+
+template <bool DUAL, int ACT, bool OUT_BF16>
+hipError_t launch_big(const Shape &s, const void *A, const int32_t *offsets, const void *B1,
+                      const void *B3, void *C, int N, int K, hipStream_t st) {
+    constexpr int BN = DUAL ? 128 : 256;
+    const unsigned nt = (unsigned)((N + BN - 1) / BN);
+    unsigned blocks = nt * row_tile_bound(s, BIG_BM);
+    blocks = (blocks + NUM_XCD - 1) / NUM_XCD * NUM_XCD;
+    hipLaunchKernelGGL((gemm_bf16_big_kernel<DUAL, ACT, OUT_BF16>), dim3(blocks), dim3(256), 0, st,
+                       (const uint16_t *)A, offsets, s.E, (const uint16_t *)B1,
                        (const uint16_t *)B3, C, N, K);
     return hipGetLastError();
 }
@@ -287,7 +473,8 @@ hipError_t launch_gemm(const Shape &s, const void *A, const int32_t *offsets, co
 template <int ACT, bool DUAL>
 hipError_t launch_up_bf16(const Shape &s, const void *A, const int32_t *offsets, const void *W1,
                           const void *W3, void *H, hipStream_t st) {
-    switch (pick_bm(s)) {
+    switch (pick_bm(s, s.d)) {
+    case BIG_BM: return launch_big<DUAL, ACT, true>(s, A, offsets, W1, W3, H, s.d_ff, s.d, st);
     case 128: return launch_gemm<128, 128, 2, 2, DUAL, ACT, true>(s, A, offsets, W1, W3, H, s.d_ff, s.d, st);
     case 64:  return launch_gemm<64, 128, 2, 2, DUAL, ACT, true>(s, A, offsets, W1, W3, H, s.d_ff, s.d, st);
     default:  return launch_gemm<32, 128, 1, 4, DUAL, ACT, true>(s, A, offsets, W1, W3, H, s.d_ff, s.d, st);
@@ -321,7 +508,8 @@ hipError_t launch_expert_down(const Shape &s, const void *H, const int32_t *offs
                            s.d_ff);
         return hipGetLastError();
     }
-    switch (pick_bm(s)) {
+    switch (pick_bm(s, s.d_ff)) {
+    case BIG_BM: return launch_big<false, ACT_NONE, false>(s, H, offsets, W2, nullptr, y_perm, s.d, s.d_ff, st);
     case 128: return launch_gemm<128, 128, 2, 2, false, ACT_NONE, false>(s, H, offsets, W2, nullptr, y_perm, s.d, s.d_ff, st);
     case 64:  return launch_gemm<64, 128, 2, 2, false, ACT_NONE, false>(s, H, offsets, W2, nullptr, y_perm, s.d, s.d_ff, st);
     default:  return launch_gemm<32, 128, 1, 4, false, ACT_NONE, false>(s, H, offsets, W2, nullptr, y_perm, s.d, s.d_ff, st);

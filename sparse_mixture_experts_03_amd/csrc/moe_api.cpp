@@ -53,6 +53,7 @@ int check_desc(const moe_desc *desc, Shape *s) {
 // Workspace layout; every region starts on a 256-byte boundary.
 struct Layout {
     size_t part_P, part_lse2;                       // router partial sums
+    size_t wsplit, part_logits;                     // bf16 router: split W_r, logit slices
     size_t topk_idx, gates, routed, kept, offsets;  // moe_forward's optional outputs
     size_t row_of_slot, token_of_row, dropped, stats;
     size_t x_perm, H, y_perm;
@@ -74,6 +75,10 @@ Layout layout(const Shape &s) {
     };
     L.part_P = take(nblk * s.E * sizeof(float));
     L.part_lse2 = take(nblk * sizeof(float));
+    if (s.dtype == MOE_DTYPE_BF16) {
+        L.wsplit = take(3 * (size_t)moe::route_epad(s) * (size_t)s.d * 2);
+        L.part_logits = take((size_t)moe::route_nsplit(s) * (size_t)s.T * (size_t)s.E * 4);
+    }
     L.topk_idx = take(Tk * 4);
     L.gates = take(Tk * 4);
     L.routed = take((size_t)s.E * 4);
@@ -154,7 +159,8 @@ int moe_route(const moe_desc *desc, const void *x, const float *W_r, const float
     const Layout L = layout(s);
     hipStream_t st = (hipStream_t)stream;
     MOE_TRY(moe::launch_route(s, x, W_r, bias, noise, topk_idx, gates, at<float>(ws, L.part_P),
-                              at<float>(ws, L.part_lse2), st));
+                              at<float>(ws, L.part_lse2), at<uint16_t>(ws, L.wsplit),
+                              at<float>(ws, L.part_logits), st));
     MOE_TRY(moe::launch_route_finalize(s, topk_idx, at<float>(ws, L.part_P),
                                        at<float>(ws, L.part_lse2), stats, st));
     return MOE_OK;
@@ -235,7 +241,8 @@ int moe_forward(const moe_desc *desc, const void *x, const float *W_r, const flo
     StageEvents ev{desc->stage_events, desc->n_stage_events};
     MOE_TRY(ev.record(st));
     MOE_TRY(moe::launch_route(s, x, W_r, bias, noise, topk_idx, gates, at<float>(ws, L.part_P),
-                              at<float>(ws, L.part_lse2), st));
+                              at<float>(ws, L.part_lse2), at<uint16_t>(ws, L.wsplit),
+                              at<float>(ws, L.part_logits), st));
     MOE_TRY(ev.record(st));
     MOE_TRY(moe::launch_route_finalize(s, topk_idx, at<float>(ws, L.part_P),
                                        at<float>(ws, L.part_lse2), stats, st));

@@ -22,9 +22,15 @@ struct Shape {
 constexpr int ROUTE_TOKENS = 32;
 inline int route_blocks(const Shape &s) { return (s.T + ROUTE_TOKENS - 1) / ROUTE_TOKENS; }
 
+// bf16 path: router matrix split into 3 bf16 terms [3][E_pad][d], and the
+// logits computed in route_nsplit() slices of d, each route_slice() wide.
+int route_epad(const Shape &s);
+int route_slice(const Shape &s);
+int route_nsplit(const Shape &s);
+
 hipError_t launch_route(const Shape &s, const void *x, const float *Wr, const float *bias,
                         const float *noise, int32_t *topk_idx, float *gates, float *part_P,
-                        float *part_lse2, hipStream_t st);
+                        float *part_lse2, uint16_t *wsplit, float *part_logits, hipStream_t st);
 hipError_t launch_route_finalize(const Shape &s, const int32_t *topk_idx, const float *part_P,
                                  const float *part_lse2, float *stats, hipStream_t st);
 

@@ -10,27 +10,44 @@
 //     P_i (mean router probability), and the z statistic mean (log sum exp h)^2;
 //   Implementation: the router runs in float32.
 //
-// Kernel route_kernel: one block of 256 threads per ROUTE_TOKENS tokens.
-//   1. Logits: a [ROUTE_TOKENS x E] fp32 tile accumulated over d in chunks
-//      staged through LDS; each thread owns 4 tokens x 4 experts and sums
-//      its dot products sequentially in j (fp32 FMA).
-//   2. Per token, one wave holds the E <= 128 logits in registers (lane l:
-//      experts l and l+64), reduces max and sum of exponentials with
-//      shuffles, and picks the top k by k arg-max reductions over 64-bit
-//      keys (orderable logit bits, then the complement of the index so that
-//      a tie goes to the lower index).
-//   3. Per-block partial sums of p (per expert) and of lse^2 go to the
-//      workspace in a fixed order; route_finalize_kernel reduces them in
-//      double, in block order, and counts top choices.
+// bf16 activations (the MFMA path), three kernels:
+//   router_split_kernel  splits the fp32 router matrix exactly into three
+//     bf16 terms, W = hi + mid + lo: hi = bf16(W), mid = bf16(W - hi),
+//     lo = bf16(W - hi - mid); each difference is exact in fp32 and the last
+//     one has at most 8 significant bits, so the three terms sum to W.  A bf16
+//     token times a bf16 term is exact in fp32, hence
+//     x.W = x.hi + x.mid + x.lo with fp32 accumulation: an fp32 router whose
+//     only rounding is in the accumulation, computed on bf16 MFMA.
+//   router_logits_kernel  v_mfma_f32_16x16x32_bf16 over a 64-token x E tile,
+//     split over d into slices (so that a 32-token decode batch still
+//     spreads over many CUs); each slice writes fp32 partial logits.
+//   route_epilogue_kernel  per token: partial logits summed in slice order,
+//     plus bias and noise, then the shared per-token epilogue below.
+// fp32 activations: route_f32_kernel, a plain fp32 FMA tile over d staged
+//   through LDS, then the same per-token epilogue.
+//
+// Per-token epilogue (one wave per token, E <= 128 logits in registers:
+// lane l holds experts l and l+64): max and sum of exponentials by shuffle
+// reductions, top-k by k arg-max reductions over 64-bit keys (orderable
+// logit bits, then the complement of the index, so a tie goes to the lower
+// index), gates, and per-block partial sums of p (per expert) and of lse^2
+// in a fixed order.  route_finalize_kernel reduces the partials in double,
+// in block order, and counts top choices.
 #include "moe_internal.h"
 
 namespace moe {
 
 namespace {
 
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
 constexpr int RT_THREADS = 256;
-constexpr int RT_DC = 32;                 // d chunk staged per iteration
-constexpr int RT_EMAX = 128;              // logits tile width (MOE_MAX_EXPERTS)
+constexpr int RT_DC = 32;      // d chunk of the fp32 path
+constexpr int RT_EMAX = 128;   // MOE_MAX_EXPERTS
+constexpr int RL_BM = 64;      // tokens per logits block
+constexpr int RL_KC = 64;      // d chunk per iteration
+constexpr int RL_LDK = RL_KC + 8;
 
 // Monotone map of fp32 bits to uint32: a < b  <=>  ord(a) < ord(b) (no NaN);
 // -0 and +0 map to the same key, as they compare equal.
@@ -57,80 +74,15 @@ __device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long v)
     return v;
 }
 
-template <bool BF16>
-__device__ __forceinline__ float load_x(const void *x, int64_t i) {
-    if (BF16) return bf16_to_f32(((const uint16_t *)x)[i]);
-    return ((const float *)x)[i];
-}
-
-template <bool BF16>
-__global__ __launch_bounds__(RT_THREADS) void route_kernel(
-    const void *__restrict__ x, const float *__restrict__ Wr, const float *__restrict__ bias,
-    const float *__restrict__ noise, int T, int d, int E, int k, int gate_switch,
-    int32_t *__restrict__ topk_idx, float *__restrict__ gates, float *__restrict__ part_P,
-    float *__restrict__ part_lse2) {
-    __shared__ float xs[ROUTE_TOKENS][RT_DC + 1];
-    __shared__ float wsh[RT_EMAX][RT_DC + 1];
-    __shared__ float hl[ROUTE_TOKENS][RT_EMAX + 1];
+// The per-token epilogue over a block's logits tile hl[ROUTE_TOKENS][.]
+// (already synchronised).  Every thread of the block must call it.
+__device__ void softmax_topk_block(const float (*hl)[RT_EMAX + 1], int t0, int T, int E, int k,
+                                   int gate_switch, int32_t *__restrict__ topk_idx,
+                                   float *__restrict__ gates, float *__restrict__ part_P,
+                                   float *__restrict__ part_lse2) {
     __shared__ float pw[4][RT_EMAX];
     __shared__ float lw[4];
-
     const int tid = threadIdx.x;
-    const int t0 = blockIdx.x * ROUTE_TOKENS;
-    const int tg = tid >> 5;  // 8 token groups of 4 tokens
-    const int eg = tid & 31;  // 32 expert groups; experts eg + 32*j
-
-    float acc[4][4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = 0.f;
-
-    for (int c0 = 0; c0 < d; c0 += RT_DC) {
-        // stage x[t0 .. t0+32)[c0 .. c0+32) and W_r[0..E)[c0 .. c0+32)
-        for (int i = tid; i < ROUTE_TOKENS * RT_DC; i += RT_THREADS) {
-            int r = i / RT_DC, c = i % RT_DC;
-            int t = t0 + r;
-            xs[r][c] = (t < T && c0 + c < d) ? load_x<BF16>(x, (int64_t)t * d + c0 + c) : 0.f;
-        }
-        for (int i = tid; i < RT_EMAX * RT_DC; i += RT_THREADS) {
-            int r = i / RT_DC, c = i % RT_DC;
-            wsh[r][c] = (r < E && c0 + c < d) ? Wr[(int64_t)r * d + c0 + c] : 0.f;
-        }
-        __syncthreads();
-#pragma unroll 4
-        for (int c = 0; c < RT_DC; ++c) {
-            float xv[4], wv[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) xv[i] = xs[tg * 4 + i][c];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) wv[j] = wsh[eg + 32 * j][c];
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(xv[i], wv[j], acc[i][j]);
-        }
-        __syncthreads();
-    }
-
-    // logits + bias + noise into LDS
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        int r = tg * 4 + i, t = t0 + r;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            int e = eg + 32 * j;
-            float h = acc[i][j];
-            if (e < E && t < T) {
-                if (bias) h += bias[e];
-                if (noise) h += noise[(int64_t)t * E + e];
-            }
-            hl[r][e] = h;
-        }
-    }
-    __syncthreads();
-
-    // per-token softmax / top-k / gates: wave w takes tokens w, w+4, ...
     const int lane = tid & 63, w = tid >> 6;
     const int e0 = lane, e1 = lane + 64;
     const bool v0 = e0 < E, v1 = e1 < E;
@@ -191,6 +143,220 @@ __global__ __launch_bounds__(RT_THREADS) void route_kernel(
     if (tid == 0) part_lse2[blockIdx.x] = ((lw[0] + lw[1]) + lw[2]) + lw[3];
 }
 
+// ---- fp32 activations ----------------------------------------------------
+
+__global__ __launch_bounds__(RT_THREADS) void route_f32_kernel(
+    const float *__restrict__ x, const float *__restrict__ Wr, const float *__restrict__ bias,
+    const float *__restrict__ noise, int T, int d, int E, int k, int gate_switch,
+    int32_t *__restrict__ topk_idx, float *__restrict__ gates, float *__restrict__ part_P,
+    float *__restrict__ part_lse2) {
+    __shared__ float xs[ROUTE_TOKENS][RT_DC + 1];
+    __shared__ float wsh[RT_EMAX][RT_DC + 1];
+    __shared__ float hl[ROUTE_TOKENS][RT_EMAX + 1];
+
+    const int tid = threadIdx.x;
+    const int t0 = blockIdx.x * ROUTE_TOKENS;
+    const int tg = tid >> 5;  // 8 token groups of 4 tokens
+    const int eg = tid & 31;  // 32 expert groups; experts eg + 32*j
+
+    float acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = 0.f;
+
+    for (int c0 = 0; c0 < d; c0 += RT_DC) {
+        for (int i = tid; i < ROUTE_TOKENS * RT_DC; i += RT_THREADS) {
+            int r = i / RT_DC, c = i % RT_DC;
+            int t = t0 + r;
+            xs[r][c] = (t < T && c0 + c < d) ? x[(int64_t)t * d + c0 + c] : 0.f;
+        }
+        for (int i = tid; i < RT_EMAX * RT_DC; i += RT_THREADS) {
+            int r = i / RT_DC, c = i % RT_DC;
+            wsh[r][c] = (r < E && c0 + c < d) ? Wr[(int64_t)r * d + c0 + c] : 0.f;
+        }
+        __syncthreads();
+#pragma unroll 4
+        for (int c = 0; c < RT_DC; ++c) {
+            float xv[4], wv[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) xv[i] = xs[tg * 4 + i][c];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) wv[j] = wsh[eg + 32 * j][c];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(xv[i], wv[j], acc[i][j]);
+        }
+        __syncthreads();
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        int r = tg * 4 + i, t = t0 + r;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            int e = eg + 32 * j;
+            float h = acc[i][j];
+            if (e < E && t < T) {
+                if (bias) h += bias[e];
+                if (noise) h += noise[(int64_t)t * E + e];
+            }
+            hl[r][e] = h;
+        }
+    }
+    __syncthreads();
+    softmax_topk_block(hl, t0, T, E, k, gate_switch, topk_idx, gates, part_P, part_lse2);
+}
+
+// ---- bf16 activations: exact three-term split + MFMA ---------------------
+
+// wsplit [3][E_pad][d] bf16: hi, mid, lo; rows E..E_pad-1 are zero.
+__global__ __launch_bounds__(256) void router_split_kernel(const float *__restrict__ Wr, int E,
+                                                           int E_pad, int d,
+                                                           uint16_t *__restrict__ wsplit) {
+    const int64_t n = (int64_t)E_pad * d;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+         i += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t row = i / d;
+        const float w = row < E ? Wr[i] : 0.f;
+        const uint16_t hi = f32_to_bf16(w);
+        const float r1 = w - bf16_to_f32(hi);
+        const uint16_t mid = f32_to_bf16(r1);
+        const float r2 = r1 - bf16_to_f32(mid);
+        wsplit[i] = hi;
+        wsplit[n + i] = mid;
+        wsplit[2 * n + i] = f32_to_bf16(r2);
+    }
+}
+
+// Logit partials of tokens [64*bx, +64) over the d slice of blockIdx.y.
+// MFMA 16x16x32 layout (lane l): A row l % 16, k 8*(l/16)..+8; B column
+// l % 16, same k; accumulator r holds row 4*(l/16) + r, column l % 16.
+template <int E_PAD, int WAVES_M, int WAVES_N>
+__global__ __launch_bounds__(256) void router_logits_kernel(const uint16_t *__restrict__ x,
+                                                            const uint16_t *__restrict__ wsplit,
+                                                            int T, int d, int E, int slice,
+                                                            float *__restrict__ part) {
+    constexpr int TMW = RL_BM / 16 / WAVES_M;   // 16-token tiles per wave
+    constexpr int TNW = E_PAD / 16 / WAVES_N;   // 16-expert tiles per wave
+    constexpr int WROWS = 3 * E_PAD;
+    constexpr int CPR = RL_KC / 8;                       // 16-byte chunks per row
+    constexpr int XCH = (RL_BM * CPR + 255) / 256;       // x chunks per thread
+    constexpr int WCH = (WROWS * CPR + 255) / 256;       // W chunks per thread
+    static_assert(WAVES_M * WAVES_N == 4 && TMW >= 1 && TNW >= 1, "wave split");
+    __shared__ __attribute__((aligned(16))) uint16_t xs[2][RL_BM][RL_LDK];
+    __shared__ __attribute__((aligned(16))) uint16_t wsh[2][WROWS][RL_LDK];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave / WAVES_N, wn = wave % WAVES_N;
+    const int t0 = blockIdx.x * RL_BM;
+    const int kbeg = blockIdx.y * slice;
+    const int kend = min(d, kbeg + slice);
+    const int64_t nw = (int64_t)E_PAD * d;
+
+    uint4 rx[XCH], rw[WCH];
+    auto gload = [&](int k0) {
+#pragma unroll
+        for (int i = 0; i < XCH; ++i) {
+            const int c = tid + i * 256;
+            const int r = c / CPR, kc = (c % CPR) * 8;
+            const bool ok = c < RL_BM * CPR && t0 + r < T && k0 + kc < kend;
+            rx[i] = ok ? *(const uint4 *)(x + (int64_t)(t0 + r) * d + k0 + kc) : make_uint4(0, 0, 0, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < WCH; ++i) {
+            const int c = tid + i * 256;
+            const int r = c / CPR, kc = (c % CPR) * 8;
+            const int q = r / E_PAD, e = r % E_PAD;
+            const bool ok = c < WROWS * CPR && k0 + kc < kend;
+            rw[i] = ok ? *(const uint4 *)(wsplit + q * nw + (int64_t)e * d + k0 + kc)
+                       : make_uint4(0, 0, 0, 0);
+        }
+    };
+    auto lstore = [&](int buf) {
+#pragma unroll
+        for (int i = 0; i < XCH; ++i) {
+            const int c = tid + i * 256;
+            if (c < RL_BM * CPR) *(uint4 *)&xs[buf][c / CPR][(c % CPR) * 8] = rx[i];
+        }
+#pragma unroll
+        for (int i = 0; i < WCH; ++i) {
+            const int c = tid + i * 256;
+            if (c < WROWS * CPR) *(uint4 *)&wsh[buf][c / CPR][(c % CPR) * 8] = rw[i];
+        }
+    };
+
+    f32x4_t acc[TMW][TNW];
+#pragma unroll
+    for (int i = 0; i < TMW; ++i)
+#pragma unroll
+        for (int j = 0; j < TNW; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    const int nchunks = (kend - kbeg + RL_KC - 1) / RL_KC;
+    const int lr = lane & 15, lk = (lane >> 4) * 8;
+    if (nchunks > 0) {
+        gload(kbeg);
+        lstore(0);
+    }
+    __syncthreads();
+    for (int c = 0; c < nchunks; ++c) {
+        const int cur = c & 1;
+        if (c + 1 < nchunks) gload(kbeg + (c + 1) * RL_KC);
+#pragma unroll
+        for (int kk = 0; kk < RL_KC; kk += 32) {
+            bf16x8_t a[TMW];
+#pragma unroll
+            for (int i = 0; i < TMW; ++i)
+                a[i] = *(const bf16x8_t *)&xs[cur][(wm * TMW + i) * 16 + lr][kk + lk];
+#pragma unroll
+            for (int q = 0; q < 3; ++q)
+#pragma unroll
+                for (int j = 0; j < TNW; ++j) {
+                    const bf16x8_t b =
+                        *(const bf16x8_t *)&wsh[cur][q * E_PAD + (wn * TNW + j) * 16 + lr][kk + lk];
+#pragma unroll
+                    for (int i = 0; i < TMW; ++i)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b, acc[i][j], 0, 0, 0);
+                }
+        }
+        if (c + 1 < nchunks) lstore(cur ^ 1);
+        __syncthreads();
+    }
+    float *pp = part + (int64_t)blockIdx.y * T * E;
+#pragma unroll
+    for (int i = 0; i < TMW; ++i)
+#pragma unroll
+        for (int j = 0; j < TNW; ++j) {
+            const int e = (wn * TNW + j) * 16 + lr;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int t = t0 + (wm * TMW + i) * 16 + (lane >> 4) * 4 + r;
+                if (t < T && e < E) pp[(int64_t)t * E + e] = acc[i][j][r];
+            }
+        }
+}
+
+__global__ __launch_bounds__(RT_THREADS) void route_epilogue_kernel(
+    const float *__restrict__ part, int nsplit, const float *__restrict__ bias,
+    const float *__restrict__ noise, int T, int E, int k, int gate_switch,
+    int32_t *__restrict__ topk_idx, float *__restrict__ gates, float *__restrict__ part_P,
+    float *__restrict__ part_lse2) {
+    __shared__ float hl[ROUTE_TOKENS][RT_EMAX + 1];
+    const int t0 = blockIdx.x * ROUTE_TOKENS;
+    for (int i = threadIdx.x; i < ROUTE_TOKENS * E; i += RT_THREADS) {
+        const int r = i / E, e = i % E, t = t0 + r;
+        float h = 0.f;
+        if (t < T) {
+            for (int s = 0; s < nsplit; ++s) h += part[((int64_t)s * T + t) * E + e];
+            if (bias) h += bias[e];
+            if (noise) h += noise[(int64_t)t * E + e];
+        }
+        hl[r][e] = h;
+    }
+    __syncthreads();
+    softmax_topk_block(hl, t0, T, E, k, gate_switch, topk_idx, gates, part_P, part_lse2);
+}
+
 __global__ __launch_bounds__(256) void route_finalize_kernel(
     const int32_t *__restrict__ topk_idx, const float *__restrict__ part_P,
     const float *__restrict__ part_lse2, int T, int E, int k, int nblk,
@@ -226,18 +392,66 @@ __global__ __launch_bounds__(256) void route_finalize_kernel(
     }
 }
 
+template <int E_PAD, int WM, int WN>
+void launch_logits(const Shape &s, const void *x, const uint16_t *wsplit, float *part,
+                   hipStream_t st) {
+    dim3 grid((unsigned)((s.T + RL_BM - 1) / RL_BM), (unsigned)route_nsplit(s));
+    hipLaunchKernelGGL((router_logits_kernel<E_PAD, WM, WN>), grid, dim3(256), 0, st,
+                       (const uint16_t *)x, wsplit, s.T, s.d, s.E, route_slice(s), part);
+}
+
 }  // namespace
+
+int route_epad(const Shape &s) {
+    if (s.E <= 16) return 16;
+    if (s.E <= 32) return 32;
+    if (s.E <= 64) return 64;
+    return 128;
+}
+
+// d slice per split: whole 64-wide chunks, enough slices to give the GPU
+// about 512 blocks, each slice at least two chunks.
+int route_slice(const Shape &s) {
+    const int tiles = (s.T + RL_BM - 1) / RL_BM;
+    const int chunks = (s.d + RL_KC - 1) / RL_KC;
+    const int want = (512 + tiles - 1) / tiles;
+    const int maxsplit = chunks / 2 > 1 ? chunks / 2 : 1;
+    int nsplit = want < maxsplit ? want : maxsplit;
+    if (nsplit < 1) nsplit = 1;
+    return (chunks + nsplit - 1) / nsplit * RL_KC;
+}
+
+int route_nsplit(const Shape &s) {
+    const int slice = route_slice(s);
+    return (s.d + slice - 1) / slice;
+}
 
 hipError_t launch_route(const Shape &s, const void *x, const float *Wr, const float *bias,
                         const float *noise, int32_t *topk_idx, float *gates, float *part_P,
-                        float *part_lse2, hipStream_t st) {
-    dim3 grid(route_blocks(s)), block(RT_THREADS);
-    if (s.dtype == 1)
-        hipLaunchKernelGGL(route_kernel<true>, grid, block, 0, st, x, Wr, bias, noise, s.T, s.d,
-                           s.E, s.k, s.gate, topk_idx, gates, part_P, part_lse2);
-    else
-        hipLaunchKernelGGL(route_kernel<false>, grid, block, 0, st, x, Wr, bias, noise, s.T, s.d,
-                           s.E, s.k, s.gate, topk_idx, gates, part_P, part_lse2);
+                        float *part_lse2, uint16_t *wsplit, float *part_logits, hipStream_t st) {
+    const dim3 grid(route_blocks(s)), block(RT_THREADS);
+    if (s.dtype == 0) {
+        hipLaunchKernelGGL(route_f32_kernel, grid, block, 0, st, (const float *)x, Wr, bias, noise,
+                           s.T, s.d, s.E, s.k, s.gate, topk_idx, gates, part_P, part_lse2);
+        return hipGetLastError();
+    }
+    const int epad = route_epad(s);
+    {
+        const int64_t n = (int64_t)epad * s.d;
+        int64_t blocks = (n + 255) / 256;
+        if (blocks > 2048) blocks = 2048;
+        hipLaunchKernelGGL(router_split_kernel, dim3((unsigned)blocks), dim3(256), 0, st, Wr, s.E,
+                           epad, s.d, wsplit);
+    }
+    switch (epad) {
+    case 16: launch_logits<16, 4, 1>(s, x, wsplit, part_logits, st); break;
+    case 32: launch_logits<32, 4, 1>(s, x, wsplit, part_logits, st); break;
+    case 64: launch_logits<64, 2, 2>(s, x, wsplit, part_logits, st); break;
+    default: launch_logits<128, 1, 4>(s, x, wsplit, part_logits, st); break;
+    }
+    hipLaunchKernelGGL(route_epilogue_kernel, grid, block, 0, st, (const float *)part_logits,
+                       route_nsplit(s), bias, noise, s.T, s.E, s.k, s.gate, topk_idx, gates,
+                       part_P, part_lse2);
     return hipGetLastError();
 }
 

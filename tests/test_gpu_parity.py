@@ -33,6 +33,13 @@ SMALL = {
     # bf16 ReLU, top-3 of 6, cf=0.8: 64-row tiles, drops
     "relu_bf16": W["tiny"].with_(name="relu_bf16", T=200, d=64, d_ff=136, E=6, k=3, cf=0.8,
                                  dtype="bf16"),
+    # 256-row tiles with direct-to-LDS loads: ~600 rows per expert, K % 64 == 0,
+    # a partial last column tile (448 = 3*128 + 64), ragged last row tile
+    "big_swiglu": W["mixtral_prefill"].with_(name="big_swiglu", T=1200, d=512, d_ff=448, E=4),
+    # the same kernel without the dual accumulator: GELU, k = 1, capacity 1.05,
+    # partial column tile in the down projection (320 = 256 + 64)
+    "big_gelu": W["switch"].with_(name="big_gelu", T=1000, d=320, d_ff=384, E=4, cf=1.05,
+                                  noise_std=0.25),
     # Switch gate with k = 2, 64-row SwiGLU tiles
     "switch_k2": W["mixtral_prefill"].with_(name="switch_k2", T=500, d=128, d_ff=256, E=16, k=2,
                                             gate="switch", x_rmsnorm=False),
