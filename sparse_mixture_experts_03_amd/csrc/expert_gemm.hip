@@ -289,19 +289,18 @@ __global__ __launch_bounds__(256) void gemm_bf16_big_kernel(
             }
         }
     }
-    auto issue = [&](int stage, int k0) {
-        char *la = lds[stage][0] + wave * 64 * ROWB;
-        char *lb = lds[stage][1] + wave * 64 * ROWB;
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-            __builtin_amdgcn_global_load_lds((const void *)(A + a_off[j] + k0),
-                                             (__attribute__((address_space(3))) void *)(la + j * 8 * ROWB),
-                                             16, 0, 0);
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-            __builtin_amdgcn_global_load_lds((const void *)(bbase + b_off[j] + k0),
-                                             (__attribute__((address_space(3))) void *)(lb + j * 8 * ROWB),
-                                             16, 0, 0);
+    // global -> LDS load q (0..15) of a stage: q < 8 from A, else from the weights
+    auto issue_one = [&](int stage, int k0, int q) {
+        if (q < 8)
+            __builtin_amdgcn_global_load_lds(
+                (const void *)(A + a_off[q] + k0),
+                (__attribute__((address_space(3))) void *)(lds[stage][0] + wave * 64 * ROWB + q * 8 * ROWB),
+                16, 0, 0);
+        else
+            __builtin_amdgcn_global_load_lds(
+                (const void *)(bbase + b_off[q - 8] + k0),
+                (__attribute__((address_space(3))) void *)(lds[stage][1] + wave * 64 * ROWB + (q - 8) * 8 * ROWB),
+                16, 0, 0);
     };
 
     f32x16_t acc[4][4];
@@ -320,35 +319,49 @@ __global__ __launch_bounds__(256) void gemm_bf16_big_kernel(
     for (int j = 0; j < 4; ++j)
         brow[j] = DUAL ? ((j >> 1) * 128 + wn * 64 + (j & 1) * 32 + lr) : (wn * 128 + j * 32 + lr);
 
-    auto read_frags = [&](int stage, int kk, bf16x8_t (&a)[4], bf16x8_t (&b)[4]) {
+    // fragment read f (0..7) of k step kk, in the order the MFMAs consume
+    // them: A0, B0, B1, B2, B3, A1, A2, A3
+    auto read_one = [&](int stage, int kk, int f, bf16x8_t (&a)[4], bf16x8_t (&b)[4]) {
         const int slot = ((kk * 2 + (lane >> 5)) ^ (lane & 7)) * 16;
-        const char *la = lds[stage][0];
-        const char *lb = lds[stage][1];
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            a[i] = *(const bf16x8_t *)(la + (wm * 128 + i * 32 + lr) * ROWB + slot);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) b[j] = *(const bf16x8_t *)(lb + brow[j] * ROWB + slot);
+        if (f == 0 || f >= 5) {
+            const int i = f == 0 ? 0 : f - 4;
+            a[i] = *(const bf16x8_t *)(lds[stage][0] + (wm * 128 + i * 32 + lr) * ROWB + slot);
+        } else {
+            b[f - 1] = *(const bf16x8_t *)(lds[stage][1] + brow[f - 1] * ROWB + slot);
+        }
     };
 
+    // The stage loop is written as explicit bundles in issue order, each
+    // closed by a scheduling barrier: 64 MFMAs (i-major, so consecutive
+    // MFMAs never share an accumulator); with each of the first 8 MFMAs of
+    // steps 0..2 one fragment read for the next step (8 MFMAs of slack
+    // before the step boundary waits for them); with each of the first 16
+    // MFMAs one global->LDS load of the next stage.  The last stage's
+    // prefetch re-loads that stage into the idle buffer (nobody reads it),
+    // which keeps the loop free of branches.
     const int KT = K / BK;
-    issue(0, 0);
+#pragma unroll
+    for (int q = 0; q < 16; ++q) issue_one(0, 0, q);
     for (int kt = 0; kt < KT; ++kt) {
         const int cur = kt & 1;
+        const int knext = min(kt + 1, KT - 1) * BK;
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
-        if (kt + 1 < KT) issue(cur ^ 1, (kt + 1) * BK);
         bf16x8_t fa[2][4], fb[2][4];
-        read_frags(cur, 0, fa[0], fb[0]);
+#pragma unroll
+        for (int f = 0; f < 8; ++f) read_one(cur, 0, f, fa[0], fb[0]);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
-            if (kk < 3) read_frags(cur, kk + 1, fa[(kk + 1) & 1], fb[(kk + 1) & 1]);
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[kk & 1][i], fb[kk & 1][j],
-                                                                        acc[i][j], 0, 0, 0);
+            for (int t = 0; t < 16; ++t) {
+                const int i = t >> 2, j = t & 3;
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[kk & 1][i], fb[kk & 1][j],
+                                                                    acc[i][j], 0, 0, 0);
+                if (kk == 0) issue_one(cur ^ 1, knext, t);
+                if (kk < 3 && t < 8) read_one(cur, kk + 1, t, fa[(kk + 1) & 1], fb[(kk + 1) & 1]);
+                __builtin_amdgcn_sched_barrier(0);
+            }
         }
     }
 
