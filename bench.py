@@ -211,6 +211,9 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=100)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy three times (a kernel of "
+                         "known traffic, to calibrate rocprofv3's FETCH_SIZE/WRITE_SIZE)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the layer runs on a single MI355X with every expert "
@@ -223,6 +226,14 @@ def main():
     from sparse_mixture_experts_03_amd import synth
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.copy_probe:
+        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")   # 1 GiB
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes": src.numel() * 4, "launches": 3}))
+        return
     B.load(build_if_missing=False)
     w = synth.WORKLOADS[args.workload]
     res = run_workload(w, args.steps, args.warmup)

@@ -42,8 +42,11 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 constexpr int ACT_RELU = 0, ACT_GELU = 1, ACT_SWIGLU = 2, ACT_NONE = 3;
 
+// SwiGLU uses the hardware exp2 and reciprocal (about 1 ulp each; the
+// result is rounded to bf16, 8 bits, right after).  GELU keeps erff.
 __device__ __forceinline__ float apply_act(int act, float a1, float a3) {
-    if (act == ACT_SWIGLU) return a1 / (1.f + expf(-a1)) * a3;
+    if (act == ACT_SWIGLU)
+        return a1 * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-1.44269504088896341f * a1)) * a3;
     if (act == ACT_GELU) return 0.5f * a1 * (1.f + erff(a1 * 0.70710678118654752f));
     if (act == ACT_RELU) return fmaxf(a1, 0.f);
     return a1;
@@ -218,7 +221,7 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(
                     const float v = apply_act(ACT, a1, a3);
                     const int64_t o = (int64_t)(row0 + row) * N + col;
                     if (OUT_BF16)
-                        ((uint16_t *)C)[o] = f32_to_bf16(v);
+                        ((__bf16 *)C)[o] = (__bf16)v;  // v_cvt_pk_bf16_f32, round to nearest even
                     else
                         ((float *)C)[o] = v;
                 }
@@ -234,9 +237,12 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(
 // Operands go from global memory straight into LDS with
 // global_load_lds_dwordx4 (no register staging): instruction j of wave w
 // fills LDS rows 8*(8w + j) .. +8, lane l writing the 16 bytes at
-// (row 8*(8w + j) + l/8, slot l%8).  The slot holds k-chunk
-// (l % 8) ^ (row % 8) of that row -- an XOR swizzle, so that the 32 rows a
-// fragment read touches fall on distinct banks.  Two LDS stages (2 x 64 KB):
+// (row 8*(8w + j) + l/8, slot l%8).  Slot s of row r holds k-chunk
+// s ^ f(r), f(r) = (r % 8) ^ ((r / 8) % 2): an XOR swizzle under which any
+// 8 consecutive rows use 8 different slots and any 16 consecutive rows use
+// 16 different (row parity, slot) pairs, so the rows a fragment read
+// serves together fall on distinct banks whether the LDS serves 8 or 16
+// lanes of a 16-byte read per cycle.  Two LDS stages (2 x 64 KB):
 // the loads for stage k+1 are issued right after the barrier that opens
 // stage k, and run under stage k's 64 MFMAs per wave.  Fragments for the
 // next 16-wide k step are read from LDS while the current step's MFMAs run.
@@ -261,14 +267,16 @@ __global__ __launch_bounds__(256) void gemm_bf16_big_kernel(
 
     // element offsets (from the operand base, at k = 0) of the 16 chunks this
     // lane loads per stage: 8 of A, 8 of the weights
-    const int sub = lane >> 3;                  // row within an 8-row group
-    const int kchunk = ((lane & 7) ^ sub) * 8;  // swizzled k-chunk, in elements
+    // LDS row 8*(8w + j) + l/8 has f = (l/8) ^ (j % 2), so lane l of load j
+    // fetches k-chunk (l % 8) ^ (l / 8) ^ (j % 2)
+    const int sub = lane >> 3;  // row within an 8-row group
     uint32_t a_off[8], b_off[8];
     const uint16_t *bbase;
     {
         const int wrow0 = wave * 64;  // first LDS row this wave fills
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
+            const int kchunk = ((lane & 7) ^ sub ^ (j & 1)) * 8;
             const int r = wrow0 + j * 8 + sub;
             a_off[j] = (uint32_t)(row0 + min(r, nrows - 1)) * (uint32_t)K + kchunk;
         }
@@ -277,6 +285,7 @@ __global__ __launch_bounds__(256) void gemm_bf16_big_kernel(
             bbase = (wave < 2 ? B1 : B3) + (int64_t)e * N * K;
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
+                const int kchunk = ((lane & 7) ^ sub ^ (j & 1)) * 8;
                 const int r = (wrow0 & 127) + j * 8 + sub;
                 b_off[j] = (uint32_t)min(n0 + r, N - 1) * (uint32_t)K + kchunk;
             }
@@ -284,6 +293,7 @@ __global__ __launch_bounds__(256) void gemm_bf16_big_kernel(
             bbase = B1 + (int64_t)e * N * K;
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
+                const int kchunk = ((lane & 7) ^ sub ^ (j & 1)) * 8;
                 const int r = wrow0 + j * 8 + sub;
                 b_off[j] = (uint32_t)min(n0 + r, N - 1) * (uint32_t)K + kchunk;
             }
@@ -322,7 +332,8 @@ __global__ __launch_bounds__(256) void gemm_bf16_big_kernel(
     // fragment read f (0..7) of k step kk, in the order the MFMAs consume
     // them: A0, B0, B1, B2, B3, A1, A2, A3
     auto read_one = [&](int stage, int kk, int f, bf16x8_t (&a)[4], bf16x8_t (&b)[4]) {
-        const int slot = ((kk * 2 + (lane >> 5)) ^ (lane & 7)) * 16;
+        // fragment rows are 32-aligned bases + lane % 32
+        const int slot = ((kk * 2 + (lane >> 5)) ^ (lr & 7) ^ ((lr >> 3) & 1)) * 16;
         if (f == 0 || f >= 5) {
             const int i = f == 0 ? 0 : f - 4;
             a[i] = *(const bf16x8_t *)(lds[stage][0] + (wm * 128 + i * 32 + lr) * ROWB + slot);
@@ -381,7 +392,7 @@ __global__ __launch_bounds__(256) void gemm_bf16_big_kernel(
                                          : apply_act(ACT, acc[i][jj][r], 0.f);
                     const int64_t o = (int64_t)(row0 + row) * N + col;
                     if (OUT_BF16)
-                        ((uint16_t *)C)[o] = f32_to_bf16(v);
+                        ((__bf16 *)C)[o] = (__bf16)v;  // v_cvt_pk_bf16_f32, round to nearest even
                     else
                         ((float *)C)[o] = v;
                 }
