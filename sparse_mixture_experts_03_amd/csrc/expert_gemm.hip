@@ -262,53 +262,48 @@ __global__ __launch_bounds__(256) void gemm_bf16_big_kernel(
     int e, row0, nrows, ntile;
     if (!find_tile<BIG_BM>(offsets, E, (N + BN - 1) / BN, e, row0, nrows, ntile)) return;
     const int n0 = ntile * BN;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    // the wave index as a scalar, so LDS destinations (M0) and operand bases
+    // are computed on the scalar unit
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave >> 1, wn = wave & 1;
 
-    // element offsets (from the operand base, at k = 0) of the 16 chunks this
-    // lane loads per stage: 8 of A, 8 of the weights
     // LDS row 8*(8w + j) + l/8 has f = (l/8) ^ (j % 2), so lane l of load j
-    // fetches k-chunk (l % 8) ^ (l / 8) ^ (j % 2)
+    // fetches k-chunk (l % 8) ^ (l / 8) ^ (j % 2).  Per-lane byte offsets
+    // from a scalar base; they do not change from stage to stage.
     const int sub = lane >> 3;  // row within an 8-row group
     uint32_t a_off[8], b_off[8];
-    const uint16_t *bbase;
+    const char *abase = (const char *)A;
+    const char *bbase;
     {
         const int wrow0 = wave * 64;  // first LDS row this wave fills
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             const int kchunk = ((lane & 7) ^ sub ^ (j & 1)) * 8;
             const int r = wrow0 + j * 8 + sub;
-            a_off[j] = (uint32_t)(row0 + min(r, nrows - 1)) * (uint32_t)K + kchunk;
+            a_off[j] = ((uint32_t)(row0 + min(r, nrows - 1)) * (uint32_t)K + kchunk) * 2u;
         }
-        if (DUAL) {
-            // waves 0,1 fill W1 rows 0..127; waves 2,3 fill W3 rows 0..127
-            bbase = (wave < 2 ? B1 : B3) + (int64_t)e * N * K;
+        // SwiGLU: waves 0,1 fill W1 rows 0..127, waves 2,3 W3 rows 0..127
+        bbase = (const char *)((DUAL && wave >= 2) ? B3 : B1) + (int64_t)e * N * K * 2;
+        const int brow0 = DUAL ? (wrow0 & 127) : wrow0;
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const int kchunk = ((lane & 7) ^ sub ^ (j & 1)) * 8;
-                const int r = (wrow0 & 127) + j * 8 + sub;
-                b_off[j] = (uint32_t)min(n0 + r, N - 1) * (uint32_t)K + kchunk;
-            }
-        } else {
-            bbase = B1 + (int64_t)e * N * K;
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const int kchunk = ((lane & 7) ^ sub ^ (j & 1)) * 8;
-                const int r = wrow0 + j * 8 + sub;
-                b_off[j] = (uint32_t)min(n0 + r, N - 1) * (uint32_t)K + kchunk;
-            }
+        for (int j = 0; j < 8; ++j) {
+            const int kchunk = ((lane & 7) ^ sub ^ (j & 1)) * 8;
+            const int r = brow0 + j * 8 + sub;
+            b_off[j] = ((uint32_t)min(n0 + r, N - 1) * (uint32_t)K + kchunk) * 2u;
         }
     }
     // global -> LDS load q (0..15) of a stage: q < 8 from A, else from the weights
     auto issue_one = [&](int stage, int k0, int q) {
+        const size_t kb = (size_t)k0 * 2;
         if (q < 8)
             __builtin_amdgcn_global_load_lds(
-                (const void *)(A + a_off[q] + k0),
+                (const void *)(abase + kb + a_off[q]),
                 (__attribute__((address_space(3))) void *)(lds[stage][0] + wave * 64 * ROWB + q * 8 * ROWB),
                 16, 0, 0);
         else
             __builtin_amdgcn_global_load_lds(
-                (const void *)(bbase + b_off[q - 8] + k0),
+                (const void *)(bbase + kb + b_off[q - 8]),
                 (__attribute__((address_space(3))) void *)(lds[stage][1] + wave * 64 * ROWB + (q - 8) * 8 * ROWB),
                 16, 0, 0);
     };
@@ -346,8 +341,10 @@ __global__ __launch_bounds__(256) void gemm_bf16_big_kernel(
     // closed by a scheduling barrier: 64 MFMAs (i-major, so consecutive
     // MFMAs never share an accumulator); with each of the first 8 MFMAs of
     // steps 0..2 one fragment read for the next step (8 MFMAs of slack
-    // before the step boundary waits for them); with each of the first 16
-    // MFMAs one global->LDS load of the next stage.  The last stage's
+    // before the step boundary waits for them); with every second MFMA of
+    // steps 0 and 1 one global->LDS load of the next stage (early enough to
+    // land before the stage ends, spread out so that their issue does not
+    // starve the MFMA pipe).  The last stage's
     // prefetch re-loads that stage into the idle buffer (nobody reads it),
     // which keeps the loop free of branches.
     const int KT = K / BK;
@@ -369,7 +366,7 @@ __global__ __launch_bounds__(256) void gemm_bf16_big_kernel(
                 const int i = t >> 2, j = t & 3;
                 acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[kk & 1][i], fb[kk & 1][j],
                                                                     acc[i][j], 0, 0, 0);
-                if (kk == 0) issue_one(cur ^ 1, knext, t);
+                if (kk < 2 && (t & 1)) issue_one(cur ^ 1, knext, kk * 8 + (t >> 1));
                 if (kk < 3 && t < 8) read_one(cur, kk + 1, t, fa[(kk + 1) & 1], fb[(kk + 1) & 1]);
                 __builtin_amdgcn_sched_barrier(0);
             }
