@@ -397,6 +397,112 @@ __global__ __launch_bounds__(256) void gemm_bf16_big_kernel(
         }
 }
 
+// ---- skinny row groups (decode batches): weight streaming ----------------
+//
+// gemm_bf16_skinny_kernel, for experts with at most 32 rows and K a
+// multiple of 128.  One wave per (expert, 16 weight rows) -- for SwiGLU the
+// same 16 rows of W1 and of W3.  The wave streams its weight rows over K in
+// 128-wide chunks, PF chunks in flight in a register ring (16-byte loads),
+// and multiplies them with the expert's rows of A (at most 32, read from
+// L2 one chunk ahead) on v_mfma_f32_16x16x32_bf16.  Within a chunk, lane
+// l = 16g + n holds the 64 contiguous bytes k = 32g .. 32g+31 of its row,
+// and MFMA j of the chunk takes k = 32g + 8j .. +8 from both operands: the
+// same permutation of k on both sides, so every product and its partner
+// meet as in the plain order.  MFMA 16x16x32 accumulator: lane l holds
+// rows 4*(l/16) + r, column l % 16.  Experts with no rows exit at once.
+constexpr int SK_KC = 128;
+constexpr int SK_MAXROWS = 32;
+
+template <int PF, bool DUAL, int ACT, bool OUT_BF16>
+__global__ __launch_bounds__(64) void gemm_bf16_skinny_kernel(
+    const uint16_t *__restrict__ A, const int32_t *__restrict__ offsets, int E,
+    const uint16_t *__restrict__ B1, const uint16_t *__restrict__ B3, void *__restrict__ C,
+    int N, int K) {
+    typedef float f32x4_t __attribute__((ext_vector_type(4)));
+    constexpr int NB = DUAL ? 2 : 1;
+    const int ntile = (N + 15) / 16;
+    const int e = blockIdx.x / ntile;
+    const int n0 = (blockIdx.x % ntile) * 16;
+    if (e >= E) return;
+    const int lo = offsets[e], M = offsets[e + 1] - lo;
+    if (M <= 0) return;
+    const int lane = threadIdx.x;
+    const int n = lane & 15, g = lane >> 4;
+    const bool two = M > 16;  // second 16-row tile of A in use (wave-uniform)
+
+    const uint16_t *a_row[2];
+    a_row[0] = A + (int64_t)(lo + min(n, M - 1)) * K + g * 32;
+    a_row[1] = A + (int64_t)(lo + min(n + 16, M - 1)) * K + g * 32;
+    const uint16_t *b_row[NB];
+    b_row[0] = B1 + ((int64_t)e * N + min(n0 + n, N - 1)) * K + g * 32;
+    if (DUAL) b_row[NB - 1] = B3 + ((int64_t)e * N + min(n0 + n, N - 1)) * K + g * 32;
+
+    f32x4_t acc[2][NB];
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+        for (int q = 0; q < NB; ++q) acc[m][q] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    uint4 rb[PF][NB][4];
+    uint4 ra[2][2][4];
+    const int nch = K / SK_KC;
+    auto load_b = [&](int slot, int ch) {
+#pragma unroll
+        for (int q = 0; q < NB; ++q)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                rb[slot][q][j] = *(const uint4 *)(b_row[q] + (int64_t)ch * SK_KC + j * 8);
+    };
+    auto load_a = [&](int slot, int ch) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) ra[slot][0][j] = *(const uint4 *)(a_row[0] + (int64_t)ch * SK_KC + j * 8);
+        if (two)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                ra[slot][1][j] = *(const uint4 *)(a_row[1] + (int64_t)ch * SK_KC + j * 8);
+    };
+#pragma unroll
+    for (int p = 0; p < PF - 1; ++p)
+        if (p < nch) load_b(p, p);
+    load_a(0, 0);
+    for (int c0 = 0; c0 < nch; c0 += PF) {
+#pragma unroll
+        for (int sl = 0; sl < PF; ++sl) {
+            const int ch = c0 + sl;
+            if (ch < nch) {
+                if (ch + PF - 1 < nch) load_b((sl + PF - 1) % PF, ch + PF - 1);
+                if (ch + 1 < nch) load_a((sl + 1) & 1, ch + 1);
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+#pragma unroll
+                    for (int q = 0; q < NB; ++q) {
+                        const bf16x8_t b = __builtin_bit_cast(bf16x8_t, rb[sl][q][j]);
+                        acc[0][q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                            __builtin_bit_cast(bf16x8_t, ra[sl & 1][0][j]), b, acc[0][q], 0, 0, 0);
+                        if (two)
+                            acc[1][q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                                __builtin_bit_cast(bf16x8_t, ra[sl & 1][1][j]), b, acc[1][q], 0, 0, 0);
+                    }
+            }
+        }
+    }
+    const int col = n0 + n;
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int row = m * 16 + 4 * g + r;
+            if (row < M && col < N) {
+                const float v = apply_act(ACT, acc[m][0][r], DUAL ? acc[m][NB - 1][r] : 0.f);
+                const int64_t o = (int64_t)(lo + row) * N + col;
+                if (OUT_BF16)
+                    ((__bf16 *)C)[o] = (__bf16)v;
+                else
+                    ((float *)C)[o] = v;
+            }
+        }
+}
+
 // ---- fp32 path -----------------------------------------------------------
 
 __device__ __forceinline__ int expert_of_row(const int32_t *__restrict__ offsets, int E, int r) {
@@ -453,6 +559,14 @@ inline unsigned row_tile_bound(const Shape &s, int BM) {
     return (unsigned)((rows + BM - 1) / BM + s.E);
 }
 
+// Most rows any one expert can receive: each token picks an expert at most
+// once, and a capacity caps it further.
+inline int64_t max_rows_per_expert(const Shape &s) {
+    int64_t m = s.T;
+    if (s.C >= 0 && s.C < m) m = s.C;
+    return m;
+}
+
 // Row-tile height from the mean rows per expert (the counts themselves
 // stay on the device).
 inline int pick_bm(const Shape &s, int K) {
@@ -491,9 +605,25 @@ hipError_t launch_big(const Shape &s, const void *A, const int32_t *offsets, con
     return hipGetLastError();
 }
 
+template <int PF, bool DUAL, int ACT, bool OUT_BF16>
+hipError_t launch_skinny(const Shape &s, const void *A, const int32_t *offsets, const void *B1,
+                         const void *B3, void *C, int N, int K, hipStream_t st) {
+    const unsigned blocks = (unsigned)s.E * (unsigned)((N + 15) / 16);
+    hipLaunchKernelGGL((gemm_bf16_skinny_kernel<PF, DUAL, ACT, OUT_BF16>), dim3(blocks), dim3(64), 0,
+                       st, (const uint16_t *)A, offsets, s.E, (const uint16_t *)B1,
+                       (const uint16_t *)B3, C, N, K);
+    return hipGetLastError();
+}
+
+inline bool use_skinny(const Shape &s, int K) {
+    return max_rows_per_expert(s) <= SK_MAXROWS && K % SK_KC == 0;
+}
+
 template <int ACT, bool DUAL>
 hipError_t launch_up_bf16(const Shape &s, const void *A, const int32_t *offsets, const void *W1,
                           const void *W3, void *H, hipStream_t st) {
+    if (use_skinny(s, s.d))
+        return launch_skinny<4, DUAL, ACT, true>(s, A, offsets, W1, W3, H, s.d_ff, s.d, st);
     switch (pick_bm(s, s.d)) {
     case BIG_BM: return launch_big<DUAL, ACT, true>(s, A, offsets, W1, W3, H, s.d_ff, s.d, st);
     case 128: return launch_gemm<128, 128, 2, 2, DUAL, ACT, true>(s, A, offsets, W1, W3, H, s.d_ff, s.d, st);
@@ -529,6 +659,8 @@ hipError_t launch_expert_down(const Shape &s, const void *H, const int32_t *offs
                            s.d_ff);
         return hipGetLastError();
     }
+    if (use_skinny(s, s.d_ff))
+        return launch_skinny<4, false, ACT_NONE, false>(s, H, offsets, W2, nullptr, y_perm, s.d, s.d_ff, st);
     switch (pick_bm(s, s.d_ff)) {
     case BIG_BM: return launch_big<false, ACT_NONE, false>(s, H, offsets, W2, nullptr, y_perm, s.d, s.d_ff, st);
     case 128: return launch_gemm<128, 128, 2, 2, false, ACT_NONE, false>(s, H, offsets, W2, nullptr, y_perm, s.d, s.d_ff, st);

@@ -40,6 +40,16 @@ SMALL = {
     # partial column tile in the down projection (320 = 256 + 64)
     "big_gelu": W["switch"].with_(name="big_gelu", T=1000, d=320, d_ff=384, E=4, cf=1.05,
                                   noise_std=0.25),
+    # weight-streaming kernel (at most 32 rows per expert, K % 128 == 0):
+    # every token on both experts -> two full 16-row tiles of A per expert
+    "skinny_full": W["mixtral_decode"].with_(name="skinny_full", T=32, d=256, d_ff=384, E=2),
+    # ragged counts across one and two 16-row tiles, top-2 of 3
+    "skinny_ragged": W["mixtral_decode"].with_(name="skinny_ragged", T=28, d=384, d_ff=256, E=3),
+    # non-dual (GELU), k = 1, 40 column tiles
+    "skinny_gelu": W["switch"].with_(name="skinny_gelu", T=24, d=128, d_ff=640, E=4, cf=0.0,
+                                     noise_std=0.0),
+    # up projection with a partial last column tile (136 = 8*16 + 8)
+    "skinny_partial_n": W["mixtral_decode"].with_(name="skinny_partial_n", T=16, d=128, d_ff=136, E=4),
     # Switch gate with k = 2, 64-row SwiGLU tiles
     "switch_k2": W["mixtral_prefill"].with_(name="switch_k2", T=500, d=128, d_ff=256, E=16, k=2,
                                             gate="switch", x_rmsnorm=False),
