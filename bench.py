@@ -11,8 +11,8 @@ same run and reported in the "decode" object.  Prints one JSON line.
 
 Timing: W untimed warm-up steps, then exactly K steps between two device
 synchronisations.  Per-kernel durations come from HIP events that the
-library records on the launch stream around each stage (the descriptor's
-stage-event hook), over the same timed steps.
+library records on the launch stream (the descriptor's stage-event hook)
+around the two expert GEMMs only, over the same timed steps.
 
 Roofline of the dominant kernel (the expert up-projection, a grouped GEMM
 on bf16 MFMA): algorithmic FLOPs per launch = N_kept * 2 * n_up * d * d_ff
@@ -64,9 +64,12 @@ class HipEvents:
                                                  ctypes.c_void_p]
         self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
 
-    def create(self, n):
+    def create(self, n, keep=None):
+        """An array of n event handles; slots outside ``keep`` stay NULL."""
         arr = (ctypes.c_void_p * n)()
         for i in range(n):
+            if keep is not None and i not in keep:
+                continue
             e = ctypes.c_void_p()
             rc = self.hip.hipEventCreate(ctypes.byref(e))
             if rc != 0:
@@ -83,7 +86,8 @@ class HipEvents:
 
     def destroy(self, arr):
         for e in arr:
-            self.hip.hipEventDestroy(e)
+            if e:
+                self.hip.hipEventDestroy(e)
 
 
 def source_sha():
@@ -140,6 +144,8 @@ def run_workload(w, steps, warmup, fresh_x_steps=0, seed=0):
         else:
             desc.stage_events = None
             desc.n_stage_events = 0
+        # only the events around the two expert GEMMs are recorded: each
+        # recorded event separates the kernels around it by a few us
         B.moe_forward(desc, xs[j], dw["Wr"], dw["bias"], noises[j], dw["W1"], dw["W3"], dw["W2"],
                       out["y"], ws, kept_counts=out["kept_counts"], stats=out["stats"],
                       stream=stream)
@@ -147,7 +153,8 @@ def run_workload(w, steps, warmup, fresh_x_steps=0, seed=0):
     for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
-    evsets = [ev.create(nev) for _ in range(steps)]
+    timed = (STAGES.index("expert_up"), STAGES.index("expert_down") + 1)
+    evsets = [ev.create(nev, keep=range(timed[0], timed[1] + 1)) for _ in range(steps)]
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     for i in range(steps):
@@ -155,7 +162,8 @@ def run_workload(w, steps, warmup, fresh_x_steps=0, seed=0):
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t_start
 
-    stage_ms = np.array([[ev.elapsed_ms(es[j], es[j + 1]) for j in range(nev - 1)] for es in evsets])
+    stage_ms = np.array([[ev.elapsed_ms(es[j], es[j + 1]) if es[j] and es[j + 1] else np.nan
+                          for j in range(nev - 1)] for es in evsets])
     for es in evsets:
         ev.destroy(es)
     kept = out["kept_counts"].cpu().numpy().astype(np.int64)
@@ -246,7 +254,7 @@ def main():
     up_ms = float(res["stage_ms"][up])
     up_flops = res["n_kept"] * 2.0 * n_up * w.d * w.d_ff
     achieved = up_flops / (up_ms * 1e-3) / 1e12
-    stages = {n: round(float(v), 4) for n, v in zip(STAGES, res["stage_ms"])}
+    stages = {n: round(float(v), 4) for n, v in zip(STAGES, res["stage_ms"]) if np.isfinite(v)}
     log(f"[bench] {w.name}: {ms_step:.3f} ms/step, stages(ms) {stages}")
     line = {
         "metric": METRIC, "value": round(tokens_s, 1), "unit": "tokens/s", "n_gpus": 1,
@@ -279,7 +287,7 @@ def main():
             "unit": "tokens/s", "steps": rd["steps"], "ms_per_step": round(ms_d, 4),
             "step_hbm_gbs": round(step_bytes / (ms_d * 1e-3) / 1e9, 1),
             "step_hbm_frac": round(step_bytes / (ms_d * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
-            "stage_ms": {n: round(float(v), 4) for n, v in zip(STAGES, rd["stage_ms"])},
+            "stage_ms": {n: round(float(v), 4) for n, v in zip(STAGES, rd["stage_ms"]) if np.isfinite(v)},
             "roofline": {"bound": "hbm", "kernel": "expert_up", "achieved": round(gbs, 1),
                          "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
                          "traffic": traffic_for(wd.name, "expert_up"),

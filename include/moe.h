@@ -112,7 +112,9 @@ extern "C" {
  * stage_events points to n_stage_events hipEvent_t handles; moe_forward
  * records event j after its j-th kernel stage (event 0 before the first),
  * for j < n_stage_events, on `stream`; MOE_FORWARD_STAGES + 1 events
- * bracket every stage.  NULL disables it.  The stages, in order: route,
+ * bracket every stage, and a NULL entry is skipped (each recorded event
+ * separates the kernels around it by a few microseconds, so record only
+ * the ones needed).  NULL disables the hook.  The stages, in order: route,
  * route-finalize, dispatch, gather, expert-up, expert-down, combine.
  * The other entry points ignore it.
  */

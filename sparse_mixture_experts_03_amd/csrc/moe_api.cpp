@@ -120,7 +120,7 @@ struct StageEvents {
     int next = 0;
     hipError_t record(hipStream_t st) {
         hipError_t e = hipSuccess;
-        if (ev && next < n) e = hipEventRecord((hipEvent_t)ev[next], st);
+        if (ev && next < n && ev[next]) e = hipEventRecord((hipEvent_t)ev[next], st);
         ++next;
         return e;
     }
