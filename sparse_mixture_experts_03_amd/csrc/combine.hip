@@ -8,10 +8,11 @@
 // nothing here, and a token dropped from every expert gets 0 (its residual,
 // outside the layer, carries it).
 //
-// combine_kernel: one wave per token, grid-stride over tokens.  Each lane
-// owns 4 consecutive columns and sums the k slots in slot order in fp32,
-// then stores fp32 or bf16.  Every output element is written exactly once,
-// so no memset and no atomics are needed.
+// combine_kernel: one wave per (token, 256-column chunk), grid-stride; each
+// lane owns 4 consecutive columns and sums the k slots in slot order in
+// fp32, then stores fp32 or bf16 (a scalar variant, one wave per token,
+// serves widths that are not a multiple of 4).  Every output element is
+// written exactly once, so no memset and no atomics are needed.
 #include "moe_internal.h"
 
 namespace moe {
@@ -24,11 +25,16 @@ __global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ 
                                                       const float *__restrict__ gates, int T,
                                                       int d, int k, void *__restrict__ y) {
     const int lane = threadIdx.x & 63;
-    for (int t = blockIdx.x * 4 + (threadIdx.x >> 6); t < T; t += gridDim.x * 4) {
-        const int32_t *rs = row_of_slot + (int64_t)t * k;
-        const float *gs = gates + (int64_t)t * k;
-        if (VEC4) {
-            for (int c = lane * 4; c < d; c += 256) {
+    if (VEC4) {
+        // one wave per (token, 256-column chunk)
+        const int nch = (d + 255) / 256;
+        for (int64_t it = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); it < (int64_t)T * nch;
+             it += (int64_t)gridDim.x * 4) {
+            const int t = (int)(it / nch);
+            const int c = (int)(it - (int64_t)t * nch) * 256 + lane * 4;
+            const int32_t *rs = row_of_slot + (int64_t)t * k;
+            const float *gs = gates + (int64_t)t * k;
+            if (c < d) {
                 float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
                 for (int s = 0; s < k; ++s) {
                     const int r = rs[s];
@@ -49,7 +55,13 @@ __global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ 
                     *(float4 *)((float *)y + (int64_t)t * d + c) = a;
                 }
             }
-        } else {
+        }
+        return;
+    }
+    for (int t = blockIdx.x * 4 + (threadIdx.x >> 6); t < T; t += gridDim.x * 4) {
+        const int32_t *rs = row_of_slot + (int64_t)t * k;
+        const float *gs = gates + (int64_t)t * k;
+        {
             for (int c = lane; c < d; c += 64) {
                 float a = 0.f;
                 for (int s = 0; s < k; ++s) {
@@ -70,13 +82,14 @@ __global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ 
 
 hipError_t launch_combine(const Shape &s, const float *y_perm, const int32_t *row_of_slot,
                           const float *gates, void *y, hipStream_t st) {
-    int blocks = (s.T + 3) / 4;
-    if (blocks > 8192) blocks = 8192;
     const bool v4 = (s.d % 4) == 0;
+    int64_t items = v4 ? (int64_t)s.T * ((s.d + 255) / 256) : (int64_t)s.T;
+    int64_t blocks = (items + 3) / 4;
+    if (blocks > 16384) blocks = 16384;
     const bool bf = s.dtype == 1;
     auto kern = bf ? (v4 ? combine_kernel<true, true> : combine_kernel<true, false>)
                    : (v4 ? combine_kernel<false, true> : combine_kernel<false, false>);
-    hipLaunchKernelGGL(kern, dim3(blocks), dim3(256), 0, st, y_perm, row_of_slot, gates, s.T, s.d,
+    hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(256), 0, st, y_perm, row_of_slot, gates, s.T, s.d,
                        s.k, y);
     return hipGetLastError();
 }

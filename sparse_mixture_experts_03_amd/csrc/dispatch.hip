@@ -6,17 +6,22 @@
 // section: the per-expert token lists are in token order, and production
 // kernels replace the loop over experts by a sort of tokens by expert.
 //
-// dispatch_kernel: one block per expert e (grid = E), 256 threads.
-//   A. Histogram of all T*k assignments over experts with LDS integer
-//      atomics (a count is order-independent, so the result is exact and
-//      reproducible).  From it every block knows routed_e, kept_e =
-//      min(routed_e, C) and its row offset sum_{e' < e} kept_e'.
-//   B. Rank of every assignment of expert e in token order: the block
-//      sweeps the assignments t-major in chunks of 256; a 64-lane ballot
-//      and popcount give each lane its rank inside the wave, four wave
-//      totals in LDS give the wave's base, and a running block base carries
-//      the count across chunks.  No atomic decides any order.
-//      rank < C: row = offset_e + rank, else dropped.
+// The T*k assignments are read t-major (token t, slot s at j = t*k + s),
+// which is token order within every expert (an expert appears at most once
+// per token).  They are cut into chunks of 256 (1024 when T*k is large).
+//   dispatch_count_kernel (one block per chunk): per-chunk histogram over
+//     experts with LDS integer atomics (a count does not depend on the
+//     order of the additions).
+//   dispatch_rank_kernel (one block per chunk): every block derives, from
+//     all chunk histograms, routed_e, kept_e = min(routed_e, C), the row
+//     offsets (exclusive prefix of kept_e) and, for its own chunk, how many
+//     assignments of each expert precede it.  It then ranks its chunk in
+//     order, 256 assignments per round: inside a wave, lanes with the same
+//     expert are grouped by ballot (leader's expert, then the lanes that
+//     match it) and ranked by popcount of the lower lanes; a table of
+//     per-wave counts in LDS adds the waves before, and a per-expert
+//     running count carries the rounds.  No atomic decides any order.
+//     rank < C: row = offset_e + rank; else dropped.
 // gather_kernel: x_perm[r] = x[token_of_row[r]] for r < offsets[E]; one
 //   wave per row, 16-byte loads and stores, grid-stride over rows.
 #include "moe_internal.h"
@@ -28,59 +33,95 @@ namespace {
 constexpr int DP_THREADS = 256;
 constexpr int DP_EMAX = 128;
 
-__global__ __launch_bounds__(DP_THREADS) void dispatch_kernel(
-    const int32_t *__restrict__ topk_idx, int64_t Tk, int k, int E, int64_t C,
-    int32_t *__restrict__ routed, int32_t *__restrict__ kept, int32_t *__restrict__ offsets,
-    int32_t *__restrict__ row_of_slot, int32_t *__restrict__ token_of_row,
-    uint8_t *__restrict__ dropped) {
+__global__ __launch_bounds__(DP_THREADS) void dispatch_count_kernel(
+    const int32_t *__restrict__ topk_idx, int64_t Tk, int E, int chunk,
+    int32_t *__restrict__ chunk_counts) {
     __shared__ int hist[DP_EMAX];
-    __shared__ int wsum[DP_THREADS / 64];
-    __shared__ int sh_off, sh_total;
     const int tid = threadIdx.x;
-    const int e = blockIdx.x;
-    const int lane = tid & 63, w = tid >> 6;
-
     if (tid < DP_EMAX) hist[tid] = 0;
     __syncthreads();
-    for (int64_t j = tid; j < Tk; j += DP_THREADS) atomicAdd(&hist[topk_idx[j]], 1);
-    __syncthreads();
-    if (tid == 0) {
-        int64_t off = 0, tot = 0;
-        for (int i = 0; i < E; ++i) {
-            int64_t kp = (C >= 0 && hist[i] > C) ? C : hist[i];
-            if (i < e) off += kp;
-            tot += kp;
-        }
-        sh_off = (int)off;
-        sh_total = (int)tot;
-        int64_t ke = (C >= 0 && hist[e] > C) ? C : hist[e];
-        routed[e] = hist[e];
-        kept[e] = (int)ke;
-        offsets[e] = (int)off;
-        if (e == E - 1) offsets[E] = (int)tot;
+    const int64_t j0 = (int64_t)blockIdx.x * chunk;
+    for (int q = 0; q < chunk / DP_THREADS; ++q) {
+        const int64_t j = j0 + q * DP_THREADS + tid;
+        if (j < Tk) atomicAdd(&hist[topk_idx[j]], 1);
     }
     __syncthreads();
-    const int off = sh_off, total = sh_total;
+    if (tid < E) chunk_counts[(int64_t)blockIdx.x * E + tid] = hist[tid];
+}
 
-    int64_t base = 0;
-    const unsigned long long lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    for (int64_t j0 = 0; j0 < Tk; j0 += DP_THREADS) {
-        const int64_t j = j0 + tid;
-        const bool pred = (j < Tk) && (topk_idx[j] == e);
-        const unsigned long long b = __ballot(pred);
-        if (lane == 0) wsum[w] = __popcll(b);
-        __syncthreads();
-        int wbase = 0, btot = 0;
-#pragma unroll
-        for (int i = 0; i < DP_THREADS / 64; ++i) {
-            int c = wsum[i];
-            wbase += (i < w) ? c : 0;
-            btot += c;
+__global__ __launch_bounds__(DP_THREADS) void dispatch_rank_kernel(
+    const int32_t *__restrict__ topk_idx, int64_t Tk, int k, int E, int64_t C, int chunk_len,
+    int nchunks, const int32_t *__restrict__ chunk_counts, int32_t *__restrict__ routed,
+    int32_t *__restrict__ kept, int32_t *__restrict__ offsets, int32_t *__restrict__ row_of_slot,
+    int32_t *__restrict__ token_of_row, uint8_t *__restrict__ dropped) {
+    __shared__ int running[DP_EMAX];  // assignments of e before the current round
+    __shared__ int off[DP_EMAX];      // first row of expert e
+    __shared__ int keptc[DP_EMAX];
+    __shared__ int wcnt[DP_THREADS / 64][DP_EMAX];
+    __shared__ int sh_total;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int chunk = blockIdx.x;
+
+    if (tid < E) {
+        int before = 0, tot = 0;
+#pragma unroll 8
+        for (int c = 0; c < nchunks; ++c) {
+            const int v = chunk_counts[(int64_t)c * E + tid];
+            before += (c < chunk) ? v : 0;
+            tot += v;
         }
-        if (pred) {
-            const int64_t rank = base + wbase + __popcll(b & lt_mask);
+        running[tid] = before;
+        keptc[tid] = (C >= 0 && tot > C) ? (int)C : tot;
+        if (chunk == 0) {
+            routed[tid] = tot;
+            kept[tid] = keptc[tid];
+        }
+    }
+    __syncthreads();
+    if (tid == 0) {
+        int o = 0;
+        for (int e = 0; e < E; ++e) {
+            off[e] = o;
+            o += keptc[e];
+        }
+        sh_total = o;
+        if (chunk == 0) {
+            for (int e = 0; e < E; ++e) offsets[e] = off[e];
+            offsets[E] = o;
+        }
+    }
+    __syncthreads();
+
+    const unsigned long long lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    const int64_t j0 = (int64_t)chunk * chunk_len;
+    for (int round = 0; round < chunk_len / DP_THREADS; ++round) {
+        for (int i = tid; i < (DP_THREADS / 64) * DP_EMAX; i += DP_THREADS) (&wcnt[0][0])[i] = 0;
+        __syncthreads();
+        const int64_t j = j0 + round * DP_THREADS + tid;
+        const bool valid = j < Tk;
+        const int ej = valid ? topk_idx[j] : -1;
+        // group the wave's lanes by expert, in lane (= assignment) order
+        bool act = valid;
+        int rank_w = 0;
+        while (true) {
+            const unsigned long long am = __ballot(act);
+            if (am == 0ull) break;
+            const int leader = __ffsll((long long)am) - 1;
+            const int e0 = __shfl(ej, leader);
+            const bool m = act && ej == e0;
+            const unsigned long long mm = __ballot(m);
+            if (m) {
+                rank_w = __popcll(mm & lt_mask);
+                act = false;
+            }
+            if (lane == leader) wcnt[w][e0] = __popcll(mm);
+        }
+        __syncthreads();
+        if (valid) {
+            int rank = running[ej] + rank_w;
+            for (int v = 0; v < w; ++v) rank += wcnt[v][ej];
             if (C < 0 || rank < C) {
-                const int row = off + (int)rank;
+                const int row = off[ej] + rank;
                 row_of_slot[j] = row;
                 token_of_row[row] = (int)(j / k);
                 dropped[j] = 0;
@@ -89,16 +130,21 @@ __global__ __launch_bounds__(DP_THREADS) void dispatch_kernel(
                 dropped[j] = 1;
             }
         }
-        base += btot;
-        __syncthreads();  // wsum is rewritten by the next chunk
+        __syncthreads();
+        if (tid < E) {
+            int add = 0;
+            for (int v = 0; v < DP_THREADS / 64; ++v) add += wcnt[v][tid];
+            running[tid] += add;
+        }
+        __syncthreads();
     }
     // rows past the last kept one hold no token
-    for (int64_t r = (int64_t)total + (int64_t)e * DP_THREADS + tid; r < Tk;
-         r += (int64_t)E * DP_THREADS)
+    for (int64_t r = (int64_t)sh_total + (int64_t)chunk * DP_THREADS + tid; r < Tk;
+         r += (int64_t)nchunks * DP_THREADS)
         token_of_row[r] = -1;
 }
 
-// One wave per permuted row; row_bytes is a multiple of VEC.
+// One wave per permuted row; row_bytes is a multiple of sizeof(V).
 template <typename V>
 __global__ __launch_bounds__(256) void gather_kernel(const char *__restrict__ x,
                                                      const int32_t *__restrict__ token_of_row,
@@ -117,11 +163,22 @@ __global__ __launch_bounds__(256) void gather_kernel(const char *__restrict__ x,
 
 }  // namespace
 
+int dispatch_chunk(const Shape &s) { return s.Tk() >= 32768 ? 4 * DP_THREADS : DP_THREADS; }
+int dispatch_chunks(const Shape &s) {
+    return (int)((s.Tk() + dispatch_chunk(s) - 1) / dispatch_chunk(s));
+}
+
 hipError_t launch_dispatch(const Shape &s, const int32_t *topk_idx, int32_t *routed,
                            int32_t *kept, int32_t *offsets, int32_t *row_of_slot,
-                           int32_t *token_of_row, uint8_t *dropped, hipStream_t st) {
-    hipLaunchKernelGGL(dispatch_kernel, dim3(s.E), dim3(DP_THREADS), 0, st, topk_idx, s.Tk(), s.k,
-                       s.E, s.C, routed, kept, offsets, row_of_slot, token_of_row, dropped);
+                           int32_t *token_of_row, uint8_t *dropped, int32_t *chunk_counts,
+                           hipStream_t st) {
+    const int nch = dispatch_chunks(s);
+    const int chunk = dispatch_chunk(s);
+    hipLaunchKernelGGL(dispatch_count_kernel, dim3(nch), dim3(DP_THREADS), 0, st, topk_idx, s.Tk(),
+                       s.E, chunk, chunk_counts);
+    hipLaunchKernelGGL(dispatch_rank_kernel, dim3(nch), dim3(DP_THREADS), 0, st, topk_idx, s.Tk(),
+                       s.k, s.E, s.C, chunk, nch, (const int32_t *)chunk_counts, routed, kept,
+                       offsets, row_of_slot, token_of_row, dropped);
     return hipGetLastError();
 }
 

@@ -399,67 +399,79 @@ __global__ __launch_bounds__(256) void gemm_bf16_big_kernel(
 
 // ---- skinny row groups (decode batches): weight streaming ----------------
 //
-// gemm_bf16_skinny_kernel, for experts with at most 32 rows and K a
-// multiple of 128.  One wave per (expert, 16 weight rows) -- for SwiGLU the
-// same 16 rows of W1 and of W3.  The wave streams its weight rows over K in
-// 128-wide chunks, PF chunks in flight in a register ring (16-byte loads),
-// and multiplies them with the expert's rows of A (at most 32, read from
-// L2 one chunk ahead) on v_mfma_f32_16x16x32_bf16.  Within a chunk, lane
-// l = 16g + n holds the 64 contiguous bytes k = 32g .. 32g+31 of its row,
-// and MFMA j of the chunk takes k = 32g + 8j .. +8 from both operands: the
-// same permutation of k on both sides, so every product and its partner
-// meet as in the plain order.  MFMA 16x16x32 accumulator: lane l holds
-// rows 4*(l/16) + r, column l % 16.  Experts with no rows exit at once.
+// gemm_bf16_skinny_kernel, for experts with at most 16*MT rows and K a
+// multiple of 128.  One wave per (expert, 16*NT weight rows) -- for SwiGLU
+// the same rows of W1 and of W3.  The wave streams its weight rows over K
+// in 128-wide chunks, PF chunks in flight in a register ring (16-byte
+// loads), and multiplies them with the expert's rows of A (read from L2
+// one chunk ahead; only the 16-row tiles the expert fills) on
+// v_mfma_f32_16x16x32_bf16.  Within a chunk, lane l = 16g + n holds the 64
+// contiguous bytes k = 32g .. 32g+31 of its row, and MFMA j of the chunk
+// takes k = 32g + 8j .. +8 from both operands: the same permutation of k on
+// both sides, so every product meets its partner as in the plain order.
+// MFMA 16x16x32 accumulator: lane l holds rows 4*(l/16) + r, column l % 16.
+// Experts with no rows exit at once.
 constexpr int SK_KC = 128;
-constexpr int SK_MAXROWS = 32;
 
-template <int PF, bool DUAL, int ACT, bool OUT_BF16>
+template <int MT, int NT, int PF, bool DUAL, int ACT, bool OUT_BF16>
 __global__ __launch_bounds__(64) void gemm_bf16_skinny_kernel(
     const uint16_t *__restrict__ A, const int32_t *__restrict__ offsets, int E,
     const uint16_t *__restrict__ B1, const uint16_t *__restrict__ B3, void *__restrict__ C,
     int N, int K) {
     typedef float f32x4_t __attribute__((ext_vector_type(4)));
+    // chunk ch sits in B slot ch % PF and A slot ch % 2; the unrolled loop
+    // below indexes both by its static position sl, which matches only when
+    // PF is even
+    static_assert(PF % 2 == 0, "the A double buffer needs an even ring length");
     constexpr int NB = DUAL ? 2 : 1;
-    const int ntile = (N + 15) / 16;
+    const int ntile = (N + 16 * NT - 1) / (16 * NT);
     const int e = blockIdx.x / ntile;
-    const int n0 = (blockIdx.x % ntile) * 16;
+    const int n0 = (blockIdx.x % ntile) * 16 * NT;
     if (e >= E) return;
     const int lo = offsets[e], M = offsets[e + 1] - lo;
     if (M <= 0) return;
     const int lane = threadIdx.x;
     const int n = lane & 15, g = lane >> 4;
-    const bool two = M > 16;  // second 16-row tile of A in use (wave-uniform)
+    const int nm = min(MT, (M + 15) / 16);  // 16-row tiles of A in use (wave-uniform)
 
-    const uint16_t *a_row[2];
-    a_row[0] = A + (int64_t)(lo + min(n, M - 1)) * K + g * 32;
-    a_row[1] = A + (int64_t)(lo + min(n + 16, M - 1)) * K + g * 32;
-    const uint16_t *b_row[NB];
-    b_row[0] = B1 + ((int64_t)e * N + min(n0 + n, N - 1)) * K + g * 32;
-    if (DUAL) b_row[NB - 1] = B3 + ((int64_t)e * N + min(n0 + n, N - 1)) * K + g * 32;
-
-    f32x4_t acc[2][NB];
+    const uint16_t *a_row[MT];
 #pragma unroll
-    for (int m = 0; m < 2; ++m)
+    for (int m = 0; m < MT; ++m) a_row[m] = A + (int64_t)(lo + min(m * 16 + n, M - 1)) * K + g * 32;
+    const uint16_t *b_row[NB][NT];
 #pragma unroll
-        for (int q = 0; q < NB; ++q) acc[m][q] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int q = 0; q < NB; ++q)
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+            b_row[q][t] = ((DUAL && q) ? B3 : B1) +
+                          ((int64_t)e * N + min(n0 + t * 16 + n, N - 1)) * K + g * 32;
 
-    uint4 rb[PF][NB][4];
-    uint4 ra[2][2][4];
+    f32x4_t acc[MT][NB][NT];
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+        for (int q = 0; q < NB; ++q)
+#pragma unroll
+            for (int t = 0; t < NT; ++t) acc[m][q][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    uint4 rb[PF][NB][NT][4];
+    uint4 ra[2][MT][4];
     const int nch = K / SK_KC;
     auto load_b = [&](int slot, int ch) {
 #pragma unroll
         for (int q = 0; q < NB; ++q)
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
-                rb[slot][q][j] = *(const uint4 *)(b_row[q] + (int64_t)ch * SK_KC + j * 8);
+            for (int t = 0; t < NT; ++t)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    rb[slot][q][t][j] = *(const uint4 *)(b_row[q][t] + (int64_t)ch * SK_KC + j * 8);
     };
     auto load_a = [&](int slot, int ch) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) ra[slot][0][j] = *(const uint4 *)(a_row[0] + (int64_t)ch * SK_KC + j * 8);
-        if (two)
+        for (int m = 0; m < MT; ++m)
+            if (m < nm)
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
-                ra[slot][1][j] = *(const uint4 *)(a_row[1] + (int64_t)ch * SK_KC + j * 8);
+                for (int j = 0; j < 4; ++j)
+                    ra[slot][m][j] = *(const uint4 *)(a_row[m] + (int64_t)ch * SK_KC + j * 8);
     };
 #pragma unroll
     for (int p = 0; p < PF - 1; ++p)
@@ -475,32 +487,38 @@ __global__ __launch_bounds__(64) void gemm_bf16_skinny_kernel(
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
 #pragma unroll
-                    for (int q = 0; q < NB; ++q) {
-                        const bf16x8_t b = __builtin_bit_cast(bf16x8_t, rb[sl][q][j]);
-                        acc[0][q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                            __builtin_bit_cast(bf16x8_t, ra[sl & 1][0][j]), b, acc[0][q], 0, 0, 0);
-                        if (two)
-                            acc[1][q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                                __builtin_bit_cast(bf16x8_t, ra[sl & 1][1][j]), b, acc[1][q], 0, 0, 0);
-                    }
+                    for (int q = 0; q < NB; ++q)
+#pragma unroll
+                        for (int t = 0; t < NT; ++t) {
+                            const bf16x8_t b = __builtin_bit_cast(bf16x8_t, rb[sl][q][t][j]);
+#pragma unroll
+                            for (int m = 0; m < MT; ++m)
+                                if (m < nm)
+                                    acc[m][q][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                                        __builtin_bit_cast(bf16x8_t, ra[sl & 1][m][j]), b,
+                                        acc[m][q][t], 0, 0, 0);
+                        }
             }
         }
     }
-    const int col = n0 + n;
 #pragma unroll
-    for (int m = 0; m < 2; ++m)
+    for (int t = 0; t < NT; ++t) {
+        const int col = n0 + t * 16 + n;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int row = m * 16 + 4 * g + r;
-            if (row < M && col < N) {
-                const float v = apply_act(ACT, acc[m][0][r], DUAL ? acc[m][NB - 1][r] : 0.f);
-                const int64_t o = (int64_t)(lo + row) * N + col;
-                if (OUT_BF16)
-                    ((__bf16 *)C)[o] = (__bf16)v;
-                else
-                    ((float *)C)[o] = v;
+        for (int m = 0; m < MT; ++m)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int row = m * 16 + 4 * g + r;
+                if (row < M && col < N) {
+                    const float v = apply_act(ACT, acc[m][0][t][r], DUAL ? acc[m][NB - 1][t][r] : 0.f);
+                    const int64_t o = (int64_t)(lo + row) * N + col;
+                    if (OUT_BF16)
+                        ((__bf16 *)C)[o] = (__bf16)v;
+                    else
+                        ((float *)C)[o] = v;
+                }
             }
-        }
+    }
 }
 
 // ---- fp32 path -----------------------------------------------------------
@@ -605,25 +623,38 @@ hipError_t launch_big(const Shape &s, const void *A, const int32_t *offsets, con
     return hipGetLastError();
 }
 
-template <int PF, bool DUAL, int ACT, bool OUT_BF16>
+template <int MT, int NT, int PF, bool DUAL, int ACT, bool OUT_BF16>
 hipError_t launch_skinny(const Shape &s, const void *A, const int32_t *offsets, const void *B1,
                          const void *B3, void *C, int N, int K, hipStream_t st) {
-    const unsigned blocks = (unsigned)s.E * (unsigned)((N + 15) / 16);
-    hipLaunchKernelGGL((gemm_bf16_skinny_kernel<PF, DUAL, ACT, OUT_BF16>), dim3(blocks), dim3(64), 0,
-                       st, (const uint16_t *)A, offsets, s.E, (const uint16_t *)B1,
+    const unsigned blocks = (unsigned)s.E * (unsigned)((N + 16 * NT - 1) / (16 * NT));
+    hipLaunchKernelGGL((gemm_bf16_skinny_kernel<MT, NT, PF, DUAL, ACT, OUT_BF16>), dim3(blocks),
+                       dim3(64), 0, st, (const uint16_t *)A, offsets, s.E, (const uint16_t *)B1,
                        (const uint16_t *)B3, C, N, K);
     return hipGetLastError();
 }
 
-inline bool use_skinny(const Shape &s, int K) {
-    return max_rows_per_expert(s) <= SK_MAXROWS && K % SK_KC == 0;
+// 16-row tiles of A the streaming kernel needs (0: it does not apply).
+inline int skinny_tiles(const Shape &s, int K) {
+    if (K % SK_KC != 0) return 0;
+    const int64_t m = max_rows_per_expert(s);
+    if (m <= 32) return 2;
+    if (m <= 48) return 3;
+    return 0;
+}
+
+template <bool DUAL, int ACT, bool OUT_BF16>
+hipError_t launch_skinny_any(const Shape &s, int mt, const void *A, const int32_t *offsets,
+                             const void *B1, const void *B3, void *C, int N, int K,
+                             hipStream_t st) {
+    if (mt == 2) return launch_skinny<2, 1, 4, DUAL, ACT, OUT_BF16>(s, A, offsets, B1, B3, C, N, K, st);
+    return launch_skinny<3, DUAL ? 1 : 2, 4, DUAL, ACT, OUT_BF16>(s, A, offsets, B1, B3, C, N, K, st);
 }
 
 template <int ACT, bool DUAL>
 hipError_t launch_up_bf16(const Shape &s, const void *A, const int32_t *offsets, const void *W1,
                           const void *W3, void *H, hipStream_t st) {
-    if (use_skinny(s, s.d))
-        return launch_skinny<4, DUAL, ACT, true>(s, A, offsets, W1, W3, H, s.d_ff, s.d, st);
+    if (const int mt = skinny_tiles(s, s.d))
+        return launch_skinny_any<DUAL, ACT, true>(s, mt, A, offsets, W1, W3, H, s.d_ff, s.d, st);
     switch (pick_bm(s, s.d)) {
     case BIG_BM: return launch_big<DUAL, ACT, true>(s, A, offsets, W1, W3, H, s.d_ff, s.d, st);
     case 128: return launch_gemm<128, 128, 2, 2, DUAL, ACT, true>(s, A, offsets, W1, W3, H, s.d_ff, s.d, st);
@@ -659,8 +690,9 @@ hipError_t launch_expert_down(const Shape &s, const void *H, const int32_t *offs
                            s.d_ff);
         return hipGetLastError();
     }
-    if (use_skinny(s, s.d_ff))
-        return launch_skinny<4, false, ACT_NONE, false>(s, H, offsets, W2, nullptr, y_perm, s.d, s.d_ff, st);
+    if (const int mt = skinny_tiles(s, s.d_ff))
+        return launch_skinny_any<false, ACT_NONE, false>(s, mt, H, offsets, W2, nullptr, y_perm, s.d,
+                                                          s.d_ff, st);
     switch (pick_bm(s, s.d_ff)) {
     case BIG_BM: return launch_big<false, ACT_NONE, false>(s, H, offsets, W2, nullptr, y_perm, s.d, s.d_ff, st);
     case 128: return launch_gemm<128, 128, 2, 2, false, ACT_NONE, false>(s, H, offsets, W2, nullptr, y_perm, s.d, s.d_ff, st);

@@ -52,8 +52,9 @@ int check_desc(const moe_desc *desc, Shape *s) {
 
 // Workspace layout; every region starts on a 256-byte boundary.
 struct Layout {
-    size_t part_P, part_lse2;                       // router partial sums
+    size_t part_P, part_lse2, fP;                   // router partial sums, f_e * P_e
     size_t wsplit, part_logits;                     // bf16 router: split W_r, logit slices
+    size_t chunk_counts;                            // dispatch: per-chunk expert histograms
     size_t topk_idx, gates, routed, kept, offsets;  // moe_forward's optional outputs
     size_t row_of_slot, token_of_row, dropped, stats;
     size_t x_perm, H, y_perm;
@@ -75,10 +76,12 @@ Layout layout(const Shape &s) {
     };
     L.part_P = take(nblk * s.E * sizeof(float));
     L.part_lse2 = take(nblk * sizeof(float));
+    L.fP = take((size_t)s.E * sizeof(double));
     if (s.dtype == MOE_DTYPE_BF16) {
         L.wsplit = take(3 * (size_t)moe::route_epad(s) * (size_t)s.d * 2);
         L.part_logits = take((size_t)moe::route_nsplit(s) * (size_t)s.T * (size_t)s.E * 4);
     }
+    L.chunk_counts = take((size_t)moe::dispatch_chunks(s) * (size_t)s.E * 4);
     L.topk_idx = take(Tk * 4);
     L.gates = take(Tk * 4);
     L.routed = take((size_t)s.E * 4);
@@ -162,7 +165,8 @@ int moe_route(const moe_desc *desc, const void *x, const float *W_r, const float
                               at<float>(ws, L.part_lse2), at<uint16_t>(ws, L.wsplit),
                               at<float>(ws, L.part_logits), st));
     MOE_TRY(moe::launch_route_finalize(s, topk_idx, at<float>(ws, L.part_P),
-                                       at<float>(ws, L.part_lse2), stats, st));
+                                       at<float>(ws, L.part_lse2), stats,
+                                       at<double>(ws, L.fP), st));
     return MOE_OK;
 }
 
@@ -176,11 +180,11 @@ int moe_dispatch(const moe_desc *desc, const void *x, const int32_t *topk_idx,
     if (!x || !topk_idx || !routed_counts || !kept_counts || !offsets || !row_of_slot ||
         !token_of_row || !dropped || !x_perm)
         return MOE_ERR_INVALID_ARG;
-    (void)ws;
-    (void)ws_bytes;  // no scratch needed
+    if ((rc = check_ws(s, ws, ws_bytes)) != MOE_OK) return rc;
+    const Layout L = layout(s);
     hipStream_t st = (hipStream_t)stream;
     MOE_TRY(moe::launch_dispatch(s, topk_idx, routed_counts, kept_counts, offsets, row_of_slot,
-                                 token_of_row, dropped, st));
+                                 token_of_row, dropped, at<int32_t>(ws, L.chunk_counts), st));
     MOE_TRY(moe::launch_gather(s, x, token_of_row, offsets, x_perm, st));
     return MOE_OK;
 }
@@ -245,10 +249,11 @@ int moe_forward(const moe_desc *desc, const void *x, const float *W_r, const flo
                               at<float>(ws, L.part_logits), st));
     MOE_TRY(ev.record(st));
     MOE_TRY(moe::launch_route_finalize(s, topk_idx, at<float>(ws, L.part_P),
-                                       at<float>(ws, L.part_lse2), stats, st));
+                                       at<float>(ws, L.part_lse2), stats,
+                                       at<double>(ws, L.fP), st));
     MOE_TRY(ev.record(st));
     MOE_TRY(moe::launch_dispatch(s, topk_idx, routed_counts, kept_counts, offsets, row_of_slot,
-                                 token_of_row, dropped, st));
+                                 token_of_row, dropped, at<int32_t>(ws, L.chunk_counts), st));
     MOE_TRY(ev.record(st));
     MOE_TRY(moe::launch_gather(s, x, token_of_row, offsets, x_perm, st));
     MOE_TRY(ev.record(st));

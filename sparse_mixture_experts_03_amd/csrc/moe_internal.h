@@ -18,9 +18,13 @@ struct Shape {
     int64_t Tk() const { return (int64_t)T * k; }
 };
 
-// ---- router: one block per ROUTE_TOKENS tokens -------------------------
-constexpr int ROUTE_TOKENS = 32;
-inline int route_blocks(const Shape &s) { return (s.T + ROUTE_TOKENS - 1) / ROUTE_TOKENS; }
+// ---- router: the per-token epilogue runs one block per route_tile() tokens
+// (32 for fp32 activations, whose block also computes the logits; 8 for
+// bf16, so that many waves work on the tokens at once)
+constexpr int ROUTE_TOKENS_F32 = 32;
+constexpr int ROUTE_TOKENS_BF16 = 8;
+inline int route_tile(const Shape &s) { return s.dtype == 1 ? ROUTE_TOKENS_BF16 : ROUTE_TOKENS_F32; }
+inline int route_blocks(const Shape &s) { return (s.T + route_tile(s) - 1) / route_tile(s); }
 
 // bf16 path: router matrix split into 3 bf16 terms [3][E_pad][d], and the
 // logits computed in route_nsplit() slices of d, each route_slice() wide.
@@ -32,12 +36,19 @@ hipError_t launch_route(const Shape &s, const void *x, const float *Wr, const fl
                         const float *noise, int32_t *topk_idx, float *gates, float *part_P,
                         float *part_lse2, uint16_t *wsplit, float *part_logits, hipStream_t st);
 hipError_t launch_route_finalize(const Shape &s, const int32_t *topk_idx, const float *part_P,
-                                 const float *part_lse2, float *stats, hipStream_t st);
+                                 const float *part_lse2, float *stats, double *fP,
+                                 hipStream_t st);
 
 // ---- dispatch: capacity, stable permutation, gather ----------------------
+// Assignments per dispatch block (256 per round; more rounds when T*k is
+// large); per-chunk expert histograms [chunks][E] int32 live in the
+// workspace.
+int dispatch_chunk(const Shape &s);
+int dispatch_chunks(const Shape &s);
 hipError_t launch_dispatch(const Shape &s, const int32_t *topk_idx, int32_t *routed,
                            int32_t *kept, int32_t *offsets, int32_t *row_of_slot,
-                           int32_t *token_of_row, uint8_t *dropped, hipStream_t st);
+                           int32_t *token_of_row, uint8_t *dropped, int32_t *chunk_counts,
+                           hipStream_t st);
 hipError_t launch_gather(const Shape &s, const void *x, const int32_t *token_of_row,
                          const int32_t *offsets, void *x_perm, hipStream_t st);
 

@@ -31,8 +31,8 @@
 // reductions, top-k by k arg-max reductions over 64-bit keys (orderable
 // logit bits, then the complement of the index, so a tie goes to the lower
 // index), gates, and per-block partial sums of p (per expert) and of lse^2
-// in a fixed order.  route_finalize_kernel reduces the partials in double,
-// in block order, and counts top choices.
+// in a fixed order.  route_stats_kernel and route_aux_kernel reduce the
+// partials in double in a fixed order and count top choices.
 #include "moe_internal.h"
 
 namespace moe {
@@ -74,8 +74,9 @@ __device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long v)
     return v;
 }
 
-// The per-token epilogue over a block's logits tile hl[ROUTE_TOKENS][.]
+// The per-token epilogue over a block's logits tile hl[TILE][.]
 // (already synchronised).  Every thread of the block must call it.
+template <int TILE>
 __device__ void softmax_topk_block(const float (*hl)[RT_EMAX + 1], int t0, int T, int E, int k,
                                    int gate_switch, int32_t *__restrict__ topk_idx,
                                    float *__restrict__ gates, float *__restrict__ part_P,
@@ -87,7 +88,7 @@ __device__ void softmax_topk_block(const float (*hl)[RT_EMAX + 1], int t0, int T
     const int e0 = lane, e1 = lane + 64;
     const bool v0 = e0 < E, v1 = e1 < E;
     float psum0 = 0.f, psum1 = 0.f, lsum = 0.f;
-    for (int r = w; r < ROUTE_TOKENS; r += 4) {
+    for (int r = w; r < TILE; r += 4) {
         const int t = t0 + r;
         if (t >= T) break;
         const float h0 = v0 ? hl[r][e0] : -INFINITY;
@@ -150,12 +151,13 @@ __global__ __launch_bounds__(RT_THREADS) void route_f32_kernel(
     const float *__restrict__ noise, int T, int d, int E, int k, int gate_switch,
     int32_t *__restrict__ topk_idx, float *__restrict__ gates, float *__restrict__ part_P,
     float *__restrict__ part_lse2) {
-    __shared__ float xs[ROUTE_TOKENS][RT_DC + 1];
+    constexpr int TILE = ROUTE_TOKENS_F32;
+    __shared__ float xs[TILE][RT_DC + 1];
     __shared__ float wsh[RT_EMAX][RT_DC + 1];
-    __shared__ float hl[ROUTE_TOKENS][RT_EMAX + 1];
+    __shared__ float hl[TILE][RT_EMAX + 1];
 
     const int tid = threadIdx.x;
-    const int t0 = blockIdx.x * ROUTE_TOKENS;
+    const int t0 = blockIdx.x * TILE;
     const int tg = tid >> 5;  // 8 token groups of 4 tokens
     const int eg = tid & 31;  // 32 expert groups; experts eg + 32*j
 
@@ -166,7 +168,7 @@ __global__ __launch_bounds__(RT_THREADS) void route_f32_kernel(
         for (int j = 0; j < 4; ++j) acc[i][j] = 0.f;
 
     for (int c0 = 0; c0 < d; c0 += RT_DC) {
-        for (int i = tid; i < ROUTE_TOKENS * RT_DC; i += RT_THREADS) {
+        for (int i = tid; i < TILE * RT_DC; i += RT_THREADS) {
             int r = i / RT_DC, c = i % RT_DC;
             int t = t0 + r;
             xs[r][c] = (t < T && c0 + c < d) ? x[(int64_t)t * d + c0 + c] : 0.f;
@@ -205,7 +207,7 @@ __global__ __launch_bounds__(RT_THREADS) void route_f32_kernel(
         }
     }
     __syncthreads();
-    softmax_topk_block(hl, t0, T, E, k, gate_switch, topk_idx, gates, part_P, part_lse2);
+    softmax_topk_block<TILE>(hl, t0, T, E, k, gate_switch, topk_idx, gates, part_P, part_lse2);
 }
 
 // ---- bf16 activations: exact three-term split + MFMA ---------------------
@@ -336,59 +338,101 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const uint16_t *__re
         }
 }
 
+// The block's tile of logits is contiguous in every slice ([t0*E, +8*E)),
+// so each thread sums up to 4 entries over the slices with all its loads
+// of one slice in flight together; the slices are added in slice order.
 __global__ __launch_bounds__(RT_THREADS) void route_epilogue_kernel(
     const float *__restrict__ part, int nsplit, const float *__restrict__ bias,
     const float *__restrict__ noise, int T, int E, int k, int gate_switch,
     int32_t *__restrict__ topk_idx, float *__restrict__ gates, float *__restrict__ part_P,
     float *__restrict__ part_lse2) {
-    __shared__ float hl[ROUTE_TOKENS][RT_EMAX + 1];
-    const int t0 = blockIdx.x * ROUTE_TOKENS;
-    for (int i = threadIdx.x; i < ROUTE_TOKENS * E; i += RT_THREADS) {
-        const int r = i / E, e = i % E, t = t0 + r;
-        float h = 0.f;
-        if (t < T) {
-            for (int s = 0; s < nsplit; ++s) h += part[((int64_t)s * T + t) * E + e];
-            if (bias) h += bias[e];
-            if (noise) h += noise[(int64_t)t * E + e];
+    constexpr int TILE = ROUTE_TOKENS_BF16;
+    __shared__ float hl[TILE][RT_EMAX + 1];
+    constexpr int MAXQ = TILE * RT_EMAX / RT_THREADS;
+    const int t0 = blockIdx.x * TILE;
+    const int tid = threadIdx.x;
+    const int64_t base = (int64_t)t0 * E;
+    const int npairs = min(TILE, T - t0) * E;
+    float h[MAXQ];
+#pragma unroll
+    for (int q = 0; q < MAXQ; ++q) h[q] = 0.f;
+    for (int sl = 0; sl < nsplit; ++sl) {
+        const float *ps = part + (int64_t)sl * T * E + base;
+#pragma unroll
+        for (int q = 0; q < MAXQ; ++q) {
+            const int i = tid + q * RT_THREADS;
+            if (i < npairs) h[q] += ps[i];
         }
-        hl[r][e] = h;
+    }
+#pragma unroll
+    for (int q = 0; q < MAXQ; ++q) {
+        const int i = tid + q * RT_THREADS;
+        if (i < npairs) {
+            const int r = i / E, e = i - r * E;
+            float v = h[q];
+            if (bias) v += bias[e];
+            if (noise) v += noise[base + i];
+            hl[r][e] = v;
+        }
     }
     __syncthreads();
-    softmax_topk_block(hl, t0, T, E, k, gate_switch, topk_idx, gates, part_P, part_lse2);
+    softmax_topk_block<TILE>(hl, t0, T, E, k, gate_switch, topk_idx, gates, part_P, part_lse2);
 }
 
-__global__ __launch_bounds__(256) void route_finalize_kernel(
+// Statistics, in two kernels and in double, every sum in a fixed order.
+// route_stats_kernel: block e < E reduces expert e's block partials of p
+// (thread t takes blocks t, t+256, ...; then the 256 thread sums are added
+// in thread order) and counts the tokens whose top choice is e; block E
+// reduces the lse^2 partials the same way.  route_aux_kernel (one block)
+// forms aux = E * sum_e f_e P_e.
+__device__ __forceinline__ double block_sum_fixed(double v, double *red) {
+    const int tid = threadIdx.x;
+    red[tid] = v;
+    __syncthreads();
+    double total = 0.0;
+    if (tid == 0)
+        for (int i = 0; i < 256; ++i) total += red[i];
+    return total;  // valid in thread 0
+}
+
+__global__ __launch_bounds__(256) void route_stats_kernel(
     const int32_t *__restrict__ topk_idx, const float *__restrict__ part_P,
     const float *__restrict__ part_lse2, int T, int E, int k, int nblk,
-    float *__restrict__ stats) {
-    __shared__ int cnt[RT_EMAX];
-    __shared__ double fP[RT_EMAX];
-    __shared__ double zsh;
+    float *__restrict__ stats, double *__restrict__ fP) {
+    __shared__ double red[256];
+    __shared__ int cnt[4];
     const int tid = threadIdx.x;
-    if (tid < RT_EMAX) cnt[tid] = 0;
-    __syncthreads();
-    for (int t = tid; t < T; t += blockDim.x) atomicAdd(&cnt[topk_idx[(int64_t)t * k]], 1);
-    if (tid == 64) {
+    const int e = blockIdx.x;
+    if (e == E) {
         double z = 0.0;
-        for (int b = 0; b < nblk; ++b) z += (double)part_lse2[b];
-        zsh = z / (double)T;
+        for (int b = tid; b < nblk; b += 256) z += (double)part_lse2[b];
+        z = block_sum_fixed(z, red);
+        if (tid == 0) stats[2 * E + 1] = (float)(z / (double)T);
+        return;
     }
-    __syncthreads();
-    if (tid < E) {
-        double P = 0.0;
-        for (int b = 0; b < nblk; ++b) P += (double)part_P[(int64_t)b * E + tid];
-        P /= (double)T;
-        double f = (double)cnt[tid] / (double)T;
-        stats[tid] = (float)f;
-        stats[E + tid] = (float)P;
-        fP[tid] = f * P;
-    }
-    __syncthreads();
+    double acc = 0.0;
+#pragma unroll 4
+    for (int b = tid; b < nblk; b += 256) acc += (double)part_P[(int64_t)b * E + e];
+    int c = 0;
+    for (int t = tid; t < T; t += 256) c += topk_idx[(int64_t)t * k] == e;
+    // integer count: the order of the additions does not matter
+    for (int o = 32; o > 0; o >>= 1) c += __shfl_xor(c, o);
+    if ((tid & 63) == 0) cnt[tid >> 6] = c;
+    const double P = block_sum_fixed(acc, red) / (double)T;
     if (tid == 0) {
+        const double f = (double)(cnt[0] + cnt[1] + cnt[2] + cnt[3]) / (double)T;
+        stats[e] = (float)f;
+        stats[E + e] = (float)P;
+        fP[e] = f * P;
+    }
+}
+
+__global__ __launch_bounds__(64) void route_aux_kernel(const double *__restrict__ fP, int E,
+                                                       float *__restrict__ stats) {
+    if (threadIdx.x == 0) {
         double a = 0.0;
         for (int i = 0; i < E; ++i) a += fP[i];
         stats[2 * E] = (float)((double)E * a);
-        stats[2 * E + 1] = (float)zsh;
     }
 }
 
@@ -456,9 +500,11 @@ hipError_t launch_route(const Shape &s, const void *x, const float *Wr, const fl
 }
 
 hipError_t launch_route_finalize(const Shape &s, const int32_t *topk_idx, const float *part_P,
-                                 const float *part_lse2, float *stats, hipStream_t st) {
-    hipLaunchKernelGGL(route_finalize_kernel, dim3(1), dim3(256), 0, st, topk_idx, part_P,
-                       part_lse2, s.T, s.E, s.k, route_blocks(s), stats);
+                                 const float *part_lse2, float *stats, double *fP,
+                                 hipStream_t st) {
+    hipLaunchKernelGGL(route_stats_kernel, dim3(s.E + 1), dim3(256), 0, st, topk_idx, part_P,
+                       part_lse2, s.T, s.E, s.k, route_blocks(s), stats, fP);
+    hipLaunchKernelGGL(route_aux_kernel, dim3(1), dim3(64), 0, st, (const double *)fP, s.E, stats);
     return hipGetLastError();
 }
 

@@ -50,6 +50,12 @@ SMALL = {
                                      noise_std=0.0),
     # up projection with a partial last column tile (136 = 8*16 + 8)
     "skinny_partial_n": W["mixtral_decode"].with_(name="skinny_partial_n", T=16, d=128, d_ff=136, E=4),
+    # streaming kernel with three 16-row tiles (capacity 47 rows): GELU with
+    # two column tiles per wave, and SwiGLU
+    "skinny_mt3_gelu": W["switch"].with_(name="skinny_mt3_gelu", T=600, d=256, d_ff=384, E=16,
+                                         noise_std=1.0 / 16),
+    "skinny_mt3_swiglu": W["mixtral_decode"].with_(name="skinny_mt3_swiglu", T=300, d=128, d_ff=256,
+                                                   E=8, k=1, cf=1.25),
     # Switch gate with k = 2, 64-row SwiGLU tiles
     "switch_k2": W["mixtral_prefill"].with_(name="switch_k2", T=500, d=128, d_ff=256, E=16, k=2,
                                             gate="switch", x_rmsnorm=False),
