@@ -8,10 +8,10 @@
 // nothing here, and a token dropped from every expert gets 0 (its residual,
 // outside the layer, carries it).
 //
-// combine_kernel: one wave per (token, 256-column chunk), grid-stride; each
-// lane owns 4 consecutive columns and sums the k slots in slot order in
-// fp32, then stores fp32 or bf16 (a scalar variant, one wave per token,
-// serves widths that are not a multiple of 4).  Every output element is
+// combine_kernel: one wave per token, grid-stride; each lane owns 4
+// consecutive columns of every 256-column chunk and sums the k slots in
+// slot order in fp32, then stores fp32 or bf16 (a scalar variant serves
+// widths that are not a multiple of 4).  Every output element is
 // written exactly once, so no memset and no atomics are needed.
 #include "moe_internal.h"
 
@@ -26,15 +26,13 @@ __global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ 
                                                       int d, int k, void *__restrict__ y) {
     const int lane = threadIdx.x & 63;
     if (VEC4) {
-        // one wave per (token, 256-column chunk)
-        const int nch = (d + 255) / 256;
-        for (int64_t it = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); it < (int64_t)T * nch;
-             it += (int64_t)gridDim.x * 4) {
-            const int t = (int)(it / nch);
-            const int c = (int)(it - (int64_t)t * nch) * 256 + lane * 4;
+        // one wave per token: its k rows and gates are read once, then the
+        // 256-column chunks follow, four at a time with their loads in flight
+        for (int t = blockIdx.x * 4 + (threadIdx.x >> 6); t < T; t += gridDim.x * 4) {
             const int32_t *rs = row_of_slot + (int64_t)t * k;
             const float *gs = gates + (int64_t)t * k;
-            if (c < d) {
+#pragma unroll 4
+            for (int c = lane * 4; c < d; c += 256) {
                 float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
                 for (int s = 0; s < k; ++s) {
                     const int r = rs[s];
@@ -83,8 +81,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ 
 hipError_t launch_combine(const Shape &s, const float *y_perm, const int32_t *row_of_slot,
                           const float *gates, void *y, hipStream_t st) {
     const bool v4 = (s.d % 4) == 0;
-    int64_t items = v4 ? (int64_t)s.T * ((s.d + 255) / 256) : (int64_t)s.T;
-    int64_t blocks = (items + 3) / 4;
+    int64_t blocks = ((int64_t)s.T + 3) / 4;
     if (blocks > 16384) blocks = 16384;
     const bool bf = s.dtype == 1;
     auto kern = bf ? (v4 ? combine_kernel<true, true> : combine_kernel<true, false>)

@@ -400,8 +400,10 @@ __global__ __launch_bounds__(256) void gemm_bf16_big_kernel(
 // ---- skinny row groups (decode batches): weight streaming ----------------
 //
 // gemm_bf16_skinny_kernel, for experts with at most 16*MT rows and K a
-// multiple of 128.  One wave per (expert, 16*NT weight rows) -- for SwiGLU
-// the same rows of W1 and of W3.  The wave streams its weight rows over K
+// multiple of 128.  One block per (expert, 16*NT weight rows) -- for SwiGLU
+// the same rows of W1 and of W3 -- of KS waves, each taking a contiguous
+// range of K (their partial sums are added in wave order through LDS at the
+// end, so the result does not depend on timing).  A wave streams its rows
 // in 128-wide chunks, PF chunks in flight in a register ring (16-byte
 // loads), and multiplies them with the expert's rows of A (read from L2
 // one chunk ahead; only the 16-row tiles the expert fills) on
@@ -413,8 +415,8 @@ __global__ __launch_bounds__(256) void gemm_bf16_big_kernel(
 // Experts with no rows exit at once.
 constexpr int SK_KC = 128;
 
-template <int MT, int NT, int PF, bool DUAL, int ACT, bool OUT_BF16>
-__global__ __launch_bounds__(64) void gemm_bf16_skinny_kernel(
+template <int MT, int NT, int PF, int KS, bool DUAL, int ACT, bool OUT_BF16>
+__global__ __launch_bounds__(64 * KS) void gemm_bf16_skinny_kernel(
     const uint16_t *__restrict__ A, const int32_t *__restrict__ offsets, int E,
     const uint16_t *__restrict__ B1, const uint16_t *__restrict__ B3, void *__restrict__ C,
     int N, int K) {
@@ -424,26 +426,34 @@ __global__ __launch_bounds__(64) void gemm_bf16_skinny_kernel(
     // PF is even
     static_assert(PF % 2 == 0, "the A double buffer needs an even ring length");
     constexpr int NB = DUAL ? 2 : 1;
+    constexpr int NACC = MT * NB * NT * 4;
+    __shared__ float red[KS > 1 ? KS - 1 : 1][NACC][64];
     const int ntile = (N + 16 * NT - 1) / (16 * NT);
     const int e = blockIdx.x / ntile;
     const int n0 = (blockIdx.x % ntile) * 16 * NT;
     if (e >= E) return;
     const int lo = offsets[e], M = offsets[e + 1] - lo;
     if (M <= 0) return;
-    const int lane = threadIdx.x;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int n = lane & 15, g = lane >> 4;
     const int nm = min(MT, (M + 15) / 16);  // 16-row tiles of A in use (wave-uniform)
+    // wave `wave` takes the contiguous chunk range [cb, ce) of K
+    const int nch_all = K / SK_KC;
+    const int cb = (int)((int64_t)wave * nch_all / KS), ce = (int)((int64_t)(wave + 1) * nch_all / KS);
 
     const uint16_t *a_row[MT];
 #pragma unroll
-    for (int m = 0; m < MT; ++m) a_row[m] = A + (int64_t)(lo + min(m * 16 + n, M - 1)) * K + g * 32;
+    for (int m = 0; m < MT; ++m)
+        a_row[m] = A + (int64_t)(lo + min(m * 16 + n, M - 1)) * K + (int64_t)cb * SK_KC + g * 32;
     const uint16_t *b_row[NB][NT];
 #pragma unroll
     for (int q = 0; q < NB; ++q)
 #pragma unroll
         for (int t = 0; t < NT; ++t)
             b_row[q][t] = ((DUAL && q) ? B3 : B1) +
-                          ((int64_t)e * N + min(n0 + t * 16 + n, N - 1)) * K + g * 32;
+                          ((int64_t)e * N + min(n0 + t * 16 + n, N - 1)) * K +
+                          (int64_t)cb * SK_KC + g * 32;
 
     f32x4_t acc[MT][NB][NT];
 #pragma unroll
@@ -455,7 +465,7 @@ __global__ __launch_bounds__(64) void gemm_bf16_skinny_kernel(
 
     uint4 rb[PF][NB][NT][4];
     uint4 ra[2][MT][4];
-    const int nch = K / SK_KC;
+    const int nch = ce - cb;
     auto load_b = [&](int slot, int ch) {
 #pragma unroll
         for (int q = 0; q < NB; ++q)
@@ -476,7 +486,7 @@ __global__ __launch_bounds__(64) void gemm_bf16_skinny_kernel(
 #pragma unroll
     for (int p = 0; p < PF - 1; ++p)
         if (p < nch) load_b(p, p);
-    load_a(0, 0);
+    if (nch > 0) load_a(0, 0);
     for (int c0 = 0; c0 < nch; c0 += PF) {
 #pragma unroll
         for (int sl = 0; sl < PF; ++sl) {
@@ -499,6 +509,35 @@ __global__ __launch_bounds__(64) void gemm_bf16_skinny_kernel(
                                         acc[m][q][t], 0, 0, 0);
                         }
             }
+        }
+    }
+    if (KS > 1) {
+        // waves 1..KS-1 hand their partial sums to wave 0, which adds them
+        // in wave order
+        if (wave > 0) {
+            int i = 0;
+#pragma unroll
+            for (int m = 0; m < MT; ++m)
+#pragma unroll
+                for (int q = 0; q < NB; ++q)
+#pragma unroll
+                    for (int t = 0; t < NT; ++t)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) red[wave - 1][i++][lane] = acc[m][q][t][r];
+        }
+        __syncthreads();
+        if (wave > 0) return;
+#pragma unroll
+        for (int w = 1; w < KS; ++w) {
+            int i = 0;
+#pragma unroll
+            for (int m = 0; m < MT; ++m)
+#pragma unroll
+                for (int q = 0; q < NB; ++q)
+#pragma unroll
+                    for (int t = 0; t < NT; ++t)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) acc[m][q][t][r] += red[w - 1][i++][lane];
         }
     }
 #pragma unroll
@@ -627,9 +666,19 @@ template <int MT, int NT, int PF, bool DUAL, int ACT, bool OUT_BF16>
 hipError_t launch_skinny(const Shape &s, const void *A, const int32_t *offsets, const void *B1,
                          const void *B3, void *C, int N, int K, hipStream_t st) {
     const unsigned blocks = (unsigned)s.E * (unsigned)((N + 16 * NT - 1) / (16 * NT));
-    hipLaunchKernelGGL((gemm_bf16_skinny_kernel<MT, NT, PF, DUAL, ACT, OUT_BF16>), dim3(blocks),
-                       dim3(64), 0, st, (const uint16_t *)A, offsets, s.E, (const uint16_t *)B1,
-                       (const uint16_t *)B3, C, N, K);
+    // split K over the waves of a block when there are too few column tiles
+    // to keep enough weight bytes in flight and K is long (each wave keeps
+    // >= 16 chunks)
+    const int nch = K / SK_KC;
+    if (blocks < 4096 && nch >= 64) {
+        hipLaunchKernelGGL((gemm_bf16_skinny_kernel<MT, NT, PF, 4, DUAL, ACT, OUT_BF16>),
+                           dim3(blocks), dim3(256), 0, st, (const uint16_t *)A, offsets, s.E,
+                           (const uint16_t *)B1, (const uint16_t *)B3, C, N, K);
+    } else {
+        hipLaunchKernelGGL((gemm_bf16_skinny_kernel<MT, NT, PF, 1, DUAL, ACT, OUT_BF16>),
+                           dim3(blocks), dim3(64), 0, st, (const uint16_t *)A, offsets, s.E,
+                           (const uint16_t *)B1, (const uint16_t *)B3, C, N, K);
+    }
     return hipGetLastError();
 }
 
@@ -646,7 +695,7 @@ template <bool DUAL, int ACT, bool OUT_BF16>
 hipError_t launch_skinny_any(const Shape &s, int mt, const void *A, const int32_t *offsets,
                              const void *B1, const void *B3, void *C, int N, int K,
                              hipStream_t st) {
-    if (mt == 2) return launch_skinny<2, 1, 4, DUAL, ACT, OUT_BF16>(s, A, offsets, B1, B3, C, N, K, st);
+    if (mt == 2) return launch_skinny<2, DUAL ? 1 : 2, 4, DUAL, ACT, OUT_BF16>(s, A, offsets, B1, B3, C, N, K, st);
     return launch_skinny<3, DUAL ? 1 : 2, 4, DUAL, ACT, OUT_BF16>(s, A, offsets, B1, B3, C, N, K, st);
 }
 

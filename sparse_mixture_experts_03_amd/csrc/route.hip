@@ -414,6 +414,7 @@ __global__ __launch_bounds__(256) void route_stats_kernel(
 #pragma unroll 4
     for (int b = tid; b < nblk; b += 256) acc += (double)part_P[(int64_t)b * E + e];
     int c = 0;
+#pragma unroll 8
     for (int t = tid; t < T; t += 256) c += topk_idx[(int64_t)t * k] == e;
     // integer count: the order of the additions does not matter
     for (int o = 32; o > 0; o >>= 1) c += __shfl_xor(c, o);
@@ -427,11 +428,14 @@ __global__ __launch_bounds__(256) void route_stats_kernel(
     }
 }
 
-__global__ __launch_bounds__(64) void route_aux_kernel(const double *__restrict__ fP, int E,
-                                                       float *__restrict__ stats) {
+__global__ __launch_bounds__(128) void route_aux_kernel(const double *__restrict__ fP, int E,
+                                                        float *__restrict__ stats) {
+    __shared__ double v[RT_EMAX];
+    if ((int)threadIdx.x < E) v[threadIdx.x] = fP[threadIdx.x];
+    __syncthreads();
     if (threadIdx.x == 0) {
         double a = 0.0;
-        for (int i = 0; i < E; ++i) a += fP[i];
+        for (int i = 0; i < E; ++i) a += v[i];
         stats[2 * E] = (float)((double)E * a);
     }
 }
@@ -504,7 +508,7 @@ hipError_t launch_route_finalize(const Shape &s, const int32_t *topk_idx, const 
                                  hipStream_t st) {
     hipLaunchKernelGGL(route_stats_kernel, dim3(s.E + 1), dim3(256), 0, st, topk_idx, part_P,
                        part_lse2, s.T, s.E, s.k, route_blocks(s), stats, fP);
-    hipLaunchKernelGGL(route_aux_kernel, dim3(1), dim3(64), 0, st, (const double *)fP, s.E, stats);
+    hipLaunchKernelGGL(route_aux_kernel, dim3(1), dim3(128), 0, st, (const double *)fP, s.E, stats);
     return hipGetLastError();
 }
 
