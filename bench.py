@@ -10,9 +10,9 @@ in decode (T=32, 100 steps with fresh tokens each step) is measured in the
 same run and reported in the "decode" object.  Prints one JSON line.
 
 Timing: W untimed warm-up steps, then exactly K steps between two device
-synchronisations.  Per-kernel durations come from HIP events that the
-library records on the launch stream (the descriptor's stage-event hook)
-around the two expert GEMMs only, over the same timed steps.
+synchronisations.  The dominant kernel's duration comes from two HIP
+events that the library records on the launch stream around it (the
+descriptor's stage-event hook), over the same timed steps.
 
 Roofline of the dominant kernel (the expert up-projection, a grouped GEMM
 on bf16 MFMA): algorithmic FLOPs per launch = N_kept * 2 * n_up * d * d_ff
@@ -144,8 +144,9 @@ def run_workload(w, steps, warmup, fresh_x_steps=0, seed=0):
         else:
             desc.stage_events = None
             desc.n_stage_events = 0
-        # only the events around the two expert GEMMs are recorded: each
-        # recorded event separates the kernels around it by a few us
+        # only the two events around the expert up-projection (the dominant
+        # kernel) are recorded: each recorded event separates the kernels
+        # around it by a few us
         B.moe_forward(desc, xs[j], dw["Wr"], dw["bias"], noises[j], dw["W1"], dw["W3"], dw["W2"],
                       out["y"], ws, kept_counts=out["kept_counts"], stats=out["stats"],
                       stream=stream)
@@ -153,8 +154,8 @@ def run_workload(w, steps, warmup, fresh_x_steps=0, seed=0):
     for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
-    timed = (STAGES.index("expert_up"), STAGES.index("expert_down") + 1)
-    evsets = [ev.create(nev, keep=range(timed[0], timed[1] + 1)) for _ in range(steps)]
+    up = STAGES.index("expert_up")
+    evsets = [ev.create(nev, keep=(up, up + 1)) for _ in range(steps)]
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     for i in range(steps):
@@ -277,7 +278,6 @@ def main():
         rd = run_workload(wd, args.decode_steps, 10, fresh_x_steps=args.decode_steps)
         ms_d = rd["elapsed"] * 1e3 / rd["steps"]
         up_ms_d = float(rd["stage_ms"][up])
-        dn_ms_d = float(rd["stage_ms"][STAGES.index("expert_down")])
         # algorithmic bytes: touched experts' weights + permuted activations + H
         up_bytes = rd["touched"] * 2 * wd.d * wd.d_ff * 2 + rd["n_kept"] * (wd.d + wd.d_ff) * 2
         step_bytes = rd["touched"] * 3 * wd.d * wd.d_ff * 2 + wd.T * wd.d * 4 + wd.E * wd.d * 4
@@ -291,8 +291,7 @@ def main():
             "roofline": {"bound": "hbm", "kernel": "expert_up", "achieved": round(gbs, 1),
                          "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
                          "traffic": traffic_for(wd.name, "expert_up"),
-                         "algorithmic_per_launch": up_bytes, "mean_launch_ms": round(up_ms_d, 4),
-                         "down_mean_launch_ms": round(dn_ms_d, 4)},
+                         "algorithmic_per_launch": up_bytes, "mean_launch_ms": round(up_ms_d, 4)},
         }
         log(f"[bench] {wd.name}: {ms_d:.3f} ms/step")
     if not args.no_cpu:

@@ -115,7 +115,9 @@ extern "C" {
  * bracket every stage, and a NULL entry is skipped (each recorded event
  * separates the kernels around it by a few microseconds, so record only
  * the ones needed).  NULL disables the hook.  The stages, in order: route,
- * route-finalize, dispatch, gather, expert-up, expert-down, combine.
+ * route-finalize, dispatch, gather, expert-up, expert-down, combine; in
+ * moe_forward the gather is folded into expert-up (its rows of x are read
+ * through token_of_row), so that stage is empty.
  * The other entry points ignore it.
  */
 typedef struct moe_desc {

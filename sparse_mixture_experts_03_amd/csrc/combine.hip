@@ -8,10 +8,10 @@
 // nothing here, and a token dropped from every expert gets 0 (its residual,
 // outside the layer, carries it).
 //
-// combine_kernel: one wave per token, grid-stride; each lane owns 4
-// consecutive columns of every 256-column chunk and sums the k slots in
-// slot order in fp32, then stores fp32 or bf16 (a scalar variant serves
-// widths that are not a multiple of 4).  Every output element is
+// combine_kernel: one wave per (token, group of 256-column chunks),
+// grid-stride; each lane owns 4 consecutive columns of a chunk and sums the
+// k slots in slot order in fp32, then stores fp32 or bf16 (a scalar
+// variant serves widths that are not a multiple of 4).  Every output element is
 // written exactly once, so no memset and no atomics are needed.
 #include "moe_internal.h"
 
@@ -23,16 +23,23 @@ template <bool BF16, bool VEC4>
 __global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ y_perm,
                                                       const int32_t *__restrict__ row_of_slot,
                                                       const float *__restrict__ gates, int T,
-                                                      int d, int k, void *__restrict__ y) {
+                                                      int d, int k, int G, void *__restrict__ y) {
     const int lane = threadIdx.x & 63;
     if (VEC4) {
-        // one wave per token: its k rows and gates are read once, then the
-        // 256-column chunks follow, four at a time with their loads in flight
-        for (int t = blockIdx.x * 4 + (threadIdx.x >> 6); t < T; t += gridDim.x * 4) {
+        // one wave per (token, group of G 256-column chunks): the token's k
+        // rows and gates are read once per group, then the group's chunks
+        // follow, four at a time with their loads in flight
+        const int nch = (d + 255) / 256;
+        const int ngrp = (nch + G - 1) / G;
+        for (int64_t it = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); it < (int64_t)T * ngrp;
+             it += (int64_t)gridDim.x * 4) {
+            const int t = (int)(it / ngrp);
+            const int grp = (int)(it - (int64_t)t * ngrp);
+            const int cend = min(d, (grp + 1) * G * 256);
             const int32_t *rs = row_of_slot + (int64_t)t * k;
             const float *gs = gates + (int64_t)t * k;
 #pragma unroll 4
-            for (int c = lane * 4; c < d; c += 256) {
+            for (int c = grp * G * 256 + lane * 4; c < cend; c += 256) {
                 float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
                 for (int s = 0; s < k; ++s) {
                     const int r = rs[s];
@@ -81,13 +88,19 @@ __global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ 
 hipError_t launch_combine(const Shape &s, const float *y_perm, const int32_t *row_of_slot,
                           const float *gates, void *y, hipStream_t st) {
     const bool v4 = (s.d % 4) == 0;
-    int64_t blocks = ((int64_t)s.T + 3) / 4;
+    // chunks per wave: whole rows when there are many tokens, single
+    // 256-column chunks when there are few (so that enough waves run)
+    const int nch = (s.d + 255) / 256;
+    int G = (int)(((int64_t)s.T * nch) / 2048);
+    G = G < 1 ? 1 : (G > nch ? nch : G);
+    const int64_t items = v4 ? (int64_t)s.T * ((nch + G - 1) / G) : (int64_t)s.T;
+    int64_t blocks = (items + 3) / 4;
     if (blocks > 16384) blocks = 16384;
     const bool bf = s.dtype == 1;
     auto kern = bf ? (v4 ? combine_kernel<true, true> : combine_kernel<true, false>)
                    : (v4 ? combine_kernel<false, true> : combine_kernel<false, false>);
-    hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(256), 0, st, y_perm, row_of_slot, gates, s.T, s.d,
-                       s.k, y);
+    hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(256), 0, st, y_perm, row_of_slot, gates,
+                       s.T, s.d, s.k, G, y);
     return hipGetLastError();
 }
 

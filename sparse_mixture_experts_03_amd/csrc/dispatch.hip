@@ -11,7 +11,8 @@
 // per token).  They are cut into chunks of 256 (1024 when T*k is large).
 //   dispatch_count_kernel (one block per chunk): per-chunk histogram over
 //     experts with LDS integer atomics (a count does not depend on the
-//     order of the additions).
+//     order of the additions).  Skipped when there is a single chunk: the
+//     ranking block then counts its own chunk.
 //   dispatch_rank_kernel (one block per chunk): every block derives, from
 //     all chunk histograms, routed_e, kept_e = min(routed_e, C), the row
 //     offsets (exclusive prefix of kept_e) and, for its own chunk, how many
@@ -62,13 +63,24 @@ __global__ __launch_bounds__(DP_THREADS) void dispatch_rank_kernel(
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int chunk = blockIdx.x;
 
+    if (nchunks == 1) {
+        // a single chunk counts its own assignments (no histogram kernel ran)
+        if (tid < DP_EMAX) running[tid] = 0;
+        __syncthreads();
+        for (int64_t j = tid; j < Tk; j += DP_THREADS) atomicAdd(&running[topk_idx[j]], 1);
+        __syncthreads();
+    }
     if (tid < E) {
         int before = 0, tot = 0;
+        if (nchunks == 1) {
+            tot = running[tid];
+        } else {
 #pragma unroll 8
-        for (int c = 0; c < nchunks; ++c) {
-            const int v = chunk_counts[(int64_t)c * E + tid];
-            before += (c < chunk) ? v : 0;
-            tot += v;
+            for (int c = 0; c < nchunks; ++c) {
+                const int v = chunk_counts[(int64_t)c * E + tid];
+                before += (c < chunk) ? v : 0;
+                tot += v;
+            }
         }
         running[tid] = before;
         keptc[tid] = (C >= 0 && tot > C) ? (int)C : tot;
@@ -174,8 +186,9 @@ hipError_t launch_dispatch(const Shape &s, const int32_t *topk_idx, int32_t *rou
                            hipStream_t st) {
     const int nch = dispatch_chunks(s);
     const int chunk = dispatch_chunk(s);
-    hipLaunchKernelGGL(dispatch_count_kernel, dim3(nch), dim3(DP_THREADS), 0, st, topk_idx, s.Tk(),
-                       s.E, chunk, chunk_counts);
+    if (nch > 1)
+        hipLaunchKernelGGL(dispatch_count_kernel, dim3(nch), dim3(DP_THREADS), 0, st, topk_idx,
+                           s.Tk(), s.E, chunk, chunk_counts);
     hipLaunchKernelGGL(dispatch_rank_kernel, dim3(nch), dim3(DP_THREADS), 0, st, topk_idx, s.Tk(),
                        s.k, s.E, s.C, chunk, nch, (const int32_t *)chunk_counts, routed, kept,
                        offsets, row_of_slot, token_of_row, dropped);

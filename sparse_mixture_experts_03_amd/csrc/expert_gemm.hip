@@ -94,9 +94,9 @@ __device__ __forceinline__ bool find_tile(const int32_t *__restrict__ offsets, i
 
 template <int BM, int BN, int WAVES_M, int WAVES_N, bool DUAL, int ACT, bool OUT_BF16>
 __global__ __launch_bounds__(256) void gemm_bf16_kernel(
-    const uint16_t *__restrict__ A, const int32_t *__restrict__ offsets, int E,
-    const uint16_t *__restrict__ B1, const uint16_t *__restrict__ B3, void *__restrict__ C,
-    int N, int K) {
+    const uint16_t *__restrict__ A, const int32_t *__restrict__ a_rows,
+    const int32_t *__restrict__ offsets, int E, const uint16_t *__restrict__ B1,
+    const uint16_t *__restrict__ B3, void *__restrict__ C, int N, int K) {
     constexpr int BK = 64;
     constexpr int LDK = BK + 8;
     constexpr int NB = DUAL ? 2 : 1;
@@ -130,7 +130,8 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(
         a_row[i] = c / CPR;
         a_kc[i] = (c % CPR) * 8;
         const int r = min(a_row[i], nrows - 1);  // rows past the expert's last repeat it
-        a_src[i] = A + (int64_t)(row0 + r) * K + a_kc[i];
+        const int ar = row0 + r;
+        a_src[i] = A + (int64_t)(a_rows ? a_rows[ar] : ar) * K + a_kc[i];
     }
     const uint16_t *b_src[B_CH];
     int b_row[B_CH], b_kc[B_CH];
@@ -250,9 +251,9 @@ constexpr int BIG_BM = 256;
 
 template <bool DUAL, int ACT, bool OUT_BF16>
 __global__ __launch_bounds__(256) void gemm_bf16_big_kernel(
-    const uint16_t *__restrict__ A, const int32_t *__restrict__ offsets, int E,
-    const uint16_t *__restrict__ B1, const uint16_t *__restrict__ B3, void *__restrict__ C,
-    int N, int K) {
+    const uint16_t *__restrict__ A, const int32_t *__restrict__ a_rows,
+    const int32_t *__restrict__ offsets, int E, const uint16_t *__restrict__ B1,
+    const uint16_t *__restrict__ B3, void *__restrict__ C, int N, int K) {
     constexpr int BK = 64;
     constexpr int BN = DUAL ? 128 : 256;   // output columns per block
     constexpr int ROWB = BK * 2;           // bytes per LDS row (8 slots of 16 bytes)
@@ -281,7 +282,8 @@ __global__ __launch_bounds__(256) void gemm_bf16_big_kernel(
         for (int j = 0; j < 8; ++j) {
             const int kchunk = ((lane & 7) ^ sub ^ (j & 1)) * 8;
             const int r = wrow0 + j * 8 + sub;
-            a_off[j] = ((uint32_t)(row0 + min(r, nrows - 1)) * (uint32_t)K + kchunk) * 2u;
+            const int ar = row0 + min(r, nrows - 1);
+            a_off[j] = ((uint32_t)(a_rows ? a_rows[ar] : ar) * (uint32_t)K + kchunk) * 2u;
         }
         // SwiGLU: waves 0,1 fill W1 rows 0..127, waves 2,3 W3 rows 0..127
         bbase = (const char *)((DUAL && wave >= 2) ? B3 : B1) + (int64_t)e * N * K * 2;
@@ -417,9 +419,9 @@ constexpr int SK_KC = 128;
 
 template <int MT, int NT, int PF, int KS, bool DUAL, int ACT, bool OUT_BF16>
 __global__ __launch_bounds__(64 * KS) void gemm_bf16_skinny_kernel(
-    const uint16_t *__restrict__ A, const int32_t *__restrict__ offsets, int E,
-    const uint16_t *__restrict__ B1, const uint16_t *__restrict__ B3, void *__restrict__ C,
-    int N, int K) {
+    const uint16_t *__restrict__ A, const int32_t *__restrict__ a_rows,
+    const int32_t *__restrict__ offsets, int E, const uint16_t *__restrict__ B1,
+    const uint16_t *__restrict__ B3, void *__restrict__ C, int N, int K) {
     typedef float f32x4_t __attribute__((ext_vector_type(4)));
     // chunk ch sits in B slot ch % PF and A slot ch % 2; the unrolled loop
     // below indexes both by its static position sl, which matches only when
@@ -445,7 +447,10 @@ __global__ __launch_bounds__(64 * KS) void gemm_bf16_skinny_kernel(
     const uint16_t *a_row[MT];
 #pragma unroll
     for (int m = 0; m < MT; ++m)
-        a_row[m] = A + (int64_t)(lo + min(m * 16 + n, M - 1)) * K + (int64_t)cb * SK_KC + g * 32;
+    {
+        const int ar = lo + min(m * 16 + n, M - 1);
+        a_row[m] = A + (int64_t)(a_rows ? a_rows[ar] : ar) * K + (int64_t)cb * SK_KC + g * 32;
+    }
     const uint16_t *b_row[NB][NT];
 #pragma unroll
     for (int q = 0; q < NB; ++q)
@@ -569,6 +574,7 @@ __device__ __forceinline__ int expert_of_row(const int32_t *__restrict__ offsets
 }
 
 __global__ __launch_bounds__(256) void up_f32_kernel(const float *__restrict__ A,
+                                                     const int32_t *__restrict__ a_rows,
                                                      const int32_t *__restrict__ offsets, int E,
                                                      const float *__restrict__ W1,
                                                      const float *__restrict__ W3, int act,
@@ -576,7 +582,7 @@ __global__ __launch_bounds__(256) void up_f32_kernel(const float *__restrict__ A
     const int n = offsets[E];
     for (int r = blockIdx.x; r < n; r += gridDim.x) {
         const int e = expert_of_row(offsets, E, r);
-        const float *a = A + (int64_t)r * d;
+        const float *a = A + (int64_t)(a_rows ? a_rows[r] : r) * d;
         for (int f = threadIdx.x; f < d_ff; f += blockDim.x) {
             const float *w1 = W1 + ((int64_t)e * d_ff + f) * d;
             float a1 = 0.f, a3 = 0.f;
@@ -637,33 +643,33 @@ inline int pick_bm(const Shape &s, int K) {
 }
 
 template <int BM, int BN, int WM_, int WN_, bool DUAL, int ACT, bool OUT_BF16>
-hipError_t launch_gemm(const Shape &s, const void *A, const int32_t *offsets, const void *B1,
+hipError_t launch_gemm(const Shape &s, const void *A, const int32_t *a_rows, const int32_t *offsets, const void *B1,
                        const void *B3, void *C, int N, int K, hipStream_t st) {
     const unsigned nt = (unsigned)((N + BN - 1) / BN);
     unsigned blocks = nt * row_tile_bound(s, BM);
     blocks = (blocks + NUM_XCD - 1) / NUM_XCD * NUM_XCD;
     dim3 grid(blocks);
     hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM_, WN_, DUAL, ACT, OUT_BF16>), grid, dim3(256),
-                       0, st, (const uint16_t *)A, offsets, s.E, (const uint16_t *)B1,
+                       0, st, (const uint16_t *)A, a_rows, offsets, s.E, (const uint16_t *)B1,
                        (const uint16_t *)B3, C, N, K);
     return hipGetLastError();
 }
 
 template <bool DUAL, int ACT, bool OUT_BF16>
-hipError_t launch_big(const Shape &s, const void *A, const int32_t *offsets, const void *B1,
+hipError_t launch_big(const Shape &s, const void *A, const int32_t *a_rows, const int32_t *offsets, const void *B1,
                       const void *B3, void *C, int N, int K, hipStream_t st) {
     constexpr int BN = DUAL ? 128 : 256;
     const unsigned nt = (unsigned)((N + BN - 1) / BN);
     unsigned blocks = nt * row_tile_bound(s, BIG_BM);
     blocks = (blocks + NUM_XCD - 1) / NUM_XCD * NUM_XCD;
     hipLaunchKernelGGL((gemm_bf16_big_kernel<DUAL, ACT, OUT_BF16>), dim3(blocks), dim3(256), 0, st,
-                       (const uint16_t *)A, offsets, s.E, (const uint16_t *)B1,
+                       (const uint16_t *)A, a_rows, offsets, s.E, (const uint16_t *)B1,
                        (const uint16_t *)B3, C, N, K);
     return hipGetLastError();
 }
 
 template <int MT, int NT, int PF, bool DUAL, int ACT, bool OUT_BF16>
-hipError_t launch_skinny(const Shape &s, const void *A, const int32_t *offsets, const void *B1,
+hipError_t launch_skinny(const Shape &s, const void *A, const int32_t *a_rows, const int32_t *offsets, const void *B1,
                          const void *B3, void *C, int N, int K, hipStream_t st) {
     const unsigned blocks = (unsigned)s.E * (unsigned)((N + 16 * NT - 1) / (16 * NT));
     // split K over the waves of a block when there are too few column tiles
@@ -672,11 +678,11 @@ hipError_t launch_skinny(const Shape &s, const void *A, const int32_t *offsets, 
     const int nch = K / SK_KC;
     if (blocks < 4096 && nch >= 64) {
         hipLaunchKernelGGL((gemm_bf16_skinny_kernel<MT, NT, PF, 4, DUAL, ACT, OUT_BF16>),
-                           dim3(blocks), dim3(256), 0, st, (const uint16_t *)A, offsets, s.E,
+                           dim3(blocks), dim3(256), 0, st, (const uint16_t *)A, a_rows, offsets, s.E,
                            (const uint16_t *)B1, (const uint16_t *)B3, C, N, K);
     } else {
         hipLaunchKernelGGL((gemm_bf16_skinny_kernel<MT, NT, PF, 1, DUAL, ACT, OUT_BF16>),
-                           dim3(blocks), dim3(64), 0, st, (const uint16_t *)A, offsets, s.E,
+                           dim3(blocks), dim3(64), 0, st, (const uint16_t *)A, a_rows, offsets, s.E,
                            (const uint16_t *)B1, (const uint16_t *)B3, C, N, K);
     }
     return hipGetLastError();
@@ -692,41 +698,42 @@ inline int skinny_tiles(const Shape &s, int K) {
 }
 
 template <bool DUAL, int ACT, bool OUT_BF16>
-hipError_t launch_skinny_any(const Shape &s, int mt, const void *A, const int32_t *offsets,
+hipError_t launch_skinny_any(const Shape &s, int mt, const void *A, const int32_t *a_rows, const int32_t *offsets,
                              const void *B1, const void *B3, void *C, int N, int K,
                              hipStream_t st) {
-    if (mt == 2) return launch_skinny<2, DUAL ? 1 : 2, 4, DUAL, ACT, OUT_BF16>(s, A, offsets, B1, B3, C, N, K, st);
-    return launch_skinny<3, DUAL ? 1 : 2, 4, DUAL, ACT, OUT_BF16>(s, A, offsets, B1, B3, C, N, K, st);
+    if (mt == 2) return launch_skinny<2, DUAL ? 1 : 2, 4, DUAL, ACT, OUT_BF16>(s, A, a_rows, offsets, B1, B3, C, N, K, st);
+    return launch_skinny<3, DUAL ? 1 : 2, 4, DUAL, ACT, OUT_BF16>(s, A, a_rows, offsets, B1, B3, C, N, K, st);
 }
 
 template <int ACT, bool DUAL>
-hipError_t launch_up_bf16(const Shape &s, const void *A, const int32_t *offsets, const void *W1,
+hipError_t launch_up_bf16(const Shape &s, const void *A, const int32_t *a_rows, const int32_t *offsets, const void *W1,
                           const void *W3, void *H, hipStream_t st) {
     if (const int mt = skinny_tiles(s, s.d))
-        return launch_skinny_any<DUAL, ACT, true>(s, mt, A, offsets, W1, W3, H, s.d_ff, s.d, st);
+        return launch_skinny_any<DUAL, ACT, true>(s, mt, A, a_rows, offsets, W1, W3, H, s.d_ff, s.d, st);
     switch (pick_bm(s, s.d)) {
-    case BIG_BM: return launch_big<DUAL, ACT, true>(s, A, offsets, W1, W3, H, s.d_ff, s.d, st);
-    case 128: return launch_gemm<128, 128, 2, 2, DUAL, ACT, true>(s, A, offsets, W1, W3, H, s.d_ff, s.d, st);
-    case 64:  return launch_gemm<64, 128, 2, 2, DUAL, ACT, true>(s, A, offsets, W1, W3, H, s.d_ff, s.d, st);
-    default:  return launch_gemm<32, 128, 1, 4, DUAL, ACT, true>(s, A, offsets, W1, W3, H, s.d_ff, s.d, st);
+    case BIG_BM: return launch_big<DUAL, ACT, true>(s, A, a_rows, offsets, W1, W3, H, s.d_ff, s.d, st);
+    case 128: return launch_gemm<128, 128, 2, 2, DUAL, ACT, true>(s, A, a_rows, offsets, W1, W3, H, s.d_ff, s.d, st);
+    case 64:  return launch_gemm<64, 128, 2, 2, DUAL, ACT, true>(s, A, a_rows, offsets, W1, W3, H, s.d_ff, s.d, st);
+    default:  return launch_gemm<32, 128, 1, 4, DUAL, ACT, true>(s, A, a_rows, offsets, W1, W3, H, s.d_ff, s.d, st);
     }
 }
 
 }  // namespace
 
-hipError_t launch_expert_up(const Shape &s, const void *x_perm, const int32_t *offsets,
-                            const void *W1, const void *W3, void *H, hipStream_t st) {
+hipError_t launch_expert_up(const Shape &s, const void *x_perm, const int32_t *a_rows,
+                            const int32_t *offsets, const void *W1, const void *W3, void *H,
+                            hipStream_t st) {
     if (s.dtype == 0) {
         int64_t blocks = s.Tk() < 16384 ? s.Tk() : 16384;
         hipLaunchKernelGGL(up_f32_kernel, dim3((unsigned)(blocks > 0 ? blocks : 1)), dim3(256), 0,
-                           st, (const float *)x_perm, offsets, s.E, (const float *)W1,
+                           st, (const float *)x_perm, a_rows, offsets, s.E, (const float *)W1,
                            (const float *)W3, s.act, (float *)H, s.d, s.d_ff);
         return hipGetLastError();
     }
     switch (s.act) {
-    case ACT_SWIGLU: return launch_up_bf16<ACT_SWIGLU, true>(s, x_perm, offsets, W1, W3, H, st);
-    case ACT_GELU:   return launch_up_bf16<ACT_GELU, false>(s, x_perm, offsets, W1, nullptr, H, st);
-    default:         return launch_up_bf16<ACT_RELU, false>(s, x_perm, offsets, W1, nullptr, H, st);
+    case ACT_SWIGLU: return launch_up_bf16<ACT_SWIGLU, true>(s, x_perm, a_rows, offsets, W1, W3, H, st);
+    case ACT_GELU:   return launch_up_bf16<ACT_GELU, false>(s, x_perm, a_rows, offsets, W1, nullptr, H, st);
+    default:         return launch_up_bf16<ACT_RELU, false>(s, x_perm, a_rows, offsets, W1, nullptr, H, st);
     }
 }
 
@@ -740,13 +747,13 @@ hipError_t launch_expert_down(const Shape &s, const void *H, const int32_t *offs
         return hipGetLastError();
     }
     if (const int mt = skinny_tiles(s, s.d_ff))
-        return launch_skinny_any<false, ACT_NONE, false>(s, mt, H, offsets, W2, nullptr, y_perm, s.d,
+        return launch_skinny_any<false, ACT_NONE, false>(s, mt, H, nullptr, offsets, W2, nullptr, y_perm, s.d,
                                                           s.d_ff, st);
     switch (pick_bm(s, s.d_ff)) {
-    case BIG_BM: return launch_big<false, ACT_NONE, false>(s, H, offsets, W2, nullptr, y_perm, s.d, s.d_ff, st);
-    case 128: return launch_gemm<128, 128, 2, 2, false, ACT_NONE, false>(s, H, offsets, W2, nullptr, y_perm, s.d, s.d_ff, st);
-    case 64:  return launch_gemm<64, 128, 2, 2, false, ACT_NONE, false>(s, H, offsets, W2, nullptr, y_perm, s.d, s.d_ff, st);
-    default:  return launch_gemm<32, 128, 1, 4, false, ACT_NONE, false>(s, H, offsets, W2, nullptr, y_perm, s.d, s.d_ff, st);
+    case BIG_BM: return launch_big<false, ACT_NONE, false>(s, H, nullptr, offsets, W2, nullptr, y_perm, s.d, s.d_ff, st);
+    case 128: return launch_gemm<128, 128, 2, 2, false, ACT_NONE, false>(s, H, nullptr, offsets, W2, nullptr, y_perm, s.d, s.d_ff, st);
+    case 64:  return launch_gemm<64, 128, 2, 2, false, ACT_NONE, false>(s, H, nullptr, offsets, W2, nullptr, y_perm, s.d, s.d_ff, st);
+    default:  return launch_gemm<32, 128, 1, 4, false, ACT_NONE, false>(s, H, nullptr, offsets, W2, nullptr, y_perm, s.d, s.d_ff, st);
     }
 }
 

@@ -52,7 +52,7 @@ int check_desc(const moe_desc *desc, Shape *s) {
 
 // Workspace layout; every region starts on a 256-byte boundary.
 struct Layout {
-    size_t part_P, part_lse2, fP;                   // router partial sums, f_e * P_e
+    size_t part_P, part_lse2, fP, arrivals;         // router partials, f_e*P_e and z, counter
     size_t wsplit, part_logits;                     // bf16 router: split W_r, logit slices
     size_t chunk_counts;                            // dispatch: per-chunk expert histograms
     size_t topk_idx, gates, routed, kept, offsets;  // moe_forward's optional outputs
@@ -76,7 +76,8 @@ Layout layout(const Shape &s) {
     };
     L.part_P = take(nblk * s.E * sizeof(float));
     L.part_lse2 = take(nblk * sizeof(float));
-    L.fP = take((size_t)s.E * sizeof(double));
+    L.fP = take(((size_t)s.E + 1) * sizeof(double));
+    L.arrivals = take(sizeof(unsigned));
     if (s.dtype == MOE_DTYPE_BF16) {
         L.wsplit = take(3 * (size_t)moe::route_epad(s) * (size_t)s.d * 2);
         L.part_logits = take((size_t)moe::route_nsplit(s) * (size_t)s.T * (size_t)s.E * 4);
@@ -163,10 +164,12 @@ int moe_route(const moe_desc *desc, const void *x, const float *W_r, const float
     hipStream_t st = (hipStream_t)stream;
     MOE_TRY(moe::launch_route(s, x, W_r, bias, noise, topk_idx, gates, at<float>(ws, L.part_P),
                               at<float>(ws, L.part_lse2), at<uint16_t>(ws, L.wsplit),
-                              at<float>(ws, L.part_logits), st));
+                              at<float>(ws, L.part_logits),
+                              at<unsigned>(ws, L.arrivals), st));
     MOE_TRY(moe::launch_route_finalize(s, topk_idx, at<float>(ws, L.part_P),
                                        at<float>(ws, L.part_lse2), stats,
-                                       at<double>(ws, L.fP), st));
+                                       at<double>(ws, L.fP),
+                                       at<unsigned>(ws, L.arrivals), st));
     return MOE_OK;
 }
 
@@ -201,7 +204,7 @@ int moe_expert_ffn(const moe_desc *desc, const void *x_perm, const int32_t *offs
     const Layout L = layout(s);
     hipStream_t st = (hipStream_t)stream;
     void *H = at<char>(ws, L.H);
-    MOE_TRY(moe::launch_expert_up(s, x_perm, offsets, W1, W3, H, st));
+    MOE_TRY(moe::launch_expert_up(s, x_perm, nullptr, offsets, W1, W3, H, st));
     MOE_TRY(moe::launch_expert_down(s, H, offsets, W2, y_perm, st));
     return MOE_OK;
 }
@@ -237,7 +240,6 @@ int moe_forward(const moe_desc *desc, const void *x, const float *W_r, const flo
     if (!token_of_row) token_of_row = at<int32_t>(ws, L.token_of_row);
     if (!dropped) dropped = at<uint8_t>(ws, L.dropped);
     if (!stats) stats = at<float>(ws, L.stats);
-    void *x_perm = at<char>(ws, L.x_perm);
     void *H = at<char>(ws, L.H);
     float *y_perm = at<float>(ws, L.y_perm);
 
@@ -246,18 +248,21 @@ int moe_forward(const moe_desc *desc, const void *x, const float *W_r, const flo
     MOE_TRY(ev.record(st));
     MOE_TRY(moe::launch_route(s, x, W_r, bias, noise, topk_idx, gates, at<float>(ws, L.part_P),
                               at<float>(ws, L.part_lse2), at<uint16_t>(ws, L.wsplit),
-                              at<float>(ws, L.part_logits), st));
+                              at<float>(ws, L.part_logits),
+                              at<unsigned>(ws, L.arrivals), st));
     MOE_TRY(ev.record(st));
     MOE_TRY(moe::launch_route_finalize(s, topk_idx, at<float>(ws, L.part_P),
                                        at<float>(ws, L.part_lse2), stats,
-                                       at<double>(ws, L.fP), st));
+                                       at<double>(ws, L.fP),
+                                       at<unsigned>(ws, L.arrivals), st));
     MOE_TRY(ev.record(st));
     MOE_TRY(moe::launch_dispatch(s, topk_idx, routed_counts, kept_counts, offsets, row_of_slot,
                                  token_of_row, dropped, at<int32_t>(ws, L.chunk_counts), st));
     MOE_TRY(ev.record(st));
-    MOE_TRY(moe::launch_gather(s, x, token_of_row, offsets, x_perm, st));
+    // the gather is folded into the up projection's loads: its rows of A are
+    // read from x through token_of_row, so x_perm is not materialised here
     MOE_TRY(ev.record(st));
-    MOE_TRY(moe::launch_expert_up(s, x_perm, offsets, W1, W3, H, st));
+    MOE_TRY(moe::launch_expert_up(s, x, token_of_row, offsets, W1, W3, H, st));
     MOE_TRY(ev.record(st));
     MOE_TRY(moe::launch_expert_down(s, H, offsets, W2, y_perm, st));
     MOE_TRY(ev.record(st));

@@ -32,12 +32,15 @@ int route_epad(const Shape &s);
 int route_slice(const Shape &s);
 int route_nsplit(const Shape &s);
 
+// arrivals: a 4-byte counter in the workspace (zeroed by launch_route's
+// kernels, used and re-zeroed by the statistics kernel); fP: E + 1 doubles.
 hipError_t launch_route(const Shape &s, const void *x, const float *Wr, const float *bias,
                         const float *noise, int32_t *topk_idx, float *gates, float *part_P,
-                        float *part_lse2, uint16_t *wsplit, float *part_logits, hipStream_t st);
+                        float *part_lse2, uint16_t *wsplit, float *part_logits,
+                        unsigned *arrivals, hipStream_t st);
 hipError_t launch_route_finalize(const Shape &s, const int32_t *topk_idx, const float *part_P,
                                  const float *part_lse2, float *stats, double *fP,
-                                 hipStream_t st);
+                                 unsigned *arrivals, hipStream_t st);
 
 // ---- dispatch: capacity, stable permutation, gather ----------------------
 // Assignments per dispatch block (256 per round; more rounds when T*k is
@@ -53,8 +56,11 @@ hipError_t launch_gather(const Shape &s, const void *x, const int32_t *token_of_
                          const int32_t *offsets, void *x_perm, hipStream_t st);
 
 // ---- expert FFN: grouped GEMMs over ragged per-expert row blocks --------
-hipError_t launch_expert_up(const Shape &s, const void *x_perm, const int32_t *offsets,
-                            const void *W1, const void *W3, void *H, hipStream_t st);
+// a_rows: row r of A is A[a_rows[r]] (the gather done by the loads);
+// nullptr: row r is A[r].
+hipError_t launch_expert_up(const Shape &s, const void *x_perm, const int32_t *a_rows,
+                            const int32_t *offsets, const void *W1, const void *W3, void *H,
+                            hipStream_t st);
 hipError_t launch_expert_down(const Shape &s, const void *H, const int32_t *offsets,
                               const void *W2, float *y_perm, hipStream_t st);
 

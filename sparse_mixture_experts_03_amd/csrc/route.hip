@@ -31,8 +31,8 @@
 // reductions, top-k by k arg-max reductions over 64-bit keys (orderable
 // logit bits, then the complement of the index, so a tie goes to the lower
 // index), gates, and per-block partial sums of p (per expert) and of lse^2
-// in a fixed order.  route_stats_kernel and route_aux_kernel reduce the
-// partials in double in a fixed order and count top choices.
+// in a fixed order.  route_stats_kernel reduces the partials in double in
+// a fixed order and counts top choices.
 #include "moe_internal.h"
 
 namespace moe {
@@ -150,7 +150,7 @@ __global__ __launch_bounds__(RT_THREADS) void route_f32_kernel(
     const float *__restrict__ x, const float *__restrict__ Wr, const float *__restrict__ bias,
     const float *__restrict__ noise, int T, int d, int E, int k, int gate_switch,
     int32_t *__restrict__ topk_idx, float *__restrict__ gates, float *__restrict__ part_P,
-    float *__restrict__ part_lse2) {
+    float *__restrict__ part_lse2, unsigned *__restrict__ arrivals) {
     constexpr int TILE = ROUTE_TOKENS_F32;
     __shared__ float xs[TILE][RT_DC + 1];
     __shared__ float wsh[RT_EMAX][RT_DC + 1];
@@ -207,6 +207,7 @@ __global__ __launch_bounds__(RT_THREADS) void route_f32_kernel(
         }
     }
     __syncthreads();
+    if (blockIdx.x == 0 && tid == 0) *arrivals = 0u;
     softmax_topk_block<TILE>(hl, t0, T, E, k, gate_switch, topk_idx, gates, part_P, part_lse2);
 }
 
@@ -345,7 +346,7 @@ __global__ __launch_bounds__(RT_THREADS) void route_epilogue_kernel(
     const float *__restrict__ part, int nsplit, const float *__restrict__ bias,
     const float *__restrict__ noise, int T, int E, int k, int gate_switch,
     int32_t *__restrict__ topk_idx, float *__restrict__ gates, float *__restrict__ part_P,
-    float *__restrict__ part_lse2) {
+    float *__restrict__ part_lse2, unsigned *__restrict__ arrivals) {
     constexpr int TILE = ROUTE_TOKENS_BF16;
     __shared__ float hl[TILE][RT_EMAX + 1];
     constexpr int MAXQ = TILE * RT_EMAX / RT_THREADS;
@@ -375,16 +376,18 @@ __global__ __launch_bounds__(RT_THREADS) void route_epilogue_kernel(
             hl[r][e] = v;
         }
     }
+    if (blockIdx.x == 0 && tid == 0) *arrivals = 0u;
     __syncthreads();
     softmax_topk_block<TILE>(hl, t0, T, E, k, gate_switch, topk_idx, gates, part_P, part_lse2);
 }
 
-// Statistics, in two kernels and in double, every sum in a fixed order.
-// route_stats_kernel: block e < E reduces expert e's block partials of p
-// (thread t takes blocks t, t+256, ...; then the 256 thread sums are added
-// in thread order) and counts the tokens whose top choice is e; block E
-// reduces the lse^2 partials the same way.  route_aux_kernel (one block)
-// forms aux = E * sum_e f_e P_e.
+// Statistics in double, every sum in a fixed order.  route_stats_kernel:
+// block e < E reduces expert e's block partials of p (thread t takes blocks
+// t, t+256, ...; then the 256 thread sums are added in thread order) and
+// counts the tokens whose top choice is e; block E reduces the lse^2
+// partials the same way.  The last block to finish (an integer arrival
+// counter, zeroed by the route kernel that runs before) adds the f_e P_e in
+// expert order for aux and writes aux and z, then re-zeroes the counter.
 __device__ __forceinline__ double block_sum_fixed(double v, double *red) {
     const int tid = threadIdx.x;
     red[tid] = v;
@@ -398,45 +401,48 @@ __device__ __forceinline__ double block_sum_fixed(double v, double *red) {
 __global__ __launch_bounds__(256) void route_stats_kernel(
     const int32_t *__restrict__ topk_idx, const float *__restrict__ part_P,
     const float *__restrict__ part_lse2, int T, int E, int k, int nblk,
-    float *__restrict__ stats, double *__restrict__ fP) {
+    float *__restrict__ stats, double *__restrict__ fP, unsigned *__restrict__ arrivals) {
     __shared__ double red[256];
     __shared__ int cnt[4];
+    __shared__ int last;
     const int tid = threadIdx.x;
     const int e = blockIdx.x;
     if (e == E) {
         double z = 0.0;
         for (int b = tid; b < nblk; b += 256) z += (double)part_lse2[b];
         z = block_sum_fixed(z, red);
-        if (tid == 0) stats[2 * E + 1] = (float)(z / (double)T);
-        return;
-    }
-    double acc = 0.0;
+        if (tid == 0) fP[E] = z / (double)T;
+    } else {
+        double acc = 0.0;
 #pragma unroll 4
-    for (int b = tid; b < nblk; b += 256) acc += (double)part_P[(int64_t)b * E + e];
-    int c = 0;
+        for (int b = tid; b < nblk; b += 256) acc += (double)part_P[(int64_t)b * E + e];
+        int c = 0;
 #pragma unroll 8
-    for (int t = tid; t < T; t += 256) c += topk_idx[(int64_t)t * k] == e;
-    // integer count: the order of the additions does not matter
-    for (int o = 32; o > 0; o >>= 1) c += __shfl_xor(c, o);
-    if ((tid & 63) == 0) cnt[tid >> 6] = c;
-    const double P = block_sum_fixed(acc, red) / (double)T;
-    if (tid == 0) {
-        const double f = (double)(cnt[0] + cnt[1] + cnt[2] + cnt[3]) / (double)T;
-        stats[e] = (float)f;
-        stats[E + e] = (float)P;
-        fP[e] = f * P;
+        for (int t = tid; t < T; t += 256) c += topk_idx[(int64_t)t * k] == e;
+        // integer count: the order of the additions does not matter
+        for (int o = 32; o > 0; o >>= 1) c += __shfl_xor(c, o);
+        if ((tid & 63) == 0) cnt[tid >> 6] = c;
+        const double P = block_sum_fixed(acc, red) / (double)T;
+        if (tid == 0) {
+            const double f = (double)(cnt[0] + cnt[1] + cnt[2] + cnt[3]) / (double)T;
+            stats[e] = (float)f;
+            stats[E + e] = (float)P;
+            fP[e] = f * P;
+        }
     }
-}
-
-__global__ __launch_bounds__(128) void route_aux_kernel(const double *__restrict__ fP, int E,
-                                                        float *__restrict__ stats) {
-    __shared__ double v[RT_EMAX];
-    if ((int)threadIdx.x < E) v[threadIdx.x] = fP[threadIdx.x];
+    if (tid == 0) {
+        __threadfence();
+        last = atomicAdd(arrivals, 1u) == (unsigned)E;
+    }
     __syncthreads();
-    if (threadIdx.x == 0) {
+    if (last && tid == 0) {
+        __threadfence();
+        const volatile double *v = fP;
         double a = 0.0;
         for (int i = 0; i < E; ++i) a += v[i];
         stats[2 * E] = (float)((double)E * a);
+        stats[2 * E + 1] = (float)v[E];
+        *arrivals = 0u;
     }
 }
 
@@ -458,12 +464,13 @@ int route_epad(const Shape &s) {
 }
 
 // d slice per split: whole 64-wide chunks, enough slices to give the GPU
-// about 512 blocks, each slice at least two chunks.
+// about 512 blocks, each slice at least two chunks, at most 8 slices.
 int route_slice(const Shape &s) {
     const int tiles = (s.T + RL_BM - 1) / RL_BM;
     const int chunks = (s.d + RL_KC - 1) / RL_KC;
     const int want = (512 + tiles - 1) / tiles;
-    const int maxsplit = chunks / 2 > 1 ? chunks / 2 : 1;
+    int maxsplit = chunks / 2 > 1 ? chunks / 2 : 1;
+    if (maxsplit > 8) maxsplit = 8;  // the epilogue adds the slices back
     int nsplit = want < maxsplit ? want : maxsplit;
     if (nsplit < 1) nsplit = 1;
     return (chunks + nsplit - 1) / nsplit * RL_KC;
@@ -476,11 +483,13 @@ int route_nsplit(const Shape &s) {
 
 hipError_t launch_route(const Shape &s, const void *x, const float *Wr, const float *bias,
                         const float *noise, int32_t *topk_idx, float *gates, float *part_P,
-                        float *part_lse2, uint16_t *wsplit, float *part_logits, hipStream_t st) {
+                        float *part_lse2, uint16_t *wsplit, float *part_logits,
+                        unsigned *arrivals, hipStream_t st) {
     const dim3 grid(route_blocks(s)), block(RT_THREADS);
     if (s.dtype == 0) {
         hipLaunchKernelGGL(route_f32_kernel, grid, block, 0, st, (const float *)x, Wr, bias, noise,
-                           s.T, s.d, s.E, s.k, s.gate, topk_idx, gates, part_P, part_lse2);
+                           s.T, s.d, s.E, s.k, s.gate, topk_idx, gates, part_P, part_lse2,
+                           arrivals);
         return hipGetLastError();
     }
     const int epad = route_epad(s);
@@ -499,16 +508,15 @@ hipError_t launch_route(const Shape &s, const void *x, const float *Wr, const fl
     }
     hipLaunchKernelGGL(route_epilogue_kernel, grid, block, 0, st, (const float *)part_logits,
                        route_nsplit(s), bias, noise, s.T, s.E, s.k, s.gate, topk_idx, gates,
-                       part_P, part_lse2);
+                       part_P, part_lse2, arrivals);
     return hipGetLastError();
 }
 
 hipError_t launch_route_finalize(const Shape &s, const int32_t *topk_idx, const float *part_P,
                                  const float *part_lse2, float *stats, double *fP,
-                                 hipStream_t st) {
+                                 unsigned *arrivals, hipStream_t st) {
     hipLaunchKernelGGL(route_stats_kernel, dim3(s.E + 1), dim3(256), 0, st, topk_idx, part_P,
-                       part_lse2, s.T, s.E, s.k, route_blocks(s), stats, fP);
-    hipLaunchKernelGGL(route_aux_kernel, dim3(1), dim3(128), 0, st, (const double *)fP, s.E, stats);
+                       part_lse2, s.T, s.E, s.k, route_blocks(s), stats, fP, arrivals);
     return hipGetLastError();
 }
 
