@@ -183,7 +183,12 @@ int moe_dispatch(const moe_desc *desc, const void *x, const int32_t *topk_idx,
  * counts).  For every row r of expert e (offsets[e] <= r < offsets[e+1]):
  *   H      = act(x_perm[r] W1_e^T) [* (x_perm[r] W3_e^T) for SwiGLU]
  *   y_perm[r] = H W2_e^T
- * H is kept in the workspace in the act dtype; accumulation is fp32.
+ * H is kept in the workspace in the act dtype; accumulation is fp32.  When
+ * the down projection has too few output tiles to fill the GPU (bf16, long
+ * d_ff) it sums K in two halves; the second half's fp32 partial rows are
+ * kept in the workspace and added into y_perm before the call returns (in
+ * moe_forward the combine adds them), so the result does not depend on
+ * which entry point ran.
  * Experts with no rows read none of their weights.  W3 must be NULL
  * unless act is SwiGLU (then it is required).
  */

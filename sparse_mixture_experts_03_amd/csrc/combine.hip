@@ -8,6 +8,9 @@
 // nothing here, and a token dropped from every expert gets 0 (its residual,
 // outside the layer, carries it).
 //
+// When the down projection split K in two, the two partial rows are added
+// (first half + second half) before the gate multiplies them.
+//
 // combine_kernel: one wave per (token, group of 256-column chunks),
 // grid-stride; each lane owns 4 consecutive columns of a chunk and sums the
 // k slots in slot order in fp32, then stores fp32 or bf16 (a scalar
@@ -21,6 +24,7 @@ namespace {
 
 template <bool BF16, bool VEC4>
 __global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ y_perm,
+                                                      const float *__restrict__ part2,
                                                       const int32_t *__restrict__ row_of_slot,
                                                       const float *__restrict__ gates, int T,
                                                       int d, int k, int G, void *__restrict__ y) {
@@ -45,7 +49,14 @@ __global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ 
                     const int r = rs[s];
                     if (r < 0) continue;
                     const float g = gs[s];
-                    const float4 v = *(const float4 *)(y_perm + (int64_t)r * d + c);
+                    float4 v = *(const float4 *)(y_perm + (int64_t)r * d + c);
+                    if (part2) {
+                        const float4 u = *(const float4 *)(part2 + (int64_t)r * d + c);
+                        v.x += u.x;
+                        v.y += u.y;
+                        v.z += u.z;
+                        v.w += u.w;
+                    }
                     a.x = fmaf(g, v.x, a.x);
                     a.y = fmaf(g, v.y, a.y);
                     a.z = fmaf(g, v.z, a.z);
@@ -72,7 +83,9 @@ __global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ 
                 for (int s = 0; s < k; ++s) {
                     const int r = rs[s];
                     if (r < 0) continue;
-                    a = fmaf(gs[s], y_perm[(int64_t)r * d + c], a);
+                    float v = y_perm[(int64_t)r * d + c];
+                    if (part2) v += part2[(int64_t)r * d + c];
+                    a = fmaf(gs[s], v, a);
                 }
                 if (BF16)
                     ((uint16_t *)y)[(int64_t)t * d + c] = f32_to_bf16(a);
@@ -85,8 +98,9 @@ __global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ 
 
 }  // namespace
 
-hipError_t launch_combine(const Shape &s, const float *y_perm, const int32_t *row_of_slot,
-                          const float *gates, void *y, hipStream_t st) {
+hipError_t launch_combine(const Shape &s, const float *y_perm, const float *y_perm_part2,
+                          const int32_t *row_of_slot, const float *gates, void *y,
+                          hipStream_t st) {
     const bool v4 = (s.d % 4) == 0;
     // chunks per wave: whole rows when there are many tokens, single
     // 256-column chunks when there are few (so that enough waves run)
@@ -99,8 +113,8 @@ hipError_t launch_combine(const Shape &s, const float *y_perm, const int32_t *ro
     const bool bf = s.dtype == 1;
     auto kern = bf ? (v4 ? combine_kernel<true, true> : combine_kernel<true, false>)
                    : (v4 ? combine_kernel<false, true> : combine_kernel<false, false>);
-    hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(256), 0, st, y_perm, row_of_slot, gates,
-                       s.T, s.d, s.k, G, y);
+    hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(256), 0, st, y_perm, y_perm_part2,
+                       row_of_slot, gates, s.T, s.d, s.k, G, y);
     return hipGetLastError();
 }
 

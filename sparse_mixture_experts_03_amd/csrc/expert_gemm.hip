@@ -65,16 +65,20 @@ constexpr int NUM_XCD = 8;
 
 template <int BM>
 __device__ __forceinline__ bool find_tile(const int32_t *__restrict__ offsets, int E, int ntiles_n,
-                                          int &e, int &row0, int &nrows, int &ntile) {
+                                          int &e, int &row0, int &nrows, int &ntile,
+                                          int nsplit = 1, int *split = nullptr) {
     int total = 0;
     for (int i = 0; i < E; ++i) total += (offsets[i + 1] - offsets[i] + BM - 1) / BM;
     total *= ntiles_n;
-    const int per = (total + NUM_XCD - 1) / NUM_XCD;
+    const int work = total * nsplit;  // K-split index slowest
+    const int per = (work + NUM_XCD - 1) / NUM_XCD;
     const int b = blockIdx.x;
     const int slot = b / NUM_XCD;
     if (slot >= per) return false;
     int L = (b % NUM_XCD) * per + slot;
-    if (L >= total) return false;
+    if (L >= work) return false;
+    if (split) *split = L / total;
+    L %= total;
     for (int i = 0; i < E; ++i) {
         const int lo = offsets[i], hi = offsets[i + 1];
         const int mt = (hi - lo + BM - 1) / BM;
@@ -253,15 +257,18 @@ template <bool DUAL, int ACT, bool OUT_BF16>
 __global__ __launch_bounds__(256) void gemm_bf16_big_kernel(
     const uint16_t *__restrict__ A, const int32_t *__restrict__ a_rows,
     const int32_t *__restrict__ offsets, int E, const uint16_t *__restrict__ B1,
-    const uint16_t *__restrict__ B3, void *__restrict__ C, int N, int K) {
+    const uint16_t *__restrict__ B3, void *__restrict__ C_, int N, int K, int nsplit,
+    void *__restrict__ C_split) {
     constexpr int BK = 64;
     constexpr int BN = DUAL ? 128 : 256;   // output columns per block
     constexpr int ROWB = BK * 2;           // bytes per LDS row (8 slots of 16 bytes)
     constexpr int OPB = 256 * ROWB;        // bytes per operand per stage
     __shared__ __attribute__((aligned(1024))) char lds[2][2][OPB];
 
-    int e, row0, nrows, ntile;
-    if (!find_tile<BIG_BM>(offsets, E, (N + BN - 1) / BN, e, row0, nrows, ntile)) return;
+    int e, row0, nrows, ntile, split = 0;
+    if (!find_tile<BIG_BM>(offsets, E, (N + BN - 1) / BN, e, row0, nrows, ntile, nsplit, &split))
+        return;
+    void *const C = split ? C_split : C_;
     const int n0 = ntile * BN;
     const int tid = threadIdx.x, lane = tid & 63;
     // the wave index as a scalar, so LDS destinations (M0) and operand bases
@@ -349,12 +356,15 @@ __global__ __launch_bounds__(256) void gemm_bf16_big_kernel(
     // starve the MFMA pipe).  The last stage's
     // prefetch re-loads that stage into the idle buffer (nobody reads it),
     // which keeps the loop free of branches.
-    const int KT = K / BK;
+    // K split: this tile covers stages [split * KT, (split + 1) * KT); the
+    // second half writes its partial sums to C_split
+    const int KT = K / BK / nsplit;
+    const int kbeg = split * KT * BK;
 #pragma unroll
-    for (int q = 0; q < 16; ++q) issue_one(0, 0, q);
+    for (int q = 0; q < 16; ++q) issue_one(0, kbeg, q);
     for (int kt = 0; kt < KT; ++kt) {
         const int cur = kt & 1;
-        const int knext = min(kt + 1, KT - 1) * BK;
+        const int knext = kbeg + min(kt + 1, KT - 1) * BK;
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
         bf16x8_t fa[2][4], fb[2][4];
@@ -657,14 +667,15 @@ hipError_t launch_gemm(const Shape &s, const void *A, const int32_t *a_rows, con
 
 template <bool DUAL, int ACT, bool OUT_BF16>
 hipError_t launch_big(const Shape &s, const void *A, const int32_t *a_rows, const int32_t *offsets, const void *B1,
-                      const void *B3, void *C, int N, int K, hipStream_t st) {
+                      const void *B3, void *C, int N, int K, hipStream_t st, int nsplit = 1,
+                      void *C_split = nullptr) {
     constexpr int BN = DUAL ? 128 : 256;
     const unsigned nt = (unsigned)((N + BN - 1) / BN);
-    unsigned blocks = nt * row_tile_bound(s, BIG_BM);
+    unsigned blocks = nt * row_tile_bound(s, BIG_BM) * (unsigned)nsplit;
     blocks = (blocks + NUM_XCD - 1) / NUM_XCD * NUM_XCD;
     hipLaunchKernelGGL((gemm_bf16_big_kernel<DUAL, ACT, OUT_BF16>), dim3(blocks), dim3(256), 0, st,
                        (const uint16_t *)A, a_rows, offsets, s.E, (const uint16_t *)B1,
-                       (const uint16_t *)B3, C, N, K);
+                       (const uint16_t *)B3, C, N, K, nsplit, C_split);
     return hipGetLastError();
 }
 
@@ -737,8 +748,20 @@ hipError_t launch_expert_up(const Shape &s, const void *x_perm, const int32_t *a
     }
 }
 
+int down_ksplit(const Shape &s) {
+    if (s.dtype == 0 || skinny_tiles(s, s.d_ff) != 0 || pick_bm(s, s.d_ff) != BIG_BM) return 1;
+    if (s.d_ff < 4096 || (s.d_ff / 64) % 2 != 0) return 1;
+    // expected 256 x 256 output tiles: full row tiles plus about half a
+    // partial one per expert; split K in two when they would fill fewer than
+    // three rounds of the 256 CUs (one block per CU)
+    const int64_t tiles =
+        (int64_t)((s.d + 255) / 256) * ((int64_t)row_tile_bound(s, BIG_BM) - s.E + s.E / 2);
+    return tiles < 3 * 256 ? 2 : 1;
+}
+
 hipError_t launch_expert_down(const Shape &s, const void *H, const int32_t *offsets,
-                              const void *W2, float *y_perm, hipStream_t st) {
+                              const void *W2, float *y_perm, float *y_perm_part2,
+                              hipStream_t st) {
     if (s.dtype == 0) {
         int64_t blocks = s.Tk() < 16384 ? s.Tk() : 16384;
         hipLaunchKernelGGL(down_f32_kernel, dim3((unsigned)(blocks > 0 ? blocks : 1)), dim3(256), 0,
@@ -750,11 +773,50 @@ hipError_t launch_expert_down(const Shape &s, const void *H, const int32_t *offs
         return launch_skinny_any<false, ACT_NONE, false>(s, mt, H, nullptr, offsets, W2, nullptr, y_perm, s.d,
                                                           s.d_ff, st);
     switch (pick_bm(s, s.d_ff)) {
-    case BIG_BM: return launch_big<false, ACT_NONE, false>(s, H, nullptr, offsets, W2, nullptr, y_perm, s.d, s.d_ff, st);
+    case BIG_BM:
+        if (down_ksplit(s) == 2) {
+            if (y_perm_part2 == nullptr) return hipErrorInvalidValue;
+            return launch_big<false, ACT_NONE, false>(s, H, nullptr, offsets, W2, nullptr, y_perm, s.d,
+                                                       s.d_ff, st, 2, y_perm_part2);
+        }
+        return launch_big<false, ACT_NONE, false>(s, H, nullptr, offsets, W2, nullptr, y_perm, s.d, s.d_ff, st);
     case 128: return launch_gemm<128, 128, 2, 2, false, ACT_NONE, false>(s, H, nullptr, offsets, W2, nullptr, y_perm, s.d, s.d_ff, st);
     case 64:  return launch_gemm<64, 128, 2, 2, false, ACT_NONE, false>(s, H, nullptr, offsets, W2, nullptr, y_perm, s.d, s.d_ff, st);
     default:  return launch_gemm<32, 128, 1, 4, false, ACT_NONE, false>(s, H, nullptr, offsets, W2, nullptr, y_perm, s.d, s.d_ff, st);
     }
+}
+
+namespace {
+
+// y_perm[r] += part2[r] for the kept rows (the second K half of a split down
+// projection): the same fp32 addition, in the same order, as the combine's
+// when it reads both halves.
+__global__ __launch_bounds__(256) void add_partial_kernel(float *__restrict__ y,
+                                                          const float *__restrict__ p2,
+                                                          const int32_t *__restrict__ offsets,
+                                                          int E, int d) {
+    const int64_t n = (int64_t)offsets[E] * d / 4;
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
+        float4 a = ((float4 *)y)[i];
+        const float4 b = ((const float4 *)p2)[i];
+        a.x += b.x;
+        a.y += b.y;
+        a.z += b.z;
+        a.w += b.w;
+        ((float4 *)y)[i] = a;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_add_partial(const Shape &s, float *y_perm, const float *part2,
+                              const int32_t *offsets, hipStream_t st) {
+    int64_t blocks = ((int64_t)(row_tile_bound(s, 1) - s.E) * s.d / 4 + 255) / 256;
+    if (blocks > 8192) blocks = 8192;
+    if (blocks < 1) blocks = 1;
+    hipLaunchKernelGGL(add_partial_kernel, dim3((unsigned)blocks), dim3(256), 0, st, y_perm, part2,
+                       offsets, s.E, s.d);
+    return hipGetLastError();
 }
 
 }  // namespace moe

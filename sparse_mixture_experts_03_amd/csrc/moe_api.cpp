@@ -58,6 +58,7 @@ struct Layout {
     size_t topk_idx, gates, routed, kept, offsets;  // moe_forward's optional outputs
     size_t row_of_slot, token_of_row, dropped, stats;
     size_t x_perm, H, y_perm;
+    size_t y_perm2;  // second K half of a split down projection (0: no split)
     size_t total;
 };
 
@@ -95,6 +96,7 @@ Layout layout(const Shape &s) {
     L.x_perm = take(rows * (size_t)s.d * elem);
     L.H = take(rows * (size_t)s.d_ff * elem);
     L.y_perm = take(rows * (size_t)s.d * 4);
+    L.y_perm2 = moe::down_ksplit(s) == 2 ? take(rows * (size_t)s.d * 4) : 0;
     L.total = o;
     return L;
 }
@@ -205,7 +207,9 @@ int moe_expert_ffn(const moe_desc *desc, const void *x_perm, const int32_t *offs
     hipStream_t st = (hipStream_t)stream;
     void *H = at<char>(ws, L.H);
     MOE_TRY(moe::launch_expert_up(s, x_perm, nullptr, offsets, W1, W3, H, st));
-    MOE_TRY(moe::launch_expert_down(s, H, offsets, W2, y_perm, st));
+    float *part2 = L.y_perm2 ? at<float>(ws, L.y_perm2) : nullptr;
+    MOE_TRY(moe::launch_expert_down(s, H, offsets, W2, y_perm, part2, st));
+    if (part2) MOE_TRY(moe::launch_add_partial(s, y_perm, part2, offsets, st));
     return MOE_OK;
 }
 
@@ -215,7 +219,7 @@ int moe_combine(const moe_desc *desc, const float *y_perm, const int32_t *row_of
     int rc = check_desc(desc, &s);
     if (rc != MOE_OK) return rc;
     if (!y_perm || !row_of_slot || !gates || !y) return MOE_ERR_INVALID_ARG;
-    MOE_TRY(moe::launch_combine(s, y_perm, row_of_slot, gates, y, (hipStream_t)stream));
+    MOE_TRY(moe::launch_combine(s, y_perm, nullptr, row_of_slot, gates, y, (hipStream_t)stream));
     return MOE_OK;
 }
 
@@ -264,9 +268,10 @@ int moe_forward(const moe_desc *desc, const void *x, const float *W_r, const flo
     MOE_TRY(ev.record(st));
     MOE_TRY(moe::launch_expert_up(s, x, token_of_row, offsets, W1, W3, H, st));
     MOE_TRY(ev.record(st));
-    MOE_TRY(moe::launch_expert_down(s, H, offsets, W2, y_perm, st));
+    float *part2 = L.y_perm2 ? at<float>(ws, L.y_perm2) : nullptr;
+    MOE_TRY(moe::launch_expert_down(s, H, offsets, W2, y_perm, part2, st));
     MOE_TRY(ev.record(st));
-    MOE_TRY(moe::launch_combine(s, y_perm, row_of_slot, gates, y, st));
+    MOE_TRY(moe::launch_combine(s, y_perm, part2, row_of_slot, gates, y, st));
     MOE_TRY(ev.record(st));
     return MOE_OK;
 }

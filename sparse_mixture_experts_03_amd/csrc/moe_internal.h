@@ -61,12 +61,22 @@ hipError_t launch_gather(const Shape &s, const void *x, const int32_t *token_of_
 hipError_t launch_expert_up(const Shape &s, const void *x_perm, const int32_t *a_rows,
                             const int32_t *offsets, const void *W1, const void *W3, void *H,
                             hipStream_t st);
+// The down projection may split K in two (down_ksplit(s) == 2, when its
+// tiles would not fill three rounds of the CUs): the second half's partial
+// sums go to y_perm_part2 (same layout as y_perm) and must be added, either
+// by launch_add_partial or by the combine (which adds them before gating).
+int down_ksplit(const Shape &s);
 hipError_t launch_expert_down(const Shape &s, const void *H, const int32_t *offsets,
-                              const void *W2, float *y_perm, hipStream_t st);
+                              const void *W2, float *y_perm, float *y_perm_part2,
+                              hipStream_t st);
+hipError_t launch_add_partial(const Shape &s, float *y_perm, const float *part2,
+                              const int32_t *offsets, hipStream_t st);
 
 // ---- combine -------------------------------------------------------------
-hipError_t launch_combine(const Shape &s, const float *y_perm, const int32_t *row_of_slot,
-                          const float *gates, void *y, hipStream_t st);
+// y_perm_part2: nullptr, or the second K half of a split down projection.
+hipError_t launch_combine(const Shape &s, const float *y_perm, const float *y_perm_part2,
+                          const int32_t *row_of_slot, const float *gates, void *y,
+                          hipStream_t st);
 
 }  // namespace moe
 

@@ -40,6 +40,10 @@ SMALL = {
     # partial column tile in the down projection (320 = 256 + 64)
     "big_gelu": W["switch"].with_(name="big_gelu", T=1000, d=320, d_ff=384, E=4, cf=1.05,
                                   noise_std=0.25),
+    # the down projection splits K = d_ff in two when its tiles would not
+    # fill the CUs: two fp32 partials added before the gate (ragged experts,
+    # a partial column tile: 320 = 256 + 64)
+    "big_splitk": W["mixtral_prefill"].with_(name="big_splitk", T=1024, d=320, d_ff=4096),
     # weight-streaming kernel (at most 32 rows per expert, K % 128 == 0):
     # every token on both experts -> two full 16-row tiles of A per expert
     "skinny_full": W["mixtral_decode"].with_(name="skinny_full", T=32, d=256, d_ff=384, E=2),
@@ -94,7 +98,8 @@ def test_forward_matches_oracle(name):
         assert ref["dropped"].sum() > 0
 
 
-@pytest.mark.parametrize("name", ["mixtral_small", "zipf_small", "tiny", "switch_small"])
+@pytest.mark.parametrize("name", ["mixtral_small", "zipf_small", "tiny", "switch_small",
+                                  "big_splitk"])
 def test_staged_entry_points(name):
     """route, dispatch, expert_ffn and combine called one by one: x_perm is
     the exact gather, y_perm matches the oracle's per-row expert outputs,
