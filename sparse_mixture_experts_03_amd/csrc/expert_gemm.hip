@@ -31,6 +31,8 @@
 //
 // gemm_f32 kernels: a plain fp32 path (one block per row, one thread per
 // output column, sequential fp32 FMA over K) for fp32 layers.
+#include <type_traits>
+
 #include "moe_internal.h"
 
 namespace moe {
@@ -240,8 +242,8 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(
 // A block computes 256 rows x 256 weight rows (SwiGLU: 128 rows of W1 and
 // the same 128 rows of W3, i.e. 128 columns of H), four waves of 128 x 128.
 // Operands go from global memory straight into LDS with
-// global_load_lds_dwordx4 (no register staging): instruction j of wave w
-// fills LDS rows 8*(8w + j) .. +8, lane l writing the 16 bytes at
+// buffer_load_dwordx4 ... lds (no register staging): instruction j of wave
+// w fills LDS rows 8*(8w + j) .. +8, lane l writing the 16 bytes at
 // (row 8*(8w + j) + l/8, slot l%8).  Slot s of row r holds k-chunk
 // s ^ f(r), f(r) = (r % 8) ^ ((r / 8) % 2): an XOR swizzle under which any
 // 8 consecutive rows use 8 different slots and any 16 consecutive rows use
@@ -251,6 +253,13 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(
 // the loads for stage k+1 are issued right after the barrier that opens
 // stage k, and run under stage k's 64 MFMAs per wave.  Fragments for the
 // next 16-wide k step are read from LDS while the current step's MFMAs run.
+//
+// The stage loop carries no vector address arithmetic: a load's address is
+// a per-lane offset fixed for the whole tile plus the stage's k offset in
+// a scalar register (buffer addressing), and a fragment read is one of
+// eight per-lane LDS offsets (operand x k step) plus an immediate (stage,
+// fragment row).  The loop is unrolled by two stages so that the stage
+// buffer is a compile-time constant.
 constexpr int BIG_BM = 256;
 
 template <bool DUAL, int ACT, bool OUT_BF16>
@@ -263,6 +272,7 @@ __global__ __launch_bounds__(256) void gemm_bf16_big_kernel(
     constexpr int BN = DUAL ? 128 : 256;   // output columns per block
     constexpr int ROWB = BK * 2;           // bytes per LDS row (8 slots of 16 bytes)
     constexpr int OPB = 256 * ROWB;        // bytes per operand per stage
+    // [operand][stage]: operand o, stage s at (2o + s) * OPB
     __shared__ __attribute__((aligned(1024))) char lds[2][2][OPB];
 
     int e, row0, nrows, ntile, split = 0;
@@ -278,11 +288,14 @@ __global__ __launch_bounds__(256) void gemm_bf16_big_kernel(
 
     // LDS row 8*(8w + j) + l/8 has f = (l/8) ^ (j % 2), so lane l of load j
     // fetches k-chunk (l % 8) ^ (l / 8) ^ (j % 2).  Per-lane byte offsets
-    // from a scalar base; they do not change from stage to stage.
+    // into the operand; they do not change from stage to stage.
     const int sub = lane >> 3;  // row within an 8-row group
     uint32_t a_off[8], b_off[8];
-    const char *abase = (const char *)A;
-    const char *bbase;
+    // buffer resources (dword 3 = 0x00020000: raw 32-bit data, no swizzle,
+    // bounds not relied on: every offset is in range by construction)
+    const __amdgpu_buffer_rsrc_t a_rsrc =
+        __builtin_amdgcn_make_buffer_rsrc((void *)A, 0, 0x7fffffff, 0x00020000);
+    __amdgpu_buffer_rsrc_t b_rsrc;
     {
         const int wrow0 = wave * 64;  // first LDS row this wave fills
 #pragma unroll
@@ -293,7 +306,8 @@ __global__ __launch_bounds__(256) void gemm_bf16_big_kernel(
             a_off[j] = ((uint32_t)(a_rows ? a_rows[ar] : ar) * (uint32_t)K + kchunk) * 2u;
         }
         // SwiGLU: waves 0,1 fill W1 rows 0..127, waves 2,3 W3 rows 0..127
-        bbase = (const char *)((DUAL && wave >= 2) ? B3 : B1) + (int64_t)e * N * K * 2;
+        const uint16_t *bb = ((DUAL && wave >= 2) ? B3 : B1) + (int64_t)e * N * K;
+        b_rsrc = __builtin_amdgcn_make_buffer_rsrc((void *)bb, 0, 0x7fffffff, 0x00020000);
         const int brow0 = DUAL ? (wrow0 & 127) : wrow0;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
@@ -304,17 +318,17 @@ __global__ __launch_bounds__(256) void gemm_bf16_big_kernel(
     }
     // global -> LDS load q (0..15) of a stage: q < 8 from A, else from the weights
     auto issue_one = [&](int stage, int k0, int q) {
-        const size_t kb = (size_t)k0 * 2;
+        const int kb = k0 * 2;
         if (q < 8)
-            __builtin_amdgcn_global_load_lds(
-                (const void *)(abase + kb + a_off[q]),
-                (__attribute__((address_space(3))) void *)(lds[stage][0] + wave * 64 * ROWB + q * 8 * ROWB),
-                16, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                a_rsrc,
+                (__attribute__((address_space(3))) void *)(lds[0][stage] + wave * 64 * ROWB + q * 8 * ROWB),
+                16, a_off[q], kb, 0, 0);
         else
-            __builtin_amdgcn_global_load_lds(
-                (const void *)(bbase + kb + b_off[q - 8]),
-                (__attribute__((address_space(3))) void *)(lds[stage][1] + wave * 64 * ROWB + (q - 8) * 8 * ROWB),
-                16, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                b_rsrc,
+                (__attribute__((address_space(3))) void *)(lds[1][stage] + wave * 64 * ROWB + (q - 8) * 8 * ROWB),
+                16, b_off[q - 8], kb, 0, 0);
     };
 
     f32x16_t acc[4][4];
@@ -325,24 +339,33 @@ __global__ __launch_bounds__(256) void gemm_bf16_big_kernel(
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-    // fragment rows in LDS: A rows wm*128 + i*32 + lane%32; weight rows of
-    // column group j (DUAL: j < 2 -> W1 rows wn*64 + j*32, j >= 2 -> W3)
+    // Fragment rows: A rows wm*128 + i*32 + lane%32; weight rows of column
+    // group j (DUAL: j < 2 -> W1 rows wn*64 + j*32, j >= 2 -> W3 rows, 128
+    // further on).  The swizzle only depends on lane % 32 and the k step,
+    // so each (operand, k step) has one per-lane offset and every fragment
+    // row, stage and operand is an immediate on top of it.
+    // (The weight operand's 64 KB base is part of the per-lane offset, which
+    // is made opaque to the compiler so that it does not move the base into
+    // the immediate, where it would not fit in the 16-bit offset field.)
     const int lr = lane & 31;
-    int brow[4];
+    uint32_t rd_a[4], rd_b[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-        brow[j] = DUAL ? ((j >> 1) * 128 + wn * 64 + (j & 1) * 32 + lr) : (wn * 128 + j * 32 + lr);
-
-    // fragment read f (0..7) of k step kk, in the order the MFMAs consume
-    // them: A0, B0, B1, B2, B3, A1, A2, A3
-    auto read_one = [&](int stage, int kk, int f, bf16x8_t (&a)[4], bf16x8_t (&b)[4]) {
-        // fragment rows are 32-aligned bases + lane % 32
-        const int slot = ((kk * 2 + (lane >> 5)) ^ (lr & 7) ^ ((lr >> 3) & 1)) * 16;
+    for (int kk = 0; kk < 4; ++kk) {
+        const uint32_t slot = (uint32_t)(((kk * 2 + (lane >> 5)) ^ (lr & 7) ^ ((lr >> 3) & 1)) * 16);
+        rd_a[kk] = (uint32_t)(wm * 128 + lr) * ROWB + slot;
+        rd_b[kk] = 2u * OPB + (uint32_t)((DUAL ? wn * 64 : wn * 128) + lr) * ROWB + slot;
+        asm volatile("" : "+v"(rd_a[kk]), "+v"(rd_b[kk]));
+    }
+    char *const lds0 = &lds[0][0][0];
+    auto read_one = [&](auto stage_c, int kk, int f, bf16x8_t (&a)[4], bf16x8_t (&b)[4]) {
+        constexpr int stage = decltype(stage_c)::value;
         if (f == 0 || f >= 5) {
             const int i = f == 0 ? 0 : f - 4;
-            a[i] = *(const bf16x8_t *)(lds[stage][0] + (wm * 128 + i * 32 + lr) * ROWB + slot);
+            a[i] = *(const bf16x8_t *)(lds0 + rd_a[kk] + (stage * OPB + i * 32 * ROWB));
         } else {
-            b[f - 1] = *(const bf16x8_t *)(lds[stage][1] + brow[f - 1] * ROWB + slot);
+            const int j = f - 1;
+            const int jo = DUAL ? ((j >> 1) * 128 + (j & 1) * 32) : j * 32;
+            b[j] = *(const bf16x8_t *)(lds0 + rd_b[kk] + (stage * OPB + jo * ROWB));
         }
     };
 
@@ -356,20 +379,19 @@ __global__ __launch_bounds__(256) void gemm_bf16_big_kernel(
     // starve the MFMA pipe).  The last stage's
     // prefetch re-loads that stage into the idle buffer (nobody reads it),
     // which keeps the loop free of branches.
-    // K split: this tile covers stages [split * KT, (split + 1) * KT); the
-    // second half writes its partial sums to C_split
+    // K split: this tile covers stages [split * KT, (split + 1) * KT) and
+    // the second half writes its partial sums to C_split
     const int KT = K / BK / nsplit;
     const int kbeg = split * KT * BK;
-#pragma unroll
-    for (int q = 0; q < 16; ++q) issue_one(0, kbeg, q);
-    for (int kt = 0; kt < KT; ++kt) {
-        const int cur = kt & 1;
+    auto stage_body = [&](auto cur_c, int kt) {
+        constexpr int cur = decltype(cur_c)::value;
+        constexpr std::integral_constant<int, cur ^ 1> nxt_c{};
         const int knext = kbeg + min(kt + 1, KT - 1) * BK;
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
         bf16x8_t fa[2][4], fb[2][4];
 #pragma unroll
-        for (int f = 0; f < 8; ++f) read_one(cur, 0, f, fa[0], fb[0]);
+        for (int f = 0; f < 8; ++f) read_one(cur_c, 0, f, fa[0], fb[0]);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
@@ -378,12 +400,21 @@ __global__ __launch_bounds__(256) void gemm_bf16_big_kernel(
                 const int i = t >> 2, j = t & 3;
                 acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[kk & 1][i], fb[kk & 1][j],
                                                                     acc[i][j], 0, 0, 0);
-                if (kk < 2 && (t & 1)) issue_one(cur ^ 1, knext, kk * 8 + (t >> 1));
-                if (kk < 3 && t < 8) read_one(cur, kk + 1, t, fa[(kk + 1) & 1], fb[(kk + 1) & 1]);
+                if (kk < 2 && (t & 1)) issue_one(nxt_c, knext, kk * 8 + (t >> 1));
+                if (kk < 3 && t < 8) read_one(cur_c, kk + 1, t, fa[(kk + 1) & 1], fb[(kk + 1) & 1]);
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
+    };
+#pragma unroll
+    for (int q = 0; q < 16; ++q) issue_one(0, kbeg, q);
+    int kt = 0;
+    for (; kt + 1 < KT; kt += 2) {
+        stage_body(std::integral_constant<int, 0>{}, kt);
+        stage_body(std::integral_constant<int, 1>{}, kt + 1);
     }
+    if (kt < KT) stage_body(std::integral_constant<int, 0>{}, kt);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -646,7 +677,10 @@ inline int pick_bm(const Shape &s, int K) {
     int64_t rows = s.Tk();
     if (s.C >= 0 && (int64_t)s.E * s.C < rows) rows = (int64_t)s.E * s.C;
     const int64_t mean = rows / s.E;
-    if (mean >= 192 && K % 64 == 0) return BIG_BM;
+    // the 256-row kernel keeps operand offsets in 32 bits
+    const bool off32 = (rows > s.T ? rows : (int64_t)s.T) * K * 2 < (int64_t(1) << 32) &&
+                       (int64_t)s.d * s.d_ff * 2 < (int64_t(1) << 32);
+    if (mean >= 192 && K % 64 == 0 && off32) return BIG_BM;
     if (mean >= 96) return 128;
     if (mean >= 24) return 64;
     return 32;
