@@ -383,16 +383,21 @@ __global__ __launch_bounds__(256) void gemm_bf16_big_kernel(
     // the second half writes its partial sums to C_split
     const int KT = K / BK / nsplit;
     const int kbeg = split * KT * BK;
+    bf16x8_t fa[2][4], fb[2][4];
     auto stage_body = [&](auto cur_c, int kt) {
         constexpr int cur = decltype(cur_c)::value;
         constexpr std::integral_constant<int, cur ^ 1> nxt_c{};
         const int knext = kbeg + min(kt + 1, KT - 1) * BK;
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
-        bf16x8_t fa[2][4], fb[2][4];
+        // this wave's loads of the stage have landed; after the barrier,
+        // everyone's have
+        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        // step 0's fragments in consumption order (kept by the scheduling
+        // barriers), so the first MFMA waits for two reads, not eight
 #pragma unroll
-        for (int f = 0; f < 8; ++f) read_one(cur_c, 0, f, fa[0], fb[0]);
-        __builtin_amdgcn_sched_barrier(0);
+        for (int f = 0; f < 8; ++f) {
+            read_one(cur_c, 0, f, fa[0], fb[0]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
 #pragma unroll
