@@ -421,6 +421,37 @@ __global__ __launch_bounds__(256) void gemm_bf16_big_kernel(
     if (kt < KT) stage_body(std::integral_constant<int, 0>{}, kt);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
+    if (nrows == BIG_BM && n0 + BN <= N) {
+        // whole tile in range: no per-element bounds checks; buffer stores
+        // whose row offset is a scalar (row * N * element size) and whose
+        // lane offset (row 4 * (lane / 32) of each 8-row group, column
+        // lane % 32) is fixed, with the 32-column group as an immediate
+        constexpr int ES = OUT_BF16 ? 2 : 4;
+        const __amdgpu_buffer_rsrc_t c_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+            (char *)C + (int64_t)row0 * N * ES, 0, 0x7fffffff, 0x00020000);
+        const uint32_t vo =
+            ((uint32_t)(4 * (lane >> 5)) * (uint32_t)N + (uint32_t)(n0 + (DUAL ? wn * 64 : wn * 128) + lr)) * ES;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int jj = 0; jj < (DUAL ? 2 : 4); ++jj) {
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const uint32_t so =
+                        (uint32_t)(wm * 128 + i * 32 + (r >> 2) * 8 + (r & 3)) * (uint32_t)(N * ES);
+                    const float v = DUAL ? apply_act(ACT, acc[i][jj][r], acc[i][jj + 2][r])
+                                         : apply_act(ACT, acc[i][jj][r], 0.f);
+                    if (OUT_BF16)
+                        __builtin_amdgcn_raw_buffer_store_b16(
+                            __builtin_bit_cast(unsigned short, (__bf16)v), c_rsrc, vo + jj * 32 * ES, so, 0);
+                    else
+                        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned int, v), c_rsrc,
+                                                              vo + jj * 32 * ES, so, 0);
+                }
+            }
+        return;
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -684,7 +715,8 @@ inline int pick_bm(const Shape &s, int K) {
     const int64_t mean = rows / s.E;
     // the 256-row kernel keeps operand offsets in 32 bits
     const bool off32 = (rows > s.T ? rows : (int64_t)s.T) * K * 2 < (int64_t(1) << 32) &&
-                       (int64_t)s.d * s.d_ff * 2 < (int64_t(1) << 32);
+                       (int64_t)s.d * s.d_ff * 2 < (int64_t(1) << 32) &&
+                       (int64_t)BIG_BM * (s.d > s.d_ff ? s.d : s.d_ff) * 4 < (int64_t(1) << 31);
     if (mean >= 192 && K % 64 == 0 && off32) return BIG_BM;
     if (mean >= 96) return 128;
     if (mean >= 24) return 64;
