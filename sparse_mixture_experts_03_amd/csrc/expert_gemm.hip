@@ -239,20 +239,23 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(
 // ---- large row tiles: direct-to-LDS loads, 256 x 256 tiles ----------------
 //
 // gemm_bf16_big_kernel, for experts with many rows and K a multiple of 64.
-// A block computes 256 rows x 256 weight rows (SwiGLU: 128 rows of W1 and
-// the same 128 rows of W3, i.e. 128 columns of H), four waves of 128 x 128.
+// A block computes up to 256 rows x 256 weight rows (SwiGLU: 128 rows of W1
+// and the same 128 rows of W3, i.e. 128 columns of H) with four waves in a
+// 2 x 2 grid.  An expert's row tiles are 256 rows, except its last, which
+// takes only as many 64-row slabs as it needs (MI = 1..4 slabs; each wave
+// then holds MI 32-row fragments), so a ragged expert pads at most 63 rows
+// instead of up to 255.
 // Operands go from global memory straight into LDS with
-// buffer_load_dwordx4 ... lds (no register staging): instruction j of wave
-// w fills LDS rows 8*(8w + j) .. +8, lane l writing the 16 bytes at
-// (row 8*(8w + j) + l/8, slot l%8).  Slot s of row r holds k-chunk
-// s ^ f(r), f(r) = (r % 8) ^ ((r / 8) % 2): an XOR swizzle under which any
-// 8 consecutive rows use 8 different slots and any 16 consecutive rows use
-// 16 different (row parity, slot) pairs, so the rows a fragment read
-// serves together fall on distinct banks whether the LDS serves 8 or 16
-// lanes of a 16-byte read per cycle.  Two LDS stages (2 x 64 KB):
-// the loads for stage k+1 are issued right after the barrier that opens
-// stage k, and run under stage k's 64 MFMAs per wave.  Fragments for the
-// next 16-wide k step are read from LDS while the current step's MFMAs run.
+// buffer_load_dwordx4 ... lds (no register staging): instruction j of a
+// wave fills 8 LDS rows, lane l writing the 16 bytes at (row + l/8, slot
+// l%8).  Slot s of row r holds k-chunk s ^ f(r), f(r) = (r % 8) ^
+// ((r / 8) % 2): an XOR swizzle under which any 8 consecutive rows use 8
+// different slots and any 16 consecutive rows use 16 different (row parity,
+// slot) pairs, so the rows a fragment read serves together fall on distinct
+// banks whether the LDS serves 8 or 16 lanes of a 16-byte read per cycle.
+// Two LDS stages (2 x 64 KB): the loads for stage k+1 are issued in the
+// first half of stage k and run under its MFMAs.  Fragments for the next
+// 16-wide k step are read from LDS while the current step's MFMAs run.
 //
 // The stage loop carries no vector address arithmetic: a load's address is
 // a per-lane offset fixed for the whole tile plus the stage's k offset in
@@ -262,53 +265,50 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(
 // buffer is a compile-time constant.
 constexpr int BIG_BM = 256;
 
-template <bool DUAL, int ACT, bool OUT_BF16>
-__global__ __launch_bounds__(256) void gemm_bf16_big_kernel(
-    const uint16_t *__restrict__ A, const int32_t *__restrict__ a_rows,
-    const int32_t *__restrict__ offsets, int E, const uint16_t *__restrict__ B1,
-    const uint16_t *__restrict__ B3, void *__restrict__ C_, int N, int K, int nsplit,
-    void *__restrict__ C_split) {
+template <int MI, bool DUAL, int ACT, bool OUT_BF16>
+__device__ __forceinline__ void big_tile(char (*lds)[2][256 * 128], const uint16_t *__restrict__ A,
+                                         const int32_t *__restrict__ a_rows,
+                                         const uint16_t *__restrict__ B1,
+                                         const uint16_t *__restrict__ B3, void *__restrict__ C, int N,
+                                         int K, int e, int row0, int nrows, int n0, int KT, int kbeg) {
     constexpr int BK = 64;
     constexpr int BN = DUAL ? 128 : 256;   // output columns per block
     constexpr int ROWB = BK * 2;           // bytes per LDS row (8 slots of 16 bytes)
     constexpr int OPB = 256 * ROWB;        // bytes per operand per stage
-    // [operand][stage]: operand o, stage s at (2o + s) * OPB
-    __shared__ __attribute__((aligned(1024))) char lds[2][2][OPB];
-
-    int e, row0, nrows, ntile, split = 0;
-    if (!find_tile<BIG_BM>(offsets, E, (N + BN - 1) / BN, e, row0, nrows, ntile, nsplit, &split))
-        return;
-    void *const C = split ? C_split : C_;
-    const int n0 = ntile * BN;
+    constexpr int WROWS = MI * 32;         // A rows per wave row (wm)
+    constexpr int NQA = 2 * MI;            // A loads per wave per stage (8 rows each)
+    constexpr int NQ = NQA + 8;            // + 8 weight loads
+    constexpr int NMF = MI * 4;            // MFMAs per wave per 16-wide k step
+    constexpr int NRD = MI + 4;            // fragment reads per k step
     const int tid = threadIdx.x, lane = tid & 63;
     // the wave index as a scalar, so LDS destinations (M0) and operand bases
     // are computed on the scalar unit
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave >> 1, wn = wave & 1;
 
-    // LDS row 8*(8w + j) + l/8 has f = (l/8) ^ (j % 2), so lane l of load j
-    // fetches k-chunk (l % 8) ^ (l / 8) ^ (j % 2).  Per-lane byte offsets
-    // into the operand; they do not change from stage to stage.
-    const int sub = lane >> 3;  // row within an 8-row group
-    uint32_t a_off[8], b_off[8];
+    // LDS A rows MI*16*w + 8j + l/8 and weight rows 64w + 8j + l/8 both have
+    // f = (l/8) ^ (j % 2), so lane l of load j fetches k-chunk
+    // (l % 8) ^ (l / 8) ^ (j % 2).  Per-lane byte offsets into the operand;
+    // they do not change from stage to stage.
+    const int sub = lane >> 3;
+    uint32_t a_off[NQA], b_off[8];
     // buffer resources (dword 3 = 0x00020000: raw 32-bit data, no swizzle,
     // bounds not relied on: every offset is in range by construction)
     const __amdgpu_buffer_rsrc_t a_rsrc =
         __builtin_amdgcn_make_buffer_rsrc((void *)A, 0, 0x7fffffff, 0x00020000);
     __amdgpu_buffer_rsrc_t b_rsrc;
     {
-        const int wrow0 = wave * 64;  // first LDS row this wave fills
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
+        for (int j = 0; j < NQA; ++j) {
             const int kchunk = ((lane & 7) ^ sub ^ (j & 1)) * 8;
-            const int r = wrow0 + j * 8 + sub;
+            const int r = wave * (MI * 16) + j * 8 + sub;
             const int ar = row0 + min(r, nrows - 1);
             a_off[j] = ((uint32_t)(a_rows ? a_rows[ar] : ar) * (uint32_t)K + kchunk) * 2u;
         }
         // SwiGLU: waves 0,1 fill W1 rows 0..127, waves 2,3 W3 rows 0..127
         const uint16_t *bb = ((DUAL && wave >= 2) ? B3 : B1) + (int64_t)e * N * K;
         b_rsrc = __builtin_amdgcn_make_buffer_rsrc((void *)bb, 0, 0x7fffffff, 0x00020000);
-        const int brow0 = DUAL ? (wrow0 & 127) : wrow0;
+        const int brow0 = DUAL ? ((wave * 64) & 127) : wave * 64;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             const int kchunk = ((lane & 7) ^ sub ^ (j & 1)) * 8;
@@ -316,48 +316,51 @@ __global__ __launch_bounds__(256) void gemm_bf16_big_kernel(
             b_off[j] = ((uint32_t)min(n0 + r, N - 1) * (uint32_t)K + kchunk) * 2u;
         }
     }
-    // global -> LDS load q (0..15) of a stage: q < 8 from A, else from the weights
+    // global -> LDS load q (0..NQ-1) of a stage: q < NQA from A, else from
+    // the weights
     auto issue_one = [&](int stage, int k0, int q) {
         const int kb = k0 * 2;
-        if (q < 8)
+        if (q < NQA)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
                 a_rsrc,
-                (__attribute__((address_space(3))) void *)(lds[0][stage] + wave * 64 * ROWB + q * 8 * ROWB),
+                (__attribute__((address_space(3))) void *)(lds[0][stage] + (wave * (MI * 16) + q * 8) * ROWB),
                 16, a_off[q], kb, 0, 0);
         else
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
                 b_rsrc,
-                (__attribute__((address_space(3))) void *)(lds[1][stage] + wave * 64 * ROWB + (q - 8) * 8 * ROWB),
-                16, b_off[q - 8], kb, 0, 0);
+                (__attribute__((address_space(3))) void *)(lds[1][stage] + (wave * 64 + (q - NQA) * 8) * ROWB),
+                16, b_off[q - NQA], kb, 0, 0);
     };
 
-    f32x16_t acc[4][4];
+    f32x16_t acc[MI][4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < MI; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-    // Fragment rows: A rows wm*128 + i*32 + lane%32; weight rows of column
-    // group j (DUAL: j < 2 -> W1 rows wn*64 + j*32, j >= 2 -> W3 rows, 128
-    // further on).  The swizzle only depends on lane % 32 and the k step,
+    // Fragment rows: A rows wm*WROWS + i*32 + lane%32; weight rows of
+    // column group j (DUAL: j < 2 -> W1 rows wn*64 + j*32, j >= 2 -> W3 rows,
+    // 128 further on).  The swizzle only depends on lane % 32 and the k step,
     // so each (operand, k step) has one per-lane offset and every fragment
-    // row, stage and operand is an immediate on top of it.
-    // (The weight operand's 64 KB base is part of the per-lane offset, which
-    // is made opaque to the compiler so that it does not move the base into
-    // the immediate, where it would not fit in the 16-bit offset field.)
+    // row, stage and operand is an immediate on top of it.  (The weight
+    // operand's 64 KB base is part of the per-lane offset, which is made
+    // opaque to the compiler so that it does not move the base into the
+    // immediate, where it would not fit in the 16-bit offset field.)
     const int lr = lane & 31;
     uint32_t rd_a[4], rd_b[4];
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
         const uint32_t slot = (uint32_t)(((kk * 2 + (lane >> 5)) ^ (lr & 7) ^ ((lr >> 3) & 1)) * 16);
-        rd_a[kk] = (uint32_t)(wm * 128 + lr) * ROWB + slot;
+        rd_a[kk] = (uint32_t)(wm * WROWS + lr) * ROWB + slot;
         rd_b[kk] = 2u * OPB + (uint32_t)((DUAL ? wn * 64 : wn * 128) + lr) * ROWB + slot;
         asm volatile("" : "+v"(rd_a[kk]), "+v"(rd_b[kk]));
     }
     char *const lds0 = &lds[0][0][0];
-    auto read_one = [&](auto stage_c, int kk, int f, bf16x8_t (&a)[4], bf16x8_t (&b)[4]) {
+    // fragment read f (0..NRD-1) of k step kk, in the order the MFMAs
+    // consume them: A0, B0, B1, B2, B3, A1, ..., A(MI-1)
+    auto read_one = [&](auto stage_c, int kk, int f, bf16x8_t (&a)[MI], bf16x8_t (&b)[4]) {
         constexpr int stage = decltype(stage_c)::value;
         if (f == 0 || f >= 5) {
             const int i = f == 0 ? 0 : f - 4;
@@ -369,21 +372,16 @@ __global__ __launch_bounds__(256) void gemm_bf16_big_kernel(
         }
     };
 
-    // The stage loop is written as explicit bundles in issue order, each
-    // closed by a scheduling barrier: 64 MFMAs (i-major, so consecutive
-    // MFMAs never share an accumulator); with each of the first 8 MFMAs of
-    // steps 0..2 one fragment read for the next step (8 MFMAs of slack
-    // before the step boundary waits for them); with every second MFMA of
-    // steps 0 and 1 one global->LDS load of the next stage (early enough to
-    // land before the stage ends, spread out so that their issue does not
-    // starve the MFMA pipe).  The last stage's
-    // prefetch re-loads that stage into the idle buffer (nobody reads it),
-    // which keeps the loop free of branches.
-    // K split: this tile covers stages [split * KT, (split + 1) * KT) and
-    // the second half writes its partial sums to C_split
-    const int KT = K / BK / nsplit;
-    const int kbeg = split * KT * BK;
-    bf16x8_t fa[2][4], fb[2][4];
+    // A stage is written as explicit bundles in issue order, each closed by
+    // a scheduling barrier: 4 k steps of NMF MFMAs (i-major, so consecutive
+    // MFMAs never share an accumulator); during each of steps 0..2 the NRD
+    // fragment reads of the next step; during steps 0 and 1 the NQ
+    // global->LDS loads of the next stage, spread evenly (every second MFMA
+    // for a full tile: early enough to land before the stage ends, spread
+    // out so that their issue does not starve the MFMA pipe).  The last
+    // stage's prefetch re-loads that stage into the idle buffer (nobody
+    // reads it), which keeps the loop free of branches.
+    bf16x8_t fa[2][MI], fb[2][4];
     auto stage_body = [&](auto cur_c, int kt) {
         constexpr int cur = decltype(cur_c)::value;
         constexpr std::integral_constant<int, cur ^ 1> nxt_c{};
@@ -392,27 +390,40 @@ __global__ __launch_bounds__(256) void gemm_bf16_big_kernel(
         // everyone's have
         asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
         // step 0's fragments in consumption order (kept by the scheduling
-        // barriers), so the first MFMA waits for two reads, not eight
+        // barriers), so the first MFMA waits for two reads, not all of them
 #pragma unroll
-        for (int f = 0; f < 8; ++f) {
+        for (int f = 0; f < NRD; ++f) {
             read_one(cur_c, 0, f, fa[0], fb[0]);
             __builtin_amdgcn_sched_barrier(0);
         }
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
 #pragma unroll
-            for (int t = 0; t < 16; ++t) {
+            for (int t = 0; t < NMF; ++t) {
                 const int i = t >> 2, j = t & 3;
                 acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[kk & 1][i], fb[kk & 1][j],
                                                                     acc[i][j], 0, 0, 0);
-                if (kk < 2 && (t & 1)) issue_one(nxt_c, knext, kk * 8 + (t >> 1));
-                if (kk < 3 && t < 8) read_one(cur_c, kk + 1, t, fa[(kk + 1) & 1], fb[(kk + 1) & 1]);
+                if (kk < 2) {
+                    // load q with the MFMA u = min(q * 2 NMF / NQ + 1, 2 NMF - 1)
+                    // of steps 0..1 (a full tile: every odd MFMA)
+                    const int u = kk * NMF + t;
+#pragma unroll
+                    for (int q = 0; q < NQ; ++q)
+                        if (min((q * 2 * NMF) / NQ + 1, 2 * NMF - 1) == u) issue_one(nxt_c, knext, q);
+                }
+                if (kk < 3) {
+                    // read f with MFMA min(f, NMF - 1) of the step
+#pragma unroll
+                    for (int f = 0; f < NRD; ++f)
+                        if (min(f, NMF - 1) == t)
+                            read_one(cur_c, kk + 1, f, fa[(kk + 1) & 1], fb[(kk + 1) & 1]);
+                }
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
     };
 #pragma unroll
-    for (int q = 0; q < 16; ++q) issue_one(0, kbeg, q);
+    for (int q = 0; q < NQ; ++q) issue_one(0, kbeg, q);
     int kt = 0;
     for (; kt + 1 < KT; kt += 2) {
         stage_body(std::integral_constant<int, 0>{}, kt);
@@ -421,7 +432,7 @@ __global__ __launch_bounds__(256) void gemm_bf16_big_kernel(
     if (kt < KT) stage_body(std::integral_constant<int, 0>{}, kt);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
-    if (nrows == BIG_BM && n0 + BN <= N) {
+    if (nrows == MI * 64 && n0 + BN <= N) {
         // whole tile in range: no per-element bounds checks; buffer stores
         // whose row offset is a scalar (row * N * element size) and whose
         // lane offset (row 4 * (lane / 32) of each 8-row group, column
@@ -432,14 +443,14 @@ __global__ __launch_bounds__(256) void gemm_bf16_big_kernel(
         const uint32_t vo =
             ((uint32_t)(4 * (lane >> 5)) * (uint32_t)N + (uint32_t)(n0 + (DUAL ? wn * 64 : wn * 128) + lr)) * ES;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < MI; ++i)
 #pragma unroll
             for (int jj = 0; jj < (DUAL ? 2 : 4); ++jj) {
                 __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const uint32_t so =
-                        (uint32_t)(wm * 128 + i * 32 + (r >> 2) * 8 + (r & 3)) * (uint32_t)(N * ES);
+                        (uint32_t)(wm * WROWS + i * 32 + (r >> 2) * 8 + (r & 3)) * (uint32_t)(N * ES);
                     const float v = DUAL ? apply_act(ACT, acc[i][jj][r], acc[i][jj + 2][r])
                                          : apply_act(ACT, acc[i][jj][r], 0.f);
                     if (OUT_BF16)
@@ -453,7 +464,7 @@ __global__ __launch_bounds__(256) void gemm_bf16_big_kernel(
         return;
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < MI; ++i)
 #pragma unroll
         for (int jj = 0; jj < (DUAL ? 2 : 4); ++jj) {
             // one 32 x 32 tile at a time: keeps the activation's temporaries
@@ -462,7 +473,7 @@ __global__ __launch_bounds__(256) void gemm_bf16_big_kernel(
             const int col = n0 + (DUAL ? wn * 64 + jj * 32 : wn * 128 + jj * 32) + lr;
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int row = wm * 128 + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+                const int row = wm * WROWS + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
                 if (row < nrows && col < N) {
                     const float v = DUAL ? apply_act(ACT, acc[i][jj][r], acc[i][jj + 2][r])
                                          : apply_act(ACT, acc[i][jj][r], 0.f);
@@ -474,6 +485,35 @@ __global__ __launch_bounds__(256) void gemm_bf16_big_kernel(
                 }
             }
         }
+}
+
+template <bool DUAL, int ACT, bool OUT_BF16>
+__global__ __launch_bounds__(256) void gemm_bf16_big_kernel(
+    const uint16_t *__restrict__ A, const int32_t *__restrict__ a_rows,
+    const int32_t *__restrict__ offsets, int E, const uint16_t *__restrict__ B1,
+    const uint16_t *__restrict__ B3, void *__restrict__ C_, int N, int K, int nsplit,
+    void *__restrict__ C_split) {
+    constexpr int BN = DUAL ? 128 : 256;
+    // [operand][stage]: operand o, stage s at (2o + s) * 32 KB
+    __shared__ __attribute__((aligned(1024))) char lds[2][2][256 * 128];
+
+    int e, row0, nrows, ntile, split = 0;
+    if (!find_tile<BIG_BM>(offsets, E, (N + BN - 1) / BN, e, row0, nrows, ntile, nsplit, &split))
+        return;
+    // K split: this tile covers stages [split * KT, (split + 1) * KT) and
+    // the second half writes its partial sums to C_split
+    void *const C = split ? C_split : C_;
+    const int KT = K / 64 / nsplit;
+    const int kbeg = split * KT * 64;
+    const int mi = (nrows + 63) >> 6;   // 64-row slabs this tile needs
+    if (mi == 4)
+        big_tile<4, DUAL, ACT, OUT_BF16>(lds, A, a_rows, B1, B3, C, N, K, e, row0, nrows, ntile * BN, KT, kbeg);
+    else if (mi == 3)
+        big_tile<3, DUAL, ACT, OUT_BF16>(lds, A, a_rows, B1, B3, C, N, K, e, row0, nrows, ntile * BN, KT, kbeg);
+    else if (mi == 2)
+        big_tile<2, DUAL, ACT, OUT_BF16>(lds, A, a_rows, B1, B3, C, N, K, e, row0, nrows, ntile * BN, KT, kbeg);
+    else
+        big_tile<1, DUAL, ACT, OUT_BF16>(lds, A, a_rows, B1, B3, C, N, K, e, row0, nrows, ntile * BN, KT, kbeg);
 }
 
 // ---- skinny row groups (decode batches): weight streaming ----------------

@@ -44,6 +44,13 @@ SMALL = {
     # fill the CUs: two fp32 partials added before the gate (ragged experts,
     # a partial column tile: 320 = 256 + 64)
     "big_splitk": W["mixtral_prefill"].with_(name="big_splitk", T=1024, d=320, d_ff=4096),
+    # Zipf-skewed expert sizes (1842 .. 50 rows): the last row tile of each
+    # expert takes 1, 2, 3 or 4 64-row slabs
+    "big_slabs": W["mixtral_prefill"].with_(name="big_slabs", T=2048, d=256, d_ff=512, zipf_s=0.8),
+    # the same with an odd number of 64-wide k stages (d = 192) and a
+    # partial column tile (d_ff = 320 = 2 * 128 + 64)
+    "big_slabs_odd": W["mixtral_prefill"].with_(name="big_slabs_odd", T=2500, d=192, d_ff=320,
+                                                zipf_s=0.7),
     # weight-streaming kernel (at most 32 rows per expert, K % 128 == 0):
     # every token on both experts -> two full 16-row tiles of A per expert
     "skinny_full": W["mixtral_decode"].with_(name="skinny_full", T=32, d=256, d_ff=384, E=2),
