@@ -174,7 +174,7 @@ def run_workload(w, steps, warmup, fresh_x_steps=0, seed=0):
                 n_kept=n_kept, touched=touched)
 
 
-def cpu_baseline(w, seed=0, target_s=12.0):
+def cpu_baseline(w, seed=0, target_s=22.0):
     """The oracle on this host's cores on a bounded sample of workload w."""
     import oracle
     from oracle.margin import reject_near_ties  # noqa: F401  (inputs are used unfiltered here)
