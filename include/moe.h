@@ -114,7 +114,9 @@ extern "C" {
  * for j < n_stage_events, on `stream`; MOE_FORWARD_STAGES + 1 events
  * bracket every stage, and a NULL entry is skipped (each recorded event
  * separates the kernels around it by a few microseconds, so record only
- * the ones needed).  NULL disables the hook.  The stages, in order: route,
+ * the ones needed).  The two events around expert-up, which is one kernel,
+ * are instead timestamped by that kernel's launch (its start and end): they
+ * add no gap.  NULL disables the hook.  The stages, in order: route,
  * route-finalize, dispatch, gather, expert-up, expert-down, combine; in
  * moe_forward the gather is folded into expert-up (its rows of x are read
  * through token_of_row), so that stage is empty.

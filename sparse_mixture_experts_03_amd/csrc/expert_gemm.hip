@@ -770,7 +770,7 @@ hipError_t launch_gemm(const Shape &s, const void *A, const int32_t *a_rows, con
     unsigned blocks = nt * row_tile_bound(s, BM);
     blocks = (blocks + NUM_XCD - 1) / NUM_XCD * NUM_XCD;
     dim3 grid(blocks);
-    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM_, WN_, DUAL, ACT, OUT_BF16>), grid, dim3(256),
+    launch_kernel((gemm_bf16_kernel<BM, BN, WM_, WN_, DUAL, ACT, OUT_BF16>), grid, dim3(256),
                        0, st, (const uint16_t *)A, a_rows, offsets, s.E, (const uint16_t *)B1,
                        (const uint16_t *)B3, C, N, K);
     return hipGetLastError();
@@ -784,7 +784,7 @@ hipError_t launch_big(const Shape &s, const void *A, const int32_t *a_rows, cons
     const unsigned nt = (unsigned)((N + BN - 1) / BN);
     unsigned blocks = nt * row_tile_bound(s, BIG_BM) * (unsigned)nsplit;
     blocks = (blocks + NUM_XCD - 1) / NUM_XCD * NUM_XCD;
-    hipLaunchKernelGGL((gemm_bf16_big_kernel<DUAL, ACT, OUT_BF16>), dim3(blocks), dim3(256), 0, st,
+    launch_kernel((gemm_bf16_big_kernel<DUAL, ACT, OUT_BF16>), dim3(blocks), dim3(256), 0, st,
                        (const uint16_t *)A, a_rows, offsets, s.E, (const uint16_t *)B1,
                        (const uint16_t *)B3, C, N, K, nsplit, C_split);
     return hipGetLastError();
@@ -799,11 +799,11 @@ hipError_t launch_skinny(const Shape &s, const void *A, const int32_t *a_rows, c
     // >= 16 chunks)
     const int nch = K / SK_KC;
     if (blocks < 4096 && nch >= 64) {
-        hipLaunchKernelGGL((gemm_bf16_skinny_kernel<MT, NT, PF, 4, DUAL, ACT, OUT_BF16>),
+        launch_kernel((gemm_bf16_skinny_kernel<MT, NT, PF, 4, DUAL, ACT, OUT_BF16>),
                            dim3(blocks), dim3(256), 0, st, (const uint16_t *)A, a_rows, offsets, s.E,
                            (const uint16_t *)B1, (const uint16_t *)B3, C, N, K);
     } else {
-        hipLaunchKernelGGL((gemm_bf16_skinny_kernel<MT, NT, PF, 1, DUAL, ACT, OUT_BF16>),
+        launch_kernel((gemm_bf16_skinny_kernel<MT, NT, PF, 1, DUAL, ACT, OUT_BF16>),
                            dim3(blocks), dim3(64), 0, st, (const uint16_t *)A, a_rows, offsets, s.E,
                            (const uint16_t *)B1, (const uint16_t *)B3, C, N, K);
     }
@@ -847,7 +847,7 @@ hipError_t launch_expert_up(const Shape &s, const void *x_perm, const int32_t *a
                             hipStream_t st) {
     if (s.dtype == 0) {
         int64_t blocks = s.Tk() < 16384 ? s.Tk() : 16384;
-        hipLaunchKernelGGL(up_f32_kernel, dim3((unsigned)(blocks > 0 ? blocks : 1)), dim3(256), 0,
+        launch_kernel(up_f32_kernel, dim3((unsigned)(blocks > 0 ? blocks : 1)), dim3(256), 0,
                            st, (const float *)x_perm, a_rows, offsets, s.E, (const float *)W1,
                            (const float *)W3, s.act, (float *)H, s.d, s.d_ff);
         return hipGetLastError();
@@ -875,7 +875,7 @@ hipError_t launch_expert_down(const Shape &s, const void *H, const int32_t *offs
                               hipStream_t st) {
     if (s.dtype == 0) {
         int64_t blocks = s.Tk() < 16384 ? s.Tk() : 16384;
-        hipLaunchKernelGGL(down_f32_kernel, dim3((unsigned)(blocks > 0 ? blocks : 1)), dim3(256), 0,
+        launch_kernel(down_f32_kernel, dim3((unsigned)(blocks > 0 ? blocks : 1)), dim3(256), 0,
                            st, (const float *)H, offsets, s.E, (const float *)W2, y_perm, s.d,
                            s.d_ff);
         return hipGetLastError();

@@ -120,6 +120,17 @@ int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
         if (rc_ != MOE_OK) return rc_;           \
     } while (0)
 
+}  // namespace
+
+namespace moe {
+LaunchEvents &next_launch_events() {
+    static thread_local LaunchEvents le{nullptr, nullptr};
+    return le;
+}
+}  // namespace moe
+
+namespace {
+
 struct StageEvents {
     void *const *ev;
     int n;
@@ -129,6 +140,13 @@ struct StageEvents {
         if (ev && next < n && ev[next]) e = hipEventRecord((hipEvent_t)ev[next], st);
         ++next;
         return e;
+    }
+    hipEvent_t at(int j) const { return (ev && j < n) ? (hipEvent_t)ev[j] : nullptr; }
+    // the next stage is one kernel: hand its two boundary events to that
+    // launch (start and stop timestamps) instead of recording them around it
+    void around_next_launch() {
+        moe::next_launch_events() = moe::LaunchEvents{at(next), at(next + 1)};
+        next += 2;
     }
 };
 
@@ -164,6 +182,13 @@ int moe_route(const moe_desc *desc, const void *x, const float *W_r, const float
     if ((rc = check_ws(s, ws, ws_bytes)) != MOE_OK) return rc;
     const Layout L = layout(s);
     hipStream_t st = (hipStream_t)stream;
+    if (moe::route_small(s)) {
+        MOE_TRY(moe::launch_route_small(s, x, W_r, bias, noise, topk_idx, gates, stats, nullptr,
+                                        at<float>(ws, L.part_P), at<float>(ws, L.part_lse2),
+                                        at<uint16_t>(ws, L.wsplit), at<float>(ws, L.part_logits),
+                                        st));
+        return MOE_OK;
+    }
     MOE_TRY(moe::launch_route(s, x, W_r, bias, noise, topk_idx, gates, at<float>(ws, L.part_P),
                               at<float>(ws, L.part_lse2), at<uint16_t>(ws, L.wsplit),
                               at<float>(ws, L.part_logits),
@@ -250,24 +275,38 @@ int moe_forward(const moe_desc *desc, const void *x, const float *W_r, const flo
     hipStream_t st = (hipStream_t)stream;
     StageEvents ev{desc->stage_events, desc->n_stage_events};
     MOE_TRY(ev.record(st));
-    MOE_TRY(moe::launch_route(s, x, W_r, bias, noise, topk_idx, gates, at<float>(ws, L.part_P),
-                              at<float>(ws, L.part_lse2), at<uint16_t>(ws, L.wsplit),
-                              at<float>(ws, L.part_logits),
-                              at<unsigned>(ws, L.arrivals), st));
-    MOE_TRY(ev.record(st));
-    MOE_TRY(moe::launch_route_finalize(s, topk_idx, at<float>(ws, L.part_P),
-                                       at<float>(ws, L.part_lse2), stats,
-                                       at<double>(ws, L.fP),
-                                       at<unsigned>(ws, L.arrivals), st));
-    MOE_TRY(ev.record(st));
-    MOE_TRY(moe::launch_dispatch(s, topk_idx, routed_counts, kept_counts, offsets, row_of_slot,
-                                 token_of_row, dropped, at<int32_t>(ws, L.chunk_counts), st));
+    if (moe::route_small(s)) {
+        // one kernel after the logits does the epilogue, statistics and
+        // dispatch; the statistics and dispatch stages are empty
+        const moe::DispatchOut disp{routed_counts, kept_counts, offsets,
+                                    row_of_slot, token_of_row, dropped};
+        MOE_TRY(moe::launch_route_small(s, x, W_r, bias, noise, topk_idx, gates, stats, &disp,
+                                        at<float>(ws, L.part_P), at<float>(ws, L.part_lse2),
+                                        at<uint16_t>(ws, L.wsplit), at<float>(ws, L.part_logits),
+                                        st));
+        MOE_TRY(ev.record(st));
+        MOE_TRY(ev.record(st));
+    } else {
+        MOE_TRY(moe::launch_route(s, x, W_r, bias, noise, topk_idx, gates, at<float>(ws, L.part_P),
+                                  at<float>(ws, L.part_lse2), at<uint16_t>(ws, L.wsplit),
+                                  at<float>(ws, L.part_logits),
+                                  at<unsigned>(ws, L.arrivals), st));
+        MOE_TRY(ev.record(st));
+        MOE_TRY(moe::launch_route_finalize(s, topk_idx, at<float>(ws, L.part_P),
+                                           at<float>(ws, L.part_lse2), stats,
+                                           at<double>(ws, L.fP),
+                                           at<unsigned>(ws, L.arrivals), st));
+        MOE_TRY(ev.record(st));
+        MOE_TRY(moe::launch_dispatch(s, topk_idx, routed_counts, kept_counts, offsets, row_of_slot,
+                                     token_of_row, dropped, at<int32_t>(ws, L.chunk_counts), st));
+    }
     MOE_TRY(ev.record(st));
     // the gather is folded into the up projection's loads: its rows of A are
     // read from x through token_of_row, so x_perm is not materialised here
-    MOE_TRY(ev.record(st));
-    MOE_TRY(moe::launch_expert_up(s, x, token_of_row, offsets, W1, W3, H, st));
-    MOE_TRY(ev.record(st));
+    ev.around_next_launch();  // events before and after expert-up
+    const hipError_t up_err = moe::launch_expert_up(s, x, token_of_row, offsets, W1, W3, H, st);
+    moe::next_launch_events() = moe::LaunchEvents{nullptr, nullptr};
+    MOE_TRY(up_err);
     float *part2 = L.y_perm2 ? at<float>(ws, L.y_perm2) : nullptr;
     MOE_TRY(moe::launch_expert_down(s, H, offsets, W2, y_perm, part2, st));
     MOE_TRY(ev.record(st));

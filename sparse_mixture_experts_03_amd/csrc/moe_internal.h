@@ -5,10 +5,28 @@
 // workspace and calls the launchers in order on the caller's stream.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 namespace moe {
+
+// Start/stop events for the next kernel launched through launch_kernel():
+// moe_forward's stage-event hook for a stage that is one kernel (expert
+// up).  The launch itself timestamps them, so timing the stage puts no
+// commands between the kernels.  Per host thread; one launch consumes them.
+struct LaunchEvents {
+    hipEvent_t start, stop;
+};
+LaunchEvents &next_launch_events();
+template <typename F, typename... Args>
+inline void launch_kernel(F kernel, dim3 grid, dim3 block, unsigned shm, hipStream_t st,
+                          Args... args) {
+    LaunchEvents &le = next_launch_events();
+    const LaunchEvents ev = le;
+    le = LaunchEvents{nullptr, nullptr};
+    hipExtLaunchKernelGGL(kernel, grid, block, shm, st, ev.start, ev.stop, 0u, args...);
+}
 
 // Problem sizes plus the derived capacity (C < 0: no limit).
 struct Shape {
@@ -38,6 +56,25 @@ hipError_t launch_route(const Shape &s, const void *x, const float *Wr, const fl
                         const float *noise, int32_t *topk_idx, float *gates, float *part_P,
                         float *part_lse2, uint16_t *wsplit, float *part_logits,
                         unsigned *arrivals, hipStream_t st);
+// Small bf16 batches (T <= ROUTE_SMALL_T tokens, T*k <= ROUTE_SMALL_TK):
+// after the logits, one block finishes the routing -- slices summed,
+// softmax, top-k, gates, statistics and (when the dispatch outputs are
+// given) the dispatch -- in place of the epilogue, statistics and dispatch
+// kernels.  The results equal theirs: every integer output bit for bit, and
+// the statistics up to the grouping of the partial sums (one block here).
+constexpr int ROUTE_SMALL_T = 64;
+constexpr int ROUTE_SMALL_TK = 2048;
+inline bool route_small(const Shape &s) {
+    return s.dtype == 1 && s.T <= ROUTE_SMALL_T && s.Tk() <= ROUTE_SMALL_TK;
+}
+struct DispatchOut {
+    int32_t *routed, *kept, *offsets, *row_of_slot, *token_of_row;
+    uint8_t *dropped;
+};
+hipError_t launch_route_small(const Shape &s, const void *x, const float *Wr, const float *bias,
+                              const float *noise, int32_t *topk_idx, float *gates, float *stats,
+                              const DispatchOut *disp, float *part_P, float *part_lse2,
+                              uint16_t *wsplit, float *part_logits, hipStream_t st);
 hipError_t launch_route_finalize(const Shape &s, const int32_t *topk_idx, const float *part_P,
                                  const float *part_lse2, float *stats, double *fP,
                                  unsigned *arrivals, hipStream_t st);

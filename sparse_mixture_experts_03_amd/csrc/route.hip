@@ -75,20 +75,21 @@ __device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long v)
 }
 
 // The per-token epilogue over a block's logits tile hl[TILE][.]
-// (already synchronised).  Every thread of the block must call it.
-template <int TILE>
+// (already synchronised), NW waves, wave w taking tokens w, w + NW, ...
+// Every thread of the block must call it.
+template <int TILE, int NW = 4>
 __device__ void softmax_topk_block(const float (*hl)[RT_EMAX + 1], int t0, int T, int E, int k,
                                    int gate_switch, int32_t *__restrict__ topk_idx,
                                    float *__restrict__ gates, float *__restrict__ part_P,
                                    float *__restrict__ part_lse2) {
-    __shared__ float pw[4][RT_EMAX];
-    __shared__ float lw[4];
+    __shared__ float pw[NW][RT_EMAX];
+    __shared__ float lw[NW];
     const int tid = threadIdx.x;
     const int lane = tid & 63, w = tid >> 6;
     const int e0 = lane, e1 = lane + 64;
     const bool v0 = e0 < E, v1 = e1 < E;
     float psum0 = 0.f, psum1 = 0.f, lsum = 0.f;
-    for (int r = w; r < TILE; r += 4) {
+    for (int r = w; r < TILE; r += NW) {
         const int t = t0 + r;
         if (t >= T) break;
         const float h0 = v0 ? hl[r][e0] : -INFINITY;
@@ -129,19 +130,24 @@ __device__ void softmax_topk_block(const float (*hl)[RT_EMAX + 1], int t0, int T
             gates[(int64_t)t * k + sl] = g;
         }
     }
-    // block partials in a fixed order: waves 0..3.  lsum is the same on
+    // block partials in a fixed order: waves 0..NW-1.  lsum is the same on
     // every lane of a wave (it sums wave-uniform values).
     pw[w][e0] = psum0;
     pw[w][e1] = psum1;
     if (lane == 0) lw[w] = lsum;
     __syncthreads();
     if (tid < E) {
-        float a = pw[0][tid] + pw[1][tid];
-        a += pw[2][tid];
-        a += pw[3][tid];
+        float a = pw[0][tid];
+#pragma unroll
+        for (int v = 1; v < NW; ++v) a += pw[v][tid];
         part_P[(int64_t)blockIdx.x * E + tid] = a;
     }
-    if (tid == 0) part_lse2[blockIdx.x] = ((lw[0] + lw[1]) + lw[2]) + lw[3];
+    if (tid == 0) {
+        float a = lw[0];
+#pragma unroll
+        for (int v = 1; v < NW; ++v) a += lw[v];
+        part_lse2[blockIdx.x] = a;
+    }
 }
 
 // ---- fp32 activations ----------------------------------------------------
@@ -446,6 +452,126 @@ __global__ __launch_bounds__(256) void route_stats_kernel(
     }
 }
 
+// Small batches: one block of 16 waves finishes the routing.  The logits of
+// the T <= 64 tokens (slices added in slice order, then bias and noise) go
+// to LDS, the shared per-token epilogue runs over all of them (its block
+// partials are then the whole sums), and the statistics follow as in
+// route_stats_kernel: P and z from the partials in double, f from the top
+// choices, aux over experts in order.  The dispatch, when asked for, counts
+// the assignments per expert (integer LDS atomics), forms kept counts and
+// offsets, then wave 0 ranks the T*k assignments in order, 64 at a time:
+// lanes with the same expert are grouped by ballot and ranked by popcount
+// of the lower lanes, on top of a per-expert running count.
+constexpr int RS_THREADS = 1024;
+
+__global__ __launch_bounds__(RS_THREADS) void route_small_kernel(
+    const float *__restrict__ part, int nsplit, const float *__restrict__ bias,
+    const float *__restrict__ noise, int T, int E, int k, int gate_switch, int64_t C,
+    int32_t *__restrict__ topk_idx, float *__restrict__ gates, float *__restrict__ part_P,
+    float *__restrict__ part_lse2, float *__restrict__ stats, int32_t *__restrict__ routed,
+    int32_t *__restrict__ kept, int32_t *__restrict__ offsets, int32_t *__restrict__ row_of_slot,
+    int32_t *__restrict__ token_of_row, uint8_t *__restrict__ dropped) {
+    constexpr int TILE = ROUTE_SMALL_T;
+    __shared__ float hl[TILE][RT_EMAX + 1];
+    __shared__ int cnt[RT_EMAX], off[RT_EMAX], run[RT_EMAX], topc[RT_EMAX];
+    __shared__ int sh_total;
+    const int tid = threadIdx.x;
+    const int TE = T * E;
+    for (int i = tid; i < TE; i += RS_THREADS) {
+        float v = 0.f;
+        for (int sl = 0; sl < nsplit; ++sl) v += part[(int64_t)sl * TE + i];
+        const int t = i / E, e = i - t * E;
+        if (bias) v += bias[e];
+        if (noise) v += noise[i];
+        hl[t][e] = v;
+    }
+    if (tid < RT_EMAX) {
+        cnt[tid] = 0;
+        topc[tid] = 0;
+    }
+    __syncthreads();
+    softmax_topk_block<TILE, RS_THREADS / 64>(hl, 0, T, E, k, gate_switch, topk_idx, gates, part_P,
+                                              part_lse2);
+    __syncthreads();  // the block's own global writes are visible to it now
+
+    // statistics
+    const int Tk = T * k;
+    for (int j = tid; j < Tk; j += RS_THREADS) {
+        const int e = topk_idx[j];
+        atomicAdd(&cnt[e], 1);                         // integer: order-free
+        if (j % k == 0) atomicAdd(&topc[e], 1);
+    }
+    __syncthreads();
+    if (tid == 0) {
+        double a = 0.0;
+        for (int e = 0; e < E; ++e) {
+            const double f = (double)topc[e] / (double)T;
+            const double P = (double)part_P[e] / (double)T;
+            stats[e] = (float)f;
+            stats[E + e] = (float)P;
+            a += f * P;
+        }
+        stats[2 * E] = (float)((double)E * a);
+        stats[2 * E + 1] = (float)((double)part_lse2[0] / (double)T);
+    }
+    if (routed == nullptr) return;
+
+    // dispatch
+    if (tid == 0) {
+        int o = 0;
+        for (int e = 0; e < E; ++e) {
+            const int kc = (C >= 0 && cnt[e] > C) ? (int)C : cnt[e];
+            off[e] = o;
+            run[e] = 0;
+            routed[e] = cnt[e];
+            kept[e] = kc;
+            offsets[e] = o;
+            o += kc;
+        }
+        offsets[E] = o;
+        sh_total = o;
+    }
+    __syncthreads();
+    if (tid < 64) {
+        const int lane = tid;
+        const unsigned long long lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+        for (int j0 = 0; j0 < Tk; j0 += 64) {
+            const int j = j0 + lane;
+            const bool valid = j < Tk;
+            const int ej = valid ? topk_idx[j] : -1;
+            bool act = valid;
+            int rank = 0;
+            while (true) {
+                const unsigned long long am = __ballot(act);
+                if (am == 0ull) break;
+                const int leader = __ffsll((long long)am) - 1;
+                const int e0 = __shfl(ej, leader);
+                const bool m = act && ej == e0;
+                const unsigned long long mm = __ballot(m);
+                if (m) {
+                    rank = run[e0] + __popcll(mm & lt_mask);
+                    act = false;
+                }
+                // every lane has read run[e0] above before the leader adds
+                if (lane == leader) run[e0] += __popcll(mm);
+            }
+            if (valid) {
+                if (C < 0 || rank < C) {
+                    const int row = off[ej] + rank;
+                    row_of_slot[j] = row;
+                    token_of_row[row] = j / k;
+                    dropped[j] = 0;
+                } else {
+                    row_of_slot[j] = -1;
+                    dropped[j] = 1;
+                }
+            }
+        }
+    }
+    // rows past the last kept one hold no token
+    for (int r = sh_total + tid; r < Tk; r += RS_THREADS) token_of_row[r] = -1;
+}
+
 template <int E_PAD, int WM, int WN>
 void launch_logits(const Shape &s, const void *x, const uint16_t *wsplit, float *part,
                    hipStream_t st) {
@@ -517,6 +643,34 @@ hipError_t launch_route_finalize(const Shape &s, const int32_t *topk_idx, const 
                                  unsigned *arrivals, hipStream_t st) {
     hipLaunchKernelGGL(route_stats_kernel, dim3(s.E + 1), dim3(256), 0, st, topk_idx, part_P,
                        part_lse2, s.T, s.E, s.k, route_blocks(s), stats, fP, arrivals);
+    return hipGetLastError();
+}
+
+hipError_t launch_route_small(const Shape &s, const void *x, const float *Wr, const float *bias,
+                              const float *noise, int32_t *topk_idx, float *gates, float *stats,
+                              const DispatchOut *disp, float *part_P, float *part_lse2,
+                              uint16_t *wsplit, float *part_logits, hipStream_t st) {
+    if (!route_small(s)) return hipErrorInvalidValue;
+    const int epad = route_epad(s);
+    {
+        const int64_t n = (int64_t)epad * s.d;
+        int64_t blocks = (n + 255) / 256;
+        if (blocks > 2048) blocks = 2048;
+        hipLaunchKernelGGL(router_split_kernel, dim3((unsigned)blocks), dim3(256), 0, st, Wr, s.E,
+                           epad, s.d, wsplit);
+    }
+    switch (epad) {
+    case 16: launch_logits<16, 4, 1>(s, x, wsplit, part_logits, st); break;
+    case 32: launch_logits<32, 4, 1>(s, x, wsplit, part_logits, st); break;
+    case 64: launch_logits<64, 2, 2>(s, x, wsplit, part_logits, st); break;
+    default: launch_logits<128, 1, 4>(s, x, wsplit, part_logits, st); break;
+    }
+    hipLaunchKernelGGL(route_small_kernel, dim3(1), dim3(RS_THREADS), 0, st, (const float *)part_logits,
+                       route_nsplit(s), bias, noise, s.T, s.E, s.k, s.gate, s.C, topk_idx, gates,
+                       part_P, part_lse2, stats, disp ? disp->routed : nullptr,
+                       disp ? disp->kept : nullptr, disp ? disp->offsets : nullptr,
+                       disp ? disp->row_of_slot : nullptr, disp ? disp->token_of_row : nullptr,
+                       disp ? disp->dropped : nullptr);
     return hipGetLastError();
 }
 

@@ -51,6 +51,9 @@ SMALL = {
     # partial column tile (d_ff = 320 = 2 * 128 + 64)
     "big_slabs_odd": W["mixtral_prefill"].with_(name="big_slabs_odd", T=2500, d=192, d_ff=320,
                                                 zipf_s=0.7),
+    # a small batch (T <= 64) routed by the single-block routing kernel,
+    # with capacity drops (C = ceil(0.5 * 48 * 2 / 8) = 6)
+    "small_drops": W["mixtral_decode"].with_(name="small_drops", T=48, d=256, d_ff=384, cf=0.5),
     # weight-streaming kernel (at most 32 rows per expert, K % 128 == 0):
     # every token on both experts -> two full 16-row tiles of A per expert
     "skinny_full": W["mixtral_decode"].with_(name="skinny_full", T=32, d=256, d_ff=384, E=2),
@@ -79,7 +82,8 @@ SMALL = {
 
 
 # cases whose capacity is known to drop assignments (the drop path is exercised)
-EXPECT_DROPS = {"switch_small", "zipf_small", "relu_bf16", "big_gelu", "skinny_mt3_gelu"}
+EXPECT_DROPS = {"switch_small", "zipf_small", "relu_bf16", "big_gelu", "skinny_mt3_gelu",
+                "small_drops"}
 
 
 def _check_all(w, wt, tk, got=None):
@@ -106,7 +110,7 @@ def test_forward_matches_oracle(name):
 
 
 @pytest.mark.parametrize("name", ["mixtral_small", "zipf_small", "tiny", "switch_small",
-                                  "big_splitk"])
+                                  "big_splitk", "decode_small", "small_drops"])
 def test_staged_entry_points(name):
     """route, dispatch, expert_ffn and combine called one by one: x_perm is
     the exact gather, y_perm matches the oracle's per-row expert outputs,
