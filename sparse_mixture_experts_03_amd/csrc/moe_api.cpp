@@ -53,7 +53,7 @@ int check_desc(const moe_desc *desc, Shape *s) {
 // Workspace layout; every region starts on a 256-byte boundary.
 struct Layout {
     size_t part_P, part_lse2, fP, arrivals;         // router partials, f_e*P_e and z, counter
-    size_t wsplit, part_logits;                     // bf16 router: split W_r, logit slices
+    size_t part_logits;                             // bf16 router: logit slices
     size_t chunk_counts;                            // dispatch: per-chunk expert histograms
     size_t topk_idx, gates, routed, kept, offsets;  // moe_forward's optional outputs
     size_t row_of_slot, token_of_row, dropped, stats;
@@ -80,7 +80,6 @@ Layout layout(const Shape &s) {
     L.fP = take(((size_t)s.E + 1) * sizeof(double));
     L.arrivals = take(sizeof(unsigned));
     if (s.dtype == MOE_DTYPE_BF16) {
-        L.wsplit = take(3 * (size_t)moe::route_epad(s) * (size_t)s.d * 2);
         L.part_logits = take((size_t)moe::route_nsplit(s) * (size_t)s.T * (size_t)s.E * 4);
     }
     L.chunk_counts = take((size_t)moe::dispatch_chunks(s) * (size_t)s.E * 4);
@@ -185,13 +184,12 @@ int moe_route(const moe_desc *desc, const void *x, const float *W_r, const float
     if (moe::route_small(s)) {
         MOE_TRY(moe::launch_route_small(s, x, W_r, bias, noise, topk_idx, gates, stats, nullptr,
                                         at<float>(ws, L.part_P), at<float>(ws, L.part_lse2),
-                                        at<uint16_t>(ws, L.wsplit), at<float>(ws, L.part_logits),
+                                        at<float>(ws, L.part_logits),
                                         st));
         return MOE_OK;
     }
     MOE_TRY(moe::launch_route(s, x, W_r, bias, noise, topk_idx, gates, at<float>(ws, L.part_P),
-                              at<float>(ws, L.part_lse2), at<uint16_t>(ws, L.wsplit),
-                              at<float>(ws, L.part_logits),
+                              at<float>(ws, L.part_lse2), at<float>(ws, L.part_logits),
                               at<unsigned>(ws, L.arrivals), st));
     MOE_TRY(moe::launch_route_finalize(s, topk_idx, at<float>(ws, L.part_P),
                                        at<float>(ws, L.part_lse2), stats,
@@ -282,14 +280,13 @@ int moe_forward(const moe_desc *desc, const void *x, const float *W_r, const flo
                                     row_of_slot, token_of_row, dropped};
         MOE_TRY(moe::launch_route_small(s, x, W_r, bias, noise, topk_idx, gates, stats, &disp,
                                         at<float>(ws, L.part_P), at<float>(ws, L.part_lse2),
-                                        at<uint16_t>(ws, L.wsplit), at<float>(ws, L.part_logits),
+                                        at<float>(ws, L.part_logits),
                                         st));
         MOE_TRY(ev.record(st));
         MOE_TRY(ev.record(st));
     } else {
         MOE_TRY(moe::launch_route(s, x, W_r, bias, noise, topk_idx, gates, at<float>(ws, L.part_P),
-                                  at<float>(ws, L.part_lse2), at<uint16_t>(ws, L.wsplit),
-                                  at<float>(ws, L.part_logits),
+                                  at<float>(ws, L.part_lse2), at<float>(ws, L.part_logits),
                                   at<unsigned>(ws, L.arrivals), st));
         MOE_TRY(ev.record(st));
         MOE_TRY(moe::launch_route_finalize(s, topk_idx, at<float>(ws, L.part_P),

@@ -44,8 +44,8 @@ constexpr int ROUTE_TOKENS_BF16 = 8;
 inline int route_tile(const Shape &s) { return s.dtype == 1 ? ROUTE_TOKENS_BF16 : ROUTE_TOKENS_F32; }
 inline int route_blocks(const Shape &s) { return (s.T + route_tile(s) - 1) / route_tile(s); }
 
-// bf16 path: router matrix split into 3 bf16 terms [3][E_pad][d], and the
-// logits computed in route_nsplit() slices of d, each route_slice() wide.
+// bf16 path: logits computed in route_nsplit() slices of d, each
+// route_slice() wide, against E padded to route_epad() experts.
 int route_epad(const Shape &s);
 int route_slice(const Shape &s);
 int route_nsplit(const Shape &s);
@@ -54,8 +54,8 @@ int route_nsplit(const Shape &s);
 // kernels, used and re-zeroed by the statistics kernel); fP: E + 1 doubles.
 hipError_t launch_route(const Shape &s, const void *x, const float *Wr, const float *bias,
                         const float *noise, int32_t *topk_idx, float *gates, float *part_P,
-                        float *part_lse2, uint16_t *wsplit, float *part_logits,
-                        unsigned *arrivals, hipStream_t st);
+                        float *part_lse2, float *part_logits, unsigned *arrivals,
+                        hipStream_t st);
 // Small bf16 batches (T <= ROUTE_SMALL_T tokens, T*k <= ROUTE_SMALL_TK):
 // after the logits, one block finishes the routing -- slices summed,
 // softmax, top-k, gates, statistics and (when the dispatch outputs are
@@ -74,7 +74,7 @@ struct DispatchOut {
 hipError_t launch_route_small(const Shape &s, const void *x, const float *Wr, const float *bias,
                               const float *noise, int32_t *topk_idx, float *gates, float *stats,
                               const DispatchOut *disp, float *part_P, float *part_lse2,
-                              uint16_t *wsplit, float *part_logits, hipStream_t st);
+                              float *part_logits, hipStream_t st);
 hipError_t launch_route_finalize(const Shape &s, const int32_t *topk_idx, const float *part_P,
                                  const float *part_lse2, float *stats, double *fP,
                                  unsigned *arrivals, hipStream_t st);

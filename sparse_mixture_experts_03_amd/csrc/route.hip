@@ -10,17 +10,17 @@
 //     P_i (mean router probability), and the z statistic mean (log sum exp h)^2;
 //   Implementation: the router runs in float32.
 //
-// bf16 activations (the MFMA path), three kernels:
-//   router_split_kernel  splits the fp32 router matrix exactly into three
-//     bf16 terms, W = hi + mid + lo: hi = bf16(W), mid = bf16(W - hi),
-//     lo = bf16(W - hi - mid); each difference is exact in fp32 and the last
-//     one has at most 8 significant bits, so the three terms sum to W.  A bf16
-//     token times a bf16 term is exact in fp32, hence
-//     x.W = x.hi + x.mid + x.lo with fp32 accumulation: an fp32 router whose
-//     only rounding is in the accumulation, computed on bf16 MFMA.
+// bf16 activations (the MFMA path), two kernels:
 //   router_logits_kernel  v_mfma_f32_16x16x32_bf16 over a 64-token x E tile,
 //     split over d into slices (so that a 32-token decode batch still
-//     spreads over many CUs); each slice writes fp32 partial logits.
+//     spreads over many CUs); each slice writes fp32 partial logits.  The
+//     fp32 router matrix is split exactly into three bf16 terms as it is
+//     staged, W = hi + mid + lo: hi = bf16(W), mid = bf16(W - hi),
+//     lo = bf16(W - hi - mid); each difference is exact in fp32 and the last
+//     one has at most 8 significant bits, so the three terms sum to W.  A
+//     bf16 token times a bf16 term is exact in fp32, hence
+//     x.W = x.hi + x.mid + x.lo with fp32 accumulation: an fp32 router whose
+//     only rounding is in the accumulation, computed on bf16 MFMA.
 //   route_epilogue_kernel  per token: partial logits summed in slice order,
 //     plus bias and noise, then the shared per-token epilogue below.
 // fp32 activations: route_f32_kernel, a plain fp32 FMA tile over d staged
@@ -219,39 +219,24 @@ __global__ __launch_bounds__(RT_THREADS) void route_f32_kernel(
 
 // ---- bf16 activations: exact three-term split + MFMA ---------------------
 
-// wsplit [3][E_pad][d] bf16: hi, mid, lo; rows E..E_pad-1 are zero.
-__global__ __launch_bounds__(256) void router_split_kernel(const float *__restrict__ Wr, int E,
-                                                           int E_pad, int d,
-                                                           uint16_t *__restrict__ wsplit) {
-    const int64_t n = (int64_t)E_pad * d;
-    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
-         i += (int64_t)gridDim.x * blockDim.x) {
-        const int64_t row = i / d;
-        const float w = row < E ? Wr[i] : 0.f;
-        const uint16_t hi = f32_to_bf16(w);
-        const float r1 = w - bf16_to_f32(hi);
-        const uint16_t mid = f32_to_bf16(r1);
-        const float r2 = r1 - bf16_to_f32(mid);
-        wsplit[i] = hi;
-        wsplit[n + i] = mid;
-        wsplit[2 * n + i] = f32_to_bf16(r2);
-    }
-}
-
 // Logit partials of tokens [64*bx, +64) over the d slice of blockIdx.y.
 // MFMA 16x16x32 layout (lane l): A row l % 16, k 8*(l/16)..+8; B column
 // l % 16, same k; accumulator r holds row 4*(l/16) + r, column l % 16.
+// The block reads its slice of the fp32 router matrix and splits it into
+// the three bf16 terms as it stages it in LDS (rows q * E_PAD + e hold
+// term q of expert e; rows of experts >= E are zero).
 template <int E_PAD, int WAVES_M, int WAVES_N>
 __global__ __launch_bounds__(256) void router_logits_kernel(const uint16_t *__restrict__ x,
-                                                            const uint16_t *__restrict__ wsplit,
+                                                            const float *__restrict__ Wr,
                                                             int T, int d, int E, int slice,
                                                             float *__restrict__ part) {
     constexpr int TMW = RL_BM / 16 / WAVES_M;   // 16-token tiles per wave
     constexpr int TNW = E_PAD / 16 / WAVES_N;   // 16-expert tiles per wave
     constexpr int WROWS = 3 * E_PAD;
-    constexpr int CPR = RL_KC / 8;                       // 16-byte chunks per row
+    constexpr int CPR = RL_KC / 8;                       // 16-byte bf16 chunks per x row
+    constexpr int WCPR = RL_KC / 4;                      // 16-byte fp32 chunks per W row
     constexpr int XCH = (RL_BM * CPR + 255) / 256;       // x chunks per thread
-    constexpr int WCH = (WROWS * CPR + 255) / 256;       // W chunks per thread
+    constexpr int WCH = (E_PAD * WCPR + 255) / 256;      // W chunks per thread
     static_assert(WAVES_M * WAVES_N == 4 && TMW >= 1 && TNW >= 1, "wave split");
     __shared__ __attribute__((aligned(16))) uint16_t xs[2][RL_BM][RL_LDK];
     __shared__ __attribute__((aligned(16))) uint16_t wsh[2][WROWS][RL_LDK];
@@ -261,9 +246,9 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const uint16_t *__re
     const int t0 = blockIdx.x * RL_BM;
     const int kbeg = blockIdx.y * slice;
     const int kend = min(d, kbeg + slice);
-    const int64_t nw = (int64_t)E_PAD * d;
 
-    uint4 rx[XCH], rw[WCH];
+    uint4 rx[XCH];
+    float4 rw[WCH];
     auto gload = [&](int k0) {
 #pragma unroll
         for (int i = 0; i < XCH; ++i) {
@@ -275,11 +260,10 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const uint16_t *__re
 #pragma unroll
         for (int i = 0; i < WCH; ++i) {
             const int c = tid + i * 256;
-            const int r = c / CPR, kc = (c % CPR) * 8;
-            const int q = r / E_PAD, e = r % E_PAD;
-            const bool ok = c < WROWS * CPR && k0 + kc < kend;
-            rw[i] = ok ? *(const uint4 *)(wsplit + q * nw + (int64_t)e * d + k0 + kc)
-                       : make_uint4(0, 0, 0, 0);
+            const int e = c / WCPR, kc = (c % WCPR) * 4;
+            const bool ok = c < E_PAD * WCPR && e < E && k0 + kc < kend;
+            rw[i] = ok ? *(const float4 *)(Wr + (int64_t)e * d + k0 + kc)
+                       : make_float4(0.f, 0.f, 0.f, 0.f);
         }
     };
     auto lstore = [&](int buf) {
@@ -291,7 +275,29 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const uint16_t *__re
 #pragma unroll
         for (int i = 0; i < WCH; ++i) {
             const int c = tid + i * 256;
-            if (c < WROWS * CPR) *(uint4 *)&wsh[buf][c / CPR][(c % CPR) * 8] = rw[i];
+            if (c < E_PAD * WCPR) {
+                // W = hi + mid + lo exactly: hi = bf16(W), mid = bf16(W - hi),
+                // lo = bf16(W - hi - mid); each difference is exact in fp32
+                // and the last has at most 8 significant bits
+                const int e = c / WCPR, kc = (c % WCPR) * 4;
+                const float w[4] = {rw[i].x, rw[i].y, rw[i].z, rw[i].w};
+                uint16_t t[3][4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const uint16_t hi = f32_to_bf16(w[j]);
+                    const float r1 = w[j] - bf16_to_f32(hi);
+                    const uint16_t mid = f32_to_bf16(r1);
+                    const float r2 = r1 - bf16_to_f32(mid);
+                    t[0][j] = hi;
+                    t[1][j] = mid;
+                    t[2][j] = f32_to_bf16(r2);
+                }
+#pragma unroll
+                for (int q = 0; q < 3; ++q)
+                    *(uint2 *)&wsh[buf][q * E_PAD + e][kc] =
+                        make_uint2((uint32_t)t[q][0] | ((uint32_t)t[q][1] << 16),
+                                   (uint32_t)t[q][2] | ((uint32_t)t[q][3] << 16));
+            }
         }
     };
 
@@ -573,11 +579,10 @@ __global__ __launch_bounds__(RS_THREADS) void route_small_kernel(
 }
 
 template <int E_PAD, int WM, int WN>
-void launch_logits(const Shape &s, const void *x, const uint16_t *wsplit, float *part,
-                   hipStream_t st) {
+void launch_logits(const Shape &s, const void *x, const float *Wr, float *part, hipStream_t st) {
     dim3 grid((unsigned)((s.T + RL_BM - 1) / RL_BM), (unsigned)route_nsplit(s));
     hipLaunchKernelGGL((router_logits_kernel<E_PAD, WM, WN>), grid, dim3(256), 0, st,
-                       (const uint16_t *)x, wsplit, s.T, s.d, s.E, route_slice(s), part);
+                       (const uint16_t *)x, Wr, s.T, s.d, s.E, route_slice(s), part);
 }
 
 }  // namespace
@@ -609,8 +614,8 @@ int route_nsplit(const Shape &s) {
 
 hipError_t launch_route(const Shape &s, const void *x, const float *Wr, const float *bias,
                         const float *noise, int32_t *topk_idx, float *gates, float *part_P,
-                        float *part_lse2, uint16_t *wsplit, float *part_logits,
-                        unsigned *arrivals, hipStream_t st) {
+                        float *part_lse2, float *part_logits, unsigned *arrivals,
+                        hipStream_t st) {
     const dim3 grid(route_blocks(s)), block(RT_THREADS);
     if (s.dtype == 0) {
         hipLaunchKernelGGL(route_f32_kernel, grid, block, 0, st, (const float *)x, Wr, bias, noise,
@@ -618,19 +623,11 @@ hipError_t launch_route(const Shape &s, const void *x, const float *Wr, const fl
                            arrivals);
         return hipGetLastError();
     }
-    const int epad = route_epad(s);
-    {
-        const int64_t n = (int64_t)epad * s.d;
-        int64_t blocks = (n + 255) / 256;
-        if (blocks > 2048) blocks = 2048;
-        hipLaunchKernelGGL(router_split_kernel, dim3((unsigned)blocks), dim3(256), 0, st, Wr, s.E,
-                           epad, s.d, wsplit);
-    }
-    switch (epad) {
-    case 16: launch_logits<16, 4, 1>(s, x, wsplit, part_logits, st); break;
-    case 32: launch_logits<32, 4, 1>(s, x, wsplit, part_logits, st); break;
-    case 64: launch_logits<64, 2, 2>(s, x, wsplit, part_logits, st); break;
-    default: launch_logits<128, 1, 4>(s, x, wsplit, part_logits, st); break;
+    switch (route_epad(s)) {
+    case 16: launch_logits<16, 4, 1>(s, x, Wr, part_logits, st); break;
+    case 32: launch_logits<32, 4, 1>(s, x, Wr, part_logits, st); break;
+    case 64: launch_logits<64, 2, 2>(s, x, Wr, part_logits, st); break;
+    default: launch_logits<128, 1, 4>(s, x, Wr, part_logits, st); break;
     }
     hipLaunchKernelGGL(route_epilogue_kernel, grid, block, 0, st, (const float *)part_logits,
                        route_nsplit(s), bias, noise, s.T, s.E, s.k, s.gate, topk_idx, gates,
@@ -649,21 +646,13 @@ hipError_t launch_route_finalize(const Shape &s, const int32_t *topk_idx, const 
 hipError_t launch_route_small(const Shape &s, const void *x, const float *Wr, const float *bias,
                               const float *noise, int32_t *topk_idx, float *gates, float *stats,
                               const DispatchOut *disp, float *part_P, float *part_lse2,
-                              uint16_t *wsplit, float *part_logits, hipStream_t st) {
+                              float *part_logits, hipStream_t st) {
     if (!route_small(s)) return hipErrorInvalidValue;
-    const int epad = route_epad(s);
-    {
-        const int64_t n = (int64_t)epad * s.d;
-        int64_t blocks = (n + 255) / 256;
-        if (blocks > 2048) blocks = 2048;
-        hipLaunchKernelGGL(router_split_kernel, dim3((unsigned)blocks), dim3(256), 0, st, Wr, s.E,
-                           epad, s.d, wsplit);
-    }
-    switch (epad) {
-    case 16: launch_logits<16, 4, 1>(s, x, wsplit, part_logits, st); break;
-    case 32: launch_logits<32, 4, 1>(s, x, wsplit, part_logits, st); break;
-    case 64: launch_logits<64, 2, 2>(s, x, wsplit, part_logits, st); break;
-    default: launch_logits<128, 1, 4>(s, x, wsplit, part_logits, st); break;
+    switch (route_epad(s)) {
+    case 16: launch_logits<16, 4, 1>(s, x, Wr, part_logits, st); break;
+    case 32: launch_logits<32, 4, 1>(s, x, Wr, part_logits, st); break;
+    case 64: launch_logits<64, 2, 2>(s, x, Wr, part_logits, st); break;
+    default: launch_logits<128, 1, 4>(s, x, Wr, part_logits, st); break;
     }
     hipLaunchKernelGGL(route_small_kernel, dim3(1), dim3(RS_THREADS), 0, st, (const float *)part_logits,
                        route_nsplit(s), bias, noise, s.T, s.E, s.k, s.gate, s.C, topk_idx, gates,
