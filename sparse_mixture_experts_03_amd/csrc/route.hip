@@ -595,13 +595,16 @@ int route_epad(const Shape &s) {
 }
 
 // d slice per split: whole 64-wide chunks, enough slices to give the GPU
-// about 512 blocks, each slice at least two chunks, at most 8 slices.
+// about 512 blocks, each slice at least two chunks, at most 8 slices (32
+// for a small batch, whose block count is tiny and whose single finishing
+// block adds the slices back at little cost).
 int route_slice(const Shape &s) {
     const int tiles = (s.T + RL_BM - 1) / RL_BM;
     const int chunks = (s.d + RL_KC - 1) / RL_KC;
     const int want = (512 + tiles - 1) / tiles;
     int maxsplit = chunks / 2 > 1 ? chunks / 2 : 1;
-    if (maxsplit > 8) maxsplit = 8;  // the epilogue adds the slices back
+    const int cap = route_small(s) ? 32 : 8;  // the epilogue adds the slices back
+    if (maxsplit > cap) maxsplit = cap;
     int nsplit = want < maxsplit ? want : maxsplit;
     if (nsplit < 1) nsplit = 1;
     return (chunks + nsplit - 1) / nsplit * RL_KC;
