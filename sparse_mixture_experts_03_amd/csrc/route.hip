@@ -81,7 +81,8 @@ template <int TILE, int NW = 4>
 __device__ void softmax_topk_block(const float (*hl)[RT_EMAX + 1], int t0, int T, int E, int k,
                                    int gate_switch, int32_t *__restrict__ topk_idx,
                                    float *__restrict__ gates, float *__restrict__ part_P,
-                                   float *__restrict__ part_lse2) {
+                                   float *__restrict__ part_lse2, int *topk_sh = nullptr,
+                                   float *P_sh = nullptr, float *lse2_sh = nullptr) {
     __shared__ float pw[NW][RT_EMAX];
     __shared__ float lw[NW];
     const int tid = threadIdx.x;
@@ -127,6 +128,7 @@ __device__ void softmax_topk_block(const float (*hl)[RT_EMAX + 1], int t0, int T
             float hb = j ? sh1 : sh0;
             float g = gate_switch ? expf(hb - m) * inv : expf(hb - h_top) / den;
             topk_idx[(int64_t)t * k + sl] = j ? si1 : si0;
+            if (topk_sh) topk_sh[t * k + sl] = j ? si1 : si0;  // LDS copy (small batches)
             gates[(int64_t)t * k + sl] = g;
         }
     }
@@ -141,12 +143,14 @@ __device__ void softmax_topk_block(const float (*hl)[RT_EMAX + 1], int t0, int T
 #pragma unroll
         for (int v = 1; v < NW; ++v) a += pw[v][tid];
         part_P[(int64_t)blockIdx.x * E + tid] = a;
+        if (P_sh) P_sh[tid] = a;
     }
     if (tid == 0) {
         float a = lw[0];
 #pragma unroll
         for (int v = 1; v < NW; ++v) a += lw[v];
         part_lse2[blockIdx.x] = a;
+        if (lse2_sh) *lse2_sh = a;
     }
 }
 
@@ -480,6 +484,8 @@ __global__ __launch_bounds__(RS_THREADS) void route_small_kernel(
     constexpr int TILE = ROUTE_SMALL_T;
     __shared__ float hl[TILE][RT_EMAX + 1];
     __shared__ int cnt[RT_EMAX], off[RT_EMAX], run[RT_EMAX], topc[RT_EMAX];
+    __shared__ int tk[ROUTE_SMALL_TK];
+    __shared__ float Psh[RT_EMAX], lse2sh;
     __shared__ int sh_total;
     const int tid = threadIdx.x;
     const int TE = T * E;
@@ -497,13 +503,13 @@ __global__ __launch_bounds__(RS_THREADS) void route_small_kernel(
     }
     __syncthreads();
     softmax_topk_block<TILE, RS_THREADS / 64>(hl, 0, T, E, k, gate_switch, topk_idx, gates, part_P,
-                                              part_lse2);
-    __syncthreads();  // the block's own global writes are visible to it now
+                                              part_lse2, tk, Psh, &lse2sh);
+    __syncthreads();
 
     // statistics
     const int Tk = T * k;
     for (int j = tid; j < Tk; j += RS_THREADS) {
-        const int e = topk_idx[j];
+        const int e = tk[j];
         atomicAdd(&cnt[e], 1);                         // integer: order-free
         if (j % k == 0) atomicAdd(&topc[e], 1);
     }
@@ -512,13 +518,13 @@ __global__ __launch_bounds__(RS_THREADS) void route_small_kernel(
         double a = 0.0;
         for (int e = 0; e < E; ++e) {
             const double f = (double)topc[e] / (double)T;
-            const double P = (double)part_P[e] / (double)T;
+            const double P = (double)Psh[e] / (double)T;
             stats[e] = (float)f;
             stats[E + e] = (float)P;
             a += f * P;
         }
         stats[2 * E] = (float)((double)E * a);
-        stats[2 * E + 1] = (float)((double)part_lse2[0] / (double)T);
+        stats[2 * E + 1] = (float)((double)lse2sh / (double)T);
     }
     if (routed == nullptr) return;
 
@@ -544,7 +550,7 @@ __global__ __launch_bounds__(RS_THREADS) void route_small_kernel(
         for (int j0 = 0; j0 < Tk; j0 += 64) {
             const int j = j0 + lane;
             const bool valid = j < Tk;
-            const int ej = valid ? topk_idx[j] : -1;
+            const int ej = valid ? tk[j] : -1;
             bool act = valid;
             int rank = 0;
             while (true) {
