@@ -253,20 +253,26 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(
 // different slots and any 16 consecutive rows use 16 different (row parity,
 // slot) pairs, so the rows a fragment read serves together fall on distinct
 // banks whether the LDS serves 8 or 16 lanes of a 16-byte read per cycle.
-// Two LDS stages (2 x 64 KB): the loads for stage k+1 are issued in the
-// first half of stage k and run under its MFMAs.  Fragments for the next
-// 16-wide k step are read from LDS while the current step's MFMAs run.
+// LDS stages of 32 KB per operand: two for A and three for the weights
+// (160 KB, all of a gfx950 CU's LDS).  During stage k the A rows of stage
+// k+1 and then the weight rows of stage k+2 are issued (first half of the
+// stage, under its MFMAs), so weight loads, the ones that miss L2 first,
+// have two stages to land and A loads one; at the start of a stage only the
+// newest 8 weight loads may still be in flight (loads return in order).
+// Fragments for the next 16-wide k step are read from LDS while the current
+// step's MFMAs run.
 //
 // The stage loop carries no vector address arithmetic: a load's address is
 // a per-lane offset fixed for the whole tile plus the stage's k offset in
 // a scalar register (buffer addressing), and a fragment read is one of
 // eight per-lane LDS offsets (operand x k step) plus an immediate (stage,
-// fragment row).  The loop is unrolled by two stages so that the stage
-// buffer is a compile-time constant.
+// fragment row).  The loop is unrolled by two stages so that the A stage
+// is a compile-time constant; the weight stage (k mod 3) is a scalar added
+// to the weight operand's per-lane offset.
 constexpr int BIG_BM = 256;
 
 template <int MI, bool DUAL, int ACT, bool OUT_BF16>
-__device__ __forceinline__ void big_tile(char (*lds)[2][256 * 128], const uint16_t *__restrict__ A,
+__device__ __forceinline__ void big_tile(char *lds, const uint16_t *__restrict__ A,
                                          const int32_t *__restrict__ a_rows,
                                          const uint16_t *__restrict__ B1,
                                          const uint16_t *__restrict__ B3, void *__restrict__ C, int N,
@@ -318,18 +324,17 @@ __device__ __forceinline__ void big_tile(char (*lds)[2][256 * 128], const uint16
     }
     // global -> LDS load q (0..NQ-1) of a stage: q < NQA from A, else from
     // the weights
-    auto issue_one = [&](int stage, int k0, int q) {
-        const int kb = k0 * 2;
+    auto issue_one = [&](int stage, int bst, int ka, int kb, int q) {
         if (q < NQA)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
                 a_rsrc,
-                (__attribute__((address_space(3))) void *)(lds[0][stage] + (wave * (MI * 16) + q * 8) * ROWB),
-                16, a_off[q], kb, 0, 0);
+                (__attribute__((address_space(3))) void *)(lds + stage * OPB + (wave * (MI * 16) + q * 8) * ROWB),
+                16, a_off[q], ka * 2, 0, 0);
         else
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
                 b_rsrc,
-                (__attribute__((address_space(3))) void *)(lds[1][stage] + (wave * 64 + (q - NQA) * 8) * ROWB),
-                16, b_off[q - NQA], kb, 0, 0);
+                (__attribute__((address_space(3))) void *)(lds + (2 + bst) * OPB + (wave * 64 + (q - NQA) * 8) * ROWB),
+                16, b_off[q - NQA], kb * 2, 0, 0);
     };
 
     f32x16_t acc[MI][4];
@@ -357,10 +362,10 @@ __device__ __forceinline__ void big_tile(char (*lds)[2][256 * 128], const uint16
         rd_b[kk] = 2u * OPB + (uint32_t)((DUAL ? wn * 64 : wn * 128) + lr) * ROWB + slot;
         asm volatile("" : "+v"(rd_a[kk]), "+v"(rd_b[kk]));
     }
-    char *const lds0 = &lds[0][0][0];
+    char *const lds0 = lds;
     // fragment read f (0..NRD-1) of k step kk, in the order the MFMAs
     // consume them: A0, B0, B1, B2, B3, A1, ..., A(MI-1)
-    auto read_one = [&](auto stage_c, int kk, int f, bf16x8_t (&a)[MI], bf16x8_t (&b)[4]) {
+    auto read_one = [&](auto stage_c, int kk, int f, bf16x8_t (&a)[MI], bf16x8_t (&b)[4], uint32_t bso) {
         constexpr int stage = decltype(stage_c)::value;
         if (f == 0 || f >= 5) {
             const int i = f == 0 ? 0 : f - 4;
@@ -368,7 +373,7 @@ __device__ __forceinline__ void big_tile(char (*lds)[2][256 * 128], const uint16
         } else {
             const int j = f - 1;
             const int jo = DUAL ? ((j >> 1) * 128 + (j & 1) * 32) : j * 32;
-            b[j] = *(const bf16x8_t *)(lds0 + rd_b[kk] + (stage * OPB + jo * ROWB));
+            b[j] = *(const bf16x8_t *)(lds0 + (rd_b[kk] + bso) + jo * ROWB);
         }
     };
 
@@ -376,24 +381,29 @@ __device__ __forceinline__ void big_tile(char (*lds)[2][256 * 128], const uint16
     // a scheduling barrier: 4 k steps of NMF MFMAs (i-major, so consecutive
     // MFMAs never share an accumulator); during each of steps 0..2 the NRD
     // fragment reads of the next step; during steps 0 and 1 the NQ
-    // global->LDS loads of the next stage, spread evenly (every second MFMA
-    // for a full tile: early enough to land before the stage ends, spread
-    // out so that their issue does not starve the MFMA pipe).  The last
-    // stage's prefetch re-loads that stage into the idle buffer (nobody
-    // reads it), which keeps the loop free of branches.
+    // global->LDS loads (A rows of stage k+1, then weight rows of stage
+    // k+2), spread evenly (every second MFMA for a full tile: early enough to
+    // land in time, spread out so that their issue does not starve the MFMA
+    // pipe).  Near the end the loads re-load the last stage into an idle
+    // buffer (nobody reads it), which keeps the loop free of branches and
+    // the count of loads in flight fixed.
     bf16x8_t fa[2][MI], fb[2][4];
-    auto stage_body = [&](auto cur_c, int kt) {
+    auto stage_body = [&](auto cur_c, int kt, int bcur) {
         constexpr int cur = decltype(cur_c)::value;
         constexpr std::integral_constant<int, cur ^ 1> nxt_c{};
-        const int knext = kbeg + min(kt + 1, KT - 1) * BK;
-        // this wave's loads of the stage have landed; after the barrier,
-        // everyone's have
-        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        const int ka = kbeg + min(kt + 1, KT - 1) * BK;
+        const int kb = kbeg + min(kt + 2, KT - 1) * BK;
+        const int bnext = bcur == 0 ? 2 : bcur - 1;   // (bcur + 2) % 3
+        const uint32_t bso = (uint32_t)bcur * OPB;
+        // this wave's loads of the stage have landed (only the 8 weight
+        // loads of the stage after next, issued last, may still be in
+        // flight); after the barrier, everyone's have
+        asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)\n\ts_barrier" ::: "memory");
         // step 0's fragments in consumption order (kept by the scheduling
         // barriers), so the first MFMA waits for two reads, not all of them
 #pragma unroll
         for (int f = 0; f < NRD; ++f) {
-            read_one(cur_c, 0, f, fa[0], fb[0]);
+            read_one(cur_c, 0, f, fa[0], fb[0], bso);
             __builtin_amdgcn_sched_barrier(0);
         }
 #pragma unroll
@@ -409,27 +419,32 @@ __device__ __forceinline__ void big_tile(char (*lds)[2][256 * 128], const uint16
                     const int u = kk * NMF + t;
 #pragma unroll
                     for (int q = 0; q < NQ; ++q)
-                        if (min((q * 2 * NMF) / NQ + 1, 2 * NMF - 1) == u) issue_one(nxt_c, knext, q);
+                        if (min((q * 2 * NMF) / NQ + 1, 2 * NMF - 1) == u) issue_one(nxt_c, bnext, ka, kb, q);
                 }
                 if (kk < 3) {
                     // read f with MFMA min(f, NMF - 1) of the step
 #pragma unroll
                     for (int f = 0; f < NRD; ++f)
                         if (min(f, NMF - 1) == t)
-                            read_one(cur_c, kk + 1, f, fa[(kk + 1) & 1], fb[(kk + 1) & 1]);
+                            read_one(cur_c, kk + 1, f, fa[(kk + 1) & 1], fb[(kk + 1) & 1], bso);
                 }
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
     };
+    // stage 0 of both operands, then the weights' stage 1
 #pragma unroll
-    for (int q = 0; q < NQ; ++q) issue_one(0, kbeg, q);
-    int kt = 0;
+    for (int q = 0; q < NQ; ++q) issue_one(0, 0, kbeg, kbeg, q);
+#pragma unroll
+    for (int q = NQA; q < NQ; ++q) issue_one(0, 1, kbeg, kbeg + min(1, KT - 1) * BK, q);
+    int kt = 0, bc = 0;
     for (; kt + 1 < KT; kt += 2) {
-        stage_body(std::integral_constant<int, 0>{}, kt);
-        stage_body(std::integral_constant<int, 1>{}, kt + 1);
+        stage_body(std::integral_constant<int, 0>{}, kt, bc);
+        bc = bc == 2 ? 0 : bc + 1;
+        stage_body(std::integral_constant<int, 1>{}, kt + 1, bc);
+        bc = bc == 2 ? 0 : bc + 1;
     }
-    if (kt < KT) stage_body(std::integral_constant<int, 0>{}, kt);
+    if (kt < KT) stage_body(std::integral_constant<int, 0>{}, kt, bc);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
     if (nrows == MI * 64 && n0 + BN <= N) {
@@ -494,8 +509,8 @@ __global__ __launch_bounds__(256) void gemm_bf16_big_kernel(
     const uint16_t *__restrict__ B3, void *__restrict__ C_, int N, int K, int nsplit,
     void *__restrict__ C_split) {
     constexpr int BN = DUAL ? 128 : 256;
-    // [operand][stage]: operand o, stage s at (2o + s) * 32 KB
-    __shared__ __attribute__((aligned(1024))) char lds[2][2][256 * 128];
+    // A stages 0, 1 at 0 and 32 KB; weight stages 0..2 at 64, 96, 128 KB
+    __shared__ __attribute__((aligned(1024))) char lds[5 * 256 * 128];
 
     int e, row0, nrows, ntile, split = 0;
     if (!find_tile<BIG_BM>(offsets, E, (N + BN - 1) / BN, e, row0, nrows, ntile, nsplit, &split))

@@ -490,8 +490,20 @@ __global__ __launch_bounds__(RS_THREADS) void route_small_kernel(
     const int tid = threadIdx.x;
     const int TE = T * E;
     for (int i = tid; i < TE; i += RS_THREADS) {
+        // the slices are added in slice order; each group's loads are all
+        // issued before the first add, so the group costs one memory round
+        // trip rather than one per slice
+        constexpr int G = 32;
         float v = 0.f;
-        for (int sl = 0; sl < nsplit; ++sl) v += part[(int64_t)sl * TE + i];
+        for (int s0 = 0; s0 < nsplit; s0 += G) {
+            float buf[G];
+#pragma unroll
+            for (int u = 0; u < G; ++u)
+                if (s0 + u < nsplit) buf[u] = part[(int64_t)(s0 + u) * TE + i];
+#pragma unroll
+            for (int u = 0; u < G; ++u)
+                if (s0 + u < nsplit) v += buf[u];
+        }
         const int t = i / E, e = i - t * E;
         if (bias) v += bias[e];
         if (noise) v += noise[i];
