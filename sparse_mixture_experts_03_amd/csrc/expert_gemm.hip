@@ -244,7 +244,8 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(
 // 2 x 2 grid.  An expert's row tiles are 256 rows, except its last, which
 // takes only as many 64-row slabs as it needs (MI = 1..4 slabs; each wave
 // then holds MI 32-row fragments), so a ragged expert pads at most 63 rows
-// instead of up to 255.
+// instead of up to 255.  Tiles are spread over the XCDs by cost
+// (find_tile_balanced).
 // Operands go from global memory straight into LDS with
 // buffer_load_dwordx4 ... lds (no register staging): instruction j of a
 // wave fills 8 LDS rows, lane l writing the 16 bytes at (row + l/8, slot
@@ -270,6 +271,99 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(
 // is a compile-time constant; the weight stage (k mod 3) is a scalar added
 // to the weight operand's per-lane offset.
 constexpr int BIG_BM = 256;
+
+// Cost-balanced tile schedule for the 256-row kernel.  The work is the
+// ordered list of (K split, expert e, column tile n, row tile m) tiles, m
+// fastest.  A tile's cost is counted by its 64-row slabs: 18, 20, 22, 25
+// for 1..4 slabs (the loads of a whole weight panel are paid for however
+// few rows a tile has; measured: a one-slab tile takes about 0.7-0.8 of a
+// full one).  XCD x = b % 8 is given the contiguous run of tiles whose
+// starting cost lies in [x C / 8, (x+1) C / 8) of the total cost C, and
+// its blocks (slot b / 8) take the run's tiles in order; so every XCD gets
+// the same amount of work and the row tiles sharing a weight panel run on
+// one XCD at the same time.  Each wave computes the schedule by itself,
+// one expert per lane (two for E > 64) with shuffle prefix sums: one read
+// of offsets and no loop over the experts.
+constexpr int BIG_W_FULL = 25;
+__device__ __forceinline__ int big_slab_cost(int rows) {
+    const int mi = (rows + 63) >> 6;
+    return mi >= 4 ? 25 : 16 + 2 * mi;
+}
+
+__device__ __forceinline__ int wave_incl_scan(int v, int lane) {
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int u = __shfl_up(v, o);
+        if (lane >= o) v += u;
+    }
+    return v;
+}
+
+__device__ __forceinline__ bool find_tile_balanced(const int32_t *__restrict__ offsets, int E, int ntn,
+                                                   int nsplit, int &e, int &row0, int &nrows, int &ntile,
+                                                   int &split) {
+    const int lane = threadIdx.x & 63;
+    // experts lane and lane + 64; every value taken out of a lane is read
+    // with readlane at a uniform lane, so it lands in a scalar register
+    int lo[2], rows[2], mt[2], cpc[2], cumT[2], cumC[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int i = lane + 64 * h;
+        lo[h] = 0, rows[h] = 0;
+        if (i < E) {
+            lo[h] = offsets[i];
+            rows[h] = offsets[i + 1] - lo[h];
+        }
+        const int full = rows[h] >> 8, part = rows[h] & 255;
+        mt[h] = full + (part ? 1 : 0);
+        cpc[h] = BIG_W_FULL * full + (part ? big_slab_cost(part) : 0);   // cost per column tile
+        cumT[h] = wave_incl_scan(mt[h] * ntn, lane);
+        cumC[h] = wave_incl_scan(cpc[h] * ntn, lane);
+    }
+    const int T0 = __builtin_amdgcn_readlane(cumT[0], 63), C0 = __builtin_amdgcn_readlane(cumC[0], 63);
+    cumT[1] += T0;
+    cumC[1] += C0;
+    const int Ts = __builtin_amdgcn_readlane(cumT[1], 63);               // tiles per K split
+    const int64_t Cs = (int64_t)__builtin_amdgcn_readlane(cumC[1], 63);  // cost per K split
+    const int64_t C = Cs * nsplit;
+    // first tile whose starting cost is >= X (X <= C)
+    auto first_at = [&](int64_t X) -> int {
+        if (Cs == 0) return 0;
+        const int sp = (int)(X / Cs);
+        if (sp >= nsplit) return Ts * nsplit;
+        const int Xr = (int)(X - (int64_t)sp * Cs);
+        const unsigned long long m0 = __ballot(cumC[0] > Xr), m1 = __ballot(cumC[1] > Xr);
+        if (m0 == 0ull && m1 == 0ull) return (sp + 1) * Ts;
+        const int h = m0 ? 0 : 1;
+        const int ln = __ffsll((long long)(m0 ? m0 : m1)) - 1;
+        const int ce = __builtin_amdgcn_readlane(cumC[h], ln), te = __builtin_amdgcn_readlane(cumT[h], ln);
+        const int c_e = __builtin_amdgcn_readlane(cpc[h], ln), mt_e = __builtin_amdgcn_readlane(mt[h], ln);
+        const int Xe = Xr - (ce - c_e * ntn);          // cost into expert
+        const int te0 = te - mt_e * ntn;               // its first tile
+        const int n = Xe / c_e, r = Xe - n * c_e;
+        const int m = (r + BIG_W_FULL - 1) / BIG_W_FULL;
+        const int idx = m <= mt_e - 1 ? n * mt_e + m : (n + 1) * mt_e;
+        return sp * Ts + te0 + idx;
+    };
+    const int x = blockIdx.x % NUM_XCD;
+    const int start = first_at(C * x / NUM_XCD);
+    const int end = x == NUM_XCD - 1 ? Ts * nsplit : first_at(C * (x + 1) / NUM_XCD);
+    const int L = start + (int)(blockIdx.x / NUM_XCD);
+    if (L >= end) return false;
+    split = L / Ts;
+    const int Lr = L - split * Ts;
+    const unsigned long long m0 = __ballot(cumT[0] > Lr), m1 = __ballot(cumT[1] > Lr);
+    const int h = m0 ? 0 : 1;
+    const int ln = __ffsll((long long)(m0 ? m0 : m1)) - 1;
+    e = ln + 64 * h;
+    const int te = __builtin_amdgcn_readlane(cumT[h], ln), mt_e = __builtin_amdgcn_readlane(mt[h], ln);
+    const int Le = Lr - (te - mt_e * ntn);
+    ntile = Le / mt_e;
+    const int m = Le - ntile * mt_e;
+    row0 = __builtin_amdgcn_readlane(lo[h], ln) + m * BIG_BM;
+    nrows = min(BIG_BM, __builtin_amdgcn_readlane(rows[h], ln) - m * BIG_BM);
+    return true;
+}
 
 template <int MI, bool DUAL, int ACT, bool OUT_BF16>
 __device__ __forceinline__ void big_tile(char *lds, const uint16_t *__restrict__ A,
@@ -513,8 +607,7 @@ __global__ __launch_bounds__(256) void gemm_bf16_big_kernel(
     __shared__ __attribute__((aligned(1024))) char lds[5 * 256 * 128];
 
     int e, row0, nrows, ntile, split = 0;
-    if (!find_tile<BIG_BM>(offsets, E, (N + BN - 1) / BN, e, row0, nrows, ntile, nsplit, &split))
-        return;
+    if (!find_tile_balanced(offsets, E, (N + BN - 1) / BN, nsplit, e, row0, nrows, ntile, split)) return;
     // K split: this tile covers stages [split * KT, (split + 1) * KT) and
     // the second half writes its partial sums to C_split
     void *const C = split ? C_split : C_;
@@ -797,8 +890,12 @@ hipError_t launch_big(const Shape &s, const void *A, const int32_t *a_rows, cons
                       void *C_split = nullptr) {
     constexpr int BN = DUAL ? 128 : 256;
     const unsigned nt = (unsigned)((N + BN - 1) / BN);
-    unsigned blocks = nt * row_tile_bound(s, BIG_BM) * (unsigned)nsplit;
-    blocks = (blocks + NUM_XCD - 1) / NUM_XCD * NUM_XCD;
+    // tiles <= `bound`; an XCD's run costs at most C / 8 plus one full tile,
+    // C <= 25 bound, and a tile costs at least 18: runs of at most
+    // (25 bound / 8 + 25) / 18 tiles
+    const unsigned bound = nt * row_tile_bound(s, BIG_BM) * (unsigned)nsplit;
+    const unsigned run = (unsigned)(((uint64_t)25 * bound + 8 * 25) / (8 * 18)) + 1;
+    const unsigned blocks = run * NUM_XCD;
     launch_kernel((gemm_bf16_big_kernel<DUAL, ACT, OUT_BF16>), dim3(blocks), dim3(256), 0, st,
                        (const uint16_t *)A, a_rows, offsets, s.E, (const uint16_t *)B1,
                        (const uint16_t *)B3, C, N, K, nsplit, C_split);
