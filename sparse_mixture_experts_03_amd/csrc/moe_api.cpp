@@ -54,6 +54,7 @@ int check_desc(const moe_desc *desc, Shape *s) {
 struct Layout {
     size_t part_P, part_lse2, fP, arrivals;         // router partials, f_e*P_e and z, counter
     size_t part_logits;                             // bf16 router: logit slices
+    size_t wsplit;                                  // bf16 router GEMM: split W_r (0: none)
     size_t chunk_counts;                            // dispatch: per-chunk expert histograms
     size_t topk_idx, gates, routed, kept, offsets;  // moe_forward's optional outputs
     size_t row_of_slot, token_of_row, dropped, stats;
@@ -80,7 +81,8 @@ Layout layout(const Shape &s) {
     L.fP = take(((size_t)s.E + 1) * sizeof(double));
     L.arrivals = take(sizeof(unsigned));
     if (s.dtype == MOE_DTYPE_BF16) {
-        L.part_logits = take((size_t)moe::route_nsplit(s) * (size_t)s.T * (size_t)s.E * 4);
+        L.part_logits = take(moe::route_part_floats(s) * 4);
+        L.wsplit = moe::route_gemm(s) ? take(moe::route_wsplit_bytes(s)) : 0;
     }
     L.chunk_counts = take((size_t)moe::dispatch_chunks(s) * (size_t)s.E * 4);
     L.topk_idx = take(Tk * 4);
@@ -190,6 +192,7 @@ int moe_route(const moe_desc *desc, const void *x, const float *W_r, const float
     }
     MOE_TRY(moe::launch_route(s, x, W_r, bias, noise, topk_idx, gates, at<float>(ws, L.part_P),
                               at<float>(ws, L.part_lse2), at<float>(ws, L.part_logits),
+                              L.wsplit ? at<char>(ws, L.wsplit) : nullptr,
                               at<unsigned>(ws, L.arrivals), st));
     MOE_TRY(moe::launch_route_finalize(s, topk_idx, at<float>(ws, L.part_P),
                                        at<float>(ws, L.part_lse2), stats,
@@ -287,6 +290,7 @@ int moe_forward(const moe_desc *desc, const void *x, const float *W_r, const flo
     } else {
         MOE_TRY(moe::launch_route(s, x, W_r, bias, noise, topk_idx, gates, at<float>(ws, L.part_P),
                                   at<float>(ws, L.part_lse2), at<float>(ws, L.part_logits),
+                                  L.wsplit ? at<char>(ws, L.wsplit) : nullptr,
                                   at<unsigned>(ws, L.arrivals), st));
         MOE_TRY(ev.record(st));
         MOE_TRY(moe::launch_route_finalize(s, topk_idx, at<float>(ws, L.part_P),

@@ -355,14 +355,51 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const uint16_t *__re
         }
 }
 
-// The block's tile of logits is contiguous in every slice ([t0*E, +8*E)),
-// so each thread sums up to 4 entries over the slices with all its loads
-// of one slice in flight together; the slices are added in slice order.
+// The three bf16 terms of W_r (the same split as the logits kernel makes
+// in LDS), stacked: row q * epad + e of ws holds term q of expert e, rows
+// of experts >= E are zero.  Thread: 4 consecutive k of one expert.  Block
+// 0 also writes the row offsets {0, T} of the router GEMM's one row group.
+__global__ __launch_bounds__(256) void router_wsplit_kernel(const float *__restrict__ Wr, int E, int epad,
+                                                            int d, int T, uint16_t *__restrict__ ws,
+                                                            int32_t *__restrict__ roffs) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;   // 4-wide group
+    if (blockIdx.x == 0 && threadIdx.x < 2) roffs[threadIdx.x] = threadIdx.x ? T : 0;
+    const int dq = d / 4;
+    if (i >= (int64_t)epad * dq) return;
+    const int e = (int)(i / dq), kc = (int)(i - (int64_t)e * dq) * 4;
+    float w[4] = {0.f, 0.f, 0.f, 0.f};
+    if (e < E) {
+        const float4 v = *(const float4 *)(Wr + (int64_t)e * d + kc);
+        w[0] = v.x, w[1] = v.y, w[2] = v.z, w[3] = v.w;
+    }
+    uint16_t t[3][4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const uint16_t hi = f32_to_bf16(w[j]);
+        const float r1 = w[j] - bf16_to_f32(hi);
+        const uint16_t mid = f32_to_bf16(r1);
+        const float r2 = r1 - bf16_to_f32(mid);
+        t[0][j] = hi;
+        t[1][j] = mid;
+        t[2][j] = f32_to_bf16(r2);
+    }
+#pragma unroll
+    for (int q = 0; q < 3; ++q)
+        *(uint2 *)(ws + ((int64_t)q * epad + e) * d + kc) =
+            make_uint2((uint32_t)t[q][0] | ((uint32_t)t[q][1] << 16), (uint32_t)t[q][2] | ((uint32_t)t[q][3] << 16));
+}
+
+// Logit (t, e) is the sum over partials o < nouter (outer stride souter)
+// and i < ninner (inner stride sinner) of part[o, i][t * stride_t + e],
+// added in (o, i) order: the d slices of the logits kernel (nouter slices,
+// one inner), or the K halves and the three W_r terms of the router GEMM.
+// Each thread handles up to 4 (token, expert) entries of the block's tile
+// with all its loads of one partial in flight together.
 __global__ __launch_bounds__(RT_THREADS) void route_epilogue_kernel(
-    const float *__restrict__ part, int nsplit, const float *__restrict__ bias,
-    const float *__restrict__ noise, int T, int E, int k, int gate_switch,
-    int32_t *__restrict__ topk_idx, float *__restrict__ gates, float *__restrict__ part_P,
-    float *__restrict__ part_lse2, unsigned *__restrict__ arrivals) {
+    const float *__restrict__ part, int nouter, int64_t souter, int ninner, int sinner, int stride_t,
+    const float *__restrict__ bias, const float *__restrict__ noise, int T, int E, int k,
+    int gate_switch, int32_t *__restrict__ topk_idx, float *__restrict__ gates,
+    float *__restrict__ part_P, float *__restrict__ part_lse2, unsigned *__restrict__ arrivals) {
     constexpr int TILE = ROUTE_TOKENS_BF16;
     __shared__ float hl[TILE][RT_EMAX + 1];
     constexpr int MAXQ = TILE * RT_EMAX / RT_THREADS;
@@ -371,16 +408,23 @@ __global__ __launch_bounds__(RT_THREADS) void route_epilogue_kernel(
     const int64_t base = (int64_t)t0 * E;
     const int npairs = min(TILE, T - t0) * E;
     float h[MAXQ];
+    int64_t off[MAXQ];
 #pragma unroll
-    for (int q = 0; q < MAXQ; ++q) h[q] = 0.f;
-    for (int sl = 0; sl < nsplit; ++sl) {
-        const float *ps = part + (int64_t)sl * T * E + base;
-#pragma unroll
-        for (int q = 0; q < MAXQ; ++q) {
-            const int i = tid + q * RT_THREADS;
-            if (i < npairs) h[q] += ps[i];
-        }
+    for (int q = 0; q < MAXQ; ++q) {
+        const int i = tid + q * RT_THREADS;
+        const int r = i / E, e = i - r * E;
+        h[q] = 0.f;
+        off[q] = (int64_t)(t0 + r) * stride_t + e;
     }
+    for (int o = 0; o < nouter; ++o)
+        for (int in = 0; in < ninner; ++in) {
+            const float *ps = part + o * souter + (int64_t)in * sinner;
+#pragma unroll
+            for (int q = 0; q < MAXQ; ++q) {
+                const int i = tid + q * RT_THREADS;
+                if (i < npairs) h[q] += ps[off[q]];
+            }
+        }
 #pragma unroll
     for (int q = 0; q < MAXQ; ++q) {
         const int i = tid + q * RT_THREADS;
@@ -633,15 +677,58 @@ int route_nsplit(const Shape &s) {
     return (s.d + slice - 1) / slice;
 }
 
+// The GEMM pays off where the logits kernel re-splits a large W_r for every
+// 64-token tile: many experts and a batch past the small-batch kernel.  The
+// 256-row kernel needs d % 64 == 0 and its operand offsets within 32 bits.
+bool route_gemm(const Shape &s) {
+    if (s.dtype != 1 || route_small(s) || route_epad(s) < 64 || s.d % 64 != 0) return false;
+    return (int64_t)s.T * s.d * 2 < (int64_t(1) << 31) && (int64_t)3 * route_epad(s) * s.d * 2 < (int64_t(1) << 31);
+}
+
+// K halves: when the 256 x 256 output tiles would fill less than one round
+// of the CUs and the 64-wide K stages split evenly.
+int route_gemm_nsplit(const Shape &s) {
+    const int64_t tiles = (int64_t)((s.T + 255) / 256) * ((3 * route_epad(s) + 255) / 256);
+    return tiles < 256 && (s.d / 64) % 2 == 0 ? 2 : 1;
+}
+
+static size_t route_wsplit_matrix_bytes(const Shape &s) {
+    return ((size_t)3 * route_epad(s) * s.d * 2 + 255) / 256 * 256;
+}
+
+size_t route_part_floats(const Shape &s) {
+    if (route_gemm(s)) return (size_t)route_gemm_nsplit(s) * s.T * 3 * route_epad(s);
+    return (size_t)route_nsplit(s) * s.T * s.E;
+}
+
+size_t route_wsplit_bytes(const Shape &s) {
+    return route_gemm(s) ? route_wsplit_matrix_bytes(s) + 256 : 0;
+}
+
 hipError_t launch_route(const Shape &s, const void *x, const float *Wr, const float *bias,
                         const float *noise, int32_t *topk_idx, float *gates, float *part_P,
-                        float *part_lse2, float *part_logits, unsigned *arrivals,
+                        float *part_lse2, float *part_logits, void *wsplit, unsigned *arrivals,
                         hipStream_t st) {
     const dim3 grid(route_blocks(s)), block(RT_THREADS);
     if (s.dtype == 0) {
         hipLaunchKernelGGL(route_f32_kernel, grid, block, 0, st, (const float *)x, Wr, bias, noise,
                            s.T, s.d, s.E, s.k, s.gate, topk_idx, gates, part_P, part_lse2,
                            arrivals);
+        return hipGetLastError();
+    }
+    if (route_gemm(s)) {
+        if (wsplit == nullptr) return hipErrorInvalidValue;
+        const int epad = route_epad(s), N = 3 * epad;
+        uint16_t *wm = (uint16_t *)wsplit;
+        int32_t *roffs = (int32_t *)((char *)wsplit + route_wsplit_matrix_bytes(s));
+        const int64_t groups = (int64_t)epad * (s.d / 4);
+        hipLaunchKernelGGL(router_wsplit_kernel, dim3((unsigned)((groups + 255) / 256)), dim3(256), 0, st, Wr,
+                           s.E, epad, s.d, s.T, wm, roffs);
+        const hipError_t err = launch_router_gemm(s, x, wm, roffs, part_logits, st);
+        if (err != hipSuccess) return err;
+        hipLaunchKernelGGL(route_epilogue_kernel, grid, block, 0, st, (const float *)part_logits,
+                           route_gemm_nsplit(s), (int64_t)s.T * N, 3, epad, N, bias, noise, s.T, s.E, s.k,
+                           s.gate, topk_idx, gates, part_P, part_lse2, arrivals);
         return hipGetLastError();
     }
     switch (route_epad(s)) {
@@ -651,8 +738,8 @@ hipError_t launch_route(const Shape &s, const void *x, const float *Wr, const fl
     default: launch_logits<128, 1, 4>(s, x, Wr, part_logits, st); break;
     }
     hipLaunchKernelGGL(route_epilogue_kernel, grid, block, 0, st, (const float *)part_logits,
-                       route_nsplit(s), bias, noise, s.T, s.E, s.k, s.gate, topk_idx, gates,
-                       part_P, part_lse2, arrivals);
+                       route_nsplit(s), (int64_t)s.T * s.E, 1, 0, s.E, bias, noise, s.T, s.E, s.k, s.gate,
+                       topk_idx, gates, part_P, part_lse2, arrivals);
     return hipGetLastError();
 }
 

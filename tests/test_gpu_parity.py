@@ -78,6 +78,16 @@ SMALL = {
     # Switch gate with k = 2, 64-row SwiGLU tiles
     "switch_k2": W["mixtral_prefill"].with_(name="switch_k2", T=500, d=128, d_ff=256, E=16, k=2,
                                             gate="switch", x_rmsnorm=False),
+    # router logits as a GEMM against the stacked W_r terms (more than 32
+    # experts past the small-batch kernel): E = 100 (padded to 128, 384
+    # stacked rows: a partial column tile), ragged T = 700 (256 + 256 + 188
+    # rows), an odd number of 64-wide k stages (d = 320: no K split), top-4
+    # of 100 with the Zipf router bias
+    "router_gemm": W["finegrained_zipf"].with_(name="router_gemm", T=700, d=320, d_ff=256, E=100),
+    # the same with E = 64 (192 stacked rows) and the K split in two
+    # (d = 256), Switch gate with noise and capacity drops
+    "router_gemm_split": W["switch"].with_(name="router_gemm_split", T=300, d=256, d_ff=384, E=64,
+                                           noise_std=1.0 / 64),
 }
 
 
@@ -110,7 +120,7 @@ def test_forward_matches_oracle(name):
 
 
 @pytest.mark.parametrize("name", ["mixtral_small", "zipf_small", "tiny", "switch_small",
-                                  "big_splitk", "decode_small", "small_drops"])
+                                  "big_splitk", "decode_small", "small_drops", "router_gemm"])
 def test_staged_entry_points(name):
     """route, dispatch, expert_ffn and combine called one by one: x_perm is
     the exact gather, y_perm matches the oracle's per-row expert outputs,
