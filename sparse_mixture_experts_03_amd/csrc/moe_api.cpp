@@ -76,7 +76,7 @@ Layout layout(const Shape &s) {
         o = align_up(o + bytes);
         return at;
     };
-    L.part_P = take(nblk * s.E * sizeof(float));
+    L.part_P = take(2 * nblk * s.E * sizeof(float));  // p sums, top-choice counts
     L.part_lse2 = take(nblk * sizeof(float));
     L.fP = take(((size_t)s.E + 1) * sizeof(double));
     L.arrivals = take(sizeof(unsigned));

@@ -30,9 +30,9 @@
 // lane l holds experts l and l+64): max and sum of exponentials by shuffle
 // reductions, top-k by k arg-max reductions over 64-bit keys (orderable
 // logit bits, then the complement of the index, so a tie goes to the lower
-// index), gates, and per-block partial sums of p (per expert) and of lse^2
-// in a fixed order.  route_stats_kernel reduces the partials in double in
-// a fixed order and counts top choices.
+// index), gates, and per-block partials: sums of p and counts of top
+// choices (per expert) and the sum of lse^2, in a fixed order.
+// route_stats_kernel reduces the partials in double in a fixed order.
 #include "moe_internal.h"
 
 namespace moe {
@@ -76,7 +76,10 @@ __device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long v)
 
 // The per-token epilogue over a block's logits tile hl[TILE][.]
 // (already synchronised), NW waves, wave w taking tokens w, w + NW, ...
-// Every thread of the block must call it.
+// Every thread of the block must call it.  Block partials, for a grid of
+// nblk blocks: part_P[e * nblk + b] = sum of p_e over the block's tokens
+// (waves in order), part_P[(E + e) * nblk + b] = how many of them have e as
+// their top choice (an exact small integer in a float), part_lse2[b].
 template <int TILE, int NW = 4>
 __device__ void softmax_topk_block(const float (*hl)[RT_EMAX + 1], int t0, int T, int E, int k,
                                    int gate_switch, int32_t *__restrict__ topk_idx,
@@ -85,6 +88,7 @@ __device__ void softmax_topk_block(const float (*hl)[RT_EMAX + 1], int t0, int T
                                    float *P_sh = nullptr, float *lse2_sh = nullptr) {
     __shared__ float pw[NW][RT_EMAX];
     __shared__ float lw[NW];
+    __shared__ int topch[TILE];   // each token's top choice
     const int tid = threadIdx.x;
     const int lane = tid & 63, w = tid >> 6;
     const int e0 = lane, e1 = lane + 64;
@@ -117,7 +121,10 @@ __device__ void softmax_topk_block(const float (*hl)[RT_EMAX + 1], int t0, int T
             if (bi == e0) k0 = 0ull;
             if (bi == e1) k1 = 0ull;
             float hb = hl[r][bi];  // the selected logit (same address on every lane)
-            if (sl == 0) h_top = hb;
+            if (sl == 0) {
+                h_top = hb;
+                if (lane == 0) topch[r] = bi;
+            }
             den += expf(hb - h_top);  // slot order, identical on every lane
             if (lane == (sl & 63)) {
                 if (sl < 64) { sh0 = hb; si0 = bi; }
@@ -142,7 +149,11 @@ __device__ void softmax_topk_block(const float (*hl)[RT_EMAX + 1], int t0, int T
         float a = pw[0][tid];
 #pragma unroll
         for (int v = 1; v < NW; ++v) a += pw[v][tid];
-        part_P[(int64_t)blockIdx.x * E + tid] = a;
+        const int64_t nblk = gridDim.x;
+        int c = 0;
+        for (int r = 0, nr = min(TILE, T - t0); r < nr; ++r) c += topch[r] == tid;
+        part_P[(int64_t)tid * nblk + blockIdx.x] = a;
+        part_P[(int64_t)(E + tid) * nblk + blockIdx.x] = (float)c;
         if (P_sh) P_sh[tid] = a;
     }
     if (tid == 0) {
@@ -444,7 +455,7 @@ __global__ __launch_bounds__(RT_THREADS) void route_epilogue_kernel(
 // Statistics in double, every sum in a fixed order.  route_stats_kernel:
 // block e < E reduces expert e's block partials of p (thread t takes blocks
 // t, t+256, ...; then the 256 thread sums are added in thread order) and
-// counts the tokens whose top choice is e; block E reduces the lse^2
+// adds up its block counts of top choices; block E reduces the lse^2
 // partials the same way.  The last block to finish (an integer arrival
 // counter, zeroed by the route kernel that runs before) adds the f_e P_e in
 // expert order for aux and writes aux and z, then re-zeroes the counter.
@@ -452,9 +463,19 @@ __device__ __forceinline__ double block_sum_fixed(double v, double *red) {
     const int tid = threadIdx.x;
     red[tid] = v;
     __syncthreads();
+    // threads 0..15 each add 16 consecutive values in order, then thread 0
+    // adds the 16 group sums in order
+    if (tid < 16) {
+        double g = 0.0;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) g += red[tid * 16 + i];
+        red[256 + tid] = g;
+    }
+    __syncthreads();
     double total = 0.0;
     if (tid == 0)
-        for (int i = 0; i < 256; ++i) total += red[i];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) total += red[256 + i];
     return total;  // valid in thread 0
 }
 
@@ -462,7 +483,7 @@ __global__ __launch_bounds__(256) void route_stats_kernel(
     const int32_t *__restrict__ topk_idx, const float *__restrict__ part_P,
     const float *__restrict__ part_lse2, int T, int E, int k, int nblk,
     float *__restrict__ stats, double *__restrict__ fP, unsigned *__restrict__ arrivals) {
-    __shared__ double red[256];
+    __shared__ double red[256 + 16];
     __shared__ int cnt[4];
     __shared__ int last;
     const int tid = threadIdx.x;
@@ -473,12 +494,17 @@ __global__ __launch_bounds__(256) void route_stats_kernel(
         z = block_sum_fixed(z, red);
         if (tid == 0) fP[E] = z / (double)T;
     } else {
+        // expert e's block partials are contiguous: p sums, then top-choice
+        // counts
+        const float *pp = part_P + (int64_t)e * nblk;
+        const float *pc = part_P + (int64_t)(E + e) * nblk;
         double acc = 0.0;
-#pragma unroll 4
-        for (int b = tid; b < nblk; b += 256) acc += (double)part_P[(int64_t)b * E + e];
         int c = 0;
 #pragma unroll 8
-        for (int t = tid; t < T; t += 256) c += topk_idx[(int64_t)t * k] == e;
+        for (int b = tid; b < nblk; b += 256) {
+            acc += (double)pp[b];
+            c += (int)pc[b];
+        }
         // integer count: the order of the additions does not matter
         for (int o = 32; o > 0; o >>= 1) c += __shfl_xor(c, o);
         if ((tid & 63) == 0) cnt[tid >> 6] = c;
@@ -495,14 +521,20 @@ __global__ __launch_bounds__(256) void route_stats_kernel(
         last = atomicAdd(arrivals, 1u) == (unsigned)E;
     }
     __syncthreads();
-    if (last && tid == 0) {
+    if (last) {
+        // every block's f_e P_e (and z) is visible: all threads load them
+        // at once, thread 0 adds them in expert order
         __threadfence();
-        const volatile double *v = fP;
-        double a = 0.0;
-        for (int i = 0; i < E; ++i) a += v[i];
-        stats[2 * E] = (float)((double)E * a);
-        stats[2 * E + 1] = (float)v[E];
-        *arrivals = 0u;
+        for (int i = tid; i <= E; i += 256)
+            red[i] = __hip_atomic_load(fP + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __syncthreads();
+        if (tid == 0) {
+            double a = 0.0;
+            for (int i = 0; i < E; ++i) a += red[i];
+            stats[2 * E] = (float)((double)E * a);
+            stats[2 * E + 1] = (float)red[E];
+            *arrivals = 0u;
+        }
     }
 }
 
