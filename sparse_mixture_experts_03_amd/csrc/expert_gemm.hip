@@ -31,6 +31,7 @@
 //
 // gemm_f32 kernels: a plain fp32 path (one block per row, one thread per
 // output column, sequential fp32 FMA over K) for fp32 layers.
+#include <atomic>
 #include <type_traits>
 
 #include "moe_internal.h"
@@ -245,7 +246,10 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(
 // takes only as many 64-row slabs as it needs (MI = 1..4 slabs; each wave
 // then holds MI 32-row fragments), so a ragged expert pads at most 63 rows
 // instead of up to 255.  Tiles are spread over the XCDs by cost
-// (find_tile_balanced).
+// (find_tile_balanced).  The plain kernel also has half-width tiles (NJ = 2
+// column groups per wave instead of 4) for the last round of a run; the
+// SwiGLU kernel is built without them (their code alone slowed its whole
+// tiles by ~1%).
 // Operands go from global memory straight into LDS with
 // buffer_load_dwordx4 ... lds (no register staging): instruction j of a
 // wave fills 8 LDS rows, lane l writing the 16 bytes at (row + l/8, slot
@@ -281,7 +285,10 @@ constexpr int BIG_BM = 256;
 // starting cost lies in [x C / 8, (x+1) C / 8) of the total cost C, and
 // its blocks (slot b / 8) take the run's tiles in order; so every XCD gets
 // the same amount of work and the row tiles sharing a weight panel run on
-// one XCD at the same time.  Each wave computes the schedule by itself,
+// one XCD at the same time.  In the plain (non-SwiGLU) kernel, the last
+// partial round of a run, when it would leave at least half of the XCD's
+// CUs idle, is done as half-width pieces (two per tile, 128 columns each).
+// Each wave computes the schedule by itself,
 // one expert per lane (two for E > 64) with shuffle prefix sums: one read
 // of offsets and no loop over the experts.
 constexpr int BIG_W_FULL = 25;
@@ -300,8 +307,8 @@ __device__ __forceinline__ int wave_incl_scan(int v, int lane) {
 }
 
 __device__ __forceinline__ bool find_tile_balanced(const int32_t *__restrict__ offsets, int E, int ntn,
-                                                   int nsplit, int &e, int &row0, int &nrows, int &ntile,
-                                                   int &split) {
+                                                   int nsplit, int cpx, int &e, int &row0, int &nrows,
+                                                   int &ntile, int &split, int &half) {
     const int lane = threadIdx.x & 63;
     // experts lane and lane + 64; every value taken out of a lane is read
     // with readlane at a uniform lane, so it lands in a scalar register
@@ -348,8 +355,23 @@ __device__ __forceinline__ bool find_tile_balanced(const int32_t *__restrict__ o
     const int x = blockIdx.x % NUM_XCD;
     const int start = first_at(C * x / NUM_XCD);
     const int end = x == NUM_XCD - 1 ? Ts * nsplit : first_at(C * (x + 1) / NUM_XCD);
-    const int L = start + (int)(blockIdx.x / NUM_XCD);
-    if (L >= end) return false;
+    // The run's last partial round (r tiles on the XCD's cpx CUs): when it
+    // would leave at least half of them idle, its tiles are done as two
+    // half-width pieces each (half = 1, 2), so the round ends sooner.
+    const int n = end - start, r = cpx > 0 ? n % cpx : 0;
+    const bool halves = cpx > 0 && r > 0 && 2 * r <= cpx;
+    const int slot = (int)(blockIdx.x / NUM_XCD);
+    int L;
+    half = 0;
+    if (!halves || slot < n - r) {
+        L = start + slot;
+        if (L >= end) return false;
+    } else {
+        const int p = slot - (n - r);
+        if (p >= 2 * r) return false;
+        L = start + (n - r) + (p >> 1);
+        half = 1 + (p & 1);
+    }
     split = L / Ts;
     const int Lr = L - split * Ts;
     const unsigned long long m0 = __ballot(cumT[0] > Lr), m1 = __ballot(cumT[1] > Lr);
@@ -365,21 +387,24 @@ __device__ __forceinline__ bool find_tile_balanced(const int32_t *__restrict__ o
     return true;
 }
 
-template <int MI, bool DUAL, int ACT, bool OUT_BF16>
+template <int MI, int NJ, bool DUAL, int ACT, bool OUT_BF16>
 __device__ __forceinline__ void big_tile(char *lds, const uint16_t *__restrict__ A,
                                          const int32_t *__restrict__ a_rows,
                                          const uint16_t *__restrict__ B1,
                                          const uint16_t *__restrict__ B3, void *__restrict__ C, int N,
                                          int K, int e, int row0, int nrows, int n0, int KT, int kbeg) {
     constexpr int BK = 64;
-    constexpr int BN = DUAL ? 128 : 256;   // output columns per block
+    static_assert(NJ == 4 || NJ == 2, "whole or half-width tiles");
+    constexpr int BN = DUAL ? 32 * NJ : 64 * NJ;   // output columns per block
+    constexpr int WCOL = DUAL ? 16 * NJ : 32 * NJ;  // output columns per wave column (wn)
     constexpr int ROWB = BK * 2;           // bytes per LDS row (8 slots of 16 bytes)
     constexpr int OPB = 256 * ROWB;        // bytes per operand per stage
     constexpr int WROWS = MI * 32;         // A rows per wave row (wm)
     constexpr int NQA = 2 * MI;            // A loads per wave per stage (8 rows each)
-    constexpr int NQ = NQA + 8;            // + 8 weight loads
-    constexpr int NMF = MI * 4;            // MFMAs per wave per 16-wide k step
-    constexpr int NRD = MI + 4;            // fragment reads per k step
+    constexpr int NQB = 2 * NJ;            // weight loads per wave per stage
+    constexpr int NQ = NQA + NQB;
+    constexpr int NMF = MI * NJ;           // MFMAs per wave per 16-wide k step
+    constexpr int NRD = MI + NJ;           // fragment reads per k step
     const int tid = threadIdx.x, lane = tid & 63;
     // the wave index as a scalar, so LDS destinations (M0) and operand bases
     // are computed on the scalar unit
@@ -391,7 +416,7 @@ __device__ __forceinline__ void big_tile(char *lds, const uint16_t *__restrict__
     // (l % 8) ^ (l / 8) ^ (j % 2).  Per-lane byte offsets into the operand;
     // they do not change from stage to stage.
     const int sub = lane >> 3;
-    uint32_t a_off[NQA], b_off[8];
+    uint32_t a_off[NQA], b_off[NQB];
     // buffer resources (dword 3 = 0x00020000: raw 32-bit data, no swizzle,
     // bounds not relied on: every offset is in range by construction)
     const __amdgpu_buffer_rsrc_t a_rsrc =
@@ -405,12 +430,13 @@ __device__ __forceinline__ void big_tile(char *lds, const uint16_t *__restrict__
             const int ar = row0 + min(r, nrows - 1);
             a_off[j] = ((uint32_t)(a_rows ? a_rows[ar] : ar) * (uint32_t)K + kchunk) * 2u;
         }
-        // SwiGLU: waves 0,1 fill W1 rows 0..127, waves 2,3 W3 rows 0..127
+        // wave w fills LDS weight rows 16 NJ w .. +16 NJ; SwiGLU: waves 0,1
+        // the W1 rows of the tile (BN of them), waves 2,3 the same W3 rows
         const uint16_t *bb = ((DUAL && wave >= 2) ? B3 : B1) + (int64_t)e * N * K;
         b_rsrc = __builtin_amdgcn_make_buffer_rsrc((void *)bb, 0, 0x7fffffff, 0x00020000);
-        const int brow0 = DUAL ? ((wave * 64) & 127) : wave * 64;
+        const int brow0 = DUAL ? ((wave * 16 * NJ) & (BN - 1)) : wave * 16 * NJ;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
+        for (int j = 0; j < NQB; ++j) {
             const int kchunk = ((lane & 7) ^ sub ^ (j & 1)) * 8;
             const int r = brow0 + j * 8 + sub;
             b_off[j] = ((uint32_t)min(n0 + r, N - 1) * (uint32_t)K + kchunk) * 2u;
@@ -427,21 +453,21 @@ __device__ __forceinline__ void big_tile(char *lds, const uint16_t *__restrict__
         else
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
                 b_rsrc,
-                (__attribute__((address_space(3))) void *)(lds + (2 + bst) * OPB + (wave * 64 + (q - NQA) * 8) * ROWB),
+                (__attribute__((address_space(3))) void *)(lds + (2 + bst) * OPB + (wave * 16 * NJ + (q - NQA) * 8) * ROWB),
                 16, b_off[q - NQA], kb * 2, 0, 0);
     };
 
-    f32x16_t acc[MI][4];
+    f32x16_t acc[MI][NJ];
 #pragma unroll
     for (int i = 0; i < MI; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < NJ; ++j)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
     // Fragment rows: A rows wm*WROWS + i*32 + lane%32; weight rows of
-    // column group j (DUAL: j < 2 -> W1 rows wn*64 + j*32, j >= 2 -> W3 rows,
-    // 128 further on).  The swizzle only depends on lane % 32 and the k step,
+    // column group j: wn*WCOL + j*32 (DUAL: j < NJ/2 -> W1 rows wn*WCOL +
+    // j*32, j >= NJ/2 -> the same W3 rows, 32*NJ further on).  The swizzle only depends on lane % 32 and the k step,
     // so each (operand, k step) has one per-lane offset and every fragment
     // row, stage and operand is an immediate on top of it.  (The weight
     // operand's 64 KB base is part of the per-lane offset, which is made
@@ -453,20 +479,20 @@ __device__ __forceinline__ void big_tile(char *lds, const uint16_t *__restrict__
     for (int kk = 0; kk < 4; ++kk) {
         const uint32_t slot = (uint32_t)(((kk * 2 + (lane >> 5)) ^ (lr & 7) ^ ((lr >> 3) & 1)) * 16);
         rd_a[kk] = (uint32_t)(wm * WROWS + lr) * ROWB + slot;
-        rd_b[kk] = 2u * OPB + (uint32_t)((DUAL ? wn * 64 : wn * 128) + lr) * ROWB + slot;
+        rd_b[kk] = 2u * OPB + (uint32_t)(wn * WCOL + lr) * ROWB + slot;
         asm volatile("" : "+v"(rd_a[kk]), "+v"(rd_b[kk]));
     }
     char *const lds0 = lds;
     // fragment read f (0..NRD-1) of k step kk, in the order the MFMAs
-    // consume them: A0, B0, B1, B2, B3, A1, ..., A(MI-1)
-    auto read_one = [&](auto stage_c, int kk, int f, bf16x8_t (&a)[MI], bf16x8_t (&b)[4], uint32_t bso) {
+    // consume them: A0, B0, ..., B(NJ-1), A1, ..., A(MI-1)
+    auto read_one = [&](auto stage_c, int kk, int f, bf16x8_t (&a)[MI], bf16x8_t (&b)[NJ], uint32_t bso) {
         constexpr int stage = decltype(stage_c)::value;
-        if (f == 0 || f >= 5) {
-            const int i = f == 0 ? 0 : f - 4;
+        if (f == 0 || f > NJ) {
+            const int i = f == 0 ? 0 : f - NJ;
             a[i] = *(const bf16x8_t *)(lds0 + rd_a[kk] + (stage * OPB + i * 32 * ROWB));
         } else {
             const int j = f - 1;
-            const int jo = DUAL ? ((j >> 1) * 128 + (j & 1) * 32) : j * 32;
+            const int jo = DUAL ? ((j / (NJ / 2)) * 32 * NJ + (j % (NJ / 2)) * 32) : j * 32;
             b[j] = *(const bf16x8_t *)(lds0 + (rd_b[kk] + bso) + jo * ROWB);
         }
     };
@@ -481,7 +507,7 @@ __device__ __forceinline__ void big_tile(char *lds, const uint16_t *__restrict__
     // pipe).  Near the end the loads re-load the last stage into an idle
     // buffer (nobody reads it), which keeps the loop free of branches and
     // the count of loads in flight fixed.
-    bf16x8_t fa[2][MI], fb[2][4];
+    bf16x8_t fa[2][MI], fb[2][NJ];
     auto stage_body = [&](auto cur_c, int kt, int bcur) {
         constexpr int cur = decltype(cur_c)::value;
         constexpr std::integral_constant<int, cur ^ 1> nxt_c{};
@@ -489,10 +515,10 @@ __device__ __forceinline__ void big_tile(char *lds, const uint16_t *__restrict__
         const int kb = kbeg + min(kt + 2, KT - 1) * BK;
         const int bnext = bcur == 0 ? 2 : bcur - 1;   // (bcur + 2) % 3
         const uint32_t bso = (uint32_t)bcur * OPB;
-        // this wave's loads of the stage have landed (only the 8 weight
+        // this wave's loads of the stage have landed (only the NQB weight
         // loads of the stage after next, issued last, may still be in
         // flight); after the barrier, everyone's have
-        asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(NQB) : "memory");
         // step 0's fragments in consumption order (kept by the scheduling
         // barriers), so the first MFMA waits for two reads, not all of them
 #pragma unroll
@@ -504,7 +530,7 @@ __device__ __forceinline__ void big_tile(char *lds, const uint16_t *__restrict__
         for (int kk = 0; kk < 4; ++kk) {
 #pragma unroll
             for (int t = 0; t < NMF; ++t) {
-                const int i = t >> 2, j = t & 3;
+                const int i = t / NJ, j = t % NJ;
                 acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[kk & 1][i], fb[kk & 1][j],
                                                                     acc[i][j], 0, 0, 0);
                 if (kk < 2) {
@@ -550,17 +576,17 @@ __device__ __forceinline__ void big_tile(char *lds, const uint16_t *__restrict__
         const __amdgpu_buffer_rsrc_t c_rsrc = __builtin_amdgcn_make_buffer_rsrc(
             (char *)C + (int64_t)row0 * N * ES, 0, 0x7fffffff, 0x00020000);
         const uint32_t vo =
-            ((uint32_t)(4 * (lane >> 5)) * (uint32_t)N + (uint32_t)(n0 + (DUAL ? wn * 64 : wn * 128) + lr)) * ES;
+            ((uint32_t)(4 * (lane >> 5)) * (uint32_t)N + (uint32_t)(n0 + wn * WCOL + lr)) * ES;
 #pragma unroll
         for (int i = 0; i < MI; ++i)
 #pragma unroll
-            for (int jj = 0; jj < (DUAL ? 2 : 4); ++jj) {
+            for (int jj = 0; jj < (DUAL ? NJ / 2 : NJ); ++jj) {
                 __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const uint32_t so =
                         (uint32_t)(wm * WROWS + i * 32 + (r >> 2) * 8 + (r & 3)) * (uint32_t)(N * ES);
-                    const float v = DUAL ? apply_act(ACT, acc[i][jj][r], acc[i][jj + 2][r])
+                    const float v = DUAL ? apply_act(ACT, acc[i][jj][r], acc[i][jj + NJ / 2][r])
                                          : apply_act(ACT, acc[i][jj][r], 0.f);
                     if (OUT_BF16)
                         __builtin_amdgcn_raw_buffer_store_b16(
@@ -575,16 +601,16 @@ __device__ __forceinline__ void big_tile(char *lds, const uint16_t *__restrict__
 #pragma unroll
     for (int i = 0; i < MI; ++i)
 #pragma unroll
-        for (int jj = 0; jj < (DUAL ? 2 : 4); ++jj) {
+        for (int jj = 0; jj < (DUAL ? NJ / 2 : NJ); ++jj) {
             // one 32 x 32 tile at a time: keeps the activation's temporaries
             // from piling up across tiles
             __builtin_amdgcn_sched_barrier(0);
-            const int col = n0 + (DUAL ? wn * 64 + jj * 32 : wn * 128 + jj * 32) + lr;
+            const int col = n0 + wn * WCOL + jj * 32 + lr;
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int row = wm * WROWS + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
                 if (row < nrows && col < N) {
-                    const float v = DUAL ? apply_act(ACT, acc[i][jj][r], acc[i][jj + 2][r])
+                    const float v = DUAL ? apply_act(ACT, acc[i][jj][r], acc[i][jj + NJ / 2][r])
                                          : apply_act(ACT, acc[i][jj][r], 0.f);
                     const int64_t o = (int64_t)(row0 + row) * N + col;
                     if (OUT_BF16)
@@ -601,27 +627,41 @@ __global__ __launch_bounds__(256) void gemm_bf16_big_kernel(
     const uint16_t *__restrict__ A, const int32_t *__restrict__ a_rows,
     const int32_t *__restrict__ offsets, int E, const uint16_t *__restrict__ B1,
     const uint16_t *__restrict__ B3, void *__restrict__ C_, int N, int K, int nsplit,
-    void *__restrict__ C_split) {
+    void *__restrict__ C_split, int cpx) {
     constexpr int BN = DUAL ? 128 : 256;
     // A stages 0, 1 at 0 and 32 KB; weight stages 0..2 at 64, 96, 128 KB
     __shared__ __attribute__((aligned(1024))) char lds[5 * 256 * 128];
 
-    int e, row0, nrows, ntile, split = 0;
-    if (!find_tile_balanced(offsets, E, (N + BN - 1) / BN, nsplit, e, row0, nrows, ntile, split)) return;
+    int e, row0, nrows, ntile, split = 0, half = 0;
+    if (!find_tile_balanced(offsets, E, (N + BN - 1) / BN, nsplit, cpx, e, row0, nrows, ntile, split, half))
+        return;
     // K split: this tile covers stages [split * KT, (split + 1) * KT) and
     // the second half writes its partial sums to C_split
     void *const C = split ? C_split : C_;
     const int KT = K / 64 / nsplit;
     const int kbeg = split * KT * 64;
     const int mi = (nrows + 63) >> 6;   // 64-row slabs this tile needs
+    if constexpr (!DUAL) if (half) {
+        // half-width piece: columns [ntile * BN + (half - 1) * BN / 2, + BN / 2)
+        const int n0 = ntile * BN + (half - 1) * (BN / 2);
+        if (mi == 4)
+            big_tile<4, 2, DUAL, ACT, OUT_BF16>(lds, A, a_rows, B1, B3, C, N, K, e, row0, nrows, n0, KT, kbeg);
+        else if (mi == 3)
+            big_tile<3, 2, DUAL, ACT, OUT_BF16>(lds, A, a_rows, B1, B3, C, N, K, e, row0, nrows, n0, KT, kbeg);
+        else if (mi == 2)
+            big_tile<2, 2, DUAL, ACT, OUT_BF16>(lds, A, a_rows, B1, B3, C, N, K, e, row0, nrows, n0, KT, kbeg);
+        else
+            big_tile<1, 2, DUAL, ACT, OUT_BF16>(lds, A, a_rows, B1, B3, C, N, K, e, row0, nrows, n0, KT, kbeg);
+        return;
+    }
     if (mi == 4)
-        big_tile<4, DUAL, ACT, OUT_BF16>(lds, A, a_rows, B1, B3, C, N, K, e, row0, nrows, ntile * BN, KT, kbeg);
+        big_tile<4, 4, DUAL, ACT, OUT_BF16>(lds, A, a_rows, B1, B3, C, N, K, e, row0, nrows, ntile * BN, KT, kbeg);
     else if (mi == 3)
-        big_tile<3, DUAL, ACT, OUT_BF16>(lds, A, a_rows, B1, B3, C, N, K, e, row0, nrows, ntile * BN, KT, kbeg);
+        big_tile<3, 4, DUAL, ACT, OUT_BF16>(lds, A, a_rows, B1, B3, C, N, K, e, row0, nrows, ntile * BN, KT, kbeg);
     else if (mi == 2)
-        big_tile<2, DUAL, ACT, OUT_BF16>(lds, A, a_rows, B1, B3, C, N, K, e, row0, nrows, ntile * BN, KT, kbeg);
+        big_tile<2, 4, DUAL, ACT, OUT_BF16>(lds, A, a_rows, B1, B3, C, N, K, e, row0, nrows, ntile * BN, KT, kbeg);
     else
-        big_tile<1, DUAL, ACT, OUT_BF16>(lds, A, a_rows, B1, B3, C, N, K, e, row0, nrows, ntile * BN, KT, kbeg);
+        big_tile<1, 4, DUAL, ACT, OUT_BF16>(lds, A, a_rows, B1, B3, C, N, K, e, row0, nrows, ntile * BN, KT, kbeg);
 }
 
 // ---- skinny row groups (decode batches): weight streaming ----------------
@@ -884,6 +924,23 @@ hipError_t launch_gemm(const Shape &s, const void *A, const int32_t *a_rows, con
     return hipGetLastError();
 }
 
+// CUs per XCD of the current device (looked up once per device; 32 on
+// MI355X if the query fails).
+int device_cus_per_xcd() {
+    static std::atomic<int> cached[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 32;
+    int n = cached[dev].load(std::memory_order_relaxed);
+    if (n == 0) {
+        int cus = 0;
+        n = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && cus >= NUM_XCD
+                ? cus / NUM_XCD
+                : 32;
+        cached[dev].store(n, std::memory_order_relaxed);
+    }
+    return n;
+}
+
 template <bool DUAL, int ACT, bool OUT_BF16>
 hipError_t launch_big(const Shape &s, const void *A, const int32_t *a_rows, const int32_t *offsets, const void *B1,
                       const void *B3, void *C, int N, int K, hipStream_t st, int nsplit = 1,
@@ -894,11 +951,13 @@ hipError_t launch_big(const Shape &s, const void *A, const int32_t *a_rows, cons
     // C <= 25 bound, and a tile costs at least 18: runs of at most
     // (25 bound / 8 + 25) / 18 tiles
     const unsigned bound = nt * row_tile_bound(s, BIG_BM) * (unsigned)nsplit;
-    const unsigned run = (unsigned)(((uint64_t)25 * bound + 8 * 25) / (8 * 18)) + 1;
+    // (plus at most cpx / 2 extra slots for the half-width pieces)
+    const int cpx = device_cus_per_xcd();
+    const unsigned run = (unsigned)(((uint64_t)25 * bound + 8 * 25) / (8 * 18)) + 1 + (unsigned)(cpx / 2);
     const unsigned blocks = run * NUM_XCD;
     launch_kernel((gemm_bf16_big_kernel<DUAL, ACT, OUT_BF16>), dim3(blocks), dim3(256), 0, st,
                        (const uint16_t *)A, a_rows, offsets, s.E, (const uint16_t *)B1,
-                       (const uint16_t *)B3, C, N, K, nsplit, C_split);
+                       (const uint16_t *)B3, C, N, K, nsplit, C_split, DUAL ? 0 : cpx);
     return hipGetLastError();
 }
 
