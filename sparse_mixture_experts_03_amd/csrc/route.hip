@@ -56,22 +56,59 @@ __device__ __forceinline__ uint32_t ord_f32(float f) {
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// Wave reductions on the VALU's cross-lane moves (DPP) instead of LDS
+// permutes: within each row of 16 lanes, swap neighbours (quad_perm 1,0,3,2),
+// pairs (2,3,0,1), then mirror the half-rows and the row, so that every lane
+// of a row holds the row's result; the four rows are then read with
+// readlane and combined in row order (a fixed order, so sums are
+// reproducible).  DPP control codes: quad_perm 0xB1 and 0x4E, row_half_mirror
+// 0x141, row_mirror 0x140.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+template <int CTRL>
+__device__ __forceinline__ unsigned long long dpp_u64(unsigned long long v) {
+    const int lo = __builtin_amdgcn_mov_dpp((int)(uint32_t)v, CTRL, 0xF, 0xF, false);
+    const int hi = __builtin_amdgcn_mov_dpp((int)(uint32_t)(v >> 32), CTRL, 0xF, 0xF, false);
+    return ((unsigned long long)(uint32_t)hi << 32) | (uint32_t)lo;
+}
+__device__ __forceinline__ float rows_f32(float v, int r) { return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), r)); }
+
 __device__ __forceinline__ float wave_max(float v) {
-    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-    return v;
+    v = fmaxf(v, dpp_f32<0xB1>(v));
+    v = fmaxf(v, dpp_f32<0x4E>(v));
+    v = fmaxf(v, dpp_f32<0x141>(v));
+    v = fmaxf(v, dpp_f32<0x140>(v));
+    return fmaxf(fmaxf(rows_f32(v, 0), rows_f32(v, 16)), fmaxf(rows_f32(v, 32), rows_f32(v, 48)));
 }
 
 __device__ __forceinline__ float wave_sum(float v) {
-    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-    return v;
+    v += dpp_f32<0xB1>(v);
+    v += dpp_f32<0x4E>(v);
+    v += dpp_f32<0x141>(v);
+    v += dpp_f32<0x140>(v);
+    return ((rows_f32(v, 0) + rows_f32(v, 16)) + rows_f32(v, 32)) + rows_f32(v, 48);
 }
 
 __device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long v) {
-    for (int o = 32; o > 0; o >>= 1) {
-        unsigned long long w = __shfl_xor(v, o);
-        v = w > v ? w : v;
+    unsigned long long w;
+    w = dpp_u64<0xB1>(v);
+    v = w > v ? w : v;
+    w = dpp_u64<0x4E>(v);
+    v = w > v ? w : v;
+    w = dpp_u64<0x141>(v);
+    v = w > v ? w : v;
+    w = dpp_u64<0x140>(v);
+    v = w > v ? w : v;
+    unsigned long long best = 0ull;
+#pragma unroll
+    for (int r = 0; r < 64; r += 16) {
+        const unsigned long long x = ((unsigned long long)(uint32_t)__builtin_amdgcn_readlane((int)(v >> 32), r) << 32) |
+                                     (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, r);
+        best = x > best ? x : best;
     }
-    return v;
+    return best;
 }
 
 // The per-token epilogue over a block's logits tile hl[TILE][.]
