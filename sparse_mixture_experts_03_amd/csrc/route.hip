@@ -111,6 +111,124 @@ __device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long v)
     return best;
 }
 
+// Reductions within groups of G = 8 or 16 lanes (a token per group): the
+// same DPP steps as wave_max, stopped at the group.
+template <int G>
+__device__ __forceinline__ float group_max(float v) {
+    v = fmaxf(v, dpp_f32<0xB1>(v));
+    v = fmaxf(v, dpp_f32<0x4E>(v));
+    v = fmaxf(v, dpp_f32<0x141>(v));
+    if (G == 16) v = fmaxf(v, dpp_f32<0x140>(v));
+    return v;
+}
+template <int G>
+__device__ __forceinline__ float group_sum(float v) {
+    v += dpp_f32<0xB1>(v);
+    v += dpp_f32<0x4E>(v);
+    v += dpp_f32<0x141>(v);
+    if (G == 16) v += dpp_f32<0x140>(v);
+    return v;
+}
+template <int G>
+__device__ __forceinline__ unsigned long long group_max_u64(unsigned long long v) {
+    unsigned long long w;
+    w = dpp_u64<0xB1>(v);
+    v = w > v ? w : v;
+    w = dpp_u64<0x4E>(v);
+    v = w > v ? w : v;
+    w = dpp_u64<0x141>(v);
+    v = w > v ? w : v;
+    if (G == 16) {
+        w = dpp_u64<0x140>(v);
+        v = w > v ? w : v;
+    }
+    return v;
+}
+
+// softmax_topk_block for E <= G: lane l serves expert l % G of token
+// l / G of the wave's current group of 64 / G tokens, so a wave takes 8
+// (E <= 8) or 4 (E <= 16) tokens at a time.  Same results as the one-token-
+// per-wave form (every reduction is within the token's lanes); the block
+// partials are added in (wave, token group) order.
+template <int G, int TILE, int NW>
+__device__ void softmax_topk_grouped(const float (*hl)[RT_EMAX + 1], int t0, int T, int E, int k,
+                                     int gate_switch, int32_t *__restrict__ topk_idx,
+                                     float *__restrict__ gates, float *__restrict__ part_P,
+                                     float *__restrict__ part_lse2, int *topk_sh, float *P_sh,
+                                     float *lse2_sh) {
+    constexpr int TPW = 64 / G;   // tokens per wave at a time
+    __shared__ float pwg[NW][64];
+    __shared__ float lsg[NW][TPW];
+    __shared__ int topchg[TILE];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, w = tid >> 6;
+    const int g = lane / G, e = lane % G;
+    const bool ve = e < E;
+    float psum = 0.f, lsum = 0.f;
+    for (int r0 = w * TPW; r0 < TILE; r0 += NW * TPW) {
+        if (t0 + r0 >= T) break;   // uniform in the wave
+        const int r = r0 + g, t = t0 + r;
+        const bool vt = r < TILE && t < T;
+        const bool v = ve && vt;
+        const float h = v ? hl[r][e] : -INFINITY;
+        const float m = group_max<G>(h);
+        const float x = v ? expf(h - m) : 0.f;
+        const float s = group_sum<G>(x);
+        const float inv = 1.f / s;
+        if (v) psum += x * inv;
+        const float lse = m + logf(s);
+        if (vt && e == 0) lsum += lse * lse;
+        unsigned long long key = v ? ((unsigned long long)ord_f32(h) << 32) | (0xffffffffu - (uint32_t)e) : 0ull;
+        float h_top = 0.f, den = 0.f, my_hb = 0.f;
+        int my_bi = 0;
+        for (int sl = 0; sl < k; ++sl) {
+            const unsigned long long best = group_max_u64<G>(key);
+            int bi = (int)(0xffffffffu - (uint32_t)(best & 0xffffffffull));
+            bi = bi < 0 ? 0 : bi;  // only for a token past T (its key is 0)
+            if (bi == e) key = 0ull;
+            const float hb = vt ? hl[r][bi] : 0.f;
+            if (sl == 0) {
+                h_top = hb;
+                if (vt && e == 0) topchg[r] = bi;
+            }
+            den += expf(hb - h_top);  // slot order, identical on the token's lanes
+            if (e == sl) {
+                my_hb = hb;
+                my_bi = bi;
+            }
+        }
+        if (vt && e < k) {
+            const float gt = gate_switch ? expf(my_hb - m) * inv : expf(my_hb - h_top) / den;
+            topk_idx[(int64_t)t * k + e] = my_bi;
+            if (topk_sh) topk_sh[t * k + e] = my_bi;  // LDS copy (small batches)
+            gates[(int64_t)t * k + e] = gt;
+        }
+    }
+    pwg[w][lane] = psum;
+    if (e == 0) lsg[w][g] = lsum;
+    __syncthreads();
+    if (tid < E) {
+        float a = 0.f;
+        for (int v = 0; v < NW; ++v)
+#pragma unroll
+            for (int q = 0; q < TPW; ++q) a += pwg[v][q * G + tid];
+        const int64_t nblk = gridDim.x;
+        int c = 0;
+        for (int r = 0, nr = min(TILE, T - t0); r < nr; ++r) c += topchg[r] == tid;
+        part_P[(int64_t)tid * nblk + blockIdx.x] = a;
+        part_P[(int64_t)(E + tid) * nblk + blockIdx.x] = (float)c;
+        if (P_sh) P_sh[tid] = a;
+    }
+    if (tid == 0) {
+        float a = 0.f;
+        for (int v = 0; v < NW; ++v)
+#pragma unroll
+            for (int q = 0; q < TPW; ++q) a += lsg[v][q];
+        part_lse2[blockIdx.x] = a;
+        if (lse2_sh) *lse2_sh = a;
+    }
+}
+
 // The per-token epilogue over a block's logits tile hl[TILE][.]
 // (already synchronised), NW waves, wave w taking tokens w, w + NW, ...
 // Every thread of the block must call it.  Block partials, for a grid of
@@ -123,6 +241,16 @@ __device__ void softmax_topk_block(const float (*hl)[RT_EMAX + 1], int t0, int T
                                    float *__restrict__ gates, float *__restrict__ part_P,
                                    float *__restrict__ part_lse2, int *topk_sh = nullptr,
                                    float *P_sh = nullptr, float *lse2_sh = nullptr) {
+    if (E <= 8) {
+        softmax_topk_grouped<8, TILE, NW>(hl, t0, T, E, k, gate_switch, topk_idx, gates, part_P, part_lse2,
+                                          topk_sh, P_sh, lse2_sh);
+        return;
+    }
+    if (E <= 16) {
+        softmax_topk_grouped<16, TILE, NW>(hl, t0, T, E, k, gate_switch, topk_idx, gates, part_P, part_lse2,
+                                           topk_sh, P_sh, lse2_sh);
+        return;
+    }
     __shared__ float pw[NW][RT_EMAX];
     __shared__ float lw[NW];
     __shared__ int topch[TILE];   // each token's top choice
