@@ -119,7 +119,7 @@ __global__ __launch_bounds__(DP_THREADS) void dispatch_rank_kernel(
             const unsigned long long am = __ballot(act);
             if (am == 0ull) break;
             const int leader = __ffsll((long long)am) - 1;
-            const int e0 = __shfl(ej, leader);
+            const int e0 = __builtin_amdgcn_readlane(ej, leader);  // leader is wave-uniform
             const bool m = act && ej == e0;
             const unsigned long long mm = __ballot(m);
             if (m) {
