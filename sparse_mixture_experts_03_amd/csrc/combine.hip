@@ -22,7 +22,9 @@ namespace moe {
 
 namespace {
 
-template <bool BF16, bool VEC4>
+// KC: k when it is a compile-time constant (the slot loop unrolled, so all
+// of a chunk group's loads are issued together), 0 for any k.
+template <bool BF16, bool VEC4, int KC>
 __global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ y_perm,
                                                       const float *__restrict__ part2,
                                                       const int32_t *__restrict__ row_of_slot,
@@ -45,7 +47,8 @@ __global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ 
 #pragma unroll 4
             for (int c = grp * G * 256 + lane * 4; c < cend; c += 256) {
                 float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
-                for (int s = 0; s < k; ++s) {
+#pragma unroll
+                for (int s = 0; s < (KC ? KC : k); ++s) {
                     const int r = rs[s];
                     if (r < 0) continue;
                     const float g = gs[s];
@@ -111,8 +114,15 @@ hipError_t launch_combine(const Shape &s, const float *y_perm, const float *y_pe
     int64_t blocks = (items + 3) / 4;
     if (blocks > 16384) blocks = 16384;
     const bool bf = s.dtype == 1;
-    auto kern = bf ? (v4 ? combine_kernel<true, true> : combine_kernel<true, false>)
-                   : (v4 ? combine_kernel<false, true> : combine_kernel<false, false>);
+    auto kern = bf ? (v4 ? combine_kernel<true, true, 0> : combine_kernel<true, false, 0>)
+                   : (v4 ? combine_kernel<false, true, 0> : combine_kernel<false, false, 0>);
+    if (v4) {
+        // common k: slot loop unrolled
+        if (s.k == 1) kern = bf ? combine_kernel<true, true, 1> : combine_kernel<false, true, 1>;
+        if (s.k == 2) kern = bf ? combine_kernel<true, true, 2> : combine_kernel<false, true, 2>;
+        if (s.k == 4) kern = bf ? combine_kernel<true, true, 4> : combine_kernel<false, true, 4>;
+        if (s.k == 8) kern = bf ? combine_kernel<true, true, 8> : combine_kernel<false, true, 8>;
+    }
     hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(256), 0, st, y_perm, y_perm_part2,
                        row_of_slot, gates, s.T, s.d, s.k, G, y);
     return hipGetLastError();
