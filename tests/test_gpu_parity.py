@@ -88,6 +88,13 @@ SMALL = {
     # (d = 256), Switch gate with noise and capacity drops
     "router_gemm_split": W["switch"].with_(name="router_gemm_split", T=300, d=256, d_ff=384, E=64,
                                            noise_std=1.0 / 64),
+    # router epilogue with one token per 16-lane group and 4 idle lanes in
+    # each (E = 12), top-3, no capacity limit
+    "grouped_e12": W["mixtral_prefill"].with_(name="grouped_e12", T=300, d=128, d_ff=192, E=12, k=3,
+                                              cf=0.0),
+    # k = E: every expert of every token (8-lane groups, 2 idle lanes)
+    "k_equals_e": W["mixtral_prefill"].with_(name="k_equals_e", T=200, d=64, d_ff=128, E=6, k=6,
+                                             cf=0.0),
 }
 
 
