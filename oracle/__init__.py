@@ -48,6 +48,8 @@ def _load():
     lib.orc_expert_ffn.restype = None
     lib.orc_combine.argtypes = [i64, i64, i64, dp, ip, fp, fp]
     lib.orc_combine.restype = None
+    lib.orc_combine_shared.argtypes = [i64, i64, i64, i64, dp, ip, fp, fp, fp, fp]
+    lib.orc_combine_shared.restype = None
     lib.orc_stats.argtypes = [i64, i64, i64, ip, dp, dp, dp, dp, dp, dp]
     lib.orc_stats.restype = None
     lib.orc_threads.argtypes = []
@@ -147,6 +149,25 @@ def combine(gates, rows, ys):
     return y
 
 
+def combine_shared(gates, rows, ys, ysh, res):
+    """y_t = fl32(res_t + routed slots in slot order + shared experts in order)
+    (section "Total versus active parameters": shared experts every token
+    visits; Implementation: the block adds the layer output to its hidden
+    state).  ysh [S*n][d]: shared expert j on token t is row j*n + t;
+    res [n][d] or None."""
+    gates = np.ascontiguousarray(gates, dtype=np.float64)
+    rows = np.ascontiguousarray(rows, dtype=np.int32)
+    ys, ysh, res = _f32(ys), _f32(ysh), _f32(res)
+    n, k = gates.shape
+    d = ys.shape[1] if ys.shape[0] else ysh.shape[1]
+    S = ysh.shape[0] // n if n else 0
+    assert ysh.shape == (S * n, d)
+    assert res is None or res.shape == (n, d)
+    y = np.empty((n, d), np.float32)
+    _load().orc_combine_shared(n, k, d, S, _p(gates), _p(rows), _p(ys), _p(ysh), _p(res), _p(y))
+    return y
+
+
 def stats(idx, p, lse):
     """f, P, aux = E*sum f P, z = mean lse^2 ("The load-balancing loss")."""
     idx = np.ascontiguousarray(idx, dtype=np.int32)
@@ -175,11 +196,18 @@ def route(x, Wr, k, mode, bias=None, noise=None):
     return dict(h=h, idx=idx, gates=g, p=p, lse=lse, f=f, P=P, aux=aux, z=z)
 
 
-def forward(x, Wr, W1, W3, W2, k, mode, cf, act, bias=None, noise=None, tokens=None):
+def forward(x, Wr, W1, W3, W2, k, mode, cf, act, bias=None, noise=None, tokens=None,
+            shared=None, residual=None):
     """Whole layer forward.  Routing, dispatch and statistics always cover
     every token (capacity couples tokens through their order); the expert
     FFN and the combine run for ``tokens`` only (all tokens if None), and
-    ``y`` then holds those tokens' rows in the order given."""
+    ``y`` then holds those tokens' rows in the order given.
+
+    ``shared``: None, or (Ws1, Ws3, Ws2) with S shared experts of the
+    routed experts' shape ([S][d_ff][d], [S][d_ff][d] or None, [S][d][d_ff]),
+    run on every selected token with weight 1; ``residual``: None or [T][d],
+    added to the layer output (section "Total versus active parameters";
+    Implementation's h + moe_out)."""
     x = _f32(x)
     T, d = x.shape
     E = Wr.shape[0]
@@ -194,7 +222,20 @@ def forward(x, Wr, W1, W3, W2, k, mode, cf, act, bias=None, noise=None, tokens=N
         np.zeros((0, d), np.float32)
     rows = np.full((len(sel), k), -1, np.int32)
     rows[kept] = np.arange(int(kept.sum()), dtype=np.int32)
-    y = combine(r["gates"][sel], rows, ys)
+    if shared is None and residual is None:
+        y = combine(r["gates"][sel], rows, ys)
+    else:
+        if shared is None:
+            ysh = np.zeros((0, d), np.float32)
+        else:
+            Ws1, Ws3, Ws2 = shared
+            S = np.asarray(Ws1).shape[0]
+            sh_t = np.tile(sel, S)                                  # row j*n + t'
+            sh_e = np.repeat(np.arange(S), len(sel))
+            ysh = expert_ffn(sh_t, sh_e, x, Ws1, Ws3, Ws2, act) if len(sh_t) else \
+                np.zeros((0, d), np.float32)
+        res = None if residual is None else _f32(residual)[sel]
+        y = combine_shared(r["gates"][sel], rows, ys, ysh, res)
     out = dict(r)
     out.update(disp)
     out.update(C=C, y=y, tokens=sel)

@@ -42,7 +42,11 @@
  *   - drop priority is token order within each expert, whatever the slot;
  *   - gates are not renormalised after drops;
  *   - f_i counts top (slot-0) choices before any drop;
- *   - GELU is the exact erf form.
+ *   - GELU is the exact erf form;
+ *   - shared experts (section "Total versus active parameters") have the
+ *     routed experts' shape and activation, no gate, and run on every
+ *     token, dropped ones included; the layer output then adds the block's
+ *     residual: y = res + routed + shared.
  */
 #include <math.h>
 #include <stdint.h>
@@ -332,6 +336,43 @@ void orc_combine(int64_t n, int64_t k, int64_t d, const double *gates,
                     acc += gates[t * k + s] * (double)ys[(int64_t)r * d + o];
             }
             y[t * d + o] = (float)acc;
+        }
+}
+
+/*
+ * Layer output with shared experts and the block's residual.
+ * Section "Total versus active parameters" names DeepSeek-V3's layer:
+ * many small routed experts beside shared experts that every token visits.
+ * The Implementation section's block adds the layer's output to its
+ * hidden state, h + moe_out.  "Capacity and dropped tokens": a dropped
+ * assignment skips its routed expert only; the residual still carries
+ * the token, and (reading) so do the shared experts, which no routing
+ * decision touches.  A shared expert has no gate (weight 1).
+ *   gates, rows, ys  as orc_combine (routed part)
+ *   S                shared experts
+ *   ysh  [S][n][d]   fp32: shared expert j on token t is row j*n + t
+ *   res  [n][d]      fp32 residual, or NULL for none
+ *   y    [n][d]      fp32 out:
+ *     y[t] = fl32(res[t] + (sum over kept slots, in slot order, of g ys[row]
+ *                           + sum over j, in order, of ysh[j][t]))
+ */
+void orc_combine_shared(int64_t n, int64_t k, int64_t d, int64_t S, const double *gates,
+                        const int32_t *rows, const float *ys, const float *ysh,
+                        const float *res, float *y)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < n; ++t)
+        for (int64_t o = 0; o < d; ++o) {
+            double moe_out = 0.0;
+            for (int64_t s = 0; s < k; ++s) {
+                int32_t r = rows[t * k + s];
+                if (r >= 0)
+                    moe_out += gates[t * k + s] * (double)ys[(int64_t)r * d + o];
+            }
+            for (int64_t j = 0; j < S; ++j)
+                moe_out += (double)ysh[(j * n + t) * d + o];
+            double h = res ? (double)res[t * d + o] : 0.0;
+            y[t * d + o] = (float)(h + moe_out);
         }
 }
 

@@ -30,6 +30,14 @@ MUTANTS = {
     "W2 read transposed": ("acc[u] += xd[f] * (double)w2[(o0 + u) * d_ff + f];",
                            "acc[u] += xd[f] * (double)w2[f * d + o0 + u];"),
     "combine uses the slot-0 gate for every slot": ("acc += gates[t * k + s] * (double)ys", "acc += gates[t * k] * (double)ys"),
+    "shared expert weighted by the slot-0 gate":
+        ("moe_out += (double)ysh[(j * n + t) * d + o];", "moe_out += gates[t * k] * (double)ysh[(j * n + t) * d + o];"),
+    "shared rows read token-major":
+        ("moe_out += (double)ysh[(j * n + t) * d + o];", "moe_out += (double)ysh[(t * S + j) * d + o];"),
+    "only the first shared expert": ("for (int64_t j = 0; j < S; ++j)", "for (int64_t j = 0; j < S && j < 1; ++j)"),
+    "dropped tokens skip the shared experts":
+        ("for (int64_t j = 0; j < S; ++j)", "for (int64_t j = 0; j < S && rows[t * k] >= 0; ++j)"),
+    "residual left out": ("double h = res ? (double)res[t * d + o] : 0.0;", "double h = 0.0;"),
     "f counts the last slot": ("f[idx[t * k]] += 1.0;", "f[idx[t * k + k - 1]] += 1.0;"),
     "z not squared": ("zz += lse[t] * lse[t];", "zz += lse[t];"),
     "lse drops the max shift": ("lse[t] = m + log(s);", "lse[t] = log(s);"),

@@ -335,6 +335,101 @@ def test_sampled_tokens_equal_full_forward():
     assert (part["y"] == full["y"][sel]).all()
 
 
+# ---------------------------------------------------------------- shared experts and residual
+
+def _shared(rng, S, d, d_ff, act):
+    Ws1 = (rng.standard_normal((S, d_ff, d)) / np.sqrt(d)).astype(np.float32)
+    Ws3 = (rng.standard_normal((S, d_ff, d)) / np.sqrt(d)).astype(np.float32) if act == "swiglu" else None
+    Ws2 = (rng.standard_normal((S, d, d_ff)) / np.sqrt(d_ff)).astype(np.float32)
+    return Ws1, Ws3, Ws2
+
+
+@pytest.mark.parametrize("act,cf", [("swiglu", 0.0), ("gelu", 0.3), ("relu", 0.3)])
+def test_shared_experts_are_ungated_dense_ffns(act, cf):
+    """With the routed experts' outputs zero (W2 = 0), the layer output is the
+    sum of the shared experts' dense FFNs on every token -- dropped tokens
+    included -- each with weight 1 (section "Total versus active
+    parameters": shared experts every token visits)."""
+    rng = _rng(30)
+    T, d, d_ff, E, k, S = 29, 16, 24, 4, 2, 3
+    x, Wr, W1, W3, W2 = _layer(rng, T, d, d_ff, E, act)
+    W2 = np.zeros_like(W2)
+    sh = _shared(rng, S, d, d_ff, act)
+    o = oracle.forward(x, Wr, W1, W3, W2, k, "renorm", cf, act, shared=sh)
+    ref = sum(_dense_expert64(x, sh[0], sh[1], sh[2], j, act) for j in range(S))
+    assert np.abs(o["y"] - ref).max() <= 1e-6 * np.abs(ref).max()
+    if cf > 0:
+        assert (o["row_of_slot"].max(axis=1) < 0).any()   # some token lost every slot
+
+
+def test_shared_expert_equals_routed_expert_with_gate_one():
+    """One shared expert gives, bit for bit, what the same weights give as the
+    only routed expert of an E = 1, k = 1 layer (gate exactly 1, nothing
+    dropped): a shared expert is an expert with weight 1 on every token."""
+    rng = _rng(31)
+    T, d, d_ff = 23, 24, 40
+    x, Wr, W1, W3, W2 = _layer(rng, T, d, d_ff, 3)
+    sh = _shared(rng, 1, d, d_ff, "swiglu")
+    routed = oracle.forward(x, Wr[:1], sh[0], sh[1], sh[2], 1, "renorm", 0.0, "swiglu")
+    shared = oracle.forward(x, Wr, W1, W3, np.zeros_like(W2), 2, "renorm", 0.0, "swiglu", shared=sh)
+    assert (routed["gates"] == 1.0).all()
+    assert (shared["y"] == routed["y"]).all()
+
+
+@pytest.mark.parametrize("cf", [0.0, 0.4])
+def test_shared_and_residual_match_loop_over_experts(cf):
+    """y = h + moe_out (the Implementation section's block), moe_out being the
+    page's loop over routed experts (token order, capacity cut, gated
+    index_add) plus the shared experts; a token dropped from every routed
+    expert keeps its residual and its shared experts ("Capacity and dropped
+    tokens")."""
+    rng = _rng(32)
+    T, d, d_ff, E, k, S = 40, 16, 32, 6, 2, 2
+    x, Wr, W1, W3, W2 = _layer(rng, T, d, d_ff, E)
+    sh = _shared(rng, S, d, d_ff, "swiglu")
+    res = rng.standard_normal((T, d)).astype(np.float32)
+    o = oracle.forward(x, Wr, W1, W3, W2, k, "renorm", cf, "swiglu", shared=sh, residual=res)
+    h = (x.astype(np.float64) @ Wr.astype(np.float64).T).astype(np.float32)
+    top = np.argsort(-h, axis=1, kind="stable")[:, :k]
+    gates = sps.softmax(np.take_along_axis(h, top, 1).astype(np.float64), axis=1)
+    C = None if cf == 0 else int(np.ceil(cf * T * k / E))
+    out = res.astype(np.float64)
+    for e in range(E):
+        token, slot = np.nonzero(top == e)
+        if C is not None:
+            token, slot = token[:C], slot[:C]
+        if len(token):
+            np.add.at(out, token, gates[token, slot][:, None] * _dense_expert64(x[token], W1, W3, W2, e, "swiglu"))
+    for j in range(S):
+        out += _dense_expert64(x, sh[0], sh[1], sh[2], j, "swiglu")
+    err = np.abs(o["y"] - out).max(axis=1)
+    assert (err <= 1e-6 * np.abs(out).max(axis=1)).all()
+    if cf > 0:
+        full = o["row_of_slot"].max(axis=1) < 0
+        assert full.any()
+        alone = res[full].astype(np.float64) + sum(
+            _dense_expert64(x[full], sh[0], sh[1], sh[2], j, "swiglu") for j in range(S))
+        assert np.abs(o["y"][full] - alone).max() <= 1e-6 * np.abs(alone).max()
+
+
+def test_residual_passes_exactly():
+    """With every expert weight zero the layer adds nothing: y is the residual,
+    bit for bit, also for tokens dropped by capacity."""
+    rng = _rng(33)
+    T, d, d_ff, E, k = 25, 8, 16, 3, 2
+    x, Wr, W1, W3, W2 = _layer(rng, T, d, d_ff, E)
+    sh = _shared(rng, 2, d, d_ff, "swiglu")
+    res = rng.standard_normal((T, d)).astype(np.float32)
+    o = oracle.forward(x, Wr, W1, W3, np.zeros_like(W2), k, "renorm", 0.5, "swiglu",
+                       shared=(sh[0], sh[1], np.zeros_like(sh[2])), residual=res)
+    assert (o["y"] == res).all()
+    sel = np.array([24, 3, 3])
+    part = oracle.forward(x, Wr, W1, W3, W2, k, "renorm", 0.5, "swiglu", tokens=sel, shared=sh,
+                          residual=res)
+    full = oracle.forward(x, Wr, W1, W3, W2, k, "renorm", 0.5, "swiglu", shared=sh, residual=res)
+    assert (part["y"] == full["y"][sel]).all()
+
+
 # ---------------------------------------------------------------- statistics
 
 def test_aux_is_one_when_balanced():
