@@ -21,6 +21,12 @@ the 2.5 PFLOP/s dense bf16 peak.  Decode is bound by HBM: algorithmic bytes
 per launch = the touched experts' W1 and W3 (2 * d * d_ff * 2 bytes each)
 plus the permuted activations in and H out, against 8 TB/s.
 
+Shared-expert workloads (--workload finegrained_zipf_shared or
+mixtral_prefill_shared) run moe_forward_shared: the same stages plus the
+shared experts on every token and the block residual fused into the
+combine.  Their FLOPs add S * T * 2 * n_mat * d * d_ff, and the line adds a
+"shared_stage" object: those FLOPs over the event-timed shared stage.
+
 CPU baseline: the CPU oracle (test infrastructure; fp64 sums) timed on this
 host on a bounded sample: routing, dispatch and statistics over all T
 tokens plus the expert FFN and combine on S sampled tokens; tokens/s is
@@ -46,6 +52,8 @@ METRIC = "MoE layer tokens/s + % bf16 MFMA peak (prefill) / % HBM BW (decode), M
 PEAK_BF16_TFLOPS = 2500.0
 PEAK_HBM_GBS = 8000.0
 STAGES = ("route", "route_finalize", "dispatch", "gather", "expert_up", "expert_down", "combine")
+STAGES_SHARED = ("route", "route_finalize", "dispatch", "gather", "expert_up", "expert_down",
+                 "shared", "combine")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
 GEMM_SRC = os.path.join(ROOT, "sparse_mixture_experts_03_amd", "csrc", "expert_gemm.hip")
 
@@ -122,18 +130,24 @@ def run_workload(w, steps, warmup, fresh_x_steps=0, seed=0):
     dw = {k: B.to_device(v, w.dtype) for k, v in wt.items()}
     del wt
     n_x = max(1, fresh_x_steps)
-    xs, noises = [], []
+    xs, noises, ress = [], [], []
     for s in range(n_x):
         tk = synth.make_tokens(w, seed, s)
         xs.append(B.to_device(tk["x"], w.dtype))
         noises.append(B.to_device(tk["noise"], w.dtype))
+        ress.append(B.to_device(tk["res"], w.dtype))
     log(f"[bench] {w.name}: inputs ready in {time.time() - t0:.1f}s")
 
     desc = B.desc_for(w)
-    ws = B.workspace(desc)
+    # shared experts and/or the block residual: moe_forward_shared
+    with_shared = w.n_shared > 0 or w.residual
+    stages = STAGES_SHARED if with_shared else STAGES
+    ws = B.workspace(desc, n_shared=w.n_shared if with_shared else None)
+    shs = [B.make_shared(desc, dw["Ws1"], dw["Ws3"], dw["Ws2"], ress[j]) for j in range(n_x)] \
+        if with_shared else None
     out = B.alloc_outputs(desc)
     ev = HipEvents()
-    nev = len(STAGES) + 1
+    nev = len(stages) + 1
     stream = torch.cuda.current_stream()
 
     def step(i, events=None):
@@ -147,20 +161,30 @@ def run_workload(w, steps, warmup, fresh_x_steps=0, seed=0):
         # only the two events around the expert up-projection (the dominant
         # kernel) are recorded: each recorded event separates the kernels
         # around it by a few us
-        B.moe_forward(desc, xs[j], dw["Wr"], dw["bias"], noises[j], dw["W1"], dw["W3"], dw["W2"],
-                      out["y"], ws, kept_counts=out["kept_counts"], stats=out["stats"],
-                      stream=stream)
+        if with_shared:
+            B.moe_forward_shared(desc, shs[j], xs[j], dw["Wr"], dw["bias"], noises[j], dw["W1"],
+                                 dw["W3"], dw["W2"], out["y"], ws, kept_counts=out["kept_counts"],
+                                 stats=out["stats"], stream=stream)
+        else:
+            B.moe_forward(desc, xs[j], dw["Wr"], dw["bias"], noises[j], dw["W1"], dw["W3"],
+                          dw["W2"], out["y"], ws, kept_counts=out["kept_counts"],
+                          stats=out["stats"], stream=stream)
 
     for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
-    up = STAGES.index("expert_up")
-    # the expert-up launch is timed with events on every `every`-th timed
-    # step (about ten samples): an event-timed launch is separated from its
-    # neighbours by a few us, which would otherwise be charged to every step
+    up = stages.index("expert_up")
+    keep = (up, up + 1)
+    if with_shared and w.n_shared > 0:
+        sh = stages.index("shared")
+        keep = keep + (sh, sh + 1)
+    # the expert-up launch (and the shared stage, if any) is timed with
+    # events on every `every`-th timed step (about ten samples): an
+    # event-timed launch is separated from its neighbours by a few us, which
+    # would otherwise be charged to every step
     every = max(1, steps // 10)
     sampled = list(range(0, steps, every))
-    evsets = [ev.create(nev, keep=(up, up + 1)) for _ in sampled]
+    evsets = [ev.create(nev, keep=keep) for _ in sampled]
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     for i in range(steps):
@@ -176,7 +200,7 @@ def run_workload(w, steps, warmup, fresh_x_steps=0, seed=0):
     n_kept = int(kept.sum())
     touched = int((kept > 0).sum())
     return dict(elapsed=elapsed, steps=steps, stage_ms=stage_ms.mean(0), stage_ms_all=stage_ms,
-                n_kept=n_kept, touched=touched, event_steps=len(sampled))
+                n_kept=n_kept, touched=touched, event_steps=len(sampled), stages=stages)
 
 
 def cpu_baseline(w, seed=0, target_s=22.0):
@@ -191,9 +215,16 @@ def cpu_baseline(w, seed=0, target_s=22.0):
     W1 = synth.widen(wt["W1"])
     W3 = None if wt["W3"] is None else synth.widen(wt["W3"])
     W2 = synth.widen(wt["W2"])
+    extra = {}
+    if w.n_shared > 0:
+        extra["shared"] = (synth.widen(wt["Ws1"]),
+                           None if wt["Ws3"] is None else synth.widen(wt["Ws3"]),
+                           synth.widen(wt["Ws2"]))
+    if w.residual:
+        extra["residual"] = synth.widen(tk["res"])
     t0 = time.perf_counter()
     r = oracle.forward(x, wt["Wr"], W1, W3, W2, w.k, w.gate, w.cf, w.act, wt["bias"], tk["noise"],
-                       tokens=np.zeros(0, np.int64))
+                       tokens=np.zeros(0, np.int64), **extra)
     t_route = time.perf_counter() - t0
     rng = np.random.default_rng(1)
 
@@ -201,7 +232,7 @@ def cpu_baseline(w, seed=0, target_s=22.0):
         sel = np.sort(rng.choice(w.T, size=S, replace=False))
         t1 = time.perf_counter()
         oracle.forward(x, wt["Wr"], W1, W3, W2, w.k, w.gate, w.cf, w.act, wt["bias"], tk["noise"],
-                       tokens=sel)
+                       tokens=sel, **extra)
         return time.perf_counter() - t1 - t_route  # the call re-routes every token
 
     S = 4
@@ -212,8 +243,8 @@ def cpu_baseline(w, seed=0, target_s=22.0):
     return {"value": 1.0 / per_token, "unit": "tokens/s", "cores": oracle.threads(),
             "kind": "oracle",
             "sample": (f"{w.name}: router, gate, dispatch and statistics on all {w.T} tokens "
-                       f"({t_route:.2f}s); expert FFN and combine on {S} sampled tokens "
-                       f"({t_ffn:.2f}s); fp64 sums")}
+                       f"({t_route:.2f}s); expert FFN{' (routed and shared)' if w.n_shared else ''} "
+                       f"and combine on {S} sampled tokens ({t_ffn:.2f}s); fp64 sums")}
 
 
 def main():
@@ -255,12 +286,15 @@ def main():
     tokens_s = w.T * res["steps"] / res["elapsed"]
     n_up = 2 if w.act == "swiglu" else 1
     n_mat = n_up + 1
-    flops_step = 2.0 * w.T * w.E * w.d + res["n_kept"] * 2.0 * n_mat * w.d * w.d_ff
-    up = STAGES.index("expert_up")
+    # active-parameter FLOPs: router, kept routed rows, and every token on
+    # each shared expert
+    shared_flops = w.n_shared * w.T * 2.0 * n_mat * w.d * w.d_ff
+    flops_step = 2.0 * w.T * w.E * w.d + res["n_kept"] * 2.0 * n_mat * w.d * w.d_ff + shared_flops
+    up = res["stages"].index("expert_up")
     up_ms = float(res["stage_ms"][up])
     up_flops = res["n_kept"] * 2.0 * n_up * w.d * w.d_ff
     achieved = up_flops / (up_ms * 1e-3) / 1e12
-    stages = {n: round(float(v), 4) for n, v in zip(STAGES, res["stage_ms"]) if np.isfinite(v)}
+    stages = {n: round(float(v), 4) for n, v in zip(res["stages"], res["stage_ms"]) if np.isfinite(v)}
     log(f"[bench] {w.name}: {ms_step:.3f} ms/step, stages(ms) {stages}")
     line = {
         "metric": METRIC, "value": round(tokens_s, 1), "unit": "tokens/s", "n_gpus": 1,
@@ -269,7 +303,9 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "T": w.T, "d": w.d, "d_ff": w.d_ff, "E": w.E, "k": w.k,
                    "gate": w.gate, "act": w.act, "capacity_factor": w.cf, "router": "fp32",
-                   "parallelism": "single_gpu"},
+                   "parallelism": "single_gpu",
+                   **({"n_shared": w.n_shared, "residual": w.residual}
+                      if (w.n_shared or w.residual) else {})},
         "tflops_per_step": round(flops_step / (ms_step * 1e-3) / 1e12, 2),
         "stage_ms": stages,
         "roofline": {"bound": "mfma", "kernel": "expert_up (grouped GEMM, SwiGLU epilogue)",
@@ -279,6 +315,15 @@ def main():
                      "algorithmic_per_launch": up_flops, "mean_launch_ms": round(up_ms, 4),
                      "event_timed_launches": res["event_steps"]},
     }
+    if w.n_shared > 0:
+        # the shared stage: the row map, then the shared experts' up and
+        # down projections (dense GEMMs of all T tokens), against the MFMA peak
+        sh_ms = float(res["stage_ms"][res["stages"].index("shared")])
+        sh_tf = shared_flops / (sh_ms * 1e-3) / 1e12
+        line["shared_stage"] = {"bound": "mfma", "achieved": round(sh_tf, 2),
+                                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                                "frac": round(sh_tf / PEAK_BF16_TFLOPS, 4),
+                                "algorithmic_per_stage": shared_flops, "mean_stage_ms": round(sh_ms, 4)}
     if not args.no_decode and w.name == "mixtral_prefill":
         wd = synth.WORKLOADS["mixtral_decode"]
         rd = run_workload(wd, args.decode_steps, 10, fresh_x_steps=args.decode_steps)

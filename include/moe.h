@@ -221,6 +221,98 @@ int moe_forward(const moe_desc *desc, const void *x, const float *W_r, const flo
                 int32_t *offsets, int32_t *row_of_slot, int32_t *token_of_row,
                 uint8_t *dropped, float *stats, void *ws, size_t ws_bytes, void *stream);
 
+/* ---- shared experts and the block residual --------------------------------
+ *
+ * Section "Total versus active parameters" of the page names DeepSeek-V3's
+ * layer: many small routed experts beside shared experts that every token
+ * visits.  The Implementation section's block adds the layer output to its
+ * hidden state (h + moe_out).  Here a shared expert has the routed experts'
+ * shape and activation, no gate (weight 1), and runs on every token,
+ * including tokens that capacity dropped from every routed expert ("Capacity
+ * and dropped tokens": such a token keeps its residual; no routing decision
+ * touches a shared expert).  The layer output becomes
+ *   y[t] = residual[t] + ( sum over kept slots, in slot order, of
+ *                          gates[t][s] * y_perm[row_of_slot[t][s]]
+ *                        + y_shared[t] )
+ *   y_shared[t] = sum over j = 0..S-1 of E^shared_j(x[t])
+ * summed in fp32 in that order (routed slots, shared experts, residual) and
+ * stored once in the act dtype.
+ *
+ * All S shared experts see every token, so they run as one dense layer:
+ * the up projection against their W1 (and W3) read as [S*d_ff][d], and the
+ * down projection with K = S*d_ff, whose fp32 accumulation sums the S
+ * experts (in expert order within each K block).  y_shared is that sum;
+ * each expert's own output is not formed.
+ *
+ * Shapes (S shared experts):
+ *   W1, W3      [S][d_ff][d]  act dtype   up projections (W3 only for SwiGLU)
+ *   W2          [S][d][d_ff]  act dtype   down projection
+ *   residual    [T][d]        act dtype   optional (NULL = none)
+ *   y_shared    [T][d]        fp32        summed output of the shared experts
+ */
+
+/* Shared experts per layer: at most this many. */
+#define MOE_MAX_SHARED 16
+
+/* Kernel stages of moe_forward_shared: those of moe_forward with "shared"
+ * (the shared experts' two matrix multiplies) between expert-down and
+ * combine. */
+#define MOE_FORWARD_SHARED_STAGES 8
+
+typedef struct moe_shared {
+    int32_t n_shared;     /* S, 0 <= S <= MOE_MAX_SHARED                    */
+    const void *W1;       /* [S][d_ff][d]; required when S > 0              */
+    const void *W3;       /* [S][d_ff][d]; SwiGLU only (then required)      */
+    const void *W2;       /* [S][d][d_ff]; required when S > 0              */
+    const void *residual; /* [T][d] or NULL                                 */
+} moe_shared;
+
+/*
+ * Workspace bytes for the entry points below with this description and
+ * S = shared->n_shared shared experts (at least moe_workspace_size(); for
+ * S > 1 it holds a copy of the shared W2 laid out [d][S*d_ff]).  Same
+ * validation and return codes as moe_workspace_size; an S outside
+ * [0, MOE_MAX_SHARED] is MOE_ERR_INVALID_ARG, S*d_ff >= 2^31
+ * MOE_ERR_UNSUPPORTED.  Only n_shared is read.  Host only.
+ */
+int moe_workspace_size_shared(const moe_desc *desc, const moe_shared *shared, size_t *bytes);
+
+/*
+ * The shared experts on every token: y_shared[t] = sum over j of
+ * E^shared_j(x[t]), E^shared_j being the expert of moe_expert_ffn on
+ * shared->W1/W3/W2[j] (H in the act dtype in the workspace, fp32
+ * accumulation; a K split of the down projection is added back before the
+ * call returns).  shared->residual is ignored.  S = 0 enqueues nothing.
+ * ws: moe_workspace_size_shared() bytes.
+ */
+int moe_shared_ffn(const moe_desc *desc, const moe_shared *shared, const void *x,
+                   float *y_shared, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * The combine of moe_combine plus the shared experts' summed output and
+ * the residual, fused in one pass (the equation above).  y_shared and
+ * residual may each be NULL (that term is absent); with both NULL the
+ * result equals moe_combine's bit for bit.
+ */
+int moe_combine_shared(const moe_desc *desc, const float *y_perm, const int32_t *row_of_slot,
+                       const float *gates, const float *y_shared, const void *residual, void *y,
+                       void *stream);
+
+/*
+ * The whole layer with shared experts and the residual: moe_forward's
+ * stages, then the shared experts on every token (moe_shared_ffn, with
+ * y_shared in the workspace), then the fused combine (moe_combine_shared).
+ * Arguments as moe_forward, plus `shared` (required; S = 0 and no residual
+ * give moe_forward's results bit for bit).  ws: moe_workspace_size_shared()
+ * bytes.  Stage events, when given, follow MOE_FORWARD_SHARED_STAGES.
+ */
+int moe_forward_shared(const moe_desc *desc, const moe_shared *shared, const void *x,
+                       const float *W_r, const float *bias, const float *noise, const void *W1,
+                       const void *W3, const void *W2, void *y, int32_t *topk_idx, float *gates,
+                       int32_t *routed_counts, int32_t *kept_counts, int32_t *offsets,
+                       int32_t *row_of_slot, int32_t *token_of_row, uint8_t *dropped,
+                       float *stats, void *ws, size_t ws_bytes, void *stream);
+
 /* A static, human-readable name for a status code. */
 const char *moe_status_string(int status);
 

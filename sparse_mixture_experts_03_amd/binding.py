@@ -7,7 +7,9 @@ the layer runs in the library's HIP kernels; there is no fallback path, and
 loading fails loudly when the library cannot be found or built.
 
 Names match the ABI: moe_workspace_size, moe_capacity, moe_route,
-moe_dispatch, moe_expert_ffn, moe_combine, moe_forward.
+moe_dispatch, moe_expert_ffn, moe_combine, moe_forward, and for shared
+experts plus the block residual moe_workspace_size_shared, moe_shared_ffn,
+moe_combine_shared, moe_forward_shared.
 """
 from __future__ import annotations
 
@@ -25,6 +27,10 @@ DTYPE = {"f32": 0, "bf16": 1}
 TORCH_DTYPE = {"f32": torch.float32, "bf16": torch.bfloat16}
 FORWARD_STAGES = 7
 STAGE_NAMES = ("route", "route_finalize", "dispatch", "gather", "expert_up", "expert_down", "combine")
+FORWARD_SHARED_STAGES = 8
+STAGE_NAMES_SHARED = ("route", "route_finalize", "dispatch", "gather", "expert_up", "expert_down",
+                      "shared", "combine")
+MAX_SHARED = 16
 
 MOE_OK = 0
 STATUS = {0: "MOE_OK", -1: "MOE_ERR_INVALID_ARG", -2: "MOE_ERR_UNSUPPORTED", -3: "MOE_ERR_HIP",
@@ -44,6 +50,11 @@ class MoeDesc(ctypes.Structure):
                 ("capacity_factor", ctypes.c_double),
                 ("stage_events", ctypes.POINTER(ctypes.c_void_p)),
                 ("n_stage_events", ctypes.c_int32)]
+
+
+class MoeShared(ctypes.Structure):
+    _fields_ = [("n_shared", ctypes.c_int32), ("W1", ctypes.c_void_p), ("W3", ctypes.c_void_p),
+                ("W2", ctypes.c_void_p), ("residual", ctypes.c_void_p)]
 
 
 def make_desc(T, d, d_ff, E, k, gate="renorm", act="swiglu", dtype="bf16", cf=0.0) -> MoeDesc:
@@ -80,10 +91,17 @@ def load(build_if_missing: bool = True):
     lib.moe_expert_ffn.argtypes = [D, P, P, P, P, P, P, P, sz, P]
     lib.moe_combine.argtypes = [D, P, P, P, P, P]
     lib.moe_forward.argtypes = [D, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, sz, P]
+    SH = ctypes.POINTER(MoeShared)
+    lib.moe_workspace_size_shared.argtypes = [D, SH, ctypes.POINTER(ctypes.c_size_t)]
+    lib.moe_shared_ffn.argtypes = [D, SH, P, P, P, sz, P]
+    lib.moe_combine_shared.argtypes = [D, P, P, P, P, P, P, P]
+    lib.moe_forward_shared.argtypes = [D, SH, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P,
+                                       sz, P]
     lib.moe_status_string.argtypes = [ctypes.c_int]
     lib.moe_status_string.restype = ctypes.c_char_p
     for fn in ("moe_workspace_size", "moe_capacity", "moe_route", "moe_dispatch",
-               "moe_expert_ffn", "moe_combine", "moe_forward"):
+               "moe_expert_ffn", "moe_combine", "moe_forward", "moe_workspace_size_shared",
+               "moe_shared_ffn", "moe_combine_shared", "moe_forward_shared"):
         getattr(lib, fn).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -133,8 +151,30 @@ def moe_capacity(desc: MoeDesc):
     return None if c.value < 0 else c.value
 
 
-def workspace(desc: MoeDesc, device="cuda") -> torch.Tensor:
-    return torch.empty(max(moe_workspace_size(desc), 1), dtype=torch.uint8, device=device)
+def workspace(desc: MoeDesc, device="cuda", n_shared=None) -> torch.Tensor:
+    """Workspace for desc (n_shared given: for the shared-expert entry points)."""
+    n = moe_workspace_size(desc) if n_shared is None else \
+        moe_workspace_size_shared(desc, MoeShared(int(n_shared), None, None, None, None))
+    return torch.empty(max(n, 1), dtype=torch.uint8, device=device)
+
+
+def make_shared(desc, Ws1=None, Ws3=None, Ws2=None, residual=None) -> MoeShared:
+    """A moe_shared over device tensors (S = Ws1.shape[0], or 0 without Ws1);
+    the tensors must outlive every call that is given the result."""
+    T, d, d_ff = desc.T, desc.d, desc.d_ff
+    dt = _act_dtype(desc)
+    S = 0 if Ws1 is None else int(Ws1.shape[0])
+    return MoeShared(S, _ptr(Ws1, dt, (S, d_ff, d), "Ws1", True),
+                     _ptr(Ws3, dt, (S, d_ff, d), "Ws3", True),
+                     _ptr(Ws2, dt, (S, d, d_ff), "Ws2", S == 0),
+                     _ptr(residual, dt, (T, d), "residual", True))
+
+
+def moe_workspace_size_shared(desc: MoeDesc, shared: MoeShared) -> int:
+    n = ctypes.c_size_t(0)
+    _check("moe_workspace_size_shared",
+           load().moe_workspace_size_shared(ctypes.byref(desc), ctypes.byref(shared), ctypes.byref(n)))
+    return n.value
 
 
 def moe_route(desc, x, W_r, bias, noise, topk_idx, gates, stats, ws, stream=None):
@@ -210,6 +250,53 @@ def moe_forward(desc, x, W_r, bias, noise, W1, W3, W2, y, ws, topk_idx=None, gat
         _ptr(stats, torch.float32, (2 * E + 2,), "stats", True),
         _ptr(ws, torch.uint8, None, "ws"), ws.numel(), _stream(stream))
     _check("moe_forward", rc)
+
+
+def moe_shared_ffn(desc, shared: MoeShared, x, y_shared, ws, stream=None):
+    T, d, S = desc.T, desc.d, shared.n_shared
+    rc = load().moe_shared_ffn(
+        ctypes.byref(desc), ctypes.byref(shared), _ptr(x, _act_dtype(desc), (T, d), "x"),
+        _ptr(y_shared, torch.float32, (T, d), "y_shared", S == 0), _ptr(ws, torch.uint8, None, "ws"),
+        ws.numel(), _stream(stream))
+    _check("moe_shared_ffn", rc)
+
+
+def moe_combine_shared(desc, y_perm, row_of_slot, gates, y_shared, residual, y, stream=None):
+    T, d, k = desc.T, desc.d, desc.k
+    dt = _act_dtype(desc)
+    rc = load().moe_combine_shared(
+        ctypes.byref(desc), _ptr(y_perm, torch.float32, (T * k, d), "y_perm"),
+        _ptr(row_of_slot, torch.int32, (T, k), "row_of_slot"),
+        _ptr(gates, torch.float32, (T, k), "gates"),
+        _ptr(y_shared, torch.float32, (T, d), "y_shared", True),
+        _ptr(residual, dt, (T, d), "residual", True), _ptr(y, dt, (T, d), "y"), _stream(stream))
+    _check("moe_combine_shared", rc)
+
+
+def moe_forward_shared(desc, shared: MoeShared, x, W_r, bias, noise, W1, W3, W2, y, ws,
+                       topk_idx=None, gates=None, routed_counts=None, kept_counts=None,
+                       offsets=None, row_of_slot=None, token_of_row=None, dropped=None,
+                       stats=None, stream=None):
+    T, d, d_ff, E, k = desc.T, desc.d, desc.d_ff, desc.E, desc.k
+    dt = _act_dtype(desc)
+    rc = load().moe_forward_shared(
+        ctypes.byref(desc), ctypes.byref(shared), _ptr(x, dt, (T, d), "x"),
+        _ptr(W_r, torch.float32, (E, d), "W_r"),
+        _ptr(bias, torch.float32, (E,), "bias", True),
+        _ptr(noise, torch.float32, (T, E), "noise", True),
+        _ptr(W1, dt, (E, d_ff, d), "W1"), _ptr(W3, dt, (E, d_ff, d), "W3", True),
+        _ptr(W2, dt, (E, d, d_ff), "W2"), _ptr(y, dt, (T, d), "y"),
+        _ptr(topk_idx, torch.int32, (T, k), "topk_idx", True),
+        _ptr(gates, torch.float32, (T, k), "gates", True),
+        _ptr(routed_counts, torch.int32, (E,), "routed_counts", True),
+        _ptr(kept_counts, torch.int32, (E,), "kept_counts", True),
+        _ptr(offsets, torch.int32, (E + 1,), "offsets", True),
+        _ptr(row_of_slot, torch.int32, (T, k), "row_of_slot", True),
+        _ptr(token_of_row, torch.int32, (T * k,), "token_of_row", True),
+        _ptr(dropped, torch.uint8, (T, k), "dropped", True),
+        _ptr(stats, torch.float32, (2 * E + 2,), "stats", True),
+        _ptr(ws, torch.uint8, None, "ws"), ws.numel(), _stream(stream))
+    _check("moe_forward_shared", rc)
 
 
 def status_string(code: int) -> str:

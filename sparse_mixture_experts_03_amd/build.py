@@ -15,7 +15,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmoe.so")
-SOURCES = ["moe_api.cpp", "route.hip", "dispatch.hip", "expert_gemm.hip", "combine.hip"]
+SOURCES = ["moe_api.cpp", "route.hip", "dispatch.hip", "expert_gemm.hip", "combine.hip",
+           "shared.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",

@@ -11,6 +11,13 @@
 // When the down projection split K in two, the two partial rows are added
 // (first half + second half) before the gate multiplies them.
 //
+// With shared experts and the block residual (section "Total versus active
+// parameters": shared experts every token visits; Implementation: the block
+// adds the layer output to its hidden state), the same pass then adds the
+// token's row of the shared experts' summed output (its two K halves first,
+// when split) and the residual last, before the single rounding to the act
+// dtype.
+//
 // combine_kernel: one wave per (token, group of 256-column chunks),
 // grid-stride; each lane owns 4 consecutive columns of a chunk and sums the
 // k slots in slot order in fp32, then stores fp32 or bf16 (a scalar
@@ -22,14 +29,31 @@ namespace moe {
 
 namespace {
 
+// Shared experts' summed output and the residual (SH kernels only).
+struct SharedIn {
+    const float *ysh;   // [T][d] fp32, or nullptr
+    const float *ysh2;  // second K half of ysh, or nullptr
+    const void *res;    // [T][d] in the act dtype, or nullptr
+};
+
+__device__ __forceinline__ float4 add4(float4 a, float4 b) {
+    a.x += b.x;
+    a.y += b.y;
+    a.z += b.z;
+    a.w += b.w;
+    return a;
+}
+
 // KC: k when it is a compile-time constant (the slot loop unrolled, so all
-// of a chunk group's loads are issued together), 0 for any k.
-template <bool BF16, bool VEC4, int KC>
+// of a chunk group's loads are issued together), 0 for any k.  SH: add the
+// shared experts and the residual after the routed slots.
+template <bool BF16, bool VEC4, int KC, bool SH>
 __global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ y_perm,
                                                       const float *__restrict__ part2,
                                                       const int32_t *__restrict__ row_of_slot,
                                                       const float *__restrict__ gates, int T,
-                                                      int d, int k, int G, void *__restrict__ y) {
+                                                      int d, int k, int G, SharedIn sh,
+                                                      void *__restrict__ y) {
     const int lane = threadIdx.x & 63;
     if (VEC4) {
         // one wave per (token, group of G 256-column chunks): the token's k
@@ -65,6 +89,25 @@ __global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ 
                     a.z = fmaf(g, v.z, a.z);
                     a.w = fmaf(g, v.w, a.w);
                 }
+                if (SH) {
+                    const int64_t o = (int64_t)t * d + c;
+                    if (sh.ysh) {
+                        float4 v = *(const float4 *)(sh.ysh + o);
+                        if (sh.ysh2) v = add4(v, *(const float4 *)(sh.ysh2 + o));
+                        a = add4(a, v);
+                    }
+                    if (sh.res) {
+                        if (BF16) {
+                            const uint2 r = *(const uint2 *)((const uint16_t *)sh.res + o);
+                            a.x += bf16_to_f32((uint16_t)(r.x & 0xffffu));
+                            a.y += bf16_to_f32((uint16_t)(r.x >> 16));
+                            a.z += bf16_to_f32((uint16_t)(r.y & 0xffffu));
+                            a.w += bf16_to_f32((uint16_t)(r.y >> 16));
+                        } else {
+                            a = add4(a, *(const float4 *)((const float *)sh.res + o));
+                        }
+                    }
+                }
                 if (BF16) {
                     uint2 o;
                     o.x = (uint32_t)f32_to_bf16(a.x) | ((uint32_t)f32_to_bf16(a.y) << 16);
@@ -90,6 +133,16 @@ __global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ 
                     if (part2) v += part2[(int64_t)r * d + c];
                     a = fmaf(gs[s], v, a);
                 }
+                if (SH) {
+                    const int64_t o = (int64_t)t * d + c;
+                    if (sh.ysh) {
+                        float v = sh.ysh[o];
+                        if (sh.ysh2) v += sh.ysh2[o];
+                        a += v;
+                    }
+                    if (sh.res)
+                        a += BF16 ? bf16_to_f32(((const uint16_t *)sh.res)[o]) : ((const float *)sh.res)[o];
+                }
                 if (BF16)
                     ((uint16_t *)y)[(int64_t)t * d + c] = f32_to_bf16(a);
                 else
@@ -101,9 +154,12 @@ __global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ 
 
 }  // namespace
 
-hipError_t launch_combine(const Shape &s, const float *y_perm, const float *y_perm_part2,
-                          const int32_t *row_of_slot, const float *gates, void *y,
-                          hipStream_t st) {
+namespace {
+
+template <bool SH>
+hipError_t combine_any(const Shape &s, const float *y_perm, const float *y_perm_part2,
+                       const int32_t *row_of_slot, const float *gates, const SharedIn &sh, void *y,
+                       hipStream_t st) {
     const bool v4 = (s.d % 4) == 0;
     // chunks per wave: whole rows when there are many tokens, single
     // 256-column chunks when there are few (so that enough waves run)
@@ -114,18 +170,37 @@ hipError_t launch_combine(const Shape &s, const float *y_perm, const float *y_pe
     int64_t blocks = (items + 3) / 4;
     if (blocks > 16384) blocks = 16384;
     const bool bf = s.dtype == 1;
-    auto kern = bf ? (v4 ? combine_kernel<true, true, 0> : combine_kernel<true, false, 0>)
-                   : (v4 ? combine_kernel<false, true, 0> : combine_kernel<false, false, 0>);
+    auto kern = bf ? (v4 ? combine_kernel<true, true, 0, SH> : combine_kernel<true, false, 0, SH>)
+                   : (v4 ? combine_kernel<false, true, 0, SH> : combine_kernel<false, false, 0, SH>);
     if (v4) {
         // common k: slot loop unrolled
-        if (s.k == 1) kern = bf ? combine_kernel<true, true, 1> : combine_kernel<false, true, 1>;
-        if (s.k == 2) kern = bf ? combine_kernel<true, true, 2> : combine_kernel<false, true, 2>;
-        if (s.k == 4) kern = bf ? combine_kernel<true, true, 4> : combine_kernel<false, true, 4>;
-        if (s.k == 8) kern = bf ? combine_kernel<true, true, 8> : combine_kernel<false, true, 8>;
+        if (s.k == 1) kern = bf ? combine_kernel<true, true, 1, SH> : combine_kernel<false, true, 1, SH>;
+        if (s.k == 2) kern = bf ? combine_kernel<true, true, 2, SH> : combine_kernel<false, true, 2, SH>;
+        if (s.k == 4) kern = bf ? combine_kernel<true, true, 4, SH> : combine_kernel<false, true, 4, SH>;
+        if (s.k == 8) kern = bf ? combine_kernel<true, true, 8, SH> : combine_kernel<false, true, 8, SH>;
     }
     hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(256), 0, st, y_perm, y_perm_part2,
-                       row_of_slot, gates, s.T, s.d, s.k, G, y);
+                       row_of_slot, gates, s.T, s.d, s.k, G, sh, y);
     return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_combine(const Shape &s, const float *y_perm, const float *y_perm_part2,
+                          const int32_t *row_of_slot, const float *gates, void *y,
+                          hipStream_t st) {
+    return combine_any<false>(s, y_perm, y_perm_part2, row_of_slot, gates,
+                              SharedIn{nullptr, nullptr, nullptr}, y, st);
+}
+
+hipError_t launch_combine_shared(const Shape &s, const float *y_perm, const float *y_perm_part2,
+                                 const int32_t *row_of_slot, const float *gates, const float *y_sh,
+                                 const float *y_sh_part2, const void *residual, void *y,
+                                 hipStream_t st) {
+    if (y_sh == nullptr && residual == nullptr)
+        return launch_combine(s, y_perm, y_perm_part2, row_of_slot, gates, y, st);
+    return combine_any<true>(s, y_perm, y_perm_part2, row_of_slot, gates,
+                             SharedIn{y_sh, y_sh_part2, residual}, y, st);
 }
 
 }  // namespace moe

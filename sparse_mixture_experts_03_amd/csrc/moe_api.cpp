@@ -60,10 +60,15 @@ struct Layout {
     size_t row_of_slot, token_of_row, dropped, stats;
     size_t x_perm, H, y_perm;
     size_t y_perm2;  // second K half of a split down projection (0: no split)
+    // shared experts (all 0 when there are none)
+    size_t sh_offsets;  // {0, T}: their single row group
+    size_t w2cat;       // W2 of S > 1 experts as [d][S*d_ff] (0: S <= 1)
+    size_t H_sh, y_sh;  // H_sh [T][S*d_ff] act dtype; y_sh [T][d] fp32 (summed over experts)
+    size_t y_sh2;       // second K half of their down projection (0: no split)
     size_t total;
 };
 
-Layout layout(const Shape &s) {
+Layout layout(const Shape &s, int S = 0) {
     Layout L{};
     const size_t elem = s.dtype == MOE_DTYPE_BF16 ? 2 : 4;
     const size_t Tk = (size_t)s.Tk();
@@ -98,6 +103,15 @@ Layout layout(const Shape &s) {
     L.H = take(rows * (size_t)s.d_ff * elem);
     L.y_perm = take(rows * (size_t)s.d * 4);
     L.y_perm2 = moe::down_ksplit(s) == 2 ? take(rows * (size_t)s.d * 4) : 0;
+    if (S > 0) {
+        const Shape q = moe::shared_shape(s, S);
+        const size_t T = (size_t)s.T;
+        L.sh_offsets = take(2 * 4);
+        L.w2cat = S > 1 ? take(moe::shared_w2cat_bytes(s, S)) : 0;
+        L.H_sh = take(T * (size_t)q.d_ff * elem);
+        L.y_sh = take(T * (size_t)s.d * 4);
+        L.y_sh2 = moe::down_ksplit(q) == 2 ? take(T * (size_t)s.d * 4) : 0;
+    }
     L.total = o;
     return L;
 }
@@ -107,9 +121,24 @@ T *at(void *ws, size_t off) {
     return reinterpret_cast<T *>(static_cast<char *>(ws) + off);
 }
 
-int check_ws(const Shape &s, const void *ws, size_t ws_bytes) {
+int check_ws(const Shape &s, const void *ws, size_t ws_bytes, int S = 0) {
     if (!ws) return MOE_ERR_INVALID_ARG;
-    if (ws_bytes < layout(s).total) return MOE_ERR_WORKSPACE;
+    if (ws_bytes < layout(s, S).total) return MOE_ERR_WORKSPACE;
+    return MOE_OK;
+}
+
+// Validates the shared-expert description against the layer's: S in range,
+// weights present when S > 0 (W3 exactly for SwiGLU), and the stacked
+// hidden width S*d_ff within int32.
+int check_shared(const Shape &s, const moe_shared *sh) {
+    if (!sh) return MOE_ERR_INVALID_ARG;
+    const int S = sh->n_shared;
+    if (S < 0 || S > MOE_MAX_SHARED) return MOE_ERR_INVALID_ARG;
+    if (S > 0) {
+        if (!sh->W1 || !sh->W2) return MOE_ERR_INVALID_ARG;
+        if ((s.act == MOE_ACT_SWIGLU) != (sh->W3 != nullptr)) return MOE_ERR_INVALID_ARG;
+        if ((int64_t)S * s.d_ff >= ((int64_t)1 << 31)) return MOE_ERR_UNSUPPORTED;
+    }
     return MOE_OK;
 }
 
@@ -120,6 +149,24 @@ int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
         int rc_ = hip_status(expr);              \
         if (rc_ != MOE_OK) return rc_;           \
     } while (0)
+
+// The shared experts on every token as one dense layer through the routed
+// experts' GEMM kernels (one row group of T rows): up against the S
+// experts' stacked W1/W3 into H_sh [T][S*d_ff], then down with K = S*d_ff
+// into y_sh, the experts' summed output (and y_sh2, the second K half, when
+// the down projection splits K).
+int run_shared_ffn(const Shape &s, const moe_shared *sh, const void *x, float *y_sh, float *y_sh2,
+                   void *ws, const Layout &L, hipStream_t st) {
+    const int S = sh->n_shared;
+    const Shape q = moe::shared_shape(s, S);
+    int32_t *offs = at<int32_t>(ws, L.sh_offsets);
+    void *w2cat = L.w2cat ? at<char>(ws, L.w2cat) : nullptr;
+    void *H = at<char>(ws, L.H_sh);
+    MOE_TRY(moe::launch_shared_prep(s, S, sh->W2, w2cat, offs, st));
+    MOE_TRY(moe::launch_expert_up(q, x, nullptr, offs, sh->W1, sh->W3, H, st));
+    MOE_TRY(moe::launch_expert_down(q, H, offs, w2cat ? w2cat : sh->W2, y_sh, y_sh2, st));
+    return MOE_OK;
+}
 
 }  // namespace
 
@@ -249,18 +296,28 @@ int moe_combine(const moe_desc *desc, const float *y_perm, const int32_t *row_of
     return MOE_OK;
 }
 
-int moe_forward(const moe_desc *desc, const void *x, const float *W_r, const float *bias,
-                const float *noise, const void *W1, const void *W3, const void *W2, void *y,
-                int32_t *topk_idx, float *gates, int32_t *routed_counts, int32_t *kept_counts,
-                int32_t *offsets, int32_t *row_of_slot, int32_t *token_of_row,
-                uint8_t *dropped, float *stats, void *ws, size_t ws_bytes, void *stream) {
+}  // extern "C"
+
+namespace {
+
+// moe_forward and moe_forward_shared: sh == nullptr is moe_forward (seven
+// stages); otherwise the shared experts run as their own stage between
+// expert-down and the combine, which adds them and the residual.
+int forward_impl(const moe_desc *desc, const moe_shared *sh, const void *x, const float *W_r,
+                 const float *bias, const float *noise, const void *W1, const void *W3,
+                 const void *W2, void *y, int32_t *topk_idx, float *gates,
+                 int32_t *routed_counts, int32_t *kept_counts, int32_t *offsets,
+                 int32_t *row_of_slot, int32_t *token_of_row, uint8_t *dropped, float *stats,
+                 void *ws, size_t ws_bytes, void *stream) {
     Shape s;
     int rc = check_desc(desc, &s);
     if (rc != MOE_OK) return rc;
     if (!x || !W_r || !W1 || !W2 || !y) return MOE_ERR_INVALID_ARG;
     if ((s.act == MOE_ACT_SWIGLU) != (W3 != nullptr)) return MOE_ERR_INVALID_ARG;
-    if ((rc = check_ws(s, ws, ws_bytes)) != MOE_OK) return rc;
-    const Layout L = layout(s);
+    if (sh && (rc = check_shared(s, sh)) != MOE_OK) return rc;
+    const int S = sh ? sh->n_shared : 0;
+    if ((rc = check_ws(s, ws, ws_bytes, S)) != MOE_OK) return rc;
+    const Layout L = layout(s, S);
     if (!topk_idx) topk_idx = at<int32_t>(ws, L.topk_idx);
     if (!gates) gates = at<float>(ws, L.gates);
     if (!routed_counts) routed_counts = at<int32_t>(ws, L.routed);
@@ -311,9 +368,91 @@ int moe_forward(const moe_desc *desc, const void *x, const float *W_r, const flo
     float *part2 = L.y_perm2 ? at<float>(ws, L.y_perm2) : nullptr;
     MOE_TRY(moe::launch_expert_down(s, H, offsets, W2, y_perm, part2, st));
     MOE_TRY(ev.record(st));
-    MOE_TRY(moe::launch_combine(s, y_perm, part2, row_of_slot, gates, y, st));
+    if (!sh) {
+        MOE_TRY(moe::launch_combine(s, y_perm, part2, row_of_slot, gates, y, st));
+        MOE_TRY(ev.record(st));
+        return MOE_OK;
+    }
+    float *y_sh = nullptr, *y_sh2 = nullptr;
+    if (S > 0) {
+        y_sh = at<float>(ws, L.y_sh);
+        y_sh2 = L.y_sh2 ? at<float>(ws, L.y_sh2) : nullptr;
+        if ((rc = run_shared_ffn(s, sh, x, y_sh, y_sh2, ws, L, st)) != MOE_OK) return rc;
+    }
+    MOE_TRY(ev.record(st));
+    MOE_TRY(moe::launch_combine_shared(s, y_perm, part2, row_of_slot, gates, y_sh, y_sh2,
+                                       sh->residual, y, st));
     MOE_TRY(ev.record(st));
     return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_forward(const moe_desc *desc, const void *x, const float *W_r, const float *bias,
+                const float *noise, const void *W1, const void *W3, const void *W2, void *y,
+                int32_t *topk_idx, float *gates, int32_t *routed_counts, int32_t *kept_counts,
+                int32_t *offsets, int32_t *row_of_slot, int32_t *token_of_row,
+                uint8_t *dropped, float *stats, void *ws, size_t ws_bytes, void *stream) {
+    return forward_impl(desc, nullptr, x, W_r, bias, noise, W1, W3, W2, y, topk_idx, gates,
+                        routed_counts, kept_counts, offsets, row_of_slot, token_of_row, dropped,
+                        stats, ws, ws_bytes, stream);
+}
+
+int moe_workspace_size_shared(const moe_desc *desc, const moe_shared *shared, size_t *bytes) {
+    Shape s;
+    int rc = check_desc(desc, &s);
+    if (rc != MOE_OK) return rc;
+    if (!bytes || !shared) return MOE_ERR_INVALID_ARG;
+    if (shared->n_shared < 0 || shared->n_shared > MOE_MAX_SHARED) return MOE_ERR_INVALID_ARG;
+    if ((int64_t)shared->n_shared * s.d_ff >= ((int64_t)1 << 31)) return MOE_ERR_UNSUPPORTED;
+    *bytes = layout(s, shared->n_shared).total;
+    return MOE_OK;
+}
+
+int moe_shared_ffn(const moe_desc *desc, const moe_shared *shared, const void *x,
+                   float *y_shared, void *ws, size_t ws_bytes, void *stream) {
+    Shape s;
+    int rc = check_desc(desc, &s);
+    if (rc != MOE_OK) return rc;
+    if ((rc = check_shared(s, shared)) != MOE_OK) return rc;
+    const int S = shared->n_shared;
+    if (S > 0 && (!x || !y_shared)) return MOE_ERR_INVALID_ARG;
+    if ((rc = check_ws(s, ws, ws_bytes, S)) != MOE_OK) return rc;
+    if (S == 0) return MOE_OK;
+    const Layout L = layout(s, S);
+    hipStream_t st = (hipStream_t)stream;
+    float *y_sh2 = L.y_sh2 ? at<float>(ws, L.y_sh2) : nullptr;
+    if ((rc = run_shared_ffn(s, shared, x, y_shared, y_sh2, ws, L, st)) != MOE_OK) return rc;
+    if (y_sh2)
+        MOE_TRY(moe::launch_add_partial(moe::shared_shape(s, S), y_shared, y_sh2,
+                                        at<int32_t>(ws, L.sh_offsets), st));
+    return MOE_OK;
+}
+
+int moe_combine_shared(const moe_desc *desc, const float *y_perm, const int32_t *row_of_slot,
+                       const float *gates, const float *y_shared, const void *residual, void *y,
+                       void *stream) {
+    Shape s;
+    int rc = check_desc(desc, &s);
+    if (rc != MOE_OK) return rc;
+    if (!y_perm || !row_of_slot || !gates || !y) return MOE_ERR_INVALID_ARG;
+    MOE_TRY(moe::launch_combine_shared(s, y_perm, nullptr, row_of_slot, gates, y_shared, nullptr,
+                                       residual, y, (hipStream_t)stream));
+    return MOE_OK;
+}
+
+int moe_forward_shared(const moe_desc *desc, const moe_shared *shared, const void *x,
+                       const float *W_r, const float *bias, const float *noise, const void *W1,
+                       const void *W3, const void *W2, void *y, int32_t *topk_idx, float *gates,
+                       int32_t *routed_counts, int32_t *kept_counts, int32_t *offsets,
+                       int32_t *row_of_slot, int32_t *token_of_row, uint8_t *dropped,
+                       float *stats, void *ws, size_t ws_bytes, void *stream) {
+    if (!shared) return MOE_ERR_INVALID_ARG;
+    return forward_impl(desc, shared, x, W_r, bias, noise, W1, W3, W2, y, topk_idx, gates,
+                        routed_counts, kept_counts, offsets, row_of_slot, token_of_row, dropped,
+                        stats, ws, ws_bytes, stream);
 }
 
 const char *moe_status_string(int status) {

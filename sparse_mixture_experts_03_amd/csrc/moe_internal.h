@@ -107,6 +107,27 @@ hipError_t launch_dispatch(const Shape &s, const int32_t *topk_idx, int32_t *rou
 hipError_t launch_gather(const Shape &s, const void *x, const int32_t *token_of_row,
                          const int32_t *offsets, void *x_perm, hipStream_t st);
 
+// Shared experts (every token, no gate), all S of them as one dense layer:
+// the up projection is one row group of T rows against the S experts' W1
+// (and W3) stacked as [S*d_ff][d] (their native layout), so H_sh is
+// [T][S*d_ff] with expert j at columns j*d_ff; the down projection is one
+// GEMM with K = S*d_ff against W2 repacked as [d][S*d_ff] (expert j's
+// columns at j*d_ff), which sums the S experts' outputs in its fp32
+// accumulation, in expert order.  shared_shape() is that layer's shape.
+inline Shape shared_shape(const Shape &s, int S) {
+    Shape q = s;
+    q.E = 1;
+    q.k = 1;
+    q.C = -1;
+    q.d_ff = S * s.d_ff;
+    return q;
+}
+// Row offsets {0, T} of the single row group; for S > 1 also the W2
+// repack W2cat[o][j*d_ff + f] = W2s[j][o][f] (act dtype).
+size_t shared_w2cat_bytes(const Shape &s, int S);
+hipError_t launch_shared_prep(const Shape &s, int S, const void *W2s, void *W2cat,
+                              int32_t *offsets, hipStream_t st);
+
 // ---- expert FFN: grouped GEMMs over ragged per-expert row blocks --------
 // a_rows: row r of A is A[a_rows[r]] (the gather done by the loads);
 // nullptr: row r is A[r].
@@ -129,6 +150,14 @@ hipError_t launch_add_partial(const Shape &s, float *y_perm, const float *part2,
 hipError_t launch_combine(const Shape &s, const float *y_perm, const float *y_perm_part2,
                           const int32_t *row_of_slot, const float *gates, void *y,
                           hipStream_t st);
+
+// Combine plus the shared experts' summed row (y_sh [T][d] fp32, or
+// nullptr; y_sh_part2 its second K half, or nullptr) and the residual (act
+// dtype, or nullptr), added in that order after the routed slots.
+hipError_t launch_combine_shared(const Shape &s, const float *y_perm, const float *y_perm_part2,
+                                 const int32_t *row_of_slot, const float *gates, const float *y_sh,
+                                 const float *y_sh_part2, const void *residual, void *y,
+                                 hipStream_t st);
 
 }  // namespace moe
 

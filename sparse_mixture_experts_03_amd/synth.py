@@ -19,7 +19,11 @@ on; the distributions are stated per tensor):
   * logit noise [T][E] fp32 ~ N(0, std noise_std) where the workload asks
     for it (the Switch-style layer: std 1/E);
   * router bias [E] fp32 for the Zipf workload: b_i = 2 ln w_{i+1}, with
-    w_r = r^-s / sum_{j=1..E} j^-s (s = 1.1), expert i at rank i+1.
+    w_r = r^-s / sum_{j=1..E} j^-s (s = 1.1), expert i at rank i+1;
+  * shared experts (workloads with n_shared > 0): Ws1, Ws3 [S][d_ff][d],
+    Ws2 [S][d][d_ff], drawn and stored like the routed experts' weights;
+  * block residual h [T][d] (workloads with residual): N(0, 1), stored
+    like x, not normalised.
 A row that has to be drawn again (rejection of near-tied logits is done by
 the caller) comes from the stream (seed, name, step, row, attempt).
 
@@ -52,6 +56,8 @@ class Workload:
     noise_std: float = 0.0
     zipf_s: float = 0.0  # > 0: Zipf router bias
     steps: int = 1       # decode: fresh x per step
+    n_shared: int = 0    # shared experts every token visits
+    residual: bool = False  # block residual added to the layer output
 
     def with_(self, **kw) -> "Workload":
         return replace(self, **kw)
@@ -73,6 +79,16 @@ WORKLOADS = {
     # Fine-grained, Zipf-skewed routing: T=16384, d=2048, d_ff=768, E=128, top-4, cf=1.0.
     "finegrained_zipf": Workload("finegrained_zipf", 16384, 2048, 768, 128, 4, "renorm", 1.0,
                                  "swiglu", "bf16", zipf_s=1.1),
+    # Shared-expert variants (section "Total versus active parameters": many
+    # small routed experts plus shared experts every token visits), with the
+    # block residual: the fine-grained layer with two shared experts of its
+    # own expert shape, and the Mixtral-shape prefill layer with one.
+    "finegrained_zipf_shared": Workload("finegrained_zipf_shared", 16384, 2048, 768, 128, 4,
+                                        "renorm", 1.0, "swiglu", "bf16", zipf_s=1.1,
+                                        n_shared=2, residual=True),
+    "mixtral_prefill_shared": Workload("mixtral_prefill_shared", 4096, 4096, 14336, 8, 2,
+                                       "renorm", 0.0, "swiglu", "bf16", x_rmsnorm=True,
+                                       n_shared=1, residual=True),
 }
 
 
@@ -136,10 +152,17 @@ def make_weights(w: Workload, seed: int = 0, experts: int | None = None) -> dict
         out[name][e] = _store(w, _normal(_stream(seed, name, e), shape, std))
 
     jobs = [(n, s, sd, e) for (n, s, sd) in names for e in range(E)]
+    S = w.n_shared
+    if S > 0:
+        for name, shape, std in names:
+            out["Ws" + name[1:]] = np.empty((S,) + shape, sdt)
+        jobs += [("Ws" + n[1:], s, sd, j) for (n, s, sd) in names for j in range(S)]
     with ThreadPoolExecutor(_workers()) as ex:
         list(ex.map(one, jobs))
     if "W3" not in out:
         out["W3"] = None
+    for name in ("Ws1", "Ws3", "Ws2"):
+        out.setdefault(name, None)
     return out
 
 
@@ -157,7 +180,8 @@ def make_tokens(w: Workload, seed: int = 0, step: int = 0) -> dict:
     noise = None
     if w.noise_std > 0:
         noise = _normal(_stream(seed, "noise", step), (w.T, w.E), w.noise_std)
-    return {"x": x, "noise": noise}
+    res = _store(w, _normal(_stream(seed, "res", step), (w.T, w.d), 1.0)) if w.residual else None
+    return {"x": x, "noise": noise, "res": res}
 
 
 def redraw_token(w: Workload, seed: int, step: int, t: int, attempt: int):

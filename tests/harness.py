@@ -31,12 +31,30 @@ def prepare(w, seed=0, step=0, margin=1e-4, weights=None, ignore=()):
     return wt, tk
 
 
+def _wid(a):
+    return None if a is None else synth.widen(a)
+
+
+def has_shared(w):
+    return w.n_shared > 0 or w.residual
+
+
 def reference(w, wt, tk, tokens=None):
-    """The oracle's forward on the exact fp32 values of the inputs."""
+    """The oracle's forward on the exact fp32 values of the inputs (with the
+    shared experts and the residual when the workload has them)."""
+    shared = None
+    if w.n_shared > 0:
+        shared = (synth.widen(wt["Ws1"]), _wid(wt["Ws3"]), synth.widen(wt["Ws2"]))
     return oracle.forward(
-        synth.widen(tk["x"]), wt["Wr"], synth.widen(wt["W1"]),
-        None if wt["W3"] is None else synth.widen(wt["W3"]), synth.widen(wt["W2"]),
-        w.k, w.gate, w.cf, w.act, wt["bias"], tk["noise"], tokens=tokens)
+        synth.widen(tk["x"]), wt["Wr"], synth.widen(wt["W1"]), _wid(wt["W3"]),
+        synth.widen(wt["W2"]), w.k, w.gate, w.cf, w.act, wt["bias"], tk["noise"], tokens=tokens,
+        shared=shared, residual=_wid(tk.get("res")) if w.residual else None)
+
+
+def shared_arg(w, desc, dw, dt):
+    """moe_shared for the workload's shared experts and residual."""
+    return B.make_shared(desc, dw.get("Ws1"), dw.get("Ws3"), dw.get("Ws2"),
+                         dt.get("res") if w.residual else None)
 
 
 def device_weights(w, wt):
@@ -47,25 +65,34 @@ def device_tokens(w, tk):
     return {k: B.to_device(v, w.dtype) for k, v in tk.items()}
 
 
-def run_forward(w, dw, dt, desc=None, stream=None):
+def run_forward(w, dw, dt, desc=None, stream=None, force_shared=False):
+    """moe_forward, or moe_forward_shared when the workload has shared
+    experts or a residual (or force_shared)."""
     desc = B.desc_for(w) if desc is None else desc
     out = B.alloc_outputs(desc)
-    ws = B.workspace(desc)
-    B.moe_forward(desc, dt["x"], dw["Wr"], dw["bias"], dt["noise"], dw["W1"], dw["W3"], dw["W2"],
-                  out["y"], ws, topk_idx=out["topk_idx"], gates=out["gates"],
-                  routed_counts=out["routed_counts"], kept_counts=out["kept_counts"],
-                  offsets=out["offsets"], row_of_slot=out["row_of_slot"],
-                  token_of_row=out["token_of_row"], dropped=out["dropped"], stats=out["stats"],
-                  stream=stream)
+    kw = dict(topk_idx=out["topk_idx"], gates=out["gates"], routed_counts=out["routed_counts"],
+              kept_counts=out["kept_counts"], offsets=out["offsets"],
+              row_of_slot=out["row_of_slot"], token_of_row=out["token_of_row"],
+              dropped=out["dropped"], stats=out["stats"], stream=stream)
+    if has_shared(w) or force_shared:
+        ws = B.workspace(desc, n_shared=w.n_shared)
+        B.moe_forward_shared(desc, shared_arg(w, desc, dw, dt), dt["x"], dw["Wr"], dw["bias"],
+                             dt["noise"], dw["W1"], dw["W3"], dw["W2"], out["y"], ws, **kw)
+    else:
+        ws = B.workspace(desc)
+        B.moe_forward(desc, dt["x"], dw["Wr"], dw["bias"], dt["noise"], dw["W1"], dw["W3"],
+                      dw["W2"], out["y"], ws, **kw)
     torch.cuda.synchronize()
     return {k: v.cpu() for k, v in out.items()}
 
 
 def run_staged(w, dw, dt):
-    """route -> dispatch -> expert_ffn -> combine through the four entry points."""
+    """route -> dispatch -> expert_ffn -> combine through the four entry
+    points (with shared experts or a residual: shared_ffn after expert_ffn,
+    and combine_shared in place of combine)."""
     desc = B.desc_for(w)
     out = B.alloc_outputs(desc)
-    ws = B.workspace(desc)
+    ws = B.workspace(desc, n_shared=w.n_shared if has_shared(w) else None)
     dtype = B.TORCH_DTYPE[w.dtype]
     x_perm = torch.empty((w.T * w.k, w.d), dtype=dtype, device="cuda")
     y_perm = torch.empty((w.T * w.k, w.d), dtype=torch.float32, device="cuda")
@@ -75,11 +102,21 @@ def run_staged(w, dw, dt):
                    out["offsets"], out["row_of_slot"], out["token_of_row"], out["dropped"], x_perm,
                    ws)
     B.moe_expert_ffn(desc, x_perm, out["offsets"], dw["W1"], dw["W3"], dw["W2"], y_perm, ws)
-    B.moe_combine(desc, y_perm, out["row_of_slot"], out["gates"], out["y"])
+    y_sh = None
+    if has_shared(w):
+        y_sh = torch.empty((w.T, w.d), dtype=torch.float32, device="cuda") if w.n_shared else None
+        sh = shared_arg(w, desc, dw, dt)
+        B.moe_shared_ffn(desc, sh, dt["x"], y_sh, ws)
+        B.moe_combine_shared(desc, y_perm, out["row_of_slot"], out["gates"], y_sh,
+                             dt.get("res") if w.residual else None, out["y"])
+    else:
+        B.moe_combine(desc, y_perm, out["row_of_slot"], out["gates"], out["y"])
     torch.cuda.synchronize()
     res = {k: v.cpu() for k, v in out.items()}
     res["x_perm"] = x_perm.cpu()
     res["y_perm"] = y_perm.cpu()
+    if y_sh is not None:
+        res["y_shared"] = y_sh.cpu()
     return res
 
 

@@ -114,3 +114,56 @@ def test_workspace_grows_with_problem():
     assert a > b > 0
     # x_perm + H + y_perm at T*k = 8192 rows dominate
     assert a >= 8192 * (4096 * 2 + 14336 * 2 + 4096 * 4)
+
+
+# ---- shared experts and the block residual ------------------------------------
+
+def _sh(S, W1=FAKE, W3=FAKE, W2=FAKE, res=None):
+    return B.MoeShared(S, W1, W3, W2, res)
+
+
+def test_shared_workspace_sizes():
+    desc = B.make_desc(4096, 4096, 14336, 8, 2)
+    base = B.moe_workspace_size(desc)
+    assert B.moe_workspace_size_shared(desc, _sh(0)) == base
+    one = B.moe_workspace_size_shared(desc, _sh(1))
+    two = B.moe_workspace_size_shared(desc, _sh(2))
+    # H_sh [T][S*d_ff] bf16 and the summed fp32 output [T][d]; S > 1 adds
+    # the repacked W2 [d][S*d_ff]
+    assert one - base >= 4096 * (14336 * 2 + 4096 * 4)
+    assert two - one >= 4096 * 14336 * 2 + 2 * 4096 * 14336 * 2
+    for S in (-1, B.MAX_SHARED + 1):
+        with pytest.raises(B.MoeError) as ei:
+            B.moe_workspace_size_shared(desc, _sh(S))
+        assert ei.value.code == -1
+
+
+def test_shared_validation_before_launch():
+    lib = B.load()
+    desc = B.make_desc(64, 32, 64, 4, 2, act="swiglu", dtype="f32")
+    d = ctypes.byref(desc)
+    need = B.moe_workspace_size_shared(desc, _sh(2))
+    routed = [FAKE, FAKE, None, None, FAKE, FAKE, FAKE, FAKE]   # x, W_r, bias, noise, W1, W3, W2, y
+    outs = [None] * 9
+
+    def fwd(sh, ws_bytes=need):
+        return lib.moe_forward_shared(d, None if sh is None else ctypes.byref(sh), *routed, *outs,
+                                      FAKE, ws_bytes, None)
+
+    assert fwd(None) == -1                         # the shared description is required
+    assert fwd(_sh(2, W1=None)) == -1              # S > 0 needs W1 and W2
+    assert fwd(_sh(2, W2=None)) == -1
+    assert fwd(_sh(2, W3=None)) == -1              # SwiGLU shared experts need W3
+    assert fwd(_sh(B.MAX_SHARED + 1)) == -1
+    assert fwd(_sh(2), need - 1) == -4
+    relu = B.make_desc(64, 32, 64, 4, 2, act="relu", dtype="f32")
+    sh = _sh(1)                                    # W3 given to a non-SwiGLU layer
+    assert lib.moe_shared_ffn(ctypes.byref(relu), ctypes.byref(sh), FAKE, FAKE, FAKE, need,
+                              None) == -1
+    assert lib.moe_shared_ffn(d, ctypes.byref(_sh(2)), None, FAKE, FAKE, need, None) == -1
+    assert lib.moe_shared_ffn(d, ctypes.byref(_sh(2)), FAKE, FAKE, FAKE, need - 1, None) == -4
+    # combine: y_perm, row_of_slot, gates and y are required
+    for i in (0, 1, 2, 5):
+        a = [FAKE, FAKE, FAKE, None, None, FAKE]
+        a[i] = None
+        assert lib.moe_combine_shared(d, *a, None) == -1
