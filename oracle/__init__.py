@@ -44,7 +44,7 @@ def _load():
     lib.orc_capacity.restype = i64
     lib.orc_dispatch.argtypes = [i64, i64, i64, i64, ip, ip, ip, ip, ip, ip, ip]
     lib.orc_dispatch.restype = None
-    lib.orc_expert_ffn.argtypes = [i64, ip, ip, i64, i64, ctypes.c_int, fp, fp, fp, fp, fp]
+    lib.orc_expert_ffn.argtypes = [i64, ip, ip, i64, i64, ctypes.c_int, fp, fp, fp, fp, fp, fp, fp, fp]
     lib.orc_expert_ffn.restype = None
     lib.orc_combine.argtypes = [i64, i64, i64, dp, ip, fp, fp]
     lib.orc_combine.restype = None
@@ -52,6 +52,14 @@ def _load():
     lib.orc_combine_shared.restype = None
     lib.orc_stats.argtypes = [i64, i64, i64, ip, dp, dp, dp, dp, dp, dp]
     lib.orc_stats.restype = None
+    lib.orc_e4m3_value.argtypes = [ctypes.c_uint8]
+    lib.orc_e4m3_value.restype = ctypes.c_double
+    lib.orc_e4m3_encode.argtypes = [ctypes.c_float]
+    lib.orc_e4m3_encode.restype = ctypes.c_uint8
+    lib.orc_quantize_e4m3.argtypes = [i64, i64, fp, ip, fp]
+    lib.orc_quantize_e4m3.restype = None
+    lib.orc_e4m3_decode.argtypes = [i64, ip, fp]
+    lib.orc_e4m3_decode.restype = None
     lib.orc_threads.argtypes = []
     lib.orc_threads.restype = ctypes.c_int
     _lib = lib
@@ -117,9 +125,11 @@ def dispatch(idx, E, C):
     return out
 
 
-def expert_ffn(tok, ex, x, W1, W3, W2, act):
+def expert_ffn(tok, ex, x, W1, W3, W2, act, scales=None):
     """E_e(x_t) for each (t, e) pair ("Implementation": SwiGLU expert; ReLU/GELU
-    experts d -> d_ff -> d).  Weights: W1, W3 [E][d_ff][d], W2 [E][d][d_ff]."""
+    experts d -> d_ff -> d).  Weights: W1, W3 [E][d_ff][d], W2 [E][d][d_ff].
+    ``scales``: None, or per-row scales (S1 [E][d_ff], S3 [E][d_ff] or None,
+    S2 [E][d]) of row-scaled weights (weight row = scale * stored row)."""
     tok = np.ascontiguousarray(tok, dtype=np.int32)
     ex = np.ascontiguousarray(ex, dtype=np.int32)
     x, W1, W2 = _f32(x), _f32(W1), _f32(W2)
@@ -130,9 +140,14 @@ def expert_ffn(tok, ex, x, W1, W3, W2, act):
     d = x.shape[1]
     d_ff = W1.shape[1]
     assert W1.shape[2] == d and W2.shape[1:] == (d, d_ff)
+    S1 = S3 = S2 = None
+    if scales is not None:
+        S1, S3, S2 = (_f32(a) for a in scales)
+        assert S1.shape == W1.shape[:2] and S2.shape == W2.shape[:2]
+        assert S3 is None or S3.shape == W1.shape[:2]
     out = np.empty((n, d), np.float32)
     _load().orc_expert_ffn(n, _p(tok), _p(ex), d, d_ff, _ACT[act], _p(x), _p(W1),
-                           _p(W3), _p(W2), _p(out))
+                           _p(W3), _p(W2), _p(S1), _p(S3), _p(S2), _p(out))
     return out
 
 
@@ -168,6 +183,41 @@ def combine_shared(gates, rows, ys, ysh, res):
     return y
 
 
+def e4m3_value(code):
+    """Value of one e4m3 code (OCP 8-bit floating point, E4M3; NaN for 0x7F, 0xFF)."""
+    return float(_load().orc_e4m3_value(int(code)))
+
+
+def e4m3_encode(v):
+    """Nearest e4m3 codes (ties to even mantissa, saturating at 448) of fp32 values."""
+    v = np.ascontiguousarray(v, dtype=np.float32)
+    lib = _load()
+    return np.array([lib.orc_e4m3_encode(float(a)) for a in v.ravel()], np.uint8).reshape(v.shape)
+
+
+def e4m3_decode(q):
+    """fp32 values of e4m3 codes."""
+    q = np.ascontiguousarray(q, dtype=np.uint8)
+    out = np.empty(q.shape, np.float32)
+    _load().orc_e4m3_decode(q.size, _p(q), _p(out))
+    return out
+
+
+def quantize_e4m3(W):
+    """Row-wise post-training quantisation of W [..., cols] (fp32): codes q
+    (uint8, same shape) and scales s [...] with W ~= s[..., None] * value(q)
+    (the model quantization entry of the inference-optimization glossary
+    page "Mixture of Experts (MoE)": post-training quantisation of a trained
+    model's weights)."""
+    W = _f32(W)
+    cols = W.shape[-1]
+    rows = W.size // cols
+    q = np.empty(W.shape, np.uint8)
+    s = np.empty(W.shape[:-1], np.float32)
+    _load().orc_quantize_e4m3(rows, cols, _p(W), _p(q), _p(s))
+    return q, s
+
+
 def stats(idx, p, lse):
     """f, P, aux = E*sum f P, z = mean lse^2 ("The load-balancing loss")."""
     idx = np.ascontiguousarray(idx, dtype=np.int32)
@@ -197,7 +247,7 @@ def route(x, Wr, k, mode, bias=None, noise=None):
 
 
 def forward(x, Wr, W1, W3, W2, k, mode, cf, act, bias=None, noise=None, tokens=None,
-            shared=None, residual=None):
+            shared=None, residual=None, scales=None):
     """Whole layer forward.  Routing, dispatch and statistics always cover
     every token (capacity couples tokens through their order); the expert
     FFN and the combine run for ``tokens`` only (all tokens if None), and
@@ -207,7 +257,8 @@ def forward(x, Wr, W1, W3, W2, k, mode, cf, act, bias=None, noise=None, tokens=N
     routed experts' shape ([S][d_ff][d], [S][d_ff][d] or None, [S][d][d_ff]),
     run on every selected token with weight 1; ``residual``: None or [T][d],
     added to the layer output (section "Total versus active parameters";
-    Implementation's h + moe_out)."""
+    Implementation's h + moe_out).  ``scales``: None, or the per-row scales
+    (S1, S3, S2) of row-scaled routed expert weights (see expert_ffn)."""
     x = _f32(x)
     T, d = x.shape
     E = Wr.shape[0]
@@ -218,7 +269,7 @@ def forward(x, Wr, W1, W3, W2, k, mode, cf, act, bias=None, noise=None, tokens=N
     kept = disp["row_of_slot"][sel] >= 0                       # [n, k]
     pair_t = np.repeat(sel, k).reshape(len(sel), k)[kept]
     pair_e = r["idx"][sel][kept]
-    ys = expert_ffn(pair_t, pair_e, x, W1, W3, W2, act) if len(pair_t) else \
+    ys = expert_ffn(pair_t, pair_e, x, W1, W3, W2, act, scales) if len(pair_t) else \
         np.zeros((0, d), np.float32)
     rows = np.full((len(sel), k), -1, np.int32)
     rows[kept] = np.arange(int(kept.sum()), dtype=np.int32)

@@ -257,11 +257,18 @@ static double orc_act(int act, double a1, double a3)
  *   x        [T][d]         fp32
  *   W1, W3   [E][d_ff][d]   fp32 (W3 only for SwiGLU, else may be NULL)
  *   W2       [E][d][d_ff]   fp32
+ *   S1, S3   [E][d_ff]      fp32 per-row weight scales, or NULL (scale 1)
+ *   S2       [E][d]         fp32 per-row weight scales, or NULL
  *   out      [n][d]         fp32: out[r] = fl32(W2_e fl32(act(W1_e x, W3_e x)))
+ * With scales, weight row i of a matrix is scale[i] times its stored row
+ * (a row-scaled quantised matrix, orc_quantize_e4m3): each row's product
+ * with the input is summed from the stored values and multiplied by the
+ * scale once, in double, which equals the product with the scaled row.
  */
 void orc_expert_ffn(int64_t n, const int32_t *tok, const int32_t *ex,
                     int64_t d, int64_t d_ff, int act, const float *x,
                     const float *W1, const float *W3, const float *W2,
+                    const float *S1, const float *S3, const float *S2,
                     float *out)
 {
 #pragma omp parallel for schedule(dynamic, 1)
@@ -291,6 +298,12 @@ void orc_expert_ffn(int64_t n, const int32_t *tok, const int32_t *ex,
                 for (int64_t j = 0; j < d; ++j)
                     for (int64_t u = 0; u < nb; ++u)
                         a3[u] += xd[j] * (double)w3[(f0 + u) * d + j];
+            if (S1)
+                for (int64_t u = 0; u < nb; ++u)
+                    a1[u] *= (double)S1[e * d_ff + f0 + u];
+            if (w3 && S3)
+                for (int64_t u = 0; u < nb; ++u)
+                    a3[u] *= (double)S3[e * d_ff + f0 + u];
             for (int64_t u = 0; u < nb; ++u)
                 H[f0 + u] = (float)orc_act(act, a1[u], a3[u]);
         }
@@ -304,7 +317,7 @@ void orc_expert_ffn(int64_t n, const int32_t *tok, const int32_t *ex,
                 for (int64_t u = 0; u < nb; ++u)
                     acc[u] += xd[f] * (double)w2[(o0 + u) * d_ff + f];
             for (int64_t u = 0; u < nb; ++u)
-                out[r * d + o0 + u] = (float)acc[u];
+                out[r * d + o0 + u] = (float)(S2 ? acc[u] * (double)S2[e * d + o0 + u] : acc[u]);
         }
         free(H);
         free(xd);
@@ -407,6 +420,97 @@ void orc_stats(int64_t T, int64_t E, int64_t k, const int32_t *idx,
         zz += lse[t] * lse[t];
     *aux = (double)E * a;
     *z = zz / (double)T;
+}
+
+/*
+ * 8-bit floating point E4M3 as the Open Compute Project's 8-bit floating
+ * point specification (OFP8) defines it: a sign bit, 4 exponent bits with
+ * bias 7 and 3 mantissa bits; exponent field 0 holds the subnormals
+ * m/8 * 2^-6; the code with every exponent and mantissa bit set (0x7F,
+ * 0xFF) is NaN, and there are no infinities, so the largest finite value
+ * is 1.75 * 2^8 = 448.  The page "Mixture of experts" (rayaq.ca) finds
+ * decoding limited by reading expert weights (Mechanics, "Total versus
+ * active parameters") and names quantisation as a help to serving
+ * ("Tradeoffs"); the glossary page "Mixture of Experts (MoE)" (inferensys.com,
+ * inference optimization), in its entry on model quantization, describes
+ * post-training quantisation of a trained model's weights to 8 bits.  The
+ * format, the per-row scale and the rounding are readings: 8-bit weights in
+ * the e4m3 format that gfx950's conversion units implement.
+ */
+double orc_e4m3_value(uint8_t c)
+{
+    const int sgn = c >> 7, ex = (c >> 3) & 15, m = c & 7;
+    if (ex == 15 && m == 7)
+        return NAN;
+    const double mag = ex == 0 ? ldexp(m / 8.0, -6) : ldexp(1.0 + m / 8.0, ex - 7);
+    return sgn ? -mag : mag;
+}
+
+/*
+ * The e4m3 code nearest to v (round to nearest, a tie to the code whose
+ * mantissa is even); magnitudes beyond 448 give 448.  The sign of v (also
+ * of a zero or of a value that rounds to zero) is kept.  Finite v only.
+ * Positive codes 0x00..0x7E increase with their value, so the nearest one
+ * is the last code not above |v| or the code after it.
+ */
+uint8_t orc_e4m3_encode(float v)
+{
+    const double a = fabs((double)v);
+    const uint8_t sgn = signbit(v) ? 0x80 : 0x00;
+    int lo = 0;
+    for (int c = 1; c <= 0x7E; ++c)
+        if (orc_e4m3_value((uint8_t)c) <= a)
+            lo = c;
+    int best = lo;
+    if (lo < 0x7E) {
+        const double dl = a - orc_e4m3_value((uint8_t)lo);
+        const double dh = orc_e4m3_value((uint8_t)(lo + 1)) - a;
+        if (dh < dl || (dh == dl && ((lo + 1) & 1) == 0))
+            best = lo + 1;
+    }
+    return (uint8_t)(sgn | best);
+}
+
+/*
+ * Post-training quantisation of a matrix, row by row (the model
+ * quantization entry of the inference-optimization glossary page: reduced
+ * precision weights, applied directly to a trained model): for each row i
+ * of W [rows][cols],
+ *   amax = max_j |W[i][j]|,  s[i] = fl32(amax / 448)  (1 if that is 0),
+ *   q[i][j] = e4m3(clamp(fl32(W[i][j] / s[i]), -448, 448)),
+ * every division a single fp32 division, so that the largest magnitude of
+ * the row lands on +-448.  Row i of the matrix is then s[i] times the values
+ * of its codes.
+ */
+void orc_quantize_e4m3(int64_t rows, int64_t cols, const float *W, uint8_t *q, float *s)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < rows; ++i) {
+        const float *w = W + i * cols;
+        float amax = 0.0f;
+        for (int64_t j = 0; j < cols; ++j)
+            if (fabsf(w[j]) > amax)
+                amax = fabsf(w[j]);
+        float si = amax / 448.0f;
+        if (si == 0.0f)
+            si = 1.0f;
+        s[i] = si;
+        for (int64_t j = 0; j < cols; ++j) {
+            float v = w[j] / si;
+            if (v > 448.0f)
+                v = 448.0f;
+            if (v < -448.0f)
+                v = -448.0f;
+            q[i * cols + j] = orc_e4m3_encode(v);
+        }
+    }
+}
+
+/* The values of n e4m3 codes, as fp32 (every finite code is exact in fp32). */
+void orc_e4m3_decode(int64_t n, const uint8_t *q, float *out)
+{
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = (float)orc_e4m3_value(q[i]);
 }
 
 #ifdef _OPENMP

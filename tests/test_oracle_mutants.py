@@ -38,6 +38,11 @@ MUTANTS = {
     "dropped tokens skip the shared experts":
         ("for (int64_t j = 0; j < S; ++j)", "for (int64_t j = 0; j < S && rows[t * k] >= 0; ++j)"),
     "residual left out": ("double h = res ? (double)res[t * d + o] : 0.0;", "double h = 0.0;"),
+    "e4m3 ties away from zero": ("(dh == dl && ((lo + 1) & 1) == 0)", "(dh == dl)"),
+    "e4m3 subnormals one binade low": ("ldexp(m / 8.0, -6)", "ldexp(m / 8.0, -7)"),
+    "e4m3 scale from 447": ("float si = amax / 448.0f;", "float si = amax / 447.0f;"),
+    "up scale of W1 applied from W3's rows": ("a1[u] *= (double)S1[e * d_ff + f0 + u];", "a1[u] *= (double)S3[e * d_ff + f0 + u];"),
+    "down scale of the block's first row for every row": ("acc[u] * (double)S2[e * d + o0 + u]", "acc[u] * (double)S2[e * d + o0]"),
     "f counts the last slot": ("f[idx[t * k]] += 1.0;", "f[idx[t * k + k - 1]] += 1.0;"),
     "z not squared": ("zz += lse[t] * lse[t];", "zz += lse[t];"),
     "lse drops the max shift": ("lse[t] = m + log(s);", "lse[t] = log(s);"),

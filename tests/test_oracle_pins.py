@@ -430,6 +430,116 @@ def test_residual_passes_exactly():
     assert (part["y"] == full["y"][sel]).all()
 
 
+# ---------------------------------------------------------------- e4m3 weights
+
+import torch  # noqa: E402  (the library routine for OCP e4m3: torch.float8_e4m3fn)
+
+
+def _torch_e4m3_value(codes):
+    return torch.from_numpy(np.ascontiguousarray(codes, np.uint8)).view(torch.float8_e4m3fn).float().numpy()
+
+
+def _torch_e4m3_encode(v):
+    return torch.from_numpy(np.ascontiguousarray(v, np.float32)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def test_e4m3_values_match_library():
+    """Every code's value equals torch's float8_e4m3fn (the OCP E4M3 format);
+    closed forms: 0x38 = 1, 0x7E = 448 (largest), 0x08 = 2^-6 (smallest
+    normal), 0x01 = 2^-9 (smallest subnormal), 0x7F and 0xFF are NaN."""
+    codes = np.arange(256, dtype=np.uint8)
+    ours = oracle.e4m3_decode(codes)
+    ref = _torch_e4m3_value(codes)
+    fin = np.isfinite(ref)
+    assert (np.isnan(ours) == ~fin).all()
+    assert (ours[fin] == ref[fin]).all()
+    assert (np.signbit(ours[fin]) == np.signbit(ref[fin])).all()
+    assert oracle.e4m3_value(0x38) == 1.0 and oracle.e4m3_value(0x7E) == 448.0
+    assert oracle.e4m3_value(0xFE) == -448.0 and oracle.e4m3_value(0x08) == 2.0 ** -6
+    assert oracle.e4m3_value(0x01) == 2.0 ** -9 and oracle.e4m3_value(0x07) == 7 * 2.0 ** -9
+    assert np.isnan(oracle.e4m3_value(0x7F)) and np.isnan(oracle.e4m3_value(0xFF))
+
+
+def _e4m3_sweep():
+    codes = np.arange(256, dtype=np.uint8)
+    fin = np.unique(_torch_e4m3_value(codes)[np.isfinite(_torch_e4m3_value(codes))])
+    mids = ((fin[:-1].astype(np.float64) + fin[1:]) / 2).astype(np.float32)   # exact ties
+    near = np.concatenate([np.nextafter(mids, np.float32(np.inf)), np.nextafter(mids, np.float32(-np.inf))])
+    rnd = np.clip(_rng(40).standard_normal(3000).astype(np.float32) * 50, -448, 448)
+    tiny = np.array([0.0, -0.0, 1e-30, -1e-30, 2.0 ** -10, -(2.0 ** -10), 3 * 2.0 ** -11], np.float32)
+    return np.concatenate([fin, mids, near, rnd, tiny]).astype(np.float32)
+
+
+def test_e4m3_encode_matches_library():
+    """Round to nearest e4m3, ties to the even mantissa, sign kept: equals
+    torch's conversion to float8_e4m3fn on every finite value, every exact
+    midpoint between neighbours, the floats next to each midpoint, random
+    values and signed zeros / underflows."""
+    v = _e4m3_sweep()
+    assert (oracle.e4m3_encode(v) == _torch_e4m3_encode(v)).all()
+
+
+def test_e4m3_encode_saturates():
+    assert oracle.e4m3_encode(np.array([460.0, 1e6, -470.0], np.float32)).tolist() == [0x7E, 0x7E, 0xFE]
+
+
+def _nearest_code_brute(v):
+    """Brute force over the 252 finite nonzero codes and zero: the nearest
+    value, a tie to the code with the even low bit."""
+    vals = {c: oracle.e4m3_value(c) for c in range(0x7F)}
+    a = abs(float(v))
+    best = min(vals, key=lambda c: (abs(vals[c] - a), c & 1))
+    return best | (0x80 if np.signbit(v) else 0)
+
+
+def test_quantize_rows_brute_force():
+    """Per row: s = fl32(amax / 448) (1 for a zero row), code = the e4m3 value
+    nearest fl32(w / s) by brute force, the largest magnitude lands on
+    +-448, and s * value(q) is within half a grid step of w."""
+    rng = _rng(41)
+    W = (rng.standard_normal((6, 40)) * np.array([[1.0], [0.02], [300.0], [1e-3], [0.0], [5.0]])).astype(np.float32)
+    W[5, 7] = -W[5].__abs__().max() * 1.5           # the row's extreme is negative
+    q, s = oracle.quantize_e4m3(W)
+    for i in range(W.shape[0]):
+        amax = np.float32(np.abs(W[i]).max())
+        si = np.float32(amax / np.float32(448.0)) if amax > 0 else np.float32(1.0)
+        assert s[i] == si
+        for j in range(W.shape[1]):
+            v = np.clip(np.float32(W[i, j] / si), -448, 448)
+            assert q[i, j] == _nearest_code_brute(v), (i, j)
+        if amax > 0:
+            jmax = int(np.argmax(np.abs(W[i])))
+            assert q[i, jmax] == (0xFE if W[i, jmax] < 0 else 0x7E)
+            deq = s[i].astype(np.float64) * oracle.e4m3_decode(q[i]).astype(np.float64)
+            # half a step: 2^-4 relative in the normal range, 2^-10 * s below 2^-6 * s
+            bound = np.maximum(np.abs(W[i]) * 2.0 ** -4, 2.0 ** -10 * s[i]) * (1 + 1e-6)
+            assert (np.abs(deq - W[i]) <= bound).all()
+    assert s[4] == 1.0 and (q[4] & 0x7F == 0).all()
+
+
+@pytest.mark.parametrize("act", ["swiglu", "gelu"])
+def test_row_scaled_ffn_equals_dequantised_dense(act):
+    """Row-scaled weights: the FFN with scales equals the dense FFN on the
+    dequantised weights s * value(q) formed in float64."""
+    rng = _rng(42)
+    T, d, d_ff, E = 19, 32, 48, 3
+    x, Wr, W1, W3, W2 = _layer(rng, T, d, d_ff, E, act)
+    q1, s1 = oracle.quantize_e4m3(W1)
+    q2, s2 = oracle.quantize_e4m3(W2)
+    q3, s3 = oracle.quantize_e4m3(W3) if act == "swiglu" else (None, None)
+    dec = lambda q: None if q is None else oracle.e4m3_decode(q)
+    o = oracle.forward(x, Wr, dec(q1), dec(q3), dec(q2), 1, "renorm", 0.0, act,
+                       scales=(s1, s3, s2))
+    D = lambda q, sc: None if q is None else sc[..., None].astype(np.float64) * dec(q).astype(np.float64)
+    W1d, W3d, W2d = D(q1, s1), D(q3, s3), D(q2, s2)
+    e = o["idx"][:, 0]
+    ref = np.stack([_dense_expert64(x[t:t + 1], W1d, W3d, W2d, e[t], act)[0] for t in range(T)])
+    assert np.abs(o["y"] - ref).max() <= 1e-6 * np.abs(ref).max()
+    # and the quantised layer stays close to the unquantised one (not a parity bound)
+    o32 = oracle.forward(x, Wr, W1, W3, W2, 1, "renorm", 0.0, act)
+    assert np.abs(o["y"] - o32["y"]).max() <= 0.1 * np.abs(o32["y"]).max()
+
+
 # ---------------------------------------------------------------- statistics
 
 def test_aux_is_one_when_balanced():
