@@ -14,6 +14,10 @@ synchronisations.  The dominant kernel's duration comes from two HIP
 events that the library records on the launch stream around it (the
 descriptor's stage-event hook), over the same timed steps.
 
+The default line also carries "decode_fp8": the decode layer with its
+expert weights quantised row by row to e4m3 (one fp32 scale per row) before
+timing, run by moe_forward_fp8 (weights 1 byte, activations bf16).
+
 Roofline of the dominant kernel (the expert up-projection, a grouped GEMM
 on bf16 MFMA): algorithmic FLOPs per launch = N_kept * 2 * n_up * d * d_ff
 (n_up = 2 matrices for SwiGLU) over its mean event-timed duration, against
@@ -129,6 +133,13 @@ def run_workload(w, steps, warmup, fresh_x_steps=0, seed=0):
     wt = synth.make_weights(w, seed)
     dw = {k: B.to_device(v, w.dtype) for k, v in wt.items()}
     del wt
+    f8 = None
+    if w.weights == "e4m3":
+        # post-training quantisation of the expert weights, before timing
+        f8 = B.quantize_experts(dw["W1"], dw["W3"], dw["W2"])
+        for key in ("W1", "W3", "W2"):
+            dw[key] = None
+        torch.cuda.synchronize()
     n_x = max(1, fresh_x_steps)
     xs, noises, ress = [], [], []
     for s in range(n_x):
@@ -146,6 +157,7 @@ def run_workload(w, steps, warmup, fresh_x_steps=0, seed=0):
     shs = [B.make_shared(desc, dw["Ws1"], dw["Ws3"], dw["Ws2"], ress[j]) for j in range(n_x)] \
         if with_shared else None
     out = B.alloc_outputs(desc)
+    fp8 = B.make_fp8(desc, f8["q1"], f8["q3"], f8["q2"], f8["s1"], f8["s3"], f8["s2"]) if f8 else None
     ev = HipEvents()
     nev = len(stages) + 1
     stream = torch.cuda.current_stream()
@@ -161,7 +173,10 @@ def run_workload(w, steps, warmup, fresh_x_steps=0, seed=0):
         # only the two events around the expert up-projection (the dominant
         # kernel) are recorded: each recorded event separates the kernels
         # around it by a few us
-        if with_shared:
+        if fp8 is not None:
+            B.moe_forward_fp8(desc, fp8, xs[j], dw["Wr"], dw["bias"], noises[j], out["y"], ws,
+                              kept_counts=out["kept_counts"], stats=out["stats"], stream=stream)
+        elif with_shared:
             B.moe_forward_shared(desc, shs[j], xs[j], dw["Wr"], dw["bias"], noises[j], dw["W1"],
                                  dw["W3"], dw["W2"], out["y"], ws, kept_counts=out["kept_counts"],
                                  stats=out["stats"], stream=stream)
@@ -247,6 +262,36 @@ def cpu_baseline(w, seed=0, target_s=22.0):
                        f"and combine on {S} sampled tokens ({t_ffn:.2f}s); fp64 sums")}
 
 
+def decode_object(wd, rd):
+    """Throughput and HBM roofline of a decode workload's run: the expert
+    up-projection (weight streaming) against 8 TB/s, algorithmic bytes =
+    the touched experts' W1 and W3 (bf16: 2 B per weight; e4m3: 1 B plus a
+    4-byte scale per row) + permuted rows in + H out."""
+    ms_d = rd["elapsed"] * 1e3 / rd["steps"]
+    up = rd["stages"].index("expert_up")
+    up_ms_d = float(rd["stage_ms"][up])
+    wbytes = 1 if wd.weights == "e4m3" else 2
+    sbytes = 4 if wd.weights == "e4m3" else 0
+    up_bytes = (rd["touched"] * 2 * wd.d_ff * (wd.d * wbytes + sbytes)
+                + rd["n_kept"] * (wd.d + wd.d_ff) * 2)
+    step_bytes = (rd["touched"] * (3 * wd.d * wd.d_ff * wbytes + (2 * wd.d_ff + wd.d) * sbytes)
+                  + wd.T * wd.d * 4 + wd.E * wd.d * 4)
+    gbs = up_bytes / (up_ms_d * 1e-3) / 1e9
+    return {
+        "workload": wd.name, "weights": "e4m3" if wd.weights == "e4m3" else "bf16",
+        "value": round(wd.T * rd["steps"] / rd["elapsed"], 1),
+        "unit": "tokens/s", "steps": rd["steps"], "ms_per_step": round(ms_d, 4),
+        "step_hbm_gbs": round(step_bytes / (ms_d * 1e-3) / 1e9, 1),
+        "step_hbm_frac": round(step_bytes / (ms_d * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+        "stage_ms": {n: round(float(v), 4) for n, v in zip(rd["stages"], rd["stage_ms"]) if np.isfinite(v)},
+        "roofline": {"bound": "hbm", "kernel": "expert_up", "achieved": round(gbs, 1),
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+                     "traffic": traffic_for(wd.name, "expert_up"),
+                     "algorithmic_per_launch": up_bytes, "mean_launch_ms": round(up_ms_d, 4),
+                     "event_timed_launches": rd["event_steps"]},
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -281,6 +326,23 @@ def main():
         return
     B.load(build_if_missing=False)
     w = synth.WORKLOADS[args.workload]
+    if w.steps > 1:
+        # a decode workload on its own: fresh tokens every step, HBM roofline
+        res = run_workload(w, args.steps, args.warmup, fresh_x_steps=args.steps)
+        obj = decode_object(w, res)
+        line = {
+            "metric": METRIC, "value": obj["value"], "unit": "tokens/s", "n_gpus": 1,
+            "steps": args.steps, "warmup": args.warmup, "ms_per_step": obj["ms_per_step"],
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+            "data": "synthetic",
+            "config": {"workload": w.name, "T": w.T, "d": w.d, "d_ff": w.d_ff, "E": w.E, "k": w.k,
+                       "gate": w.gate, "act": w.act, "capacity_factor": w.cf, "router": "fp32",
+                       "expert_weights": obj["weights"], "parallelism": "single_gpu"},
+            "stage_ms": obj["stage_ms"], "step_hbm_frac": obj["step_hbm_frac"],
+            "roofline": obj["roofline"],
+        }
+        print(json.dumps(line), flush=True)
+        return
     res = run_workload(w, args.steps, args.warmup)
     ms_step = res["elapsed"] * 1e3 / res["steps"]
     tokens_s = w.T * res["steps"] / res["elapsed"]
@@ -325,27 +387,11 @@ def main():
                                 "frac": round(sh_tf / PEAK_BF16_TFLOPS, 4),
                                 "algorithmic_per_stage": shared_flops, "mean_stage_ms": round(sh_ms, 4)}
     if not args.no_decode and w.name == "mixtral_prefill":
-        wd = synth.WORKLOADS["mixtral_decode"]
-        rd = run_workload(wd, args.decode_steps, 10, fresh_x_steps=args.decode_steps)
-        ms_d = rd["elapsed"] * 1e3 / rd["steps"]
-        up_ms_d = float(rd["stage_ms"][up])
-        # algorithmic bytes: touched experts' weights + permuted activations + H
-        up_bytes = rd["touched"] * 2 * wd.d * wd.d_ff * 2 + rd["n_kept"] * (wd.d + wd.d_ff) * 2
-        step_bytes = rd["touched"] * 3 * wd.d * wd.d_ff * 2 + wd.T * wd.d * 4 + wd.E * wd.d * 4
-        gbs = up_bytes / (up_ms_d * 1e-3) / 1e9
-        line["decode"] = {
-            "workload": wd.name, "value": round(wd.T * rd["steps"] / rd["elapsed"], 1),
-            "unit": "tokens/s", "steps": rd["steps"], "ms_per_step": round(ms_d, 4),
-            "step_hbm_gbs": round(step_bytes / (ms_d * 1e-3) / 1e9, 1),
-            "step_hbm_frac": round(step_bytes / (ms_d * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
-            "stage_ms": {n: round(float(v), 4) for n, v in zip(STAGES, rd["stage_ms"]) if np.isfinite(v)},
-            "roofline": {"bound": "hbm", "kernel": "expert_up", "achieved": round(gbs, 1),
-                         "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
-                         "traffic": traffic_for(wd.name, "expert_up"),
-                         "algorithmic_per_launch": up_bytes, "mean_launch_ms": round(up_ms_d, 4),
-                         "event_timed_launches": rd["event_steps"]},
-        }
-        log(f"[bench] {wd.name}: {ms_d:.3f} ms/step")
+        for key, name in (("decode", "mixtral_decode"), ("decode_fp8", "mixtral_decode_fp8")):
+            wd = synth.WORKLOADS[name]
+            rd = run_workload(wd, args.decode_steps, 10, fresh_x_steps=args.decode_steps)
+            line[key] = decode_object(wd, rd)
+            log(f"[bench] {wd.name}: {line[key]['ms_per_step']:.3f} ms/step")
     if not args.no_cpu:
         log("[bench] CPU oracle baseline ...")
         line["cpu_baseline"] = cpu_baseline(w)

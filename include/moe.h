@@ -313,6 +313,71 @@ int moe_forward_shared(const moe_desc *desc, const moe_shared *shared, const voi
                        int32_t *row_of_slot, int32_t *token_of_row, uint8_t *dropped,
                        float *stats, void *ws, size_t ws_bytes, void *stream);
 
+/* ---- expert weights in 8-bit floating point (E4M3) ----------------------------
+ *
+ * Page "Mixture of experts", Mechanics, "Total versus active parameters":
+ * decoding at small batch sizes is limited by reading expert weights;
+ * "Tradeoffs": quantisation helps serving.  The glossary page "Mixture of
+ * Experts (MoE)" (inferensys.com, inference optimization), entry on model
+ * quantization: post-training quantisation of a trained model's weights.
+ * Here every weight row i (a row of W1[e], W3[e] or W2[e]) is stored as
+ * E4M3 codes (the Open Compute Project 8-bit floating point format: bias
+ * 7, 3 mantissa bits, largest value 448, 0x7F/0xFF NaN) and one fp32
+ * scale: row i = s[i] * value(q[i][:]).  Activations stay bf16; the codes
+ * are widened to bf16 exactly inside the kernels, and each row's
+ * accumulated product is multiplied by its scale in fp32.
+ *
+ * Shapes:
+ *   W1, W3   [E][d_ff][d]  uint8  e4m3 codes (W3 only for SwiGLU)
+ *   W2       [E][d][d_ff]  uint8  e4m3 codes
+ *   s1, s3   [E][d_ff]     fp32   scales of the rows of W1, W3
+ *   s2       [E][d]        fp32   scales of the rows of W2
+ */
+typedef struct moe_fp8_experts {
+    const uint8_t *W1, *W3, *W2;
+    const float *s1, *s3, *s2;
+} moe_fp8_experts;
+
+/*
+ * Row-wise post-training quantisation of a [rows][cols] matrix (fp32 when
+ * dtype is MOE_DTYPE_F32, bf16 when MOE_DTYPE_BF16) to E4M3 codes q
+ * [rows][cols] and scales [rows]:
+ *   amax = max_j |W[i][j]|,  scales[i] = fl32(amax / 448)  (1 when that is 0)
+ *   q[i][j] = e4m3(clamp(fl32(W[i][j] / scales[i]), -448, 448))
+ * with correctly rounded fp32 divisions and the conversion rounding to the
+ * nearest e4m3 value, ties to the even code; the largest magnitude of each
+ * row becomes +-448.  Finite inputs only (a NaN in a row makes that row
+ * unspecified).  Applied to an expert weight tensor viewed as
+ * [E * rows_per_expert][cols] it gives the codes and scales above.
+ * rows = 0 enqueues nothing.  Errors: MOE_ERR_INVALID_ARG (bad dtype,
+ * rows < 0, cols < 1, null pointer with rows > 0).
+ */
+int moe_quantize_e4m3(int32_t dtype, const void *W, int64_t rows, int64_t cols, uint8_t *q,
+                      float *scales, void *stream);
+
+/*
+ * moe_expert_ffn with E4M3 expert weights.  Supported for decode-sized
+ * batches, where reading the weights is the bound: desc->dtype bf16, at
+ * most 48 rows per expert (T, or the capacity C when smaller, <= 48), and
+ * d, d_ff multiples of 128; otherwise MOE_ERR_UNSUPPORTED.  w->W3 and
+ * w->s3 are required for SwiGLU and must be NULL otherwise.
+ */
+int moe_expert_ffn_fp8(const moe_desc *desc, const void *x_perm, const int32_t *offsets,
+                       const moe_fp8_experts *w, float *y_perm, void *ws, size_t ws_bytes,
+                       void *stream);
+
+/*
+ * moe_forward with E4M3 expert weights (w in place of W1, W3, W2); the
+ * same shapes are supported as for moe_expert_ffn_fp8.  Routing, dispatch,
+ * statistics and the combine are those of moe_forward.  ws:
+ * moe_workspace_size() bytes.  Stage events as moe_forward.
+ */
+int moe_forward_fp8(const moe_desc *desc, const void *x, const float *W_r, const float *bias,
+                    const float *noise, const moe_fp8_experts *w, void *y, int32_t *topk_idx,
+                    float *gates, int32_t *routed_counts, int32_t *kept_counts, int32_t *offsets,
+                    int32_t *row_of_slot, int32_t *token_of_row, uint8_t *dropped, float *stats,
+                    void *ws, size_t ws_bytes, void *stream);
+
 /* A static, human-readable name for a status code. */
 const char *moe_status_string(int status);
 

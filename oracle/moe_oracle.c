@@ -451,16 +451,20 @@ double orc_e4m3_value(uint8_t c)
  * mantissa is even); magnitudes beyond 448 give 448.  The sign of v (also
  * of a zero or of a value that rounds to zero) is kept.  Finite v only.
  * Positive codes 0x00..0x7E increase with their value, so the nearest one
- * is the last code not above |v| or the code after it.
+ * is the last code not above |v| (found by bisection) or the code after it.
  */
 uint8_t orc_e4m3_encode(float v)
 {
     const double a = fabs((double)v);
     const uint8_t sgn = signbit(v) ? 0x80 : 0x00;
-    int lo = 0;
-    for (int c = 1; c <= 0x7E; ++c)
-        if (orc_e4m3_value((uint8_t)c) <= a)
-            lo = c;
+    int lo = 0, hi = 0x7F; /* value(lo) <= a, and hi is past the last candidate */
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) / 2;
+        if (orc_e4m3_value((uint8_t)mid) <= a)
+            lo = mid;
+        else
+            hi = mid;
+    }
     int best = lo;
     if (lo < 0x7E) {
         const double dl = a - orc_e4m3_value((uint8_t)lo);

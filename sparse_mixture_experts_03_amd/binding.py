@@ -9,7 +9,8 @@ loading fails loudly when the library cannot be found or built.
 Names match the ABI: moe_workspace_size, moe_capacity, moe_route,
 moe_dispatch, moe_expert_ffn, moe_combine, moe_forward, and for shared
 experts plus the block residual moe_workspace_size_shared, moe_shared_ffn,
-moe_combine_shared, moe_forward_shared.
+moe_combine_shared, moe_forward_shared, and for E4M3 expert weights
+moe_quantize_e4m3, moe_expert_ffn_fp8, moe_forward_fp8.
 """
 from __future__ import annotations
 
@@ -57,6 +58,11 @@ class MoeShared(ctypes.Structure):
                 ("W2", ctypes.c_void_p), ("residual", ctypes.c_void_p)]
 
 
+class MoeFp8Experts(ctypes.Structure):
+    _fields_ = [("W1", ctypes.c_void_p), ("W3", ctypes.c_void_p), ("W2", ctypes.c_void_p),
+                ("s1", ctypes.c_void_p), ("s3", ctypes.c_void_p), ("s2", ctypes.c_void_p)]
+
+
 def make_desc(T, d, d_ff, E, k, gate="renorm", act="swiglu", dtype="bf16", cf=0.0) -> MoeDesc:
     return MoeDesc(int(T), int(d), int(d_ff), int(E), int(k), GATE[gate], ACT[act], DTYPE[dtype],
                    float(cf), None, 0)
@@ -97,11 +103,16 @@ def load(build_if_missing: bool = True):
     lib.moe_combine_shared.argtypes = [D, P, P, P, P, P, P, P]
     lib.moe_forward_shared.argtypes = [D, SH, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P,
                                        sz, P]
+    F8 = ctypes.POINTER(MoeFp8Experts)
+    lib.moe_quantize_e4m3.argtypes = [ctypes.c_int32, P, ctypes.c_int64, ctypes.c_int64, P, P, P]
+    lib.moe_expert_ffn_fp8.argtypes = [D, P, P, F8, P, P, sz, P]
+    lib.moe_forward_fp8.argtypes = [D, P, P, P, P, F8, P, P, P, P, P, P, P, P, P, P, P, sz, P]
     lib.moe_status_string.argtypes = [ctypes.c_int]
     lib.moe_status_string.restype = ctypes.c_char_p
     for fn in ("moe_workspace_size", "moe_capacity", "moe_route", "moe_dispatch",
                "moe_expert_ffn", "moe_combine", "moe_forward", "moe_workspace_size_shared",
-               "moe_shared_ffn", "moe_combine_shared", "moe_forward_shared"):
+               "moe_shared_ffn", "moe_combine_shared", "moe_forward_shared", "moe_quantize_e4m3",
+               "moe_expert_ffn_fp8", "moe_forward_fp8"):
         getattr(lib, fn).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -297,6 +308,80 @@ def moe_forward_shared(desc, shared: MoeShared, x, W_r, bias, noise, W1, W3, W2,
         _ptr(stats, torch.float32, (2 * E + 2,), "stats", True),
         _ptr(ws, torch.uint8, None, "ws"), ws.numel(), _stream(stream))
     _check("moe_forward_shared", rc)
+
+
+def moe_quantize_e4m3(W, q, scales, stream=None):
+    """Row-wise E4M3 quantisation of W [..., cols] (bf16 or fp32) into q
+    (uint8, W's shape) and scales (fp32, W.shape[:-1])."""
+    if W.dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError("W must be bf16 or fp32")
+    cols = int(W.shape[-1])
+    rows = W.numel() // cols if cols else 0
+    dt = DTYPE["bf16"] if W.dtype == torch.bfloat16 else DTYPE["f32"]
+    rc = load().moe_quantize_e4m3(dt, _ptr(W, None, None, "W"), rows, cols,
+                                  _ptr(q, torch.uint8, tuple(W.shape), "q"),
+                                  _ptr(scales, torch.float32, tuple(W.shape[:-1]), "scales"),
+                                  _stream(stream))
+    _check("moe_quantize_e4m3", rc)
+
+
+def quantize_experts(W1, W3, W2, stream=None) -> dict:
+    """E4M3 codes and row scales of expert weights (device tensors):
+    q1, q3, q2 (uint8) and s1, s3, s2 (fp32); W3 may be None."""
+    out = {}
+    for name, W in (("1", W1), ("3", W3), ("2", W2)):
+        if W is None:
+            out["q" + name] = out["s" + name] = None
+            continue
+        q = torch.empty(W.shape, dtype=torch.uint8, device=W.device)
+        sc = torch.empty(W.shape[:-1], dtype=torch.float32, device=W.device)
+        moe_quantize_e4m3(W, q, sc, stream)
+        out["q" + name], out["s" + name] = q, sc
+    return out
+
+
+def make_fp8(desc, q1, q3, q2, s1, s3, s2) -> MoeFp8Experts:
+    """A moe_fp8_experts over device tensors (they must outlive its use)."""
+    d, d_ff, E = desc.d, desc.d_ff, desc.E
+    return MoeFp8Experts(_ptr(q1, torch.uint8, (E, d_ff, d), "q1"),
+                         _ptr(q3, torch.uint8, (E, d_ff, d), "q3", True),
+                         _ptr(q2, torch.uint8, (E, d, d_ff), "q2"),
+                         _ptr(s1, torch.float32, (E, d_ff), "s1"),
+                         _ptr(s3, torch.float32, (E, d_ff), "s3", True),
+                         _ptr(s2, torch.float32, (E, d), "s2"))
+
+
+def moe_expert_ffn_fp8(desc, x_perm, offsets, fp8: MoeFp8Experts, y_perm, ws, stream=None):
+    T, d, E, k = desc.T, desc.d, desc.E, desc.k
+    rc = load().moe_expert_ffn_fp8(
+        ctypes.byref(desc), _ptr(x_perm, _act_dtype(desc), (T * k, d), "x_perm"),
+        _ptr(offsets, torch.int32, (E + 1,), "offsets"), ctypes.byref(fp8),
+        _ptr(y_perm, torch.float32, (T * k, d), "y_perm"), _ptr(ws, torch.uint8, None, "ws"),
+        ws.numel(), _stream(stream))
+    _check("moe_expert_ffn_fp8", rc)
+
+
+def moe_forward_fp8(desc, fp8: MoeFp8Experts, x, W_r, bias, noise, y, ws, topk_idx=None,
+                    gates=None, routed_counts=None, kept_counts=None, offsets=None,
+                    row_of_slot=None, token_of_row=None, dropped=None, stats=None, stream=None):
+    T, d, E, k = desc.T, desc.d, desc.E, desc.k
+    dt = _act_dtype(desc)
+    rc = load().moe_forward_fp8(
+        ctypes.byref(desc), _ptr(x, dt, (T, d), "x"), _ptr(W_r, torch.float32, (E, d), "W_r"),
+        _ptr(bias, torch.float32, (E,), "bias", True),
+        _ptr(noise, torch.float32, (T, E), "noise", True), ctypes.byref(fp8),
+        _ptr(y, dt, (T, d), "y"),
+        _ptr(topk_idx, torch.int32, (T, k), "topk_idx", True),
+        _ptr(gates, torch.float32, (T, k), "gates", True),
+        _ptr(routed_counts, torch.int32, (E,), "routed_counts", True),
+        _ptr(kept_counts, torch.int32, (E,), "kept_counts", True),
+        _ptr(offsets, torch.int32, (E + 1,), "offsets", True),
+        _ptr(row_of_slot, torch.int32, (T, k), "row_of_slot", True),
+        _ptr(token_of_row, torch.int32, (T * k,), "token_of_row", True),
+        _ptr(dropped, torch.uint8, (T, k), "dropped", True),
+        _ptr(stats, torch.float32, (2 * E + 2,), "stats", True),
+        _ptr(ws, torch.uint8, None, "ws"), ws.numel(), _stream(stream))
+    _check("moe_forward_fp8", rc)
 
 
 def status_string(code: int) -> str:

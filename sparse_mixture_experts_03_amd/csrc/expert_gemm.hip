@@ -40,20 +40,7 @@ namespace moe {
 
 namespace {
 
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
-
-constexpr int ACT_RELU = 0, ACT_GELU = 1, ACT_SWIGLU = 2, ACT_NONE = 3;
-
-// SwiGLU uses the hardware exp2 and reciprocal (about 1 ulp each; the
-// result is rounded to bf16, 8 bits, right after).  GELU keeps erff.
-__device__ __forceinline__ float apply_act(int act, float a1, float a3) {
-    if (act == ACT_SWIGLU)
-        return a1 * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-1.44269504088896341f * a1)) * a3;
-    if (act == ACT_GELU) return 0.5f * a1 * (1.f + erff(a1 * 0.70710678118654752f));
-    if (act == ACT_RELU) return fmaxf(a1, 0.f);
-    return a1;
-}
 
 // Tile schedule.  The work is the set of (expert e, column tile n, row tile
 // m) with m < ceil(rows_e / BM), ordered e-major, then n, then m.  The 1-D

@@ -300,20 +300,36 @@ int moe_combine(const moe_desc *desc, const float *y_perm, const int32_t *row_of
 
 namespace {
 
-// moe_forward and moe_forward_shared: sh == nullptr is moe_forward (seven
-// stages); otherwise the shared experts run as their own stage between
-// expert-down and the combine, which adds them and the residual.
-int forward_impl(const moe_desc *desc, const moe_shared *sh, const void *x, const float *W_r,
-                 const float *bias, const float *noise, const void *W1, const void *W3,
-                 const void *W2, void *y, int32_t *topk_idx, float *gates,
-                 int32_t *routed_counts, int32_t *kept_counts, int32_t *offsets,
+// Validates E4M3 expert weights for this description (shape support first).
+int check_fp8(const Shape &s, const moe_fp8_experts *w) {
+    if (!w) return MOE_ERR_INVALID_ARG;
+    if (!moe::fp8_supported(s)) return MOE_ERR_UNSUPPORTED;
+    if (!w->W1 || !w->W2 || !w->s1 || !w->s2) return MOE_ERR_INVALID_ARG;
+    const bool swiglu = s.act == MOE_ACT_SWIGLU;
+    if (swiglu != (w->W3 != nullptr) || swiglu != (w->s3 != nullptr)) return MOE_ERR_INVALID_ARG;
+    return MOE_OK;
+}
+
+// moe_forward, moe_forward_shared and moe_forward_fp8: sh == nullptr and
+// f8 == nullptr is moe_forward (seven stages); with sh the shared experts
+// run as their own stage between expert-down and the combine, which adds
+// them and the residual; with f8 the expert GEMMs read E4M3 weights.
+int forward_impl(const moe_desc *desc, const moe_shared *sh, const moe_fp8_experts *f8,
+                 const void *x, const float *W_r, const float *bias, const float *noise,
+                 const void *W1, const void *W3, const void *W2, void *y, int32_t *topk_idx,
+                 float *gates, int32_t *routed_counts, int32_t *kept_counts, int32_t *offsets,
                  int32_t *row_of_slot, int32_t *token_of_row, uint8_t *dropped, float *stats,
                  void *ws, size_t ws_bytes, void *stream) {
     Shape s;
     int rc = check_desc(desc, &s);
     if (rc != MOE_OK) return rc;
-    if (!x || !W_r || !W1 || !W2 || !y) return MOE_ERR_INVALID_ARG;
-    if ((s.act == MOE_ACT_SWIGLU) != (W3 != nullptr)) return MOE_ERR_INVALID_ARG;
+    if (f8) {
+        if (!x || !W_r || !y) return MOE_ERR_INVALID_ARG;
+        if ((rc = check_fp8(s, f8)) != MOE_OK) return rc;
+    } else {
+        if (!x || !W_r || !W1 || !W2 || !y) return MOE_ERR_INVALID_ARG;
+        if ((s.act == MOE_ACT_SWIGLU) != (W3 != nullptr)) return MOE_ERR_INVALID_ARG;
+    }
     if (sh && (rc = check_shared(s, sh)) != MOE_OK) return rc;
     const int S = sh ? sh->n_shared : 0;
     if ((rc = check_ws(s, ws, ws_bytes, S)) != MOE_OK) return rc;
@@ -362,11 +378,17 @@ int forward_impl(const moe_desc *desc, const moe_shared *sh, const void *x, cons
     // the gather is folded into the up projection's loads: its rows of A are
     // read from x through token_of_row, so x_perm is not materialised here
     ev.around_next_launch();  // events before and after expert-up
-    const hipError_t up_err = moe::launch_expert_up(s, x, token_of_row, offsets, W1, W3, H, st);
+    const hipError_t up_err =
+        f8 ? moe::launch_expert_up_fp8(s, x, token_of_row, offsets, f8->W1, f8->W3, f8->s1, f8->s3, H, st)
+           : moe::launch_expert_up(s, x, token_of_row, offsets, W1, W3, H, st);
     moe::next_launch_events() = moe::LaunchEvents{nullptr, nullptr};
     MOE_TRY(up_err);
-    float *part2 = L.y_perm2 ? at<float>(ws, L.y_perm2) : nullptr;
-    MOE_TRY(moe::launch_expert_down(s, H, offsets, W2, y_perm, part2, st));
+    // the e4m3 path never splits K (streaming kernel only)
+    float *part2 = (!f8 && L.y_perm2) ? at<float>(ws, L.y_perm2) : nullptr;
+    if (f8)
+        MOE_TRY(moe::launch_expert_down_fp8(s, H, offsets, f8->W2, f8->s2, y_perm, st));
+    else
+        MOE_TRY(moe::launch_expert_down(s, H, offsets, W2, y_perm, part2, st));
     MOE_TRY(ev.record(st));
     if (!sh) {
         MOE_TRY(moe::launch_combine(s, y_perm, part2, row_of_slot, gates, y, st));
@@ -395,7 +417,7 @@ int moe_forward(const moe_desc *desc, const void *x, const float *W_r, const flo
                 int32_t *topk_idx, float *gates, int32_t *routed_counts, int32_t *kept_counts,
                 int32_t *offsets, int32_t *row_of_slot, int32_t *token_of_row,
                 uint8_t *dropped, float *stats, void *ws, size_t ws_bytes, void *stream) {
-    return forward_impl(desc, nullptr, x, W_r, bias, noise, W1, W3, W2, y, topk_idx, gates,
+    return forward_impl(desc, nullptr, nullptr, x, W_r, bias, noise, W1, W3, W2, y, topk_idx, gates,
                         routed_counts, kept_counts, offsets, row_of_slot, token_of_row, dropped,
                         stats, ws, ws_bytes, stream);
 }
@@ -450,9 +472,48 @@ int moe_forward_shared(const moe_desc *desc, const moe_shared *shared, const voi
                        int32_t *row_of_slot, int32_t *token_of_row, uint8_t *dropped,
                        float *stats, void *ws, size_t ws_bytes, void *stream) {
     if (!shared) return MOE_ERR_INVALID_ARG;
-    return forward_impl(desc, shared, x, W_r, bias, noise, W1, W3, W2, y, topk_idx, gates,
+    return forward_impl(desc, shared, nullptr, x, W_r, bias, noise, W1, W3, W2, y, topk_idx, gates,
                         routed_counts, kept_counts, offsets, row_of_slot, token_of_row, dropped,
                         stats, ws, ws_bytes, stream);
+}
+
+int moe_quantize_e4m3(int32_t dtype, const void *W, int64_t rows, int64_t cols, uint8_t *q,
+                      float *scales, void *stream) {
+    if (dtype != MOE_DTYPE_F32 && dtype != MOE_DTYPE_BF16) return MOE_ERR_INVALID_ARG;
+    if (rows < 0 || cols < 1) return MOE_ERR_INVALID_ARG;
+    if (rows == 0) return MOE_OK;
+    if (!W || !q || !scales) return MOE_ERR_INVALID_ARG;
+    MOE_TRY(moe::launch_quantize_e4m3(dtype == MOE_DTYPE_BF16 ? 1 : 0, W, rows, cols, q, scales,
+                                      (hipStream_t)stream));
+    return MOE_OK;
+}
+
+int moe_expert_ffn_fp8(const moe_desc *desc, const void *x_perm, const int32_t *offsets,
+                       const moe_fp8_experts *w, float *y_perm, void *ws, size_t ws_bytes,
+                       void *stream) {
+    Shape s;
+    int rc = check_desc(desc, &s);
+    if (rc != MOE_OK) return rc;
+    if (!x_perm || !offsets || !y_perm) return MOE_ERR_INVALID_ARG;
+    if ((rc = check_fp8(s, w)) != MOE_OK) return rc;
+    if ((rc = check_ws(s, ws, ws_bytes)) != MOE_OK) return rc;
+    const Layout L = layout(s);
+    hipStream_t st = (hipStream_t)stream;
+    void *H = at<char>(ws, L.H);
+    MOE_TRY(moe::launch_expert_up_fp8(s, x_perm, nullptr, offsets, w->W1, w->W3, w->s1, w->s3, H, st));
+    MOE_TRY(moe::launch_expert_down_fp8(s, H, offsets, w->W2, w->s2, y_perm, st));
+    return MOE_OK;
+}
+
+int moe_forward_fp8(const moe_desc *desc, const void *x, const float *W_r, const float *bias,
+                    const float *noise, const moe_fp8_experts *w, void *y, int32_t *topk_idx,
+                    float *gates, int32_t *routed_counts, int32_t *kept_counts, int32_t *offsets,
+                    int32_t *row_of_slot, int32_t *token_of_row, uint8_t *dropped, float *stats,
+                    void *ws, size_t ws_bytes, void *stream) {
+    if (!w) return MOE_ERR_INVALID_ARG;
+    return forward_impl(desc, nullptr, w, x, W_r, bias, noise, nullptr, nullptr, nullptr, y,
+                        topk_idx, gates, routed_counts, kept_counts, offsets, row_of_slot,
+                        token_of_row, dropped, stats, ws, ws_bytes, stream);
 }
 
 const char *moe_status_string(int status) {

@@ -145,6 +145,19 @@ hipError_t launch_expert_down(const Shape &s, const void *H, const int32_t *offs
 hipError_t launch_add_partial(const Shape &s, float *y_perm, const float *part2,
                               const int32_t *offsets, hipStream_t st);
 
+// ---- expert weights in e4m3 (decode batches) ------------------------------
+// Row-wise post-training quantisation (dtype 1: bf16 input, 0: fp32).
+hipError_t launch_quantize_e4m3(int dtype, const void *W, int64_t rows, int64_t cols, uint8_t *q,
+                                float *scales, hipStream_t st);
+// The e4m3-weight expert GEMMs exist for the weight-streaming shapes only:
+// bf16 activations, at most 48 rows per expert, d and d_ff multiples of 128.
+bool fp8_supported(const Shape &s);
+hipError_t launch_expert_up_fp8(const Shape &s, const void *A, const int32_t *a_rows,
+                                const int32_t *offsets, const uint8_t *W1, const uint8_t *W3,
+                                const float *S1, const float *S3, void *H, hipStream_t st);
+hipError_t launch_expert_down_fp8(const Shape &s, const void *H, const int32_t *offsets,
+                                  const uint8_t *W2, const float *S2, float *y_perm, hipStream_t st);
+
 // ---- combine -------------------------------------------------------------
 // y_perm_part2: nullptr, or the second K half of a split down projection.
 hipError_t launch_combine(const Shape &s, const float *y_perm, const float *y_perm_part2,
@@ -175,6 +188,21 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
     return __uint_as_float((uint32_t)b << 16);
+}
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+
+// Expert activations of the GEMM epilogues (ACT_NONE: the down projection).
+constexpr int ACT_RELU = 0, ACT_GELU = 1, ACT_SWIGLU = 2, ACT_NONE = 3;
+
+// SwiGLU uses the hardware exp2 and reciprocal (about 1 ulp each; the
+// result is rounded to bf16, 8 bits, right after).  GELU keeps erff.
+__device__ __forceinline__ float apply_act(int act, float a1, float a3) {
+    if (act == ACT_SWIGLU)
+        return a1 * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-1.44269504088896341f * a1)) * a3;
+    if (act == ACT_GELU) return 0.5f * a1 * (1.f + erff(a1 * 0.70710678118654752f));
+    if (act == ACT_RELU) return fmaxf(a1, 0.f);
+    return a1;
 }
 
 }  // namespace moe

@@ -58,6 +58,7 @@ class Workload:
     steps: int = 1       # decode: fresh x per step
     n_shared: int = 0    # shared experts every token visits
     residual: bool = False  # block residual added to the layer output
+    weights: str = "act"    # "act": experts in the act dtype; "e4m3": quantised from those
 
     def with_(self, **kw) -> "Workload":
         return replace(self, **kw)
@@ -89,6 +90,11 @@ WORKLOADS = {
     "mixtral_prefill_shared": Workload("mixtral_prefill_shared", 4096, 4096, 14336, 8, 2,
                                        "renorm", 0.0, "swiglu", "bf16", x_rmsnorm=True,
                                        n_shared=1, residual=True),
+    # The Mixtral-shape decode layer with its expert weights quantised row
+    # by row to e4m3 (from the bf16 draws; the quantisation itself is the
+    # library's or the oracle's, not this module's).
+    "mixtral_decode_fp8": Workload("mixtral_decode_fp8", 32, 4096, 14336, 8, 2, "renorm", 0.0,
+                                   "swiglu", "bf16", x_rmsnorm=True, steps=100, weights="e4m3"),
 }
 
 

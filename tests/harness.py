@@ -51,6 +51,60 @@ def reference(w, wt, tk, tokens=None):
         shared=shared, residual=_wid(tk.get("res")) if w.residual else None)
 
 
+def quantize_ref(wt):
+    """The oracle's own e4m3 quantisation of the (widened) expert weights:
+    codes and scales per matrix (q1, s1, q3, s3, q2, s2)."""
+    out = {}
+    for n in ("1", "3", "2"):
+        W = wt["W" + n]
+        if W is None:
+            out["q" + n] = out["s" + n] = None
+        else:
+            out["q" + n], out["s" + n] = oracle.quantize_e4m3(synth.widen(W))
+    return out
+
+
+def reference_fp8(w, wt, tk, qref, tokens=None):
+    """The oracle's forward with the e4m3 expert weights of qref: each row
+    the value of its codes times its scale."""
+    dec = lambda q: None if q is None else oracle.e4m3_decode(q)
+    return oracle.forward(
+        synth.widen(tk["x"]), wt["Wr"], dec(qref["q1"]), dec(qref["q3"]), dec(qref["q2"]),
+        w.k, w.gate, w.cf, w.act, wt["bias"], tk["noise"], tokens=tokens,
+        scales=(qref["s1"], qref["s3"], qref["s2"]))
+
+
+def device_fp8(dw):
+    """The library's e4m3 quantisation of the device expert weights."""
+    return B.quantize_experts(dw["W1"], dw.get("W3"), dw["W2"])
+
+
+def assert_fp8_equal(got, qref):
+    """Codes and scales bit for bit."""
+    for n in ("1", "3", "2"):
+        if qref["q" + n] is None:
+            assert got["q" + n] is None
+            continue
+        np.testing.assert_array_equal(got["q" + n].cpu().numpy(), qref["q" + n], err_msg="q" + n)
+        np.testing.assert_array_equal(got["s" + n].cpu().numpy().view(np.uint32),
+                                      qref["s" + n].view(np.uint32), err_msg="s" + n)
+
+
+def run_forward_fp8(w, dw, dt, f8, stream=None):
+    desc = B.desc_for(w)
+    out = B.alloc_outputs(desc)
+    ws = B.workspace(desc)
+    fp8 = B.make_fp8(desc, f8["q1"], f8["q3"], f8["q2"], f8["s1"], f8["s3"], f8["s2"])
+    B.moe_forward_fp8(desc, fp8, dt["x"], dw["Wr"], dw["bias"], dt["noise"], out["y"], ws,
+                      topk_idx=out["topk_idx"], gates=out["gates"],
+                      routed_counts=out["routed_counts"], kept_counts=out["kept_counts"],
+                      offsets=out["offsets"], row_of_slot=out["row_of_slot"],
+                      token_of_row=out["token_of_row"], dropped=out["dropped"],
+                      stats=out["stats"], stream=stream)
+    torch.cuda.synchronize()
+    return {k: v.cpu() for k, v in out.items()}
+
+
 def shared_arg(w, desc, dw, dt):
     """moe_shared for the workload's shared experts and residual."""
     return B.make_shared(desc, dw.get("Ws1"), dw.get("Ws3"), dw.get("Ws2"),

@@ -167,3 +167,49 @@ def test_shared_validation_before_launch():
         a = [FAKE, FAKE, FAKE, None, None, FAKE]
         a[i] = None
         assert lib.moe_combine_shared(d, *a, None) == -1
+
+
+# ---- e4m3 expert weights -------------------------------------------------------
+
+def test_quantize_validation():
+    lib = B.load()
+    assert lib.moe_quantize_e4m3(5, FAKE, 4, 8, FAKE, FAKE, None) == -1
+    assert lib.moe_quantize_e4m3(1, FAKE, -1, 8, FAKE, FAKE, None) == -1
+    assert lib.moe_quantize_e4m3(1, FAKE, 4, 0, FAKE, FAKE, None) == -1
+    assert lib.moe_quantize_e4m3(1, None, 4, 8, FAKE, FAKE, None) == -1
+    assert lib.moe_quantize_e4m3(1, None, 0, 8, None, None, None) == 0   # nothing to do
+
+
+def _f8(W3=FAKE, s3=FAKE, s1=FAKE):
+    return B.MoeFp8Experts(FAKE, W3, FAKE, s1, s3, FAKE)
+
+
+@pytest.mark.parametrize("desc_kw,w,code", [
+    (dict(T=32, d=512, d_ff=768), _f8(s1=None), -1),                 # a scale missing
+    (dict(T=32, d=512, d_ff=768), _f8(W3=None), -1),                 # SwiGLU needs W3 and s3
+    (dict(T=32, d=512, d_ff=768, act="relu"), _f8(), -1),            # ... and only SwiGLU
+    (dict(T=100, d=512, d_ff=768), _f8(), -2),                       # > 48 rows per expert
+    (dict(T=100, d=512, d_ff=768, cf=0.25), _f8(), 0),               # capacity 7 rows: fine
+    (dict(T=32, d=520, d_ff=768), _f8(), -2),                        # d not a multiple of 128
+    (dict(T=32, d=512, d_ff=768, dtype="f32"), _f8(), -2),           # bf16 activations only
+])
+def test_fp8_validation_before_launch(desc_kw, w, code):
+    lib = B.load()
+    kw = dict(E=8, k=2)
+    kw.update(desc_kw)
+    desc = B.make_desc(kw.pop("T"), kw.pop("d"), kw.pop("d_ff"), kw.pop("E"), kw.pop("k"), **kw)
+    d = ctypes.byref(desc)
+    need = B.moe_workspace_size(desc)
+    if code == 0:
+        # a valid call: shown by reaching the workspace check (one byte short),
+        # so that nothing is launched on the fake pointers
+        rc = lib.moe_forward_fp8(d, FAKE, FAKE, None, None, ctypes.byref(w), FAKE, *([None] * 9),
+                                 FAKE, need - 1, None)
+        assert rc == -4
+    else:
+        rc = lib.moe_forward_fp8(d, FAKE, FAKE, None, None, ctypes.byref(w), FAKE, *([None] * 9),
+                                 FAKE, need, None)
+        assert rc == code
+        assert lib.moe_expert_ffn_fp8(d, FAKE, FAKE, ctypes.byref(w), FAKE, FAKE, need, None) == code
+    assert lib.moe_forward_fp8(d, FAKE, FAKE, None, None, None, FAKE, *([None] * 9), FAKE, need,
+                               None) == -1

@@ -47,3 +47,27 @@ def test_full_size(name):
         assert (y[full] == 0).all()
     print(f"[full] {name}: ok, y rel err {rel:.2e}, kept {int(ref['offsets'][-1])}, "
           f"dropped {int(ref['dropped'].sum())}", flush=True)
+
+
+def test_full_size_fp8_decode():
+    """The Mixtral-shape decode layer with e4m3 expert weights at full size:
+    the library's quantisation of all 8 experts equals the oracle's bit for
+    bit, and the forward matches the oracle on every token."""
+    w = synth.WORKLOADS["mixtral_decode_fp8"]
+    print("[full] mixtral_decode_fp8: generating inputs", flush=True)
+    wt, tk = H.prepare(w)
+    print("[full] mixtral_decode_fp8: oracle quantisation", flush=True)
+    qref = H.quantize_ref(wt)
+    dw, dt = H.device_weights(w, wt), H.device_tokens(w, tk)
+    print("[full] mixtral_decode_fp8: GPU quantisation", flush=True)
+    f8 = H.device_fp8(dw)
+    H.assert_fp8_equal(f8, qref)
+    print("[full] mixtral_decode_fp8: oracle forward", flush=True)
+    ref = H.reference_fp8(w, wt, tk, qref)
+    print("[full] mixtral_decode_fp8: GPU forward", flush=True)
+    got = H.run_forward_fp8(w, dw, dt, f8)
+    H.assert_routing_exact(w, got, ref)
+    H.assert_gates_close(got, ref)
+    H.assert_stats_close(w, got, ref)
+    rel = H.assert_y_close(w, H.y_float(got["y"]), ref["y"])
+    print(f"[full] mixtral_decode_fp8: ok, y rel err {rel:.2e}", flush=True)
