@@ -59,7 +59,8 @@ STAGES = ("route", "route_finalize", "dispatch", "gather", "expert_up", "expert_
 STAGES_SHARED = ("route", "route_finalize", "dispatch", "gather", "expert_up", "expert_down",
                  "shared", "combine")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
-GEMM_SRC = os.path.join(ROOT, "sparse_mixture_experts_03_amd", "csrc", "expert_gemm.hip")
+GEMM_SRCS = [os.path.join(ROOT, "sparse_mixture_experts_03_amd", "csrc", f)
+             for f in ("expert_gemm.hip", "expert_fp8.hip")]
 
 
 def log(*a):
@@ -103,8 +104,12 @@ class HipEvents:
 
 
 def source_sha():
-    with open(GEMM_SRC, "rb") as fh:
-        return hashlib.sha256(fh.read()).hexdigest()[:16]
+    """Hash of the GEMM kernel sources (the bf16 and the e4m3 ones)."""
+    h = hashlib.sha256()
+    for path in GEMM_SRCS:
+        with open(path, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
 
 
 def traffic_for(workload, kernel, launches_per_step=1):
