@@ -213,3 +213,22 @@ def test_fp8_validation_before_launch(desc_kw, w, code):
         assert lib.moe_expert_ffn_fp8(d, FAKE, FAKE, ctypes.byref(w), FAKE, FAKE, need, None) == code
     assert lib.moe_forward_fp8(d, FAKE, FAKE, None, None, None, FAKE, *([None] * 9), FAKE, need,
                                None) == -1
+
+
+def test_header_compiles_as_c_and_links(tmp_path):
+    """include/moe.h is a C header: a C11 program compiled by gcc against it
+    and linked to libmoe.so calls the host-only entry points."""
+    import shutil
+    import subprocess
+    lib = B.load()
+    exe = tmp_path / "abi_host"
+    src = os.path.join(ROOT, "tests", "c", "abi_host.c")
+    libdir = os.path.dirname(B.LIB_PATH)
+    gcc = shutil.which("gcc")
+    assert gcc, "gcc is needed"
+    subprocess.run([gcc, "-std=c11", "-Wall", "-Wextra", "-Werror", "-I", os.path.join(ROOT, "include"),
+                    src, "-o", str(exe), "-L", libdir, "-lmoe", f"-Wl,-rpath,{libdir}"], check=True)
+    r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=60)
+    assert r.returncode == 0, r.stderr
+    assert r.stdout.startswith("ok ")
+    del lib
