@@ -60,6 +60,10 @@ def _load():
     lib.orc_quantize_e4m3.restype = None
     lib.orc_e4m3_decode.argtypes = [i64, ip, fp]
     lib.orc_e4m3_decode.restype = None
+    lib.orc_backward.argtypes = [i64, i64, i64, i64, i64, ctypes.c_int, ctypes.c_int, fp, fp, fp, fp,
+                                 fp, fp, fp, ip, fp, ctypes.c_double, ctypes.c_double, fp, fp, fp,
+                                 fp, fp, fp]
+    lib.orc_backward.restype = ctypes.c_int
     lib.orc_threads.argtypes = []
     lib.orc_threads.restype = ctypes.c_int
     _lib = lib
@@ -231,6 +235,35 @@ def stats(idx, p, lse):
     z = np.zeros(1, np.float64)
     _load().orc_stats(T, E, k, _p(idx), _p(p), _p(lse), _p(f), _p(P), _p(aux), _p(z))
     return f, P, float(aux[0]), float(z[0])
+
+
+def backward(x, Wr, W1, W3, W2, k, mode, cf, act, dy, alpha_aux=0.0, alpha_z=0.0, bias=None,
+             noise=None, rows=None):
+    """Gradients of L = sum <dy, y> + alpha_aux aux + alpha_z z for the routing
+    the forward takes (held fixed): dx, dWr, dbias (or None), dW1, dW3 (or
+    None), dW2 (the Mechanics equations differentiated; see moe_oracle.c).
+    ``rows``: the forward's row_of_slot (computed here if None)."""
+    x, Wr, W1, W2, dy = _f32(x), _f32(Wr), _f32(W1), _f32(W2), _f32(dy)
+    W3 = _f32(W3) if act == "swiglu" else None
+    bias, noise = _f32(bias), _f32(noise)
+    T, d = x.shape
+    E, d_ff = W1.shape[0], W1.shape[1]
+    if rows is None:
+        fw = forward(x, Wr, W1, W3, W2, k, mode, cf, act, bias, noise, tokens=np.zeros(0, np.int64))
+        rows = fw["row_of_slot"]
+    rows = np.ascontiguousarray(rows, dtype=np.int32)
+    out = dict(dx=np.empty((T, d), np.float32), dWr=np.empty((E, d), np.float32),
+               dbias=np.empty(E, np.float32) if bias is not None else None,
+               dW1=np.empty(W1.shape, np.float32),
+               dW3=np.empty(W1.shape, np.float32) if W3 is not None else None,
+               dW2=np.empty(W2.shape, np.float32))
+    rc = _load().orc_backward(T, d, d_ff, E, k, _GATE[mode], _ACT[act], _p(x), _p(Wr), _p(bias),
+                              _p(noise), _p(W1), _p(W3), _p(W2), _p(rows), _p(dy),
+                              float(alpha_aux), float(alpha_z), _p(out["dx"]), _p(out["dWr"]),
+                              _p(out["dbias"]), _p(out["dW1"]), _p(out["dW3"]), _p(out["dW2"]))
+    if rc != 0:
+        raise ValueError("orc_backward failed")
+    return out
 
 
 def threads():

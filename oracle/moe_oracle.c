@@ -517,6 +517,268 @@ void orc_e4m3_decode(int64_t n, const uint8_t *q, float *out)
         out[i] = (float)orc_e4m3_value(q[i]);
 }
 
+/*
+ * Backward of the layer (training): the gradients of
+ *   L = sum_t <dy_t, y_t> + alpha_aux * aux + alpha_z * z
+ * with respect to x, W_r, the router bias and the expert weights, for the
+ * routing the forward took (the top-k choices and the capacity drops are
+ * discrete, so they are held fixed; "Replacing the feed-forward block": the
+ * router learns through the gate values, which are differentiable).
+ *   - combine: y_t = sum over kept slots of g_ts E_e(x_t), so dE_e(x_t) =
+ *     g_ts dy_t and dg_ts = <dy_t, E_e(x_t)> (0 for a dropped slot);
+ *   - expert: a1 = W1 x, a3 = W3 x, H = act(a1, a3), E = W2 H (H stored in
+ *     fp32 as in the forward); dH = W2^T dE, then through the activation
+ *     (SwiGLU: H = silu(a1) a3, silu' = s (1 + a1 (1 - s)), s the logistic
+ *     function; GELU: (a Phi(a))' = Phi(a) + a phi(a); ReLU: 1 for a > 0);
+ *     dx += W1^T da1 + W3^T da3, dW1 += da1 x^T, dW3 += da3 x^T,
+ *     dW2 += dE H^T, summed over the expert's kept rows in token order;
+ *   - gates ("Top-k gating"): renormalised g = softmax of the selected
+ *     logits, dh_sel = g (dg - <g, dg>); Switch g = p of the selected
+ *     experts, dp = dg at those experts, dh = p (dp - <p, dp>);
+ *   - "The load-balancing loss": aux = E sum_i f_i P_i with f_i the share of
+ *     top choices (a count, constant) and P_i = mean_t p_ti, so
+ *     d aux / d P_i = E f_i and dh_t += alpha_aux p_t (a - <p_t, a>) with
+ *     a_i = E f_i / T; z = mean_t lse_t^2, so dh_t += alpha_z (2 / T) lse_t p_t;
+ *   - router: h = W_r x + b + n, so dW_r = sum_t dh_t x_t^T, db = sum_t dh_t,
+ *     dx_t += W_r^T dh_t.
+ * Every sum in double, in index order; outputs rounded to fp32 once.
+ *   rows [T][k]: row of slot (t, s) in the forward's permutation, -1 if
+ *   dropped (only its sign is used here).  dbias may be NULL.
+ * Returns 0, or -1 on a bad argument or allocation failure.
+ */
+int orc_backward(int64_t T, int64_t d, int64_t d_ff, int64_t E, int64_t k, int gate, int act,
+                 const float *x, const float *Wr, const float *bias, const float *noise,
+                 const float *W1, const float *W3, const float *W2, const int32_t *rows,
+                 const float *dy, double alpha_aux, double alpha_z, float *dx, float *dWr,
+                 float *dbias, float *dW1, float *dW3, float *dW2)
+{
+    const int swiglu = act == ORC_ACT_SWIGLU;
+    float *h = (float *)malloc((size_t)(T * E) * sizeof(float));
+    int32_t *idx = (int32_t *)malloc((size_t)(T * k) * sizeof(int32_t));
+    double *g = (double *)malloc((size_t)(T * k) * sizeof(double));
+    double *p = (double *)malloc((size_t)(T * E) * sizeof(double));
+    double *lse = (double *)malloc((size_t)T * sizeof(double));
+    double *dg = (double *)calloc((size_t)(T * k), sizeof(double));
+    double *dh = (double *)calloc((size_t)(T * E), sizeof(double));
+    double *dxd = (double *)calloc((size_t)(T * d), sizeof(double));
+    /* per kept slot: da1, da3, H (fp32 values) and dE */
+    int64_t *pair_of = (int64_t *)malloc((size_t)(T * k) * sizeof(int64_t));
+    int rc = -1;
+    if (!h || !idx || !g || !p || !lse || !dg || !dh || !dxd || !pair_of)
+        goto out;
+    orc_router_logits(T, d, E, x, Wr, bias, noise, h);
+    if (orc_gate(T, E, k, gate, h, idx, g, p, lse) != 0)
+        goto out;
+    int64_t n = 0;
+    for (int64_t i = 0; i < T * k; ++i)
+        pair_of[i] = rows[i] >= 0 ? n++ : -1;
+    {
+        double *da1 = (double *)calloc((size_t)(n * d_ff) + 1, sizeof(double));
+        double *da3 = (double *)calloc((size_t)(n * d_ff) + 1, sizeof(double));
+        double *Hs = (double *)calloc((size_t)(n * d_ff) + 1, sizeof(double));
+        double *dE = (double *)calloc((size_t)(n * d) + 1, sizeof(double));
+        if (!da1 || !da3 || !Hs || !dE) {
+            free(da1);
+            free(da3);
+            free(Hs);
+            free(dE);
+            goto out;
+        }
+        /* expert part, one token at a time */
+#pragma omp parallel for schedule(dynamic, 1)
+        for (int64_t t = 0; t < T; ++t) {
+            const float *xt = x + t * d;
+            for (int64_t s = 0; s < k; ++s) {
+                const int64_t q = pair_of[t * k + s];
+                if (q < 0)
+                    continue;
+                const int64_t e = idx[t * k + s];
+                const float *w1 = W1 + e * d_ff * d, *w3 = swiglu ? W3 + e * d_ff * d : NULL;
+                const float *w2 = W2 + e * d * d_ff;
+                double *a1 = da1 + q * d_ff, *a3 = da3 + q * d_ff, *Hq = Hs + q * d_ff;
+                for (int64_t f = 0; f < d_ff; ++f) {
+                    double u = 0.0, v = 0.0;
+                    for (int64_t j = 0; j < d; ++j) {
+                        u += (double)xt[j] * (double)w1[f * d + j];
+                        if (w3)
+                            v += (double)xt[j] * (double)w3[f * d + j];
+                    }
+                    a1[f] = u; /* pre-activations for now */
+                    a3[f] = v;
+                    Hq[f] = (double)(float)orc_act(act, u, v);
+                }
+                /* E(x_t) (stored fp32 in the forward), dg and dE */
+                double dgs = 0.0;
+                for (int64_t o = 0; o < d; ++o) {
+                    double acc = 0.0;
+                    for (int64_t f = 0; f < d_ff; ++f)
+                        acc += Hq[f] * (double)w2[o * d_ff + f];
+                    dgs += (double)dy[t * d + o] * (double)(float)acc;
+                    dE[q * d + o] = g[t * k + s] * (double)dy[t * d + o];
+                }
+                dg[t * k + s] = dgs;
+                /* dH = W2^T dE, then the activation's derivative */
+                for (int64_t f = 0; f < d_ff; ++f) {
+                    double dH = 0.0;
+                    for (int64_t o = 0; o < d; ++o)
+                        dH += (double)w2[o * d_ff + f] * dE[q * d + o];
+                    const double u = a1[f], v = a3[f];
+                    if (act == ORC_ACT_SWIGLU) {
+                        const double sg = 1.0 / (1.0 + exp(-u));
+                        a1[f] = dH * v * sg * (1.0 + u * (1.0 - sg));
+                        a3[f] = dH * u * sg;
+                    } else if (act == ORC_ACT_GELU) {
+                        const double Phi = 0.5 * (1.0 + erf(u / sqrt(2.0)));
+                        const double phi = exp(-0.5 * u * u) / sqrt(2.0 * acos(-1.0)); /* normal density */
+                        a1[f] = dH * (Phi + u * phi);
+                        a3[f] = 0.0;
+                    } else {
+                        a1[f] = u > 0.0 ? dH : 0.0;
+                        a3[f] = 0.0;
+                    }
+                }
+                /* dx_t += W1^T da1 + W3^T da3 */
+                for (int64_t j = 0; j < d; ++j) {
+                    double acc = 0.0;
+                    for (int64_t f = 0; f < d_ff; ++f) {
+                        acc += a1[f] * (double)w1[f * d + j];
+                        if (w3)
+                            acc += a3[f] * (double)w3[f * d + j];
+                    }
+                    dxd[t * d + j] += acc;
+                }
+            }
+        }
+        /* weight gradients: per expert row, the kept rows in token order */
+#pragma omp parallel for schedule(dynamic, 1)
+        for (int64_t ef = 0; ef < E * d_ff; ++ef) {
+            const int64_t e = ef / d_ff, f = ef - e * d_ff;
+            double *acc1 = (double *)calloc((size_t)d, sizeof(double));
+            double *acc3 = (double *)calloc((size_t)d, sizeof(double));
+            if (!acc1 || !acc3) {
+                free(acc1);
+                free(acc3);
+                continue;
+            }
+            for (int64_t t = 0; t < T; ++t)
+                for (int64_t s = 0; s < k; ++s) {
+                    const int64_t q = pair_of[t * k + s];
+                    if (q < 0 || idx[t * k + s] != e)
+                        continue;
+                    for (int64_t j = 0; j < d; ++j) {
+                        acc1[j] += da1[q * d_ff + f] * (double)x[t * d + j];
+                        acc3[j] += da3[q * d_ff + f] * (double)x[t * d + j];
+                    }
+                }
+            for (int64_t j = 0; j < d; ++j) {
+                dW1[(e * d_ff + f) * d + j] = (float)acc1[j];
+                if (swiglu)
+                    dW3[(e * d_ff + f) * d + j] = (float)acc3[j];
+            }
+            free(acc1);
+            free(acc3);
+        }
+#pragma omp parallel for schedule(dynamic, 1)
+        for (int64_t eo = 0; eo < E * d; ++eo) {
+            const int64_t e = eo / d, o = eo - e * d;
+            double *acc = (double *)calloc((size_t)d_ff, sizeof(double));
+            if (!acc)
+                continue;
+            for (int64_t t = 0; t < T; ++t)
+                for (int64_t s = 0; s < k; ++s) {
+                    const int64_t q = pair_of[t * k + s];
+                    if (q < 0 || idx[t * k + s] != e)
+                        continue;
+                    for (int64_t f = 0; f < d_ff; ++f)
+                        acc[f] += dE[q * d + o] * Hs[q * d_ff + f];
+                }
+            for (int64_t f = 0; f < d_ff; ++f)
+                dW2[(e * d + o) * d_ff + f] = (float)acc[f];
+            free(acc);
+        }
+        free(da1);
+        free(da3);
+        free(Hs);
+        free(dE);
+    }
+    /* router: gates, then the statistics' terms */
+    {
+        double *fsh = (double *)calloc((size_t)E, sizeof(double));
+        if (!fsh)
+            goto out;
+        for (int64_t t = 0; t < T; ++t)
+            fsh[idx[t * k]] += 1.0;
+        for (int64_t i = 0; i < E; ++i)
+            fsh[i] /= (double)T;
+#pragma omp parallel for schedule(static)
+        for (int64_t t = 0; t < T; ++t) {
+            const double *pt = p + t * E;
+            double *dht = dh + t * E;
+            if (gate == ORC_GATE_RENORM) {
+                double dot = 0.0;
+                for (int64_t s = 0; s < k; ++s)
+                    dot += g[t * k + s] * dg[t * k + s];
+                for (int64_t s = 0; s < k; ++s)
+                    dht[idx[t * k + s]] += g[t * k + s] * (dg[t * k + s] - dot);
+            } else {
+                double dot = 0.0;
+                for (int64_t s = 0; s < k; ++s)
+                    dot += pt[idx[t * k + s]] * dg[t * k + s];
+                for (int64_t i = 0; i < E; ++i)
+                    dht[i] -= pt[i] * dot;
+                for (int64_t s = 0; s < k; ++s)
+                    dht[idx[t * k + s]] += pt[idx[t * k + s]] * dg[t * k + s];
+            }
+            if (alpha_aux != 0.0) {
+                double dot = 0.0;
+                for (int64_t i = 0; i < E; ++i)
+                    dot += pt[i] * ((double)E * fsh[i] / (double)T);
+                for (int64_t i = 0; i < E; ++i)
+                    dht[i] += alpha_aux * pt[i] * ((double)E * fsh[i] / (double)T - dot);
+            }
+            if (alpha_z != 0.0)
+                for (int64_t i = 0; i < E; ++i)
+                    dht[i] += alpha_z * 2.0 / (double)T * lse[t] * pt[i];
+            for (int64_t j = 0; j < d; ++j) {
+                double acc = 0.0;
+                for (int64_t i = 0; i < E; ++i)
+                    acc += dht[i] * (double)Wr[i * d + j];
+                dxd[t * d + j] += acc;
+            }
+        }
+        free(fsh);
+    }
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < E; ++i) {
+        for (int64_t j = 0; j < d; ++j) {
+            double acc = 0.0;
+            for (int64_t t = 0; t < T; ++t)
+                acc += dh[t * E + i] * (double)x[t * d + j];
+            dWr[i * d + j] = (float)acc;
+        }
+        if (dbias) {
+            double acc = 0.0;
+            for (int64_t t = 0; t < T; ++t)
+                acc += dh[t * E + i];
+            dbias[i] = (float)acc;
+        }
+    }
+    for (int64_t i = 0; i < T * d; ++i)
+        dx[i] = (float)dxd[i];
+    rc = 0;
+out:
+    free(h);
+    free(idx);
+    free(g);
+    free(p);
+    free(lse);
+    free(dg);
+    free(dh);
+    free(dxd);
+    free(pair_of);
+    return rc;
+}
+
 #ifdef _OPENMP
 #include <omp.h>
 #endif

@@ -1,5 +1,6 @@
 """Plant plausible mistakes in copies of the oracle source (on the CPU) and
-check that the pins in test_oracle_pins.py catch every one of them.
+check that the pins in test_oracle_pins.py and test_oracle_backward.py catch
+every one of them.
 
 Each mutant is one textual change of moe_oracle.c; the copy is compiled to
 a temporary library and the pin suite runs against it in a subprocess.
@@ -43,6 +44,16 @@ MUTANTS = {
     "e4m3 scale from 447": ("float si = amax / 448.0f;", "float si = amax / 447.0f;"),
     "up scale of W1 applied from W3's rows": ("a1[u] *= (double)S1[e * d_ff + f0 + u];", "a1[u] *= (double)S3[e * d_ff + f0 + u];"),
     "down scale of the block's first row for every row": ("acc[u] * (double)S2[e * d + o0 + u]", "acc[u] * (double)S2[e * d + o0]"),
+    "SwiGLU derivative without the (1 + a(1 - s)) factor":
+        ("a1[f] = dH * v * sg * (1.0 + u * (1.0 - sg));", "a1[f] = dH * v * sg;"),
+    "GELU derivative without a * phi": ("a1[f] = dH * (Phi + u * phi);", "a1[f] = dH * Phi;"),
+    "expert output gradient not gated": ("dE[q * d + o] = g[t * k + s] * (double)dy[t * d + o];",
+                                         "dE[q * d + o] = (double)dy[t * d + o];"),
+    "Switch gate gradient without the softmax's coupling": ("dht[i] -= pt[i] * dot;", "dht[i] -= 0.0 * dot;"),
+    "aux gradient without the factor E":
+        ("dht[i] += alpha_aux * pt[i] * ((double)E * fsh[i] / (double)T - dot);",
+         "dht[i] += alpha_aux * pt[i] * (fsh[i] / (double)T - dot);"),
+    "z gradient without the factor 2": ("alpha_z * 2.0 / (double)T", "alpha_z * 1.0 / (double)T"),
     "f counts the last slot": ("f[idx[t * k]] += 1.0;", "f[idx[t * k + k - 1]] += 1.0;"),
     "z not squared": ("zz += lse[t] * lse[t];", "zz += lse[t];"),
     "lse drops the max shift": ("lse[t] = m + log(s);", "lse[t] = log(s);"),
@@ -62,6 +73,7 @@ def test_pins_catch_planted_mistake(name, tmp_path):
                     str(mut), "-o", str(lib), "-lm"], check=True)
     env = dict(os.environ, MOE_ORACLE_LIB=str(lib), OMP_NUM_THREADS="2")
     r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
-                        os.path.join(ROOT, "tests", "test_oracle_pins.py")],
+                        os.path.join(ROOT, "tests", "test_oracle_pins.py"),
+                        os.path.join(ROOT, "tests", "test_oracle_backward.py")],
                        cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
     assert r.returncode != 0, f"pins did not catch: {name}\n{r.stdout[-2000:]}"
