@@ -378,6 +378,41 @@ int moe_forward_fp8(const moe_desc *desc, const void *x, const float *W_r, const
                     int32_t *row_of_slot, int32_t *token_of_row, uint8_t *dropped, float *stats,
                     void *ws, size_t ws_bytes, void *stream);
 
+/* ---- backward (training gradients) -------------------------------------------
+ *
+ * Page "Mixture of experts", Mechanics: the top-k choice is discrete, but
+ * the gate values are differentiable, which is how the router learns
+ * ("Replacing the feed-forward block"); "The load-balancing loss": with f_i
+ * a count, d aux / d P_i = E f_i; the z statistic is mean_t lse_t^2.
+ * moe_backward gives the gradients of
+ *     L = sum_t <dy_t, y_t> + alpha_aux * aux + alpha_z * z
+ * with respect to x, W_r, the router bias and the expert weights, for the
+ * routing moe_forward took (held fixed: pass its topk_idx, gates, offsets,
+ * row_of_slot, token_of_row and stats, with the same x, weights, bias and
+ * noise).  The expert activations are recomputed (nothing else of the
+ * forward is needed).  bf16 layers only (MOE_ERR_UNSUPPORTED otherwise).
+ *   dy     [T][d]          bf16   gradient of the layer output
+ *   dx     [T][d]          fp32
+ *   dW_r   [E][d]          fp32
+ *   dbias  [E]             fp32   optional (requires bias)
+ *   dW1, dW3 [E][d_ff][d]  fp32   (dW3 exactly for SwiGLU)
+ *   dW2    [E][d][d_ff]    fp32
+ * Every gradient is written in full (an expert without rows gets zeros);
+ * sums run in a fixed order, so results are reproducible.  Internally the
+ * weights are transposed into the workspace once per call, the expert
+ * GEMMs use the forward's grouped GEMM kernels, and the weight gradients a
+ * GEMM over each expert's row block.  ws: moe_backward_workspace_size().
+ */
+int moe_backward_workspace_size(const moe_desc *desc, size_t *bytes);
+
+int moe_backward(const moe_desc *desc, const void *x, const float *W_r, const float *bias,
+                 const float *noise, const void *W1, const void *W3, const void *W2,
+                 const int32_t *topk_idx, const float *gates, const int32_t *offsets,
+                 const int32_t *row_of_slot, const int32_t *token_of_row, const float *stats,
+                 const void *dy, float alpha_aux, float alpha_z, float *dx, float *dW_r,
+                 float *dbias, float *dW1, float *dW3, float *dW2, void *ws, size_t ws_bytes,
+                 void *stream);
+
 /* A static, human-readable name for a status code. */
 const char *moe_status_string(int status);
 

@@ -10,7 +10,8 @@ Names match the ABI: moe_workspace_size, moe_capacity, moe_route,
 moe_dispatch, moe_expert_ffn, moe_combine, moe_forward, and for shared
 experts plus the block residual moe_workspace_size_shared, moe_shared_ffn,
 moe_combine_shared, moe_forward_shared, and for E4M3 expert weights
-moe_quantize_e4m3, moe_expert_ffn_fp8, moe_forward_fp8.
+moe_quantize_e4m3, moe_expert_ffn_fp8, moe_forward_fp8, and for training
+moe_backward_workspace_size, moe_backward.
 """
 from __future__ import annotations
 
@@ -107,12 +108,14 @@ def load(build_if_missing: bool = True):
     lib.moe_quantize_e4m3.argtypes = [ctypes.c_int32, P, ctypes.c_int64, ctypes.c_int64, P, P, P]
     lib.moe_expert_ffn_fp8.argtypes = [D, P, P, F8, P, P, sz, P]
     lib.moe_forward_fp8.argtypes = [D, P, P, P, P, F8, P, P, P, P, P, P, P, P, P, P, P, sz, P]
+    lib.moe_backward_workspace_size.argtypes = [D, ctypes.POINTER(ctypes.c_size_t)]
+    lib.moe_backward.argtypes = [D] + [P] * 14 + [ctypes.c_float, ctypes.c_float] + [P] * 7 + [sz, P]
     lib.moe_status_string.argtypes = [ctypes.c_int]
     lib.moe_status_string.restype = ctypes.c_char_p
     for fn in ("moe_workspace_size", "moe_capacity", "moe_route", "moe_dispatch",
                "moe_expert_ffn", "moe_combine", "moe_forward", "moe_workspace_size_shared",
                "moe_shared_ffn", "moe_combine_shared", "moe_forward_shared", "moe_quantize_e4m3",
-               "moe_expert_ffn_fp8", "moe_forward_fp8"):
+               "moe_expert_ffn_fp8", "moe_forward_fp8", "moe_backward_workspace_size", "moe_backward"):
         getattr(lib, fn).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -382,6 +385,56 @@ def moe_forward_fp8(desc, fp8: MoeFp8Experts, x, W_r, bias, noise, y, ws, topk_i
         _ptr(stats, torch.float32, (2 * E + 2,), "stats", True),
         _ptr(ws, torch.uint8, None, "ws"), ws.numel(), _stream(stream))
     _check("moe_forward_fp8", rc)
+
+
+def moe_backward_workspace_size(desc: MoeDesc) -> int:
+    n = ctypes.c_size_t(0)
+    _check("moe_backward_workspace_size",
+           load().moe_backward_workspace_size(ctypes.byref(desc), ctypes.byref(n)))
+    return n.value
+
+
+def backward_workspace(desc: MoeDesc, device="cuda") -> torch.Tensor:
+    return torch.empty(max(moe_backward_workspace_size(desc), 1), dtype=torch.uint8, device=device)
+
+
+def alloc_grads(desc, bias=False, device="cuda") -> dict:
+    T, d, d_ff, E = desc.T, desc.d, desc.d_ff, desc.E
+    f32 = dict(dtype=torch.float32, device=device)
+    return dict(dx=torch.empty((T, d), **f32), dW_r=torch.empty((E, d), **f32),
+                dbias=torch.empty((E,), **f32) if bias else None,
+                dW1=torch.empty((E, d_ff, d), **f32),
+                dW3=torch.empty((E, d_ff, d), **f32) if desc.act == ACT["swiglu"] else None,
+                dW2=torch.empty((E, d, d_ff), **f32))
+
+
+def moe_backward(desc, x, W_r, bias, noise, W1, W3, W2, fwd: dict, dy, grads: dict, ws,
+                 alpha_aux=0.0, alpha_z=0.0, stream=None):
+    """Gradients for the routing of a moe_forward call whose outputs are in
+    ``fwd`` (topk_idx, gates, offsets, row_of_slot, token_of_row, stats)."""
+    T, d, d_ff, E, k = desc.T, desc.d, desc.d_ff, desc.E, desc.k
+    dt = _act_dtype(desc)
+    rc = load().moe_backward(
+        ctypes.byref(desc), _ptr(x, dt, (T, d), "x"), _ptr(W_r, torch.float32, (E, d), "W_r"),
+        _ptr(bias, torch.float32, (E,), "bias", True),
+        _ptr(noise, torch.float32, (T, E), "noise", True),
+        _ptr(W1, dt, (E, d_ff, d), "W1"), _ptr(W3, dt, (E, d_ff, d), "W3", True),
+        _ptr(W2, dt, (E, d, d_ff), "W2"),
+        _ptr(fwd["topk_idx"], torch.int32, (T, k), "topk_idx"),
+        _ptr(fwd["gates"], torch.float32, (T, k), "gates"),
+        _ptr(fwd["offsets"], torch.int32, (E + 1,), "offsets"),
+        _ptr(fwd["row_of_slot"], torch.int32, (T, k), "row_of_slot"),
+        _ptr(fwd["token_of_row"], torch.int32, (T * k,), "token_of_row"),
+        _ptr(fwd["stats"], torch.float32, (2 * E + 2,), "stats"),
+        _ptr(dy, dt, (T, d), "dy"), float(alpha_aux), float(alpha_z),
+        _ptr(grads["dx"], torch.float32, (T, d), "dx"),
+        _ptr(grads["dW_r"], torch.float32, (E, d), "dW_r"),
+        _ptr(grads.get("dbias"), torch.float32, (E,), "dbias", True),
+        _ptr(grads["dW1"], torch.float32, (E, d_ff, d), "dW1"),
+        _ptr(grads.get("dW3"), torch.float32, (E, d_ff, d), "dW3", True),
+        _ptr(grads["dW2"], torch.float32, (E, d, d_ff), "dW2"),
+        _ptr(ws, torch.uint8, None, "ws"), ws.numel(), _stream(stream))
+    _check("moe_backward", rc)
 
 
 def status_string(code: int) -> str:

@@ -1,0 +1,437 @@
+// backward.hip -- the layer's backward (training gradients).
+//
+// Page "Mixture of experts" (rayaq.ca), Mechanics: the top-k choice is
+// discrete, the gate values are differentiable, and that is how the router
+// learns ("Replacing the feed-forward block"); the load-balancing loss
+// aux = E sum f_i P_i has d aux / d P_i = E f_i, f being a count ("The
+// load-balancing loss"); the z statistic is mean lse^2.  The routing of
+// the forward (top-k indices, gates, capacity drops, the permutation) is
+// an input and is held fixed.
+//
+// The expert part runs through the forward's grouped GEMM launchers
+// (C = A B^T over the ragged per-expert row blocks), so every operand must
+// be K-contiguous: the weights are transposed once per call (W2 to
+// [E][d_ff][d]; W1 and W3 side by side to [E][d][n_up d_ff]).  The kernels
+// here:
+//   transpose_kernel       64 x 64 tiles through LDS, batched, any strides
+//   act_fwd_kernel         H = act(a1, a3) from the recomputed pre-activations
+//   combine_bwd_kernel     per kept row: dE = g dy_t (bf16), dg = <dy_t, E(x_t)>
+//   act_bwd_kernel         dA = [da1 | da3] from dH and the pre-activations
+//   logits_kernel          p = softmax(W_r x + b + n), lse (fp32)
+//   router_bwd_kernel      dh_t from dg (gate convention), aux and z terms
+//   dx_kernel              dx_t = sum over kept slots of dX_perm + W_r^T dh_t
+//   dwr_kernel, dbias_kernel   dW_r = sum_t dh_t x_t^T, db = sum_t dh_t
+//   wgrad_kernel           weight gradients: per expert, C = P^T Q over its
+//                          rows (a GEMM whose K range is the expert's row
+//                          block, read from the device offsets), bf16
+//                          operands transposed to K-contiguous rows, fp32 out
+// Every sum has a fixed order (no atomics); results are reproducible.
+#include "moe_internal.h"
+
+namespace moe {
+
+namespace {
+
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ float wave_sum_f32(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+    return v;
+}
+
+__device__ __forceinline__ float wave_max_f32b(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+    return v;
+}
+
+// dst[b][c][r] = src[b][r][c] for r < R, c < C (bf16); strides in elements
+__global__ __launch_bounds__(256) void transpose_kernel(const uint16_t *__restrict__ src, int64_t R,
+                                                        int64_t C, int64_t lds, int64_t sbs,
+                                                        uint16_t *__restrict__ dst, int64_t ldd,
+                                                        int64_t dbs) {
+    __shared__ uint16_t tile[64][65];
+    const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+    const int64_t c0 = (int64_t)blockIdx.x * 64, r0 = (int64_t)blockIdx.y * 64;
+    const uint16_t *s = src + (int64_t)blockIdx.z * sbs;
+    uint16_t *d = dst + (int64_t)blockIdx.z * dbs;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const int64_t r = r0 + ty + 4 * i, c = c0 + tx;
+        tile[ty + 4 * i][tx] = (r < R && c < C) ? s[r * lds + c] : (uint16_t)0;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const int64_t c = c0 + ty + 4 * i, r = r0 + tx;
+        if (r < R && c < C) d[c * ldd + r] = tile[tx][ty + 4 * i];
+    }
+}
+
+// H[r][f] = act(a1, a3) for the kept rows (r < offsets[E])
+__global__ __launch_bounds__(256) void act_fwd_kernel(const float *__restrict__ a1,
+                                                      const float *__restrict__ a3,
+                                                      const int32_t *__restrict__ offsets, int E,
+                                                      int d_ff, int act, uint16_t *__restrict__ H) {
+    const int64_t n = (int64_t)offsets[E] * d_ff;
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
+        const float v = apply_act(act, a1[i], act == ACT_SWIGLU ? a3[i] : 0.f);
+        H[i] = f32_to_bf16(v);
+    }
+}
+
+// one wave per kept row: its token and slot, dE = g dy_t, dg = <dy_t, Y_r>
+__global__ __launch_bounds__(256) void combine_bwd_kernel(
+    const uint16_t *__restrict__ dy, const float *__restrict__ Y, const int32_t *__restrict__ token_of_row,
+    const int32_t *__restrict__ row_of_slot, const float *__restrict__ gates,
+    const int32_t *__restrict__ offsets, int E, int k, int d, uint16_t *__restrict__ dE,
+    float *__restrict__ dg) {
+    const int lane = threadIdx.x & 63;
+    const int rows = offsets[E];
+    for (int r = blockIdx.x * 4 + (threadIdx.x >> 6); r < rows; r += gridDim.x * 4) {
+        const int t = token_of_row[r];
+        int s = 0;
+        for (int q = 0; q < k; ++q)
+            if (row_of_slot[(int64_t)t * k + q] == r) s = q;
+        const float g = gates[(int64_t)t * k + s];
+        float dot = 0.f;
+        for (int o = lane; o < d; o += 64) {
+            const float v = bf16_to_f32(dy[(int64_t)t * d + o]);
+            dot = fmaf(v, Y[(int64_t)r * d + o], dot);
+            dE[(int64_t)r * d + o] = f32_to_bf16(g * v);
+        }
+        dot = wave_sum_f32(dot);
+        if (lane == 0) dg[(int64_t)t * k + s] = dot;
+    }
+}
+
+// dA[r] = [da1 | da3] (bf16; width n_up * d_ff) from dH and the pre-activations
+__global__ __launch_bounds__(256) void act_bwd_kernel(const float *__restrict__ a1,
+                                                      const float *__restrict__ a3,
+                                                      const float *__restrict__ dH,
+                                                      const int32_t *__restrict__ offsets, int E,
+                                                      int d_ff, int act, uint16_t *__restrict__ dA) {
+    const int64_t n = (int64_t)offsets[E] * d_ff;
+    const int nup = act == ACT_SWIGLU ? 2 : 1;
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
+        const int64_t r = i / d_ff, f = i - r * d_ff;
+        const float u = a1[i], g = dH[i];
+        uint16_t *row = dA + r * nup * d_ff;
+        if (act == ACT_SWIGLU) {
+            const float v = a3[i];
+            const float sg = 1.f / (1.f + expf(-u));
+            row[f] = f32_to_bf16(g * v * sg * (1.f + u * (1.f - sg)));
+            row[d_ff + f] = f32_to_bf16(g * u * sg);
+        } else if (act == ACT_GELU) {
+            const float Phi = 0.5f * (1.f + erff(u * 0.70710678118654752f));
+            const float phi = expf(-0.5f * u * u) * 0.39894228040143268f;
+            row[f] = f32_to_bf16(g * (Phi + u * phi));
+        } else {
+            row[f] = f32_to_bf16(u > 0.f ? g : 0.f);
+        }
+    }
+}
+
+// one wave per token: logits in fp32 (lane i: experts i, i + 64), softmax, lse
+__global__ __launch_bounds__(256) void logits_kernel(const uint16_t *__restrict__ x,
+                                                     const float *__restrict__ Wr,
+                                                     const float *__restrict__ bias,
+                                                     const float *__restrict__ noise, int T, int d,
+                                                     int E, float *__restrict__ p,
+                                                     float *__restrict__ lse) {
+    const int lane = threadIdx.x & 63;
+    for (int t = blockIdx.x * 4 + (threadIdx.x >> 6); t < T; t += gridDim.x * 4) {
+        float h0 = -INFINITY, h1 = -INFINITY;
+        for (int i = 0; i < E; ++i) {
+            float acc = 0.f;
+            for (int j = lane; j < d; j += 64)
+                acc = fmaf(bf16_to_f32(x[(int64_t)t * d + j]), Wr[(int64_t)i * d + j], acc);
+            acc = wave_sum_f32(acc);
+            if (bias) acc += bias[i];
+            if (noise) acc += noise[(int64_t)t * E + i];
+            if (i == lane) h0 = acc;
+            if (i == lane + 64) h1 = acc;
+        }
+        const float m = wave_max_f32b(fmaxf(h0, h1));
+        const float e0 = lane < E ? expf(h0 - m) : 0.f;
+        const float e1 = lane + 64 < E ? expf(h1 - m) : 0.f;
+        const float sum = wave_sum_f32(e0 + e1);
+        if (lane < E) p[(int64_t)t * E + lane] = e0 / sum;
+        if (lane + 64 < E) p[(int64_t)t * E + lane + 64] = e1 / sum;
+        if (lane == 0) lse[t] = m + logf(sum);
+    }
+}
+
+// one wave per token: dh from the gate convention, then the aux and z terms
+__global__ __launch_bounds__(256) void router_bwd_kernel(
+    const float *__restrict__ p, const float *__restrict__ lse, const int32_t *__restrict__ topk_idx,
+    const float *__restrict__ gates, const float *__restrict__ dg, const int32_t *__restrict__ row_of_slot,
+    const float *__restrict__ f, int T, int E, int k, int gate, float alpha_aux, float alpha_z,
+    float *__restrict__ dh) {
+    const int lane = threadIdx.x & 63;
+    for (int t = blockIdx.x * 4 + (threadIdx.x >> 6); t < T; t += gridDim.x * 4) {
+        const float *pt = p + (int64_t)t * E;
+        const float p0 = lane < E ? pt[lane] : 0.f, p1 = lane + 64 < E ? pt[lane + 64] : 0.f;
+        float d0 = 0.f, d1 = 0.f;
+        // <g, dg> (renormalised) or <p_sel, dg> (Switch), in slot order
+        float dot = 0.f;
+        for (int s = 0; s < k; ++s) {
+            const int64_t q = (int64_t)t * k + s;
+            const float dgs = row_of_slot[q] >= 0 ? dg[q] : 0.f;
+            const int e = topk_idx[q];
+            dot += (gate == 0 ? gates[q] : pt[e]) * dgs;
+        }
+        for (int s = 0; s < k; ++s) {
+            const int64_t q = (int64_t)t * k + s;
+            const float dgs = row_of_slot[q] >= 0 ? dg[q] : 0.f;
+            const int e = topk_idx[q];
+            if (gate == 0) {
+                const float v = gates[q] * (dgs - dot);
+                if (e == lane) d0 += v;
+                if (e == lane + 64) d1 += v;
+            } else {
+                if (e == lane) d0 += p0 * dgs;
+                if (e == lane + 64) d1 += p1 * dgs;
+            }
+        }
+        if (gate != 0) {
+            d0 -= p0 * dot;
+            d1 -= p1 * dot;
+        }
+        if (alpha_aux != 0.f) {
+            const float a0 = lane < E ? (float)E * f[lane] / (float)T : 0.f;
+            const float a1 = lane + 64 < E ? (float)E * f[lane + 64] / (float)T : 0.f;
+            const float pa = wave_sum_f32(p0 * a0 + p1 * a1);
+            d0 += alpha_aux * p0 * (a0 - pa);
+            d1 += alpha_aux * p1 * (a1 - pa);
+        }
+        if (alpha_z != 0.f) {
+            const float c = alpha_z * 2.f / (float)T * lse[t];
+            d0 += c * p0;
+            d1 += c * p1;
+        }
+        if (lane < E) dh[(int64_t)t * E + lane] = d0;
+        if (lane + 64 < E) dh[(int64_t)t * E + lane + 64] = d1;
+    }
+}
+
+// dx[t] = sum over kept slots (slot order) of dXp[row] + W_r^T dh_t (fp32)
+__global__ __launch_bounds__(256) void dx_kernel(const float *__restrict__ dXp,
+                                                 const int32_t *__restrict__ row_of_slot,
+                                                 const float *__restrict__ dh,
+                                                 const float *__restrict__ Wr, int T, int d, int E,
+                                                 int k, float *__restrict__ dx) {
+    const int lane = threadIdx.x & 63;
+    for (int t = blockIdx.x * 4 + (threadIdx.x >> 6); t < T; t += gridDim.x * 4) {
+        for (int j = lane; j < d; j += 64) {
+            float acc = 0.f;
+            for (int s = 0; s < k; ++s) {
+                const int r = row_of_slot[(int64_t)t * k + s];
+                if (r >= 0) acc += dXp[(int64_t)r * d + j];
+            }
+            float racc = 0.f;
+            for (int i = 0; i < E; ++i) racc = fmaf(dh[(int64_t)t * E + i], Wr[(int64_t)i * d + j], racc);
+            dx[(int64_t)t * d + j] = acc + racc;
+        }
+    }
+}
+
+// dW_r[i][j] = sum_t dh[t][i] x[t][j]: a thread per column j, 16 experts per
+// pass, tokens in order
+constexpr int DWR_EG = 16;
+__global__ __launch_bounds__(256) void dwr_kernel(const float *__restrict__ dh,
+                                                  const uint16_t *__restrict__ x, int T, int d, int E,
+                                                  float *__restrict__ dWr) {
+    const int j = blockIdx.x * 256 + threadIdx.x;
+    const int i0 = blockIdx.y * DWR_EG;
+    if (j >= d) return;
+    float acc[DWR_EG];
+#pragma unroll
+    for (int u = 0; u < DWR_EG; ++u) acc[u] = 0.f;
+    for (int t = 0; t < T; ++t) {
+        const float xv = bf16_to_f32(x[(int64_t)t * d + j]);
+#pragma unroll
+        for (int u = 0; u < DWR_EG; ++u)
+            if (i0 + u < E) acc[u] = fmaf(dh[(int64_t)t * E + i0 + u], xv, acc[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < DWR_EG; ++u)
+        if (i0 + u < E) dWr[(int64_t)(i0 + u) * d + j] = acc[u];
+}
+
+// dbias[i] = sum_t dh[t][i]: one block per expert, 256 strided partials
+// added in thread order
+__global__ __launch_bounds__(256) void dbias_kernel(const float *__restrict__ dh, int T, int E,
+                                                    float *__restrict__ dbias) {
+    __shared__ float part[256];
+    const int i = blockIdx.x;
+    float acc = 0.f;
+    for (int t = threadIdx.x; t < T; t += 256) acc += dh[(int64_t)t * E + i];
+    part[threadIdx.x] = acc;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        float s = 0.f;
+        for (int u = 0; u < 256; ++u) s += part[u];
+        dbias[i] = s;
+    }
+}
+
+// Weight gradients: for expert e, C_e[m][n] = sum over k in [offsets[e],
+// offsets[e+1]) of P[m][k] Q[n][k], P [M][ldk] and Q [N][ldk] bf16
+// (k-contiguous; the transposed activations), C [E][M][N] fp32.  128 x 128
+// tiles, four waves of 64 x 64 on v_mfma_f32_32x32x16_bf16, 32-wide k
+// chunks staged in LDS; the chunk start is aligned down to 8 elements and
+// elements outside the expert's range are zeroed.  An expert without rows
+// gets zeros.
+constexpr int WG_BK = 32, WG_LD = WG_BK + 8;
+__global__ __launch_bounds__(256) void wgrad_kernel(const uint16_t *__restrict__ P,
+                                                    const uint16_t *__restrict__ Q, int64_t ldk,
+                                                    const int32_t *__restrict__ offsets, int M, int N,
+                                                    float *__restrict__ C) {
+    __shared__ __attribute__((aligned(16))) uint16_t As[128][WG_LD];
+    __shared__ __attribute__((aligned(16))) uint16_t Bs[128][WG_LD];
+    const int tm = (M + 127) / 128, tn = (N + 127) / 128;
+    const int e = blockIdx.x / (tm * tn);
+    const int rem = blockIdx.x - e * tm * tn;
+    const int m0 = (rem / tn) * 128, n0 = (rem % tn) * 128;
+    const int k0 = offsets[e], k1 = offsets[e + 1];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int wm = wave >> 1, wn = wave & 1, lr = lane & 31, lh = lane >> 5;
+    f32x16_t acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+    for (int kb = k0 & ~7; kb < k1; kb += WG_BK) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int c = threadIdx.x + h * 256;  // 512 chunks of 8 per operand
+            const int row = c >> 2, kc = (c & 3) * 8;
+            const int kg = kb + kc;
+            uint4 va = make_uint4(0, 0, 0, 0), vb = make_uint4(0, 0, 0, 0);
+            if (kg < k1) {
+                if (m0 + row < M) va = *(const uint4 *)(P + (int64_t)(m0 + row) * ldk + kg);
+                if (n0 + row < N) vb = *(const uint4 *)(Q + (int64_t)(n0 + row) * ldk + kg);
+                if (kg < k0 || kg + 8 > k1) {
+                    uint16_t *ea = (uint16_t *)&va, *eb = (uint16_t *)&vb;
+#pragma unroll
+                    for (int u = 0; u < 8; ++u)
+                        if (kg + u < k0 || kg + u >= k1) {
+                            ea[u] = 0;
+                            eb[u] = 0;
+                        }
+                }
+            }
+            *(uint4 *)&As[row][kc] = va;
+            *(uint4 *)&Bs[row][kc] = vb;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int kk = 0; kk < WG_BK / 16; ++kk) {
+            bf16x8_t a[2], b[2];
+#pragma unroll
+            for (int i = 0; i < 2; ++i) a[i] = *(const bf16x8_t *)&As[wm * 64 + i * 32 + lr][kk * 16 + lh * 8];
+#pragma unroll
+            for (int j = 0; j < 2; ++j) b[j] = *(const bf16x8_t *)&Bs[wn * 64 + j * 32 + lr][kk * 16 + lh * 8];
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+        }
+        __syncthreads();
+    }
+    float *Ce = C + (int64_t)e * M * N;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int col = n0 + wn * 64 + j * 32 + lr;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int row = m0 + wm * 64 + i * 32 + (r >> 2) * 8 + lh * 4 + (r & 3);
+                if (row < M && col < N) Ce[(int64_t)row * N + col] = acc[i][j][r];
+            }
+        }
+}
+
+inline unsigned grid_for(int64_t items, int64_t per_block, int64_t cap) {
+    int64_t b = (items + per_block - 1) / per_block;
+    if (b > cap) b = cap;
+    return (unsigned)(b < 1 ? 1 : b);
+}
+
+}  // namespace
+
+hipError_t launch_transpose_bf16(const void *src, int64_t R, int64_t C, int64_t lds, int64_t sbs,
+                                 void *dst, int64_t ldd, int64_t dbs, int batch, hipStream_t st) {
+    if (R <= 0 || C <= 0 || batch <= 0) return hipSuccess;
+    dim3 grid((unsigned)((C + 63) / 64), (unsigned)((R + 63) / 64), (unsigned)batch);
+    hipLaunchKernelGGL(transpose_kernel, grid, dim3(256), 0, st, (const uint16_t *)src, R, C, lds, sbs,
+                       (uint16_t *)dst, ldd, dbs);
+    return hipGetLastError();
+}
+
+hipError_t launch_act_fwd(const Shape &s, const float *a1, const float *a3, const int32_t *offsets,
+                          void *H, hipStream_t st) {
+    hipLaunchKernelGGL(act_fwd_kernel, dim3(grid_for((int64_t)s.Tk() * s.d_ff, 256, 16384)), dim3(256), 0,
+                       st, a1, a3, offsets, s.E, s.d_ff, s.act, (uint16_t *)H);
+    return hipGetLastError();
+}
+
+hipError_t launch_combine_bwd(const Shape &s, const void *dy, const float *Y, const int32_t *token_of_row,
+                              const int32_t *row_of_slot, const float *gates, const int32_t *offsets,
+                              void *dE, float *dg, hipStream_t st) {
+    hipLaunchKernelGGL(combine_bwd_kernel, dim3(grid_for(s.Tk(), 4, 16384)), dim3(256), 0, st,
+                       (const uint16_t *)dy, Y, token_of_row, row_of_slot, gates, offsets, s.E, s.k, s.d,
+                       (uint16_t *)dE, dg);
+    return hipGetLastError();
+}
+
+hipError_t launch_act_bwd(const Shape &s, const float *a1, const float *a3, const float *dH,
+                          const int32_t *offsets, void *dA, hipStream_t st) {
+    hipLaunchKernelGGL(act_bwd_kernel, dim3(grid_for((int64_t)s.Tk() * s.d_ff, 256, 16384)), dim3(256), 0,
+                       st, a1, a3, dH, offsets, s.E, s.d_ff, s.act, (uint16_t *)dA);
+    return hipGetLastError();
+}
+
+hipError_t launch_router_bwd(const Shape &s, const void *x, const float *Wr, const float *bias,
+                             const float *noise, const int32_t *topk_idx, const float *gates,
+                             const float *dg, const int32_t *row_of_slot, const float *f,
+                             float alpha_aux, float alpha_z, float *p, float *lse, float *dh,
+                             hipStream_t st) {
+    const unsigned g = grid_for(s.T, 4, 16384);
+    hipLaunchKernelGGL(logits_kernel, dim3(g), dim3(256), 0, st, (const uint16_t *)x, Wr, bias, noise, s.T,
+                       s.d, s.E, p, lse);
+    hipLaunchKernelGGL(router_bwd_kernel, dim3(g), dim3(256), 0, st, (const float *)p, (const float *)lse,
+                       topk_idx, gates, dg, row_of_slot, f, s.T, s.E, s.k, s.gate, alpha_aux, alpha_z, dh);
+    return hipGetLastError();
+}
+
+hipError_t launch_dx(const Shape &s, const float *dXp, const int32_t *row_of_slot, const float *dh,
+                     const float *Wr, float *dx, hipStream_t st) {
+    hipLaunchKernelGGL(dx_kernel, dim3(grid_for(s.T, 4, 16384)), dim3(256), 0, st, dXp, row_of_slot, dh, Wr,
+                       s.T, s.d, s.E, s.k, dx);
+    return hipGetLastError();
+}
+
+hipError_t launch_dwr(const Shape &s, const float *dh, const void *x, float *dWr, float *dbias,
+                      hipStream_t st) {
+    dim3 grid((unsigned)((s.d + 255) / 256), (unsigned)((s.E + DWR_EG - 1) / DWR_EG));
+    hipLaunchKernelGGL(dwr_kernel, grid, dim3(256), 0, st, dh, (const uint16_t *)x, s.T, s.d, s.E, dWr);
+    if (dbias) hipLaunchKernelGGL(dbias_kernel, dim3((unsigned)s.E), dim3(256), 0, st, dh, s.T, s.E, dbias);
+    return hipGetLastError();
+}
+
+hipError_t launch_wgrad(int E, int M, int N, const int32_t *offsets, const void *P, const void *Q,
+                        int64_t ldk, float *C, hipStream_t st) {
+    const unsigned blocks = (unsigned)E * (unsigned)((M + 127) / 128) * (unsigned)((N + 127) / 128);
+    hipLaunchKernelGGL(wgrad_kernel, dim3(blocks), dim3(256), 0, st, (const uint16_t *)P, (const uint16_t *)Q,
+                       ldk, offsets, M, N, C);
+    return hipGetLastError();
+}
+
+}  // namespace moe

@@ -300,6 +300,70 @@ int moe_combine(const moe_desc *desc, const float *y_perm, const int32_t *row_of
 
 namespace {
 
+// Workspace of moe_backward (every region 256-byte aligned).  R bounds the
+// kept rows; ldk (R rounded up to 8) is the row length of the transposed
+// activations.
+struct BwdLayout {
+    size_t w2t, wcat;                 // W2 as [E][d_ff][d]; W1 | W3 as [E][d][n_up d_ff]
+    size_t x_perm, a1, a3, H, Y, part2;
+    size_t dE, dg, dH, dA, dXp;
+    size_t dET, HT, dAT, XT;
+    size_t p, lse, dh;
+    size_t total;
+    int64_t R, ldk;
+};
+
+BwdLayout bwd_layout(const Shape &s) {
+    BwdLayout L{};
+    const size_t nup = s.act == MOE_ACT_SWIGLU ? 2 : 1;
+    int64_t R = s.Tk();
+    if (s.C >= 0 && (int64_t)s.E * s.C < R) R = (int64_t)s.E * s.C;
+    L.R = R;
+    L.ldk = (R + 7) / 8 * 8;
+    const size_t r = (size_t)R, lk = (size_t)L.ldk, d = (size_t)s.d, f = (size_t)s.d_ff, E = (size_t)s.E;
+    size_t o = 0;
+    auto take = [&](size_t bytes) {
+        size_t at = o;
+        o = align_up(o + bytes);
+        return at;
+    };
+    L.w2t = take(E * f * d * 2);
+    L.wcat = take(E * d * nup * f * 2);
+    L.x_perm = take(r * d * 2);
+    L.a1 = take(r * f * 4);
+    L.a3 = nup == 2 ? take(r * f * 4) : 0;
+    L.H = take(r * f * 2);
+    L.Y = take(r * d * 4);
+    L.part2 = take(r * (nup * f > d ? nup * f : d) * 4);
+    L.dE = take(r * d * 2);
+    L.dg = take((size_t)s.Tk() * 4);
+    L.dH = take(r * f * 4);
+    L.dA = take(r * nup * f * 2);
+    L.dXp = take(r * d * 4);
+    L.dET = take(d * lk * 2);
+    L.HT = take(f * lk * 2);
+    L.dAT = take(nup * f * lk * 2);
+    L.XT = take(d * lk * 2);
+    L.p = take((size_t)s.T * E * 4);
+    L.lse = take((size_t)s.T * 4);
+    L.dh = take((size_t)s.T * E * 4);
+    L.total = o;
+    return L;
+}
+
+// C = A B^T over the per-expert row blocks with N = n, K = kdim (the
+// forward's down-projection launcher on a re-labelled shape), adding the
+// second K half when it splits K.
+int grouped_gemm_f32(const Shape &s, int n, int kdim, const void *A, const int32_t *offsets,
+                     const void *B, float *C, float *part2, hipStream_t st) {
+    Shape q = s;
+    q.d = n;
+    q.d_ff = kdim;
+    MOE_TRY(moe::launch_expert_down(q, A, offsets, B, C, part2, st));
+    if (moe::down_ksplit(q) == 2) MOE_TRY(moe::launch_add_partial(q, C, part2, offsets, st));
+    return MOE_OK;
+}
+
 // Validates E4M3 expert weights for this description (shape support first).
 int check_fp8(const Shape &s, const moe_fp8_experts *w) {
     if (!w) return MOE_ERR_INVALID_ARG;
@@ -514,6 +578,82 @@ int moe_forward_fp8(const moe_desc *desc, const void *x, const float *W_r, const
     return forward_impl(desc, nullptr, w, x, W_r, bias, noise, nullptr, nullptr, nullptr, y,
                         topk_idx, gates, routed_counts, kept_counts, offsets, row_of_slot,
                         token_of_row, dropped, stats, ws, ws_bytes, stream);
+}
+
+int moe_backward_workspace_size(const moe_desc *desc, size_t *bytes) {
+    Shape s;
+    int rc = check_desc(desc, &s);
+    if (rc != MOE_OK) return rc;
+    if (!bytes) return MOE_ERR_INVALID_ARG;
+    if (s.dtype != MOE_DTYPE_BF16) return MOE_ERR_UNSUPPORTED;
+    *bytes = bwd_layout(s).total;
+    return MOE_OK;
+}
+
+int moe_backward(const moe_desc *desc, const void *x, const float *W_r, const float *bias,
+                 const float *noise, const void *W1, const void *W3, const void *W2,
+                 const int32_t *topk_idx, const float *gates, const int32_t *offsets,
+                 const int32_t *row_of_slot, const int32_t *token_of_row, const float *stats,
+                 const void *dy, float alpha_aux, float alpha_z, float *dx, float *dW_r,
+                 float *dbias, float *dW1, float *dW3, float *dW2, void *ws, size_t ws_bytes,
+                 void *stream) {
+    Shape s;
+    int rc = check_desc(desc, &s);
+    if (rc != MOE_OK) return rc;
+    if (s.dtype != MOE_DTYPE_BF16) return MOE_ERR_UNSUPPORTED;
+    if (!x || !W_r || !W1 || !W2 || !topk_idx || !gates || !offsets || !row_of_slot ||
+        !token_of_row || !stats || !dy || !dx || !dW_r || !dW1 || !dW2 || !ws)
+        return MOE_ERR_INVALID_ARG;
+    const bool swiglu = s.act == MOE_ACT_SWIGLU;
+    if (swiglu != (W3 != nullptr) || swiglu != (dW3 != nullptr)) return MOE_ERR_INVALID_ARG;
+    if (dbias && !bias) return MOE_ERR_INVALID_ARG;
+    if (!std::isfinite(alpha_aux) || !std::isfinite(alpha_z)) return MOE_ERR_INVALID_ARG;
+    const BwdLayout L = bwd_layout(s);
+    if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+    hipStream_t st = (hipStream_t)stream;
+    const int d = s.d, f = s.d_ff, E = s.E, nup = swiglu ? 2 : 1;
+    char *w = (char *)ws;
+    void *w2t = w + L.w2t, *wcat = w + L.wcat, *xp = w + L.x_perm, *H = w + L.H;
+    float *a1 = (float *)(w + L.a1), *a3 = swiglu ? (float *)(w + L.a3) : nullptr;
+    float *Y = (float *)(w + L.Y), *part2 = (float *)(w + L.part2), *dg = (float *)(w + L.dg);
+    float *dH = (float *)(w + L.dH), *dXp = (float *)(w + L.dXp);
+    void *dE = w + L.dE, *dA = w + L.dA;
+    void *dET = w + L.dET, *HT = w + L.HT, *dAT = w + L.dAT, *XT = w + L.XT;
+    float *p = (float *)(w + L.p), *lse = (float *)(w + L.lse), *dh = (float *)(w + L.dh);
+    const int64_t df = (int64_t)d * f;
+
+    // weights as K-contiguous operands of the gradient GEMMs
+    MOE_TRY(moe::launch_transpose_bf16(W2, d, f, f, df, w2t, d, df, E, st));
+    MOE_TRY(moe::launch_transpose_bf16(W1, f, d, d, df, wcat, (int64_t)nup * f, (int64_t)nup * df, E, st));
+    if (swiglu)
+        MOE_TRY(moe::launch_transpose_bf16(W3, f, d, d, df, (char *)wcat + (size_t)f * 2, (int64_t)nup * f,
+                                           (int64_t)nup * df, E, st));
+    // recompute the forward's expert part: x rows, pre-activations, H, E(x)
+    MOE_TRY(moe::launch_gather(s, x, token_of_row, offsets, xp, st));
+    if ((rc = grouped_gemm_f32(s, f, d, xp, offsets, W1, a1, part2, st)) != MOE_OK) return rc;
+    if (swiglu && (rc = grouped_gemm_f32(s, f, d, xp, offsets, W3, a3, part2, st)) != MOE_OK) return rc;
+    MOE_TRY(moe::launch_act_fwd(s, a1, a3, offsets, H, st));
+    if ((rc = grouped_gemm_f32(s, d, f, H, offsets, W2, Y, part2, st)) != MOE_OK) return rc;
+    // combine, down projection and activation backward; dX_perm
+    MOE_TRY(moe::launch_combine_bwd(s, dy, Y, token_of_row, row_of_slot, gates, offsets, dE, dg, st));
+    if ((rc = grouped_gemm_f32(s, f, d, dE, offsets, w2t, dH, part2, st)) != MOE_OK) return rc;
+    MOE_TRY(moe::launch_act_bwd(s, a1, a3, dH, offsets, dA, st));
+    if ((rc = grouped_gemm_f32(s, d, nup * f, dA, offsets, wcat, dXp, part2, st)) != MOE_OK) return rc;
+    // router: gates, load-balancing and z terms; dx, dW_r, dbias
+    MOE_TRY(moe::launch_router_bwd(s, x, W_r, bias, noise, topk_idx, gates, dg, row_of_slot, stats,
+                                   alpha_aux, alpha_z, p, lse, dh, st));
+    MOE_TRY(moe::launch_dx(s, dXp, row_of_slot, dh, W_r, dx, st));
+    MOE_TRY(moe::launch_dwr(s, dh, x, dW_r, dbias, st));
+    // weight gradients over each expert's rows
+    MOE_TRY(moe::launch_transpose_bf16(dE, L.R, d, d, 0, dET, L.ldk, 0, 1, st));
+    MOE_TRY(moe::launch_transpose_bf16(H, L.R, f, f, 0, HT, L.ldk, 0, 1, st));
+    MOE_TRY(moe::launch_transpose_bf16(dA, L.R, (int64_t)nup * f, (int64_t)nup * f, 0, dAT, L.ldk, 0, 1, st));
+    MOE_TRY(moe::launch_transpose_bf16(xp, L.R, d, d, 0, XT, L.ldk, 0, 1, st));
+    MOE_TRY(moe::launch_wgrad(E, d, f, offsets, dET, HT, L.ldk, dW2, st));
+    MOE_TRY(moe::launch_wgrad(E, f, d, offsets, dAT, XT, L.ldk, dW1, st));
+    if (swiglu)
+        MOE_TRY(moe::launch_wgrad(E, f, d, offsets, (char *)dAT + (size_t)f * L.ldk * 2, XT, L.ldk, dW3, st));
+    return MOE_OK;
 }
 
 const char *moe_status_string(int status) {

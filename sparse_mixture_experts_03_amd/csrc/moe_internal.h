@@ -158,6 +158,28 @@ hipError_t launch_expert_up_fp8(const Shape &s, const void *A, const int32_t *a_
 hipError_t launch_expert_down_fp8(const Shape &s, const void *H, const int32_t *offsets,
                                   const uint8_t *W2, const float *S2, float *y_perm, hipStream_t st);
 
+// ---- backward (training gradients) --------------------------------------
+hipError_t launch_transpose_bf16(const void *src, int64_t R, int64_t C, int64_t lds, int64_t sbs,
+                                 void *dst, int64_t ldd, int64_t dbs, int batch, hipStream_t st);
+hipError_t launch_act_fwd(const Shape &s, const float *a1, const float *a3, const int32_t *offsets,
+                          void *H, hipStream_t st);
+hipError_t launch_combine_bwd(const Shape &s, const void *dy, const float *Y, const int32_t *token_of_row,
+                              const int32_t *row_of_slot, const float *gates, const int32_t *offsets,
+                              void *dE, float *dg, hipStream_t st);
+hipError_t launch_act_bwd(const Shape &s, const float *a1, const float *a3, const float *dH,
+                          const int32_t *offsets, void *dA, hipStream_t st);
+hipError_t launch_router_bwd(const Shape &s, const void *x, const float *Wr, const float *bias,
+                             const float *noise, const int32_t *topk_idx, const float *gates,
+                             const float *dg, const int32_t *row_of_slot, const float *f,
+                             float alpha_aux, float alpha_z, float *p, float *lse, float *dh,
+                             hipStream_t st);
+hipError_t launch_dx(const Shape &s, const float *dXp, const int32_t *row_of_slot, const float *dh,
+                     const float *Wr, float *dx, hipStream_t st);
+hipError_t launch_dwr(const Shape &s, const float *dh, const void *x, float *dWr, float *dbias,
+                      hipStream_t st);
+hipError_t launch_wgrad(int E, int M, int N, const int32_t *offsets, const void *P, const void *Q,
+                        int64_t ldk, float *C, hipStream_t st);
+
 // ---- combine -------------------------------------------------------------
 // y_perm_part2: nullptr, or the second K half of a split down projection.
 hipError_t launch_combine(const Shape &s, const float *y_perm, const float *y_perm_part2,

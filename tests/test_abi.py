@@ -232,3 +232,31 @@ def test_header_compiles_as_c_and_links(tmp_path):
     assert r.returncode == 0, r.stderr
     assert r.stdout.startswith("ok ")
     del lib
+
+
+def test_backward_validation_before_launch():
+    lib = B.load()
+    desc = B.make_desc(64, 32, 64, 4, 2, act="swiglu", dtype="bf16")
+    d = ctypes.byref(desc)
+    need = B.moe_backward_workspace_size(desc)
+    assert need > 0
+    args = [FAKE] * 14
+    args[2] = None          # bias
+    args[3] = None          # noise
+    outs = [FAKE, FAKE, None, FAKE, FAKE, FAKE]   # dx, dW_r, dbias, dW1, dW3, dW2
+    call = lambda a, o, n: lib.moe_backward(d, *a, 0.0, 0.0, *o, FAKE, n, None)
+    assert call(args, outs, need - 1) == -4
+    for i in (0, 1, 4, 6, 7, 8, 9, 10, 11, 12, 13):
+        a = list(args)
+        a[i] = None
+        assert call(a, outs, need) == -1, i
+    o = list(outs)
+    o[4] = None              # SwiGLU needs dW3
+    assert call(args, o, need) == -1
+    o = list(outs)
+    o[2] = FAKE              # dbias without a bias
+    assert call(args, o, need) == -1
+    f32 = B.make_desc(64, 32, 64, 4, 2, act="swiglu", dtype="f32")
+    assert lib.moe_backward(ctypes.byref(f32), *args, 0.0, 0.0, *outs, FAKE, need, None) == -2
+    with pytest.raises(B.MoeError):
+        B.moe_backward_workspace_size(f32)
