@@ -36,8 +36,11 @@ host on a bounded sample: routing, dispatch and statistics over all T
 tokens plus the expert FFN and combine on S sampled tokens; tokens/s is
 1 / (t_route / T + t_ffn / S).
 
+--backward times moe_backward (training gradients, routing of one forward
+held fixed) on the workload instead, and prints its own JSON line.
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                       [--no-cpu] [--no-decode]
+                       [--no-cpu] [--no-decode] [--backward]
 """
 import argparse
 import ctypes
@@ -267,6 +270,59 @@ def cpu_baseline(w, seed=0, target_s=22.0):
                        f"and combine on {S} sampled tokens ({t_ffn:.2f}s); fp64 sums")}
 
 
+def run_backward(w, steps, warmup, seed=0):
+    """Times ``steps`` moe_backward calls of workload w (after one forward
+    that fixes the routing); loss weights 0.01 (aux) and 0.001 (z), the
+    page's.  FLOPs: the recomputed expert forward (n_mat GEMMs) plus dgrad
+    (n_mat) and wgrad (n_mat) over the kept rows, and 2 T E d for each of
+    the router's logits, dx and dW_r."""
+    import torch
+    from sparse_mixture_experts_03_amd import binding as B
+    from sparse_mixture_experts_03_amd import synth
+
+    wt = synth.make_weights(w, seed)
+    dw = {k: B.to_device(v, w.dtype) for k, v in wt.items()}
+    del wt
+    tk = synth.make_tokens(w, seed, 0)
+    x, noise = B.to_device(tk["x"], w.dtype), B.to_device(tk["noise"], w.dtype)
+    desc = B.desc_for(w)
+    fwd = B.alloc_outputs(desc)
+    ws = B.workspace(desc)
+    B.moe_forward(desc, x, dw["Wr"], dw["bias"], noise, dw["W1"], dw["W3"], dw["W2"], fwd["y"], ws,
+                  **{k: fwd[k] for k in fwd if k != "y"})
+    del ws
+    dy = B.to_device(synth.to_bf16(np.random.default_rng(seed + 1).standard_normal(
+        (w.T, w.d)).astype(np.float32)), "bf16")
+    grads = B.alloc_grads(desc, bias=dw["bias"] is not None)
+    bws = B.backward_workspace(desc)
+
+    def step():
+        B.moe_backward(desc, x, dw["Wr"], dw["bias"], noise, dw["W1"], dw["W3"], dw["W2"], fwd, dy,
+                       grads, bws, 0.01, 0.001)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    n_kept = int(fwd["kept_counts"].sum().item())
+    n_mat = 3 if w.act == "swiglu" else 2
+    flops = 3 * n_kept * 2.0 * n_mat * w.d * w.d_ff + 3 * 2.0 * w.T * w.E * w.d
+    ms = elapsed * 1e3 / steps
+    tf = flops / (ms * 1e-3) / 1e12
+    return {"metric": "MoE layer backward tokens/s (training gradients)", "value": round(w.T / (ms * 1e-3), 1),
+            "unit": "tokens/s", "n_gpus": 1, "steps": steps, "warmup": warmup,
+            "ms_per_step": round(ms, 4), "higher_is_better": True, "dtype": "bf16",
+            "data": "synthetic",
+            "config": {"workload": w.name, "T": w.T, "d": w.d, "d_ff": w.d_ff, "E": w.E, "k": w.k,
+                       "gate": w.gate, "act": w.act, "capacity_factor": w.cf, "pass": "backward"},
+            "tflops": round(tf, 2), "frac_of_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+            "flops_per_step": flops}
+
+
 def decode_object(wd, rd):
     """Throughput and HBM roofline of a decode workload's run: the expert
     up-projection (weight streaming) against 8 TB/s, algorithmic bytes =
@@ -306,6 +362,8 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=100)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--backward", action="store_true",
+                    help="time moe_backward on the workload instead of the forward")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy three times (a kernel of "
                          "known traffic, to calibrate rocprofv3's FETCH_SIZE/WRITE_SIZE)")
@@ -331,6 +389,9 @@ def main():
         return
     B.load(build_if_missing=False)
     w = synth.WORKLOADS[args.workload]
+    if args.backward:
+        print(json.dumps(run_backward(w, args.steps, args.warmup)), flush=True)
+        return
     if w.steps > 1:
         # a decode workload on its own: fresh tokens every step, HBM roofline
         res = run_workload(w, args.steps, args.warmup, fresh_x_steps=args.steps)

@@ -17,10 +17,13 @@
 //   act_fwd_kernel         H = act(a1, a3) from the recomputed pre-activations
 //   combine_bwd_kernel     per kept row: dE = g dy_t (bf16), dg = <dy_t, E(x_t)>
 //   act_bwd_kernel         dA = [da1 | da3] from dH and the pre-activations
-//   logits_kernel          p = softmax(W_r x + b + n), lse (fp32)
+//   logits_kernel          p = softmax(W_r x + b + n), lse (fp32; 32 tokens
+//                          per block sharing each W_r read)
 //   router_bwd_kernel      dh_t from dg (gate convention), aux and z terms
 //   dx_kernel              dx_t = sum over kept slots of dX_perm + W_r^T dh_t
-//   dwr_kernel, dbias_kernel   dW_r = sum_t dh_t x_t^T, db = sum_t dh_t
+//   dwr_partial_kernel, dwr_reduce_kernel, dbias_kernel
+//                          dW_r = sum_t dh_t x_t^T (token splits, then the
+//                          splits in order), db = sum_t dh_t
 //   wgrad_kernel           weight gradients: per expert, C = P^T Q over its
 //                          rows (a GEMM whose K range is the expert's row
 //                          block, read from the device offsets), bf16
@@ -46,16 +49,46 @@ __device__ __forceinline__ float wave_max_f32b(float v) {
     return v;
 }
 
-// dst[b][c][r] = src[b][r][c] for r < R, c < C (bf16); strides in elements
+// dst[b][c][r] = src[b][r][c] for r < R, c < C (bf16); strides in elements.
+// VEC: 4-element (8-byte) reads along c and writes along r (C, R, the
+// strides and the bases multiples of 4); otherwise one element at a time.
+template <bool VEC>
 __global__ __launch_bounds__(256) void transpose_kernel(const uint16_t *__restrict__ src, int64_t R,
                                                         int64_t C, int64_t lds, int64_t sbs,
                                                         uint16_t *__restrict__ dst, int64_t ldd,
                                                         int64_t dbs) {
-    __shared__ uint16_t tile[64][65];
-    const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+    __shared__ uint16_t tile[64][66];
     const int64_t c0 = (int64_t)blockIdx.x * 64, r0 = (int64_t)blockIdx.y * 64;
     const uint16_t *s = src + (int64_t)blockIdx.z * sbs;
     uint16_t *d = dst + (int64_t)blockIdx.z * dbs;
+    if (VEC) {
+        // 64 rows x 16 groups of 4 = 1024 groups, 4 per thread
+        const int g = threadIdx.x & 15, rr = threadIdx.x >> 4;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int64_t r = r0 + rr + 16 * i, c = c0 + 4 * g;
+            uint2 v = make_uint2(0, 0);
+            if (r < R && c < C) v = *(const uint2 *)(s + r * lds + c);
+            tile[rr + 16 * i][4 * g + 0] = (uint16_t)(v.x & 0xffffu);
+            tile[rr + 16 * i][4 * g + 1] = (uint16_t)(v.x >> 16);
+            tile[rr + 16 * i][4 * g + 2] = (uint16_t)(v.y & 0xffffu);
+            tile[rr + 16 * i][4 * g + 3] = (uint16_t)(v.y >> 16);
+        }
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int cc = rr + 16 * i;
+            const int64_t c = c0 + cc, r = r0 + 4 * g;
+            if (c < C && r < R) {
+                uint2 v;
+                v.x = (uint32_t)tile[4 * g + 0][cc] | ((uint32_t)tile[4 * g + 1][cc] << 16);
+                v.y = (uint32_t)tile[4 * g + 2][cc] | ((uint32_t)tile[4 * g + 3][cc] << 16);
+                *(uint2 *)(d + c * ldd + r) = v;
+            }
+        }
+        return;
+    }
+    const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
         const int64_t r = r0 + ty + 4 * i, c = c0 + tx;
@@ -133,8 +166,9 @@ __global__ __launch_bounds__(256) void act_bwd_kernel(const float *__restrict__ 
     }
 }
 
-// one wave per token: logits in fp32 (lane i: experts i, i + 64), softmax, lse
-__global__ __launch_bounds__(256) void logits_kernel(const uint16_t *__restrict__ x,
+// logits for few experts (E <= 32): one wave per token (lane i: experts i,
+// i + 64), softmax, lse
+__global__ __launch_bounds__(256) void logits_wave_kernel(const uint16_t *__restrict__ x,
                                                      const float *__restrict__ Wr,
                                                      const float *__restrict__ bias,
                                                      const float *__restrict__ noise, int T, int d,
@@ -159,6 +193,62 @@ __global__ __launch_bounds__(256) void logits_kernel(const uint16_t *__restrict_
         const float sum = wave_sum_f32(e0 + e1);
         if (lane < E) p[(int64_t)t * E + lane] = e0 / sum;
         if (lane + 64 < E) p[(int64_t)t * E + lane + 64] = e1 / sum;
+        if (lane == 0) lse[t] = m + logf(sum);
+    }
+}
+
+// logits in fp32, then p = softmax and lse: a block per 32 tokens (8 per
+// wave), their rows of x staged in LDS 1024 columns at a time; lane i
+// accumulates experts i and i + 64 for the wave's 8 tokens, reading its own
+// W_r rows 4 columns at a time, each x value a broadcast from LDS.
+constexpr int LG_TB = 32, LG_TW = 8, LG_DC = 1024;
+__global__ __launch_bounds__(256) void logits_kernel(const uint16_t *__restrict__ x,
+                                                     const float *__restrict__ Wr,
+                                                     const float *__restrict__ bias,
+                                                     const float *__restrict__ noise, int T, int d,
+                                                     int E, float *__restrict__ p,
+                                                     float *__restrict__ lse) {
+    __shared__ float xs[LG_TB][LG_DC + 4];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int t0 = blockIdx.x * LG_TB;
+    const bool e0 = lane < E, e1 = lane + 64 < E;
+    float acc0[LG_TW], acc1[LG_TW];
+#pragma unroll
+    for (int u = 0; u < LG_TW; ++u) acc0[u] = acc1[u] = 0.f;
+    for (int c0 = 0; c0 < d; c0 += LG_DC) {
+        const int cw = min(LG_DC, d - c0);
+        __syncthreads();
+        for (int q = threadIdx.x; q < LG_TB * cw; q += 256) {
+            const int tt = q / cw, j = q - tt * cw;
+            xs[tt][j] = t0 + tt < T ? bf16_to_f32(x[(int64_t)(t0 + tt) * d + c0 + j]) : 0.f;
+        }
+        __syncthreads();
+        const float *w0 = Wr + (int64_t)lane * d + c0, *w1 = Wr + (int64_t)(lane + 64) * d + c0;
+        for (int j = 0; j < cw; j += 4) {
+            float4 a = make_float4(0.f, 0.f, 0.f, 0.f), b = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (e0) a = *(const float4 *)(w0 + j);
+            if (e1) b = *(const float4 *)(w1 + j);
+#pragma unroll
+            for (int u = 0; u < LG_TW; ++u) {
+                const float *xr = &xs[wave * LG_TW + u][j];
+                acc0[u] = fmaf(xr[0], a.x, fmaf(xr[1], a.y, fmaf(xr[2], a.z, fmaf(xr[3], a.w, acc0[u]))));
+                acc1[u] = fmaf(xr[0], b.x, fmaf(xr[1], b.y, fmaf(xr[2], b.z, fmaf(xr[3], b.w, acc1[u]))));
+            }
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < LG_TW; ++u) {
+        const int t = t0 + wave * LG_TW + u;
+        if (t >= T) break;
+        float h0 = -INFINITY, h1 = -INFINITY;
+        if (e0) h0 = acc0[u] + (bias ? bias[lane] : 0.f) + (noise ? noise[(int64_t)t * E + lane] : 0.f);
+        if (e1) h1 = acc1[u] + (bias ? bias[lane + 64] : 0.f) + (noise ? noise[(int64_t)t * E + lane + 64] : 0.f);
+        const float m = wave_max_f32b(fmaxf(h0, h1));
+        const float x0 = e0 ? expf(h0 - m) : 0.f;
+        const float x1 = e1 ? expf(h1 - m) : 0.f;
+        const float sum = wave_sum_f32(x0 + x1);
+        if (e0) p[(int64_t)t * E + lane] = x0 / sum;
+        if (e1) p[(int64_t)t * E + lane + 64] = x1 / sum;
         if (lane == 0) lse[t] = m + logf(sum);
     }
 }
@@ -216,40 +306,62 @@ __global__ __launch_bounds__(256) void router_bwd_kernel(
     }
 }
 
-// dx[t] = sum over kept slots (slot order) of dXp[row] + W_r^T dh_t (fp32)
+// dx[t] = sum over kept slots (slot order) of dXp[row] + W_r^T dh_t (fp32):
+// a block per 16 tokens with their dh rows in LDS; a thread per column j
+// reads W_r[i][j] once for the 16 tokens
+constexpr int DX_TT = 16;
 __global__ __launch_bounds__(256) void dx_kernel(const float *__restrict__ dXp,
                                                  const int32_t *__restrict__ row_of_slot,
                                                  const float *__restrict__ dh,
                                                  const float *__restrict__ Wr, int T, int d, int E,
                                                  int k, float *__restrict__ dx) {
-    const int lane = threadIdx.x & 63;
-    for (int t = blockIdx.x * 4 + (threadIdx.x >> 6); t < T; t += gridDim.x * 4) {
-        for (int j = lane; j < d; j += 64) {
+    __shared__ float dhs[DX_TT][128];
+    const int t0 = blockIdx.x * DX_TT;
+    for (int q = threadIdx.x; q < DX_TT * E; q += 256) {
+        const int tt = q / E, i = q - tt * E;
+        dhs[tt][i] = t0 + tt < T ? dh[(int64_t)(t0 + tt) * E + i] : 0.f;
+    }
+    __syncthreads();
+    for (int j = blockIdx.y * 256 + threadIdx.x; j < d; j += gridDim.y * 256) {
+        float racc[DX_TT];
+#pragma unroll
+        for (int tt = 0; tt < DX_TT; ++tt) racc[tt] = 0.f;
+        for (int i = 0; i < E; ++i) {
+            const float wv = Wr[(int64_t)i * d + j];
+#pragma unroll
+            for (int tt = 0; tt < DX_TT; ++tt) racc[tt] = fmaf(dhs[tt][i], wv, racc[tt]);
+        }
+#pragma unroll
+        for (int tt = 0; tt < DX_TT; ++tt) {
+            const int t = t0 + tt;
+            if (t >= T) break;
             float acc = 0.f;
             for (int s = 0; s < k; ++s) {
                 const int r = row_of_slot[(int64_t)t * k + s];
                 if (r >= 0) acc += dXp[(int64_t)r * d + j];
             }
-            float racc = 0.f;
-            for (int i = 0; i < E; ++i) racc = fmaf(dh[(int64_t)t * E + i], Wr[(int64_t)i * d + j], racc);
-            dx[(int64_t)t * d + j] = acc + racc;
+            dx[(int64_t)t * d + j] = acc + racc[tt];
         }
     }
 }
 
-// dW_r[i][j] = sum_t dh[t][i] x[t][j]: a thread per column j, 16 experts per
-// pass, tokens in order
-constexpr int DWR_EG = 16;
-__global__ __launch_bounds__(256) void dwr_kernel(const float *__restrict__ dh,
-                                                  const uint16_t *__restrict__ x, int T, int d, int E,
-                                                  float *__restrict__ dWr) {
+// dW_r[i][j] = sum_t dh[t][i] x[t][j] in two passes with a fixed order: a
+// thread per (column j, split of the tokens) sums its tokens in order for
+// 16 experts at a time into partials [split][i][j]; then the splits are
+// added in split order.
+constexpr int DWR_EG = 16, DWR_SPLITS = 64;
+__global__ __launch_bounds__(256) void dwr_partial_kernel(const float *__restrict__ dh,
+                                                          const uint16_t *__restrict__ x, int T, int d,
+                                                          int E, float *__restrict__ part) {
     const int j = blockIdx.x * 256 + threadIdx.x;
     const int i0 = blockIdx.y * DWR_EG;
+    const int sp = blockIdx.z;
     if (j >= d) return;
+    const int t0 = (int)((int64_t)sp * T / DWR_SPLITS), t1 = (int)((int64_t)(sp + 1) * T / DWR_SPLITS);
     float acc[DWR_EG];
 #pragma unroll
     for (int u = 0; u < DWR_EG; ++u) acc[u] = 0.f;
-    for (int t = 0; t < T; ++t) {
+    for (int t = t0; t < t1; ++t) {
         const float xv = bf16_to_f32(x[(int64_t)t * d + j]);
 #pragma unroll
         for (int u = 0; u < DWR_EG; ++u)
@@ -257,7 +369,16 @@ __global__ __launch_bounds__(256) void dwr_kernel(const float *__restrict__ dh,
     }
 #pragma unroll
     for (int u = 0; u < DWR_EG; ++u)
-        if (i0 + u < E) dWr[(int64_t)(i0 + u) * d + j] = acc[u];
+        if (i0 + u < E) part[((int64_t)sp * E + i0 + u) * d + j] = acc[u];
+}
+
+__global__ __launch_bounds__(256) void dwr_reduce_kernel(const float *__restrict__ part, int64_t n,
+                                                         float *__restrict__ dWr) {
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
+        float s = 0.f;
+        for (int sp = 0; sp < DWR_SPLITS; ++sp) s += part[sp * n + i];
+        dWr[i] = s;
+    }
 }
 
 // dbias[i] = sum_t dh[t][i]: one block per expert, 256 strided partials
@@ -370,8 +491,14 @@ hipError_t launch_transpose_bf16(const void *src, int64_t R, int64_t C, int64_t 
                                  void *dst, int64_t ldd, int64_t dbs, int batch, hipStream_t st) {
     if (R <= 0 || C <= 0 || batch <= 0) return hipSuccess;
     dim3 grid((unsigned)((C + 63) / 64), (unsigned)((R + 63) / 64), (unsigned)batch);
-    hipLaunchKernelGGL(transpose_kernel, grid, dim3(256), 0, st, (const uint16_t *)src, R, C, lds, sbs,
-                       (uint16_t *)dst, ldd, dbs);
+    const bool vec = R % 4 == 0 && C % 4 == 0 && lds % 4 == 0 && ldd % 4 == 0 && sbs % 4 == 0 &&
+                     dbs % 4 == 0 && (uintptr_t)src % 8 == 0 && (uintptr_t)dst % 8 == 0;
+    if (vec)
+        hipLaunchKernelGGL(transpose_kernel<true>, grid, dim3(256), 0, st, (const uint16_t *)src, R, C, lds,
+                           sbs, (uint16_t *)dst, ldd, dbs);
+    else
+        hipLaunchKernelGGL(transpose_kernel<false>, grid, dim3(256), 0, st, (const uint16_t *)src, R, C, lds,
+                           sbs, (uint16_t *)dst, ldd, dbs);
     return hipGetLastError();
 }
 
@@ -404,8 +531,12 @@ hipError_t launch_router_bwd(const Shape &s, const void *x, const float *Wr, con
                              float alpha_aux, float alpha_z, float *p, float *lse, float *dh,
                              hipStream_t st) {
     const unsigned g = grid_for(s.T, 4, 16384);
-    hipLaunchKernelGGL(logits_kernel, dim3(g), dim3(256), 0, st, (const uint16_t *)x, Wr, bias, noise, s.T,
-                       s.d, s.E, p, lse);
+    if (s.E <= 32)
+        hipLaunchKernelGGL(logits_wave_kernel, dim3(g), dim3(256), 0, st, (const uint16_t *)x, Wr, bias, noise,
+                           s.T, s.d, s.E, p, lse);
+    else
+        hipLaunchKernelGGL(logits_kernel, dim3((unsigned)((s.T + LG_TB - 1) / LG_TB)), dim3(256), 0, st,
+                           (const uint16_t *)x, Wr, bias, noise, s.T, s.d, s.E, p, lse);
     hipLaunchKernelGGL(router_bwd_kernel, dim3(g), dim3(256), 0, st, (const float *)p, (const float *)lse,
                        topk_idx, gates, dg, row_of_slot, f, s.T, s.E, s.k, s.gate, alpha_aux, alpha_z, dh);
     return hipGetLastError();
@@ -413,15 +544,21 @@ hipError_t launch_router_bwd(const Shape &s, const void *x, const float *Wr, con
 
 hipError_t launch_dx(const Shape &s, const float *dXp, const int32_t *row_of_slot, const float *dh,
                      const float *Wr, float *dx, hipStream_t st) {
-    hipLaunchKernelGGL(dx_kernel, dim3(grid_for(s.T, 4, 16384)), dim3(256), 0, st, dXp, row_of_slot, dh, Wr,
-                       s.T, s.d, s.E, s.k, dx);
+    dim3 grid((unsigned)((s.T + DX_TT - 1) / DX_TT), (unsigned)((s.d + 255) / 256));
+    hipLaunchKernelGGL(dx_kernel, grid, dim3(256), 0, st, dXp, row_of_slot, dh, Wr, s.T, s.d, s.E, s.k, dx);
     return hipGetLastError();
 }
 
-hipError_t launch_dwr(const Shape &s, const float *dh, const void *x, float *dWr, float *dbias,
-                      hipStream_t st) {
-    dim3 grid((unsigned)((s.d + 255) / 256), (unsigned)((s.E + DWR_EG - 1) / DWR_EG));
-    hipLaunchKernelGGL(dwr_kernel, grid, dim3(256), 0, st, dh, (const uint16_t *)x, s.T, s.d, s.E, dWr);
+size_t dwr_part_floats(const Shape &s) { return (size_t)DWR_SPLITS * s.E * s.d; }
+
+hipError_t launch_dwr(const Shape &s, const float *dh, const void *x, float *part, float *dWr,
+                      float *dbias, hipStream_t st) {
+    dim3 grid((unsigned)((s.d + 255) / 256), (unsigned)((s.E + DWR_EG - 1) / DWR_EG), DWR_SPLITS);
+    hipLaunchKernelGGL(dwr_partial_kernel, grid, dim3(256), 0, st, dh, (const uint16_t *)x, s.T, s.d, s.E,
+                       part);
+    const int64_t n = (int64_t)s.E * s.d;
+    hipLaunchKernelGGL(dwr_reduce_kernel, dim3(grid_for(n, 256, 4096)), dim3(256), 0, st, (const float *)part,
+                       n, dWr);
     if (dbias) hipLaunchKernelGGL(dbias_kernel, dim3((unsigned)s.E), dim3(256), 0, st, dh, s.T, s.E, dbias);
     return hipGetLastError();
 }

@@ -308,7 +308,7 @@ struct BwdLayout {
     size_t x_perm, a1, a3, H, Y, part2;
     size_t dE, dg, dH, dA, dXp;
     size_t dET, HT, dAT, XT;
-    size_t p, lse, dh;
+    size_t p, lse, dh, dwr_part;
     size_t total;
     int64_t R, ldk;
 };
@@ -347,6 +347,7 @@ BwdLayout bwd_layout(const Shape &s) {
     L.p = take((size_t)s.T * E * 4);
     L.lse = take((size_t)s.T * 4);
     L.dh = take((size_t)s.T * E * 4);
+    L.dwr_part = take(moe::dwr_part_floats(s) * 4);
     L.total = o;
     return L;
 }
@@ -643,7 +644,7 @@ int moe_backward(const moe_desc *desc, const void *x, const float *W_r, const fl
     MOE_TRY(moe::launch_router_bwd(s, x, W_r, bias, noise, topk_idx, gates, dg, row_of_slot, stats,
                                    alpha_aux, alpha_z, p, lse, dh, st));
     MOE_TRY(moe::launch_dx(s, dXp, row_of_slot, dh, W_r, dx, st));
-    MOE_TRY(moe::launch_dwr(s, dh, x, dW_r, dbias, st));
+    MOE_TRY(moe::launch_dwr(s, dh, x, (float *)(w + L.dwr_part), dW_r, dbias, st));
     // weight gradients over each expert's rows
     MOE_TRY(moe::launch_transpose_bf16(dE, L.R, d, d, 0, dET, L.ldk, 0, 1, st));
     MOE_TRY(moe::launch_transpose_bf16(H, L.R, f, f, 0, HT, L.ldk, 0, 1, st));

@@ -175,8 +175,9 @@ hipError_t launch_router_bwd(const Shape &s, const void *x, const float *Wr, con
                              hipStream_t st);
 hipError_t launch_dx(const Shape &s, const float *dXp, const int32_t *row_of_slot, const float *dh,
                      const float *Wr, float *dx, hipStream_t st);
-hipError_t launch_dwr(const Shape &s, const float *dh, const void *x, float *dWr, float *dbias,
-                      hipStream_t st);
+size_t dwr_part_floats(const Shape &s);
+hipError_t launch_dwr(const Shape &s, const float *dh, const void *x, float *part, float *dWr,
+                      float *dbias, hipStream_t st);
 hipError_t launch_wgrad(int E, int M, int N, const int32_t *offsets, const void *P, const void *Q,
                         int64_t ldk, float *C, hipStream_t st);
 
