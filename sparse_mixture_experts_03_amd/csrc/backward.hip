@@ -224,6 +224,7 @@ __global__ __launch_bounds__(256) void logits_kernel(const uint16_t *__restrict_
         }
         __syncthreads();
         const float *w0 = Wr + (int64_t)lane * d + c0, *w1 = Wr + (int64_t)(lane + 64) * d + c0;
+#pragma unroll 4
         for (int j = 0; j < cw; j += 4) {
             float4 a = make_float4(0.f, 0.f, 0.f, 0.f), b = make_float4(0.f, 0.f, 0.f, 0.f);
             if (e0) a = *(const float4 *)(w0 + j);
@@ -326,6 +327,7 @@ __global__ __launch_bounds__(256) void dx_kernel(const float *__restrict__ dXp,
         float racc[DX_TT];
 #pragma unroll
         for (int tt = 0; tt < DX_TT; ++tt) racc[tt] = 0.f;
+#pragma unroll 8
         for (int i = 0; i < E; ++i) {
             const float wv = Wr[(int64_t)i * d + j];
 #pragma unroll
@@ -361,6 +363,7 @@ __global__ __launch_bounds__(256) void dwr_partial_kernel(const float *__restric
     float acc[DWR_EG];
 #pragma unroll
     for (int u = 0; u < DWR_EG; ++u) acc[u] = 0.f;
+#pragma unroll 8
     for (int t = t0; t < t1; ++t) {
         const float xv = bf16_to_f32(x[(int64_t)t * d + j]);
 #pragma unroll
