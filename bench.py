@@ -198,6 +198,10 @@ def run_workload(w, steps, warmup, fresh_x_steps=0, seed=0):
     torch.cuda.synchronize()
     up = stages.index("expert_up")
     keep = (up, up + 1)
+    if not with_shared:
+        # the combine's launch is timestamped like expert-up's (moe_forward)
+        cb = stages.index("combine")
+        keep = keep + (cb, cb + 1)
     if with_shared and w.n_shared > 0:
         sh = stages.index("shared")
         keep = keep + (sh, sh + 1)
@@ -323,6 +327,25 @@ def run_backward(w, steps, warmup, seed=0):
             "flops_per_step": flops}
 
 
+def combine_object(w, res):
+    """The combine's HBM rate over its event-timed launches: algorithmic bytes
+    = kept rows of y_perm (fp32) + gates and row indices + y (act dtype),
+    against 8 TB/s (a K-split down projection's second partial, when read,
+    is extra traffic not counted)."""
+    if "combine" not in res["stages"]:
+        return None
+    cb = res["stages"].index("combine")
+    ms = float(res["stage_ms"][cb])
+    if not np.isfinite(ms) or ms <= 0:
+        return None
+    ab = 2 if w.dtype == "bf16" else 4
+    nbytes = res["n_kept"] * w.d * 4 + w.T * w.k * 8 + w.T * w.d * ab
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": round(gbs / PEAK_HBM_GBS, 4), "algorithmic_per_launch": int(nbytes),
+            "mean_launch_ms": round(ms, 4)}
+
+
 def decode_object(wd, rd):
     """Throughput and HBM roofline of a decode workload's run: the expert
     up-projection (weight streaming) against 8 TB/s, algorithmic bytes =
@@ -345,6 +368,7 @@ def decode_object(wd, rd):
         "step_hbm_gbs": round(step_bytes / (ms_d * 1e-3) / 1e9, 1),
         "step_hbm_frac": round(step_bytes / (ms_d * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
         "stage_ms": {n: round(float(v), 4) for n, v in zip(rd["stages"], rd["stage_ms"]) if np.isfinite(v)},
+        "combine": combine_object(wd, rd),
         "roofline": {"bound": "hbm", "kernel": "expert_up", "achieved": round(gbs, 1),
                      "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
                      "traffic": traffic_for(wd.name, "expert_up"),
@@ -422,6 +446,7 @@ def main():
     up_ms = float(res["stage_ms"][up])
     up_flops = res["n_kept"] * 2.0 * n_up * w.d * w.d_ff
     achieved = up_flops / (up_ms * 1e-3) / 1e12
+    up_all = res["stage_ms_all"][:, up]
     stages = {n: round(float(v), 4) for n, v in zip(res["stages"], res["stage_ms"]) if np.isfinite(v)}
     log(f"[bench] {w.name}: {ms_step:.3f} ms/step, stages(ms) {stages}")
     line = {
@@ -441,8 +466,14 @@ def main():
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic_for(w.name, "expert_up"),
                      "algorithmic_per_launch": up_flops, "mean_launch_ms": round(up_ms, 4),
+                     "launch_ms_median_min_p90": [round(float(np.median(up_all)), 4),
+                                                  round(float(np.min(up_all)), 4),
+                                                  round(float(np.percentile(up_all, 90)), 4)],
                      "event_timed_launches": res["event_steps"]},
     }
+    line["combine"] = combine_object(w, res)
+    line["gather"] = ("folded into the expert up-projection's loads in moe_forward (rows of x read "
+                      "through token_of_row): its bytes are part of that kernel's traffic")
     if w.n_shared > 0:
         # the shared stage: the row map, then the shared experts' up and
         # down projections (dense GEMMs of all T tokens), against the MFMA peak

@@ -116,7 +116,8 @@ extern "C" {
  * separates the kernels around it by a few microseconds, so record only
  * the ones needed).  The two events around expert-up, which is one kernel,
  * are instead timestamped by that kernel's launch (its start and end): they
- * add no gap.  NULL disables the hook.  The stages, in order: route,
+ * add no gap; in moe_forward the same holds for the two around the combine
+ * (so the expert-down stage then ends at the combine's start).  NULL disables the hook.  The stages, in order: route,
  * route-finalize, dispatch, gather, expert-up, expert-down, combine; in
  * moe_forward the gather is folded into expert-up (its rows of x are read
  * through token_of_row), so that stage is empty.

@@ -179,8 +179,8 @@ hipError_t combine_any(const Shape &s, const float *y_perm, const float *y_perm_
         if (s.k == 4) kern = bf ? combine_kernel<true, true, 4, SH> : combine_kernel<false, true, 4, SH>;
         if (s.k == 8) kern = bf ? combine_kernel<true, true, 8, SH> : combine_kernel<false, true, 8, SH>;
     }
-    hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(256), 0, st, y_perm, y_perm_part2,
-                       row_of_slot, gates, s.T, s.d, s.k, G, sh, y);
+    launch_kernel(kern, dim3((unsigned)blocks), dim3(256), 0, st, y_perm, y_perm_part2, row_of_slot,
+                  gates, s.T, s.d, s.k, G, sh, y);
     return hipGetLastError();
 }
 

@@ -454,12 +454,14 @@ int forward_impl(const moe_desc *desc, const moe_shared *sh, const moe_fp8_exper
         MOE_TRY(moe::launch_expert_down_fp8(s, H, offsets, f8->W2, f8->s2, y_perm, st));
     else
         MOE_TRY(moe::launch_expert_down(s, H, offsets, W2, y_perm, part2, st));
-    MOE_TRY(ev.record(st));
     if (!sh) {
-        MOE_TRY(moe::launch_combine(s, y_perm, part2, row_of_slot, gates, y, st));
-        MOE_TRY(ev.record(st));
+        ev.around_next_launch();  // events before and after the combine (one kernel)
+        const hipError_t c_err = moe::launch_combine(s, y_perm, part2, row_of_slot, gates, y, st);
+        moe::next_launch_events() = moe::LaunchEvents{nullptr, nullptr};
+        MOE_TRY(c_err);
         return MOE_OK;
     }
+    MOE_TRY(ev.record(st));
     float *y_sh = nullptr, *y_sh2 = nullptr;
     if (S > 0) {
         y_sh = at<float>(ws, L.y_sh);
