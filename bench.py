@@ -37,10 +37,12 @@ tokens plus the expert FFN and combine on S sampled tokens; tokens/s is
 1 / (t_route / T + t_ffn / S).
 
 --backward times moe_backward (training gradients, routing of one forward
-held fixed) on the workload instead, and prints its own JSON line.
+held fixed) on the workload instead, and prints its own JSON line; --cold
+flushes the last-level cache (a 512 MB device fill) before every forward
+step and reports per-step median, minimum and 90th percentile.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                       [--no-cpu] [--no-decode] [--backward]
+                       [--no-cpu] [--no-decode] [--backward] [--cold]
 """
 import argparse
 import ctypes
@@ -274,6 +276,45 @@ def cpu_baseline(w, seed=0, target_s=22.0):
                        f"and combine on {S} sampled tokens ({t_ffn:.2f}s); fp64 sums")}
 
 
+def run_cold(w, steps, warmup, seed=0, flush_bytes=512 << 20):
+    """Per-step times of moe_forward with the last-level cache flushed before
+    every step (a device fill of ``flush_bytes``, outside the timed events):
+    each step is bracketed by its own events on the launch stream.  Returns
+    the median, minimum and 90th percentile."""
+    import torch
+    from sparse_mixture_experts_03_amd import binding as B
+    from sparse_mixture_experts_03_amd import synth
+
+    wt = synth.make_weights(w, seed)
+    dw = {k: B.to_device(v, w.dtype) for k, v in wt.items()}
+    del wt
+    tk = synth.make_tokens(w, seed, 0)
+    x, noise = B.to_device(tk["x"], w.dtype), B.to_device(tk["noise"], w.dtype)
+    desc = B.desc_for(w)
+    ws = B.workspace(desc)
+    out = B.alloc_outputs(desc)
+    scratch = torch.empty(flush_bytes // 4, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    times = []
+    for i in range(warmup + steps):
+        scratch.fill_(float(i))
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        B.moe_forward(desc, x, dw["Wr"], dw["bias"], noise, dw["W1"], dw["W3"], dw["W2"], out["y"], ws,
+                      stream=stream)
+        b.record(stream)
+        if i >= warmup:
+            times.append((a, b))
+    torch.cuda.synchronize()
+    ms = np.array([a.elapsed_time(b) for a, b in times])
+    med = float(np.median(ms))
+    return {"metric": METRIC, "workload": w.name, "mode": "last-level cache flushed before each step",
+            "value": round(w.T / (med * 1e-3), 1), "unit": "tokens/s", "steps": steps,
+            "ms_per_step_median_min_p90": [round(med, 4), round(float(ms.min()), 4),
+                                           round(float(np.percentile(ms, 90)), 4)],
+            "flush_bytes": flush_bytes}
+
+
 def run_backward(w, steps, warmup, seed=0):
     """Times ``steps`` moe_backward calls of workload w (after one forward
     that fixes the routing); loss weights 0.01 (aux) and 0.001 (z), the
@@ -388,6 +429,8 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--backward", action="store_true",
                     help="time moe_backward on the workload instead of the forward")
+    ap.add_argument("--cold", action="store_true",
+                    help="flush the last-level cache before every step and time each step alone")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy three times (a kernel of "
                          "known traffic, to calibrate rocprofv3's FETCH_SIZE/WRITE_SIZE)")
@@ -415,6 +458,9 @@ def main():
     w = synth.WORKLOADS[args.workload]
     if args.backward:
         print(json.dumps(run_backward(w, args.steps, args.warmup)), flush=True)
+        return
+    if args.cold:
+        print(json.dumps(run_cold(w, args.steps, args.warmup)), flush=True)
         return
     if w.steps > 1:
         # a decode workload on its own: fresh tokens every step, HBM roofline
