@@ -49,7 +49,26 @@ def build(verbose: bool = False) -> str:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
     os.replace(LIB + ".tmp", LIB)
+    build_c_client(verbose)
     return LIB
+
+
+# A plain C program against include/moe.h and the HIP runtime's C API, run
+# by the GPU tests (tests/c/forward_c.c); built next to the library.
+C_CLIENT_SRC = os.path.join(ROOT, "tests", "c", "forward_c.c")
+C_CLIENT = os.path.join(PKG, "moe_forward_c")
+
+
+def build_c_client(verbose: bool = False) -> str:
+    cmd = ["gcc", "-std=c11", "-O2", "-Wall", "-Wextra", "-D__HIP_PLATFORM_AMD__",
+           "-I", INCLUDE, "-I", "/opt/rocm/include", C_CLIENT_SRC, "-o", C_CLIENT + ".tmp",
+           "-L", PKG, "-lmoe", "-L", "/opt/rocm/lib", "-lamdhip64", "-lm",
+           "-Wl,-rpath,$ORIGIN", "-Wl,-rpath,/opt/rocm/lib"]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    os.replace(C_CLIENT + ".tmp", C_CLIENT)
+    return C_CLIENT
 
 
 if __name__ == "__main__":
