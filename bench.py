@@ -39,10 +39,13 @@ tokens plus the expert FFN and combine on S sampled tokens; tokens/s is
 --backward times moe_backward (training gradients, routing of one forward
 held fixed) on the workload instead, and prints its own JSON line; --cold
 flushes the last-level cache (a 512 MB device fill) before every forward
-step and reports per-step median, minimum and 90th percentile.
+step and reports per-step median, minimum and 90th percentile;
+--library-gemm times torch's own GEMM (hipBLASLt) on the up projection's
+FLOPs for context.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                        [--no-cpu] [--no-decode] [--backward] [--cold]
+                       [--library-gemm]
 """
 import argparse
 import ctypes
@@ -418,6 +421,47 @@ def decode_object(wd, rd):
     }
 
 
+def run_library_gemm(w, steps, warmup, seed=0):
+    """The up projection's FLOPs through torch's own GEMM (hipBLASLt), for
+    context: X [N][d] times the stacked [W1; W3] of one expert, transposed
+    (torch.nn.functional.linear, weights [n_up*d_ff][d] as stored), once as one
+    dense call over all N = T*k rows and once as E calls of N/E rows each
+    (the balanced grouped problem as separate library calls).  bf16 in, fp32
+    accumulation, bf16 out, as in the layer's own kernel."""
+    import torch
+    import torch.nn.functional as F
+
+    n_up = 2 if w.act == "swiglu" else 1
+    N = w.T * w.k
+    g = torch.Generator(device="cuda").manual_seed(seed)
+    X = torch.randn((N, w.d), generator=g, device="cuda").to(torch.bfloat16)
+    Wt = [(torch.randn((n_up * w.d_ff, w.d), generator=g, device="cuda") * w.d ** -0.5)
+          .to(torch.bfloat16) for _ in range(w.E)]
+    rows = N // w.E
+    flops = 2.0 * N * w.d * n_up * w.d_ff
+
+    def timed(fn):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(steps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b) / steps
+        return {"ms": round(ms, 4), "tflops": round(flops / ms * 1e-9, 1),
+                "frac_bf16_peak": round(flops / ms * 1e-9 / PEAK_BF16_TFLOPS, 4)}
+
+    dense = timed(lambda: F.linear(X, Wt[0]))
+    per_expert = timed(lambda: [F.linear(X[e * rows:(e + 1) * rows], Wt[e]) for e in range(w.E)])
+    return {"library_gemm": "torch.nn.functional.linear (hipBLASLt)", "workload": w.name,
+            "shape": {"rows": N, "K": w.d, "N": n_up * w.d_ff, "E": w.E},
+            "gflop": round(flops * 1e-9, 1), "steps": steps, "warmup": warmup,
+            "dense_one_call": dense, "per_expert_calls": per_expert}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -431,6 +475,9 @@ def main():
                     help="time moe_backward on the workload instead of the forward")
     ap.add_argument("--cold", action="store_true",
                     help="flush the last-level cache before every step and time each step alone")
+    ap.add_argument("--library-gemm", action="store_true",
+                    help="only time torch's GEMM (hipBLASLt) on the up projection's FLOPs, "
+                         "one dense call and one call per expert, for context")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy three times (a kernel of "
                          "known traffic, to calibrate rocprofv3's FETCH_SIZE/WRITE_SIZE)")
@@ -454,8 +501,11 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"copy_probe_bytes": src.numel() * 4, "launches": 3}))
         return
-    B.load(build_if_missing=False)
     w = synth.WORKLOADS[args.workload]
+    if args.library_gemm:
+        print(json.dumps(run_library_gemm(w, args.steps, args.warmup)), flush=True)
+        return
+    B.load(build_if_missing=False)
     if args.backward:
         print(json.dumps(run_backward(w, args.steps, args.warmup)), flush=True)
         return
