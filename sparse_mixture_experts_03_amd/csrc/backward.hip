@@ -24,10 +24,15 @@
 //   dwr_partial_kernel, dwr_reduce_kernel, dbias_kernel
 //                          dW_r = sum_t dh_t x_t^T (token splits, then the
 //                          splits in order), db = sum_t dh_t
+//   pad_offsets_kernel     each expert's start in the padded row layout
+//                          (row counts rounded up to 64)
+//   transpose_padded_kernel  the activations transposed into that layout
+//                          (K-contiguous rows, zero pads)
 //   wgrad_kernel           weight gradients: per expert, C = P^T Q over its
-//                          rows (a GEMM whose K range is the expert's row
-//                          block, read from the device offsets), bf16
-//                          operands transposed to K-contiguous rows, fp32 out
+//                          k range, 128 x 128 tiles, for operands past
+//                          2 GiB; otherwise the forward's 256 x 256 tile
+//                          runs them (its weight-gradient form, in
+//                          expert_gemm.hip)
 // Every sum has a fixed order (no atomics); results are reproducible.
 #include "moe_internal.h"
 
@@ -99,6 +104,95 @@ __global__ __launch_bounds__(256) void transpose_kernel(const uint16_t *__restri
     for (int i = 0; i < 16; ++i) {
         const int64_t c = c0 + ty + 4 * i, r = r0 + tx;
         if (r < R && c < C) d[c * ldd + r] = tile[tx][ty + 4 * i];
+    }
+}
+
+// poff[e] = sum over e' < e of (offsets[e'+1] - offsets[e']) rounded up to
+// 64, poff[E] the total: one wave, experts e and e + 64 on lane e % 64
+// (E <= 128), two inclusive scans by shuffles.
+__global__ __launch_bounds__(64) void pad_offsets_kernel(const int32_t *__restrict__ offsets, int E,
+                                                         int32_t *__restrict__ poff) {
+    const int l = threadIdx.x;
+    int c0 = 0, c1 = 0;
+    if (l < E) c0 = (offsets[l + 1] - offsets[l] + 63) & ~63;
+    if (l + 64 < E) c1 = (offsets[l + 65] - offsets[l + 64] + 63) & ~63;
+    int s0 = c0, s1 = c1;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int u0 = __shfl_up(s0, o), u1 = __shfl_up(s1, o);
+        if (l >= o) {
+            s0 += u0;
+            s1 += u1;
+        }
+    }
+    const int tot0 = __shfl(s0, 63), tot1 = __shfl(s1, 63);
+    if (l < E) poff[l] = s0 - c0;
+    if (l + 64 < E) poff[l + 64] = tot0 + s1 - c1;
+    if (l == 0) poff[E] = tot0 + tot1;
+}
+
+// The padded transpose: block (x, y) takes source columns 64x.. and padded
+// positions 64y..; a 64-wide run of positions lies inside one expert's
+// range (every range starts on a multiple of 64), found by binary search
+// over poff; its source rows are offsets[e] + (64y - poff[e]) + i for the
+// expert's count, zeros past it.  VEC as in transpose_kernel.
+template <bool VEC>
+__global__ __launch_bounds__(256) void transpose_padded_kernel(const uint16_t *__restrict__ src, int64_t C,
+                                                               int64_t lds, const int32_t *__restrict__ offsets,
+                                                               const int32_t *__restrict__ poff, int E,
+                                                               uint16_t *__restrict__ dst, int64_t ldp) {
+    __shared__ uint16_t tile[64][66];
+    const int64_t c0 = (int64_t)blockIdx.x * 64;
+    const int j0 = (int)blockIdx.y * 64;
+    if (j0 >= poff[E]) return;
+    int lo = 0, hi = E - 1;   // largest e with poff[e] <= j0
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (poff[mid] <= j0) lo = mid;
+        else hi = mid - 1;
+    }
+    const int e = lo;
+    const int64_t rb = (int64_t)offsets[e] + (j0 - poff[e]);
+    const int nv = min(64, offsets[e + 1] - offsets[e] - (j0 - poff[e]));   // valid rows (may be <= 0)
+    if (VEC) {
+        const int g = threadIdx.x & 15, rr = threadIdx.x >> 4;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = rr + 16 * i;
+            const int64_t c = c0 + 4 * g;
+            uint2 v = make_uint2(0, 0);
+            if (r < nv && c < C) v = *(const uint2 *)(src + (rb + r) * lds + c);
+            tile[r][4 * g + 0] = (uint16_t)(v.x & 0xffffu);
+            tile[r][4 * g + 1] = (uint16_t)(v.x >> 16);
+            tile[r][4 * g + 2] = (uint16_t)(v.y & 0xffffu);
+            tile[r][4 * g + 3] = (uint16_t)(v.y >> 16);
+        }
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int cc = rr + 16 * i;
+            const int64_t c = c0 + cc;
+            if (c < C) {
+                uint2 v;
+                v.x = (uint32_t)tile[4 * g + 0][cc] | ((uint32_t)tile[4 * g + 1][cc] << 16);
+                v.y = (uint32_t)tile[4 * g + 2][cc] | ((uint32_t)tile[4 * g + 3][cc] << 16);
+                *(uint2 *)(dst + c * ldp + j0 + 4 * g) = v;
+            }
+        }
+        return;
+    }
+    const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const int r = ty + 4 * i;
+        const int64_t c = c0 + tx;
+        tile[r][tx] = (r < nv && c < C) ? src[(rb + r) * lds + c] : (uint16_t)0;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const int64_t c = c0 + ty + 4 * i;
+        if (c < C) dst[c * ldp + j0 + tx] = tile[tx][ty + 4 * i];
     }
 }
 
@@ -502,6 +596,29 @@ hipError_t launch_transpose_bf16(const void *src, int64_t R, int64_t C, int64_t 
     else
         hipLaunchKernelGGL(transpose_kernel<false>, grid, dim3(256), 0, st, (const uint16_t *)src, R, C, lds,
                            sbs, (uint16_t *)dst, ldd, dbs);
+    return hipGetLastError();
+}
+
+int64_t padded_rows_bound(int64_t R, int E) { return (R + 63 * (int64_t)E + 63) / 64 * 64; }
+
+hipError_t launch_pad_offsets(const int32_t *offsets, int E, int32_t *poff, hipStream_t st) {
+    if (E < 1 || E > 128) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(pad_offsets_kernel, dim3(1), dim3(64), 0, st, offsets, E, poff);
+    return hipGetLastError();
+}
+
+hipError_t launch_transpose_padded(const void *src, int64_t C, int64_t lds, const int32_t *offsets,
+                                   const int32_t *poff, int E, int64_t ldp, void *dst, hipStream_t st) {
+    if (C <= 0 || ldp <= 0) return hipSuccess;
+    if (ldp % 64 != 0 || ldp / 64 > 65535) return hipErrorInvalidValue;
+    dim3 grid((unsigned)((C + 63) / 64), (unsigned)(ldp / 64));
+    const bool vec = C % 4 == 0 && lds % 4 == 0 && (uintptr_t)src % 8 == 0 && (uintptr_t)dst % 8 == 0;
+    if (vec)
+        hipLaunchKernelGGL(transpose_padded_kernel<true>, grid, dim3(256), 0, st, (const uint16_t *)src, C, lds,
+                           offsets, poff, E, (uint16_t *)dst, ldp);
+    else
+        hipLaunchKernelGGL(transpose_padded_kernel<false>, grid, dim3(256), 0, st, (const uint16_t *)src, C, lds,
+                           offsets, poff, E, (uint16_t *)dst, ldp);
     return hipGetLastError();
 }
 

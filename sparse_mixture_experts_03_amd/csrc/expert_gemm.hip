@@ -380,6 +380,9 @@ __device__ __forceinline__ void big_tile(char *lds, const uint16_t *__restrict__
                                          const uint16_t *__restrict__ B1,
                                          const uint16_t *__restrict__ B3, void *__restrict__ C, int N,
                                          int K, int e, int row0, int nrows, int n0, int KT, int kbeg) {
+    // Device pass only: the host pass needs just the kernels' stubs (and
+    // its clang rejects these instantiations from the weight-gradient form).
+#if defined(__HIP_DEVICE_COMPILE__)
     constexpr int BK = 64;
     static_assert(NJ == 4 || NJ == 2, "whole or half-width tiles");
     constexpr int BN = DUAL ? 32 * NJ : 64 * NJ;   // output columns per block
@@ -607,9 +610,18 @@ __device__ __forceinline__ void big_tile(char *lds, const uint16_t *__restrict__
                 }
             }
         }
+#endif
 }
 
-template <bool DUAL, int ACT, bool OUT_BF16>
+// WG: the weight-gradient form (launch_wgrad_big).  C_e = P Q^T for each
+// expert e over its k range [offsets[e], offsets[e+1]) (multiples of 64:
+// the zero-padded transposed activations), with A = P [E][K], B1 = Q [N][K]
+// (K the row stride), E = the rows of each C_e, C_ = C [experts][E][N] fp32.
+// Block b is tile (e, m, n), rows m*256.., columns n*256.., in (e, m, n)
+// order with n fastest: the hardware's round-robin over the XCDs gives
+// each XCD every eighth column tile of the same row tiles.  An expert
+// without rows writes zeros.
+template <bool DUAL, int ACT, bool OUT_BF16, bool WG = false>
 __global__ __launch_bounds__(256) void gemm_bf16_big_kernel(
     const uint16_t *__restrict__ A, const int32_t *__restrict__ a_rows,
     const int32_t *__restrict__ offsets, int E, const uint16_t *__restrict__ B1,
@@ -620,13 +632,35 @@ __global__ __launch_bounds__(256) void gemm_bf16_big_kernel(
     __shared__ __attribute__((aligned(1024))) char lds[5 * 256 * 128];
 
     int e, row0, nrows, ntile, split = 0, half = 0;
-    if (!find_tile_balanced(offsets, E, (N + BN - 1) / BN, nsplit, cpx, e, row0, nrows, ntile, split, half))
-        return;
-    // K split: this tile covers stages [split * KT, (split + 1) * KT) and
-    // the second half writes its partial sums to C_split
-    void *const C = split ? C_split : C_;
-    const int KT = K / 64 / nsplit;
-    const int kbeg = split * KT * 64;
+    void *C;
+    int KT, kbeg;
+    if constexpr (WG) {
+        const int M = E;
+        const int tm = (M + 255) / 256, tn = (N + 255) / 256;
+        const int x = (int)blockIdx.x / (tm * tn);
+        const int rem = (int)blockIdx.x - x * tm * tn;
+        row0 = (rem / tn) * 256;
+        ntile = rem % tn;
+        nrows = min(256, M - row0);
+        kbeg = offsets[x];
+        KT = (offsets[x + 1] - kbeg) / 64;
+        C = (float *)C_ + (int64_t)x * M * N;
+        e = 0;   // the operands carry no per-expert base
+        if (KT == 0) {
+            const int n0 = ntile * 256, ncols = min(256, N - n0);
+            for (int i = threadIdx.x; i < nrows * 256; i += 256)
+                if ((i & 255) < ncols) ((float *)C)[(int64_t)(row0 + (i >> 8)) * N + n0 + (i & 255)] = 0.f;
+            return;
+        }
+    } else {
+        if (!find_tile_balanced(offsets, E, (N + BN - 1) / BN, nsplit, cpx, e, row0, nrows, ntile, split, half))
+            return;
+        // K split: this tile covers stages [split * KT, (split + 1) * KT) and
+        // the second half writes its partial sums to C_split
+        C = split ? C_split : C_;
+        KT = K / 64 / nsplit;
+        kbeg = split * KT * 64;
+    }
     const int mi = (nrows + 63) >> 6;   // 64-row slabs this tile needs
     if constexpr (!DUAL) if (half) {
         // half-width piece: columns [ntile * BN + (half - 1) * BN / 2, + BN / 2)
@@ -1107,5 +1141,23 @@ hipError_t launch_add_partial(const Shape &s, float *y_perm, const float *part2,
                        offsets, s.E, s.d);
     return hipGetLastError();
 }
+
+bool wgrad_big_fits(int M, int N, int64_t ldk) {
+    // 32-bit buffer offsets (row * ldk + k) * 2 for both operands
+    const int64_t mx = (int64_t)(M > N ? M : N) * ldk * 2;
+    return M % 8 == 0 && N % 8 == 0 && ldk % 64 == 0 && mx < ((int64_t)1 << 31);
+}
+
+hipError_t launch_wgrad_big(int E, int M, int N, const int32_t *koff, const void *P, const void *Q,
+                            int64_t ldk, float *C, hipStream_t st) {
+    if (!wgrad_big_fits(M, N, ldk)) return hipErrorInvalidValue;
+    const int64_t blocks = (int64_t)E * ((M + 255) / 256) * ((N + 255) / 256);
+    if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+    launch_kernel((gemm_bf16_big_kernel<false, ACT_NONE, false, true>), dim3((unsigned)blocks), dim3(256), 0, st,
+                  (const uint16_t *)P, nullptr, koff, M, (const uint16_t *)Q, nullptr, (void *)C, N, (int)ldk, 1,
+                  nullptr, 0);
+    return hipGetLastError();
+}
+
 
 }  // namespace moe

@@ -301,14 +301,15 @@ int moe_combine(const moe_desc *desc, const float *y_perm, const int32_t *row_of
 namespace {
 
 // Workspace of moe_backward (every region 256-byte aligned).  R bounds the
-// kept rows; ldk (R rounded up to 8) is the row length of the transposed
-// activations.
+// kept rows; ldk bounds the padded row positions (each expert's rows start
+// on a multiple of 64, pads zero) and is the row length of the transposed
+// activations; poff holds the E + 1 padded offsets.
 struct BwdLayout {
     size_t w2t, wcat;                 // W2 as [E][d_ff][d]; W1 | W3 as [E][d][n_up d_ff]
     size_t x_perm, a1, a3, H, Y, part2;
     size_t dE, dg, dH, dA, dXp;
     size_t dET, HT, dAT, XT;
-    size_t p, lse, dh, dwr_part;
+    size_t p, lse, dh, dwr_part, poff;
     size_t total;
     int64_t R, ldk;
 };
@@ -319,7 +320,7 @@ BwdLayout bwd_layout(const Shape &s) {
     int64_t R = s.Tk();
     if (s.C >= 0 && (int64_t)s.E * s.C < R) R = (int64_t)s.E * s.C;
     L.R = R;
-    L.ldk = (R + 7) / 8 * 8;
+    L.ldk = moe::padded_rows_bound(R, s.E);
     const size_t r = (size_t)R, lk = (size_t)L.ldk, d = (size_t)s.d, f = (size_t)s.d_ff, E = (size_t)s.E;
     size_t o = 0;
     auto take = [&](size_t bytes) {
@@ -348,6 +349,7 @@ BwdLayout bwd_layout(const Shape &s) {
     L.lse = take((size_t)s.T * 4);
     L.dh = take((size_t)s.T * E * 4);
     L.dwr_part = take(moe::dwr_part_floats(s) * 4);
+    L.poff = take((E + 1) * 4);
     L.total = o;
     return L;
 }
@@ -647,15 +649,19 @@ int moe_backward(const moe_desc *desc, const void *x, const float *W_r, const fl
                                    alpha_aux, alpha_z, p, lse, dh, st));
     MOE_TRY(moe::launch_dx(s, dXp, row_of_slot, dh, W_r, dx, st));
     MOE_TRY(moe::launch_dwr(s, dh, x, (float *)(w + L.dwr_part), dW_r, dbias, st));
-    // weight gradients over each expert's rows
-    MOE_TRY(moe::launch_transpose_bf16(dE, L.R, d, d, 0, dET, L.ldk, 0, 1, st));
-    MOE_TRY(moe::launch_transpose_bf16(H, L.R, f, f, 0, HT, L.ldk, 0, 1, st));
-    MOE_TRY(moe::launch_transpose_bf16(dA, L.R, (int64_t)nup * f, (int64_t)nup * f, 0, dAT, L.ldk, 0, 1, st));
-    MOE_TRY(moe::launch_transpose_bf16(xp, L.R, d, d, 0, XT, L.ldk, 0, 1, st));
-    MOE_TRY(moe::launch_wgrad(E, d, f, offsets, dET, HT, L.ldk, dW2, st));
-    MOE_TRY(moe::launch_wgrad(E, f, d, offsets, dAT, XT, L.ldk, dW1, st));
-    if (swiglu)
-        MOE_TRY(moe::launch_wgrad(E, f, d, offsets, (char *)dAT + (size_t)f * L.ldk * 2, XT, L.ldk, dW3, st));
+    // weight gradients over each expert's rows, from the activations
+    // transposed into the padded layout
+    int32_t *poff = (int32_t *)(w + L.poff);
+    MOE_TRY(moe::launch_pad_offsets(offsets, E, poff, st));
+    MOE_TRY(moe::launch_transpose_padded(dE, d, d, offsets, poff, E, L.ldk, dET, st));
+    MOE_TRY(moe::launch_transpose_padded(H, f, f, offsets, poff, E, L.ldk, HT, st));
+    MOE_TRY(moe::launch_transpose_padded(dA, (int64_t)nup * f, (int64_t)nup * f, offsets, poff, E, L.ldk, dAT, st));
+    MOE_TRY(moe::launch_transpose_padded(xp, d, d, offsets, poff, E, L.ldk, XT, st));
+    const bool big = moe::wgrad_big_fits(d, f, L.ldk);
+    auto wgrad = big ? moe::launch_wgrad_big : moe::launch_wgrad;
+    MOE_TRY(wgrad(E, d, f, poff, dET, HT, L.ldk, dW2, st));
+    MOE_TRY(wgrad(E, f, d, poff, dAT, XT, L.ldk, dW1, st));
+    if (swiglu) MOE_TRY(wgrad(E, f, d, poff, (char *)dAT + (size_t)f * L.ldk * 2, XT, L.ldk, dW3, st));
     return MOE_OK;
 }
 

@@ -178,8 +178,29 @@ hipError_t launch_dx(const Shape &s, const float *dXp, const int32_t *row_of_slo
 size_t dwr_part_floats(const Shape &s);
 hipError_t launch_dwr(const Shape &s, const float *dh, const void *x, float *part, float *dWr,
                       float *dbias, hipStream_t st);
-hipError_t launch_wgrad(int E, int M, int N, const int32_t *offsets, const void *P, const void *Q,
+// Weight gradients read the activations transposed into a padded layout:
+// expert e's kept rows become positions poff[e] .. poff[e] + count_e - 1 of
+// each row, poff[e] = the sum over e' < e of count_e' rounded up to 64, and
+// the pad positions up to poff[e + 1] hold zeros.  padded_rows_bound bounds
+// poff[E] (a multiple of 64) for R kept rows at most.
+int64_t padded_rows_bound(int64_t R, int E);
+hipError_t launch_pad_offsets(const int32_t *offsets, int E, int32_t *poff, hipStream_t st);
+// dst[c][poff[e] + i] = src[offsets[e] + i][c] (bf16, c < C, row stride lds
+// of src, ldp of dst), zeros on the pad positions; positions past poff[E]
+// are not written.
+hipError_t launch_transpose_padded(const void *src, int64_t C, int64_t lds, const int32_t *offsets,
+                                   const int32_t *poff, int E, int64_t ldp, void *dst, hipStream_t st);
+// C[e][m][n] = sum over k in [koff[e], koff[e+1]) of P[m][k] Q[n][k]
+// (P [M][ldk], Q [N][ldk] bf16, C fp32).  launch_wgrad: 128 x 128 tiles, any
+// k range; launch_wgrad_big: the 256 x 256 direct-to-LDS tiles of the
+// forward's grouped GEMM, for k ranges that start and end on multiples of
+// 64 (the padded layout), M and N multiples of 8 and both operands under
+// 2 GiB (wgrad_big_fits).
+hipError_t launch_wgrad(int E, int M, int N, const int32_t *koff, const void *P, const void *Q,
                         int64_t ldk, float *C, hipStream_t st);
+bool wgrad_big_fits(int M, int N, int64_t ldk);
+hipError_t launch_wgrad_big(int E, int M, int N, const int32_t *koff, const void *P, const void *Q,
+                            int64_t ldk, float *C, hipStream_t st);
 
 // ---- combine -------------------------------------------------------------
 // y_perm_part2: nullptr, or the second K half of a split down projection.
