@@ -1019,7 +1019,14 @@ hipError_t launch_skinny_any(const Shape &s, int mt, const void *A, const int32_
     // rows per wave, 2-chunk ring (the rows of A, re-read from L2 for every
     // chunk, then cost 0.5-0.75 of the weight bytes instead of 1-1.5:
     // Switch layer 0.395 -> 0.382 ms per step; more SwiGLU rows per wave
-    // were slower)
+    // were slower), and 128 rows per wave when K is not split over the
+    // waves of a block (one wave per SIMD; Switch layer 0.385 -> 0.351 ms
+    // per step, its down projection gaining; the split decode down
+    // projection is no faster with them)
+    if (!DUAL && !((int64_t)s.E * ((N + 63) / 64) < 4096 && K / SK_KC >= 64)) {
+        if (mt == 2) return launch_skinny<2, 8, 2, DUAL, ACT, OUT_BF16>(s, A, a_rows, offsets, B1, B3, C, N, K, st);
+        return launch_skinny<3, 8, 2, DUAL, ACT, OUT_BF16>(s, A, a_rows, offsets, B1, B3, C, N, K, st);
+    }
     if (mt == 2) return launch_skinny<2, DUAL ? 1 : 4, DUAL ? 4 : 2, DUAL, ACT, OUT_BF16>(s, A, a_rows, offsets, B1, B3, C, N, K, st);
     return launch_skinny<3, DUAL ? 1 : 4, DUAL ? 4 : 2, DUAL, ACT, OUT_BF16>(s, A, a_rows, offsets, B1, B3, C, N, K, st);
 }
