@@ -18,12 +18,17 @@
 //   combine_bwd_kernel     per kept row: dE = g dy_t (bf16), dg = <dy_t, E(x_t)>
 //   act_bwd_kernel         dA = [da1 | da3] from dH and the pre-activations
 //   logits_kernel          p = softmax(W_r x + b + n), lse (fp32; 32 tokens
-//                          per block sharing each W_r read)
+//                          per block sharing each W_r read); for d a
+//                          multiple of 64 the logits run on matrix cores
+//                          instead (split_wr_kernel, the weight-gradient
+//                          GEMM, logits_finish_kernel)
 //   router_bwd_kernel      dh_t from dg (gate convention), aux and z terms
 //   dx_kernel              dx_t = sum over kept slots of dX_perm + W_r^T dh_t
 //   dwr_partial_kernel, dwr_reduce_kernel, dbias_kernel
 //                          dW_r = sum_t dh_t x_t^T (token splits, then the
-//                          splits in order), db = sum_t dh_t
+//                          splits in order), db = sum_t dh_t; dW_r runs on
+//                          matrix cores instead when it fits (split_dh_kernel,
+//                          the weight-gradient GEMM, dwr_sum_kernel)
 //   pad_offsets_kernel     each expert's start in the padded row layout
 //                          (row counts rounded up to 64)
 //   transpose_padded_kernel  the activations transposed into that layout
@@ -495,6 +500,113 @@ __global__ __launch_bounds__(256) void dbias_kernel(const float *__restrict__ dh
     }
 }
 
+// dh [T][E] -> the three bf16 terms, transposed: P[q Ep + e][t] for t < Tp
+// (zeros for t >= T or e >= E); 64 x 64 tiles through LDS.
+__global__ __launch_bounds__(256) void split_dh_kernel(const float *__restrict__ dh, int T, int E, int Ep,
+                                                       int64_t Tp, uint16_t *__restrict__ P) {
+    __shared__ float tile[64][65];
+    const int t0 = blockIdx.x * 64, e0 = blockIdx.y * 64;
+    const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const int t = t0 + ty + 4 * i, e = e0 + tx;
+        tile[ty + 4 * i][tx] = (t < T && e < E) ? dh[(int64_t)t * E + e] : 0.f;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const int e = e0 + ty + 4 * i;
+        const int64_t t = t0 + tx;
+        if (e < Ep && t < Tp) {
+            const float v = tile[tx][ty + 4 * i];
+            const uint16_t hi = f32_to_bf16(v);
+            const float r1 = v - bf16_to_f32(hi);   // exact
+            const uint16_t mid = f32_to_bf16(r1);
+            const uint16_t lo = f32_to_bf16(r1 - bf16_to_f32(mid));
+            P[(int64_t)e * Tp + t] = hi;
+            P[(int64_t)(Ep + e) * Tp + t] = mid;
+            P[(int64_t)(2 * Ep + e) * Tp + t] = lo;
+        }
+    }
+}
+
+// W_r [E][d] -> its three bf16 terms as rows e, Ep + e, 2 Ep + e of Ws
+// [3 Ep][d] (zero rows for e >= E)
+__global__ __launch_bounds__(256) void split_wr_kernel(const float *__restrict__ Wr, int E, int Ep, int d,
+                                                       uint16_t *__restrict__ Ws) {
+    const int64_t n = (int64_t)Ep * d;
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
+        const int e = (int)(i / d);
+        const float v = e < E ? Wr[i] : 0.f;
+        const uint16_t hi = f32_to_bf16(v);
+        const float r1 = v - bf16_to_f32(hi);   // exact
+        const uint16_t mid = f32_to_bf16(r1);
+        Ws[i] = hi;
+        Ws[n + i] = mid;
+        Ws[2 * n + i] = f32_to_bf16(r1 - bf16_to_f32(mid));
+    }
+}
+
+// p and lse from the partial logits C [ns][T][3 Ep]: one wave per token,
+// lane i holds experts i and i + 64 (E <= 128)
+__global__ __launch_bounds__(256) void logits_finish_kernel(const float *__restrict__ C, int ns, int T, int E,
+                                                            int Ep, const float *__restrict__ bias,
+                                                            const float *__restrict__ noise,
+                                                            float *__restrict__ p, float *__restrict__ lse) {
+    const int lane = threadIdx.x & 63;
+    const int64_t stride = (int64_t)T * 3 * Ep;
+    for (int t = blockIdx.x * 4 + (threadIdx.x >> 6); t < T; t += gridDim.x * 4) {
+        float h[2] = {-INFINITY, -INFINITY};
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int e = lane + 64 * u;
+            if (e < E) {
+                float a = 0.f;
+                for (int q = 2; q >= 0; --q)
+                    for (int sp = 0; sp < ns; ++sp) a += C[sp * stride + (int64_t)t * 3 * Ep + q * Ep + e];
+                if (bias) a += bias[e];
+                if (noise) a += noise[(int64_t)t * E + e];
+                h[u] = a;
+            }
+        }
+        const float m = wave_max_f32b(fmaxf(h[0], h[1]));
+        const float e0 = lane < E ? expf(h[0] - m) : 0.f;
+        const float e1 = lane + 64 < E ? expf(h[1] - m) : 0.f;
+        const float sum = wave_sum_f32(e0 + e1);
+        if (lane < E) p[(int64_t)t * E + lane] = e0 / sum;
+        if (lane + 64 < E) p[(int64_t)t * E + lane + 64] = e1 / sum;
+        if (lane == 0) lse[t] = m + logf(sum);
+    }
+}
+
+// idx = {0, T, 0, Tp, then the ns + 1 token-range starts (multiples of 64)}
+__global__ void dwr_index_kernel(int T, int64_t Tp, int ns, int32_t *__restrict__ idx) {
+    const int i = threadIdx.x;
+    if (i == 0) {
+        idx[0] = 0;
+        idx[1] = T;
+        idx[2] = 0;
+        idx[3] = (int)Tp;
+    }
+    const int64_t chunks = Tp / 64;
+    for (int j = i; j <= ns; j += blockDim.x) idx[4 + j] = (int)(j * chunks / ns * 64);
+}
+
+// dW_r[e][c] = sum over the terms lo, mid, hi, and within each over the
+// token ranges in order, of the partial products C[sp][q Ep + e][c]
+__global__ __launch_bounds__(256) void dwr_sum_kernel(const float *__restrict__ C, int ns, int E, int Ep,
+                                                      int d, float *__restrict__ dWr) {
+    const int64_t n = (int64_t)E * d;
+    const int64_t stride = (int64_t)3 * Ep * d;
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
+        const int e = (int)(i / d), c = (int)(i - (int64_t)e * d);
+        float a = 0.f;
+        for (int q = 2; q >= 0; --q)
+            for (int sp = 0; sp < ns; ++sp) a += C[sp * stride + (int64_t)(q * Ep + e) * d + c];
+        dWr[i] = a;
+    }
+}
+
 // Weight gradients: for expert e, C_e[m][n] = sum over k in [offsets[e],
 // offsets[e+1]) of P[m][k] Q[n][k], P [M][ldk] and Q [N][ldk] bf16
 // (k-contiguous; the transposed activations), C [E][M][N] fp32.  128 x 128
@@ -649,14 +761,16 @@ hipError_t launch_router_bwd(const Shape &s, const void *x, const float *Wr, con
                              const float *noise, const int32_t *topk_idx, const float *gates,
                              const float *dg, const int32_t *row_of_slot, const float *f,
                              float alpha_aux, float alpha_z, float *p, float *lse, float *dh,
-                             hipStream_t st) {
+                             hipStream_t st, bool logits) {
     const unsigned g = grid_for(s.T, 4, 16384);
-    if (s.E <= 32)
-        hipLaunchKernelGGL(logits_wave_kernel, dim3(g), dim3(256), 0, st, (const uint16_t *)x, Wr, bias, noise,
-                           s.T, s.d, s.E, p, lse);
-    else
-        hipLaunchKernelGGL(logits_kernel, dim3((unsigned)((s.T + LG_TB - 1) / LG_TB)), dim3(256), 0, st,
-                           (const uint16_t *)x, Wr, bias, noise, s.T, s.d, s.E, p, lse);
+    if (logits) {
+        if (s.E <= 32)
+            hipLaunchKernelGGL(logits_wave_kernel, dim3(g), dim3(256), 0, st, (const uint16_t *)x, Wr, bias,
+                               noise, s.T, s.d, s.E, p, lse);
+        else
+            hipLaunchKernelGGL(logits_kernel, dim3((unsigned)((s.T + LG_TB - 1) / LG_TB)), dim3(256), 0, st,
+                               (const uint16_t *)x, Wr, bias, noise, s.T, s.d, s.E, p, lse);
+    }
     hipLaunchKernelGGL(router_bwd_kernel, dim3(g), dim3(256), 0, st, (const float *)p, (const float *)lse,
                        topk_idx, gates, dg, row_of_slot, f, s.T, s.E, s.k, s.gate, alpha_aux, alpha_z, dh);
     return hipGetLastError();
@@ -679,6 +793,75 @@ hipError_t launch_dwr(const Shape &s, const float *dh, const void *x, float *par
     const int64_t n = (int64_t)s.E * s.d;
     hipLaunchKernelGGL(dwr_reduce_kernel, dim3(grid_for(n, 256, 4096)), dim3(256), 0, st, (const float *)part,
                        n, dWr);
+    if (dbias) hipLaunchKernelGGL(dbias_kernel, dim3((unsigned)s.E), dim3(256), 0, st, dh, s.T, s.E, dbias);
+    return hipGetLastError();
+}
+
+DwrPlan dwr_plan(const Shape &s) {
+    DwrPlan pl{};
+    pl.Ep = (s.E + 7) / 8 * 8;
+    pl.Tp = ((int64_t)s.T + 63) / 64 * 64;
+    // E < 16: the token-split kernel is as fast (Mixtral layer, E = 8: 56
+    // against 55 us; the three terms fill only 3 Ep of a tile's 256 rows)
+    if (s.E < 16 || !wgrad_big_fits(3 * pl.Ep, s.d, pl.Tp) || pl.Tp / 64 > 65535) return pl;   // ns = 0
+    // about 512 blocks of 256 x 256 output tiles, each range >= 4 k stages
+    const int64_t tiles = (int64_t)((3 * pl.Ep + 255) / 256) * ((s.d + 255) / 256);
+    int64_t ns = (512 + tiles - 1) / tiles;
+    const int64_t most = pl.Tp / 256 > 0 ? pl.Tp / 256 : 1;
+    if (ns > most) ns = most;
+    if (ns > 64) ns = 64;
+    pl.ns = (int)(ns < 1 ? 1 : ns);
+    pl.xt_bytes = (size_t)s.d * pl.Tp * 2;
+    pl.p_bytes = (size_t)3 * pl.Ep * pl.Tp * 2;
+    pl.c_bytes = (size_t)pl.ns * 3 * pl.Ep * s.d * 4;
+    pl.idx_bytes = (size_t)(4 + pl.ns + 1) * 4;
+    return pl;
+}
+
+LogitsPlan logits_plan(const Shape &s) {
+    LogitsPlan pl{};
+    pl.Ep = (s.E + 7) / 8 * 8;
+    if (s.d % 64 != 0 || s.T % 8 != 0 || !wgrad_big_fits(s.T, 3 * pl.Ep, s.d)) return pl;   // ns = 0
+    const int64_t tiles = (int64_t)((s.T + 255) / 256) * ((3 * pl.Ep + 255) / 256);
+    int64_t ns = (512 + tiles - 1) / tiles;
+    const int64_t most = s.d / 256 > 0 ? s.d / 256 : 1;
+    if (ns > most) ns = most;
+    if (ns > 64) ns = 64;
+    pl.ns = (int)(ns < 1 ? 1 : ns);
+    pl.ws_bytes = (size_t)3 * pl.Ep * s.d * 2;
+    pl.c_bytes = (size_t)pl.ns * s.T * 3 * pl.Ep * 4;
+    pl.idx_bytes = (size_t)(4 + pl.ns + 1) * 4;
+    return pl;
+}
+
+hipError_t launch_logits_mfma(const Shape &s, const LogitsPlan &pl, const void *x, const float *Wr,
+                              const float *bias, const float *noise, void *wsplit, float *cpart,
+                              int32_t *idx, float *p, float *lse, hipStream_t st) {
+    if (pl.ns < 1) return hipErrorInvalidValue;
+    // ranges of d: idx[4 ..] (the first four entries are not used here)
+    hipLaunchKernelGGL(dwr_index_kernel, dim3(1), dim3(64), 0, st, s.d, (int64_t)s.d, pl.ns, idx);
+    hipLaunchKernelGGL(split_wr_kernel, dim3(grid_for((int64_t)pl.Ep * s.d, 256, 4096)), dim3(256), 0, st, Wr,
+                       s.E, pl.Ep, s.d, (uint16_t *)wsplit);
+    hipError_t err = launch_wgrad_big(pl.ns, s.T, 3 * pl.Ep, idx + 4, x, wsplit, s.d, cpart, st);
+    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL(logits_finish_kernel, dim3(grid_for(s.T, 4, 16384)), dim3(256), 0, st,
+                       (const float *)cpart, pl.ns, s.T, s.E, pl.Ep, bias, noise, p, lse);
+    return hipGetLastError();
+}
+
+hipError_t launch_dwr_mfma(const Shape &s, const DwrPlan &pl, const float *dh, const void *x, void *xt,
+                           void *pterms, float *cpart, int32_t *idx, float *dWr, float *dbias,
+                           hipStream_t st) {
+    if (pl.ns < 1) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(dwr_index_kernel, dim3(1), dim3(64), 0, st, s.T, pl.Tp, pl.ns, idx);
+    hipLaunchKernelGGL(split_dh_kernel, dim3((unsigned)(pl.Tp / 64), (unsigned)((pl.Ep + 63) / 64)), dim3(256),
+                       0, st, dh, s.T, s.E, pl.Ep, pl.Tp, (uint16_t *)pterms);
+    hipError_t err = launch_transpose_padded(x, s.d, s.d, idx, idx + 2, 1, pl.Tp, xt, st);
+    if (err != hipSuccess) return err;
+    err = launch_wgrad_big(pl.ns, 3 * pl.Ep, s.d, idx + 4, pterms, xt, pl.Tp, cpart, st);
+    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL(dwr_sum_kernel, dim3(grid_for((int64_t)s.E * s.d, 256, 4096)), dim3(256), 0, st,
+                       (const float *)cpart, pl.ns, s.E, pl.Ep, s.d, dWr);
     if (dbias) hipLaunchKernelGGL(dbias_kernel, dim3((unsigned)s.E), dim3(256), 0, st, dh, s.T, s.E, dbias);
     return hipGetLastError();
 }

@@ -310,6 +310,8 @@ struct BwdLayout {
     size_t dE, dg, dH, dA, dXp;
     size_t dET, HT, dAT, XT;
     size_t p, lse, dh, dwr_part, poff;
+    size_t dwr_xt, dwr_p, dwr_c, dwr_idx;   // dW_r on matrix cores (dwr_plan)
+    size_t lg_w, lg_c, lg_idx;              // logits on matrix cores (logits_plan)
     size_t total;
     int64_t R, ldk;
 };
@@ -348,8 +350,21 @@ BwdLayout bwd_layout(const Shape &s) {
     L.p = take((size_t)s.T * E * 4);
     L.lse = take((size_t)s.T * 4);
     L.dh = take((size_t)s.T * E * 4);
-    L.dwr_part = take(moe::dwr_part_floats(s) * 4);
     L.poff = take((E + 1) * 4);
+    const moe::DwrPlan pl = moe::dwr_plan(s);
+    if (pl.ns == 0) L.dwr_part = take(moe::dwr_part_floats(s) * 4);
+    if (pl.ns > 0) {
+        L.dwr_xt = take(pl.xt_bytes);
+        L.dwr_p = take(pl.p_bytes);
+        L.dwr_c = take(pl.c_bytes);
+        L.dwr_idx = take(pl.idx_bytes);
+    }
+    const moe::LogitsPlan lp = moe::logits_plan(s);
+    if (lp.ns > 0) {
+        L.lg_w = take(lp.ws_bytes);
+        L.lg_c = take(lp.c_bytes);
+        L.lg_idx = take(lp.idx_bytes);
+    }
     L.total = o;
     return L;
 }
@@ -645,10 +660,19 @@ int moe_backward(const moe_desc *desc, const void *x, const float *W_r, const fl
     MOE_TRY(moe::launch_act_bwd(s, a1, a3, dH, offsets, dA, st));
     if ((rc = grouped_gemm_f32(s, d, nup * f, dA, offsets, wcat, dXp, part2, st)) != MOE_OK) return rc;
     // router: gates, load-balancing and z terms; dx, dW_r, dbias
+    const moe::LogitsPlan lpl = moe::logits_plan(s);
+    if (lpl.ns > 0)
+        MOE_TRY(moe::launch_logits_mfma(s, lpl, x, W_r, bias, noise, w + L.lg_w, (float *)(w + L.lg_c),
+                                        (int32_t *)(w + L.lg_idx), p, lse, st));
     MOE_TRY(moe::launch_router_bwd(s, x, W_r, bias, noise, topk_idx, gates, dg, row_of_slot, stats,
-                                   alpha_aux, alpha_z, p, lse, dh, st));
+                                   alpha_aux, alpha_z, p, lse, dh, st, lpl.ns == 0));
     MOE_TRY(moe::launch_dx(s, dXp, row_of_slot, dh, W_r, dx, st));
-    MOE_TRY(moe::launch_dwr(s, dh, x, (float *)(w + L.dwr_part), dW_r, dbias, st));
+    const moe::DwrPlan dpl = moe::dwr_plan(s);
+    if (dpl.ns > 0)
+        MOE_TRY(moe::launch_dwr_mfma(s, dpl, dh, x, w + L.dwr_xt, w + L.dwr_p, (float *)(w + L.dwr_c),
+                                     (int32_t *)(w + L.dwr_idx), dW_r, dbias, st));
+    else
+        MOE_TRY(moe::launch_dwr(s, dh, x, (float *)(w + L.dwr_part), dW_r, dbias, st));
     // weight gradients over each expert's rows, from the activations
     // transposed into the padded layout
     int32_t *poff = (int32_t *)(w + L.poff);

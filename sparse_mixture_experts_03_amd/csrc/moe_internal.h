@@ -168,11 +168,12 @@ hipError_t launch_combine_bwd(const Shape &s, const void *dy, const float *Y, co
                               void *dE, float *dg, hipStream_t st);
 hipError_t launch_act_bwd(const Shape &s, const float *a1, const float *a3, const float *dH,
                           const int32_t *offsets, void *dA, hipStream_t st);
+// logits: false when p and lse are already there (launch_logits_mfma)
 hipError_t launch_router_bwd(const Shape &s, const void *x, const float *Wr, const float *bias,
                              const float *noise, const int32_t *topk_idx, const float *gates,
                              const float *dg, const int32_t *row_of_slot, const float *f,
                              float alpha_aux, float alpha_z, float *p, float *lse, float *dh,
-                             hipStream_t st);
+                             hipStream_t st, bool logits = true);
 hipError_t launch_dx(const Shape &s, const float *dXp, const int32_t *row_of_slot, const float *dh,
                      const float *Wr, float *dx, hipStream_t st);
 size_t dwr_part_floats(const Shape &s);
@@ -196,6 +197,38 @@ hipError_t launch_transpose_padded(const void *src, int64_t C, int64_t lds, cons
 // forward's grouped GEMM, for k ranges that start and end on multiples of
 // 64 (the padded layout), M and N multiples of 8 and both operands under
 // 2 GiB (wgrad_big_fits).
+// dW_r = sum over tokens of dh_t x_t^T on matrix cores: dh [T][E] fp32 split
+// into three bf16 terms (hi, mid = the rest's bf16, lo = what remains; their
+// sum carries dh's 24 significant bits), stacked as the rows of P [3 Ep][Tp]
+// (Ep = E rounded up to 8, Tp = T rounded up to 64, zero pads), x transposed
+// to [d][Tp]; the weight-gradient GEMM over ns token ranges (its "experts")
+// writes ns partial [3 Ep][d] products, which dwr_sum adds term by term
+// (lo, mid, hi), range by range in order.  ns == 0: not used (E < 16, or K
+// too large for 32-bit buffer offsets); the token-split kernel runs instead.
+struct DwrPlan {
+    int Ep, ns;
+    int64_t Tp;
+    size_t xt_bytes, p_bytes, c_bytes, idx_bytes;
+};
+DwrPlan dwr_plan(const Shape &s);
+hipError_t launch_dwr_mfma(const Shape &s, const DwrPlan &pl, const float *dh, const void *x, void *xt,
+                           void *pterms, float *cpart, int32_t *idx, float *dWr, float *dbias,
+                           hipStream_t st);
+// The router logits of the backward on matrix cores: W_r split into the
+// same three bf16 terms (rows q Ep + e of Ws [3 Ep][d]), h = x Ws^T through
+// the weight-gradient GEMM over ns ranges of d (its "experts"; x is already
+// [T][d], K-contiguous), the partial products added term by term (lo, mid,
+// hi) and range by range in order, then bias, noise, softmax and lse.
+// ns == 0: not used (d not a multiple of 64, T not a multiple of 8, or
+// operands past 32-bit offsets); the fp32 kernels run instead.
+struct LogitsPlan {
+    int Ep, ns;
+    size_t ws_bytes, c_bytes, idx_bytes;
+};
+LogitsPlan logits_plan(const Shape &s);
+hipError_t launch_logits_mfma(const Shape &s, const LogitsPlan &pl, const void *x, const float *Wr,
+                              const float *bias, const float *noise, void *wsplit, float *cpart,
+                              int32_t *idx, float *p, float *lse, hipStream_t st);
 hipError_t launch_wgrad(int E, int M, int N, const int32_t *koff, const void *P, const void *Q,
                         int64_t ldk, float *C, hipStream_t st);
 bool wgrad_big_fits(int M, int N, int64_t ldk);
