@@ -8,7 +8,9 @@ dW1, dW3, dW2) must be within 2e-2 * max|ref| (bf16 operands, fp32
 accumulation).  Cases: several row and column tiles with ragged tails,
 capacity drops, both gate conventions, SwiGLU / GELU / ReLU, an expert
 without rows, a decode-sized batch (the streaming kernels), and the
-256-row tiles with a K split in the recomputed down projection.
+256-row tiles with a K split in the recomputed down projection; and the
+full-size Mixtral prefill layer (sampled dx against the oracle, exact
+scaling in dy, reproducibility).
 """
 import numpy as np
 import pytest
@@ -104,3 +106,49 @@ def test_backward_deterministic():
     for key in a:
         if a[key] is not None:
             assert np.array_equal(a[key], b[key]), key
+
+
+def test_full_size_backward_mixtral():
+    """The Mixtral prefill layer at full size (T=4096, d=4096, d_ff=14336,
+    E=8, top-2, no capacity limit), in the launch configuration of
+    `bench.py --backward`, with the load-balancing and z weights at 0: then
+    each token's dx depends on that token alone, so the oracle's backward on
+    8 sampled tokens (their own routing, all kept) gives their dx exactly.
+    Every gradient of dy scaled by 2 must be exactly twice that of dy (a
+    power-of-two scale passes every bf16 and fp32 step unchanged), and the
+    call must repeat bit for bit."""
+    w = W["mixtral_prefill"]
+    print(f"[bwd] full size {w.name}", flush=True)
+    wt, tk = H.prepare(w)
+    dw, dt = H.device_weights(w, wt), H.device_tokens(w, tk)
+    desc = B.desc_for(w)
+    fwd = B.alloc_outputs(desc)
+    B.moe_forward(desc, dt["x"], dw["Wr"], dw["bias"], dt["noise"], dw["W1"], dw["W3"], dw["W2"],
+                  fwd["y"], B.workspace(desc), **{k: fwd[k] for k in fwd if k != "y"})
+    dy_bits = synth.to_bf16(np.random.default_rng(9).standard_normal((w.T, w.d)).astype(np.float32))
+    bws = B.backward_workspace(desc)
+    out = []
+    for scale in (1.0, 2.0, 1.0):
+        grads = B.alloc_grads(desc, bias=False)
+        dy = B.to_device(synth.to_bf16(synth.widen(dy_bits) * scale), "bf16")
+        B.moe_backward(desc, dt["x"], dw["Wr"], None, dt["noise"], dw["W1"], dw["W3"], dw["W2"],
+                       fwd, dy, grads, bws, 0.0, 0.0)
+        torch.cuda.synchronize()
+        out.append({k: v.cpu().numpy() for k, v in grads.items() if v is not None})
+    for key in out[0]:
+        assert np.isfinite(out[0][key]).all(), key
+        assert np.array_equal(out[0][key], out[2][key]), f"{key}: not reproducible"
+        assert np.array_equal(out[1][key], 2 * out[0][key]), f"{key}: dy * 2 does not double it"
+    # dx of sampled tokens against the oracle on those tokens alone
+    sample = H.sample_tokens(w.T, 8, seed=3)
+    ref_fw = H.reference(w, wt, tk, tokens=np.zeros(0, np.int64))
+    H.assert_routing_exact(w, {k: v.cpu() for k, v in fwd.items()}, ref_fw)
+    rows = ref_fw["row_of_slot"][sample]
+    assert (rows >= 0).all()
+    ref = oracle.backward(synth.widen(tk["x"][sample]), wt["Wr"], synth.widen(wt["W1"]),
+                          synth.widen(wt["W3"]), synth.widen(wt["W2"]), w.k, w.gate, w.cf, w.act,
+                          synth.widen(dy_bits[sample]), 0.0, 0.0, None, None, rows=rows)
+    g, r = out[0]["dx"][sample], ref["dx"]
+    scale = float(np.abs(r).max())
+    err = float(np.abs(g.astype(np.float64) - r).max())
+    assert err <= 2e-2 * scale, f"dx: max|err| {err:.3e} > 2e-2 * {scale:.3e}"
