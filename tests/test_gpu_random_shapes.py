@@ -2,7 +2,10 @@
 activation, capacity factor and dtype drawn within the supported ranges
 (bf16 widths multiples of 8), every one compared with the oracle like the
 hand-picked cases (routing bit-exact, statistics, y within tolerance,
-fully dropped tokens exactly zero).  The draws are fixed (seed 2024), so a
+fully dropped tokens exactly zero); likewise with 1-3 shared experts and
+the residual, with e4m3 expert weights (decode-sized batches, codes and
+scales bit-exact), and for the backward (every gradient within 2e-2 of
+its largest reference value).  The draws are fixed (seed 2024), so a
 failure names its case."""
 import numpy as np
 import pytest
@@ -47,3 +50,78 @@ def test_random_shape_matches_oracle(w):
     H.assert_y_close(w, y, ref["y"])
     full = (ref["row_of_slot"] < 0).all(axis=1)
     assert (y[full] == 0).all()
+
+
+def _draw_shared(i):
+    w = _draw(100 + i)
+    rng = np.random.default_rng([2024, 200 + i])
+    return w.with_(name=f"rand_sh{i}", dtype="bf16", d=max(8, w.d // 8 * 8), d_ff=max(8, w.d_ff // 8 * 8),
+                   n_shared=int(rng.integers(1, 4)), residual=bool(rng.integers(0, 2)))
+
+
+def _draw_fp8(i):
+    # decode-sized batches (at most 48 rows per expert), K a multiple of 128
+    rng = np.random.default_rng([2024, 300 + i])
+    E = int(rng.choice([1, 2, 4, 8, 13, 16]))
+    return synth.Workload(f"rand_f8_{i}", int(rng.integers(1, 49)), 128 * int(rng.integers(1, 9)),
+                          128 * int(rng.integers(1, 9)), E, int(rng.integers(1, min(E, 4) + 1)),
+                          str(rng.choice(["renorm", "switch"])), float(rng.choice([0.0, 0.5, 1.25])),
+                          str(rng.choice(["swiglu", "gelu", "relu"])), "bf16",
+                          noise_std=float(rng.choice([0.0, 0.1])), weights="e4m3")
+
+
+def _draw_bwd(i):
+    # small enough for the oracle's fp64 backward in about a second
+    rng = np.random.default_rng([2024, 400 + i])
+    E = int(rng.choice([1, 2, 3, 6, 8, 16, 20]))
+    return synth.Workload(f"rand_bw{i}", int(rng.choice([1, 9, 64, 100, 257, 300])),
+                          8 * int(rng.integers(1, 33)), 8 * int(rng.integers(1, 65)), E,
+                          int(rng.integers(1, min(E, 3) + 1)), str(rng.choice(["renorm", "switch"])),
+                          float(rng.choice([0.0, 0.5, 1.25])), str(rng.choice(["swiglu", "gelu", "relu"])),
+                          "bf16", noise_std=float(rng.choice([0.0, 0.1])))
+
+
+SHARED_CASES = [_draw_shared(i) for i in range(8)]
+FP8_CASES = [_draw_fp8(i) for i in range(10)]
+BWD_CASES = [_draw_bwd(i) for i in range(10)]
+
+
+def _ids(w):
+    return f"{w.name}-T{w.T}-d{w.d}-f{w.d_ff}-E{w.E}-k{w.k}-{w.gate}-{w.act}-cf{w.cf}"
+
+
+@pytest.mark.parametrize("w", SHARED_CASES, ids=_ids)
+def test_random_shape_shared_matches_oracle(w):
+    print(f"[rand shared] {w}", flush=True)
+    wt, tk = H.prepare(w)
+    ref = H.reference(w, wt, tk)
+    got = H.run_forward(w, H.device_weights(w, wt), H.device_tokens(w, tk))
+    H.assert_routing_exact(w, got, ref)
+    H.assert_stats_close(w, got, ref)
+    H.assert_y_close(w, H.y_float(got["y"]), ref["y"])
+
+
+@pytest.mark.parametrize("w", FP8_CASES, ids=_ids)
+def test_random_shape_fp8_matches_oracle(w):
+    print(f"[rand fp8] {w}", flush=True)
+    wt, tk = H.prepare(w)
+    qref = H.quantize_ref(wt)
+    dw, dt = H.device_weights(w, wt), H.device_tokens(w, tk)
+    f8 = H.device_fp8(dw)
+    H.assert_fp8_equal(f8, qref)
+    ref = H.reference_fp8(w, wt, tk, qref)
+    got = H.run_forward_fp8(w, dw, dt, f8)
+    H.assert_routing_exact(w, got, ref)
+    H.assert_stats_close(w, got, ref)
+    y = H.y_float(got["y"])
+    H.assert_y_close(w, y, ref["y"])
+    assert (y[(ref["row_of_slot"] < 0).all(axis=1)] == 0).all()
+
+
+@pytest.mark.parametrize("w", BWD_CASES, ids=_ids)
+def test_random_shape_backward_matches_oracle(w):
+    from test_gpu_backward import _check, _run
+
+    print(f"[rand bwd] {w}", flush=True)
+    got, ref, _ = _run(w)
+    _check(got, ref)
