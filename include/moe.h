@@ -391,7 +391,9 @@ int moe_forward_fp8(const moe_desc *desc, const void *x, const float *W_r, const
  * routing moe_forward took (held fixed: pass its topk_idx, gates, offsets,
  * row_of_slot, token_of_row and stats, with the same x, weights, bias and
  * noise).  The expert activations are recomputed (nothing else of the
- * forward is needed).  bf16 layers only (MOE_ERR_UNSUPPORTED otherwise).
+ * forward is needed).  bf16 layers only, and at most about 4.19 million
+ * kept rows (65535 * 64 once each expert's count is rounded up to 64);
+ * MOE_ERR_UNSUPPORTED otherwise, before any launch.
  *   dy     [T][d]          bf16   gradient of the layer output
  *   dx     [T][d]          fp32
  *   dW_r   [E][d]          fp32
@@ -402,7 +404,9 @@ int moe_forward_fp8(const moe_desc *desc, const void *x, const float *W_r, const
  * sums run in a fixed order, so results are reproducible.  Internally the
  * weights are transposed into the workspace once per call, the expert
  * GEMMs use the forward's grouped GEMM kernels, and the weight gradients a
- * GEMM over each expert's row block.  ws: moe_backward_workspace_size().
+ * GEMM over each expert's row block (activations transposed into a layout
+ * whose experts start on multiples of 64 rows, zero-padded).  ws:
+ * moe_backward_workspace_size().
  */
 int moe_backward_workspace_size(const moe_desc *desc, size_t *bytes);
 

@@ -606,7 +606,9 @@ int moe_backward_workspace_size(const moe_desc *desc, size_t *bytes) {
     if (rc != MOE_OK) return rc;
     if (!bytes) return MOE_ERR_INVALID_ARG;
     if (s.dtype != MOE_DTYPE_BF16) return MOE_ERR_UNSUPPORTED;
-    *bytes = bwd_layout(s).total;
+    const BwdLayout L = bwd_layout(s);
+    if (L.ldk / 64 > 65535) return MOE_ERR_UNSUPPORTED;   // padded transposes' grid
+    *bytes = L.total;
     return MOE_OK;
 }
 
@@ -629,6 +631,9 @@ int moe_backward(const moe_desc *desc, const void *x, const float *W_r, const fl
     if (dbias && !bias) return MOE_ERR_INVALID_ARG;
     if (!std::isfinite(alpha_aux) || !std::isfinite(alpha_z)) return MOE_ERR_INVALID_ARG;
     const BwdLayout L = bwd_layout(s);
+    // kept rows (rounded per expert to 64) past 65535 * 64: the padded
+    // transposes' grid would not fit; rejected before any launch
+    if (L.ldk / 64 > 65535) return MOE_ERR_UNSUPPORTED;
     if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
     hipStream_t st = (hipStream_t)stream;
     const int d = s.d, f = s.d_ff, E = s.E, nup = swiglu ? 2 : 1;

@@ -260,3 +260,21 @@ def test_backward_validation_before_launch():
     assert lib.moe_backward(ctypes.byref(f32), *args, 0.0, 0.0, *outs, FAKE, need, None) == -2
     with pytest.raises(B.MoeError):
         B.moe_backward_workspace_size(f32)
+
+
+def test_backward_rejects_too_many_rows_before_launch():
+    """Kept rows past 65535 * 64 (after each expert's count is rounded up to
+    64) do not fit the padded transposes' grid: MOE_ERR_UNSUPPORTED from the
+    workspace query and from moe_backward, before any launch."""
+    lib = B.load()
+    big = B.make_desc(65535 * 64 + 1, 8, 8, 1, 1, act="relu", dtype="bf16")
+    with pytest.raises(B.MoeError):
+        B.moe_backward_workspace_size(big)
+    args = [FAKE] * 14
+    args[2] = None          # bias
+    args[3] = None          # noise
+    args[5] = None          # W3 (ReLU)
+    outs = [FAKE, FAKE, None, FAKE, None, FAKE]
+    assert lib.moe_backward(ctypes.byref(big), *args, 0.0, 0.0, *outs, FAKE, 1 << 62, None) == -2
+    ok = B.make_desc(65535 * 64 - 128, 8, 8, 1, 1, act="relu", dtype="bf16")
+    assert B.moe_backward_workspace_size(ok) > 0
