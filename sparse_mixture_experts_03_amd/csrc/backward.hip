@@ -248,20 +248,11 @@ __global__ __launch_bounds__(256) void act_bwd_kernel(const float *__restrict__ 
     const int nup = act == ACT_SWIGLU ? 2 : 1;
     for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
         const int64_t r = i / d_ff, f = i - r * d_ff;
-        const float u = a1[i], g = dH[i];
         uint16_t *row = dA + r * nup * d_ff;
-        if (act == ACT_SWIGLU) {
-            const float v = a3[i];
-            const float sg = 1.f / (1.f + expf(-u));
-            row[f] = f32_to_bf16(g * v * sg * (1.f + u * (1.f - sg)));
-            row[d_ff + f] = f32_to_bf16(g * u * sg);
-        } else if (act == ACT_GELU) {
-            const float Phi = 0.5f * (1.f + erff(u * 0.70710678118654752f));
-            const float phi = expf(-0.5f * u * u) * 0.39894228040143268f;
-            row[f] = f32_to_bf16(g * (Phi + u * phi));
-        } else {
-            row[f] = f32_to_bf16(u > 0.f ? g : 0.f);
-        }
+        uint16_t da1, da3 = 0;
+        act_bwd_elem(act, a1[i], act == ACT_SWIGLU ? a3[i] : 0.f, dH[i], da1, da3);
+        row[f] = da1;
+        if (act == ACT_SWIGLU) row[d_ff + f] = da3;
     }
 }
 

@@ -269,6 +269,7 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 
+
 // Expert activations of the GEMM epilogues (ACT_NONE: the down projection).
 constexpr int ACT_RELU = 0, ACT_GELU = 1, ACT_SWIGLU = 2, ACT_NONE = 3;
 
@@ -280,6 +281,24 @@ __device__ __forceinline__ float apply_act(int act, float a1, float a3) {
     if (act == ACT_GELU) return 0.5f * a1 * (1.f + erff(a1 * 0.70710678118654752f));
     if (act == ACT_RELU) return fmaxf(a1, 0.f);
     return a1;
+}
+
+// Activation backward of one element: u = a1, v = a3 (SwiGLU), g = dH; da1
+// and (SwiGLU) da3 as bf16 bits.  SwiGLU: H = silu(u) v; GELU (erf form);
+// ReLU (derivative 0 at u = 0).
+__device__ __forceinline__ void act_bwd_elem(int act, float u, float v, float g, uint16_t &da1,
+                                             uint16_t &da3) {
+    if (act == ACT_SWIGLU) {
+        const float sg = 1.f / (1.f + expf(-u));
+        da1 = f32_to_bf16(g * v * sg * (1.f + u * (1.f - sg)));
+        da3 = f32_to_bf16(g * u * sg);
+    } else if (act == ACT_GELU) {
+        const float Phi = 0.5f * (1.f + erff(u * 0.70710678118654752f));
+        const float phi = expf(-0.5f * u * u) * 0.39894228040143268f;
+        da1 = f32_to_bf16(g * (Phi + u * phi));
+    } else {
+        da1 = f32_to_bf16(u > 0.f ? g : 0.f);
+    }
 }
 
 }  // namespace moe

@@ -8,7 +8,8 @@ dW1, dW3, dW2) must be within 2e-2 * max|ref| (bf16 operands, fp32
 accumulation).  Cases: several row and column tiles with ragged tails,
 capacity drops, both gate conventions, SwiGLU / GELU / ReLU, an expert
 without rows, a decode-sized batch (the streaming kernels), and the
-256-row tiles with a K split in the recomputed down projection; and the
+256-row tiles with a K split in the recomputed down projection (and
+those tiles for every GEMM of a ReLU layer in b_big_relu); and the
 full-size Mixtral prefill layer (sampled dx against the oracle, exact
 scaling in dy, reproducibility).
 """
@@ -34,6 +35,9 @@ BWD = {
                                  dtype="bf16"),
     "b_decode": W["mixtral_decode"].with_(name="b_decode", d=256, d_ff=384),
     "b_big_splitk": W["mixtral_prefill"].with_(name="b_big_splitk", T=1024, d=320, d_ff=4096, E=4),
+    # 256-row tiles for every GEMM of a ReLU layer
+    "b_big_relu": W["mixtral_prefill"].with_(name="b_big_relu", T=512, d=128, d_ff=264, E=2, k=1,
+                                             act="relu"),
 }
 
 
