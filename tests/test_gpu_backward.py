@@ -35,6 +35,9 @@ BWD = {
                                  dtype="bf16"),
     "b_decode": W["mixtral_decode"].with_(name="b_decode", d=256, d_ff=384),
     "b_big_splitk": W["mixtral_prefill"].with_(name="b_big_splitk", T=1024, d=320, d_ff=4096, E=4),
+    # E >= 16, T a multiple of 8 and d of 64: the router's logits and dW_r
+    # on matrix cores; capacity drops
+    "b_router_mfma": W["finegrained_zipf"].with_(name="b_router_mfma", T=256, d=192, d_ff=64, E=32),
     # 256-row tiles for every GEMM of a ReLU layer
     "b_big_relu": W["mixtral_prefill"].with_(name="b_big_relu", T=512, d=128, d_ff=264, E=2, k=1,
                                              act="relu"),
