@@ -73,6 +73,8 @@ extern "C" {
 #define MOE_ERR_UNSUPPORTED (-2) /* valid but outside what the kernels handle */
 #define MOE_ERR_HIP (-3)         /* the HIP runtime reported an error        */
 #define MOE_ERR_WORKSPACE (-4)   /* ws_bytes below moe_workspace_size()       */
+#define MOE_ERR_SCRATCH (-5)     /* moe_forward_noalloc: needs more than the
+                                    static scratch (MOE_NOALLOC_SCRATCH_BYTES) */
 
 /* ---- gate conventions ("Top-k gating") ---------------------------------- */
 /* Renormalised top-k (Mixtral): softmax over the k selected logits. */
@@ -417,6 +419,37 @@ int moe_backward(const moe_desc *desc, const void *x, const float *W_r, const fl
                  const void *dy, float alpha_aux, float alpha_z, float *dx, float *dW_r,
                  float *dbias, float *dW1, float *dW3, float *dW2, void *ws, size_t ws_bytes,
                  void *stream);
+
+/* ---- a forward pass that allocates nothing ----------------------------------
+ *
+ * For callers that cannot call hipMalloc or take a workspace argument:
+ * code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation.  moe_forward_noalloc is moe_forward (same arguments minus ws
+ * and ws_bytes, same kernels, same results bit for bit) whose workspace is a
+ * static device array of MOE_NOALLOC_SCRATCH_BYTES inside the library: each
+ * device the library runs on holds its own copy of that array from its first
+ * use until the process ends.  The call allocates nothing and calls no
+ * allocating routine; its first call on a device looks up that device's
+ * copy (hipGetSymbolAddress) with the device current.
+ *
+ * Limit: the description's moe_workspace_size() must be at most
+ * MOE_NOALLOC_SCRATCH_BYTES (64 MiB: e.g. a decode batch of the
+ * Mixtral-shape layer, or T = 4096 on the Switch-shape layer); larger
+ * problems return MOE_ERR_SCRATCH before anything is enqueued.
+ * Every call on one device shares that device's array, which keeps the
+ * last call's contents: calls that overlap on one device (concurrent
+ * streams, or host threads) race and must be serialised by the caller
+ * (successive calls on one stream are ordered and safe).  Nothing in the
+ * array needs to start at zero: the kernels initialise what they read.
+ * Other errors as moe_forward; a failed device lookup returns MOE_ERR_HIP.
+ */
+#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+int moe_forward_noalloc(const moe_desc *desc, const void *x, const float *W_r, const float *bias,
+                        const float *noise, const void *W1, const void *W3, const void *W2,
+                        void *y, int32_t *topk_idx, float *gates, int32_t *routed_counts,
+                        int32_t *kept_counts, int32_t *offsets, int32_t *row_of_slot,
+                        int32_t *token_of_row, uint8_t *dropped, float *stats, void *stream);
 
 /* A static, human-readable name for a status code. */
 const char *moe_status_string(int status);

@@ -11,7 +11,9 @@ moe_dispatch, moe_expert_ffn, moe_combine, moe_forward, and for shared
 experts plus the block residual moe_workspace_size_shared, moe_shared_ffn,
 moe_combine_shared, moe_forward_shared, and for E4M3 expert weights
 moe_quantize_e4m3, moe_expert_ffn_fp8, moe_forward_fp8, and for training
-moe_backward_workspace_size, moe_backward.
+moe_backward_workspace_size, moe_backward, and the forward without a
+workspace argument (its workspace is a static device array in the library)
+moe_forward_noalloc.
 """
 from __future__ import annotations
 
@@ -36,7 +38,8 @@ MAX_SHARED = 16
 
 MOE_OK = 0
 STATUS = {0: "MOE_OK", -1: "MOE_ERR_INVALID_ARG", -2: "MOE_ERR_UNSUPPORTED", -3: "MOE_ERR_HIP",
-          -4: "MOE_ERR_WORKSPACE"}
+          -4: "MOE_ERR_WORKSPACE", -5: "MOE_ERR_SCRATCH"}
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 class MoeError(RuntimeError):
@@ -98,6 +101,7 @@ def load(build_if_missing: bool = True):
     lib.moe_expert_ffn.argtypes = [D, P, P, P, P, P, P, P, sz, P]
     lib.moe_combine.argtypes = [D, P, P, P, P, P]
     lib.moe_forward.argtypes = [D, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, sz, P]
+    lib.moe_forward_noalloc.argtypes = [D, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P]
     SH = ctypes.POINTER(MoeShared)
     lib.moe_workspace_size_shared.argtypes = [D, SH, ctypes.POINTER(ctypes.c_size_t)]
     lib.moe_shared_ffn.argtypes = [D, SH, P, P, P, sz, P]
@@ -115,7 +119,8 @@ def load(build_if_missing: bool = True):
     for fn in ("moe_workspace_size", "moe_capacity", "moe_route", "moe_dispatch",
                "moe_expert_ffn", "moe_combine", "moe_forward", "moe_workspace_size_shared",
                "moe_shared_ffn", "moe_combine_shared", "moe_forward_shared", "moe_quantize_e4m3",
-               "moe_expert_ffn_fp8", "moe_forward_fp8", "moe_backward_workspace_size", "moe_backward"):
+               "moe_expert_ffn_fp8", "moe_forward_fp8", "moe_backward_workspace_size", "moe_backward",
+               "moe_forward_noalloc"):
         getattr(lib, fn).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -264,6 +269,31 @@ def moe_forward(desc, x, W_r, bias, noise, W1, W3, W2, y, ws, topk_idx=None, gat
         _ptr(stats, torch.float32, (2 * E + 2,), "stats", True),
         _ptr(ws, torch.uint8, None, "ws"), ws.numel(), _stream(stream))
     _check("moe_forward", rc)
+
+
+def moe_forward_noalloc(desc, x, W_r, bias, noise, W1, W3, W2, y, topk_idx=None, gates=None,
+                        routed_counts=None, kept_counts=None, offsets=None, row_of_slot=None,
+                        token_of_row=None, dropped=None, stats=None, stream=None):
+    """moe_forward with the library's static device scratch as its workspace
+    (no workspace argument; calls on one device must not overlap)."""
+    T, d, d_ff, E, k = desc.T, desc.d, desc.d_ff, desc.E, desc.k
+    dt = _act_dtype(desc)
+    rc = load().moe_forward_noalloc(
+        ctypes.byref(desc), _ptr(x, dt, (T, d), "x"), _ptr(W_r, torch.float32, (E, d), "W_r"),
+        _ptr(bias, torch.float32, (E,), "bias", True),
+        _ptr(noise, torch.float32, (T, E), "noise", True),
+        _ptr(W1, dt, (E, d_ff, d), "W1"), _ptr(W3, dt, (E, d_ff, d), "W3", True),
+        _ptr(W2, dt, (E, d, d_ff), "W2"), _ptr(y, dt, (T, d), "y"),
+        _ptr(topk_idx, torch.int32, (T, k), "topk_idx", True),
+        _ptr(gates, torch.float32, (T, k), "gates", True),
+        _ptr(routed_counts, torch.int32, (E,), "routed_counts", True),
+        _ptr(kept_counts, torch.int32, (E,), "kept_counts", True),
+        _ptr(offsets, torch.int32, (E + 1,), "offsets", True),
+        _ptr(row_of_slot, torch.int32, (T, k), "row_of_slot", True),
+        _ptr(token_of_row, torch.int32, (T * k,), "token_of_row", True),
+        _ptr(dropped, torch.uint8, (T, k), "dropped", True),
+        _ptr(stats, torch.float32, (2 * E + 2,), "stats", True), _stream(stream))
+    _check("moe_forward_noalloc", rc)
 
 
 def moe_shared_ffn(desc, shared: MoeShared, x, y_shared, ws, stream=None):

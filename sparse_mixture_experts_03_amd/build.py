@@ -16,7 +16,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmoe.so")
 SOURCES = ["moe_api.cpp", "route.hip", "dispatch.hip", "expert_gemm.hip", "combine.hip",
-           "shared.hip", "expert_fp8.hip", "backward.hip"]
+           "shared.hip", "expert_fp8.hip", "backward.hip", "noalloc.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",

@@ -506,6 +506,23 @@ int moe_forward(const moe_desc *desc, const void *x, const float *W_r, const flo
                         stats, ws, ws_bytes, stream);
 }
 
+int moe_forward_noalloc(const moe_desc *desc, const void *x, const float *W_r, const float *bias,
+                        const float *noise, const void *W1, const void *W3, const void *W2,
+                        void *y, int32_t *topk_idx, float *gates, int32_t *routed_counts,
+                        int32_t *kept_counts, int32_t *offsets, int32_t *row_of_slot,
+                        int32_t *token_of_row, uint8_t *dropped, float *stats, void *stream) {
+    Shape s;
+    int rc = check_desc(desc, &s);
+    if (rc != MOE_OK) return rc;
+    const size_t need = layout(s).total;
+    if (need > MOE_NOALLOC_SCRATCH_BYTES) return MOE_ERR_SCRATCH;
+    void *ws = nullptr;
+    if (moe::noalloc_scratch(&ws) != hipSuccess) return MOE_ERR_HIP;
+    return forward_impl(desc, nullptr, nullptr, x, W_r, bias, noise, W1, W3, W2, y, topk_idx, gates,
+                        routed_counts, kept_counts, offsets, row_of_slot, token_of_row, dropped,
+                        stats, ws, need, stream);
+}
+
 int moe_workspace_size_shared(const moe_desc *desc, const moe_shared *shared, size_t *bytes) {
     Shape s;
     int rc = check_desc(desc, &s);
@@ -701,6 +718,9 @@ const char *moe_status_string(int status) {
     case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED: valid but not supported by the kernels";
     case MOE_ERR_HIP: return "MOE_ERR_HIP: the HIP runtime reported an error";
     case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE: workspace smaller than moe_workspace_size()";
+    case MOE_ERR_SCRATCH:
+        return "MOE_ERR_SCRATCH: moe_forward_noalloc needs more than its static scratch "
+               "(MOE_NOALLOC_SCRATCH_BYTES)";
     default: return "unknown moe status";
     }
 }

@@ -235,6 +235,12 @@ bool wgrad_big_fits(int M, int N, int64_t ldk);
 hipError_t launch_wgrad_big(int E, int M, int N, const int32_t *koff, const void *P, const void *Q,
                             int64_t ldk, float *C, hipStream_t st);
 
+// ---- static scratch of moe_forward_noalloc --------------------------------
+// The device address of the current device's copy of the library's static
+// scratch array (MOE_NOALLOC_SCRATCH_BYTES), looked up on first use per
+// device and kept.
+hipError_t noalloc_scratch(void **ptr);
+
 // ---- combine -------------------------------------------------------------
 // y_perm_part2: nullptr, or the second K half of a split down projection.
 hipError_t launch_combine(const Shape &s, const float *y_perm, const float *y_perm_part2,

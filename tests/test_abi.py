@@ -36,7 +36,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_status_strings():
     assert B.status_string(0) == "MOE_OK"
-    for code in (-1, -2, -3, -4):
+    for code in (-1, -2, -3, -4, -5):
         assert B.STATUS[code] in B.status_string(code)
     assert "unknown" in B.status_string(7)
 
@@ -65,6 +65,7 @@ def test_invalid_descriptions_are_rejected(field, value, code):
     assert lib.moe_expert_ffn(ctypes.byref(desc), *n[:7], 1 << 40, None) == code
     assert lib.moe_combine(ctypes.byref(desc), *n[:4], None) == code
     assert lib.moe_forward(ctypes.byref(desc), *n[:18], 1 << 40, None) == code
+    assert lib.moe_forward_noalloc(ctypes.byref(desc), *n[:17], None) == code
 
 
 def test_f32_allows_any_width():
@@ -278,3 +279,12 @@ def test_backward_rejects_too_many_rows_before_launch():
     assert lib.moe_backward(ctypes.byref(big), *args, 0.0, 0.0, *outs, FAKE, 1 << 62, None) == -2
     ok = B.make_desc(65535 * 64 - 128, 8, 8, 1, 1, act="relu", dtype="bf16")
     assert B.moe_backward_workspace_size(ok) > 0
+
+
+def test_noalloc_rejects_past_its_scratch_before_launch():
+    """A layer whose workspace exceeds the static scratch is refused with
+    MOE_ERR_SCRATCH before any HIP call (so also without a GPU)."""
+    lib = B.load()
+    desc = B.make_desc(4096, 4096, 14336, 8, 2)
+    assert B.moe_workspace_size(desc) > B.NOALLOC_SCRATCH_BYTES
+    assert lib.moe_forward_noalloc(ctypes.byref(desc), *([FAKE] * 17), None) == -5
