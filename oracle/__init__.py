@@ -45,7 +45,7 @@ def _load():
     lib.orc_dispatch.argtypes = [i64, i64, i64, i64, ip, ip, ip, ip, ip, ip, ip]
     lib.orc_dispatch.restype = None
     lib.orc_expert_ffn.argtypes = [i64, ip, ip, i64, i64, ctypes.c_int, fp, fp, fp, fp, fp, fp, fp, fp]
-    lib.orc_expert_ffn.restype = None
+    lib.orc_expert_ffn.restype = ctypes.c_int
     lib.orc_combine.argtypes = [i64, i64, i64, dp, ip, fp, fp]
     lib.orc_combine.restype = None
     lib.orc_combine_shared.argtypes = [i64, i64, i64, i64, dp, ip, fp, fp, fp, fp]
@@ -66,6 +66,8 @@ def _load():
     lib.orc_backward.restype = ctypes.c_int
     lib.orc_threads.argtypes = []
     lib.orc_threads.restype = ctypes.c_int
+    lib.orc_set_threads.argtypes = [ctypes.c_int]
+    lib.orc_set_threads.restype = None
     _lib = lib
     return lib
 
@@ -150,8 +152,10 @@ def expert_ffn(tok, ex, x, W1, W3, W2, act, scales=None):
         assert S1.shape == W1.shape[:2] and S2.shape == W2.shape[:2]
         assert S3 is None or S3.shape == W1.shape[:2]
     out = np.empty((n, d), np.float32)
-    _load().orc_expert_ffn(n, _p(tok), _p(ex), d, d_ff, _ACT[act], _p(x), _p(W1),
-                           _p(W3), _p(W2), _p(S1), _p(S3), _p(S2), _p(out))
+    rc = _load().orc_expert_ffn(n, _p(tok), _p(ex), d, d_ff, _ACT[act], _p(x), _p(W1),
+                                _p(W3), _p(W2), _p(S1), _p(S3), _p(S2), _p(out))
+    if rc != 0:
+        raise MemoryError("orc_expert_ffn: could not allocate its per-thread scratch")
     return out
 
 
@@ -269,6 +273,12 @@ def backward(x, Wr, W1, W3, W2, k, mode, cf, act, dy, alpha_aux=0.0, alpha_z=0.0
 def threads():
     """Host threads the oracle's parallel loops use."""
     return int(_load().orc_threads())
+
+
+def set_threads(n):
+    """Sets the host threads of the oracle's parallel loops (results do not
+    depend on it: threads split tokens and rows, never a sum)."""
+    _load().orc_set_threads(int(n))
 
 
 def route(x, Wr, k, mode, bias=None, noise=None):

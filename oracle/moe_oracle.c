@@ -114,8 +114,16 @@ int orc_gate(int64_t T, int64_t E, int64_t k, int mode, const float *h,
     if (k < 1 || k > E || (mode != ORC_GATE_RENORM && mode != ORC_GATE_SWITCH))
         return -1;
     int bad = 0;
-#pragma omp parallel for schedule(static) reduction(| : bad)
+#pragma omp parallel reduction(| : bad)
+    {
+    /* per-thread mark of the experts already taken, reset for every token */
+    char *taken = (char *)malloc((size_t)E);
+    if (!taken)
+        bad = 1;
+#pragma omp for schedule(static)
     for (int64_t t = 0; t < T; ++t) {
+        if (!taken)
+            continue;
         const float *ht = h + t * E;
         /* full softmax in double */
         double m = (double)ht[0];
@@ -133,11 +141,7 @@ int orc_gate(int64_t T, int64_t E, int64_t k, int mode, const float *h,
 
         /* top-k by k successive scans for the best expert not yet taken;
          * the strict '>' on an ascending scan keeps the lower index on a tie */
-        char *taken = (char *)calloc((size_t)E, 1);
-        if (!taken) {
-            bad = 1;
-            continue;
-        }
+        memset(taken, 0, (size_t)E);
         int32_t *it = idx + t * k;
         for (int64_t sl = 0; sl < k; ++sl) {
             int64_t best = -1;
@@ -147,7 +151,6 @@ int orc_gate(int64_t T, int64_t E, int64_t k, int mode, const float *h,
             taken[best] = 1;
             it[sl] = (int32_t)best;
         }
-        free(taken);
 
         double *gt = gates + t * k;
         if (mode == ORC_GATE_RENORM) {
@@ -162,6 +165,8 @@ int orc_gate(int64_t T, int64_t E, int64_t k, int mode, const float *h,
             for (int64_t sl = 0; sl < k; ++sl)
                 gt[sl] = exp((double)ht[it[sl]] - m) / s;
         }
+    }
+    free(taken);
     }
     return bad ? -1 : 0;
 }
@@ -260,31 +265,36 @@ static double orc_act(int act, double a1, double a3)
  *   S1, S3   [E][d_ff]      fp32 per-row weight scales, or NULL (scale 1)
  *   S2       [E][d]         fp32 per-row weight scales, or NULL
  *   out      [n][d]         fp32: out[r] = fl32(W2_e fl32(act(W1_e x, W3_e x)))
+ * Returns 0, or -1 when a thread's scratch cannot be allocated (then out is
+ * incomplete and must not be used).
  * With scales, weight row i of a matrix is scale[i] times its stored row
  * (a row-scaled quantised matrix, orc_quantize_e4m3): each row's product
  * with the input is summed from the stored values and multiplied by the
  * scale once, in double, which equals the product with the scaled row.
  */
-void orc_expert_ffn(int64_t n, const int32_t *tok, const int32_t *ex,
-                    int64_t d, int64_t d_ff, int act, const float *x,
-                    const float *W1, const float *W3, const float *W2,
-                    const float *S1, const float *S3, const float *S2,
-                    float *out)
+int orc_expert_ffn(int64_t n, const int32_t *tok, const int32_t *ex,
+                   int64_t d, int64_t d_ff, int act, const float *x,
+                   const float *W1, const float *W3, const float *W2,
+                   const float *S1, const float *S3, const float *S2,
+                   float *out)
 {
-#pragma omp parallel for schedule(dynamic, 1)
+    int bad = 0;
+#pragma omp parallel reduction(| : bad)
+    {
+    /* per-thread scratch: the hidden row and the widened input row */
+    float *H = (float *)malloc((size_t)d_ff * sizeof(float));
+    double *xd = (double *)malloc((size_t)(d > d_ff ? d : d_ff) * sizeof(double));
+    if (!H || !xd)
+        bad = 1;
+#pragma omp for schedule(dynamic, 1)
     for (int64_t r = 0; r < n; ++r) {
+        if (!H || !xd)
+            continue;   /* reported through the return value */
         const float *xr = x + (int64_t)tok[r] * d;
         const int64_t e = ex[r];
         const float *w1 = W1 + e * d_ff * d;
         const float *w3 = (act == ORC_ACT_SWIGLU) ? W3 + e * d_ff * d : NULL;
         const float *w2 = W2 + e * d * d_ff;
-        float *H = (float *)malloc((size_t)d_ff * sizeof(float));
-        double *xd = (double *)malloc((size_t)(d > d_ff ? d : d_ff) * sizeof(double));
-        if (!H || !xd) {
-            free(H);
-            free(xd);
-            continue;
-        }
         for (int64_t j = 0; j < d; ++j)
             xd[j] = (double)xr[j];
         /* hidden: H_f = fl32(act(sum_j x_j W1[f][j], sum_j x_j W3[f][j])) */
@@ -319,9 +329,11 @@ void orc_expert_ffn(int64_t n, const int32_t *tok, const int32_t *ex,
             for (int64_t u = 0; u < nb; ++u)
                 out[r * d + o0 + u] = (float)(S2 ? acc[u] * (double)S2[e * d + o0 + u] : acc[u]);
         }
-        free(H);
-        free(xd);
     }
+    free(H);
+    free(xd);
+    }
+    return bad ? -1 : 0;
 }
 
 /*
@@ -790,5 +802,17 @@ int orc_threads(void)
     return omp_get_max_threads();
 #else
     return 1;
+#endif
+}
+
+/* Sets that number (n >= 1); results do not depend on it, since threads
+ * split tokens and rows, never a sum. */
+void orc_set_threads(int n)
+{
+#ifdef _OPENMP
+    if (n >= 1)
+        omp_set_num_threads(n);
+#else
+    (void)n;
 #endif
 }
