@@ -176,6 +176,11 @@ int moe_route(const moe_desc *desc, const void *x, const float *W_r, const float
  * Then x_perm[r] = x[token_of_row[r]] for r < offsets[E].
  * Input x, topk_idx; outputs routed_counts, kept_counts, offsets,
  * row_of_slot, token_of_row, dropped, x_perm.
+ * topk_idx must hold, for every token, k distinct experts in [0, E) (as
+ * moe_route returns them).  An entry outside [0, E), or one repeating an
+ * expert of an earlier slot of the same token, is not a valid choice: it is
+ * treated as dropped (dropped = 1, row_of_slot = -1) and counted nowhere,
+ * so no expert gets more rows than tokens.
  */
 int moe_dispatch(const moe_desc *desc, const void *x, const int32_t *topk_idx,
                  int32_t *routed_counts, int32_t *kept_counts, int32_t *offsets,

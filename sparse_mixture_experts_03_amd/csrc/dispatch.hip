@@ -34,8 +34,24 @@ namespace {
 constexpr int DP_THREADS = 256;
 constexpr int DP_EMAX = 128;
 
+// The expert of assignment j (token j / k, slot j % k), or -1 when the
+// assignment is not a valid choice: an index outside [0, E), or an expert
+// the token already chose in an earlier slot.  Routing from moe_route never
+// has either; moe_dispatch takes caller indices, and an invalid one is
+// treated as dropped (not routed, no row) instead of indexing the LDS
+// histograms out of range or giving an expert more rows than tokens.
+__device__ __forceinline__ int assignment_expert(const int32_t *__restrict__ topk_idx, int64_t j, int k,
+                                                 int E) {
+    const int e = topk_idx[j];
+    if ((unsigned)e >= (unsigned)E) return -1;
+    const int64_t t0 = j - j % k;
+    for (int64_t i = t0; i < j; ++i)
+        if (topk_idx[i] == e) return -1;
+    return e;
+}
+
 __global__ __launch_bounds__(DP_THREADS) void dispatch_count_kernel(
-    const int32_t *__restrict__ topk_idx, int64_t Tk, int E, int chunk,
+    const int32_t *__restrict__ topk_idx, int64_t Tk, int k, int E, int chunk,
     int32_t *__restrict__ chunk_counts) {
     __shared__ int hist[DP_EMAX];
     const int tid = threadIdx.x;
@@ -44,7 +60,10 @@ __global__ __launch_bounds__(DP_THREADS) void dispatch_count_kernel(
     const int64_t j0 = (int64_t)blockIdx.x * chunk;
     for (int q = 0; q < chunk / DP_THREADS; ++q) {
         const int64_t j = j0 + q * DP_THREADS + tid;
-        if (j < Tk) atomicAdd(&hist[topk_idx[j]], 1);
+        if (j < Tk) {
+            const int e = assignment_expert(topk_idx, j, k, E);
+            if (e >= 0) atomicAdd(&hist[e], 1);
+        }
     }
     __syncthreads();
     if (tid < E) chunk_counts[(int64_t)blockIdx.x * E + tid] = hist[tid];
@@ -67,7 +86,10 @@ __global__ __launch_bounds__(DP_THREADS) void dispatch_rank_kernel(
         // a single chunk counts its own assignments (no histogram kernel ran)
         if (tid < DP_EMAX) running[tid] = 0;
         __syncthreads();
-        for (int64_t j = tid; j < Tk; j += DP_THREADS) atomicAdd(&running[topk_idx[j]], 1);
+        for (int64_t j = tid; j < Tk; j += DP_THREADS) {
+            const int e = assignment_expert(topk_idx, j, k, E);
+            if (e >= 0) atomicAdd(&running[e], 1);
+        }
         __syncthreads();
     }
     if (tid < E) {
@@ -110,8 +132,9 @@ __global__ __launch_bounds__(DP_THREADS) void dispatch_rank_kernel(
         for (int i = tid; i < (DP_THREADS / 64) * DP_EMAX; i += DP_THREADS) (&wcnt[0][0])[i] = 0;
         __syncthreads();
         const int64_t j = j0 + round * DP_THREADS + tid;
-        const bool valid = j < Tk;
-        const int ej = valid ? topk_idx[j] : -1;
+        const bool inrange = j < Tk;
+        const int ej = inrange ? assignment_expert(topk_idx, j, k, E) : -1;
+        const bool valid = ej >= 0;
         // group the wave's lanes by expert, in lane (= assignment) order
         bool act = valid;
         int rank_w = 0;
@@ -141,6 +164,9 @@ __global__ __launch_bounds__(DP_THREADS) void dispatch_rank_kernel(
                 row_of_slot[j] = -1;
                 dropped[j] = 1;
             }
+        } else if (inrange) {   // not a valid choice: dropped
+            row_of_slot[j] = -1;
+            dropped[j] = 1;
         }
         __syncthreads();
         if (tid < E) {
@@ -188,7 +214,7 @@ hipError_t launch_dispatch(const Shape &s, const int32_t *topk_idx, int32_t *rou
     const int chunk = dispatch_chunk(s);
     if (nch > 1)
         hipLaunchKernelGGL(dispatch_count_kernel, dim3(nch), dim3(DP_THREADS), 0, st, topk_idx,
-                           s.Tk(), s.E, chunk, chunk_counts);
+                           s.Tk(), s.k, s.E, chunk, chunk_counts);
     hipLaunchKernelGGL(dispatch_rank_kernel, dim3(nch), dim3(DP_THREADS), 0, st, topk_idx, s.Tk(),
                        s.k, s.E, s.C, chunk, nch, (const int32_t *)chunk_counts, routed, kept,
                        offsets, row_of_slot, token_of_row, dropped);

@@ -242,3 +242,58 @@ def test_workspace_too_small_raises_before_launch():
     with pytest.raises(B.MoeError) as ei:
         B.moe_forward(desc, dt["x"], dw["Wr"], None, None, dw["W1"], None, dw["W2"], out["y"], ws)
     assert ei.value.code == -4
+
+
+@pytest.mark.parametrize("T,E,k,cf", [(100, 5, 2, 0.5), (300, 6, 2, 0.8), (3000, 16, 3, 1.0)])
+def test_dispatch_drops_invalid_indices(T, E, k, cf):
+    """moe_dispatch on caller indices that include entries outside [0, E)
+    and experts repeated within a token: those entries count nowhere and
+    come back dropped; the valid ones are ranked in token order against the
+    capacity as usual (checked against a plain sequential fill).  The second
+    shape spans several dispatch chunks."""
+    rng = np.random.default_rng(7)
+    idx = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    bad = rng.random((T, k)) < 0.1
+    idx[bad] = rng.choice([-1, E, E + 5, -7], size=int(bad.sum()))
+    rep = np.nonzero(rng.random(T) < 0.1)[0]
+    idx[rep, k - 1] = idx[rep, 0]                      # a repeat of slot 0's expert
+    desc = B.make_desc(T, 64, 64, E, k, gate="renorm", act="relu", dtype="bf16", cf=cf)
+    C = B.moe_capacity(desc)
+    # expected: assignments in token-major order, an invalid one skipped
+    routed = np.zeros(E, np.int64)
+    rank = np.full((T, k), -1, np.int64)
+    for t in range(T):
+        for s in range(k):
+            e = int(idx[t, s])
+            if e < 0 or e >= E or e in idx[t, :s]:
+                continue
+            rank[t, s] = routed[e]
+            routed[e] += 1
+    kept = routed if C is None else np.minimum(routed, C)
+    offs = np.concatenate([[0], np.cumsum(kept)])
+    keep = (rank >= 0) & ((rank < C) if C is not None else True)
+    rows_exp = np.where(keep, offs[np.where(rank >= 0, idx, 0)] + rank, -1)
+    x = torch.randn((T, 64), device="cuda").to(torch.bfloat16)
+    i32 = dict(dtype=torch.int32, device="cuda")
+    out = dict(routed=torch.empty(E, **i32), kept=torch.empty(E, **i32),
+               offsets=torch.empty(E + 1, **i32), rows=torch.empty((T, k), **i32),
+               tok=torch.empty(T * k, **i32),
+               dropped=torch.empty((T, k), dtype=torch.uint8, device="cuda"),
+               x_perm=torch.empty((T * k, 64), dtype=torch.bfloat16, device="cuda"))
+    B.moe_dispatch(desc, x, torch.from_numpy(idx).cuda(), out["routed"], out["kept"],
+                   out["offsets"], out["rows"], out["tok"], out["dropped"], out["x_perm"],
+                   B.workspace(desc))
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(out["routed"].cpu().numpy(), routed)
+    np.testing.assert_array_equal(out["kept"].cpu().numpy(), kept)
+    np.testing.assert_array_equal(out["offsets"].cpu().numpy(), offs)
+    np.testing.assert_array_equal(out["rows"].cpu().numpy(), rows_exp)
+    np.testing.assert_array_equal(out["dropped"].cpu().numpy(), (rows_exp < 0).astype(np.uint8))
+    tok = out["tok"].cpu().numpy()
+    n = int(offs[-1])
+    r_t, r_s = np.nonzero(rows_exp >= 0)
+    exp_tok = np.full(T * k, -1, np.int64)
+    exp_tok[rows_exp[r_t, r_s]] = r_t
+    np.testing.assert_array_equal(tok, exp_tok)
+    np.testing.assert_array_equal(out["x_perm"][:n].view(torch.int16).cpu().numpy(),
+                                  x[torch.from_numpy(tok[:n]).long().cuda()].view(torch.int16).cpu().numpy())
