@@ -408,17 +408,20 @@ __device__ __forceinline__ void big_tile(char *lds, const uint16_t *__restrict__
     const int sub = lane >> 3;
     uint32_t a_off[NQA], b_off[NQB];
     // buffer resources (dword 3 = 0x00020000: raw 32-bit data, no swizzle,
-    // bounds not relied on: every offset is in range by construction)
-    const __amdgpu_buffer_rsrc_t a_rsrc =
-        __builtin_amdgcn_make_buffer_rsrc((void *)A, 0, 0x7fffffff, 0x00020000);
+    // bounds not relied on: every offset is in range by construction).
+    // Byte offsets stay below 2^31: A is addressed from the tile's first row
+    // (or, for rows read through a_rows, from the first row of A, which
+    // then has at most T rows), a weight operand from its expert's first
+    // row; the host picks this kernel only where those spans fit.
+    const __amdgpu_buffer_rsrc_t a_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(a_rows ? A : A + (int64_t)row0 * K), 0, 0x7fffffff, 0x00020000);
     __amdgpu_buffer_rsrc_t b_rsrc;
     {
 #pragma unroll
         for (int j = 0; j < NQA; ++j) {
             const int kchunk = ((lane & 7) ^ sub ^ (j & 1)) * 8;
-            const int r = wave * (MI * 16) + j * 8 + sub;
-            const int ar = row0 + min(r, nrows - 1);
-            a_off[j] = ((uint32_t)(a_rows ? a_rows[ar] : ar) * (uint32_t)K + kchunk) * 2u;
+            const int r = min(wave * (MI * 16) + j * 8 + sub, nrows - 1);
+            a_off[j] = ((uint32_t)(a_rows ? a_rows[row0 + r] : r) * (uint32_t)K + kchunk) * 2u;
         }
         // wave w fills LDS weight rows 16 NJ w .. +16 NJ; SwiGLU: waves 0,1
         // the W1 rows of the tile (BN of them), waves 2,3 the same W3 rows
@@ -916,17 +919,28 @@ inline int64_t max_rows_per_expert(const Shape &s) {
     return m;
 }
 
+// Whether the 256-row kernel's 32-bit buffer offsets (below 2^31, the
+// range its buffer resources cover) reach every operand byte: A from the
+// tile's first row (256 rows) or, for rows read through a row map, from
+// the first of the T rows of x; a weight matrix [N][K] of one expert from
+// its first row (N * K = d * d_ff for every projection); C from the tile's
+// first row.  Each A or weight span allows one more row for the stage's k
+// offset in the scalar offset.
+inline bool big_offsets_fit(const Shape &s, int K, bool gathered) {
+    const int64_t lim = int64_t(1) << 31;
+    const int64_t arows = gathered ? (int64_t)s.T : (int64_t)BIG_BM;
+    const int64_t wide = s.d > s.d_ff ? s.d : s.d_ff;
+    return (arows + 1) * K * 2 < lim && ((int64_t)s.d * s.d_ff + wide) * 2 < lim &&
+           (int64_t)BIG_BM * wide * 4 < lim;
+}
+
 // Row-tile height from the mean rows per expert (the counts themselves
-// stay on the device).
-inline int pick_bm(const Shape &s, int K) {
+// stay on the device).  gathered: A's rows are read through a row map.
+inline int pick_bm(const Shape &s, int K, bool gathered = false) {
     int64_t rows = s.Tk();
     if (s.C >= 0 && (int64_t)s.E * s.C < rows) rows = (int64_t)s.E * s.C;
     const int64_t mean = rows / s.E;
-    // the 256-row kernel keeps operand offsets in 32 bits
-    const bool off32 = (rows > s.T ? rows : (int64_t)s.T) * K * 2 < (int64_t(1) << 32) &&
-                       (int64_t)s.d * s.d_ff * 2 < (int64_t(1) << 32) &&
-                       (int64_t)BIG_BM * (s.d > s.d_ff ? s.d : s.d_ff) * 4 < (int64_t(1) << 31);
-    if (mean >= 192 && K % 64 == 0 && off32) return BIG_BM;
+    if (mean >= 192 && K % 64 == 0 && big_offsets_fit(s, K, gathered)) return BIG_BM;
     if (mean >= 96) return 128;
     if (mean >= 24) return 64;
     return 32;
@@ -1036,7 +1050,7 @@ hipError_t launch_up_bf16(const Shape &s, const void *A, const int32_t *a_rows, 
                           const void *W3, void *H, hipStream_t st) {
     if (const int mt = skinny_tiles(s, s.d))
         return launch_skinny_any<DUAL, ACT, true>(s, mt, A, a_rows, offsets, W1, W3, H, s.d_ff, s.d, st);
-    switch (pick_bm(s, s.d)) {
+    switch (pick_bm(s, s.d, a_rows != nullptr)) {
     case BIG_BM: return launch_big<DUAL, ACT, true>(s, A, a_rows, offsets, W1, W3, H, s.d_ff, s.d, st);
     case 128: return launch_gemm<128, 128, 2, 2, DUAL, ACT, true>(s, A, a_rows, offsets, W1, W3, H, s.d_ff, s.d, st);
     case 64:  return launch_gemm<64, 128, 2, 2, DUAL, ACT, true>(s, A, a_rows, offsets, W1, W3, H, s.d_ff, s.d, st);

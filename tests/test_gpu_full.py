@@ -71,3 +71,30 @@ def test_full_size_fp8_decode():
     H.assert_stats_close(w, got, ref)
     rel = H.assert_y_close(w, H.y_float(got["y"]), ref["y"])
     print(f"[full] mixtral_decode_fp8: ok, y rel err {rel:.2e}", flush=True)
+
+
+def test_down_projection_operand_past_2gib():
+    """A layer whose hidden activations H exceed 2 GiB (T = 40960 tokens,
+    top-2 of 8, d_ff = 14336: 81920 rows x 14336 x 2 bytes = 2.35 GB): the
+    256-row tiles address A from each tile's first row, so rows past the
+    2 GiB mark (row 74898 on) are read like the others.  The sample holds
+    tokens of the last rows of H (through the oracle's permutation) and
+    spread-out ones."""
+    w = synth.WORKLOADS["mixtral_prefill"].with_(name="h_past_2gib", T=40960, d=256)
+    print("[full] h_past_2gib: generating inputs", flush=True)
+    wt, tk = H.prepare(w)
+    route_ref = H.reference(w, wt, tk, tokens=np.zeros(0, np.int64))
+    n_rows = int(route_ref["offsets"][-1])
+    assert n_rows * w.d_ff * 2 > (1 << 31)
+    late = route_ref["token_of_row"][n_rows - 2000:n_rows:63]           # rows past 2 GiB
+    sel = H.sample_tokens(w.T, 64, seed=3, must=late)
+    print(f"[full] h_past_2gib: oracle FFN on {len(sel)} tokens", flush=True)
+    ref = H.reference(w, wt, tk, tokens=sel)
+    print("[full] h_past_2gib: GPU forward", flush=True)
+    got = H.run_forward(w, H.device_weights(w, wt), H.device_tokens(w, tk))
+    H.assert_routing_exact(w, got, ref)
+    y = H.y_float(got["y"])
+    rel = H.assert_y_close(w, y[sel], ref["y"])
+    assert np.isfinite(y).all()
+    assert (np.abs(y[late]).max(axis=1) > 0).all()
+    print(f"[full] h_past_2gib: ok, y rel err {rel:.2e}", flush=True)
