@@ -297,11 +297,30 @@ def test_k_equals_E_is_full_softmax_mixture(mode):
     assert np.abs(o["y"] - ref).max() <= 1e-6 * np.abs(ref).max()
 
 
+def _dense_moe64(x, top, gates, C, W1, W3, W2, act):
+    """The layer output written as the equations state it, on dense [T][E]
+    matrices: y_t = sum_i G[t, i] K[t, i] E_i(x_t) ("Replacing the
+    feed-forward block"), with G[t, i] the gate of expert i for token t (0
+    when i is not among its top k) and K[t, i] = 1 while the number of tokens
+    up to and including t that chose i is at most C ("Capacity and dropped
+    tokens": slots filled in position order).  Every expert is applied to
+    every token (float64), then one contraction over experts."""
+    T, k = top.shape
+    E = W1.shape[0]
+    A = np.zeros((T, E))
+    G = np.zeros((T, E))
+    rows = np.repeat(np.arange(T), k)
+    A[rows, top.ravel()] = 1.0
+    G[rows, top.ravel()] = gates.ravel()
+    K = np.ones((T, E)) if C is None else (np.cumsum(A, axis=0) <= C).astype(np.float64)
+    Y = np.stack([_dense_expert64(x, W1, W3, W2, e, act) for e in range(E)])   # [E][T][d]
+    return np.einsum("te,etd->td", G * K * A, Y)
+
+
 @pytest.mark.parametrize("cf", [0.0, 1.0, 0.4])
-def test_matches_loop_over_experts(cf):
-    """The per-token combine equals the page's loop over experts: per expert,
-    its tokens in token order cut at the capacity, gated outputs added back
-    with index_add ("Implementation")."""
+def test_matches_dense_equations(cf):
+    """The oracle's dispatch + per-row FFN + slot-ordered combine equals the
+    equations on dense [T][E] gate and capacity matrices."""
     rng = _rng(10)
     T, d, d_ff, E, k = 40, 16, 32, 6, 2
     x, Wr, W1, W3, W2 = _layer(rng, T, d, d_ff, E)
@@ -311,13 +330,7 @@ def test_matches_loop_over_experts(cf):
     tl = np.take_along_axis(h, top, 1).astype(np.float64)
     gates = sps.softmax(tl, axis=1)
     C = None if cf == 0 else int(np.ceil(cf * T * k / E))
-    out = np.zeros((T, d))
-    for e in range(E):
-        token, slot = np.nonzero(top == e)
-        if C is not None:
-            token, slot = token[:C], slot[:C]
-        if len(token):
-            np.add.at(out, token, gates[token, slot][:, None] * _dense_expert64(x[token], W1, W3, W2, e, "swiglu"))
+    out = _dense_moe64(x, top, gates, C, W1, W3, W2, "swiglu")
     assert np.abs(o["y"] - out).max() <= 1e-6 * np.abs(out).max()
     if cf == 0.4:
         assert o["dropped"].sum() > 0
@@ -377,12 +390,11 @@ def test_shared_expert_equals_routed_expert_with_gate_one():
 
 
 @pytest.mark.parametrize("cf", [0.0, 0.4])
-def test_shared_and_residual_match_loop_over_experts(cf):
+def test_shared_and_residual_match_dense_equations(cf):
     """y = h + moe_out (the Implementation section's block), moe_out being the
-    page's loop over routed experts (token order, capacity cut, gated
-    index_add) plus the shared experts; a token dropped from every routed
-    expert keeps its residual and its shared experts ("Capacity and dropped
-    tokens")."""
+    routed experts by the dense gate and capacity matrices plus the shared
+    experts; a token dropped from every routed expert keeps its residual and
+    its shared experts ("Capacity and dropped tokens")."""
     rng = _rng(32)
     T, d, d_ff, E, k, S = 40, 16, 32, 6, 2, 2
     x, Wr, W1, W3, W2 = _layer(rng, T, d, d_ff, E)
@@ -393,13 +405,7 @@ def test_shared_and_residual_match_loop_over_experts(cf):
     top = np.argsort(-h, axis=1, kind="stable")[:, :k]
     gates = sps.softmax(np.take_along_axis(h, top, 1).astype(np.float64), axis=1)
     C = None if cf == 0 else int(np.ceil(cf * T * k / E))
-    out = res.astype(np.float64)
-    for e in range(E):
-        token, slot = np.nonzero(top == e)
-        if C is not None:
-            token, slot = token[:C], slot[:C]
-        if len(token):
-            np.add.at(out, token, gates[token, slot][:, None] * _dense_expert64(x[token], W1, W3, W2, e, "swiglu"))
+    out = res.astype(np.float64) + _dense_moe64(x, top, gates, C, W1, W3, W2, "swiglu")
     for j in range(S):
         out += _dense_expert64(x, sh[0], sh[1], sh[2], j, "swiglu")
     err = np.abs(o["y"] - out).max(axis=1)
