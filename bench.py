@@ -36,6 +36,17 @@ host on a bounded sample: routing, dispatch and statistics over all T
 tokens plus the expert FFN and combine on S sampled tokens; tokens/s is
 1 / (t_route / T + t_ffn / S).
 
+The default line also carries "switch" and "finegrained_zipf": the
+Switch-style and fine-grained Zipf layers, HBM-bound, each timed over
+--layer-steps steps with the last-level cache flushed (a 512 MB device
+fill) before every step (median, minimum, 90th percentile), against 8 TB/s
+over their algorithmic bytes: the touched experts' weights (from the run's
+kept counts) + x + y + W_r (+ the noise input); plus their dominant
+kernel's event-timed rate.  "sclk" samples the shader clock (amdsmi) while
+prefill steps run back to back for about a second; "cpu_baseline_1thread"
+times the oracle on one host thread for the tiny layer and the decode
+layer.
+
 --backward times moe_backward (training gradients, routing of one forward
 held fixed) on the workload instead, and prints its own JSON line; --cold
 flushes the last-level cache (a 512 MB device fill) before every forward
@@ -136,8 +147,10 @@ def traffic_for(workload, kernel, launches_per_step=1):
     return ent["hbm_bytes_per_launch"]
 
 
-def run_workload(w, steps, warmup, fresh_x_steps=0, seed=0):
-    """Times ``steps`` forward steps of workload w. Returns a result dict."""
+def run_workload(w, steps, warmup, fresh_x_steps=0, seed=0, sclk_seconds=0.0):
+    """Times ``steps`` forward steps of workload w. Returns a result dict
+    (with sclk_seconds > 0 also the shader clock sampled afterwards while
+    steps run back to back for that long, outside the timed region)."""
     import torch
     from sparse_mixture_experts_03_amd import binding as B
     from sparse_mixture_experts_03_amd import synth
@@ -231,8 +244,9 @@ def run_workload(w, steps, warmup, fresh_x_steps=0, seed=0):
     kept = out["kept_counts"].cpu().numpy().astype(np.int64)
     n_kept = int(kept.sum())
     touched = int((kept > 0).sum())
+    sclk = sample_sclk(lambda: step(warmup), sclk_seconds) if sclk_seconds > 0 else None
     return dict(elapsed=elapsed, steps=steps, stage_ms=stage_ms.mean(0), stage_ms_all=stage_ms,
-                n_kept=n_kept, touched=touched, event_steps=len(sampled), stages=stages)
+                n_kept=n_kept, touched=touched, event_steps=len(sampled), stages=stages, sclk=sclk)
 
 
 def cpu_baseline(w, seed=0, target_s=22.0):
@@ -316,6 +330,163 @@ def run_cold(w, steps, warmup, seed=0, flush_bytes=512 << 20):
             "ms_per_step_median_min_p90": [round(med, 4), round(float(ms.min()), 4),
                                            round(float(np.percentile(ms, 90)), 4)],
             "flush_bytes": flush_bytes}
+
+
+def layer_bytes(w, n_kept, touched):
+    """Algorithmic HBM bytes of one forward step of workload w: the touched
+    experts' weights, x in, y out, the router matrix (and bias), and the
+    noise input when the workload has one."""
+    n_mat = 3 if w.act == "swiglu" else 2
+    eb = 2 if w.dtype == "bf16" else 4
+    b = touched * n_mat * w.d * w.d_ff * eb + 2 * w.T * w.d * eb + w.E * w.d * 4
+    if w.noise_std > 0:
+        b += w.T * w.E * 4
+    if w.zipf_s > 0:
+        b += w.E * 4
+    return int(b)
+
+
+def kernel_bytes(w, stage, n_kept, touched):
+    """Algorithmic bytes of one expert GEMM launch: its touched weights, the
+    rows of A it reads and the rows it writes."""
+    eb = 2 if w.dtype == "bf16" else 4
+    if stage == "expert_up":
+        n_up = 2 if w.act == "swiglu" else 1
+        return int(touched * n_up * w.d_ff * w.d * eb + n_kept * (w.d + w.d_ff) * eb)
+    return int(touched * w.d * w.d_ff * eb + n_kept * w.d_ff * eb + n_kept * w.d * 4)
+
+
+def hbm_layer_object(w, steps, warmup=5):
+    """An HBM-bound layer (Switch, fine-grained Zipf) in the default line:
+    per-step median, minimum and p90 with the last-level cache flushed
+    before every step, against 8 TB/s over the algorithmic bytes; the warm
+    back-to-back rate and the dominant kernel's event-timed rate beside."""
+    res = run_workload(w, steps, warmup)
+    cold = run_cold(w, steps, 3)
+    med, mn, p90 = cold["ms_per_step_median_min_p90"]
+    nbytes = layer_bytes(w, res["n_kept"], res["touched"])
+    gbs = nbytes / (med * 1e-3) / 1e9
+    stages = {n: float(v) for n, v in zip(res["stages"], res["stage_ms"]) if np.isfinite(v)}
+    dom = max(("expert_up", "expert_down"), key=lambda n: stages.get(n, 0.0))
+    kb = kernel_bytes(w, dom, res["n_kept"], res["touched"])
+    kgbs = kb / (stages[dom] * 1e-3) / 1e9
+    ms_warm = res["elapsed"] * 1e3 / res["steps"]
+    return {
+        "workload": w.name, "T": w.T, "d": w.d, "d_ff": w.d_ff, "E": w.E, "k": w.k,
+        "gate": w.gate, "act": w.act, "capacity_factor": w.cf,
+        "kept_rows": res["n_kept"], "touched_experts": res["touched"],
+        "value": round(w.T / (med * 1e-3), 1), "unit": "tokens/s", "steps": steps,
+        "cache": "last-level cache flushed (512 MB device fill) before every timed step",
+        "ms_per_step_median_min_p90": [med, mn, p90],
+        "ms_per_step_warm": round(ms_warm, 4),
+        "stage_ms_warm": {n: round(v, 4) for n, v in stages.items()},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+                     "algorithmic_per_step": nbytes, "traffic": None},
+        "dominant_kernel": {"stage": dom, "mean_launch_ms": round(stages[dom], 4),
+                            "algorithmic_per_launch": kb, "achieved": round(kgbs, 1),
+                            "unit": "GB/s", "frac": round(kgbs / PEAK_HBM_GBS, 4)},
+    }
+
+
+def sample_sclk(step, seconds=1.0, period_s=0.002):
+    """The shader clock while ``step`` runs back to back for about
+    ``seconds``: amdsmi's GPU metrics polled from a second thread; returns
+    the median and range of the samples in MHz (None if amdsmi is not
+    usable here)."""
+    import threading
+
+    import torch
+    try:
+        import amdsmi
+        amdsmi.amdsmi_init()
+        h = amdsmi.amdsmi_get_processor_handles()[0]
+    except Exception as e:  # noqa: BLE001 -- reported, never fatal
+        return {"mhz": None, "reason": f"amdsmi unavailable: {e}"[:160]}
+
+    def read():
+        m = amdsmi.amdsmi_get_gpu_metrics_info(h)
+        v = m.get("current_gfxclks")
+        if isinstance(v, (list, tuple)):
+            v = [c for c in v if isinstance(c, (int, float)) and 0 < c < 10000]
+            if v:
+                return float(np.mean(v))
+        v = m.get("current_gfxclk")
+        if isinstance(v, (int, float)) and 0 < v < 10000:
+            return float(v)
+        return None
+
+    samples, stop = [], threading.Event()
+
+    def poll():
+        while not stop.is_set():
+            try:
+                v = read()
+            except Exception:  # noqa: BLE001
+                v = None
+            if v is not None:
+                samples.append(v)
+            time.sleep(period_s)
+
+    th = threading.Thread(target=poll, daemon=True)
+    th.start()
+    t0 = time.perf_counter()
+    n = 0
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(20):
+            step()
+        torch.cuda.synchronize()
+        n += 20
+    stop.set()
+    th.join()
+    try:
+        amdsmi.amdsmi_shut_down()
+    except Exception:  # noqa: BLE001
+        pass
+    if not samples:
+        return {"mhz": None, "reason": "no clock samples from amdsmi"}
+    a = np.array(samples)
+    busy = a[a >= 500.0]          # samples at idle clocks (before the first step lands) left out
+    a = busy if len(busy) else a
+    return {"mhz": round(float(np.median(a)), 1), "min": round(float(a.min()), 1),
+            "max": round(float(a.max()), 1), "samples": len(a), "steps": n,
+            "source": "amdsmi gpu metrics (current_gfxclks, mean over XCDs), polled every 2 ms; "
+                      "samples below 500 MHz (idle) left out"}
+
+
+def cpu_one_thread(seed=0):
+    """The oracle on one host thread: the tiny layer (all 64 tokens) and the
+    Mixtral-shape decode layer (routing of all 32 tokens, expert FFN and
+    combine for 4 of them; tokens/s = 1 / (t_route / T + t_ffn / 4))."""
+    import oracle
+    from sparse_mixture_experts_03_amd import synth
+
+    n0 = oracle.threads()
+    oracle.set_threads(1)
+    out = {}
+    try:
+        for name, n_ffn in (("tiny", None), ("mixtral_decode", 4)):
+            w = synth.WORKLOADS[name]
+            wt = synth.make_weights(w, seed)
+            tk = synth.make_tokens(w, seed, 0)
+            x = synth.widen(tk["x"])
+            W1, W2 = synth.widen(wt["W1"]), synth.widen(wt["W2"])
+            W3 = None if wt["W3"] is None else synth.widen(wt["W3"])
+            args = (x, wt["Wr"], W1, W3, W2, w.k, w.gate, w.cf, w.act, wt["bias"], tk["noise"])
+            t0 = time.perf_counter()
+            oracle.forward(*args, tokens=np.zeros(0, np.int64))
+            t_route = time.perf_counter() - t0
+            sel = np.arange(w.T) if n_ffn is None else np.arange(n_ffn)
+            t1 = time.perf_counter()
+            oracle.forward(*args, tokens=sel)
+            t_ffn = max(time.perf_counter() - t1 - t_route, 1e-9)
+            out[name] = {"value": round(1.0 / (t_route / w.T + t_ffn / len(sel)), 2),
+                         "unit": "tokens/s", "cores": 1, "kind": "oracle",
+                         "sample": f"{name}: routing of all {w.T} tokens, expert FFN and combine "
+                                   f"of {len(sel)}"}
+    finally:
+        oracle.set_threads(n0)
+    return out
 
 
 def run_backward(w, steps, warmup, seed=0):
@@ -471,6 +642,9 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=100)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-layers", action="store_true",
+                    help="leave out the Switch and fine-grained Zipf layers of the default line")
+    ap.add_argument("--layer-steps", type=int, default=50)
     ap.add_argument("--backward", action="store_true",
                     help="time moe_backward on the workload instead of the forward")
     ap.add_argument("--cold", action="store_true",
@@ -529,7 +703,8 @@ def main():
         }
         print(json.dumps(line), flush=True)
         return
-    res = run_workload(w, args.steps, args.warmup)
+    res = run_workload(w, args.steps, args.warmup,
+                       sclk_seconds=1.0 if w.name == "mixtral_prefill" else 0.0)
     ms_step = res["elapsed"] * 1e3 / res["steps"]
     tokens_s = w.T * res["steps"] / res["elapsed"]
     n_up = 2 if w.act == "swiglu" else 1
@@ -567,6 +742,11 @@ def main():
                                                   round(float(np.percentile(up_all, 90)), 4)],
                      "event_timed_launches": res["event_steps"]},
     }
+    # per-step distribution of the same layer with the last-level cache
+    # flushed before each step (its 2.8 GB of weights never fit it anyway)
+    cold = run_cold(w, max(args.steps, 20), 3)
+    line["step_ms_median_min_p90"] = cold["ms_per_step_median_min_p90"]
+    line["step_ms_mode"] = "each step timed alone by its own events, last-level cache flushed before it"
     line["combine"] = combine_object(w, res)
     line["gather"] = ("folded into the expert up-projection's loads in moe_forward (rows of x read "
                       "through token_of_row): its bytes are part of that kernel's traffic")
@@ -585,9 +765,19 @@ def main():
             rd = run_workload(wd, args.decode_steps, 10, fresh_x_steps=args.decode_steps)
             line[key] = decode_object(wd, rd)
             log(f"[bench] {wd.name}: {line[key]['ms_per_step']:.3f} ms/step")
+    if not args.no_layers and w.name == "mixtral_prefill":
+        for name in ("switch", "finegrained_zipf"):
+            log(f"[bench] {name}: {args.layer_steps} warm + {args.layer_steps} cold steps ...")
+            line[name] = hbm_layer_object(synth.WORKLOADS[name], args.layer_steps)
+            log(f"[bench] {name}: median {line[name]['ms_per_step_median_min_p90'][0]:.4f} ms/step "
+                f"(cold), {line[name]['roofline']['frac']:.3f} of HBM")
+    if res["sclk"] is not None:
+        line["sclk"] = res["sclk"]
     if not args.no_cpu:
         log("[bench] CPU oracle baseline ...")
         line["cpu_baseline"] = cpu_baseline(w)
+        if w.name == "mixtral_prefill":
+            line["cpu_baseline_1thread"] = cpu_one_thread()
     print(json.dumps(line), flush=True)
 
 
