@@ -1077,21 +1077,6 @@ hipError_t launch_expert_up(const Shape &s, const void *x_perm, const int32_t *a
     }
 }
 
-// The router logits of a large batch as one row group: x [T][d] against the
-// stacked W_r terms [3 epad][d], fp32 out [T][3 epad] (the second K half,
-// if any, right after the first).
-hipError_t launch_router_gemm(const Shape &s, const void *x, const void *wsplit,
-                              const int32_t *roffs, float *part, hipStream_t st) {
-    Shape r = s;
-    r.E = 1;
-    r.k = 1;
-    r.C = -1;
-    const int N = 3 * route_epad(s);
-    const int ns = route_gemm_nsplit(s);
-    return launch_big<false, ACT_NONE, false>(r, x, nullptr, roffs, wsplit, nullptr, part, N, s.d, st, ns,
-                                              ns == 2 ? part + (size_t)s.T * N : nullptr);
-}
-
 int down_ksplit(const Shape &s) {
     if (s.dtype == 0 || skinny_tiles(s, s.d_ff) != 0 || pick_bm(s, s.d_ff) != BIG_BM) return 1;
     if (s.d_ff < 4096 || (s.d_ff / 64) % 2 != 0) return 1;

@@ -87,7 +87,7 @@ Layout layout(const Shape &s, int S = 0) {
     L.arrivals = take(sizeof(unsigned));
     if (s.dtype == MOE_DTYPE_BF16) {
         L.part_logits = take(moe::route_part_floats(s) * 4);
-        L.wsplit = moe::route_gemm(s) ? take(moe::route_wsplit_bytes(s)) : 0;
+        L.wsplit = moe::route_fused(s) ? take(moe::route_wsplit_bytes(s)) : 0;
     }
     L.chunk_counts = take((size_t)moe::dispatch_chunks(s) * (size_t)s.E * 4);
     L.topk_idx = take(Tk * 4);

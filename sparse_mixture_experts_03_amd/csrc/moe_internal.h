@@ -50,23 +50,24 @@ int route_epad(const Shape &s);
 int route_slice(const Shape &s);
 int route_nsplit(const Shape &s);
 
-// Large bf16 batches with many experts (route_gemm): W_r is split once
-// into its three bf16 terms, stacked as a [3 * route_epad()][d] matrix, and
-// the logits are one 256 x 256-tile GEMM of x against it (fp32 out,
-// [T][3 * epad] per K half, route_gemm_nsplit() halves).  The epilogue
-// adds the halves and the terms in a fixed order.
-bool route_gemm(const Shape &s);
-int route_gemm_nsplit(const Shape &s);
+// bf16 batches past the small-batch kernel with more than 32 experts and
+// d % 64 == 0 (route_fused): W_r is split once into its three bf16 terms,
+// stacked as a [3 * route_epad()][d] matrix, and one kernel computes each
+// tile of route_fused_bt() tokens' logits on MFMA and finishes its routing
+// (softmax, top-k, gates, statistic partials) without writing the logits.
+bool route_fused(const Shape &s);
+int route_fused_bt(const Shape &s);
+int route_fused_ntiles(const Shape &s);
+// statistic partials per expert: one per route block, or per fused tile
+int route_stat_blocks(const Shape &s);
 // floats of the logit partials in the workspace, and bytes of the split
-// matrix plus the row offsets {0, T} of its single row group
+// matrix (fused router)
 size_t route_part_floats(const Shape &s);
 size_t route_wsplit_bytes(const Shape &s);
-hipError_t launch_router_gemm(const Shape &s, const void *x, const void *wsplit,
-                              const int32_t *roffs, float *part, hipStream_t st);
 
 // arrivals: a 4-byte counter in the workspace (zeroed by launch_route's
 // kernels, used and re-zeroed by the statistics kernel); fP: E + 1 doubles.
-// wsplit: route_wsplit_bytes() of workspace (used when route_gemm()).
+// wsplit: route_wsplit_bytes() of workspace (used when route_fused()).
 hipError_t launch_route(const Shape &s, const void *x, const float *Wr, const float *bias,
                         const float *noise, int32_t *topk_idx, float *gates, float *part_P,
                         float *part_lse2, float *part_logits, void *wsplit, unsigned *arrivals,

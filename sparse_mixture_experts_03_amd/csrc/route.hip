@@ -10,7 +10,12 @@
 //     P_i (mean router probability), and the z statistic mean (log sum exp h)^2;
 //   Implementation: the router runs in float32.
 //
-// bf16 activations (the MFMA path), two kernels:
+// bf16 activations (the MFMA path):
+//   route_fused_kernel (batches past the small-batch kernel, d % 64 == 0):
+//     after router_wsplit_kernel has split W_r once into its three bf16
+//     terms (below), one kernel per token tile computes the logits on MFMA
+//     and finishes the routing in its epilogue -- see its comment.
+//   Otherwise two kernels:
 //   router_logits_kernel  v_mfma_f32_16x16x32_bf16 over a 64-token x E tile,
 //     split over d into slices (so that a 32-token decode batch still
 //     spreads over many CUs); each slice writes fp32 partial logits.  The
@@ -26,13 +31,16 @@
 // fp32 activations: route_f32_kernel, a plain fp32 FMA tile over d staged
 //   through LDS, then the same per-token epilogue.
 //
-// Per-token epilogue (one wave per token, E <= 128 logits in registers:
-// lane l holds experts l and l+64): max and sum of exponentials by shuffle
-// reductions, top-k by k arg-max reductions over 64-bit keys (orderable
+// Per-token epilogue (one token per group of 8 or 16 lanes, E <= 128
+// logits in registers: for E > 16 lane c of a 16-lane row holds experts c,
+// c + 16, ...): max and sum of exponentials by DPP reductions within the
+// group, top-k by k arg-max reductions over 64-bit keys (orderable
 // logit bits, then the complement of the index, so a tie goes to the lower
 // index), gates, and per-block partials: sums of p and counts of top
 // choices (per expert) and the sum of lse^2, in a fixed order.
 // route_stats_kernel reduces the partials in double in a fixed order.
+#include <type_traits>
+
 #include "moe_internal.h"
 
 namespace moe {
@@ -56,13 +64,13 @@ __device__ __forceinline__ uint32_t ord_f32(float f) {
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// Wave reductions on the VALU's cross-lane moves (DPP) instead of LDS
-// permutes: within each row of 16 lanes, swap neighbours (quad_perm 1,0,3,2),
-// pairs (2,3,0,1), then mirror the half-rows and the row, so that every lane
-// of a row holds the row's result; the four rows are then read with
-// readlane and combined in row order (a fixed order, so sums are
-// reproducible).  DPP control codes: quad_perm 0xB1 and 0x4E, row_half_mirror
-// 0x141, row_mirror 0x140.
+// Reductions within groups of G = 8 or 16 lanes (one token per group) on
+// the VALU's cross-lane moves (DPP) instead of LDS permutes: swap
+// neighbours (quad_perm 1,0,3,2), pairs (2,3,0,1), then mirror the
+// half-rows and (G = 16) the row, so that every lane of the group holds the
+// group's result, bit for bit the same on every lane (each step combines two
+// equal-shaped partial results commutatively).  DPP control codes: quad_perm
+// 0xB1 and 0x4E, row_half_mirror 0x141, row_mirror 0x140.
 template <int CTRL>
 __device__ __forceinline__ float dpp_f32(float v) {
     return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
@@ -73,46 +81,7 @@ __device__ __forceinline__ unsigned long long dpp_u64(unsigned long long v) {
     const int hi = __builtin_amdgcn_mov_dpp((int)(uint32_t)(v >> 32), CTRL, 0xF, 0xF, false);
     return ((unsigned long long)(uint32_t)hi << 32) | (uint32_t)lo;
 }
-__device__ __forceinline__ float rows_f32(float v, int r) { return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), r)); }
 
-__device__ __forceinline__ float wave_max(float v) {
-    v = fmaxf(v, dpp_f32<0xB1>(v));
-    v = fmaxf(v, dpp_f32<0x4E>(v));
-    v = fmaxf(v, dpp_f32<0x141>(v));
-    v = fmaxf(v, dpp_f32<0x140>(v));
-    return fmaxf(fmaxf(rows_f32(v, 0), rows_f32(v, 16)), fmaxf(rows_f32(v, 32), rows_f32(v, 48)));
-}
-
-__device__ __forceinline__ float wave_sum(float v) {
-    v += dpp_f32<0xB1>(v);
-    v += dpp_f32<0x4E>(v);
-    v += dpp_f32<0x141>(v);
-    v += dpp_f32<0x140>(v);
-    return ((rows_f32(v, 0) + rows_f32(v, 16)) + rows_f32(v, 32)) + rows_f32(v, 48);
-}
-
-__device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long v) {
-    unsigned long long w;
-    w = dpp_u64<0xB1>(v);
-    v = w > v ? w : v;
-    w = dpp_u64<0x4E>(v);
-    v = w > v ? w : v;
-    w = dpp_u64<0x141>(v);
-    v = w > v ? w : v;
-    w = dpp_u64<0x140>(v);
-    v = w > v ? w : v;
-    unsigned long long best = 0ull;
-#pragma unroll
-    for (int r = 0; r < 64; r += 16) {
-        const unsigned long long x = ((unsigned long long)(uint32_t)__builtin_amdgcn_readlane((int)(v >> 32), r) << 32) |
-                                     (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, r);
-        best = x > best ? x : best;
-    }
-    return best;
-}
-
-// Reductions within groups of G = 8 or 16 lanes (a token per group): the
-// same DPP steps as wave_max, stopped at the group.
 template <int G>
 __device__ __forceinline__ float group_max(float v) {
     v = fmaxf(v, dpp_f32<0xB1>(v));
@@ -155,7 +124,7 @@ __device__ void softmax_topk_grouped(const float (*hl)[RT_EMAX + 1], int t0, int
                                      int gate_switch, int32_t *__restrict__ topk_idx,
                                      float *__restrict__ gates, float *__restrict__ part_P,
                                      float *__restrict__ part_lse2, int *topk_sh, float *P_sh,
-                                     float *lse2_sh) {
+                                     float *lse2_sh, int pslot, int pslots) {
     constexpr int TPW = 64 / G;   // tokens per wave at a time
     __shared__ float pwg[NW][64];
     __shared__ float lsg[NW][TPW];
@@ -212,11 +181,11 @@ __device__ void softmax_topk_grouped(const float (*hl)[RT_EMAX + 1], int t0, int
         for (int v = 0; v < NW; ++v)
 #pragma unroll
             for (int q = 0; q < TPW; ++q) a += pwg[v][q * G + tid];
-        const int64_t nblk = gridDim.x;
+        const int64_t nblk = pslots;
         int c = 0;
         for (int r = 0, nr = min(TILE, T - t0); r < nr; ++r) c += topchg[r] == tid;
-        part_P[(int64_t)tid * nblk + blockIdx.x] = a;
-        part_P[(int64_t)(E + tid) * nblk + blockIdx.x] = (float)c;
+        part_P[(int64_t)tid * nblk + pslot] = a;
+        part_P[(int64_t)(E + tid) * nblk + pslot] = (float)c;
         if (P_sh) P_sh[tid] = a;
     }
     if (tid == 0) {
@@ -224,110 +193,179 @@ __device__ void softmax_topk_grouped(const float (*hl)[RT_EMAX + 1], int t0, int
         for (int v = 0; v < NW; ++v)
 #pragma unroll
             for (int q = 0; q < TPW; ++q) a += lsg[v][q];
-        part_lse2[blockIdx.x] = a;
+        part_lse2[pslot] = a;
+        if (lse2_sh) *lse2_sh = a;
+    }
+}
+
+// softmax_topk_block for 16 < E <= 16 V: one token per row of 16 lanes,
+// lane c of a row holding experts c, c + 16, ..., c + 16 (V - 1), so a wave
+// serves 4 tokens at once and every reduction stays within a row (DPP
+// moves only: no readlane, no LDS).  Each lane first reduces its V values
+// (max, sum in v order, largest key), then the row.  Selected slot s is
+// kept by lane s % 16 of the row, in its register s / 16.  Partials: per
+// expert, the waves' row sums added in (wave, row) order.
+template <int V, int TILE, int NW>
+__device__ __forceinline__ void softmax_topk_rows(const float (*hl)[RT_EMAX + 1], int t0, int T, int E, int k,
+                                                  int gate_switch, int32_t *__restrict__ topk_idx,
+                                                  float *__restrict__ gates, float *__restrict__ part_P,
+                                                  float *__restrict__ part_lse2, int *topk_sh, float *P_sh,
+                                                  float *lse2_sh, int pslot, int pslots) {
+    __shared__ float pwr[NW][V][64];
+    __shared__ float lsr[NW][4];
+    __shared__ int topcr[TILE];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, w = tid >> 6;
+    const int g = lane >> 4, c = lane & 15;
+    float psum[V], lsum = 0.f;
+#pragma unroll
+    for (int v = 0; v < V; ++v) psum[v] = 0.f;
+    for (int r0 = w * 4; r0 < TILE; r0 += NW * 4) {
+        if (t0 + r0 >= T) break;   // uniform in the wave
+        const int r = r0 + g, t = t0 + r;
+        const bool vt = r < TILE && t < T;
+        float h[V];
+        bool ve[V];
+#pragma unroll
+        for (int v = 0; v < V; ++v) {
+            ve[v] = c + 16 * v < E;
+            // a row past the batch holds no token: finite stand-ins, nothing stored
+            h[v] = ve[v] ? (vt ? hl[r][c + 16 * v] : 0.f) : -INFINITY;
+        }
+        float mx = h[0];
+#pragma unroll
+        for (int v = 1; v < V; ++v) mx = fmaxf(mx, h[v]);
+        mx = group_max<16>(mx);
+        float xv[V], sl = 0.f;
+#pragma unroll
+        for (int v = 0; v < V; ++v) {
+            xv[v] = ve[v] ? expf(h[v] - mx) : 0.f;
+            sl += xv[v];
+        }
+        const float sm = group_sum<16>(sl);
+        const float inv = 1.f / sm;
+        if (vt) {
+#pragma unroll
+            for (int v = 0; v < V; ++v) psum[v] += xv[v] * inv;
+            const float lse = mx + logf(sm);
+            lsum += lse * lse;
+        }
+        unsigned long long key[V];
+#pragma unroll
+        for (int v = 0; v < V; ++v)
+            key[v] = ve[v] ? ((unsigned long long)ord_f32(h[v]) << 32) | (0xffffffffu - (uint32_t)(c + 16 * v))
+                           : 0ull;
+        float h_top = 0.f, den = 0.f, sh[V];
+        int si[V];
+#pragma unroll
+        for (int v = 0; v < V; ++v) {
+            sh[v] = 0.f;
+            si[v] = 0;
+        }
+        for (int s = 0; s < k; ++s) {
+            unsigned long long b = key[0];
+#pragma unroll
+            for (int v = 1; v < V; ++v) b = key[v] > b ? key[v] : b;
+            b = group_max_u64<16>(b);
+            int bi = (int)(0xffffffffu - (uint32_t)(b & 0xffffffffull));
+            bi = bi < 0 ? 0 : bi;   // unreachable while k <= E (validated on the host)
+#pragma unroll
+            for (int v = 0; v < V; ++v)
+                if (c + 16 * v == bi) key[v] = 0ull;
+            const float hb = vt ? hl[r][bi] : 0.f;   // one address per row
+            if (s == 0) {
+                h_top = hb;
+                if (c == 0 && vt) topcr[r] = bi;
+            }
+            den += expf(hb - h_top);   // slot order, identical on the row's lanes
+            if (c == (s & 15)) {
+#pragma unroll
+                for (int v = 0; v < V; ++v)
+                    if (v == (s >> 4)) {
+                        sh[v] = hb;
+                        si[v] = bi;
+                    }
+            }
+        }
+        if (vt) {
+#pragma unroll
+            for (int v = 0; v < V; ++v) {
+                const int s = c + 16 * v;
+                if (s < k) {
+                    const float gt = gate_switch ? expf(sh[v] - mx) * inv : expf(sh[v] - h_top) / den;
+                    topk_idx[(int64_t)t * k + s] = si[v];
+                    if (topk_sh) topk_sh[t * k + s] = si[v];   // LDS copy (small batches)
+                    gates[(int64_t)t * k + s] = gt;
+                }
+            }
+        }
+    }
+#pragma unroll
+    for (int v = 0; v < V; ++v) pwr[w][v][lane] = psum[v];
+    if (c == 0) lsr[w][g] = lsum;
+    __syncthreads();
+    if (tid < E) {
+        const int v = tid >> 4, cc = tid & 15;
+        float a = 0.f;
+        for (int wv = 0; wv < NW; ++wv)
+#pragma unroll
+            for (int gg = 0; gg < 4; ++gg) a += pwr[wv][v][16 * gg + cc];
+        int cnt = 0;
+        for (int r = 0, nr = min(TILE, T - t0); r < nr; ++r) cnt += topcr[r] == tid;
+        part_P[(int64_t)tid * pslots + pslot] = a;
+        part_P[(int64_t)(E + tid) * pslots + pslot] = (float)cnt;
+        if (P_sh) P_sh[tid] = a;
+    }
+    if (tid == 0) {
+        float a = 0.f;
+        for (int wv = 0; wv < NW; ++wv)
+#pragma unroll
+            for (int gg = 0; gg < 4; ++gg) a += lsr[wv][gg];
+        part_lse2[pslot] = a;
         if (lse2_sh) *lse2_sh = a;
     }
 }
 
 // The per-token epilogue over a block's logits tile hl[TILE][.]
 // (already synchronised), NW waves, wave w taking tokens w, w + NW, ...
-// Every thread of the block must call it.  Block partials, for a grid of
-// nblk blocks: part_P[e * nblk + b] = sum of p_e over the block's tokens
-// (waves in order), part_P[(E + e) * nblk + b] = how many of them have e as
-// their top choice (an exact small integer in a float), part_lse2[b].
+// Every thread of the block must call it.  Partials of tile pslot out of
+// pslots (by default the block's index in the grid): part_P[e * pslots + b]
+// = sum of p_e over the tile's tokens (waves in order), part_P[(E + e) *
+// pslots + b] = how many of them have e as their top choice (an exact small
+// integer in a float), part_lse2[b].
 template <int TILE, int NW = 4>
 __device__ void softmax_topk_block(const float (*hl)[RT_EMAX + 1], int t0, int T, int E, int k,
                                    int gate_switch, int32_t *__restrict__ topk_idx,
                                    float *__restrict__ gates, float *__restrict__ part_P,
                                    float *__restrict__ part_lse2, int *topk_sh = nullptr,
-                                   float *P_sh = nullptr, float *lse2_sh = nullptr) {
+                                   float *P_sh = nullptr, float *lse2_sh = nullptr,
+                                   int pslot = -1, int pslots = 0) {
+    if (pslot < 0) {
+        pslot = blockIdx.x;
+        pslots = gridDim.x;
+    }
     if (E <= 8) {
         softmax_topk_grouped<8, TILE, NW>(hl, t0, T, E, k, gate_switch, topk_idx, gates, part_P, part_lse2,
-                                          topk_sh, P_sh, lse2_sh);
+                                          topk_sh, P_sh, lse2_sh, pslot, pslots);
         return;
     }
     if (E <= 16) {
         softmax_topk_grouped<16, TILE, NW>(hl, t0, T, E, k, gate_switch, topk_idx, gates, part_P, part_lse2,
-                                           topk_sh, P_sh, lse2_sh);
+                                           topk_sh, P_sh, lse2_sh, pslot, pslots);
         return;
     }
-    __shared__ float pw[NW][RT_EMAX];
-    __shared__ float lw[NW];
-    __shared__ int topch[TILE];   // each token's top choice
-    const int tid = threadIdx.x;
-    const int lane = tid & 63, w = tid >> 6;
-    const int e0 = lane, e1 = lane + 64;
-    const bool v0 = e0 < E, v1 = e1 < E;
-    float psum0 = 0.f, psum1 = 0.f, lsum = 0.f;
-    for (int r = w; r < TILE; r += NW) {
-        const int t = t0 + r;
-        if (t >= T) break;
-        const float h0 = v0 ? hl[r][e0] : -INFINITY;
-        const float h1 = v1 ? hl[r][e1] : -INFINITY;
-        const float m = wave_max(fmaxf(h0, h1));
-        const float x0 = v0 ? expf(h0 - m) : 0.f;
-        const float x1 = v1 ? expf(h1 - m) : 0.f;
-        const float s = wave_sum(x0 + x1);
-        const float inv = 1.f / s;
-        psum0 += x0 * inv;
-        psum1 += x1 * inv;
-        const float lse = m + logf(s);
-        lsum += lse * lse;
-
-        unsigned long long k0 = v0 ? ((unsigned long long)ord_f32(h0) << 32) | (0xffffffffu - (uint32_t)e0) : 0ull;
-        unsigned long long k1 = v1 ? ((unsigned long long)ord_f32(h1) << 32) | (0xffffffffu - (uint32_t)e1) : 0ull;
-        // lane (s & 63) keeps slot s: register 0 for s < 64, register 1 above
-        float h_top = 0.f, den = 0.f, sh0 = 0.f, sh1 = 0.f;
-        int si0 = 0, si1 = 0;
-        for (int sl = 0; sl < k; ++sl) {
-            unsigned long long best = wave_max_u64(k0 > k1 ? k0 : k1);
-            int bi = (int)(0xffffffffu - (uint32_t)(best & 0xffffffffull));
-            bi = bi < 0 ? 0 : bi;  // unreachable while k <= E (validated on the host)
-            if (bi == e0) k0 = 0ull;
-            if (bi == e1) k1 = 0ull;
-            float hb = hl[r][bi];  // the selected logit (same address on every lane)
-            if (sl == 0) {
-                h_top = hb;
-                if (lane == 0) topch[r] = bi;
-            }
-            den += expf(hb - h_top);  // slot order, identical on every lane
-            if (lane == (sl & 63)) {
-                if (sl < 64) { sh0 = hb; si0 = bi; }
-                else         { sh1 = hb; si1 = bi; }
-            }
-        }
-        for (int sl = lane, j = 0; sl < k; sl += 64, ++j) {
-            float hb = j ? sh1 : sh0;
-            float g = gate_switch ? expf(hb - m) * inv : expf(hb - h_top) / den;
-            topk_idx[(int64_t)t * k + sl] = j ? si1 : si0;
-            if (topk_sh) topk_sh[t * k + sl] = j ? si1 : si0;  // LDS copy (small batches)
-            gates[(int64_t)t * k + sl] = g;
-        }
+    if (E <= 32) {
+        softmax_topk_rows<2, TILE, NW>(hl, t0, T, E, k, gate_switch, topk_idx, gates, part_P, part_lse2,
+                                       topk_sh, P_sh, lse2_sh, pslot, pslots);
+        return;
     }
-    // block partials in a fixed order: waves 0..NW-1.  lsum is the same on
-    // every lane of a wave (it sums wave-uniform values).
-    pw[w][e0] = psum0;
-    pw[w][e1] = psum1;
-    if (lane == 0) lw[w] = lsum;
-    __syncthreads();
-    if (tid < E) {
-        float a = pw[0][tid];
-#pragma unroll
-        for (int v = 1; v < NW; ++v) a += pw[v][tid];
-        const int64_t nblk = gridDim.x;
-        int c = 0;
-        for (int r = 0, nr = min(TILE, T - t0); r < nr; ++r) c += topch[r] == tid;
-        part_P[(int64_t)tid * nblk + blockIdx.x] = a;
-        part_P[(int64_t)(E + tid) * nblk + blockIdx.x] = (float)c;
-        if (P_sh) P_sh[tid] = a;
+    if (E <= 64) {
+        softmax_topk_rows<4, TILE, NW>(hl, t0, T, E, k, gate_switch, topk_idx, gates, part_P, part_lse2,
+                                       topk_sh, P_sh, lse2_sh, pslot, pslots);
+        return;
     }
-    if (tid == 0) {
-        float a = lw[0];
-#pragma unroll
-        for (int v = 1; v < NW; ++v) a += lw[v];
-        part_lse2[blockIdx.x] = a;
-        if (lse2_sh) *lse2_sh = a;
-    }
+    softmax_topk_rows<8, TILE, NW>(hl, t0, T, E, k, gate_switch, topk_idx, gates, part_P, part_lse2, topk_sh,
+                                   P_sh, lse2_sh, pslot, pslots);
 }
 
 // ---- fp32 activations ----------------------------------------------------
@@ -532,14 +570,14 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const uint16_t *__re
 }
 
 // The three bf16 terms of W_r (the same split as the logits kernel makes
-// in LDS), stacked: row q * epad + e of ws holds term q of expert e, rows
-// of experts >= E are zero.  Thread: 4 consecutive k of one expert.  Block
-// 0 also writes the row offsets {0, T} of the router GEMM's one row group.
+// in LDS), stacked: row q * epad + e holds term q of expert e, rows of
+// experts >= E are zero.  Stored for the fused router's fragment loads:
+// [d / 32][3 epad][32] -- the 32 columns k = 32 c .. 32 c + 31 of every row
+// together, so 16 consecutive rows of one such block (one MFMA B fragment)
+// are one contiguous kilobyte.  Thread: 4 consecutive k of one expert.
 __global__ __launch_bounds__(256) void router_wsplit_kernel(const float *__restrict__ Wr, int E, int epad,
-                                                            int d, int T, uint16_t *__restrict__ ws,
-                                                            int32_t *__restrict__ roffs) {
+                                                            int d, uint16_t *__restrict__ ws) {
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;   // 4-wide group
-    if (blockIdx.x == 0 && threadIdx.x < 2) roffs[threadIdx.x] = threadIdx.x ? T : 0;
     const int dq = d / 4;
     if (i >= (int64_t)epad * dq) return;
     const int e = (int)(i / dq), kc = (int)(i - (int64_t)e * dq) * 4;
@@ -561,8 +599,198 @@ __global__ __launch_bounds__(256) void router_wsplit_kernel(const float *__restr
     }
 #pragma unroll
     for (int q = 0; q < 3; ++q)
-        *(uint2 *)(ws + ((int64_t)q * epad + e) * d + kc) =
+        *(uint2 *)(ws + (((int64_t)(kc >> 5) * 3 + q) * epad + e) * 32 + (kc & 31)) =
             make_uint2((uint32_t)t[q][0] | ((uint32_t)t[q][1] << 16), (uint32_t)t[q][2] | ((uint32_t)t[q][3] << 16));
+}
+
+// The fused router for bf16 batches past the small-batch kernel with more
+// than 32 experts: one block per tile of BT tokens, all E_PAD experts, the
+// whole of d.  The logits go from the MFMAs to LDS and through the per-token
+// epilogue in the same kernel; they never reach memory.
+//
+// Products: x (bf16) against the three stacked bf16 terms of W_r, stored
+// [d / 32][3][E_PAD][32] (router_wsplit_kernel), all three added into the
+// same fp32 accumulator
+// on v_mfma_f32_16x16x32_bf16, so a logit is an fp32 sum of exact products
+// of x with W_r's 24 significant bits.
+//
+// Five waves.  Wave 4 only loads x: 64-wide k stages of the tile go from
+// global memory straight into an LDS ring of NBUF stages (buffer loads to
+// LDS, no registers), NBUF - 1 stages ahead; before each block barrier it
+// waits until the next stage has landed.  Its loads are the only ones in
+// its own in-order return queue, so the compute waves' loads never wait
+// behind them.  Waves 0..3 each own NG groups of 16 experts (all three
+// terms): they load their weight fragments from L2 straight into registers
+// PW - 1 stages ahead (a ring of PW register slots, the stage loop unrolled
+// by PW) and multiply them with the tile's x fragments read from the ring.
+// MFMA step j in {0, 1} of a stage covers k 32j .. 32j + 31, lane group
+// g = lane / 16 supplying k 32j + 8g .. +8 of both operands; a weight
+// fragment of a step is one contiguous kilobyte.  A stage's rows are
+// 128 bytes; chunk s of row r sits in slot s ^ f(r), f(r) = (r % 8) ^
+// ((r / 8) % 2), so the 16 rows a fragment read serves fall on distinct
+// banks (the loader fetches chunk (lane % 8) ^ f(row) into slot lane % 8).
+//
+// After the last stage the ring becomes the logit tile: bias and noise
+// are added, and all five waves run the shared per-token epilogue; the
+// statistic partials are indexed by tile.
+template <int E_PAD, int BT, int PW>
+__global__ __launch_bounds__(320) void route_fused_kernel(
+    const uint16_t *__restrict__ x, const uint16_t *__restrict__ wsplit, const float *__restrict__ bias,
+    const float *__restrict__ noise, int T, int d, int E, int k, int gate_switch,
+    int32_t *__restrict__ topk_idx, float *__restrict__ gates, float *__restrict__ part_P,
+    float *__restrict__ part_lse2, unsigned *__restrict__ arrivals) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    constexpr int NG = E_PAD / 64;              // 16-expert groups per compute wave
+    constexpr int TM = BT / 16;                 // 16-token fragments
+    constexpr int NBUF = BT == 64 ? 8 : 16;     // x stages in the ring
+    constexpr int LPS = BT / 8;                 // loader instructions per stage (8 rows each)
+    constexpr int SB = BT * 128;                // bytes per stage
+    constexpr int RING = NBUF * SB;
+    constexpr int HLB = BT * (RT_EMAX + 1) * 4;
+    static_assert(NG >= 1 && TM >= 1 && (NBUF - 2) * LPS <= 63, "tile shape");
+    __shared__ __attribute__((aligned(1024))) char lds[RING > HLB ? RING : HLB];
+    float(*hl)[RT_EMAX + 1] = (float(*)[RT_EMAX + 1])lds;
+
+    const int tile = blockIdx.x, t0 = tile * BT;
+    const int nst = d / 64;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int g = lane >> 4, lr = lane & 15;
+    if (tile == 0 && tid == 0) *arrivals = 0u;
+    f32x4_t acc[TM][NG];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int gi = 0; gi < NG; ++gi) acc[i][gi] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    if (wave == 4) {
+        // the loader: rows past the batch read its last token (their logits
+        // are never used); offsets from the tile's first row
+        const __amdgpu_buffer_rsrc_t rsrc =
+            __builtin_amdgcn_make_buffer_rsrc((void *)(x + (int64_t)t0 * d), 0, 0x7fffffff, 0x00020000);
+        const int last = T - 1 - t0;
+        uint32_t voff[LPS];
+#pragma unroll
+        for (int q = 0; q < LPS; ++q) {
+            const int r = q * 8 + (lane >> 3);
+            const int f = (r & 7) ^ ((r >> 3) & 1);
+            voff[q] = ((uint32_t)min(r, last) * (uint32_t)d + (uint32_t)(((lane & 7) ^ f) * 8)) * 2u;
+        }
+        auto issue = [&](int st) {
+            const int sc = min(st, nst - 1);   // past the end: the last stage again, into a ring slot nobody reads
+            char *dst = lds + (st % NBUF) * SB;
+#pragma unroll
+            for (int q = 0; q < LPS; ++q)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    rsrc, (__attribute__((address_space(3))) void *)(dst + q * 1024), 16, voff[q], sc * 128, 0, 0);
+        };
+        for (int s = 0; s < NBUF - 1; ++s) issue(s);
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"((NBUF - 2) * LPS) : "memory");   // stage 0 has landed
+        __syncthreads();
+        for (int st = 0; st < nst; ++st) {
+            issue(st + NBUF - 1);   // into the slot stage st - 1 left, which every wave has finished
+            asm volatile("s_waitcnt vmcnt(%0)" ::"n"((NBUF - 2) * LPS) : "memory");   // stage st + 1 has landed
+            __syncthreads();
+        }
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // no ring write in flight when it becomes the logit tile
+    } else {
+        // compute wave `wave`: experts (wave * NG + gi) * 16 + lr, all three terms
+        const uint16_t *wrow[NG][3];
+#pragma unroll
+        for (int gi = 0; gi < NG; ++gi)
+#pragma unroll
+            for (int q = 0; q < 3; ++q)
+                wrow[gi][q] = wsplit + (int64_t)(q * E_PAD + (wave * NG + gi) * 16 + lr) * 32 + 8 * g;
+        uint4 wr[PW][NG][3][2];
+        auto load_w = [&](auto slot_c, int st) {
+            constexpr int slot = decltype(slot_c)::value;
+            const int sc = min(st, nst - 1);
+#pragma unroll
+            for (int gi = 0; gi < NG; ++gi)
+#pragma unroll
+                for (int q = 0; q < 3; ++q)
+#pragma unroll
+                    for (int h = 0; h < 2; ++h)
+                        wr[slot][gi][q][h] =
+                            *(const uint4 *)(wrow[gi][q] + (int64_t)(2 * sc + h) * (3 * E_PAD * 32));
+        };
+        const int fsw = (lr & 7) ^ ((lr >> 3) & 1);
+        int st = 0;
+        // one stage from ring slot st % NBUF and weight slot `cur`; the
+        // weights of stage st + PW - 1 are fetched into the slot stage st - 1
+        // left
+        auto stage = [&](auto cur_c) {
+            constexpr int cur = decltype(cur_c)::value;
+            constexpr std::integral_constant<int, (cur + PW - 1) % PW> nxt_c{};
+            load_w(nxt_c, st + PW - 1);
+            const char *xb = lds + (st % NBUF) * SB;
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                bf16x8_t a[TM];
+#pragma unroll
+                for (int i = 0; i < TM; ++i)
+                    a[i] = *(const bf16x8_t *)(xb + (i * 16 + lr) * 128 + (((4 * j + g) ^ fsw) * 16));
+#pragma unroll
+                for (int q = 0; q < 3; ++q)
+#pragma unroll
+                    for (int gi = 0; gi < NG; ++gi) {
+                        const bf16x8_t b = __builtin_bit_cast(bf16x8_t, wr[cur][gi][q][j]);
+#pragma unroll
+                        for (int i = 0; i < TM; ++i)
+                            acc[i][gi] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b, acc[i][gi], 0, 0, 0);
+                    }
+            }
+            __syncthreads();
+            ++st;
+        };
+        load_w(std::integral_constant<int, 0>{}, 0);
+        if constexpr (PW > 2) load_w(std::integral_constant<int, 1>{}, 1);
+        if constexpr (PW > 3) load_w(std::integral_constant<int, 2>{}, 2);
+        __syncthreads();
+        if constexpr (PW == 2) {
+            while (st + 1 < nst) {
+                stage(std::integral_constant<int, 0>{});
+                stage(std::integral_constant<int, 1>{});
+            }
+            if (st < nst) stage(std::integral_constant<int, 0>{});
+        } else {
+            static_assert(PW == 4, "weight ring of 2 or 4 slots");
+            while (st + 3 < nst) {
+                stage(std::integral_constant<int, 0>{});
+                stage(std::integral_constant<int, 1>{});
+                stage(std::integral_constant<int, 2>{});
+                stage(std::integral_constant<int, 3>{});
+            }
+            if (st < nst) stage(std::integral_constant<int, 0>{});
+            if (st < nst) stage(std::integral_constant<int, 1>{});
+            if (st < nst) stage(std::integral_constant<int, 2>{});
+        }
+    }
+    __syncthreads();   // the ring is free: it becomes the logit tile
+
+    // accumulator r of lane l (compute waves): token i * 16 + 4 g + r, expert
+    // (wave * NG + gi) * 16 + lr
+    if (wave < 4) {
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int gi = 0; gi < NG; ++gi)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int row = i * 16 + 4 * g + r, t = t0 + row;
+                    const int e = (wave * NG + gi) * 16 + lr;
+                    float v = acc[i][gi][r];
+                    if (e < E && t < T) {
+                        if (bias) v += bias[e];
+                        if (noise) v += noise[(int64_t)t * E + e];
+                    }
+                    hl[row][e] = v;
+                }
+    }
+    __syncthreads();
+    softmax_topk_block<BT, 5>(hl, t0, T, E, k, gate_switch, topk_idx, gates, part_P, part_lse2, nullptr,
+                              nullptr, nullptr, tile, gridDim.x);
+#endif
 }
 
 // Logit (t, e) is the sum over partials o < nouter (outer stride souter)
@@ -874,33 +1102,55 @@ int route_nsplit(const Shape &s) {
     return (s.d + slice - 1) / slice;
 }
 
-// The GEMM pays off where the logits kernel re-splits a large W_r for every
-// 64-token tile: many experts and a batch past the small-batch kernel.  The
-// 256-row kernel needs d % 64 == 0 and its operand offsets within 32 bits.
-bool route_gemm(const Shape &s) {
-    if (s.dtype != 1 || route_small(s) || route_epad(s) < 64 || s.d % 64 != 0) return false;
-    return (int64_t)s.T * s.d * 2 < (int64_t(1) << 31) && (int64_t)3 * route_epad(s) * s.d * 2 < (int64_t(1) << 31);
+// The fused router serves bf16 batches past the small-batch kernel with
+// more than 32 experts and d a multiple of its 64-wide k stages.  Token
+// tiles as large as still give about 256 blocks (each block reads all of
+// the weight terms from L2, so fewer, larger tiles read fewer bytes):
+// 64 tokens for at least 16384, 32 for at least 8192, else 16.
+bool route_fused(const Shape &s) {
+    return s.dtype == 1 && !route_small(s) && s.d % 64 == 0 && route_epad(s) >= 64;
 }
 
-// K halves: when the 256 x 256 output tiles would fill less than one round
-// of the CUs and the 64-wide K stages split evenly.
-int route_gemm_nsplit(const Shape &s) {
-    const int64_t tiles = (int64_t)((s.T + 255) / 256) * ((3 * route_epad(s) + 255) / 256);
-    return tiles < 256 && (s.d / 64) % 2 == 0 ? 2 : 1;
-}
+int route_fused_bt(const Shape &s) { return s.T >= 16384 ? 64 : (s.T >= 8192 ? 32 : 16); }
+
+int route_fused_ntiles(const Shape &s) { return (s.T + route_fused_bt(s) - 1) / route_fused_bt(s); }
 
 static size_t route_wsplit_matrix_bytes(const Shape &s) {
     return ((size_t)3 * route_epad(s) * s.d * 2 + 255) / 256 * 256;
 }
 
 size_t route_part_floats(const Shape &s) {
-    if (route_gemm(s)) return (size_t)route_gemm_nsplit(s) * s.T * 3 * route_epad(s);
+    if (route_fused(s)) return 0;
     return (size_t)route_nsplit(s) * s.T * s.E;
 }
 
-size_t route_wsplit_bytes(const Shape &s) {
-    return route_gemm(s) ? route_wsplit_matrix_bytes(s) + 256 : 0;
+size_t route_wsplit_bytes(const Shape &s) { return route_fused(s) ? route_wsplit_matrix_bytes(s) : 0; }
+
+int route_stat_blocks(const Shape &s) { return route_fused(s) ? route_fused_ntiles(s) : route_blocks(s); }
+
+namespace {
+
+template <int E_PAD, int BT>
+void launch_fused(const Shape &s, const void *x, const uint16_t *wm, const float *bias, const float *noise,
+                  int32_t *topk_idx, float *gates, float *part_P, float *part_lse2, unsigned *arrivals,
+                  hipStream_t st) {
+    hipLaunchKernelGGL((route_fused_kernel<E_PAD, BT, 4>), dim3((unsigned)route_fused_ntiles(s)), dim3(320), 0,
+                       st, (const uint16_t *)x, wm, bias, noise, s.T, s.d, s.E, s.k, s.gate, topk_idx, gates,
+                       part_P, part_lse2, arrivals);
 }
+
+template <int E_PAD>
+void launch_fused_e(const Shape &s, const void *x, const uint16_t *wm, const float *bias, const float *noise,
+                    int32_t *topk_idx, float *gates, float *part_P, float *part_lse2, unsigned *arrivals,
+                    hipStream_t st) {
+    switch (route_fused_bt(s)) {
+    case 64: launch_fused<E_PAD, 64>(s, x, wm, bias, noise, topk_idx, gates, part_P, part_lse2, arrivals, st); break;
+    case 32: launch_fused<E_PAD, 32>(s, x, wm, bias, noise, topk_idx, gates, part_P, part_lse2, arrivals, st); break;
+    default: launch_fused<E_PAD, 16>(s, x, wm, bias, noise, topk_idx, gates, part_P, part_lse2, arrivals, st); break;
+    }
+}
+
+}  // namespace
 
 hipError_t launch_route(const Shape &s, const void *x, const float *Wr, const float *bias,
                         const float *noise, int32_t *topk_idx, float *gates, float *part_P,
@@ -913,19 +1163,17 @@ hipError_t launch_route(const Shape &s, const void *x, const float *Wr, const fl
                            arrivals);
         return hipGetLastError();
     }
-    if (route_gemm(s)) {
+    if (route_fused(s)) {
         if (wsplit == nullptr) return hipErrorInvalidValue;
-        const int epad = route_epad(s), N = 3 * epad;
+        const int epad = route_epad(s);
         uint16_t *wm = (uint16_t *)wsplit;
-        int32_t *roffs = (int32_t *)((char *)wsplit + route_wsplit_matrix_bytes(s));
         const int64_t groups = (int64_t)epad * (s.d / 4);
         hipLaunchKernelGGL(router_wsplit_kernel, dim3((unsigned)((groups + 255) / 256)), dim3(256), 0, st, Wr,
-                           s.E, epad, s.d, s.T, wm, roffs);
-        const hipError_t err = launch_router_gemm(s, x, wm, roffs, part_logits, st);
-        if (err != hipSuccess) return err;
-        hipLaunchKernelGGL(route_epilogue_kernel, grid, block, 0, st, (const float *)part_logits,
-                           route_gemm_nsplit(s), (int64_t)s.T * N, 3, epad, N, bias, noise, s.T, s.E, s.k,
-                           s.gate, topk_idx, gates, part_P, part_lse2, arrivals);
+                           s.E, epad, s.d, wm);
+        if (epad == 64)
+            launch_fused_e<64>(s, x, wm, bias, noise, topk_idx, gates, part_P, part_lse2, arrivals, st);
+        else
+            launch_fused_e<128>(s, x, wm, bias, noise, topk_idx, gates, part_P, part_lse2, arrivals, st);
         return hipGetLastError();
     }
     switch (route_epad(s)) {
@@ -944,7 +1192,7 @@ hipError_t launch_route_finalize(const Shape &s, const int32_t *topk_idx, const 
                                  const float *part_lse2, float *stats, double *fP,
                                  unsigned *arrivals, hipStream_t st) {
     hipLaunchKernelGGL(route_stats_kernel, dim3(s.E + 1), dim3(256), 0, st, topk_idx, part_P,
-                       part_lse2, s.T, s.E, s.k, route_blocks(s), stats, fP, arrivals);
+                       part_lse2, s.T, s.E, s.k, route_stat_blocks(s), stats, fP, arrivals);
     return hipGetLastError();
 }
 

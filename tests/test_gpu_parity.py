@@ -95,12 +95,28 @@ SMALL = {
     # k = E: every expert of every token (8-lane groups, 2 idle lanes)
     "k_equals_e": W["mixtral_prefill"].with_(name="k_equals_e", T=200, d=64, d_ff=128, E=6, k=6,
                                              cf=0.0),
+    # the fused router (logits and routing in one kernel per token tile):
+    # 128-token tiles (T >= 8192) with a ragged last tile (8200 = 64 * 128 +
+    # 8), 128 experts padded from 100, K split in 4 (d = 512: 8 stages, 65
+    # tiles), top-4 with the Zipf bias and capacity drops
+    "fused_bt128": W["finegrained_zipf"].with_(name="fused_bt128", T=8200, d=512, d_ff=32, E=100),
+    # 64-token tiles, 48 experts (padded to 64), K split in 8 (d = 1024, 16
+    # tiles), Switch gate with noise and drops
+    "fused_e48_split8": W["switch"].with_(name="fused_e48_split8", T=1000, d=1024, d_ff=64, E=48,
+                                          noise_std=1.0 / 48),
+    # 20 experts (padded to 32: two expert groups and two token halves per
+    # block), d = 192 (3 stages, split 3 ways, one stage each), top-3
+    "fused_e20": W["mixtral_prefill"].with_(name="fused_e20", T=777, d=192, d_ff=64, E=20, k=3,
+                                            cf=1.1),
+    # 9 experts (padded to 16: the grouped epilogue, 16 lanes per token), one
+    # 64-token tile plus one token
+    "fused_e9": W["mixtral_prefill"].with_(name="fused_e9", T=65, d=128, d_ff=64, E=9, k=2),
 }
 
 
 # cases whose capacity is known to drop assignments (the drop path is exercised)
 EXPECT_DROPS = {"switch_small", "zipf_small", "relu_bf16", "big_gelu", "skinny_mt3_gelu",
-                "small_drops"}
+                "small_drops", "fused_bt128", "fused_e48_split8"}
 
 
 def _check_all(w, wt, tk, got=None):
