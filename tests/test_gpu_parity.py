@@ -108,6 +108,12 @@ SMALL = {
     # block), d = 192 (3 stages, split 3 ways, one stage each), top-3
     "fused_e20": W["mixtral_prefill"].with_(name="fused_e20", T=777, d=192, d_ff=64, E=20, k=3,
                                             cf=1.1),
+    # many experts on the 256-row tiles: Zipf-skewed top-4 of 64 with drops
+    # (SwiGLU up with K = 320, down with K = 512 and a partial column tile,
+    # 320 = 256 + 64), and GELU top-1 of 40 without capacity
+    "adapt_zipf": W["finegrained_zipf"].with_(name="adapt_zipf", T=4096, d=320, d_ff=512, E=64),
+    "adapt_gelu": W["switch"].with_(name="adapt_gelu", T=12000, d=192, d_ff=256, E=40, cf=0.0,
+                                    noise_std=1.0 / 40),
     # 9 experts (padded to 16: the grouped epilogue, 16 lanes per token), one
     # 64-token tile plus one token
     "fused_e9": W["mixtral_prefill"].with_(name="fused_e9", T=65, d=128, d_ff=64, E=9, k=2),
@@ -116,7 +122,7 @@ SMALL = {
 
 # cases whose capacity is known to drop assignments (the drop path is exercised)
 EXPECT_DROPS = {"switch_small", "zipf_small", "relu_bf16", "big_gelu", "skinny_mt3_gelu",
-                "small_drops", "fused_bt128", "fused_e48_split8"}
+                "small_drops", "fused_bt128", "fused_e48_split8", "adapt_zipf"}
 
 
 def _check_all(w, wt, tk, got=None):
