@@ -64,6 +64,9 @@ def _load():
                                  fp, fp, fp, ip, fp, ctypes.c_double, ctypes.c_double, fp, fp, fp,
                                  fp, fp, fp]
     lib.orc_backward.restype = ctypes.c_int
+    lib.orc_expert_wgrad_sel.argtypes = [i64, ip, dp, i64, i64, ctypes.c_int, fp, fp, fp, fp, fp, i64, ip,
+                                         fp, fp, fp]
+    lib.orc_expert_wgrad_sel.restype = ctypes.c_int
     lib.orc_threads.argtypes = []
     lib.orc_threads.restype = ctypes.c_int
     lib.orc_set_threads.argtypes = [ctypes.c_int]
@@ -268,6 +271,30 @@ def backward(x, Wr, W1, W3, W2, k, mode, cf, act, dy, alpha_aux=0.0, alpha_z=0.0
     if rc != 0:
         raise ValueError("orc_backward failed")
     return out
+
+
+def expert_wgrad_sel(x, W1e, W3e, W2e, tok, gate, dy, act, fsel):
+    """Weight gradients of one expert for the hidden units ``fsel`` (the
+    backward's rows of dW1 and dW3 and columns of dW2, see
+    orc_expert_wgrad_sel): x, dy [T][d]; W1e, W3e [d_ff][d] (W3e only for
+    SwiGLU), W2e [d][d_ff] of that expert; tok, gate [n] its kept rows in
+    token order.  Returns dW1 [nf][d], dW3 [nf][d] or None, dW2 [d][nf]."""
+    x, W1e, W2e, dy = _f32(x), _f32(W1e), _f32(W2e), _f32(dy)
+    W3e = _f32(W3e) if act == "swiglu" else None
+    tok = np.ascontiguousarray(tok, dtype=np.int32)
+    gate = np.ascontiguousarray(gate, dtype=np.float64)
+    fsel = np.ascontiguousarray(fsel, dtype=np.int32)
+    d_ff, d = W1e.shape
+    assert W2e.shape == (d, d_ff) and x.shape[1] == d and dy.shape == x.shape
+    nf = len(fsel)
+    dW1 = np.empty((nf, d), np.float32)
+    dW3 = np.empty((nf, d), np.float32) if W3e is not None else None
+    dW2 = np.empty((d, nf), np.float32)
+    rc = _load().orc_expert_wgrad_sel(len(tok), _p(tok), _p(gate), d, d_ff, _ACT[act], _p(x), _p(W1e),
+                                      _p(W3e), _p(W2e), _p(dy), nf, _p(fsel), _p(dW1), _p(dW3), _p(dW2))
+    if rc != 0:
+        raise MemoryError("orc_expert_wgrad_sel: could not allocate its scratch")
+    return dict(dW1=dW1, dW3=dW3, dW2=dW2)
 
 
 def threads():

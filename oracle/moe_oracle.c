@@ -791,6 +791,101 @@ out:
     return rc;
 }
 
+/*
+ * Weight gradients of ONE expert for selected hidden units only (the
+ * layer's backward of orc_backward restricted to what a sample of a large
+ * layer needs): for every f in fsel, row f of dW1 and dW3 and column f of
+ * dW2, from the expert's kept rows in token order (page "Mixture of
+ * experts", Mechanics: the gate multiplies the expert output; the expert is
+ * the Implementation section's w2(act(w1 x) [* w3 x])).  For each kept row
+ * r (token t_r, gate g_r):
+ *   dE_r      = g_r * dy[t_r]                        (gradient of the expert output)
+ *   a1, a3    = W1[f] . x[t_r],  W3[f] . x[t_r]      (double)
+ *   H_r       = fl32(act(a1, a3))                    (the forward's stored hidden unit)
+ *   dH_r      = sum_o W2[o][f] dE_r[o]
+ *   da1, da3  = the activation's derivative times dH_r
+ * and, summed over the rows in order and rounded once,
+ *   dW1s[i][j] = sum_r da1_r x[t_r][j],  dW3s[i][j] = sum_r da3_r x[t_r][j],
+ *   dW2s[o][i] = sum_r dE_r[o] H_r          (f = fsel[i]).
+ *   tok, gate  [n]        kept rows of the expert: token and gate
+ *   W1, W3     [d_ff][d]  this expert's up projections (W3 only for SwiGLU)
+ *   W2         [d][d_ff]  this expert's down projection
+ *   dy         [T][d], x [T][d]
+ *   dW1s, dW3s [nf][d];  dW2s [d][nf]
+ * Returns 0, or -1 when scratch cannot be allocated.
+ */
+int orc_expert_wgrad_sel(int64_t n, const int32_t *tok, const double *gate, int64_t d, int64_t d_ff,
+                         int act, const float *x, const float *W1, const float *W3, const float *W2,
+                         const float *dy, int64_t nf, const int32_t *fsel, float *dW1s, float *dW3s,
+                         float *dW2s)
+{
+    const int swiglu = act == ORC_ACT_SWIGLU;
+    int bad = 0;
+#pragma omp parallel reduction(| : bad)
+    {
+    double *da1 = (double *)malloc((size_t)(n + 1) * sizeof(double));
+    double *da3 = (double *)malloc((size_t)(n + 1) * sizeof(double));
+    double *Hr = (double *)malloc((size_t)(n + 1) * sizeof(double));
+    if (!da1 || !da3 || !Hr)
+        bad = 1;
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t i = 0; i < nf; ++i) {
+        if (!da1 || !da3 || !Hr)
+            continue;
+        const int64_t f = fsel[i];
+        const float *w1 = W1 + f * d, *w3 = swiglu ? W3 + f * d : NULL;
+        for (int64_t r = 0; r < n; ++r) {
+            const float *xt = x + (int64_t)tok[r] * d;
+            const float *dyt = dy + (int64_t)tok[r] * d;
+            double u = 0.0, v = 0.0;
+            for (int64_t j = 0; j < d; ++j) {
+                u += (double)xt[j] * (double)w1[j];
+                if (w3)
+                    v += (double)xt[j] * (double)w3[j];
+            }
+            Hr[r] = (double)(float)orc_act(act, u, v);
+            double dH = 0.0;
+            for (int64_t o = 0; o < d; ++o)
+                dH += (double)W2[o * d_ff + f] * (gate[r] * (double)dyt[o]);
+            if (act == ORC_ACT_SWIGLU) {
+                const double sg = 1.0 / (1.0 + exp(-u));
+                da1[r] = dH * v * sg * (1.0 + u * (1.0 - sg));
+                da3[r] = dH * u * sg;
+            } else if (act == ORC_ACT_GELU) {
+                const double Phi = 0.5 * (1.0 + erf(u / sqrt(2.0)));
+                const double phi = exp(-0.5 * u * u) / sqrt(2.0 * acos(-1.0));
+                da1[r] = dH * (Phi + u * phi);
+                da3[r] = 0.0;
+            } else {
+                da1[r] = u > 0.0 ? dH : 0.0;
+                da3[r] = 0.0;
+            }
+        }
+        for (int64_t j = 0; j < d; ++j) {
+            double a = 0.0, b = 0.0;
+            for (int64_t r = 0; r < n; ++r) {
+                const double xv = (double)x[(int64_t)tok[r] * d + j];
+                a += da1[r] * xv;
+                b += da3[r] * xv;
+            }
+            dW1s[i * d + j] = (float)a;
+            if (swiglu)
+                dW3s[i * d + j] = (float)b;
+        }
+        for (int64_t o = 0; o < d; ++o) {
+            double a = 0.0;
+            for (int64_t r = 0; r < n; ++r)
+                a += (gate[r] * (double)dy[(int64_t)tok[r] * d + o]) * Hr[r];
+            dW2s[o * nf + i] = (float)a;
+        }
+    }
+    free(da1);
+    free(da3);
+    free(Hr);
+    }
+    return bad ? -1 : 0;
+}
+
 #ifdef _OPENMP
 #include <omp.h>
 #endif

@@ -231,3 +231,17 @@ def sample_tokens(T, n, seed=0, must=()):
         if len(out) >= min(n, T):
             break
     return np.array(sorted(out), np.int64)
+
+
+def tile_edge_tokens(ref, tile=256):
+    """Tokens whose permuted rows sit at the edges of the grouped GEMMs' row
+    tiles, through the oracle's permutation: every expert's first and last
+    kept row and the first and last row of each of its tiles of `tile` rows
+    (so every expert's last, partial tile is covered)."""
+    offs, tor = ref["offsets"], ref["token_of_row"]
+    rows = []
+    for e in range(len(offs) - 1):
+        lo, hi = int(offs[e]), int(offs[e + 1])
+        for r0 in range(lo, hi, tile):
+            rows += [r0, min(r0 + tile, hi) - 1]
+    return np.unique(tor[np.array(rows, np.int64)]) if rows else np.zeros(0, np.int64)

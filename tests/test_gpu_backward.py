@@ -123,7 +123,8 @@ def test_full_size_backward_mixtral():
     8 sampled tokens (their own routing, all kept) gives their dx exactly.
     Every gradient of dy scaled by 2 must be exactly twice that of dy (a
     power-of-two scale passes every bf16 and fp32 step unchanged), and the
-    call must repeat bit for bit."""
+    call must repeat bit for bit.  The busiest expert's weight gradients are
+    compared on 16 hidden units (rows of dW1, dW3, columns of dW2)."""
     w = W["mixtral_prefill"]
     print(f"[bwd] full size {w.name}", flush=True)
     wt, tk = H.prepare(w)
@@ -159,3 +160,23 @@ def test_full_size_backward_mixtral():
     scale = float(np.abs(r).max())
     err = float(np.abs(g.astype(np.float64) - r).max())
     assert err <= 2e-2 * scale, f"dx: max|err| {err:.3e} > 2e-2 * {scale:.3e}"
+    # weight gradients of the busiest expert: 16 rows of dW1 and dW3 and 16
+    # columns of dW2 (hidden units spread over d_ff, the first and the last
+    # included) against the oracle's one-expert gradients over all its rows
+    e = int(np.argmax(ref_fw["kept"]))
+    lo, hi = int(ref_fw["offsets"][e]), int(ref_fw["offsets"][e + 1])
+    tok = ref_fw["token_of_row"][lo:hi]
+    t_s = np.nonzero((ref_fw["idx"] == e) & (ref_fw["row_of_slot"] >= 0))
+    gate = np.zeros(hi - lo)
+    gate[ref_fw["row_of_slot"][t_s] - lo] = ref_fw["gates"][t_s]
+    fsel = np.unique(np.concatenate([[0, w.d_ff - 1],
+                                     np.random.default_rng(4).choice(w.d_ff, 14, replace=False)]))
+    print(f"[bwd] oracle weight gradients of expert {e} ({hi - lo} rows, {len(fsel)} hidden units)", flush=True)
+    wg = oracle.expert_wgrad_sel(synth.widen(tk["x"]), synth.widen(wt["W1"][e]), synth.widen(wt["W3"][e]),
+                                 synth.widen(wt["W2"][e]), tok, gate, synth.widen(dy_bits), w.act, fsel)
+    for key, got_k, ref_k in (("dW1", out[0]["dW1"][e][fsel], wg["dW1"]),
+                              ("dW3", out[0]["dW3"][e][fsel], wg["dW3"]),
+                              ("dW2", out[0]["dW2"][e][:, fsel], wg["dW2"])):
+        scale = float(np.abs(ref_k).max())
+        err = float(np.abs(got_k.astype(np.float64) - ref_k).max())
+        assert err <= 2e-2 * scale, f"{key}[{e}]: max|err| {err:.3e} > 2e-2 * {scale:.3e}"

@@ -7,6 +7,9 @@ output is compared on a sample of tokens the oracle computes one by one
 checked on all tokens: every output is finite, and a token dropped from
 every expert has output exactly 0 (without shared experts and residual;
 with them, the sample includes such tokens and their outputs are compared).
+The sample includes the tokens at the first and last row of every 256-row
+tile of every expert (through the oracle's permutation), so each expert's
+last, partial row tile is checked.
 """
 import numpy as np
 import pytest
@@ -17,8 +20,8 @@ import harness as H
 
 pytestmark = pytest.mark.gpu
 
-N_SAMPLE = {"switch": 96, "mixtral_prefill": 24, "mixtral_decode": 32, "finegrained_zipf": 96,
-            "finegrained_zipf_shared": 96, "mixtral_prefill_shared": 16}
+N_SAMPLE = {"switch": 96, "mixtral_prefill": 96, "mixtral_decode": 32, "finegrained_zipf": 96,
+            "finegrained_zipf_shared": 96, "mixtral_prefill_shared": 48}
 
 
 @pytest.mark.parametrize("name", ["switch", "mixtral_prefill", "mixtral_decode", "finegrained_zipf",
@@ -29,9 +32,14 @@ def test_full_size(name):
     wt, tk = H.prepare(w)
     print(f"[full] {name}: routing on the oracle", flush=True)
     route_ref = H.reference(w, wt, tk, tokens=np.zeros(0, np.int64))
-    # sample: some fully dropped tokens if there are any, the rest spread out
+    # sample: the tokens at the edges of every expert's 256-row tiles (all of
+    # them for the Mixtral layers; as many as fit for the others), some
+    # fully dropped tokens if there are any, the rest spread out
     full_drop = np.nonzero((route_ref["row_of_slot"] < 0).all(axis=1))[0]
-    sel = H.sample_tokens(w.T, N_SAMPLE[name], seed=1, must=full_drop[:4])
+    edges = H.tile_edge_tokens(route_ref)
+    n = N_SAMPLE[name]
+    sel = H.sample_tokens(w.T, max(n, len(edges) + 12) if name.startswith("mixtral_prefill") else n,
+                          seed=1, must=np.concatenate([full_drop[:4], edges[:max(0, n - 12)]]))
     print(f"[full] {name}: oracle FFN on {len(sel)} tokens", flush=True)
     ref = H.reference(w, wt, tk, tokens=sel)
     print(f"[full] {name}: GPU forward", flush=True)

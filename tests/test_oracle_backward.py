@@ -117,3 +117,28 @@ def test_z_gradient_closed_form():
     h = (x.astype(np.float64) @ Wr.astype(np.float64).T + b).astype(np.float32).astype(np.float64)
     ref = (2.0 / T * sps.logsumexp(h, axis=1)[:, None] * sps.softmax(h, axis=1)).sum(axis=0)
     np.testing.assert_allclose(o["dbias"], ref, rtol=1e-6)
+
+
+@pytest.mark.parametrize("mode,act,cf,k", [("renorm", "swiglu", 0.5, 2), ("switch", "gelu", 1.0, 1),
+                                           ("renorm", "relu", 0.0, 3)])
+def test_selected_weight_gradients_match_autograd(mode, act, cf, k):
+    """The one-expert, selected-hidden-unit weight gradients (used where the
+    whole backward is too large) against torch autograd: rows of dW1 and dW3
+    and columns of dW2 of every expert, for a spread of hidden units, with
+    the expert's kept rows in token order from the oracle's routing."""
+    T, d, d_ff, E = 30, 12, 16, 4
+    x, Wr, b, n, W1, W3, W2, dy = _inputs(21 + k, T, d, d_ff, E, act)
+    fw = oracle.forward(x, Wr, W1, W3, W2, k, mode, cf, act, b, n)
+    ref = _autograd(x, Wr, b, n, W1, W3, W2, dy, fw["idx"], fw["row_of_slot"], k, mode, act, 0.0, 0.0)
+    fsel = np.array([0, 5, 6, 15])
+    for e in range(E):
+        lo, hi = fw["offsets"][e], fw["offsets"][e + 1]
+        tok = fw["token_of_row"][lo:hi]
+        t_s = np.nonzero((fw["idx"] == e) & (fw["row_of_slot"] >= 0))
+        gate = np.zeros(hi - lo)
+        gate[fw["row_of_slot"][t_s] - lo] = fw["gates"][t_s]
+        got = oracle.expert_wgrad_sel(x, W1[e], None if W3 is None else W3[e], W2[e], tok, gate, dy, act, fsel)
+        _close(got["dW1"], ref["dW1"][e][fsel], 1e-6, f"dW1[{e}]")
+        _close(got["dW2"], ref["dW2"][e][:, fsel], 1e-6, f"dW2[{e}]")
+        if act == "swiglu":
+            _close(got["dW3"], ref["dW3"][e][fsel], 1e-6, f"dW3[{e}]")
