@@ -122,7 +122,9 @@ extern "C" {
  * (so the expert-down stage then ends at the combine's start).  NULL disables the hook.  The stages, in order: route,
  * route-finalize, dispatch, gather, expert-up, expert-down, combine; in
  * moe_forward the gather is folded into expert-up (its rows of x are read
- * through token_of_row), so that stage is empty.
+ * through token_of_row), so that stage is empty, and the statistics are
+ * finished by extra blocks of the dispatch launch, so route-finalize is
+ * empty as well.
  * The other entry points ignore it.
  */
 typedef struct moe_desc {

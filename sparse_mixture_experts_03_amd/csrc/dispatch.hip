@@ -26,6 +26,7 @@
 // gather_kernel: x_perm[r] = x[token_of_row[r]] for r < offsets[E]; one
 //   wave per row, 16-byte loads and stores, grid-stride over rows.
 #include "moe_internal.h"
+#include "route_stats.h"
 
 namespace moe {
 
@@ -69,11 +70,27 @@ __global__ __launch_bounds__(DP_THREADS) void dispatch_count_kernel(
     if (tid < E) chunk_counts[(int64_t)blockIdx.x * E + tid] = hist[tid];
 }
 
+// Blocks past the last chunk (when moe_forward passes the statistics'
+// arguments) finish the load-balancing statistics instead (route_stats.h),
+// so that reduction runs beside the ranking rather than as its own launch.
+struct StatsArgs {
+    const float *part_P, *part_lse2;
+    int T, nblk;
+    float *stats;
+    double *fP;
+    unsigned *arrivals;
+};
+
 __global__ __launch_bounds__(DP_THREADS) void dispatch_rank_kernel(
     const int32_t *__restrict__ topk_idx, int64_t Tk, int k, int E, int64_t C, int chunk_len,
     int nchunks, const int32_t *__restrict__ chunk_counts, int32_t *__restrict__ routed,
     int32_t *__restrict__ kept, int32_t *__restrict__ offsets, int32_t *__restrict__ row_of_slot,
-    int32_t *__restrict__ token_of_row, uint8_t *__restrict__ dropped) {
+    int32_t *__restrict__ token_of_row, uint8_t *__restrict__ dropped, StatsArgs sa) {
+    if ((int)blockIdx.x >= nchunks) {
+        route_stats_block((int)blockIdx.x - nchunks, sa.part_P, sa.part_lse2, sa.T, E, sa.nblk, sa.stats, sa.fP,
+                          sa.arrivals);
+        return;
+    }
     __shared__ int running[DP_EMAX];  // assignments of e before the current round
     __shared__ int off[DP_EMAX];      // first row of expert e
     __shared__ int keptc[DP_EMAX];
@@ -97,7 +114,8 @@ __global__ __launch_bounds__(DP_THREADS) void dispatch_rank_kernel(
         if (nchunks == 1) {
             tot = running[tid];
         } else {
-#pragma unroll 8
+            // 32 histogram loads in flight at a time
+#pragma unroll 32
             for (int c = 0; c < nchunks; ++c) {
                 const int v = chunk_counts[(int64_t)c * E + tid];
                 before += (c < chunk) ? v : 0;
@@ -112,16 +130,29 @@ __global__ __launch_bounds__(DP_THREADS) void dispatch_rank_kernel(
         }
     }
     __syncthreads();
-    if (tid == 0) {
-        int o = 0;
-        for (int e = 0; e < E; ++e) {
-            off[e] = o;
-            o += keptc[e];
+    if (tid < 64) {
+        // exclusive prefix of the kept counts over the experts: wave 0, two
+        // experts per lane (lane l: experts l and l + 64), shuffle scans
+        const int k0 = tid < E ? keptc[tid] : 0, k1 = tid + 64 < E ? keptc[tid + 64] : 0;
+        int i0 = k0, i1 = k1;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const int u0 = __shfl_up(i0, o), u1 = __shfl_up(i1, o);
+            if (tid >= o) {
+                i0 += u0;
+                i1 += u1;
+            }
         }
-        sh_total = o;
+        const int tot0 = __shfl(i0, 63);
+        i1 += tot0;
+        if (tid < E) off[tid] = i0 - k0;
+        if (tid + 64 < E) off[tid + 64] = i1 - k1;
+        const int total = __shfl(i1, 63);
+        if (tid == 0) sh_total = total;
         if (chunk == 0) {
-            for (int e = 0; e < E; ++e) offsets[e] = off[e];
-            offsets[E] = o;
+            if (tid < E) offsets[tid] = i0 - k0;
+            if (tid + 64 < E) offsets[tid + 64] = i1 - k1;
+            if (tid == 0) offsets[E] = total;
         }
     }
     __syncthreads();
@@ -209,15 +240,21 @@ int dispatch_chunks(const Shape &s) {
 hipError_t launch_dispatch(const Shape &s, const int32_t *topk_idx, int32_t *routed,
                            int32_t *kept, int32_t *offsets, int32_t *row_of_slot,
                            int32_t *token_of_row, uint8_t *dropped, int32_t *chunk_counts,
-                           hipStream_t st) {
+                           hipStream_t st, const RouteStatsIn *stats) {
     const int nch = dispatch_chunks(s);
     const int chunk = dispatch_chunk(s);
     if (nch > 1)
         hipLaunchKernelGGL(dispatch_count_kernel, dim3(nch), dim3(DP_THREADS), 0, st, topk_idx,
                            s.Tk(), s.k, s.E, chunk, chunk_counts);
-    hipLaunchKernelGGL(dispatch_rank_kernel, dim3(nch), dim3(DP_THREADS), 0, st, topk_idx, s.Tk(),
+    StatsArgs sa{};
+    unsigned blocks = (unsigned)nch;
+    if (stats) {
+        sa = StatsArgs{stats->part_P, stats->part_lse2, s.T, stats->nblk, stats->stats, stats->fP, stats->arrivals};
+        blocks += (unsigned)s.E + 1;
+    }
+    hipLaunchKernelGGL(dispatch_rank_kernel, dim3(blocks), dim3(DP_THREADS), 0, st, topk_idx, s.Tk(),
                        s.k, s.E, s.C, chunk, nch, (const int32_t *)chunk_counts, routed, kept,
-                       offsets, row_of_slot, token_of_row, dropped);
+                       offsets, row_of_slot, token_of_row, dropped, sa);
     return hipGetLastError();
 }
 

@@ -448,13 +448,15 @@ int forward_impl(const moe_desc *desc, const moe_shared *sh, const moe_fp8_exper
                                   L.wsplit ? at<char>(ws, L.wsplit) : nullptr,
                                   at<unsigned>(ws, L.arrivals), st));
         MOE_TRY(ev.record(st));
-        MOE_TRY(moe::launch_route_finalize(s, topk_idx, at<float>(ws, L.part_P),
-                                           at<float>(ws, L.part_lse2), stats,
-                                           at<double>(ws, L.fP),
-                                           at<unsigned>(ws, L.arrivals), st));
+        // the statistics are finished by extra blocks of the dispatch launch
+        // (the same reduction as launch_route_finalize's), so the
+        // route-finalize stage is empty
         MOE_TRY(ev.record(st));
+        const moe::RouteStatsIn rs{at<float>(ws, L.part_P), at<float>(ws, L.part_lse2),
+                                   moe::route_stat_blocks(s), stats, at<double>(ws, L.fP),
+                                   at<unsigned>(ws, L.arrivals)};
         MOE_TRY(moe::launch_dispatch(s, topk_idx, routed_counts, kept_counts, offsets, row_of_slot,
-                                     token_of_row, dropped, at<int32_t>(ws, L.chunk_counts), st));
+                                     token_of_row, dropped, at<int32_t>(ws, L.chunk_counts), st, &rs));
     }
     MOE_TRY(ev.record(st));
     // the gather is folded into the up projection's loads: its rows of A are

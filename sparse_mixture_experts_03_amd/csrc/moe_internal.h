@@ -101,10 +101,19 @@ hipError_t launch_route_finalize(const Shape &s, const int32_t *topk_idx, const 
 // workspace.
 int dispatch_chunk(const Shape &s);
 int dispatch_chunks(const Shape &s);
+// The statistics' inputs and outputs (those of launch_route_finalize), for a
+// dispatch launch that also finishes the statistics in extra blocks.
+struct RouteStatsIn {
+    const float *part_P, *part_lse2;
+    int nblk;
+    float *stats;
+    double *fP;
+    unsigned *arrivals;
+};
 hipError_t launch_dispatch(const Shape &s, const int32_t *topk_idx, int32_t *routed,
                            int32_t *kept, int32_t *offsets, int32_t *row_of_slot,
                            int32_t *token_of_row, uint8_t *dropped, int32_t *chunk_counts,
-                           hipStream_t st);
+                           hipStream_t st, const RouteStatsIn *stats = nullptr);
 hipError_t launch_gather(const Shape &s, const void *x, const int32_t *token_of_row,
                          const int32_t *offsets, void *x_perm, hipStream_t st);
 

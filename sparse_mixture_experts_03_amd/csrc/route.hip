@@ -42,6 +42,7 @@
 #include <type_traits>
 
 #include "moe_internal.h"
+#include "route_stats.h"
 
 namespace moe {
 
@@ -845,90 +846,12 @@ __global__ __launch_bounds__(RT_THREADS) void route_epilogue_kernel(
     softmax_topk_block<TILE>(hl, t0, T, E, k, gate_switch, topk_idx, gates, part_P, part_lse2);
 }
 
-// Statistics in double, every sum in a fixed order.  route_stats_kernel:
-// block e < E reduces expert e's block partials of p (thread t takes blocks
-// t, t+256, ...; then the 256 thread sums are added in thread order) and
-// adds up its block counts of top choices; block E reduces the lse^2
-// partials the same way.  The last block to finish (an integer arrival
-// counter, zeroed by the route kernel that runs before) adds the f_e P_e in
-// expert order for aux and writes aux and z, then re-zeroes the counter.
-__device__ __forceinline__ double block_sum_fixed(double v, double *red) {
-    const int tid = threadIdx.x;
-    red[tid] = v;
-    __syncthreads();
-    // threads 0..15 each add 16 consecutive values in order, then thread 0
-    // adds the 16 group sums in order
-    if (tid < 16) {
-        double g = 0.0;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) g += red[tid * 16 + i];
-        red[256 + tid] = g;
-    }
-    __syncthreads();
-    double total = 0.0;
-    if (tid == 0)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) total += red[256 + i];
-    return total;  // valid in thread 0
-}
-
+// Statistics in double, every sum in a fixed order (route_stats_block, in
+// route_stats.h): E + 1 blocks, the last to finish writing aux and z.
 __global__ __launch_bounds__(256) void route_stats_kernel(
-    const int32_t *__restrict__ topk_idx, const float *__restrict__ part_P,
-    const float *__restrict__ part_lse2, int T, int E, int k, int nblk,
+    const float *__restrict__ part_P, const float *__restrict__ part_lse2, int T, int E, int nblk,
     float *__restrict__ stats, double *__restrict__ fP, unsigned *__restrict__ arrivals) {
-    __shared__ double red[256 + 16];
-    __shared__ int cnt[4];
-    __shared__ int last;
-    const int tid = threadIdx.x;
-    const int e = blockIdx.x;
-    if (e == E) {
-        double z = 0.0;
-        for (int b = tid; b < nblk; b += 256) z += (double)part_lse2[b];
-        z = block_sum_fixed(z, red);
-        if (tid == 0) fP[E] = z / (double)T;
-    } else {
-        // expert e's block partials are contiguous: p sums, then top-choice
-        // counts
-        const float *pp = part_P + (int64_t)e * nblk;
-        const float *pc = part_P + (int64_t)(E + e) * nblk;
-        double acc = 0.0;
-        int c = 0;
-#pragma unroll 8
-        for (int b = tid; b < nblk; b += 256) {
-            acc += (double)pp[b];
-            c += (int)pc[b];
-        }
-        // integer count: the order of the additions does not matter
-        for (int o = 32; o > 0; o >>= 1) c += __shfl_xor(c, o);
-        if ((tid & 63) == 0) cnt[tid >> 6] = c;
-        const double P = block_sum_fixed(acc, red) / (double)T;
-        if (tid == 0) {
-            const double f = (double)(cnt[0] + cnt[1] + cnt[2] + cnt[3]) / (double)T;
-            stats[e] = (float)f;
-            stats[E + e] = (float)P;
-            fP[e] = f * P;
-        }
-    }
-    if (tid == 0) {
-        __threadfence();
-        last = atomicAdd(arrivals, 1u) == (unsigned)E;
-    }
-    __syncthreads();
-    if (last) {
-        // every block's f_e P_e (and z) is visible: all threads load them
-        // at once, thread 0 adds them in expert order
-        __threadfence();
-        for (int i = tid; i <= E; i += 256)
-            red[i] = __hip_atomic_load(fP + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __syncthreads();
-        if (tid == 0) {
-            double a = 0.0;
-            for (int i = 0; i < E; ++i) a += red[i];
-            stats[2 * E] = (float)((double)E * a);
-            stats[2 * E + 1] = (float)red[E];
-            *arrivals = 0u;
-        }
-    }
+    route_stats_block(blockIdx.x, part_P, part_lse2, T, E, nblk, stats, fP, arrivals);
 }
 
 // Small batches: one block of 16 waves finishes the routing.  The logits of
@@ -1191,8 +1114,9 @@ hipError_t launch_route(const Shape &s, const void *x, const float *Wr, const fl
 hipError_t launch_route_finalize(const Shape &s, const int32_t *topk_idx, const float *part_P,
                                  const float *part_lse2, float *stats, double *fP,
                                  unsigned *arrivals, hipStream_t st) {
-    hipLaunchKernelGGL(route_stats_kernel, dim3(s.E + 1), dim3(256), 0, st, topk_idx, part_P,
-                       part_lse2, s.T, s.E, s.k, route_stat_blocks(s), stats, fP, arrivals);
+    (void)topk_idx;
+    hipLaunchKernelGGL(route_stats_kernel, dim3(s.E + 1), dim3(256), 0, st, part_P, part_lse2, s.T, s.E,
+                       route_stat_blocks(s), stats, fP, arrivals);
     return hipGetLastError();
 }
 
