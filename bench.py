@@ -385,7 +385,8 @@ def hbm_layer_object(w, steps, warmup=5):
                      "algorithmic_per_step": nbytes, "traffic": None},
         "dominant_kernel": {"stage": dom, "mean_launch_ms": round(stages[dom], 4),
                             "algorithmic_per_launch": kb, "achieved": round(kgbs, 1),
-                            "unit": "GB/s", "frac": round(kgbs / PEAK_HBM_GBS, 4)},
+                            "unit": "GB/s", "frac": round(kgbs / PEAK_HBM_GBS, 4),
+                            "traffic": traffic_for(w.name, dom)},
     }
 
 
