@@ -12,7 +12,8 @@
 //   dispatch_count_kernel (one block per chunk): per-chunk histogram over
 //     experts with LDS integer atomics (a count does not depend on the
 //     order of the additions).  Skipped when there is a single chunk: the
-//     ranking block then counts its own chunk.
+//     ranking block then counts its own chunk.  Both kernels load their
+//     chunk's indices in one round trip into LDS and check them there.
 //   dispatch_rank_kernel (one block per chunk): every block derives, from
 //     all chunk histograms, routed_e, kept_e = min(routed_e, C), the row
 //     offsets (exclusive prefix of kept_e) and, for its own chunk, how many
@@ -34,20 +35,22 @@ namespace {
 
 constexpr int DP_THREADS = 256;
 constexpr int DP_EMAX = 128;
+constexpr int DP_MAXR = 4;   // rounds of DP_THREADS assignments per chunk (chunk <= 1024)
 
-// The expert of assignment j (token j / k, slot j % k), or -1 when the
-// assignment is not a valid choice: an index outside [0, E), or an expert
-// the token already chose in an earlier slot.  Routing from moe_route never
-// has either; moe_dispatch takes caller indices, and an invalid one is
-// treated as dropped (not routed, no row) instead of indexing the LDS
-// histograms out of range or giving an expert more rows than tokens.
-__device__ __forceinline__ int assignment_expert(const int32_t *__restrict__ topk_idx, int64_t j, int k,
-                                                 int E) {
-    const int e = topk_idx[j];
+// The expert of assignment j (token j / k, slot j % k), whose index e was
+// read, or -1 when the assignment is not a valid choice: an index outside
+// [0, E), or an expert the token already chose in an earlier slot.  Routing
+// from moe_route never has either; moe_dispatch takes caller indices, and
+// an invalid one is treated as dropped (not routed, no row) instead of
+// indexing the LDS histograms out of range or giving an expert more rows
+// than tokens.  The token's earlier slots come from tkc, the chunk's
+// indices in LDS (chunk start j0), or from memory when the token began in
+// the previous chunk.
+__device__ __forceinline__ int valid_expert(int e, int64_t j, int64_t j0, int k, int E, const int *tkc,
+                                            const int32_t *__restrict__ topk_idx) {
     if ((unsigned)e >= (unsigned)E) return -1;
-    const int64_t t0 = j - j % k;
-    for (int64_t i = t0; i < j; ++i)
-        if (topk_idx[i] == e) return -1;
+    for (int64_t i = j - j % k; i < j; ++i)
+        if ((i >= j0 ? tkc[i - j0] : topk_idx[i]) == e) return -1;
     return e;
 }
 
@@ -55,14 +58,27 @@ __global__ __launch_bounds__(DP_THREADS) void dispatch_count_kernel(
     const int32_t *__restrict__ topk_idx, int64_t Tk, int k, int E, int chunk,
     int32_t *__restrict__ chunk_counts) {
     __shared__ int hist[DP_EMAX];
+    __shared__ int tkc[DP_MAXR * DP_THREADS];   // the chunk's expert indices
     const int tid = threadIdx.x;
+    const int nr = chunk / DP_THREADS;
+    const int64_t j0 = (int64_t)blockIdx.x * chunk;
+    // all of the chunk's loads in flight together, then validity from LDS
+    int raw[DP_MAXR];
+#pragma unroll
+    for (int q = 0; q < DP_MAXR; ++q) {
+        const int64_t j = j0 + q * DP_THREADS + tid;
+        raw[q] = (q < nr && j < Tk) ? topk_idx[j] : -1;
+    }
+#pragma unroll
+    for (int q = 0; q < DP_MAXR; ++q)
+        if (q < nr) tkc[q * DP_THREADS + tid] = raw[q];
     if (tid < DP_EMAX) hist[tid] = 0;
     __syncthreads();
-    const int64_t j0 = (int64_t)blockIdx.x * chunk;
-    for (int q = 0; q < chunk / DP_THREADS; ++q) {
+#pragma unroll
+    for (int q = 0; q < DP_MAXR; ++q) {
         const int64_t j = j0 + q * DP_THREADS + tid;
-        if (j < Tk) {
-            const int e = assignment_expert(topk_idx, j, k, E);
+        if (q < nr && j < Tk) {
+            const int e = valid_expert(raw[q], j, j0, k, E, tkc, topk_idx);
             if (e >= 0) atomicAdd(&hist[e], 1);
         }
     }
@@ -95,33 +111,52 @@ __global__ __launch_bounds__(DP_THREADS) void dispatch_rank_kernel(
     __shared__ int off[DP_EMAX];      // first row of expert e
     __shared__ int keptc[DP_EMAX];
     __shared__ int wcnt[DP_THREADS / 64][DP_EMAX];
+    __shared__ int tkc[DP_MAXR * DP_THREADS];   // the chunk's expert indices
     __shared__ int sh_total;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int chunk = blockIdx.x;
+    const int nr = chunk_len / DP_THREADS;      // rounds of 256 assignments
+    const int64_t j0 = (int64_t)chunk * chunk_len;
 
+    // One memory round trip for everything the ranking reads: the chunk
+    // histograms (expert tid's count in every chunk) and this chunk's
+    // indices are all loaded before the first use.
+    int before = 0, tot = 0;
+    if (nchunks > 1 && tid < E) {
+#pragma unroll 32
+        for (int c = 0; c < nchunks; ++c) {
+            const int v = chunk_counts[(int64_t)c * E + tid];
+            before += (c < chunk) ? v : 0;
+            tot += v;
+        }
+    }
+    int raw[DP_MAXR];
+#pragma unroll
+    for (int q = 0; q < DP_MAXR; ++q) {
+        const int64_t j = j0 + q * DP_THREADS + tid;
+        raw[q] = (q < nr && j < Tk) ? topk_idx[j] : -1;
+    }
+#pragma unroll
+    for (int q = 0; q < DP_MAXR; ++q)
+        if (q < nr) tkc[q * DP_THREADS + tid] = raw[q];
+    if (tid < DP_EMAX) running[tid] = 0;
+    __syncthreads();
+    // assignment j's expert, or -1 when it is not a valid choice
+    int ej[DP_MAXR];
+#pragma unroll
+    for (int q = 0; q < DP_MAXR; ++q) {
+        const int64_t j = j0 + q * DP_THREADS + tid;
+        ej[q] = (q < nr && j < Tk) ? valid_expert(raw[q], j, j0, k, E, tkc, topk_idx) : -1;
+    }
     if (nchunks == 1) {
         // a single chunk counts its own assignments (no histogram kernel ran)
-        if (tid < DP_EMAX) running[tid] = 0;
+#pragma unroll
+        for (int q = 0; q < DP_MAXR; ++q)
+            if (ej[q] >= 0) atomicAdd(&running[ej[q]], 1);
         __syncthreads();
-        for (int64_t j = tid; j < Tk; j += DP_THREADS) {
-            const int e = assignment_expert(topk_idx, j, k, E);
-            if (e >= 0) atomicAdd(&running[e], 1);
-        }
-        __syncthreads();
+        if (tid < E) tot = running[tid];
     }
     if (tid < E) {
-        int before = 0, tot = 0;
-        if (nchunks == 1) {
-            tot = running[tid];
-        } else {
-            // 32 histogram loads in flight at a time
-#pragma unroll 32
-            for (int c = 0; c < nchunks; ++c) {
-                const int v = chunk_counts[(int64_t)c * E + tid];
-                before += (c < chunk) ? v : 0;
-                tot += v;
-            }
-        }
         running[tid] = before;
         keptc[tid] = (C >= 0 && tot > C) ? (int)C : tot;
         if (chunk == 0) {
@@ -158,14 +193,15 @@ __global__ __launch_bounds__(DP_THREADS) void dispatch_rank_kernel(
     __syncthreads();
 
     const unsigned long long lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    const int64_t j0 = (int64_t)chunk * chunk_len;
-    for (int round = 0; round < chunk_len / DP_THREADS; ++round) {
+#pragma unroll
+    for (int round = 0; round < DP_MAXR; ++round) {
+        if (round >= nr) break;
         for (int i = tid; i < (DP_THREADS / 64) * DP_EMAX; i += DP_THREADS) (&wcnt[0][0])[i] = 0;
         __syncthreads();
         const int64_t j = j0 + round * DP_THREADS + tid;
         const bool inrange = j < Tk;
-        const int ej = inrange ? assignment_expert(topk_idx, j, k, E) : -1;
-        const bool valid = ej >= 0;
+        const int e_j = ej[round];
+        const bool valid = e_j >= 0;
         // group the wave's lanes by expert, in lane (= assignment) order
         bool act = valid;
         int rank_w = 0;
@@ -173,8 +209,8 @@ __global__ __launch_bounds__(DP_THREADS) void dispatch_rank_kernel(
             const unsigned long long am = __ballot(act);
             if (am == 0ull) break;
             const int leader = __ffsll((long long)am) - 1;
-            const int e0 = __builtin_amdgcn_readlane(ej, leader);  // leader is wave-uniform
-            const bool m = act && ej == e0;
+            const int e0 = __builtin_amdgcn_readlane(e_j, leader);  // leader is wave-uniform
+            const bool m = act && e_j == e0;
             const unsigned long long mm = __ballot(m);
             if (m) {
                 rank_w = __popcll(mm & lt_mask);
@@ -184,10 +220,10 @@ __global__ __launch_bounds__(DP_THREADS) void dispatch_rank_kernel(
         }
         __syncthreads();
         if (valid) {
-            int rank = running[ej] + rank_w;
-            for (int v = 0; v < w; ++v) rank += wcnt[v][ej];
+            int rank = running[e_j] + rank_w;
+            for (int v = 0; v < w; ++v) rank += wcnt[v][e_j];
             if (C < 0 || rank < C) {
-                const int row = off[ej] + rank;
+                const int row = off[e_j] + rank;
                 row_of_slot[j] = row;
                 token_of_row[row] = (int)(j / k);
                 dropped[j] = 0;

@@ -64,6 +64,10 @@ __device__ __forceinline__ uint32_t ord_f32(float f) {
     uint32_t u = (f == 0.f) ? 0u : __float_as_uint(f);
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
+// Its inverse (a zero comes back as +0, which no use below tells from -0).
+__device__ __forceinline__ float unord_f32(uint32_t o) {
+    return __uint_as_float((o & 0x80000000u) ? (o & 0x7fffffffu) : ~o);
+}
 
 // Reductions within groups of G = 8 or 16 lanes (one token per group) on
 // the VALU's cross-lane moves (DPP) instead of LDS permutes: swap
@@ -156,7 +160,7 @@ __device__ void softmax_topk_grouped(const float (*hl)[RT_EMAX + 1], int t0, int
             int bi = (int)(0xffffffffu - (uint32_t)(best & 0xffffffffull));
             bi = bi < 0 ? 0 : bi;  // only for a token past T (its key is 0)
             if (bi == e) key = 0ull;
-            const float hb = vt ? hl[r][bi] : 0.f;
+            const float hb = vt ? unord_f32((uint32_t)(best >> 32)) : 0.f;   // the key holds the logit
             if (sl == 0) {
                 h_top = hb;
                 if (vt && e == 0) topchg[r] = bi;
@@ -199,7 +203,8 @@ __device__ void softmax_topk_grouped(const float (*hl)[RT_EMAX + 1], int t0, int
     }
 }
 
-// softmax_topk_block for 16 < E <= 16 V: one token per row of 16 lanes,
+// softmax_topk_block for 16 < E <= 16 V: one token per row of 16 lanes
+// (waves past the first NW of the block only join its barriers),
 // lane c of a row holding experts c, c + 16, ..., c + 16 (V - 1), so a wave
 // serves 4 tokens at once and every reduction stays within a row (DPP
 // moves only: no readlane, no LDS).  Each lane first reduces its V values
@@ -221,7 +226,7 @@ __device__ __forceinline__ void softmax_topk_rows(const float (*hl)[RT_EMAX + 1]
     float psum[V], lsum = 0.f;
 #pragma unroll
     for (int v = 0; v < V; ++v) psum[v] = 0.f;
-    for (int r0 = w * 4; r0 < TILE; r0 += NW * 4) {
+    for (int r0 = w * 4; w < NW && r0 < TILE; r0 += NW * 4) {
         if (t0 + r0 >= T) break;   // uniform in the wave
         const int r = r0 + g, t = t0 + r;
         const bool vt = r < TILE && t < T;
@@ -273,7 +278,8 @@ __device__ __forceinline__ void softmax_topk_rows(const float (*hl)[RT_EMAX + 1]
 #pragma unroll
             for (int v = 0; v < V; ++v)
                 if (c + 16 * v == bi) key[v] = 0ull;
-            const float hb = vt ? hl[r][bi] : 0.f;   // one address per row
+            // the chosen logit is in the key itself (no LDS read on the chain)
+            const float hb = vt ? unord_f32((uint32_t)(b >> 32)) : 0.f;
             if (s == 0) {
                 h_top = hb;
                 if (c == 0 && vt) topcr[r] = bi;
@@ -301,9 +307,11 @@ __device__ __forceinline__ void softmax_topk_rows(const float (*hl)[RT_EMAX + 1]
             }
         }
     }
+    if (w < NW) {
 #pragma unroll
-    for (int v = 0; v < V; ++v) pwr[w][v][lane] = psum[v];
-    if (c == 0) lsr[w][g] = lsum;
+        for (int v = 0; v < V; ++v) pwr[w][v][lane] = psum[v];
+        if (c == 0) lsr[w][g] = lsum;
+    }
     __syncthreads();
     if (tid < E) {
         const int v = tid >> 4, cc = tid & 15;
@@ -329,13 +337,14 @@ __device__ __forceinline__ void softmax_topk_rows(const float (*hl)[RT_EMAX + 1]
 
 // The per-token epilogue over a block's logits tile hl[TILE][.]
 // (already synchronised), NW waves, wave w taking tokens w, w + NW, ...
-// Every thread of the block must call it.  Partials of tile pslot out of
+// Every thread of the block must call it.  Inlined into its kernel: as a
+// call it would run with a stack and without the caller's constants.  Partials of tile pslot out of
 // pslots (by default the block's index in the grid): part_P[e * pslots + b]
 // = sum of p_e over the tile's tokens (waves in order), part_P[(E + e) *
 // pslots + b] = how many of them have e as their top choice (an exact small
 // integer in a float), part_lse2[b].
 template <int TILE, int NW = 4>
-__device__ void softmax_topk_block(const float (*hl)[RT_EMAX + 1], int t0, int T, int E, int k,
+__device__ __forceinline__ void softmax_topk_block(const float (*hl)[RT_EMAX + 1], int t0, int T, int E, int k,
                                    int gate_switch, int32_t *__restrict__ topk_idx,
                                    float *__restrict__ gates, float *__restrict__ part_P,
                                    float *__restrict__ part_lse2, int *topk_sh = nullptr,
@@ -417,6 +426,16 @@ __global__ __launch_bounds__(RT_THREADS) void route_f32_kernel(
         }
         __syncthreads();
     }
+    // every bias and noise load is issued before the first add (clamped
+    // indices): one memory round trip
+    float bv[4], nz[4][4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int ec = min(eg + 32 * j, E - 1);
+        bv[j] = bias ? bias[ec] : 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) nz[i][j] = noise ? noise[(int64_t)min(t0 + tg * 4 + i, T - 1) * E + ec] : 0.f;
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         int r = tg * 4 + i, t = t0 + r;
@@ -425,8 +444,8 @@ __global__ __launch_bounds__(RT_THREADS) void route_f32_kernel(
             int e = eg + 32 * j;
             float h = acc[i][j];
             if (e < E && t < T) {
-                if (bias) h += bias[e];
-                if (noise) h += noise[(int64_t)t * E + e];
+                if (bias) h += bv[j];
+                if (noise) h += nz[i][j];
             }
             hl[r][e] = h;
         }
@@ -772,6 +791,20 @@ __global__ __launch_bounds__(320) void route_fused_kernel(
     // accumulator r of lane l (compute waves): token i * 16 + 4 g + r, expert
     // (wave * NG + gi) * 16 + lr
     if (wave < 4) {
+        // every bias and noise load of the lane is issued before the first
+        // add (clamped indices, so none is conditional): one memory round
+        // trip instead of one per logit
+        float bv[NG], nz[TM][NG][4];
+#pragma unroll
+        for (int gi = 0; gi < NG; ++gi) {
+            const int ec = min((wave * NG + gi) * 16 + lr, E - 1);
+            bv[gi] = bias ? bias[ec] : 0.f;
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    nz[i][gi][r] = noise ? noise[(int64_t)min(t0 + i * 16 + 4 * g + r, T - 1) * E + ec] : 0.f;
+        }
 #pragma unroll
         for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -782,15 +815,18 @@ __global__ __launch_bounds__(320) void route_fused_kernel(
                     const int e = (wave * NG + gi) * 16 + lr;
                     float v = acc[i][gi][r];
                     if (e < E && t < T) {
-                        if (bias) v += bias[e];
-                        if (noise) v += noise[(int64_t)t * E + e];
+                        if (bias) v += bv[gi];
+                        if (noise) v += nz[i][gi][r];
                     }
                     hl[row][e] = v;
                 }
     }
     __syncthreads();
-    softmax_topk_block<BT, 5>(hl, t0, T, E, k, gate_switch, topk_idx, gates, part_P, part_lse2, nullptr,
-                              nullptr, nullptr, tile, gridDim.x);
+    // E_PAD / 16 logits per lane cover every E of this padding (E > E_PAD / 2).
+    // Waves 0..3, one per SIMD, take the tokens; the loader wave would
+    // share a SIMD with wave 0.
+    softmax_topk_rows<E_PAD / 16, BT, 4>(hl, t0, T, E, k, gate_switch, topk_idx, gates, part_P, part_lse2,
+                                         nullptr, nullptr, nullptr, tile, gridDim.x);
 #endif
 }
 
@@ -830,14 +866,23 @@ __global__ __launch_bounds__(RT_THREADS) void route_epilogue_kernel(
                 if (i < npairs) h[q] += ps[off[q]];
             }
         }
+    // every bias and noise load is issued before the first add (clamped
+    // indices): one memory round trip
+    float bv[MAXQ], nz[MAXQ];
+#pragma unroll
+    for (int q = 0; q < MAXQ; ++q) {
+        const int i = min(tid + q * RT_THREADS, npairs - 1);
+        bv[q] = bias ? bias[i % E] : 0.f;
+        nz[q] = noise ? noise[base + i] : 0.f;
+    }
 #pragma unroll
     for (int q = 0; q < MAXQ; ++q) {
         const int i = tid + q * RT_THREADS;
         if (i < npairs) {
             const int r = i / E, e = i - r * E;
             float v = h[q];
-            if (bias) v += bias[e];
-            if (noise) v += noise[base + i];
+            if (bias) v += bv[q];
+            if (noise) v += nz[q];
             hl[r][e] = v;
         }
     }
@@ -886,6 +931,9 @@ __global__ __launch_bounds__(RS_THREADS) void route_small_kernel(
         // issued before the first add, so the group costs one memory round
         // trip rather than one per slice
         constexpr int G = 32;
+        const int t = i / E, e = i - t * E;
+        // bias and noise are loaded with the first group of slices
+        const float bv = bias ? bias[e] : 0.f, nz = noise ? noise[i] : 0.f;
         float v = 0.f;
         for (int s0 = 0; s0 < nsplit; s0 += G) {
             float buf[G];
@@ -896,9 +944,8 @@ __global__ __launch_bounds__(RS_THREADS) void route_small_kernel(
             for (int u = 0; u < G; ++u)
                 if (s0 + u < nsplit) v += buf[u];
         }
-        const int t = i / E, e = i - t * E;
-        if (bias) v += bias[e];
-        if (noise) v += noise[i];
+        if (bias) v += bv;
+        if (noise) v += nz;
         hl[t][e] = v;
     }
     if (tid < RT_EMAX) {

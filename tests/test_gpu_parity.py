@@ -266,13 +266,15 @@ def test_workspace_too_small_raises_before_launch():
     assert ei.value.code == -4
 
 
-@pytest.mark.parametrize("T,E,k,cf", [(100, 5, 2, 0.5), (300, 6, 2, 0.8), (3000, 16, 3, 1.0)])
+@pytest.mark.parametrize("T,E,k,cf", [(100, 5, 2, 0.5), (300, 6, 2, 0.8), (3000, 16, 3, 1.0),
+                                      (12000, 16, 3, 1.0), (9000, 128, 4, 1.25)])
 def test_dispatch_drops_invalid_indices(T, E, k, cf):
     """moe_dispatch on caller indices that include entries outside [0, E)
     and experts repeated within a token: those entries count nowhere and
     come back dropped; the valid ones are ranked in token order against the
-    capacity as usual (checked against a plain sequential fill).  The second
-    shape spans several dispatch chunks."""
+    capacity as usual (checked against a plain sequential fill).  The larger
+    shapes span several dispatch chunks, of 256 and of 1024 assignments; with
+    k = 3 some tokens begin in one chunk and end in the next."""
     rng = np.random.default_rng(7)
     idx = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
     bad = rng.random((T, k)) < 0.1
