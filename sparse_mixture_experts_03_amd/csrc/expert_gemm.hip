@@ -272,7 +272,9 @@ constexpr int BIG_BM = 256;
 // starting cost lies in [x C / 8, (x+1) C / 8) of the total cost C, and
 // its blocks (slot b / 8) take the run's tiles in order; so every XCD gets
 // the same amount of work and the row tiles sharing a weight panel run on
-// one XCD at the same time.  In the plain (non-SwiGLU) kernel, the last
+// one XCD at the same time.  When all tiles fit in one round of the CUs
+// (at most 8 x CUs-per-XCD of them), the runs split the list by count
+// instead, so that no XCD has more tiles than CUs.  In the plain (non-SwiGLU) kernel, the last
 // partial round of a run, when it would leave at least half of the XCD's
 // CUs idle, is done as half-width pieces (two per tile, 128 columns each).
 // Each wave computes the schedule by itself,
@@ -294,8 +296,8 @@ __device__ __forceinline__ int wave_incl_scan(int v, int lane) {
 }
 
 __device__ __forceinline__ bool find_tile_balanced(const int32_t *__restrict__ offsets, int E, int ntn,
-                                                   int nsplit, int cpx, int &e, int &row0, int &nrows,
-                                                   int &ntile, int &split, int &half) {
+                                                   int nsplit, int cpx, bool halves_ok, int &e, int &row0,
+                                                   int &nrows, int &ntile, int &split, int &half) {
     const int lane = threadIdx.x & 63;
     // experts lane and lane + 64; every value taken out of a lane is read
     // with readlane at a uniform lane, so it lands in a scalar register
@@ -340,13 +342,24 @@ __device__ __forceinline__ bool find_tile_balanced(const int32_t *__restrict__ o
         return sp * Ts + te0 + idx;
     };
     const int x = blockIdx.x % NUM_XCD;
-    const int start = first_at(C * x / NUM_XCD);
-    const int end = x == NUM_XCD - 1 ? Ts * nsplit : first_at(C * (x + 1) / NUM_XCD);
+    const int ntot = Ts * nsplit;
+    int start, end;
+    if (cpx > 0 && ntot <= NUM_XCD * cpx) {
+        // one round: every CU takes at most one tile, so the XCDs split the
+        // list by count and the slowest tile sets the time (a split by cost
+        // would give the XCDs of cheap tiles more tiles than CUs: a second
+        // round there)
+        start = ntot * x / NUM_XCD;
+        end = ntot * (x + 1) / NUM_XCD;
+    } else {
+        start = first_at(C * x / NUM_XCD);
+        end = x == NUM_XCD - 1 ? ntot : first_at(C * (x + 1) / NUM_XCD);
+    }
     // The run's last partial round (r tiles on the XCD's cpx CUs): when it
     // would leave at least half of them idle, its tiles are done as two
     // half-width pieces each (half = 1, 2), so the round ends sooner.
     const int n = end - start, r = cpx > 0 ? n % cpx : 0;
-    const bool halves = cpx > 0 && r > 0 && 2 * r <= cpx;
+    const bool halves = halves_ok && cpx > 0 && r > 0 && 2 * r <= cpx;
     const int slot = (int)(blockIdx.x / NUM_XCD);
     int L;
     half = 0;
@@ -656,7 +669,8 @@ __global__ __launch_bounds__(256) void gemm_bf16_big_kernel(
             return;
         }
     } else {
-        if (!find_tile_balanced(offsets, E, (N + BN - 1) / BN, nsplit, cpx, e, row0, nrows, ntile, split, half))
+        if (!find_tile_balanced(offsets, E, (N + BN - 1) / BN, nsplit, cpx, !DUAL, e, row0, nrows, ntile, split,
+                                half))
             return;
         // K split: this tile covers stages [split * KT, (split + 1) * KT) and
         // the second half writes its partial sums to C_split
@@ -992,7 +1006,7 @@ hipError_t launch_big(const Shape &s, const void *A, const int32_t *a_rows, cons
     const unsigned blocks = run * NUM_XCD;
     launch_kernel((gemm_bf16_big_kernel<DUAL, ACT, OUT_BF16>), dim3(blocks), dim3(256), 0, st,
                        (const uint16_t *)A, a_rows, offsets, s.E, (const uint16_t *)B1,
-                       (const uint16_t *)B3, C, N, K, nsplit, C_split, DUAL ? 0 : cpx);
+                       (const uint16_t *)B3, C, N, K, nsplit, C_split, cpx);
     return hipGetLastError();
 }
 
