@@ -543,6 +543,54 @@ def run_backward(w, steps, warmup, seed=0):
             "flops_per_step": flops}
 
 
+def gather_object(w, launches=20, seed=0):
+    """The gather of the staged moe_dispatch (the copy of the kept rows of x
+    into expert order), which moe_forward folds into the up projection's
+    loads: its launch timed by the stage-event hook (the launch's own start
+    and end timestamps), against 8 TB/s over the kept rows read and
+    written plus their row indices."""
+    import torch
+    from sparse_mixture_experts_03_amd import binding as B
+    from sparse_mixture_experts_03_amd import synth
+
+    wt = synth.make_weights(w, seed, experts=1)
+    tk = synth.make_tokens(w, seed, 0)
+    desc = B.desc_for(w)
+    x = B.to_device(tk["x"], w.dtype)
+    out = B.alloc_outputs(desc)
+    ws = B.workspace(desc)
+    B.moe_route(desc, x, B.to_device(wt["Wr"], "f32"), B.to_device(wt["bias"], "f32"),
+                B.to_device(tk["noise"], "f32"), out["topk_idx"], out["gates"], out["stats"], ws)
+    x_perm = torch.empty((w.T * w.k, w.d), dtype=x.dtype, device=x.device)
+    ev = HipEvents()
+
+    def disp(events=None):
+        desc.stage_events = ctypes.cast(events, ctypes.POINTER(ctypes.c_void_p)) if events else None
+        desc.n_stage_events = 2 if events else 0
+        B.moe_dispatch(desc, x, out["topk_idx"], out["routed_counts"], out["kept_counts"], out["offsets"],
+                       out["row_of_slot"], out["token_of_row"], out["dropped"], x_perm, ws)
+
+    for _ in range(3):
+        disp()
+    sets = [ev.create(2) for _ in range(launches)]
+    torch.cuda.synchronize()
+    for es in sets:
+        disp(es)
+    torch.cuda.synchronize()
+    ms = np.array([ev.elapsed_ms(es[0], es[1]) for es in sets])
+    for es in sets:
+        ev.destroy(es)
+    desc.stage_events, desc.n_stage_events = None, 0
+    n_kept = int(out["kept_counts"].sum().item())
+    eb = 2 if w.dtype == "bf16" else 4
+    nbytes = 2 * n_kept * w.d * eb + n_kept * 4
+    gbs = nbytes / (float(ms.mean()) * 1e-3) / 1e9
+    return {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": round(gbs / PEAK_HBM_GBS, 4), "algorithmic_per_launch": nbytes,
+            "mean_launch_ms": round(float(ms.mean()), 4), "launches": launches,
+            "entry_point": "moe_dispatch (staged path)"}
+
+
 def combine_object(w, res):
     """The combine's HBM rate over its event-timed launches: algorithmic bytes
     = kept rows of y_perm (fp32) + gates and row indices + y (act dtype),
@@ -749,8 +797,9 @@ def main():
     line["step_ms_median_min_p90"] = cold["ms_per_step_median_min_p90"]
     line["step_ms_mode"] = "each step timed alone by its own events, last-level cache flushed before it"
     line["combine"] = combine_object(w, res)
-    line["gather"] = ("folded into the expert up-projection's loads in moe_forward (rows of x read "
-                      "through token_of_row): its bytes are part of that kernel's traffic")
+    line["gather"] = gather_object(w) if w.n_shared == 0 and not w.residual else None
+    line["gather_in_forward"] = ("folded into the expert up-projection's loads (rows of x read through "
+                                 "token_of_row): its bytes are part of that kernel's traffic")
     if w.n_shared > 0:
         # the shared stage: the row map, then the shared experts' up and
         # down projections (dense GEMMs of all T tokens), against the MFMA peak

@@ -124,7 +124,8 @@ extern "C" {
  * moe_forward the gather is folded into expert-up (its rows of x are read
  * through token_of_row), so that stage is empty, and the statistics are
  * finished by extra blocks of the dispatch launch, so route-finalize is
- * empty as well.
+ * empty as well.  moe_dispatch takes events 0 and 1, when given, as the
+ * start and end timestamps of its gather launch.
  * The other entry points ignore it.
  */
 typedef struct moe_desc {

@@ -301,14 +301,14 @@ hipError_t launch_gather(const Shape &s, const void *x, const int32_t *token_of_
     if (blocks > 8192) blocks = 8192;
     if (blocks < 1) blocks = 1;
     if (row_bytes % 16 == 0)
-        hipLaunchKernelGGL(gather_kernel<uint4>, dim3((unsigned)blocks), dim3(256), 0, st,
-                           (const char *)x, token_of_row, offsets, s.E, row_bytes, (char *)x_perm);
+        launch_kernel(gather_kernel<uint4>, dim3((unsigned)blocks), dim3(256), 0, st, (const char *)x,
+                      token_of_row, offsets, s.E, row_bytes, (char *)x_perm);
     else if (row_bytes % 4 == 0)
-        hipLaunchKernelGGL(gather_kernel<uint32_t>, dim3((unsigned)blocks), dim3(256), 0, st,
-                           (const char *)x, token_of_row, offsets, s.E, row_bytes, (char *)x_perm);
+        launch_kernel(gather_kernel<uint32_t>, dim3((unsigned)blocks), dim3(256), 0, st, (const char *)x,
+                      token_of_row, offsets, s.E, row_bytes, (char *)x_perm);
     else
-        hipLaunchKernelGGL(gather_kernel<uint16_t>, dim3((unsigned)blocks), dim3(256), 0, st,
-                           (const char *)x, token_of_row, offsets, s.E, row_bytes, (char *)x_perm);
+        launch_kernel(gather_kernel<uint16_t>, dim3((unsigned)blocks), dim3(256), 0, st, (const char *)x,
+                      token_of_row, offsets, s.E, row_bytes, (char *)x_perm);
     return hipGetLastError();
 }
 

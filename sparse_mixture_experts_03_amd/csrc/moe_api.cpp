@@ -263,6 +263,9 @@ int moe_dispatch(const moe_desc *desc, const void *x, const int32_t *topk_idx,
     hipStream_t st = (hipStream_t)stream;
     MOE_TRY(moe::launch_dispatch(s, topk_idx, routed_counts, kept_counts, offsets, row_of_slot,
                                  token_of_row, dropped, at<int32_t>(ws, L.chunk_counts), st));
+    // stage events 0 and 1, when given, are the gather launch's start and end
+    StageEvents ev{desc->stage_events, desc->n_stage_events};
+    ev.around_next_launch();
     MOE_TRY(moe::launch_gather(s, x, token_of_row, offsets, x_perm, st));
     return MOE_OK;
 }
