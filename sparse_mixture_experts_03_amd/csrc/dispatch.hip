@@ -95,6 +95,8 @@ struct StatsArgs {
     float *stats;
     double *fP;
     unsigned *arrivals;
+    unsigned *zero_ctr;   // words cleared by block 0 (the GEMMs' tile counters)
+    int n_zero;
 };
 
 __global__ __launch_bounds__(DP_THREADS) void dispatch_rank_kernel(
@@ -116,6 +118,7 @@ __global__ __launch_bounds__(DP_THREADS) void dispatch_rank_kernel(
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int chunk = blockIdx.x;
     const int nr = chunk_len / DP_THREADS;      // rounds of 256 assignments
+    if (chunk == 0 && tid < sa.n_zero) sa.zero_ctr[tid] = 0u;
     const int64_t j0 = (int64_t)chunk * chunk_len;
 
     // One memory round trip for everything the ranking reads: the chunk
@@ -276,21 +279,37 @@ int dispatch_chunks(const Shape &s) {
 hipError_t launch_dispatch(const Shape &s, const int32_t *topk_idx, int32_t *routed,
                            int32_t *kept, int32_t *offsets, int32_t *row_of_slot,
                            int32_t *token_of_row, uint8_t *dropped, int32_t *chunk_counts,
-                           hipStream_t st, const RouteStatsIn *stats) {
+                           hipStream_t st, const RouteStatsIn *stats, unsigned *zero_ctr, int n_zero) {
     const int nch = dispatch_chunks(s);
     const int chunk = dispatch_chunk(s);
     if (nch > 1)
         hipLaunchKernelGGL(dispatch_count_kernel, dim3(nch), dim3(DP_THREADS), 0, st, topk_idx,
                            s.Tk(), s.k, s.E, chunk, chunk_counts);
+    if (n_zero > DP_THREADS) return hipErrorInvalidValue;
     StatsArgs sa{};
     unsigned blocks = (unsigned)nch;
     if (stats) {
-        sa = StatsArgs{stats->part_P, stats->part_lse2, s.T, stats->nblk, stats->stats, stats->fP, stats->arrivals};
+        sa = StatsArgs{stats->part_P, stats->part_lse2, s.T, stats->nblk, stats->stats, stats->fP, stats->arrivals,
+                       nullptr, 0};
         blocks += (unsigned)s.E + 1;
     }
+    sa.zero_ctr = zero_ctr;
+    sa.n_zero = zero_ctr ? n_zero : 0;
     hipLaunchKernelGGL(dispatch_rank_kernel, dim3(blocks), dim3(DP_THREADS), 0, st, topk_idx, s.Tk(),
                        s.k, s.E, s.C, chunk, nch, (const int32_t *)chunk_counts, routed, kept,
                        offsets, row_of_slot, token_of_row, dropped, sa);
+    return hipGetLastError();
+}
+
+namespace {
+__global__ __launch_bounds__(256) void zero_u32_kernel(unsigned *__restrict__ p, int n) {
+    for (int i = threadIdx.x; i < n; i += 256) p[i] = 0u;
+}
+}  // namespace
+
+hipError_t launch_zero_u32(unsigned *p, int n, hipStream_t st) {
+    if (n <= 0) return hipSuccess;
+    hipLaunchKernelGGL(zero_u32_kernel, dim3(1), dim3(256), 0, st, p, n);
     return hipGetLastError();
 }
 

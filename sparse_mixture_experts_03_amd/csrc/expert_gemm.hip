@@ -296,8 +296,9 @@ __device__ __forceinline__ int wave_incl_scan(int v, int lane) {
 }
 
 __device__ __forceinline__ bool find_tile_balanced(const int32_t *__restrict__ offsets, int E, int ntn,
-                                                   int nsplit, int cpx, bool halves_ok, int &e, int &row0,
-                                                   int &nrows, int &ntile, int &split, int &half) {
+                                                   int nsplit, int cpx, bool halves_ok, int slot, int &ntot_out,
+                                                   int &e, int &row0, int &nrows, int &ntile, int &split,
+                                                   int &half) {
     const int lane = threadIdx.x & 63;
     // experts lane and lane + 64; every value taken out of a lane is read
     // with readlane at a uniform lane, so it lands in a scalar register
@@ -343,6 +344,7 @@ __device__ __forceinline__ bool find_tile_balanced(const int32_t *__restrict__ o
     };
     const int x = blockIdx.x % NUM_XCD;
     const int ntot = Ts * nsplit;
+    ntot_out = ntot;
     int start, end;
     if (cpx > 0 && ntot <= NUM_XCD * cpx) {
         // one round: every CU takes at most one tile, so the XCDs split the
@@ -360,7 +362,6 @@ __device__ __forceinline__ bool find_tile_balanced(const int32_t *__restrict__ o
     // half-width pieces each (half = 1, 2), so the round ends sooner.
     const int n = end - start, r = cpx > 0 ? n % cpx : 0;
     const bool halves = halves_ok && cpx > 0 && r > 0 && 2 * r <= cpx;
-    const int slot = (int)(blockIdx.x / NUM_XCD);
     int L;
     half = 0;
     if (!halves || slot < n - r) {
@@ -408,7 +409,12 @@ __device__ __forceinline__ void big_tile(char *lds, const uint16_t *__restrict__
     constexpr int NQ = NQA + NQB;
     constexpr int NMF = MI * NJ;           // MFMAs per wave per 16-wide k step
     constexpr int NRD = MI + NJ;           // fragment reads per k step
-    const int tid = threadIdx.x, lane = tid & 63;
+    // the thread index passed through an empty asm: what is derived from it
+    // is computed per tile, not hoisted out of a caller's loop over tiles
+    // (where it would stay live across the stage loop and spill)
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));
+    const int lane = tid & 63;
     // the wave index as a scalar, so LDS destinations (M0) and operand bases
     // are computed on the scalar unit
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -629,6 +635,38 @@ __device__ __forceinline__ void big_tile(char *lds, const uint16_t *__restrict__
 #endif
 }
 
+// One tile (or half-width piece, half = 1, 2) of the 256-row kernel, by its
+// number of 64-row slabs.
+template <bool DUAL, int ACT, bool OUT_BF16>
+__device__ __forceinline__ void big_tile_any(char *lds, const uint16_t *__restrict__ A,
+                                             const int32_t *__restrict__ a_rows, const uint16_t *__restrict__ B1,
+                                             const uint16_t *__restrict__ B3, void *__restrict__ C, int N, int K,
+                                             int e, int row0, int nrows, int ntile, int half, int KT, int kbeg) {
+    constexpr int BN = DUAL ? 128 : 256;
+    const int mi = (nrows + 63) >> 6;   // 64-row slabs this tile needs
+    if constexpr (!DUAL) if (half) {
+        // half-width piece: columns [ntile * BN + (half - 1) * BN / 2, + BN / 2)
+        const int n0 = ntile * BN + (half - 1) * (BN / 2);
+        if (mi == 4)
+            big_tile<4, 2, DUAL, ACT, OUT_BF16>(lds, A, a_rows, B1, B3, C, N, K, e, row0, nrows, n0, KT, kbeg);
+        else if (mi == 3)
+            big_tile<3, 2, DUAL, ACT, OUT_BF16>(lds, A, a_rows, B1, B3, C, N, K, e, row0, nrows, n0, KT, kbeg);
+        else if (mi == 2)
+            big_tile<2, 2, DUAL, ACT, OUT_BF16>(lds, A, a_rows, B1, B3, C, N, K, e, row0, nrows, n0, KT, kbeg);
+        else
+            big_tile<1, 2, DUAL, ACT, OUT_BF16>(lds, A, a_rows, B1, B3, C, N, K, e, row0, nrows, n0, KT, kbeg);
+        return;
+    }
+    if (mi == 4)
+        big_tile<4, 4, DUAL, ACT, OUT_BF16>(lds, A, a_rows, B1, B3, C, N, K, e, row0, nrows, ntile * BN, KT, kbeg);
+    else if (mi == 3)
+        big_tile<3, 4, DUAL, ACT, OUT_BF16>(lds, A, a_rows, B1, B3, C, N, K, e, row0, nrows, ntile * BN, KT, kbeg);
+    else if (mi == 2)
+        big_tile<2, 4, DUAL, ACT, OUT_BF16>(lds, A, a_rows, B1, B3, C, N, K, e, row0, nrows, ntile * BN, KT, kbeg);
+    else
+        big_tile<1, 4, DUAL, ACT, OUT_BF16>(lds, A, a_rows, B1, B3, C, N, K, e, row0, nrows, ntile * BN, KT, kbeg);
+}
+
 // WG: the weight-gradient form (launch_wgrad_big).  C_e = P Q^T for each
 // expert e over its k range [offsets[e], offsets[e+1]) (multiples of 64:
 // the zero-padded transposed activations), with A = P [E][K], B1 = Q [N][K]
@@ -642,7 +680,7 @@ __global__ __launch_bounds__(256) void gemm_bf16_big_kernel(
     const uint16_t *__restrict__ A, const int32_t *__restrict__ a_rows,
     const int32_t *__restrict__ offsets, int E, const uint16_t *__restrict__ B1,
     const uint16_t *__restrict__ B3, void *__restrict__ C_, int N, int K, int nsplit,
-    void *__restrict__ C_split, int cpx) {
+    void *__restrict__ C_split, int cpx, unsigned *__restrict__ tctr) {
     constexpr int BN = DUAL ? 128 : 256;
     // A stages 0, 1 at 0 and 32 KB; weight stages 0..2 at 64, 96, 128 KB
     __shared__ __attribute__((aligned(1024))) char lds[5 * 256 * 128];
@@ -669,37 +707,40 @@ __global__ __launch_bounds__(256) void gemm_bf16_big_kernel(
             return;
         }
     } else {
-        if (!find_tile_balanced(offsets, E, (N + BN - 1) / BN, nsplit, cpx, !DUAL, e, row0, nrows, ntile, split,
-                                half))
-            return;
-        // K split: this tile covers stages [split * KT, (split + 1) * KT) and
-        // the second half writes its partial sums to C_split
-        C = split ? C_split : C_;
-        KT = K / 64 / nsplit;
-        kbeg = split * KT * 64;
-    }
-    const int mi = (nrows + 63) >> 6;   // 64-row slabs this tile needs
-    if constexpr (!DUAL) if (half) {
-        // half-width piece: columns [ntile * BN + (half - 1) * BN / 2, + BN / 2)
-        const int n0 = ntile * BN + (half - 1) * (BN / 2);
-        if (mi == 4)
-            big_tile<4, 2, DUAL, ACT, OUT_BF16>(lds, A, a_rows, B1, B3, C, N, K, e, row0, nrows, n0, KT, kbeg);
-        else if (mi == 3)
-            big_tile<3, 2, DUAL, ACT, OUT_BF16>(lds, A, a_rows, B1, B3, C, N, K, e, row0, nrows, n0, KT, kbeg);
-        else if (mi == 2)
-            big_tile<2, 2, DUAL, ACT, OUT_BF16>(lds, A, a_rows, B1, B3, C, N, K, e, row0, nrows, n0, KT, kbeg);
-        else
-            big_tile<1, 2, DUAL, ACT, OUT_BF16>(lds, A, a_rows, B1, B3, C, N, K, e, row0, nrows, n0, KT, kbeg);
+        // Slot s of XCD x = b % 8 is block b's first tile, s = b / 8.  With
+        // tile counters (tctr: one per XCD, zero at launch), the grid holds
+        // at most one block per CU and the blocks stay resident: after its
+        // first slot a block takes slot P + t, P blocks per XCD, t the
+        // ticket it draws from its XCD's counter, asking for it when it
+        // starts a tile so that the answer arrives during the tile.  Tiles
+        // are thus handed out in list order to the block that frees up, as
+        // the hardware hands out blocks, without a block launch per tile or
+        // blocks left to launch after the work.  Which block computes a tile
+        // does not change its result.  Without counters every block takes
+        // its one slot.
+        const int x = (int)(blockIdx.x % NUM_XCD), P = (int)(gridDim.x / NUM_XCD);
+        int slot = (int)(blockIdx.x / NUM_XCD), ntot = 0;
+        while (find_tile_balanced(offsets, E, (N + BN - 1) / BN, nsplit, cpx, !DUAL, slot, ntot, e, row0, nrows,
+                                  ntile, split, half)) {
+            unsigned next = 0;
+            if (tctr && threadIdx.x == 0) next = (unsigned)P + atomicAdd(tctr + x, 1u);
+            C = split ? C_split : C_;
+            KT = K / 64 / nsplit;   // K split: stages [split * KT, (split + 1) * KT), the second
+            kbeg = split * KT * 64;  // half writing its partial sums to C_split
+            big_tile_any<DUAL, ACT, OUT_BF16>(lds, A, a_rows, B1, B3, C, N, K, e, row0, nrows, ntile, half, KT,
+                                              kbeg);
+            if (!tctr) return;
+            // the LDS stages are free once every wave is past its last
+            // stage: word 0 carries the ticket to the block
+            __syncthreads();
+            if (threadIdx.x == 0) *(volatile unsigned *)lds = next;
+            __syncthreads();
+            slot = __builtin_amdgcn_readfirstlane((int)*(volatile unsigned *)lds);   // uniform: a scalar
+            __syncthreads();   // read before the next tile's loads overwrite it
+        }
         return;
     }
-    if (mi == 4)
-        big_tile<4, 4, DUAL, ACT, OUT_BF16>(lds, A, a_rows, B1, B3, C, N, K, e, row0, nrows, ntile * BN, KT, kbeg);
-    else if (mi == 3)
-        big_tile<3, 4, DUAL, ACT, OUT_BF16>(lds, A, a_rows, B1, B3, C, N, K, e, row0, nrows, ntile * BN, KT, kbeg);
-    else if (mi == 2)
-        big_tile<2, 4, DUAL, ACT, OUT_BF16>(lds, A, a_rows, B1, B3, C, N, K, e, row0, nrows, ntile * BN, KT, kbeg);
-    else
-        big_tile<1, 4, DUAL, ACT, OUT_BF16>(lds, A, a_rows, B1, B3, C, N, K, e, row0, nrows, ntile * BN, KT, kbeg);
+    big_tile_any<DUAL, ACT, OUT_BF16>(lds, A, a_rows, B1, B3, C, N, K, e, row0, nrows, ntile, 0, KT, kbeg);
 }
 
 // ---- skinny row groups (decode batches): weight streaming ----------------
@@ -992,7 +1033,7 @@ int device_cus_per_xcd() {
 
 template <bool DUAL, int ACT, bool OUT_BF16>
 hipError_t launch_big(const Shape &s, const void *A, const int32_t *a_rows, const int32_t *offsets, const void *B1,
-                      const void *B3, void *C, int N, int K, hipStream_t st, int nsplit = 1,
+                      const void *B3, void *C, int N, int K, hipStream_t st, unsigned *tctr, int nsplit = 1,
                       void *C_split = nullptr) {
     constexpr int BN = DUAL ? 128 : 256;
     const unsigned nt = (unsigned)((N + BN - 1) / BN);
@@ -1003,10 +1044,12 @@ hipError_t launch_big(const Shape &s, const void *A, const int32_t *a_rows, cons
     // (plus at most cpx / 2 extra slots for the half-width pieces)
     const int cpx = device_cus_per_xcd();
     const unsigned run = (unsigned)(((uint64_t)25 * bound + 8 * 25) / (8 * 18)) + 1 + (unsigned)(cpx / 2);
-    const unsigned blocks = run * NUM_XCD;
+    // with tile counters: at most one block per CU, the blocks taking tiles
+    // until the list is done
+    const unsigned blocks = (tctr && run > (unsigned)cpx ? (unsigned)cpx : run) * NUM_XCD;
     launch_kernel((gemm_bf16_big_kernel<DUAL, ACT, OUT_BF16>), dim3(blocks), dim3(256), 0, st,
                        (const uint16_t *)A, a_rows, offsets, s.E, (const uint16_t *)B1,
-                       (const uint16_t *)B3, C, N, K, nsplit, C_split, cpx);
+                       (const uint16_t *)B3, C, N, K, nsplit, C_split, cpx, tctr);
     return hipGetLastError();
 }
 
@@ -1061,11 +1104,11 @@ hipError_t launch_skinny_any(const Shape &s, int mt, const void *A, const int32_
 
 template <int ACT, bool DUAL>
 hipError_t launch_up_bf16(const Shape &s, const void *A, const int32_t *a_rows, const int32_t *offsets, const void *W1,
-                          const void *W3, void *H, hipStream_t st) {
+                          const void *W3, void *H, hipStream_t st, unsigned *tctr) {
     if (const int mt = skinny_tiles(s, s.d))
         return launch_skinny_any<DUAL, ACT, true>(s, mt, A, a_rows, offsets, W1, W3, H, s.d_ff, s.d, st);
     switch (pick_bm(s, s.d, a_rows != nullptr)) {
-    case BIG_BM: return launch_big<DUAL, ACT, true>(s, A, a_rows, offsets, W1, W3, H, s.d_ff, s.d, st);
+    case BIG_BM: return launch_big<DUAL, ACT, true>(s, A, a_rows, offsets, W1, W3, H, s.d_ff, s.d, st, tctr);
     case 128: return launch_gemm<128, 128, 2, 2, DUAL, ACT, true>(s, A, a_rows, offsets, W1, W3, H, s.d_ff, s.d, st);
     case 64:  return launch_gemm<64, 128, 2, 2, DUAL, ACT, true>(s, A, a_rows, offsets, W1, W3, H, s.d_ff, s.d, st);
     default:  return launch_gemm<32, 128, 1, 4, DUAL, ACT, true>(s, A, a_rows, offsets, W1, W3, H, s.d_ff, s.d, st);
@@ -1076,7 +1119,7 @@ hipError_t launch_up_bf16(const Shape &s, const void *A, const int32_t *a_rows, 
 
 hipError_t launch_expert_up(const Shape &s, const void *x_perm, const int32_t *a_rows,
                             const int32_t *offsets, const void *W1, const void *W3, void *H,
-                            hipStream_t st) {
+                            hipStream_t st, unsigned *tctr) {
     if (s.dtype == 0) {
         int64_t blocks = s.Tk() < 16384 ? s.Tk() : 16384;
         launch_kernel(up_f32_kernel, dim3((unsigned)(blocks > 0 ? blocks : 1)), dim3(256), 0,
@@ -1085,9 +1128,9 @@ hipError_t launch_expert_up(const Shape &s, const void *x_perm, const int32_t *a
         return hipGetLastError();
     }
     switch (s.act) {
-    case ACT_SWIGLU: return launch_up_bf16<ACT_SWIGLU, true>(s, x_perm, a_rows, offsets, W1, W3, H, st);
-    case ACT_GELU:   return launch_up_bf16<ACT_GELU, false>(s, x_perm, a_rows, offsets, W1, nullptr, H, st);
-    default:         return launch_up_bf16<ACT_RELU, false>(s, x_perm, a_rows, offsets, W1, nullptr, H, st);
+    case ACT_SWIGLU: return launch_up_bf16<ACT_SWIGLU, true>(s, x_perm, a_rows, offsets, W1, W3, H, st, tctr);
+    case ACT_GELU:   return launch_up_bf16<ACT_GELU, false>(s, x_perm, a_rows, offsets, W1, nullptr, H, st, tctr);
+    default:         return launch_up_bf16<ACT_RELU, false>(s, x_perm, a_rows, offsets, W1, nullptr, H, st, tctr);
     }
 }
 
@@ -1104,7 +1147,7 @@ int down_ksplit(const Shape &s) {
 
 hipError_t launch_expert_down(const Shape &s, const void *H, const int32_t *offsets,
                               const void *W2, float *y_perm, float *y_perm_part2,
-                              hipStream_t st) {
+                              hipStream_t st, unsigned *tctr) {
     if (s.dtype == 0) {
         int64_t blocks = s.Tk() < 16384 ? s.Tk() : 16384;
         launch_kernel(down_f32_kernel, dim3((unsigned)(blocks > 0 ? blocks : 1)), dim3(256), 0,
@@ -1120,9 +1163,10 @@ hipError_t launch_expert_down(const Shape &s, const void *H, const int32_t *offs
         if (down_ksplit(s) == 2) {
             if (y_perm_part2 == nullptr) return hipErrorInvalidValue;
             return launch_big<false, ACT_NONE, false>(s, H, nullptr, offsets, W2, nullptr, y_perm, s.d,
-                                                       s.d_ff, st, 2, y_perm_part2);
+                                                       s.d_ff, st, tctr, 2, y_perm_part2);
         }
-        return launch_big<false, ACT_NONE, false>(s, H, nullptr, offsets, W2, nullptr, y_perm, s.d, s.d_ff, st);
+        return launch_big<false, ACT_NONE, false>(s, H, nullptr, offsets, W2, nullptr, y_perm, s.d, s.d_ff, st,
+                                                   tctr);
     case 128: return launch_gemm<128, 128, 2, 2, false, ACT_NONE, false>(s, H, nullptr, offsets, W2, nullptr, y_perm, s.d, s.d_ff, st);
     case 64:  return launch_gemm<64, 128, 2, 2, false, ACT_NONE, false>(s, H, nullptr, offsets, W2, nullptr, y_perm, s.d, s.d_ff, st);
     default:  return launch_gemm<32, 128, 1, 4, false, ACT_NONE, false>(s, H, nullptr, offsets, W2, nullptr, y_perm, s.d, s.d_ff, st);
@@ -1175,7 +1219,7 @@ hipError_t launch_wgrad_big(int E, int M, int N, const int32_t *koff, const void
     if (blocks > 0x7fffffff) return hipErrorInvalidValue;
     launch_kernel((gemm_bf16_big_kernel<false, ACT_NONE, false, true>), dim3((unsigned)blocks), dim3(256), 0, st,
                   (const uint16_t *)P, nullptr, koff, M, (const uint16_t *)Q, nullptr, (void *)C, N, (int)ldk, 1,
-                  nullptr, 0);
+                  nullptr, 0, nullptr);
     return hipGetLastError();
 }
 

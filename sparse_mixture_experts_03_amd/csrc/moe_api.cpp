@@ -60,6 +60,7 @@ struct Layout {
     size_t row_of_slot, token_of_row, dropped, stats;
     size_t x_perm, H, y_perm;
     size_t y_perm2;  // second K half of a split down projection (0: no split)
+    size_t tile_ctr; // the 256-row GEMMs' tile counters: routed up, down, shared up, down
     // shared experts (all 0 when there are none)
     size_t sh_offsets;  // {0, T}: their single row group
     size_t w2cat;       // W2 of S > 1 experts as [d][S*d_ff] (0: S <= 1)
@@ -85,6 +86,7 @@ Layout layout(const Shape &s, int S = 0) {
     L.part_lse2 = take(nblk * sizeof(float));
     L.fP = take(((size_t)s.E + 1) * sizeof(double));
     L.arrivals = take(sizeof(unsigned));
+    L.tile_ctr = take(4 * moe::TILE_CTR_WORDS * sizeof(unsigned));
     if (s.dtype == MOE_DTYPE_BF16) {
         L.part_logits = take(moe::route_part_floats(s) * 4);
         L.wsplit = moe::route_fused(s) ? take(moe::route_wsplit_bytes(s)) : 0;
@@ -156,15 +158,16 @@ int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
 // into y_sh, the experts' summed output (and y_sh2, the second K half, when
 // the down projection splits K).
 int run_shared_ffn(const Shape &s, const moe_shared *sh, const void *x, float *y_sh, float *y_sh2,
-                   void *ws, const Layout &L, hipStream_t st) {
+                   void *ws, const Layout &L, hipStream_t st, unsigned *tctr) {
     const int S = sh->n_shared;
     const Shape q = moe::shared_shape(s, S);
     int32_t *offs = at<int32_t>(ws, L.sh_offsets);
     void *w2cat = L.w2cat ? at<char>(ws, L.w2cat) : nullptr;
     void *H = at<char>(ws, L.H_sh);
     MOE_TRY(moe::launch_shared_prep(s, S, sh->W2, w2cat, offs, st));
-    MOE_TRY(moe::launch_expert_up(q, x, nullptr, offs, sh->W1, sh->W3, H, st));
-    MOE_TRY(moe::launch_expert_down(q, H, offs, w2cat ? w2cat : sh->W2, y_sh, y_sh2, st));
+    MOE_TRY(moe::launch_expert_up(q, x, nullptr, offs, sh->W1, sh->W3, H, st, tctr));
+    MOE_TRY(moe::launch_expert_down(q, H, offs, w2cat ? w2cat : sh->W2, y_sh, y_sh2, st,
+                                    tctr ? tctr + moe::TILE_CTR_WORDS : nullptr));
     return MOE_OK;
 }
 
@@ -282,9 +285,11 @@ int moe_expert_ffn(const moe_desc *desc, const void *x_perm, const int32_t *offs
     const Layout L = layout(s);
     hipStream_t st = (hipStream_t)stream;
     void *H = at<char>(ws, L.H);
-    MOE_TRY(moe::launch_expert_up(s, x_perm, nullptr, offsets, W1, W3, H, st));
+    unsigned *tctr = at<unsigned>(ws, L.tile_ctr);
+    MOE_TRY(moe::launch_zero_u32(tctr, 2 * moe::TILE_CTR_WORDS, st));
+    MOE_TRY(moe::launch_expert_up(s, x_perm, nullptr, offsets, W1, W3, H, st, tctr));
     float *part2 = L.y_perm2 ? at<float>(ws, L.y_perm2) : nullptr;
-    MOE_TRY(moe::launch_expert_down(s, H, offsets, W2, y_perm, part2, st));
+    MOE_TRY(moe::launch_expert_down(s, H, offsets, W2, y_perm, part2, st, tctr + moe::TILE_CTR_WORDS));
     if (part2) MOE_TRY(moe::launch_add_partial(s, y_perm, part2, offsets, st));
     return MOE_OK;
 }
@@ -315,6 +320,7 @@ struct BwdLayout {
     size_t p, lse, dh, dwr_part, poff;
     size_t dwr_xt, dwr_p, dwr_c, dwr_idx;   // dW_r on matrix cores (dwr_plan)
     size_t lg_w, lg_c, lg_idx;              // logits on matrix cores (logits_plan)
+    size_t tile_ctr;                        // tile counters of the five grouped GEMMs
     size_t total;
     int64_t R, ldk;
 };
@@ -354,6 +360,7 @@ BwdLayout bwd_layout(const Shape &s) {
     L.lse = take((size_t)s.T * 4);
     L.dh = take((size_t)s.T * E * 4);
     L.poff = take((E + 1) * 4);
+    L.tile_ctr = take(5 * moe::TILE_CTR_WORDS * 4);
     const moe::DwrPlan pl = moe::dwr_plan(s);
     if (pl.ns == 0) L.dwr_part = take(moe::dwr_part_floats(s) * 4);
     if (pl.ns > 0) {
@@ -376,11 +383,11 @@ BwdLayout bwd_layout(const Shape &s) {
 // forward's down-projection launcher on a re-labelled shape), adding the
 // second K half when it splits K.
 int grouped_gemm_f32(const Shape &s, int n, int kdim, const void *A, const int32_t *offsets,
-                     const void *B, float *C, float *part2, hipStream_t st) {
+                     const void *B, float *C, float *part2, hipStream_t st, unsigned *tctr) {
     Shape q = s;
     q.d = n;
     q.d_ff = kdim;
-    MOE_TRY(moe::launch_expert_down(q, A, offsets, B, C, part2, st));
+    MOE_TRY(moe::launch_expert_down(q, A, offsets, B, C, part2, st, tctr));
     if (moe::down_ksplit(q) == 2) MOE_TRY(moe::launch_add_partial(q, C, part2, offsets, st));
     return MOE_OK;
 }
@@ -430,6 +437,10 @@ int forward_impl(const moe_desc *desc, const moe_shared *sh, const moe_fp8_exper
     if (!stats) stats = at<float>(ws, L.stats);
     void *H = at<char>(ws, L.H);
     float *y_perm = at<float>(ws, L.y_perm);
+    // tile counters, cleared by the dispatch launch (none on the small-batch
+    // path, whose kernels need none)
+    unsigned *tctr = moe::route_small(s) ? nullptr : at<unsigned>(ws, L.tile_ctr);
+    constexpr int CW = moe::TILE_CTR_WORDS;
 
     hipStream_t st = (hipStream_t)stream;
     StageEvents ev{desc->stage_events, desc->n_stage_events};
@@ -459,7 +470,8 @@ int forward_impl(const moe_desc *desc, const moe_shared *sh, const moe_fp8_exper
                                    moe::route_stat_blocks(s), stats, at<double>(ws, L.fP),
                                    at<unsigned>(ws, L.arrivals)};
         MOE_TRY(moe::launch_dispatch(s, topk_idx, routed_counts, kept_counts, offsets, row_of_slot,
-                                     token_of_row, dropped, at<int32_t>(ws, L.chunk_counts), st, &rs));
+                                     token_of_row, dropped, at<int32_t>(ws, L.chunk_counts), st, &rs, tctr,
+                                     4 * CW));
     }
     MOE_TRY(ev.record(st));
     // the gather is folded into the up projection's loads: its rows of A are
@@ -467,7 +479,7 @@ int forward_impl(const moe_desc *desc, const moe_shared *sh, const moe_fp8_exper
     ev.around_next_launch();  // events before and after expert-up
     const hipError_t up_err =
         f8 ? moe::launch_expert_up_fp8(s, x, token_of_row, offsets, f8->W1, f8->W3, f8->s1, f8->s3, H, st)
-           : moe::launch_expert_up(s, x, token_of_row, offsets, W1, W3, H, st);
+           : moe::launch_expert_up(s, x, token_of_row, offsets, W1, W3, H, st, tctr);
     moe::next_launch_events() = moe::LaunchEvents{nullptr, nullptr};
     MOE_TRY(up_err);
     // the e4m3 path never splits K (streaming kernel only)
@@ -475,7 +487,7 @@ int forward_impl(const moe_desc *desc, const moe_shared *sh, const moe_fp8_exper
     if (f8)
         MOE_TRY(moe::launch_expert_down_fp8(s, H, offsets, f8->W2, f8->s2, y_perm, st));
     else
-        MOE_TRY(moe::launch_expert_down(s, H, offsets, W2, y_perm, part2, st));
+        MOE_TRY(moe::launch_expert_down(s, H, offsets, W2, y_perm, part2, st, tctr ? tctr + CW : nullptr));
     if (!sh) {
         ev.around_next_launch();  // events before and after the combine (one kernel)
         const hipError_t c_err = moe::launch_combine(s, y_perm, part2, row_of_slot, gates, y, st);
@@ -488,7 +500,8 @@ int forward_impl(const moe_desc *desc, const moe_shared *sh, const moe_fp8_exper
     if (S > 0) {
         y_sh = at<float>(ws, L.y_sh);
         y_sh2 = L.y_sh2 ? at<float>(ws, L.y_sh2) : nullptr;
-        if ((rc = run_shared_ffn(s, sh, x, y_sh, y_sh2, ws, L, st)) != MOE_OK) return rc;
+        if ((rc = run_shared_ffn(s, sh, x, y_sh, y_sh2, ws, L, st, tctr ? tctr + 2 * CW : nullptr)) != MOE_OK)
+            return rc;
     }
     MOE_TRY(ev.record(st));
     MOE_TRY(moe::launch_combine_shared(s, y_perm, part2, row_of_slot, gates, y_sh, y_sh2,
@@ -552,7 +565,9 @@ int moe_shared_ffn(const moe_desc *desc, const moe_shared *shared, const void *x
     const Layout L = layout(s, S);
     hipStream_t st = (hipStream_t)stream;
     float *y_sh2 = L.y_sh2 ? at<float>(ws, L.y_sh2) : nullptr;
-    if ((rc = run_shared_ffn(s, shared, x, y_shared, y_sh2, ws, L, st)) != MOE_OK) return rc;
+    unsigned *tctr = at<unsigned>(ws, L.tile_ctr) + 2 * moe::TILE_CTR_WORDS;
+    MOE_TRY(moe::launch_zero_u32(tctr, 2 * moe::TILE_CTR_WORDS, st));
+    if ((rc = run_shared_ffn(s, shared, x, y_shared, y_sh2, ws, L, st, tctr)) != MOE_OK) return rc;
     if (y_sh2)
         MOE_TRY(moe::launch_add_partial(moe::shared_shape(s, S), y_shared, y_sh2,
                                         at<int32_t>(ws, L.sh_offsets), st));
@@ -675,17 +690,22 @@ int moe_backward(const moe_desc *desc, const void *x, const float *W_r, const fl
     if (swiglu)
         MOE_TRY(moe::launch_transpose_bf16(W3, f, d, d, df, (char *)wcat + (size_t)f * 2, (int64_t)nup * f,
                                            (int64_t)nup * df, E, st));
+    // tile counters of the five grouped GEMMs below, cleared once
+    unsigned *tc = (unsigned *)(w + L.tile_ctr);
+    constexpr int CW = moe::TILE_CTR_WORDS;
+    MOE_TRY(moe::launch_zero_u32(tc, 5 * CW, st));
     // recompute the forward's expert part: x rows, pre-activations, H, E(x)
     MOE_TRY(moe::launch_gather(s, x, token_of_row, offsets, xp, st));
-    if ((rc = grouped_gemm_f32(s, f, d, xp, offsets, W1, a1, part2, st)) != MOE_OK) return rc;
-    if (swiglu && (rc = grouped_gemm_f32(s, f, d, xp, offsets, W3, a3, part2, st)) != MOE_OK) return rc;
+    if ((rc = grouped_gemm_f32(s, f, d, xp, offsets, W1, a1, part2, st, tc)) != MOE_OK) return rc;
+    if (swiglu && (rc = grouped_gemm_f32(s, f, d, xp, offsets, W3, a3, part2, st, tc + CW)) != MOE_OK) return rc;
     MOE_TRY(moe::launch_act_fwd(s, a1, a3, offsets, H, st));
-    if ((rc = grouped_gemm_f32(s, d, f, H, offsets, W2, Y, part2, st)) != MOE_OK) return rc;
+    if ((rc = grouped_gemm_f32(s, d, f, H, offsets, W2, Y, part2, st, tc + 2 * CW)) != MOE_OK) return rc;
     // combine, down projection and activation backward; dX_perm
     MOE_TRY(moe::launch_combine_bwd(s, dy, Y, token_of_row, row_of_slot, gates, offsets, dE, dg, st));
-    if ((rc = grouped_gemm_f32(s, f, d, dE, offsets, w2t, dH, part2, st)) != MOE_OK) return rc;
+    if ((rc = grouped_gemm_f32(s, f, d, dE, offsets, w2t, dH, part2, st, tc + 3 * CW)) != MOE_OK) return rc;
     MOE_TRY(moe::launch_act_bwd(s, a1, a3, dH, offsets, dA, st));
-    if ((rc = grouped_gemm_f32(s, d, nup * f, dA, offsets, wcat, dXp, part2, st)) != MOE_OK) return rc;
+    if ((rc = grouped_gemm_f32(s, d, nup * f, dA, offsets, wcat, dXp, part2, st, tc + 4 * CW)) != MOE_OK)
+        return rc;
     // router: gates, load-balancing and z terms; dx, dW_r, dbias
     const moe::LogitsPlan lpl = moe::logits_plan(s);
     if (lpl.ns > 0)

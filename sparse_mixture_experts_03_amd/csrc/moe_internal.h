@@ -110,10 +110,15 @@ struct RouteStatsIn {
     double *fP;
     unsigned *arrivals;
 };
+// zero_ctr (n_zero words), when given, is cleared by the ranking launch:
+// the tile counters of the expert GEMMs that follow (launch_expert_up/down).
 hipError_t launch_dispatch(const Shape &s, const int32_t *topk_idx, int32_t *routed,
                            int32_t *kept, int32_t *offsets, int32_t *row_of_slot,
                            int32_t *token_of_row, uint8_t *dropped, int32_t *chunk_counts,
-                           hipStream_t st, const RouteStatsIn *stats = nullptr);
+                           hipStream_t st, const RouteStatsIn *stats = nullptr,
+                           unsigned *zero_ctr = nullptr, int n_zero = 0);
+// Clears n words (a one-block kernel; no memset node in a captured graph).
+hipError_t launch_zero_u32(unsigned *p, int n, hipStream_t st);
 hipError_t launch_gather(const Shape &s, const void *x, const int32_t *token_of_row,
                          const int32_t *offsets, void *x_perm, hipStream_t st);
 
@@ -141,9 +146,14 @@ hipError_t launch_shared_prep(const Shape &s, int S, const void *W2s, void *W2ca
 // ---- expert FFN: grouped GEMMs over ragged per-expert row blocks --------
 // a_rows: row r of A is A[a_rows[r]] (the gather done by the loads);
 // nullptr: row r is A[r].
+// tctr: TILE_CTR_WORDS words, zero when the launch starts (or nullptr):
+// the 256-row tile kernel's per-XCD tile counters, which let its blocks
+// stay resident and take tiles in turn.  Each launch needs its own (or the
+// same ones cleared again); the other kernels ignore them.
+constexpr int TILE_CTR_WORDS = 8;
 hipError_t launch_expert_up(const Shape &s, const void *x_perm, const int32_t *a_rows,
                             const int32_t *offsets, const void *W1, const void *W3, void *H,
-                            hipStream_t st);
+                            hipStream_t st, unsigned *tctr);
 // The down projection may split K in two (down_ksplit(s) == 2, when its
 // tiles would not fill three rounds of the CUs): the second half's partial
 // sums go to y_perm_part2 (same layout as y_perm) and must be added, either
@@ -151,7 +161,7 @@ hipError_t launch_expert_up(const Shape &s, const void *x_perm, const int32_t *a
 int down_ksplit(const Shape &s);
 hipError_t launch_expert_down(const Shape &s, const void *H, const int32_t *offsets,
                               const void *W2, float *y_perm, float *y_perm_part2,
-                              hipStream_t st);
+                              hipStream_t st, unsigned *tctr);
 hipError_t launch_add_partial(const Shape &s, float *y_perm, const float *part2,
                               const int32_t *offsets, hipStream_t st);
 
