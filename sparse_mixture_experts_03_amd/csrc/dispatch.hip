@@ -18,9 +18,9 @@
 //     all chunk histograms, routed_e, kept_e = min(routed_e, C), the row
 //     offsets (exclusive prefix of kept_e) and, for its own chunk, how many
 //     assignments of each expert precede it.  It then ranks its chunk in
-//     order, 256 assignments per round: inside a wave, lanes with the same
-//     expert are grouped by ballot (leader's expert, then the lanes that
-//     match it) and ranked by popcount of the lower lanes; a table of
+//     order, 256 assignments per round: inside a wave, the lanes with the
+//     same expert are found bit by bit of the expert index (one ballot per
+//     bit) and ranked by popcount of the lower lanes; a table of
 //     per-wave counts in LDS adds the waves before, and a per-expert
 //     running count carries the rounds.  No atomic decides any order.
 //     rank < C: row = offset_e + rank; else dropped.
@@ -196,6 +196,7 @@ __global__ __launch_bounds__(DP_THREADS) void dispatch_rank_kernel(
     __syncthreads();
 
     const unsigned long long lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    const int nbits = expert_bits(E);
 #pragma unroll
     for (int round = 0; round < DP_MAXR; ++round) {
         if (round >= nr) break;
@@ -205,22 +206,10 @@ __global__ __launch_bounds__(DP_THREADS) void dispatch_rank_kernel(
         const bool inrange = j < Tk;
         const int e_j = ej[round];
         const bool valid = e_j >= 0;
-        // group the wave's lanes by expert, in lane (= assignment) order
-        bool act = valid;
-        int rank_w = 0;
-        while (true) {
-            const unsigned long long am = __ballot(act);
-            if (am == 0ull) break;
-            const int leader = __ffsll((long long)am) - 1;
-            const int e0 = __builtin_amdgcn_readlane(e_j, leader);  // leader is wave-uniform
-            const bool m = act && e_j == e0;
-            const unsigned long long mm = __ballot(m);
-            if (m) {
-                rank_w = __popcll(mm & lt_mask);
-                act = false;
-            }
-            if (lane == leader) wcnt[w][e0] = __popcll(mm);
-        }
+        // the wave's lanes with this lane's expert, in lane (= assignment) order
+        const unsigned long long mm = lanes_with_same_expert(e_j, valid, nbits);
+        const int rank_w = __popcll(mm & lt_mask);
+        if (valid && rank_w == 0) wcnt[w][e_j] = __popcll(mm);   // the group's lowest lane
         __syncthreads();
         if (valid) {
             int rank = running[e_j] + rank_w;

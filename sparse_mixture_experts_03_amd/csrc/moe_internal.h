@@ -282,6 +282,28 @@ hipError_t launch_combine_shared(const Shape &s, const float *y_perm, const floa
 namespace moe {
 
 // fp32 -> bf16 bits, round to nearest even (NaN becomes a quiet NaN).
+// The lanes of the wave whose expert equals this lane's (valid lanes only;
+// 0 for an invalid lane), found bit by bit: for each of the nbits low bits
+// of e (nbits uniform, 2^nbits >= E), keep the lanes whose bit agrees.  One
+// ballot per bit, whatever the number of distinct experts in the wave.  A
+// lane's rank among its expert's lanes in lane order is then the popcount
+// of the mask below it, and the group's lowest lane can publish its size.
+__device__ __forceinline__ unsigned long long lanes_with_same_expert(int e, bool valid, int nbits) {
+    unsigned long long m = __ballot(valid);
+    for (int b = 0; b < nbits; ++b) {
+        const bool bit = (e >> b) & 1;
+        const unsigned long long bm = __ballot(bit);
+        m &= bit ? bm : ~bm;
+    }
+    return valid ? m : 0ull;
+}
+// Bits that tell apart the expert indices 0 .. E - 1.
+__host__ __device__ inline int expert_bits(int E) {
+    int b = 0;
+    while ((1 << b) < E) ++b;
+    return b;
+}
+
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
     uint32_t u = __float_as_uint(f);
     if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);

@@ -907,7 +907,8 @@ __global__ __launch_bounds__(256) void route_stats_kernel(
 // choices, aux over experts in order.  The dispatch, when asked for, counts
 // the assignments per expert (integer LDS atomics), forms kept counts and
 // offsets, then wave 0 ranks the T*k assignments in order, 64 at a time:
-// lanes with the same expert are grouped by ballot and ranked by popcount
+// lanes with the same expert are found bit by bit of the expert index (one
+// ballot per bit) and ranked by popcount
 // of the lower lanes, on top of a per-expert running count.
 constexpr int RS_THREADS = 1024;
 
@@ -1002,22 +1003,11 @@ __global__ __launch_bounds__(RS_THREADS) void route_small_kernel(
             const int j = j0 + lane;
             const bool valid = j < Tk;
             const int ej = valid ? tk[j] : -1;
-            bool act = valid;
-            int rank = 0;
-            while (true) {
-                const unsigned long long am = __ballot(act);
-                if (am == 0ull) break;
-                const int leader = __ffsll((long long)am) - 1;
-                const int e0 = __builtin_amdgcn_readlane(ej, leader);  // leader is wave-uniform
-                const bool m = act && ej == e0;
-                const unsigned long long mm = __ballot(m);
-                if (m) {
-                    rank = run[e0] + __popcll(mm & lt_mask);
-                    act = false;
-                }
-                // every lane has read run[e0] above before the leader adds
-                if (lane == leader) run[e0] += __popcll(mm);
-            }
+            const unsigned long long mm = lanes_with_same_expert(ej, valid, expert_bits(E));
+            const int below = __popcll(mm & lt_mask);
+            const int rank = valid ? run[ej] + below : 0;
+            // every lane has read run[] above before the group's lowest lane adds
+            if (valid && below == 0) run[ej] += __popcll(mm);
             if (valid) {
                 if (C < 0 || rank < C) {
                     const int row = off[ej] + rank;
