@@ -401,10 +401,12 @@ int moe_forward_fp8(const moe_desc *desc, const void *x, const float *W_r, const
  * routing moe_forward took (held fixed: pass its topk_idx, gates, offsets,
  * row_of_slot, token_of_row and stats, with the same x, weights, bias and
  * noise).  The expert activations are recomputed (nothing else of the
- * forward is needed).  bf16 layers only, and at most about 4.19 million
- * kept rows (65535 * 64 once each expert's count is rounded up to 64);
- * MOE_ERR_UNSUPPORTED otherwise, before any launch.
- *   dy     [T][d]          bf16   gradient of the layer output
+ * forward is needed).  bf16 layers: at most about 4.19 million kept rows
+ * (65535 * 64 once each expert's count is rounded up to 64),
+ * MOE_ERR_UNSUPPORTED otherwise, before any launch.  fp32 layers: any shape
+ * the forward takes.
+ *   dy     [T][d]          the layer's dtype (bf16 or fp32): gradient of
+ *                          the layer output
  *   dx     [T][d]          fp32
  *   dW_r   [E][d]          fp32
  *   dbias  [E]             fp32   optional (requires bias)
@@ -412,11 +414,13 @@ int moe_forward_fp8(const moe_desc *desc, const void *x, const float *W_r, const
  *   dW2    [E][d][d_ff]    fp32
  * Every gradient is written in full (an expert without rows gets zeros);
  * sums run in a fixed order, so results are reproducible.  Internally the
- * weights are transposed into the workspace once per call, the expert
- * GEMMs use the forward's grouped GEMM kernels, and the weight gradients a
- * GEMM over each expert's row block (activations transposed into a layout
- * whose experts start on multiples of 64 rows, zero-padded).  ws:
- * moe_backward_workspace_size().
+ * weights are transposed into the workspace once per call and the expert
+ * GEMMs use the forward's grouped GEMM kernels.  bf16 layers: the weight
+ * gradients are a GEMM over each expert's row block (activations transposed
+ * into a layout whose experts start on multiples of 64 rows, zero-padded)
+ * and intermediate activations are rounded to bf16; fp32 layers keep every
+ * intermediate in fp32 and sum each weight gradient over the expert's rows
+ * in row order.  ws: moe_backward_workspace_size() (it differs by dtype).
  */
 int moe_backward_workspace_size(const moe_desc *desc, size_t *bytes);
 

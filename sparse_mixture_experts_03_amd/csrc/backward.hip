@@ -38,6 +38,10 @@
 //                          2 GiB; otherwise the forward's 256 x 256 tile
 //                          runs them (its weight-gradient form, in
 //                          expert_gemm.hip)
+// fp32 layers use the same steps with plain kernels where the bf16 path
+// uses matrix cores: transpose_f32_kernel for the weights, the fp32
+// grouped GEMM of the forward, and wgrad_f32_kernel (one thread per weight,
+// the expert's rows in order).
 // Every sum has a fixed order (no atomics); results are reproducible.
 #include "moe_internal.h"
 
@@ -58,6 +62,12 @@ __device__ __forceinline__ float wave_max_f32b(float v) {
     for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
     return v;
 }
+
+// activations in the layer's storage type: bf16 bits or fp32
+__device__ __forceinline__ float ld_elem(const uint16_t *p, int64_t i) { return bf16_to_f32(p[i]); }
+__device__ __forceinline__ float ld_elem(const float *p, int64_t i) { return p[i]; }
+__device__ __forceinline__ void st_elem(uint16_t *p, int64_t i, float v) { p[i] = f32_to_bf16(v); }
+__device__ __forceinline__ void st_elem(float *p, int64_t i, float v) { p[i] = v; }
 
 // dst[b][c][r] = src[b][r][c] for r < R, c < C (bf16); strides in elements.
 // VEC: 4-element (8-byte) reads along c and writes along r (C, R, the
@@ -202,22 +212,22 @@ __global__ __launch_bounds__(256) void transpose_padded_kernel(const uint16_t *_
 }
 
 // H[r][f] = act(a1, a3) for the kept rows (r < offsets[E])
+template <typename HT>
 __global__ __launch_bounds__(256) void act_fwd_kernel(const float *__restrict__ a1,
                                                       const float *__restrict__ a3,
                                                       const int32_t *__restrict__ offsets, int E,
-                                                      int d_ff, int act, uint16_t *__restrict__ H) {
+                                                      int d_ff, int act, HT *__restrict__ H) {
     const int64_t n = (int64_t)offsets[E] * d_ff;
-    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
-        const float v = apply_act(act, a1[i], act == ACT_SWIGLU ? a3[i] : 0.f);
-        H[i] = f32_to_bf16(v);
-    }
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
+        st_elem(H, i, apply_act(act, a1[i], act == ACT_SWIGLU ? a3[i] : 0.f));
 }
 
 // one wave per kept row: its token and slot, dE = g dy_t, dg = <dy_t, Y_r>
+template <typename DT>
 __global__ __launch_bounds__(256) void combine_bwd_kernel(
-    const uint16_t *__restrict__ dy, const float *__restrict__ Y, const int32_t *__restrict__ token_of_row,
+    const DT *__restrict__ dy, const float *__restrict__ Y, const int32_t *__restrict__ token_of_row,
     const int32_t *__restrict__ row_of_slot, const float *__restrict__ gates,
-    const int32_t *__restrict__ offsets, int E, int k, int d, uint16_t *__restrict__ dE,
+    const int32_t *__restrict__ offsets, int E, int k, int d, DT *__restrict__ dE,
     float *__restrict__ dg) {
     const int lane = threadIdx.x & 63;
     const int rows = offsets[E];
@@ -229,36 +239,39 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(
         const float g = gates[(int64_t)t * k + s];
         float dot = 0.f;
         for (int o = lane; o < d; o += 64) {
-            const float v = bf16_to_f32(dy[(int64_t)t * d + o]);
+            const float v = ld_elem(dy, (int64_t)t * d + o);
             dot = fmaf(v, Y[(int64_t)r * d + o], dot);
-            dE[(int64_t)r * d + o] = f32_to_bf16(g * v);
+            st_elem(dE, (int64_t)r * d + o, g * v);
         }
         dot = wave_sum_f32(dot);
         if (lane == 0) dg[(int64_t)t * k + s] = dot;
     }
 }
 
-// dA[r] = [da1 | da3] (bf16; width n_up * d_ff) from dH and the pre-activations
+// dA[r] = [da1 | da3] (storage type; width n_up * d_ff) from dH and the
+// pre-activations
+template <typename DT>
 __global__ __launch_bounds__(256) void act_bwd_kernel(const float *__restrict__ a1,
                                                       const float *__restrict__ a3,
                                                       const float *__restrict__ dH,
                                                       const int32_t *__restrict__ offsets, int E,
-                                                      int d_ff, int act, uint16_t *__restrict__ dA) {
+                                                      int d_ff, int act, DT *__restrict__ dA) {
     const int64_t n = (int64_t)offsets[E] * d_ff;
     const int nup = act == ACT_SWIGLU ? 2 : 1;
     for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
         const int64_t r = i / d_ff, f = i - r * d_ff;
-        uint16_t *row = dA + r * nup * d_ff;
-        uint16_t da1, da3 = 0;
-        act_bwd_elem(act, a1[i], act == ACT_SWIGLU ? a3[i] : 0.f, dH[i], da1, da3);
-        row[f] = da1;
-        if (act == ACT_SWIGLU) row[d_ff + f] = da3;
+        DT *row = dA + r * nup * d_ff;
+        float da1, da3;
+        act_bwd_f32(act, a1[i], act == ACT_SWIGLU ? a3[i] : 0.f, dH[i], da1, da3);
+        st_elem(row, f, da1);
+        if (act == ACT_SWIGLU) st_elem(row, d_ff + f, da3);
     }
 }
 
 // logits for few experts (E <= 32): one wave per token (lane i: experts i,
 // i + 64), softmax, lse
-__global__ __launch_bounds__(256) void logits_wave_kernel(const uint16_t *__restrict__ x,
+template <typename XT>
+__global__ __launch_bounds__(256) void logits_wave_kernel(const XT *__restrict__ x,
                                                      const float *__restrict__ Wr,
                                                      const float *__restrict__ bias,
                                                      const float *__restrict__ noise, int T, int d,
@@ -270,7 +283,7 @@ __global__ __launch_bounds__(256) void logits_wave_kernel(const uint16_t *__rest
         for (int i = 0; i < E; ++i) {
             float acc = 0.f;
             for (int j = lane; j < d; j += 64)
-                acc = fmaf(bf16_to_f32(x[(int64_t)t * d + j]), Wr[(int64_t)i * d + j], acc);
+                acc = fmaf(ld_elem(x, (int64_t)t * d + j), Wr[(int64_t)i * d + j], acc);
             acc = wave_sum_f32(acc);
             if (bias) acc += bias[i];
             if (noise) acc += noise[(int64_t)t * E + i];
@@ -292,7 +305,8 @@ __global__ __launch_bounds__(256) void logits_wave_kernel(const uint16_t *__rest
 // accumulates experts i and i + 64 for the wave's 8 tokens, reading its own
 // W_r rows 4 columns at a time, each x value a broadcast from LDS.
 constexpr int LG_TB = 32, LG_TW = 8, LG_DC = 1024;
-__global__ __launch_bounds__(256) void logits_kernel(const uint16_t *__restrict__ x,
+template <typename XT>
+__global__ __launch_bounds__(256) void logits_kernel(const XT *__restrict__ x,
                                                      const float *__restrict__ Wr,
                                                      const float *__restrict__ bias,
                                                      const float *__restrict__ noise, int T, int d,
@@ -310,7 +324,7 @@ __global__ __launch_bounds__(256) void logits_kernel(const uint16_t *__restrict_
         __syncthreads();
         for (int q = threadIdx.x; q < LG_TB * cw; q += 256) {
             const int tt = q / cw, j = q - tt * cw;
-            xs[tt][j] = t0 + tt < T ? bf16_to_f32(x[(int64_t)(t0 + tt) * d + c0 + j]) : 0.f;
+            xs[tt][j] = t0 + tt < T ? ld_elem(x, (int64_t)(t0 + tt) * d + c0 + j) : 0.f;
         }
         __syncthreads();
         const float *w0 = Wr + (int64_t)lane * d + c0, *w1 = Wr + (int64_t)(lane + 64) * d + c0;
@@ -442,8 +456,9 @@ __global__ __launch_bounds__(256) void dx_kernel(const float *__restrict__ dXp,
 // 16 experts at a time into partials [split][i][j]; then the splits are
 // added in split order.
 constexpr int DWR_EG = 16, DWR_SPLITS = 64;
+template <typename XT>
 __global__ __launch_bounds__(256) void dwr_partial_kernel(const float *__restrict__ dh,
-                                                          const uint16_t *__restrict__ x, int T, int d,
+                                                          const XT *__restrict__ x, int T, int d,
                                                           int E, float *__restrict__ part) {
     const int j = blockIdx.x * 256 + threadIdx.x;
     const int i0 = blockIdx.y * DWR_EG;
@@ -455,7 +470,7 @@ __global__ __launch_bounds__(256) void dwr_partial_kernel(const float *__restric
     for (int u = 0; u < DWR_EG; ++u) acc[u] = 0.f;
 #pragma unroll 8
     for (int t = t0; t < t1; ++t) {
-        const float xv = bf16_to_f32(x[(int64_t)t * d + j]);
+        const float xv = ld_elem(x, (int64_t)t * d + j);
 #pragma unroll
         for (int u = 0; u < DWR_EG; ++u)
             if (i0 + u < E) acc[u] = fmaf(dh[(int64_t)t * E + i0 + u], xv, acc[u]);
@@ -685,6 +700,34 @@ inline unsigned grid_for(int64_t items, int64_t per_block, int64_t cap) {
     return (unsigned)(b < 1 ? 1 : b);
 }
 
+// fp32 layers (small; plain kernels, one thread per output, sums in a
+// fixed order):
+// dst[b][c][r] = src[b][r][c] for r < R, c < C; strides in elements
+__global__ __launch_bounds__(256) void transpose_f32_kernel(const float *__restrict__ src, int64_t R, int64_t C,
+                                                            int64_t lds, int64_t sbs, float *__restrict__ dst,
+                                                            int64_t ldd, int64_t dbs, int batch) {
+    const int64_t n = (int64_t)batch * R * C;
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
+        const int64_t b = i / (R * C), rc = i - b * R * C, r = rc / C, c = rc - r * C;
+        dst[b * dbs + c * ldd + r] = src[b * sbs + r * lds + c];
+    }
+}
+
+// C[e][m][n] = sum over the rows r of expert e (in row order) of
+// P[r][m] Q[r][n]: the weight gradients of an fp32 layer
+__global__ __launch_bounds__(256) void wgrad_f32_kernel(int E, int M, int N, const int32_t *__restrict__ offsets,
+                                                        const float *__restrict__ P, int64_t ldp,
+                                                        const float *__restrict__ Q, int64_t ldq,
+                                                        float *__restrict__ C) {
+    const int64_t n_out = (int64_t)E * M * N;
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n_out; i += (int64_t)gridDim.x * 256) {
+        const int64_t e = i / ((int64_t)M * N), mn = i - e * M * N, m = mn / N, n = mn - m * N;
+        float acc = 0.f;
+        for (int r = offsets[e]; r < offsets[e + 1]; ++r) acc = fmaf(P[(int64_t)r * ldp + m], Q[(int64_t)r * ldq + n], acc);
+        C[i] = acc;
+    }
+}
+
 }  // namespace
 
 hipError_t launch_transpose_bf16(const void *src, int64_t R, int64_t C, int64_t lds, int64_t sbs,
@@ -727,24 +770,53 @@ hipError_t launch_transpose_padded(const void *src, int64_t C, int64_t lds, cons
 
 hipError_t launch_act_fwd(const Shape &s, const float *a1, const float *a3, const int32_t *offsets,
                           void *H, hipStream_t st) {
-    hipLaunchKernelGGL(act_fwd_kernel, dim3(grid_for((int64_t)s.Tk() * s.d_ff, 256, 16384)), dim3(256), 0,
-                       st, a1, a3, offsets, s.E, s.d_ff, s.act, (uint16_t *)H);
+    const dim3 g(grid_for((int64_t)s.Tk() * s.d_ff, 256, 16384));
+    if (s.dtype == 0)
+        hipLaunchKernelGGL(act_fwd_kernel<float>, g, dim3(256), 0, st, a1, a3, offsets, s.E, s.d_ff, s.act,
+                           (float *)H);
+    else
+        hipLaunchKernelGGL(act_fwd_kernel<uint16_t>, g, dim3(256), 0, st, a1, a3, offsets, s.E, s.d_ff, s.act,
+                           (uint16_t *)H);
     return hipGetLastError();
 }
 
 hipError_t launch_combine_bwd(const Shape &s, const void *dy, const float *Y, const int32_t *token_of_row,
                               const int32_t *row_of_slot, const float *gates, const int32_t *offsets,
                               void *dE, float *dg, hipStream_t st) {
-    hipLaunchKernelGGL(combine_bwd_kernel, dim3(grid_for(s.Tk(), 4, 16384)), dim3(256), 0, st,
-                       (const uint16_t *)dy, Y, token_of_row, row_of_slot, gates, offsets, s.E, s.k, s.d,
-                       (uint16_t *)dE, dg);
+    const dim3 g(grid_for(s.Tk(), 4, 16384));
+    if (s.dtype == 0)
+        hipLaunchKernelGGL(combine_bwd_kernel<float>, g, dim3(256), 0, st, (const float *)dy, Y, token_of_row,
+                           row_of_slot, gates, offsets, s.E, s.k, s.d, (float *)dE, dg);
+    else
+        hipLaunchKernelGGL(combine_bwd_kernel<uint16_t>, g, dim3(256), 0, st, (const uint16_t *)dy, Y,
+                           token_of_row, row_of_slot, gates, offsets, s.E, s.k, s.d, (uint16_t *)dE, dg);
     return hipGetLastError();
 }
 
 hipError_t launch_act_bwd(const Shape &s, const float *a1, const float *a3, const float *dH,
                           const int32_t *offsets, void *dA, hipStream_t st) {
-    hipLaunchKernelGGL(act_bwd_kernel, dim3(grid_for((int64_t)s.Tk() * s.d_ff, 256, 16384)), dim3(256), 0,
-                       st, a1, a3, dH, offsets, s.E, s.d_ff, s.act, (uint16_t *)dA);
+    const dim3 g(grid_for((int64_t)s.Tk() * s.d_ff, 256, 16384));
+    if (s.dtype == 0)
+        hipLaunchKernelGGL(act_bwd_kernel<float>, g, dim3(256), 0, st, a1, a3, dH, offsets, s.E, s.d_ff, s.act,
+                           (float *)dA);
+    else
+        hipLaunchKernelGGL(act_bwd_kernel<uint16_t>, g, dim3(256), 0, st, a1, a3, dH, offsets, s.E, s.d_ff,
+                           s.act, (uint16_t *)dA);
+    return hipGetLastError();
+}
+
+hipError_t launch_transpose_f32(const float *src, int64_t R, int64_t C, int64_t lds, int64_t sbs, float *dst,
+                                int64_t ldd, int64_t dbs, int batch, hipStream_t st) {
+    if (R <= 0 || C <= 0 || batch <= 0) return hipSuccess;
+    hipLaunchKernelGGL(transpose_f32_kernel, dim3(grid_for((int64_t)batch * R * C, 256, 16384)), dim3(256), 0,
+                       st, src, R, C, lds, sbs, dst, ldd, dbs, batch);
+    return hipGetLastError();
+}
+
+hipError_t launch_wgrad_f32(int E, int M, int N, const int32_t *offsets, const float *P, int64_t ldp,
+                            const float *Q, int64_t ldq, float *C, hipStream_t st) {
+    hipLaunchKernelGGL(wgrad_f32_kernel, dim3(grid_for((int64_t)E * M * N, 256, 16384)), dim3(256), 0, st, E, M,
+                       N, offsets, P, ldp, Q, ldq, C);
     return hipGetLastError();
 }
 
@@ -755,12 +827,22 @@ hipError_t launch_router_bwd(const Shape &s, const void *x, const float *Wr, con
                              hipStream_t st, bool logits) {
     const unsigned g = grid_for(s.T, 4, 16384);
     if (logits) {
-        if (s.E <= 32)
-            hipLaunchKernelGGL(logits_wave_kernel, dim3(g), dim3(256), 0, st, (const uint16_t *)x, Wr, bias,
-                               noise, s.T, s.d, s.E, p, lse);
-        else
-            hipLaunchKernelGGL(logits_kernel, dim3((unsigned)((s.T + LG_TB - 1) / LG_TB)), dim3(256), 0, st,
-                               (const uint16_t *)x, Wr, bias, noise, s.T, s.d, s.E, p, lse);
+        const dim3 gl((unsigned)((s.T + LG_TB - 1) / LG_TB));
+        if (s.dtype == 0) {
+            if (s.E <= 32)
+                hipLaunchKernelGGL(logits_wave_kernel<float>, dim3(g), dim3(256), 0, st, (const float *)x, Wr,
+                                   bias, noise, s.T, s.d, s.E, p, lse);
+            else
+                hipLaunchKernelGGL(logits_kernel<float>, gl, dim3(256), 0, st, (const float *)x, Wr, bias, noise,
+                                   s.T, s.d, s.E, p, lse);
+        } else {
+            if (s.E <= 32)
+                hipLaunchKernelGGL(logits_wave_kernel<uint16_t>, dim3(g), dim3(256), 0, st, (const uint16_t *)x,
+                                   Wr, bias, noise, s.T, s.d, s.E, p, lse);
+            else
+                hipLaunchKernelGGL(logits_kernel<uint16_t>, gl, dim3(256), 0, st, (const uint16_t *)x, Wr, bias,
+                                   noise, s.T, s.d, s.E, p, lse);
+        }
     }
     hipLaunchKernelGGL(router_bwd_kernel, dim3(g), dim3(256), 0, st, (const float *)p, (const float *)lse,
                        topk_idx, gates, dg, row_of_slot, f, s.T, s.E, s.k, s.gate, alpha_aux, alpha_z, dh);
@@ -779,8 +861,12 @@ size_t dwr_part_floats(const Shape &s) { return (size_t)DWR_SPLITS * s.E * s.d; 
 hipError_t launch_dwr(const Shape &s, const float *dh, const void *x, float *part, float *dWr,
                       float *dbias, hipStream_t st) {
     dim3 grid((unsigned)((s.d + 255) / 256), (unsigned)((s.E + DWR_EG - 1) / DWR_EG), DWR_SPLITS);
-    hipLaunchKernelGGL(dwr_partial_kernel, grid, dim3(256), 0, st, dh, (const uint16_t *)x, s.T, s.d, s.E,
-                       part);
+    if (s.dtype == 0)
+        hipLaunchKernelGGL(dwr_partial_kernel<float>, grid, dim3(256), 0, st, dh, (const float *)x, s.T, s.d,
+                           s.E, part);
+    else
+        hipLaunchKernelGGL(dwr_partial_kernel<uint16_t>, grid, dim3(256), 0, st, dh, (const uint16_t *)x, s.T,
+                           s.d, s.E, part);
     const int64_t n = (int64_t)s.E * s.d;
     hipLaunchKernelGGL(dwr_reduce_kernel, dim3(grid_for(n, 256, 4096)), dim3(256), 0, st, (const float *)part,
                        n, dWr);

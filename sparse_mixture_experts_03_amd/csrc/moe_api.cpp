@@ -637,12 +637,101 @@ int moe_forward_fp8(const moe_desc *desc, const void *x, const float *W_r, const
                         token_of_row, dropped, stats, ws, ws_bytes, stream);
 }
 
+// fp32 layers: the same steps as the bf16 backward with plain fp32 kernels
+// (weights transposed by launch_transpose_f32, expert GEMMs through the
+// forward's fp32 grouped GEMM, weight gradients by launch_wgrad_f32, the
+// router part by the same kernels on fp32 x).
+struct BwdLayoutF32 {
+    size_t w2t, wcat, x_perm, a1, a3, H, Y, dE, dg, dH, dA, dXp, p, lse, dh, dwr_part, total;
+};
+
+static BwdLayoutF32 bwd_layout_f32(const Shape &s) {
+    BwdLayoutF32 L{};
+    const size_t nup = s.act == MOE_ACT_SWIGLU ? 2 : 1;
+    const size_t E = (size_t)s.E, d = (size_t)s.d, f = (size_t)s.d_ff;
+    size_t r = (size_t)s.Tk();
+    if (s.C >= 0 && E * (size_t)s.C < r) r = E * (size_t)s.C;
+    size_t o = 0;
+    auto take = [&](size_t bytes) {
+        size_t at = o;
+        o = align_up(o + bytes);
+        return at;
+    };
+    L.w2t = take(E * f * d * 4);
+    L.wcat = take(E * d * nup * f * 4);
+    L.x_perm = take(r * d * 4);
+    L.a1 = take(r * f * 4);
+    L.a3 = nup == 2 ? take(r * f * 4) : 0;
+    L.H = take(r * f * 4);
+    L.Y = take(r * d * 4);
+    L.dE = take(r * d * 4);
+    L.dg = take((size_t)s.Tk() * 4);
+    L.dH = take(r * f * 4);
+    L.dA = take(r * nup * f * 4);
+    L.dXp = take(r * d * 4);
+    L.p = take((size_t)s.T * E * 4);
+    L.lse = take((size_t)s.T * 4);
+    L.dh = take((size_t)s.T * E * 4);
+    L.dwr_part = take(moe::dwr_part_floats(s) * 4);
+    L.total = o;
+    return L;
+}
+
+static int backward_f32(const Shape &s, const float *x, const float *W_r, const float *bias, const float *noise,
+                        const float *W1, const float *W3, const float *W2, const int32_t *topk_idx,
+                        const float *gates, const int32_t *offsets, const int32_t *row_of_slot,
+                        const int32_t *token_of_row, const float *stats, const float *dy, float alpha_aux,
+                        float alpha_z, float *dx, float *dW_r, float *dbias, float *dW1, float *dW3, float *dW2,
+                        void *ws, hipStream_t st) {
+    const BwdLayoutF32 L = bwd_layout_f32(s);
+    const bool swiglu = s.act == MOE_ACT_SWIGLU;
+    const int d = s.d, f = s.d_ff, E = s.E, nup = swiglu ? 2 : 1;
+    char *w = (char *)ws;
+    float *w2t = (float *)(w + L.w2t), *wcat = (float *)(w + L.wcat), *xp = (float *)(w + L.x_perm);
+    float *a1 = (float *)(w + L.a1), *a3 = swiglu ? (float *)(w + L.a3) : nullptr, *H = (float *)(w + L.H);
+    float *Y = (float *)(w + L.Y), *dE = (float *)(w + L.dE), *dg = (float *)(w + L.dg);
+    float *dH = (float *)(w + L.dH), *dA = (float *)(w + L.dA), *dXp = (float *)(w + L.dXp);
+    float *p = (float *)(w + L.p), *lse = (float *)(w + L.lse), *dh = (float *)(w + L.dh);
+    const int64_t df = (int64_t)d * f;
+    int rc;
+    // weights as [K][N] operands of the gradient GEMMs: W2 to [E][d_ff][d],
+    // W1 | W3 side by side to [E][d][n_up d_ff]
+    MOE_TRY(moe::launch_transpose_f32(W2, d, f, f, df, w2t, d, df, E, st));
+    MOE_TRY(moe::launch_transpose_f32(W1, f, d, d, df, wcat, (int64_t)nup * f, (int64_t)nup * df, E, st));
+    if (swiglu)
+        MOE_TRY(moe::launch_transpose_f32(W3, f, d, d, df, wcat + f, (int64_t)nup * f, (int64_t)nup * df, E, st));
+    // recompute the forward's expert part
+    MOE_TRY(moe::launch_gather(s, x, token_of_row, offsets, xp, st));
+    if ((rc = grouped_gemm_f32(s, f, d, xp, offsets, W1, a1, nullptr, st, nullptr)) != MOE_OK) return rc;
+    if (swiglu && (rc = grouped_gemm_f32(s, f, d, xp, offsets, W3, a3, nullptr, st, nullptr)) != MOE_OK) return rc;
+    MOE_TRY(moe::launch_act_fwd(s, a1, a3, offsets, H, st));
+    if ((rc = grouped_gemm_f32(s, d, f, H, offsets, W2, Y, nullptr, st, nullptr)) != MOE_OK) return rc;
+    // combine, down projection and activation backward; dX_perm
+    MOE_TRY(moe::launch_combine_bwd(s, dy, Y, token_of_row, row_of_slot, gates, offsets, dE, dg, st));
+    if ((rc = grouped_gemm_f32(s, f, d, dE, offsets, w2t, dH, nullptr, st, nullptr)) != MOE_OK) return rc;
+    MOE_TRY(moe::launch_act_bwd(s, a1, a3, dH, offsets, dA, st));
+    if ((rc = grouped_gemm_f32(s, d, nup * f, dA, offsets, wcat, dXp, nullptr, st, nullptr)) != MOE_OK) return rc;
+    // router: gates, load-balancing and z terms; dx, dW_r, dbias
+    MOE_TRY(moe::launch_router_bwd(s, x, W_r, bias, noise, topk_idx, gates, dg, row_of_slot, stats, alpha_aux,
+                                   alpha_z, p, lse, dh, st, true));
+    MOE_TRY(moe::launch_dx(s, dXp, row_of_slot, dh, W_r, dx, st));
+    MOE_TRY(moe::launch_dwr(s, dh, x, (float *)(w + L.dwr_part), dW_r, dbias, st));
+    // weight gradients over each expert's rows
+    MOE_TRY(moe::launch_wgrad_f32(E, d, f, offsets, dE, d, H, f, dW2, st));
+    MOE_TRY(moe::launch_wgrad_f32(E, f, d, offsets, dA, (int64_t)nup * f, xp, d, dW1, st));
+    if (swiglu) MOE_TRY(moe::launch_wgrad_f32(E, f, d, offsets, dA + f, (int64_t)nup * f, xp, d, dW3, st));
+    return MOE_OK;
+}
+
 int moe_backward_workspace_size(const moe_desc *desc, size_t *bytes) {
     Shape s;
     int rc = check_desc(desc, &s);
     if (rc != MOE_OK) return rc;
     if (!bytes) return MOE_ERR_INVALID_ARG;
-    if (s.dtype != MOE_DTYPE_BF16) return MOE_ERR_UNSUPPORTED;
+    if (s.dtype != MOE_DTYPE_BF16) {
+        *bytes = bwd_layout_f32(s).total;
+        return MOE_OK;
+    }
     const BwdLayout L = bwd_layout(s);
     if (L.ldk / 64 > 65535) return MOE_ERR_UNSUPPORTED;   // padded transposes' grid
     *bytes = L.total;
@@ -659,7 +748,6 @@ int moe_backward(const moe_desc *desc, const void *x, const float *W_r, const fl
     Shape s;
     int rc = check_desc(desc, &s);
     if (rc != MOE_OK) return rc;
-    if (s.dtype != MOE_DTYPE_BF16) return MOE_ERR_UNSUPPORTED;
     if (!x || !W_r || !W1 || !W2 || !topk_idx || !gates || !offsets || !row_of_slot ||
         !token_of_row || !stats || !dy || !dx || !dW_r || !dW1 || !dW2 || !ws)
         return MOE_ERR_INVALID_ARG;
@@ -667,6 +755,13 @@ int moe_backward(const moe_desc *desc, const void *x, const float *W_r, const fl
     if (swiglu != (W3 != nullptr) || swiglu != (dW3 != nullptr)) return MOE_ERR_INVALID_ARG;
     if (dbias && !bias) return MOE_ERR_INVALID_ARG;
     if (!std::isfinite(alpha_aux) || !std::isfinite(alpha_z)) return MOE_ERR_INVALID_ARG;
+    if (s.dtype != MOE_DTYPE_BF16) {
+        if (ws_bytes < bwd_layout_f32(s).total) return MOE_ERR_WORKSPACE;
+        return backward_f32(s, (const float *)x, W_r, bias, noise, (const float *)W1, (const float *)W3,
+                            (const float *)W2, topk_idx, gates, offsets, row_of_slot, token_of_row, stats,
+                            (const float *)dy, alpha_aux, alpha_z, dx, dW_r, dbias, dW1, dW3, dW2, ws,
+                            (hipStream_t)stream);
+    }
     const BwdLayout L = bwd_layout(s);
     // kept rows (rounded per expert to 64) past 65535 * 64: the padded
     // transposes' grid would not fit; rejected before any launch

@@ -181,6 +181,12 @@ hipError_t launch_expert_down_fp8(const Shape &s, const void *H, const int32_t *
 // ---- backward (training gradients) --------------------------------------
 hipError_t launch_transpose_bf16(const void *src, int64_t R, int64_t C, int64_t lds, int64_t sbs,
                                  void *dst, int64_t ldd, int64_t dbs, int batch, hipStream_t st);
+// fp32 layers' backward: batched transpose (dst[b][c][r] = src[b][r][c]) and
+// the per-expert weight gradients C[e][m][n] = sum over e's rows of P[r][m] Q[r][n]
+hipError_t launch_transpose_f32(const float *src, int64_t R, int64_t C, int64_t lds, int64_t sbs, float *dst,
+                                int64_t ldd, int64_t dbs, int batch, hipStream_t st);
+hipError_t launch_wgrad_f32(int E, int M, int N, const int32_t *offsets, const float *P, int64_t ldp,
+                            const float *Q, int64_t ldq, float *C, hipStream_t st);
 hipError_t launch_act_fwd(const Shape &s, const float *a1, const float *a3, const int32_t *offsets,
                           void *H, hipStream_t st);
 hipError_t launch_combine_bwd(const Shape &s, const void *dy, const float *Y, const int32_t *token_of_row,
@@ -334,19 +340,26 @@ __device__ __forceinline__ float apply_act(int act, float a1, float a3) {
 // Activation backward of one element: u = a1, v = a3 (SwiGLU), g = dH; da1
 // and (SwiGLU) da3 as bf16 bits.  SwiGLU: H = silu(u) v; GELU (erf form);
 // ReLU (derivative 0 at u = 0).
-__device__ __forceinline__ void act_bwd_elem(int act, float u, float v, float g, uint16_t &da1,
-                                             uint16_t &da3) {
+__device__ __forceinline__ void act_bwd_f32(int act, float u, float v, float g, float &da1, float &da3) {
+    da3 = 0.f;
     if (act == ACT_SWIGLU) {
         const float sg = 1.f / (1.f + expf(-u));
-        da1 = f32_to_bf16(g * v * sg * (1.f + u * (1.f - sg)));
-        da3 = f32_to_bf16(g * u * sg);
+        da1 = g * v * sg * (1.f + u * (1.f - sg));
+        da3 = g * u * sg;
     } else if (act == ACT_GELU) {
         const float Phi = 0.5f * (1.f + erff(u * 0.70710678118654752f));
         const float phi = expf(-0.5f * u * u) * 0.39894228040143268f;
-        da1 = f32_to_bf16(g * (Phi + u * phi));
+        da1 = g * (Phi + u * phi);
     } else {
-        da1 = f32_to_bf16(u > 0.f ? g : 0.f);
+        da1 = u > 0.f ? g : 0.f;
     }
+}
+__device__ __forceinline__ void act_bwd_elem(int act, float u, float v, float g, uint16_t &da1,
+                                             uint16_t &da3) {
+    float a, b;
+    act_bwd_f32(act, u, v, g, a, b);
+    da1 = f32_to_bf16(a);
+    if (act == ACT_SWIGLU) da3 = f32_to_bf16(b);
 }
 
 }  // namespace moe

@@ -257,10 +257,15 @@ def test_backward_validation_before_launch():
     o = list(outs)
     o[2] = FAKE              # dbias without a bias
     assert call(args, o, need) == -1
+    # fp32 layers: their own workspace, the same argument checks
     f32 = B.make_desc(64, 32, 64, 4, 2, act="swiglu", dtype="f32")
-    assert lib.moe_backward(ctypes.byref(f32), *args, 0.0, 0.0, *outs, FAKE, need, None) == -2
-    with pytest.raises(B.MoeError):
-        B.moe_backward_workspace_size(f32)
+    need32 = B.moe_backward_workspace_size(f32)
+    assert need32 > 0
+    d32 = ctypes.byref(f32)
+    assert lib.moe_backward(d32, *args, 0.0, 0.0, *outs, FAKE, need32 - 1, None) == -4
+    a = list(args)
+    a[0] = None
+    assert lib.moe_backward(d32, *a, 0.0, 0.0, *outs, FAKE, need32, None) == -1
 
 
 def test_backward_rejects_too_many_rows_before_launch():

@@ -5,7 +5,7 @@ hand-picked cases (routing bit-exact, statistics, y within tolerance,
 fully dropped tokens exactly zero); likewise with 1-3 shared experts and
 the residual, with e4m3 expert weights (decode-sized batches, codes and
 scales bit-exact), and for the backward (every gradient within 2e-2 of
-its largest reference value).  The draws are fixed (seed 2024), so a
+its largest reference value for bf16 layers, 1e-5 for fp32 ones).  The draws are fixed (seed 2024), so a
 failure names its case."""
 import numpy as np
 import pytest
@@ -81,9 +81,20 @@ def _draw_bwd(i):
                           "bf16", noise_std=float(rng.choice([0.0, 0.1])))
 
 
+def _draw_bwd_f32(i):
+    # fp32 layers through the backward: any width
+    rng = np.random.default_rng([2024, 600 + i])
+    E = int(rng.choice([1, 3, 6, 16, 40]))
+    return synth.Workload(f"rand_bw32_{i}", int(rng.choice([1, 9, 64, 100, 257])),
+                          int(rng.integers(1, 97)), int(rng.integers(1, 161)), E,
+                          int(rng.integers(1, min(E, 3) + 1)), str(rng.choice(["renorm", "switch"])),
+                          float(rng.choice([0.0, 0.5, 1.25])), str(rng.choice(["swiglu", "gelu", "relu"])),
+                          "f32", noise_std=float(rng.choice([0.0, 0.1])))
+
+
 SHARED_CASES = [_draw_shared(i) for i in range(8)]
 FP8_CASES = [_draw_fp8(i) for i in range(10)]
-BWD_CASES = [_draw_bwd(i) for i in range(10)]
+BWD_CASES = [_draw_bwd(i) for i in range(10)] + [_draw_bwd_f32(i) for i in range(6)]
 
 
 def _ids(w):
@@ -124,4 +135,4 @@ def test_random_shape_backward_matches_oracle(w):
 
     print(f"[rand bwd] {w}", flush=True)
     got, ref, _ = _run(w)
-    _check(got, ref)
+    _check(got, ref, 2e-2 if w.dtype == "bf16" else 1e-5)
