@@ -34,8 +34,8 @@
 // Per-token epilogue (one token per group of 8 or 16 lanes, E <= 128
 // logits in registers: for E > 16 lane c of a 16-lane row holds experts c,
 // c + 16, ...): max and sum of exponentials by DPP reductions within the
-// group, top-k by k arg-max reductions over 64-bit keys (orderable
-// logit bits, then the complement of the index, so a tie goes to the lower
+// group, top-k by k rounds of two reductions on orderable logit bits (the
+// largest key, then the lowest index holding it, so a tie goes to the lower
 // index), gates, and per-block partials: sums of p and counts of top
 // choices (per expert) and the sum of lse^2, in a fixed order.
 // route_stats_kernel reduces the partials in double in a fixed order.
@@ -69,32 +69,33 @@ __device__ __forceinline__ float unord_f32(uint32_t o) {
     return __uint_as_float((o & 0x80000000u) ? (o & 0x7fffffffu) : ~o);
 }
 
+// Exponential, logarithm and reciprocal on the hardware's transcendental
+// unit (v_exp_f32 = 2^x, v_log_f32 = log2 x, v_rcp_f32): about 1e-6
+// relative error on the epilogue's arguments (the rounding of x * log2 e
+// dominates), which no routing decision depends on -- the choices compare
+// the logits themselves.
+__device__ __forceinline__ float exp_hw(float x) { return __builtin_amdgcn_exp2f(x * 1.44269504088896341f); }
+__device__ __forceinline__ float log_hw(float x) { return __builtin_amdgcn_logf(x) * 0.693147180559945309f; }
+__device__ __forceinline__ float rcp_hw(float x) { return __builtin_amdgcn_rcpf(x); }
+
 // Reductions within groups of G = 8 or 16 lanes (one token per group) on
 // the VALU's cross-lane moves (DPP) instead of LDS permutes: swap
 // neighbours (quad_perm 1,0,3,2), pairs (2,3,0,1), then mirror the
 // half-rows and (G = 16) the row, so that every lane of the group holds the
 // group's result, bit for bit the same on every lane (each step combines two
 // equal-shaped partial results commutatively).  DPP control codes: quad_perm
-// 0xB1 and 0x4E, row_half_mirror 0x141, row_mirror 0x140.
+// 0xB1 and 0x4E, row_half_mirror 0x141, row_mirror 0x140.  Maxima and
+// minima run on unsigned integers (ordered logit keys, expert indices),
+// where the move folds into the max/min instruction.
 template <int CTRL>
 __device__ __forceinline__ float dpp_f32(float v) {
     return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
 }
 template <int CTRL>
-__device__ __forceinline__ unsigned long long dpp_u64(unsigned long long v) {
-    const int lo = __builtin_amdgcn_mov_dpp((int)(uint32_t)v, CTRL, 0xF, 0xF, false);
-    const int hi = __builtin_amdgcn_mov_dpp((int)(uint32_t)(v >> 32), CTRL, 0xF, 0xF, false);
-    return ((unsigned long long)(uint32_t)hi << 32) | (uint32_t)lo;
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, true);
 }
 
-template <int G>
-__device__ __forceinline__ float group_max(float v) {
-    v = fmaxf(v, dpp_f32<0xB1>(v));
-    v = fmaxf(v, dpp_f32<0x4E>(v));
-    v = fmaxf(v, dpp_f32<0x141>(v));
-    if (G == 16) v = fmaxf(v, dpp_f32<0x140>(v));
-    return v;
-}
 template <int G>
 __device__ __forceinline__ float group_sum(float v) {
     v += dpp_f32<0xB1>(v);
@@ -104,20 +105,27 @@ __device__ __forceinline__ float group_sum(float v) {
     return v;
 }
 template <int G>
-__device__ __forceinline__ unsigned long long group_max_u64(unsigned long long v) {
-    unsigned long long w;
-    w = dpp_u64<0xB1>(v);
-    v = w > v ? w : v;
-    w = dpp_u64<0x4E>(v);
-    v = w > v ? w : v;
-    w = dpp_u64<0x141>(v);
-    v = w > v ? w : v;
-    if (G == 16) {
-        w = dpp_u64<0x140>(v);
-        v = w > v ? w : v;
-    }
+__device__ __forceinline__ uint32_t group_max_u32(uint32_t v) {
+    v = max(v, dpp_u32<0xB1>(v));
+    v = max(v, dpp_u32<0x4E>(v));
+    v = max(v, dpp_u32<0x141>(v));
+    if (G == 16) v = max(v, dpp_u32<0x140>(v));
     return v;
 }
+template <int G>
+__device__ __forceinline__ uint32_t group_min_u32(uint32_t v) {
+    v = min(v, dpp_u32<0xB1>(v));
+    v = min(v, dpp_u32<0x4E>(v));
+    v = min(v, dpp_u32<0x141>(v));
+    if (G == 16) v = min(v, dpp_u32<0x140>(v));
+    return v;
+}
+
+// Top-k over ordered keys: each round takes the group's largest key, then
+// the lowest expert index holding it (so a tie goes to the lower index, and
+// -0 ties with +0, which share a key), and clears that key.  A padding
+// expert or a taken one has key 0, below every logit's, so with k <= E a
+// real expert always wins.
 
 // softmax_topk_block for E <= G: lane l serves expert l % G of token
 // l / G of the wave's current group of 64 / G tokens, so a wave takes 8
@@ -144,35 +152,34 @@ __device__ void softmax_topk_grouped(const float (*hl)[RT_EMAX + 1], int t0, int
         const int r = r0 + g, t = t0 + r;
         const bool vt = r < TILE && t < T;
         const bool v = ve && vt;
-        const float h = v ? hl[r][e] : -INFINITY;
-        const float m = group_max<G>(h);
-        const float x = v ? expf(h - m) : 0.f;
+        const float h = v ? hl[r][e] : 0.f;
+        uint32_t key = v ? ord_f32(h) : 0u;
+        const float m = unord_f32(group_max_u32<G>(key));
+        const float x = v ? exp_hw(h - m) : 0.f;
         const float s = group_sum<G>(x);
-        const float inv = 1.f / s;
+        const float inv = rcp_hw(s);
         if (v) psum += x * inv;
-        const float lse = m + logf(s);
+        const float lse = m + log_hw(s);
         if (vt && e == 0) lsum += lse * lse;
-        unsigned long long key = v ? ((unsigned long long)ord_f32(h) << 32) | (0xffffffffu - (uint32_t)e) : 0ull;
         float h_top = 0.f, den = 0.f, my_hb = 0.f;
         int my_bi = 0;
         for (int sl = 0; sl < k; ++sl) {
-            const unsigned long long best = group_max_u64<G>(key);
-            int bi = (int)(0xffffffffu - (uint32_t)(best & 0xffffffffull));
-            bi = bi < 0 ? 0 : bi;  // only for a token past T (its key is 0)
-            if (bi == e) key = 0ull;
-            const float hb = vt ? unord_f32((uint32_t)(best >> 32)) : 0.f;   // the key holds the logit
+            const uint32_t b = group_max_u32<G>(key);
+            const uint32_t bi = group_min_u32<G>(key == b ? (uint32_t)e : 0xffffffffu);
+            if ((uint32_t)e == bi) key = 0u;
+            const float hb = unord_f32(b);   // the key holds the logit
             if (sl == 0) {
                 h_top = hb;
-                if (vt && e == 0) topchg[r] = bi;
+                if (vt && e == 0) topchg[r] = (int)bi;
             }
-            den += expf(hb - h_top);  // slot order, identical on the token's lanes
+            den += exp_hw(hb - h_top);  // slot order, identical on the token's lanes
             if (e == sl) {
                 my_hb = hb;
-                my_bi = bi;
+                my_bi = (int)bi;
             }
         }
         if (vt && e < k) {
-            const float gt = gate_switch ? expf(my_hb - m) * inv : expf(my_hb - h_top) / den;
+            const float gt = gate_switch ? exp_hw(my_hb - m) * inv : exp_hw(my_hb - h_top) * rcp_hw(den);
             topk_idx[(int64_t)t * k + e] = my_bi;
             if (topk_sh) topk_sh[t * k + e] = my_bi;  // LDS copy (small batches)
             gates[(int64_t)t * k + e] = gt;
@@ -208,9 +215,10 @@ __device__ void softmax_topk_grouped(const float (*hl)[RT_EMAX + 1], int t0, int
 // lane c of a row holding experts c, c + 16, ..., c + 16 (V - 1), so a wave
 // serves 4 tokens at once and every reduction stays within a row (DPP
 // moves only: no readlane, no LDS).  Each lane first reduces its V values
-// (max, sum in v order, largest key), then the row.  Selected slot s is
-// kept by lane s % 16 of the row, in its register s / 16.  Partials: per
-// expert, the waves' row sums added in (wave, row) order.
+// (max, sum in v order, largest key, lowest index), then the row.
+// Selected slot s is kept by lane s % 16 of the row, in its register
+// s / 16 (one register when k <= 16).  Partials: per expert, the waves'
+// row sums added in (wave, row) order.
 template <int V, int TILE, int NW>
 __device__ __forceinline__ void softmax_topk_rows(const float (*hl)[RT_EMAX + 1], int t0, int T, int E, int k,
                                                   int gate_switch, int32_t *__restrict__ topk_idx,
@@ -231,81 +239,93 @@ __device__ __forceinline__ void softmax_topk_rows(const float (*hl)[RT_EMAX + 1]
         const int r = r0 + g, t = t0 + r;
         const bool vt = r < TILE && t < T;
         float h[V];
+        uint32_t key[V];
         bool ve[V];
 #pragma unroll
         for (int v = 0; v < V; ++v) {
             ve[v] = c + 16 * v < E;
             // a row past the batch holds no token: finite stand-ins, nothing stored
-            h[v] = ve[v] ? (vt ? hl[r][c + 16 * v] : 0.f) : -INFINITY;
+            h[v] = ve[v] && vt ? hl[r][c + 16 * v] : 0.f;
+            key[v] = ve[v] ? ord_f32(h[v]) : 0u;
         }
-        float mx = h[0];
+        uint32_t km = key[0];
 #pragma unroll
-        for (int v = 1; v < V; ++v) mx = fmaxf(mx, h[v]);
-        mx = group_max<16>(mx);
+        for (int v = 1; v < V; ++v) km = max(km, key[v]);
+        const float mx = unord_f32(group_max_u32<16>(km));
         float xv[V], sl = 0.f;
 #pragma unroll
         for (int v = 0; v < V; ++v) {
-            xv[v] = ve[v] ? expf(h[v] - mx) : 0.f;
+            xv[v] = ve[v] ? exp_hw(h[v] - mx) : 0.f;
             sl += xv[v];
         }
         const float sm = group_sum<16>(sl);
-        const float inv = 1.f / sm;
+        const float inv = rcp_hw(sm);
         if (vt) {
 #pragma unroll
             for (int v = 0; v < V; ++v) psum[v] += xv[v] * inv;
-            const float lse = mx + logf(sm);
+            const float lse = mx + log_hw(sm);
             lsum += lse * lse;
         }
-        unsigned long long key[V];
+        // NS slot registers per lane: 1 when k <= 16, else V
+        auto select = [&](auto ns_c) {
+            constexpr int NS = decltype(ns_c)::value;
+            float sh[NS];
+            int si[NS];
 #pragma unroll
-        for (int v = 0; v < V; ++v)
-            key[v] = ve[v] ? ((unsigned long long)ord_f32(h[v]) << 32) | (0xffffffffu - (uint32_t)(c + 16 * v))
-                           : 0ull;
-        float h_top = 0.f, den = 0.f, sh[V];
-        int si[V];
-#pragma unroll
-        for (int v = 0; v < V; ++v) {
-            sh[v] = 0.f;
-            si[v] = 0;
-        }
-        for (int s = 0; s < k; ++s) {
-            unsigned long long b = key[0];
-#pragma unroll
-            for (int v = 1; v < V; ++v) b = key[v] > b ? key[v] : b;
-            b = group_max_u64<16>(b);
-            int bi = (int)(0xffffffffu - (uint32_t)(b & 0xffffffffull));
-            bi = bi < 0 ? 0 : bi;   // unreachable while k <= E (validated on the host)
-#pragma unroll
-            for (int v = 0; v < V; ++v)
-                if (c + 16 * v == bi) key[v] = 0ull;
-            // the chosen logit is in the key itself (no LDS read on the chain)
-            const float hb = vt ? unord_f32((uint32_t)(b >> 32)) : 0.f;
-            if (s == 0) {
-                h_top = hb;
-                if (c == 0 && vt) topcr[r] = bi;
+            for (int q = 0; q < NS; ++q) {
+                sh[q] = 0.f;
+                si[q] = 0;
             }
-            den += expf(hb - h_top);   // slot order, identical on the row's lanes
-            if (c == (s & 15)) {
+            float h_top = 0.f, den = 0.f;
+            for (int s = 0; s < k; ++s) {
+                uint32_t b = key[0];
 #pragma unroll
-                for (int v = 0; v < V; ++v)
-                    if (v == (s >> 4)) {
-                        sh[v] = hb;
-                        si[v] = bi;
+                for (int v = 1; v < V; ++v) b = max(b, key[v]);
+                b = group_max_u32<16>(b);
+                uint32_t cand = 0xffffffffu;
+#pragma unroll
+                for (int v = V - 1; v >= 0; --v) cand = key[v] == b ? (uint32_t)(c + 16 * v) : cand;
+                const uint32_t bi = group_min_u32<16>(cand);
+#pragma unroll
+                for (int v = 0; v < V; ++v) key[v] = (uint32_t)(c + 16 * v) == bi ? 0u : key[v];
+                const float hb = unord_f32(b);   // the key holds the logit
+                if (s == 0) {
+                    h_top = hb;
+                    if (c == 0 && vt) topcr[r] = (int)bi;
+                }
+                den += exp_hw(hb - h_top);   // slot order, identical on the row's lanes
+                if (NS == 1) {
+                    if (c == s) {
+                        sh[0] = hb;
+                        si[0] = (int)bi;
                     }
-            }
-        }
-        if (vt) {
+                } else if (c == (s & 15)) {
 #pragma unroll
-            for (int v = 0; v < V; ++v) {
-                const int s = c + 16 * v;
-                if (s < k) {
-                    const float gt = gate_switch ? expf(sh[v] - mx) * inv : expf(sh[v] - h_top) / den;
-                    topk_idx[(int64_t)t * k + s] = si[v];
-                    if (topk_sh) topk_sh[t * k + s] = si[v];   // LDS copy (small batches)
-                    gates[(int64_t)t * k + s] = gt;
+                    for (int q = 0; q < NS; ++q)
+                        if (q == (s >> 4)) {
+                            sh[q] = hb;
+                            si[q] = (int)bi;
+                        }
                 }
             }
-        }
+            if (vt) {
+                const float rden = rcp_hw(den);
+#pragma unroll
+                for (int q = 0; q < NS; ++q) {
+                    const int s = c + 16 * q;
+                    if (s < k) {
+                        const float gt = gate_switch ? exp_hw(sh[q] - mx) * inv : exp_hw(sh[q] - h_top) * rden;
+                        topk_idx[(int64_t)t * k + s] = si[q];
+                        if (topk_sh) topk_sh[t * k + s] = si[q];   // LDS copy (small batches)
+                        gates[(int64_t)t * k + s] = gt;
+                    }
+                }
+            }
+        };
+        if (k <= 16)
+            select(std::integral_constant<int, 1>{});
+        else
+            select(std::integral_constant<int, V>{});
     }
     if (w < NW) {
 #pragma unroll
