@@ -654,13 +654,15 @@ __global__ __launch_bounds__(256) void router_wsplit_kernel(const float *__restr
 // on v_mfma_f32_16x16x32_bf16, so a logit is an fp32 sum of exact products
 // of x with W_r's 24 significant bits.
 //
-// Five waves.  Wave 4 only loads x: 64-wide k stages of the tile go from
+// NCW + 1 waves.  Wave NCW only loads x: 64-wide k stages of the tile go from
 // global memory straight into an LDS ring of NBUF stages (buffer loads to
 // LDS, no registers), NBUF - 1 stages ahead; before each block barrier it
 // waits until the next stage has landed.  Its loads are the only ones in
 // its own in-order return queue, so the compute waves' loads never wait
-// behind them.  Waves 0..3 each own NG groups of 16 experts (all three
-// terms): they load their weight fragments from L2 straight into registers
+// behind them.  Compute waves 0 .. NCW - 1 (8 for 128 experts and tiles
+// of 32 or 64 tokens, two per SIMD, so that one computes while the other
+// waits; else 4) each own NG =
+// E_PAD / (16 NCW) groups of 16 experts (all three terms): they load their weight fragments from L2 straight into registers
 // PW - 1 stages ahead (a ring of PW register slots, the stage loop unrolled
 // by PW) and multiply them with the tile's x fragments read from the ring.
 // MFMA step j in {0, 1} of a stage covers k 32j .. 32j + 31, lane group
@@ -671,23 +673,23 @@ __global__ __launch_bounds__(256) void router_wsplit_kernel(const float *__restr
 // banks (the loader fetches chunk (lane % 8) ^ f(row) into slot lane % 8).
 //
 // After the last stage the ring becomes the logit tile: bias and noise
-// are added, and all five waves run the shared per-token epilogue; the
+// are added, and the compute waves run the shared per-token epilogue; the
 // statistic partials are indexed by tile.
-template <int E_PAD, int BT, int PW>
-__global__ __launch_bounds__(320) void route_fused_kernel(
+template <int E_PAD, int BT, int PW, int NCW>
+__global__ __launch_bounds__(64 * (NCW + 1)) void route_fused_kernel(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ wsplit, const float *__restrict__ bias,
     const float *__restrict__ noise, int T, int d, int E, int k, int gate_switch,
     int32_t *__restrict__ topk_idx, float *__restrict__ gates, float *__restrict__ part_P,
     float *__restrict__ part_lse2, unsigned *__restrict__ arrivals) {
 #if defined(__HIP_DEVICE_COMPILE__)
-    constexpr int NG = E_PAD / 64;              // 16-expert groups per compute wave
+    constexpr int NG = E_PAD / (16 * NCW);      // 16-expert groups per compute wave
     constexpr int TM = BT / 16;                 // 16-token fragments
     constexpr int NBUF = BT == 64 ? 8 : 16;     // x stages in the ring
     constexpr int LPS = BT / 8;                 // loader instructions per stage (8 rows each)
     constexpr int SB = BT * 128;                // bytes per stage
     constexpr int RING = NBUF * SB;
     constexpr int HLB = BT * (RT_EMAX + 1) * 4;
-    static_assert(NG >= 1 && TM >= 1 && (NBUF - 2) * LPS <= 63, "tile shape");
+    static_assert(NG >= 1 && NG * 16 * NCW == E_PAD && TM >= 1 && (NBUF - 2) * LPS <= 63, "tile shape");
     __shared__ __attribute__((aligned(1024))) char lds[RING > HLB ? RING : HLB];
     float(*hl)[RT_EMAX + 1] = (float(*)[RT_EMAX + 1])lds;
 
@@ -703,7 +705,7 @@ __global__ __launch_bounds__(320) void route_fused_kernel(
 #pragma unroll
         for (int gi = 0; gi < NG; ++gi) acc[i][gi] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    if (wave == 4) {
+    if (wave == NCW) {
         // the loader: rows past the batch read its last token (their logits
         // are never used); offsets from the tile's first row
         const __amdgpu_buffer_rsrc_t rsrc =
@@ -810,7 +812,7 @@ __global__ __launch_bounds__(320) void route_fused_kernel(
 
     // accumulator r of lane l (compute waves): token i * 16 + 4 g + r, expert
     // (wave * NG + gi) * 16 + lr
-    if (wave < 4) {
+    if (wave < NCW) {
         // every bias and noise load of the lane is issued before the first
         // add (clamped indices, so none is conditional): one memory round
         // trip instead of one per logit
@@ -843,9 +845,8 @@ __global__ __launch_bounds__(320) void route_fused_kernel(
     }
     __syncthreads();
     // E_PAD / 16 logits per lane cover every E of this padding (E > E_PAD / 2).
-    // Waves 0..3, one per SIMD, take the tokens; the loader wave would
-    // share a SIMD with wave 0.
-    softmax_topk_rows<E_PAD / 16, BT, 4>(hl, t0, T, E, k, gate_switch, topk_idx, gates, part_P, part_lse2,
+    // The compute waves take the tokens.
+    softmax_topk_rows<E_PAD / 16, BT, NCW>(hl, t0, T, E, k, gate_switch, topk_idx, gates, part_P, part_lse2,
                                          nullptr, nullptr, nullptr, tile, gridDim.x);
 #endif
 }
@@ -1114,7 +1115,9 @@ template <int E_PAD, int BT>
 void launch_fused(const Shape &s, const void *x, const uint16_t *wm, const float *bias, const float *noise,
                   int32_t *topk_idx, float *gates, float *part_P, float *part_lse2, unsigned *arrivals,
                   hipStream_t st) {
-    hipLaunchKernelGGL((route_fused_kernel<E_PAD, BT, 4>), dim3((unsigned)route_fused_ntiles(s)), dim3(320), 0,
+    constexpr int NCW = E_PAD == 128 && BT >= 32 ? 8 : 4;
+    hipLaunchKernelGGL((route_fused_kernel<E_PAD, BT, 2, NCW>), dim3((unsigned)route_fused_ntiles(s)),
+                       dim3(64 * (NCW + 1)), 0,
                        st, (const uint16_t *)x, wm, bias, noise, s.T, s.d, s.E, s.k, s.gate, topk_idx, gates,
                        part_P, part_lse2, arrivals);
 }
