@@ -16,6 +16,11 @@
 // lse^2 partials.  The last of the E + 1 blocks to finish (an integer
 // arrival counter, zeroed by the route kernel before) adds the f_e P_e in
 // expert order for aux, writes aux and z, and re-zeroes the counter.
+// The f_e P_e values (and z) pass between blocks through agent-scope
+// atomic stores and loads, which are coherent across the XCDs' L2 caches
+// without writing them back or invalidating them (a fence per block did
+// both, and held up the loads of every kernel block beside them); each
+// block waits for its store to complete before it counts its arrival.
 // Every thread of the block must call it.
 #pragma once
 
@@ -55,7 +60,7 @@ __device__ __forceinline__ void route_stats_block(int e, const float *__restrict
         double z = 0.0;
         for (int b = tid; b < nblk; b += 256) z += (double)part_lse2[b];
         z = block_sum_fixed(z, red);
-        if (tid == 0) fP[E] = z / (double)T;
+        if (tid == 0) __hip_atomic_store(fP + E, z / (double)T, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     } else {
         // expert e's block partials are contiguous: p sums, then top-choice
         // counts
@@ -76,18 +81,17 @@ __device__ __forceinline__ void route_stats_block(int e, const float *__restrict
             const double f = (double)(cnt[0] + cnt[1] + cnt[2] + cnt[3]) / (double)T;
             stats[e] = (float)f;
             stats[E + e] = (float)P;
-            fP[e] = f * P;
+            __hip_atomic_store(fP + e, f * P, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
     }
     if (tid == 0) {
-        __threadfence();
-        last = atomicAdd(arrivals, 1u) == (unsigned)E;
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the store above has completed
+        last = __hip_atomic_fetch_add(arrivals, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (unsigned)E;
     }
     __syncthreads();
     if (last) {
-        // every block's f_e P_e (and z) is visible: all threads load them
-        // at once, thread 0 adds them in expert order
-        __threadfence();
+        // every block's f_e P_e (and z) has been stored: all threads load
+        // them at once, thread 0 adds them in expert order
         for (int i = tid; i <= E; i += 256)
             red[i] = __hip_atomic_load(fP + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         __syncthreads();
