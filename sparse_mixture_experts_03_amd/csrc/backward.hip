@@ -72,11 +72,15 @@ __device__ __forceinline__ void st_elem(float *p, int64_t i, float v) { p[i] = v
 // dst[b][c][r] = src[b][r][c] for r < R, c < C (bf16); strides in elements.
 // VEC: 4-element (8-byte) reads along c and writes along r (C, R, the
 // strides and the bases multiples of 4); otherwise one element at a time.
+// With row offsets, matrix b is skipped when expert b has no rows: nothing
+// reads its transposed weights then (skewed routing leaves most experts of
+// a fine-grained layer without rows).
 template <bool VEC>
 __global__ __launch_bounds__(256) void transpose_kernel(const uint16_t *__restrict__ src, int64_t R,
                                                         int64_t C, int64_t lds, int64_t sbs,
                                                         uint16_t *__restrict__ dst, int64_t ldd,
-                                                        int64_t dbs) {
+                                                        int64_t dbs, const int32_t *__restrict__ offsets) {
+    if (offsets && offsets[blockIdx.z + 1] == offsets[blockIdx.z]) return;   // uniform in the block
     __shared__ uint16_t tile[64][66];
     const int64_t c0 = (int64_t)blockIdx.x * 64, r0 = (int64_t)blockIdx.y * 64;
     const uint16_t *s = src + (int64_t)blockIdx.z * sbs;
@@ -705,10 +709,12 @@ inline unsigned grid_for(int64_t items, int64_t per_block, int64_t cap) {
 // dst[b][c][r] = src[b][r][c] for r < R, c < C; strides in elements
 __global__ __launch_bounds__(256) void transpose_f32_kernel(const float *__restrict__ src, int64_t R, int64_t C,
                                                             int64_t lds, int64_t sbs, float *__restrict__ dst,
-                                                            int64_t ldd, int64_t dbs, int batch) {
+                                                            int64_t ldd, int64_t dbs, int batch,
+                                                            const int32_t *__restrict__ offsets) {
     const int64_t n = (int64_t)batch * R * C;
     for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
         const int64_t b = i / (R * C), rc = i - b * R * C, r = rc / C, c = rc - r * C;
+        if (offsets && offsets[b + 1] == offsets[b]) continue;   // an expert without rows
         dst[b * dbs + c * ldd + r] = src[b * sbs + r * lds + c];
     }
 }
@@ -731,17 +737,18 @@ __global__ __launch_bounds__(256) void wgrad_f32_kernel(int E, int M, int N, con
 }  // namespace
 
 hipError_t launch_transpose_bf16(const void *src, int64_t R, int64_t C, int64_t lds, int64_t sbs,
-                                 void *dst, int64_t ldd, int64_t dbs, int batch, hipStream_t st) {
+                                 void *dst, int64_t ldd, int64_t dbs, int batch, hipStream_t st,
+                                 const int32_t *offsets) {
     if (R <= 0 || C <= 0 || batch <= 0) return hipSuccess;
     dim3 grid((unsigned)((C + 63) / 64), (unsigned)((R + 63) / 64), (unsigned)batch);
     const bool vec = R % 4 == 0 && C % 4 == 0 && lds % 4 == 0 && ldd % 4 == 0 && sbs % 4 == 0 &&
                      dbs % 4 == 0 && (uintptr_t)src % 8 == 0 && (uintptr_t)dst % 8 == 0;
     if (vec)
         hipLaunchKernelGGL(transpose_kernel<true>, grid, dim3(256), 0, st, (const uint16_t *)src, R, C, lds,
-                           sbs, (uint16_t *)dst, ldd, dbs);
+                           sbs, (uint16_t *)dst, ldd, dbs, offsets);
     else
         hipLaunchKernelGGL(transpose_kernel<false>, grid, dim3(256), 0, st, (const uint16_t *)src, R, C, lds,
-                           sbs, (uint16_t *)dst, ldd, dbs);
+                           sbs, (uint16_t *)dst, ldd, dbs, offsets);
     return hipGetLastError();
 }
 
@@ -806,10 +813,10 @@ hipError_t launch_act_bwd(const Shape &s, const float *a1, const float *a3, cons
 }
 
 hipError_t launch_transpose_f32(const float *src, int64_t R, int64_t C, int64_t lds, int64_t sbs, float *dst,
-                                int64_t ldd, int64_t dbs, int batch, hipStream_t st) {
+                                int64_t ldd, int64_t dbs, int batch, hipStream_t st, const int32_t *offsets) {
     if (R <= 0 || C <= 0 || batch <= 0) return hipSuccess;
     hipLaunchKernelGGL(transpose_f32_kernel, dim3(grid_for((int64_t)batch * R * C, 256, 16384)), dim3(256), 0,
-                       st, src, R, C, lds, sbs, dst, ldd, dbs, batch);
+                       st, src, R, C, lds, sbs, dst, ldd, dbs, batch, offsets);
     return hipGetLastError();
 }
 

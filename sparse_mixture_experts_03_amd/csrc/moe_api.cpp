@@ -696,10 +696,11 @@ static int backward_f32(const Shape &s, const float *x, const float *W_r, const 
     int rc;
     // weights as [K][N] operands of the gradient GEMMs: W2 to [E][d_ff][d],
     // W1 | W3 side by side to [E][d][n_up d_ff]
-    MOE_TRY(moe::launch_transpose_f32(W2, d, f, f, df, w2t, d, df, E, st));
-    MOE_TRY(moe::launch_transpose_f32(W1, f, d, d, df, wcat, (int64_t)nup * f, (int64_t)nup * df, E, st));
+    MOE_TRY(moe::launch_transpose_f32(W2, d, f, f, df, w2t, d, df, E, st, offsets));
+    MOE_TRY(moe::launch_transpose_f32(W1, f, d, d, df, wcat, (int64_t)nup * f, (int64_t)nup * df, E, st, offsets));
     if (swiglu)
-        MOE_TRY(moe::launch_transpose_f32(W3, f, d, d, df, wcat + f, (int64_t)nup * f, (int64_t)nup * df, E, st));
+        MOE_TRY(moe::launch_transpose_f32(W3, f, d, d, df, wcat + f, (int64_t)nup * f, (int64_t)nup * df, E, st,
+                                          offsets));
     // recompute the forward's expert part
     MOE_TRY(moe::launch_gather(s, x, token_of_row, offsets, xp, st));
     if ((rc = grouped_gemm_f32(s, f, d, xp, offsets, W1, a1, nullptr, st, nullptr)) != MOE_OK) return rc;
@@ -779,12 +780,13 @@ int moe_backward(const moe_desc *desc, const void *x, const float *W_r, const fl
     float *p = (float *)(w + L.p), *lse = (float *)(w + L.lse), *dh = (float *)(w + L.dh);
     const int64_t df = (int64_t)d * f;
 
-    // weights as K-contiguous operands of the gradient GEMMs
-    MOE_TRY(moe::launch_transpose_bf16(W2, d, f, f, df, w2t, d, df, E, st));
-    MOE_TRY(moe::launch_transpose_bf16(W1, f, d, d, df, wcat, (int64_t)nup * f, (int64_t)nup * df, E, st));
+    // weights as K-contiguous operands of the gradient GEMMs (experts
+    // without rows skipped: no GEMM reads their transposed weights)
+    MOE_TRY(moe::launch_transpose_bf16(W2, d, f, f, df, w2t, d, df, E, st, offsets));
+    MOE_TRY(moe::launch_transpose_bf16(W1, f, d, d, df, wcat, (int64_t)nup * f, (int64_t)nup * df, E, st, offsets));
     if (swiglu)
         MOE_TRY(moe::launch_transpose_bf16(W3, f, d, d, df, (char *)wcat + (size_t)f * 2, (int64_t)nup * f,
-                                           (int64_t)nup * df, E, st));
+                                           (int64_t)nup * df, E, st, offsets));
     // tile counters of the five grouped GEMMs below, cleared once
     unsigned *tc = (unsigned *)(w + L.tile_ctr);
     constexpr int CW = moe::TILE_CTR_WORDS;

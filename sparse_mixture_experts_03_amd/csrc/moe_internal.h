@@ -179,12 +179,15 @@ hipError_t launch_expert_down_fp8(const Shape &s, const void *H, const int32_t *
                                   const uint8_t *W2, const float *S2, float *y_perm, hipStream_t st);
 
 // ---- backward (training gradients) --------------------------------------
+// batched transposes of the expert weights; with row offsets (may be
+// nullptr) the matrices of experts without rows are skipped
 hipError_t launch_transpose_bf16(const void *src, int64_t R, int64_t C, int64_t lds, int64_t sbs,
-                                 void *dst, int64_t ldd, int64_t dbs, int batch, hipStream_t st);
+                                 void *dst, int64_t ldd, int64_t dbs, int batch, hipStream_t st,
+                                 const int32_t *offsets);
 // fp32 layers' backward: batched transpose (dst[b][c][r] = src[b][r][c]) and
 // the per-expert weight gradients C[e][m][n] = sum over e's rows of P[r][m] Q[r][n]
 hipError_t launch_transpose_f32(const float *src, int64_t R, int64_t C, int64_t lds, int64_t sbs, float *dst,
-                                int64_t ldd, int64_t dbs, int batch, hipStream_t st);
+                                int64_t ldd, int64_t dbs, int batch, hipStream_t st, const int32_t *offsets);
 hipError_t launch_wgrad_f32(int E, int M, int N, const int32_t *offsets, const float *P, int64_t ldp,
                             const float *Q, int64_t ldq, float *C, hipStream_t st);
 hipError_t launch_act_fwd(const Shape &s, const float *a1, const float *a3, const int32_t *offsets,
