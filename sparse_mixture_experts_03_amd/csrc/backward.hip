@@ -24,6 +24,7 @@
 //                          GEMM, logits_finish_kernel)
 //   router_bwd_kernel      dh_t from dg (gate convention), aux and z terms
 //   dx_kernel              dx_t = sum over kept slots of dX_perm + W_r^T dh_t
+//                          (the product on fp32 matrix cores)
 //   dwr_partial_kernel, dwr_reduce_kernel, dbias_kernel
 //                          dW_r = sum_t dh_t x_t^T (token splits, then the
 //                          splits in order), db = sum_t dh_t; dW_r runs on
@@ -415,43 +416,117 @@ __global__ __launch_bounds__(256) void router_bwd_kernel(
     }
 }
 
-// dx[t] = sum over kept slots (slot order) of dXp[row] + W_r^T dh_t (fp32):
-// a block per 16 tokens with their dh rows in LDS; a thread per column j
-// reads W_r[i][j] once for the 16 tokens
-constexpr int DX_TT = 16;
+// dx[t] = sum over kept slots (slot order) of dXp[row] + W_r^T dh_t.  The
+// product is a GEMM with K = E on v_mfma_f32_16x16x4_f32 (fp32 operands,
+// products exact as in fp32 FMAs, fp32 accumulation in k order; twice the
+// rate of unpacked fp32 FMAs): a block per 64 tokens x 64 columns.  Chunks
+// of 32 experts of dh (64 x 32) and W_r (32 x 64) are staged in LDS by rows;
+// wave w takes tokens 16w .. 16w + 15 and four 16-column fragments, lane l
+// reading dh[16w + l % 16][k + l / 16] and W_r[k + l / 16][16n + l % 16]
+// (accumulator r of lane l: token 4 (l / 16) + r, column l % 16).  The
+// product goes back through LDS, and four threads per token row add the
+// kept slots' rows of dXp (slot order) and store 64 contiguous columns.
+constexpr int DX_TT = 64, DX_JJ = 64, DX_KC = 32;
 __global__ __launch_bounds__(256) void dx_kernel(const float *__restrict__ dXp,
                                                  const int32_t *__restrict__ row_of_slot,
                                                  const float *__restrict__ dh,
                                                  const float *__restrict__ Wr, int T, int d, int E,
                                                  int k, float *__restrict__ dx) {
-    __shared__ float dhs[DX_TT][128];
-    const int t0 = blockIdx.x * DX_TT;
-    for (int q = threadIdx.x; q < DX_TT * E; q += 256) {
-        const int tt = q / E, i = q - tt * E;
-        dhs[tt][i] = t0 + tt < T ? dh[(int64_t)(t0 + tt) * E + i] : 0.f;
+    typedef float f32x4_t __attribute__((ext_vector_type(4)));
+    constexpr int SOPS = DX_TT * (DX_KC + 1) + DX_KC * (DX_JJ + 1), SOUT = DX_TT * (DX_JJ + 1);
+    __shared__ float sm[SOPS > SOUT ? SOPS : SOUT];       // both operands, then the output tile
+    float(*sA)[DX_KC + 1] = (float(*)[DX_KC + 1])sm;      // [64][33]
+    float(*sB)[DX_JJ + 1] = (float(*)[DX_JJ + 1])(sm + DX_TT * (DX_KC + 1));   // [32][65]
+    float(*sC)[DX_JJ + 1] = (float(*)[DX_JJ + 1])sm;      // [64][65]
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int lr = lane & 15, lk = lane >> 4;
+    const int t0 = blockIdx.x * DX_TT, j0 = blockIdx.y * DX_JJ;
+    f32x4_t acc[4];
+#pragma unroll
+    for (int n = 0; n < 4; ++n) acc[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    // staging: thread tid loads 8 consecutive dh values of token tid / 4 and
+    // 8 consecutive W_r values of expert row tid / 8
+    const int ar = tid >> 2, ac = (tid & 3) * 8;
+    const int br = tid >> 3, bc = (tid & 7) * 8;
+    for (int kc = 0; kc < E; kc += DX_KC) {
+        float av[8], bv[8];
+        {
+            const int t = t0 + ar, kk = kc + ac;
+            if (t < T && (E & 3) == 0 && kk + 8 <= E) {
+                const float4 u0 = *(const float4 *)(dh + (int64_t)t * E + kk);
+                const float4 u1 = *(const float4 *)(dh + (int64_t)t * E + kk + 4);
+                av[0] = u0.x, av[1] = u0.y, av[2] = u0.z, av[3] = u0.w;
+                av[4] = u1.x, av[5] = u1.y, av[6] = u1.z, av[7] = u1.w;
+            } else {
+#pragma unroll
+                for (int q = 0; q < 8; ++q) av[q] = (t < T && kk + q < E) ? dh[(int64_t)t * E + kk + q] : 0.f;
+            }
+            const int kb = kc + br, j = j0 + bc;
+            if (kb < E && (d & 3) == 0 && j + 8 <= d) {
+                const float4 u0 = *(const float4 *)(Wr + (int64_t)kb * d + j);
+                const float4 u1 = *(const float4 *)(Wr + (int64_t)kb * d + j + 4);
+                bv[0] = u0.x, bv[1] = u0.y, bv[2] = u0.z, bv[3] = u0.w;
+                bv[4] = u1.x, bv[5] = u1.y, bv[6] = u1.z, bv[7] = u1.w;
+            } else {
+#pragma unroll
+                for (int q = 0; q < 8; ++q) bv[q] = (kb < E && j + q < d) ? Wr[(int64_t)kb * d + j + q] : 0.f;
+            }
+        }
+        __syncthreads();   // the previous chunk's fragments have been read
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            sA[ar][ac + q] = av[q];
+            sB[br][bc + q] = bv[q];
+        }
+        __syncthreads();
+#pragma unroll
+        for (int q = 0; q < DX_KC / 4; ++q) {
+            const float a = sA[16 * w + lr][4 * q + lk];
+#pragma unroll
+            for (int n = 0; n < 4; ++n)
+                acc[n] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, sB[4 * q + lk][16 * n + lr], acc[n], 0, 0, 0);
+        }
     }
     __syncthreads();
-    for (int j = blockIdx.y * 256 + threadIdx.x; j < d; j += gridDim.y * 256) {
-        float racc[DX_TT];
 #pragma unroll
-        for (int tt = 0; tt < DX_TT; ++tt) racc[tt] = 0.f;
-#pragma unroll 8
-        for (int i = 0; i < E; ++i) {
-            const float wv = Wr[(int64_t)i * d + j];
+    for (int n = 0; n < 4; ++n)
 #pragma unroll
-            for (int tt = 0; tt < DX_TT; ++tt) racc[tt] = fmaf(dhs[tt][i], wv, racc[tt]);
-        }
+        for (int r = 0; r < 4; ++r) sC[16 * w + 4 * lk + r][16 * n + lr] = acc[n][r];
+    __syncthreads();
+    // four threads per token row, 16 columns each
+    const int t = t0 + (tid >> 2), c0 = (tid & 3) * 16;
+    if (t >= T) return;
+    float v[16];
 #pragma unroll
-        for (int tt = 0; tt < DX_TT; ++tt) {
-            const int t = t0 + tt;
-            if (t >= T) break;
-            float acc = 0.f;
-            for (int s = 0; s < k; ++s) {
-                const int r = row_of_slot[(int64_t)t * k + s];
-                if (r >= 0) acc += dXp[(int64_t)r * d + j];
+    for (int q = 0; q < 16; ++q) v[q] = 0.f;
+    const bool vec = (d & 3) == 0 && j0 + c0 + 16 <= d;   // 16-byte rows
+    for (int sl = 0; sl < k; ++sl) {
+        const int row = row_of_slot[(int64_t)t * k + sl];
+        if (row < 0) continue;
+        const float *src = dXp + (int64_t)row * d + j0 + c0;
+        if (vec) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const float4 u = *(const float4 *)(src + 4 * q);
+                v[4 * q] += u.x, v[4 * q + 1] += u.y, v[4 * q + 2] += u.z, v[4 * q + 3] += u.w;
             }
-            dx[(int64_t)t * d + j] = acc + racc[tt];
+        } else {
+#pragma unroll
+            for (int q = 0; q < 16; ++q)
+                if (j0 + c0 + q < d) v[q] += src[q];
         }
+    }
+#pragma unroll
+    for (int q = 0; q < 16; ++q) v[q] += sC[tid >> 2][c0 + q];
+    float *dst = dx + (int64_t)t * d + j0 + c0;
+    if (vec) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            *(float4 *)(dst + 4 * q) = make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
+    } else {
+#pragma unroll
+        for (int q = 0; q < 16; ++q)
+            if (j0 + c0 + q < d) dst[q] = v[q];
     }
 }
 
@@ -858,7 +933,7 @@ hipError_t launch_router_bwd(const Shape &s, const void *x, const float *Wr, con
 
 hipError_t launch_dx(const Shape &s, const float *dXp, const int32_t *row_of_slot, const float *dh,
                      const float *Wr, float *dx, hipStream_t st) {
-    dim3 grid((unsigned)((s.T + DX_TT - 1) / DX_TT), (unsigned)((s.d + 255) / 256));
+    dim3 grid((unsigned)((s.T + DX_TT - 1) / DX_TT), (unsigned)((s.d + DX_JJ - 1) / DX_JJ));
     hipLaunchKernelGGL(dx_kernel, grid, dim3(256), 0, st, dXp, row_of_slot, dh, Wr, s.T, s.d, s.E, s.k, dx);
     return hipGetLastError();
 }
