@@ -16,7 +16,14 @@ descriptor's stage-event hook), over the same timed steps.
 
 The default line also carries "decode_fp8": the decode layer with its
 expert weights quantised row by row to e4m3 (one fp32 scale per row) before
-timing, run by moe_forward_fp8 (weights 1 byte, activations bf16).
+timing (weights 1 byte, activations bf16).
+
+The weight-streaming layers (decode, decode_fp8 and the Switch layer, whose
+experts hold at most 48 rows) are timed on expert weights re-ordered once,
+before timing, into the streaming tile layout (moe_pack_stream; then
+moe_forward_packed), which gives the same results bit for bit as row-major
+weights; each of their objects carries the row-major entry point's
+(moe_forward, moe_forward_fp8) figures beside, under "row_major".
 
 Roofline of the dominant kernel (the expert up-projection, a grouped GEMM
 on bf16 MFMA): algorithmic FLOPs per launch = N_kept * 2 * n_up * d * d_ff
@@ -56,7 +63,7 @@ FLOPs for context.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                        [--no-cpu] [--no-decode] [--backward] [--cold]
-                       [--library-gemm]
+                       [--library-gemm] [--packed]
 """
 import argparse
 import ctypes
@@ -78,6 +85,8 @@ STAGES = ("route", "route_finalize", "dispatch", "gather", "expert_up", "expert_
 STAGES_SHARED = ("route", "route_finalize", "dispatch", "gather", "expert_up", "expert_down",
                  "shared", "combine")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
+LAYOUT_PACKED = ("streaming tile layout (moe_pack_stream once before timing; moe_forward_packed; "
+                 "the same values and results bit for bit as row-major)")
 GEMM_SRCS = [os.path.join(ROOT, "sparse_mixture_experts_03_amd", "csrc", f)
              for f in ("expert_gemm.hip", "expert_fp8.hip")]
 
@@ -147,10 +156,32 @@ def traffic_for(workload, kernel, launches_per_step=1):
     return ent["hbm_bytes_per_launch"]
 
 
-def run_workload(w, steps, warmup, fresh_x_steps=0, seed=0, sclk_seconds=0.0):
+def pack_weights(w, desc, dw, f8):
+    """The expert weights of a weight-streaming layer (bf16 values, or the
+    e4m3 codes f8) re-ordered once into the streaming tile layout
+    (moe_pack_stream), before any timing; the row-major copies are freed.
+    Returns the moe_packed_experts and the tensors it points to."""
+    from sparse_mixture_experts_03_amd import binding as B
+
+    if f8 is not None:
+        t = B.pack_experts(f8["q1"], f8["q3"], f8["q2"])
+        t.update(s1=f8["s1"], s3=f8["s3"], s2=f8["s2"])
+        pk = B.make_packed(desc, "e4m3", t["p1"], t["p3"], t["p2"], t["s1"], t["s3"], t["s2"])
+        for key in ("q1", "q3", "q2"):
+            f8[key] = None
+    else:
+        t = B.pack_experts(dw["W1"], dw["W3"], dw["W2"])
+        pk = B.make_packed(desc, "bf16", t["p1"], t["p3"], t["p2"])
+        for key in ("W1", "W3", "W2"):
+            dw[key] = None
+    return pk, t
+
+
+def run_workload(w, steps, warmup, fresh_x_steps=0, seed=0, sclk_seconds=0.0, packed=False):
     """Times ``steps`` forward steps of workload w. Returns a result dict
     (with sclk_seconds > 0 also the shader clock sampled afterwards while
-    steps run back to back for that long, outside the timed region)."""
+    steps run back to back for that long, outside the timed region).
+    packed: expert weights in the streaming tile layout, moe_forward_packed."""
     import torch
     from sparse_mixture_experts_03_amd import binding as B
     from sparse_mixture_experts_03_amd import synth
@@ -183,6 +214,11 @@ def run_workload(w, steps, warmup, fresh_x_steps=0, seed=0, sclk_seconds=0.0):
     shs = [B.make_shared(desc, dw["Ws1"], dw["Ws3"], dw["Ws2"], ress[j]) for j in range(n_x)] \
         if with_shared else None
     out = B.alloc_outputs(desc)
+    pk = None
+    if packed:
+        pk, pk_tensors = pack_weights(w, desc, dw, f8)  # noqa: F841  (kept alive for the steps)
+        f8 = None
+        torch.cuda.synchronize()
     fp8 = B.make_fp8(desc, f8["q1"], f8["q3"], f8["q2"], f8["s1"], f8["s3"], f8["s2"]) if f8 else None
     ev = HipEvents()
     nev = len(stages) + 1
@@ -199,7 +235,10 @@ def run_workload(w, steps, warmup, fresh_x_steps=0, seed=0, sclk_seconds=0.0):
         # only the two events around the expert up-projection (the dominant
         # kernel) are recorded: each recorded event separates the kernels
         # around it by a few us
-        if fp8 is not None:
+        if pk is not None:
+            B.moe_forward_packed(desc, pk, xs[j], dw["Wr"], dw["bias"], noises[j], out["y"], ws,
+                                 kept_counts=out["kept_counts"], stats=out["stats"], stream=stream)
+        elif fp8 is not None:
             B.moe_forward_fp8(desc, fp8, xs[j], dw["Wr"], dw["bias"], noises[j], out["y"], ws,
                               kept_counts=out["kept_counts"], stats=out["stats"], stream=stream)
         elif with_shared:
@@ -293,11 +332,12 @@ def cpu_baseline(w, seed=0, target_s=22.0):
                        f"and combine on {S} sampled tokens ({t_ffn:.2f}s); fp64 sums")}
 
 
-def run_cold(w, steps, warmup, seed=0, flush_bytes=512 << 20):
-    """Per-step times of moe_forward with the last-level cache flushed before
-    every step (a device fill of ``flush_bytes``, outside the timed events):
-    each step is bracketed by its own events on the launch stream.  Returns
-    the median, minimum and 90th percentile."""
+def run_cold(w, steps, warmup, seed=0, flush_bytes=512 << 20, packed=False):
+    """Per-step times of moe_forward (packed: moe_forward_packed) with the
+    last-level cache flushed before every step (a device fill of
+    ``flush_bytes``, outside the timed events): each step is bracketed by
+    its own events on the launch stream.  Returns the median, minimum and
+    90th percentile."""
     import torch
     from sparse_mixture_experts_03_amd import binding as B
     from sparse_mixture_experts_03_amd import synth
@@ -310,6 +350,7 @@ def run_cold(w, steps, warmup, seed=0, flush_bytes=512 << 20):
     desc = B.desc_for(w)
     ws = B.workspace(desc)
     out = B.alloc_outputs(desc)
+    pk = pack_weights(w, desc, dw, None)[0] if packed else None
     scratch = torch.empty(flush_bytes // 4, dtype=torch.float32, device="cuda")
     stream = torch.cuda.current_stream()
     times = []
@@ -317,8 +358,11 @@ def run_cold(w, steps, warmup, seed=0, flush_bytes=512 << 20):
         scratch.fill_(float(i))
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record(stream)
-        B.moe_forward(desc, x, dw["Wr"], dw["bias"], noise, dw["W1"], dw["W3"], dw["W2"], out["y"], ws,
-                      stream=stream)
+        if pk is not None:
+            B.moe_forward_packed(desc, pk, x, dw["Wr"], dw["bias"], noise, out["y"], ws, stream=stream)
+        else:
+            B.moe_forward(desc, x, dw["Wr"], dw["bias"], noise, dw["W1"], dw["W3"], dw["W2"], out["y"], ws,
+                          stream=stream)
         b.record(stream)
         if i >= warmup:
             times.append((a, b))
@@ -356,13 +400,14 @@ def kernel_bytes(w, stage, n_kept, touched):
     return int(touched * w.d * w.d_ff * eb + n_kept * w.d_ff * eb + n_kept * w.d * 4)
 
 
-def hbm_layer_object(w, steps, warmup=5):
+def hbm_layer_object(w, steps, warmup=5, packed=False):
     """An HBM-bound layer (Switch, fine-grained Zipf) in the default line:
     per-step median, minimum and p90 with the last-level cache flushed
     before every step, against 8 TB/s over the algorithmic bytes; the warm
-    back-to-back rate and the dominant kernel's event-timed rate beside."""
-    res = run_workload(w, steps, warmup)
-    cold = run_cold(w, steps, 3)
+    back-to-back rate and the dominant kernel's event-timed rate beside.
+    packed: weights in the streaming tile layout (moe_forward_packed)."""
+    res = run_workload(w, steps, warmup, packed=packed)
+    cold = run_cold(w, steps, 3, packed=packed)
     med, mn, p90 = cold["ms_per_step_median_min_p90"]
     nbytes = layer_bytes(w, res["n_kept"], res["touched"])
     gbs = nbytes / (med * 1e-3) / 1e9
@@ -375,6 +420,7 @@ def hbm_layer_object(w, steps, warmup=5):
         "workload": w.name, "T": w.T, "d": w.d, "d_ff": w.d_ff, "E": w.E, "k": w.k,
         "gate": w.gate, "act": w.act, "capacity_factor": w.cf,
         "kept_rows": res["n_kept"], "touched_experts": res["touched"],
+        "weight_layout": LAYOUT_PACKED if packed else "row-major (moe_forward)",
         "value": round(w.T / (med * 1e-3), 1), "unit": "tokens/s", "steps": steps,
         "cache": "last-level cache flushed (512 MB device fill) before every timed step",
         "ms_per_step_median_min_p90": [med, mn, p90],
@@ -386,7 +432,7 @@ def hbm_layer_object(w, steps, warmup=5):
         "dominant_kernel": {"stage": dom, "mean_launch_ms": round(stages[dom], 4),
                             "algorithmic_per_launch": kb, "achieved": round(kgbs, 1),
                             "unit": "GB/s", "frac": round(kgbs / PEAK_HBM_GBS, 4),
-                            "traffic": traffic_for(w.name, dom)},
+                            "traffic": traffic_for(w.name + ("_packed" if packed else ""), dom)},
     }
 
 
@@ -610,7 +656,7 @@ def combine_object(w, res):
             "mean_launch_ms": round(ms, 4)}
 
 
-def decode_object(wd, rd):
+def decode_object(wd, rd, packed=False):
     """Throughput and HBM roofline of a decode workload's run: the expert
     up-projection (weight streaming) against 8 TB/s, algorithmic bytes =
     the touched experts' W1 and W3 (bf16: 2 B per weight; e4m3: 1 B plus a
@@ -627,6 +673,7 @@ def decode_object(wd, rd):
     gbs = up_bytes / (up_ms_d * 1e-3) / 1e9
     return {
         "workload": wd.name, "weights": "e4m3" if wd.weights == "e4m3" else "bf16",
+        "weight_layout": LAYOUT_PACKED if packed else "row-major",
         "value": round(wd.T * rd["steps"] / rd["elapsed"], 1),
         "unit": "tokens/s", "steps": rd["steps"], "ms_per_step": round(ms_d, 4),
         "step_hbm_gbs": round(step_bytes / (ms_d * 1e-3) / 1e9, 1),
@@ -635,7 +682,7 @@ def decode_object(wd, rd):
         "combine": combine_object(wd, rd),
         "roofline": {"bound": "hbm", "kernel": "expert_up", "achieved": round(gbs, 1),
                      "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
-                     "traffic": traffic_for(wd.name, "expert_up"),
+                     "traffic": traffic_for(wd.name + ("_packed" if packed else ""), "expert_up"),
                      "algorithmic_per_launch": up_bytes, "mean_launch_ms": round(up_ms_d, 4),
                      "event_timed_launches": rd["event_steps"]},
     }
@@ -694,6 +741,9 @@ def main():
     ap.add_argument("--no-layers", action="store_true",
                     help="leave out the Switch and fine-grained Zipf layers of the default line")
     ap.add_argument("--layer-steps", type=int, default=50)
+    ap.add_argument("--packed", action="store_true",
+                    help="expert weights in the streaming tile layout (moe_forward_packed; "
+                         "weight-streaming shapes: decode batches, the Switch layer)")
     ap.add_argument("--backward", action="store_true",
                     help="time moe_backward on the workload instead of the forward")
     ap.add_argument("--cold", action="store_true",
@@ -737,8 +787,8 @@ def main():
         return
     if w.steps > 1:
         # a decode workload on its own: fresh tokens every step, HBM roofline
-        res = run_workload(w, args.steps, args.warmup, fresh_x_steps=args.steps)
-        obj = decode_object(w, res)
+        res = run_workload(w, args.steps, args.warmup, fresh_x_steps=args.steps, packed=args.packed)
+        obj = decode_object(w, res, packed=args.packed)
         line = {
             "metric": METRIC, "value": obj["value"], "unit": "tokens/s", "n_gpus": 1,
             "steps": args.steps, "warmup": args.warmup, "ms_per_step": obj["ms_per_step"],
@@ -748,12 +798,12 @@ def main():
                        "gate": w.gate, "act": w.act, "capacity_factor": w.cf, "router": "fp32",
                        "expert_weights": obj["weights"], "parallelism": "single_gpu"},
             "stage_ms": obj["stage_ms"], "step_hbm_frac": obj["step_hbm_frac"],
-            "roofline": obj["roofline"],
+            "weight_layout": obj["weight_layout"], "roofline": obj["roofline"],
         }
         print(json.dumps(line), flush=True)
         return
     res = run_workload(w, args.steps, args.warmup,
-                       sclk_seconds=1.0 if w.name == "mixtral_prefill" else 0.0)
+                       sclk_seconds=1.0 if w.name == "mixtral_prefill" else 0.0, packed=args.packed)
     ms_step = res["elapsed"] * 1e3 / res["steps"]
     tokens_s = w.T * res["steps"] / res["elapsed"]
     n_up = 2 if w.act == "swiglu" else 1
@@ -793,7 +843,7 @@ def main():
     }
     # per-step distribution of the same layer with the last-level cache
     # flushed before each step (its 2.8 GB of weights never fit it anyway)
-    cold = run_cold(w, max(args.steps, 20), 3)
+    cold = run_cold(w, max(args.steps, 20), 3, packed=args.packed)
     line["step_ms_median_min_p90"] = cold["ms_per_step_median_min_p90"]
     line["step_ms_mode"] = "each step timed alone by its own events, last-level cache flushed before it"
     line["combine"] = combine_object(w, res)
@@ -810,15 +860,32 @@ def main():
                                 "frac": round(sh_tf / PEAK_BF16_TFLOPS, 4),
                                 "algorithmic_per_stage": shared_flops, "mean_stage_ms": round(sh_ms, 4)}
     if not args.no_decode and w.name == "mixtral_prefill":
+        # weight-streaming layers run on packed weights (the library's
+        # fastest form for them); the row-major entry point is timed beside
         for key, name in (("decode", "mixtral_decode"), ("decode_fp8", "mixtral_decode_fp8")):
             wd = synth.WORKLOADS[name]
-            rd = run_workload(wd, args.decode_steps, 10, fresh_x_steps=args.decode_steps)
-            line[key] = decode_object(wd, rd)
-            log(f"[bench] {wd.name}: {line[key]['ms_per_step']:.3f} ms/step")
+            rd = run_workload(wd, args.decode_steps, 10, fresh_x_steps=args.decode_steps, packed=True)
+            line[key] = decode_object(wd, rd, packed=True)
+            rr = decode_object(wd, run_workload(wd, args.decode_steps, 10, fresh_x_steps=args.decode_steps))
+            line[key]["row_major"] = {
+                "entry_point": "moe_forward_fp8" if wd.weights == "e4m3" else "moe_forward",
+                "ms_per_step": rr["ms_per_step"], "step_hbm_frac": rr["step_hbm_frac"],
+                "stage_ms": rr["stage_ms"], "expert_up_frac": rr["roofline"]["frac"]}
+            log(f"[bench] {wd.name}: {line[key]['ms_per_step']:.3f} ms/step packed, "
+                f"{rr['ms_per_step']:.3f} row-major")
     if not args.no_layers and w.name == "mixtral_prefill":
         for name in ("switch", "finegrained_zipf"):
             log(f"[bench] {name}: {args.layer_steps} warm + {args.layer_steps} cold steps ...")
-            line[name] = hbm_layer_object(synth.WORKLOADS[name], args.layer_steps)
+            # the Switch layer's experts hold at most 40 rows: weight streaming,
+            # on packed weights; the row-major entry point beside
+            packed = name == "switch"
+            line[name] = hbm_layer_object(synth.WORKLOADS[name], args.layer_steps, packed=packed)
+            if packed:
+                rr = hbm_layer_object(synth.WORKLOADS[name], args.layer_steps)
+                line[name]["row_major"] = {
+                    "entry_point": "moe_forward", "ms_per_step_median_min_p90": rr["ms_per_step_median_min_p90"],
+                    "ms_per_step_warm": rr["ms_per_step_warm"], "stage_ms_warm": rr["stage_ms_warm"],
+                    "frac": rr["roofline"]["frac"]}
             log(f"[bench] {name}: median {line[name]['ms_per_step_median_min_p90'][0]:.4f} ms/step "
                 f"(cold), {line[name]['roofline']['frac']:.3f} of HBM")
     if res["sclk"] is not None:

@@ -389,6 +389,79 @@ int moe_forward_fp8(const moe_desc *desc, const void *x, const float *W_r, const
                     int32_t *row_of_slot, int32_t *token_of_row, uint8_t *dropped, float *stats,
                     void *ws, size_t ws_bytes, void *stream);
 
+/* ---- expert weights in the streaming tile layout ------------------------------
+ *
+ * Page "Mixture of experts", Mechanics, "Total versus active parameters":
+ * at small batch sizes a step is limited by reading the expert weights.
+ * For such batches (the shapes moe_expert_ffn_fp8 accepts: bf16
+ * activations, at most 48 rows per expert, d and d_ff multiples of 128) the
+ * expert GEMMs stream every touched weight row once, 16 rows at a time per
+ * wavefront.  In row-major storage each of their 16-byte load instructions
+ * touches 16 rows; in the streaming tile layout the same values are ordered
+ * so that each instruction reads 1 KB of contiguous memory, which the
+ * memory system serves faster.  The values, the products and their order
+ * are unchanged, so the results equal those of moe_forward (bf16 weights)
+ * or moe_forward_fp8 (e4m3 codes) bit for bit.  Packing is a one-time
+ * re-ordering of the weights, done when they are loaded.
+ *
+ * Streaming tile layout of a [rows][cols] matrix of elem_bytes-byte
+ * elements (2: bf16, 1: e4m3 codes), rows % 16 == 0, cols % 128 == 0, in
+ * units of 16 bytes (16 / elem_bytes elements):
+ *   - blocks of 16 rows x 128 columns; block (rb, cb) (rows 16 rb ..,
+ *     columns 128 cb ..) is the (rb * cols / 128 + cb)-th block of
+ *     128 * elem_bytes units;
+ *   - in row n (0..15) of a block, unit u covers columns
+ *     u * 16 / elem_bytes .. +16 / elem_bytes of the block; with
+ *     V = 2 * elem_bytes units per 32 columns, unit u = V * g + r
+ *     (g = 0..3, r = 0..V-1) is stored at unit position r * 64 + 16 * g + n
+ *     of the block.
+ * An expert weight tensor [E][rows_per_expert][cols] is packed as one
+ * [E * rows_per_expert][cols] matrix (rows_per_expert % 16 == 0 keeps every
+ * block inside one expert).  Row scales of e4m3 weights stay as
+ * moe_quantize_e4m3 writes them.
+ */
+#define MOE_WEIGHTS_BF16 1 /* bf16 values (the value of MOE_DTYPE_BF16) */
+#define MOE_WEIGHTS_E4M3 2 /* e4m3 codes with fp32 row scales           */
+
+typedef struct moe_packed_experts {
+    int32_t format;            /* MOE_WEIGHTS_BF16 or MOE_WEIGHTS_E4M3 */
+    const void *W1, *W3, *W2;  /* packed [E*d_ff][d], [E*d_ff][d] (SwiGLU only), [E*d][d_ff] */
+    const float *s1, *s3, *s2; /* E4M3: scales [E][d_ff], [E][d_ff] (SwiGLU only), [E][d];
+                                  BF16: all NULL */
+} moe_packed_experts;
+
+/*
+ * Writes W [rows][cols] (elem_bytes 2 or 1) to W_packed (rows * cols *
+ * elem_bytes bytes, not overlapping W) in the streaming tile layout.
+ * rows = 0 enqueues nothing.  Errors: MOE_ERR_INVALID_ARG (elem_bytes not
+ * 1 or 2, rows < 0, rows % 16 != 0, cols < 128, cols % 128 != 0, null
+ * pointer with rows > 0).
+ */
+int moe_pack_stream(int32_t elem_bytes, const void *W, int64_t rows, int64_t cols, void *W_packed,
+                    void *stream);
+
+/*
+ * moe_expert_ffn with packed expert weights.  Supported shapes are those of
+ * moe_expert_ffn_fp8 (otherwise MOE_ERR_UNSUPPORTED).  MOE_ERR_INVALID_ARG
+ * for an unknown format, a missing W1/W2 (or, for e4m3, s1/s2), or W3 (s3)
+ * given without SwiGLU or missing with it; scales given for bf16 weights.
+ */
+int moe_expert_ffn_packed(const moe_desc *desc, const void *x_perm, const int32_t *offsets,
+                          const moe_packed_experts *w, float *y_perm, void *ws, size_t ws_bytes,
+                          void *stream);
+
+/*
+ * moe_forward with packed expert weights (w in place of W1, W3, W2), for the
+ * shapes of moe_expert_ffn_packed.  Routing, dispatch, statistics and the
+ * combine are those of moe_forward; ws: moe_workspace_size() bytes; stage
+ * events as moe_forward.
+ */
+int moe_forward_packed(const moe_desc *desc, const void *x, const float *W_r, const float *bias,
+                       const float *noise, const moe_packed_experts *w, void *y, int32_t *topk_idx,
+                       float *gates, int32_t *routed_counts, int32_t *kept_counts, int32_t *offsets,
+                       int32_t *row_of_slot, int32_t *token_of_row, uint8_t *dropped, float *stats,
+                       void *ws, size_t ws_bytes, void *stream);
+
 /* ---- backward (training gradients) -------------------------------------------
  *
  * Page "Mixture of experts", Mechanics: the top-k choice is discrete, but

@@ -10,7 +10,9 @@ Names match the ABI: moe_workspace_size, moe_capacity, moe_route,
 moe_dispatch, moe_expert_ffn, moe_combine, moe_forward, and for shared
 experts plus the block residual moe_workspace_size_shared, moe_shared_ffn,
 moe_combine_shared, moe_forward_shared, and for E4M3 expert weights
-moe_quantize_e4m3, moe_expert_ffn_fp8, moe_forward_fp8, and for training
+moe_quantize_e4m3, moe_expert_ffn_fp8, moe_forward_fp8, and for expert weights in
+the streaming tile layout moe_pack_stream, moe_expert_ffn_packed,
+moe_forward_packed, and for training
 moe_backward_workspace_size, moe_backward, and the forward without a
 workspace argument (its workspace is a static device array in the library)
 moe_forward_noalloc.
@@ -67,6 +69,15 @@ class MoeFp8Experts(ctypes.Structure):
                 ("s1", ctypes.c_void_p), ("s3", ctypes.c_void_p), ("s2", ctypes.c_void_p)]
 
 
+class MoePackedExperts(ctypes.Structure):
+    _fields_ = [("format", ctypes.c_int32), ("W1", ctypes.c_void_p), ("W3", ctypes.c_void_p),
+                ("W2", ctypes.c_void_p), ("s1", ctypes.c_void_p), ("s3", ctypes.c_void_p),
+                ("s2", ctypes.c_void_p)]
+
+
+WEIGHTS = {"bf16": 1, "e4m3": 2}
+
+
 def make_desc(T, d, d_ff, E, k, gate="renorm", act="swiglu", dtype="bf16", cf=0.0) -> MoeDesc:
     return MoeDesc(int(T), int(d), int(d_ff), int(E), int(k), GATE[gate], ACT[act], DTYPE[dtype],
                    float(cf), None, 0)
@@ -112,6 +123,10 @@ def load(build_if_missing: bool = True):
     lib.moe_quantize_e4m3.argtypes = [ctypes.c_int32, P, ctypes.c_int64, ctypes.c_int64, P, P, P]
     lib.moe_expert_ffn_fp8.argtypes = [D, P, P, F8, P, P, sz, P]
     lib.moe_forward_fp8.argtypes = [D, P, P, P, P, F8, P, P, P, P, P, P, P, P, P, P, P, sz, P]
+    PK = ctypes.POINTER(MoePackedExperts)
+    lib.moe_pack_stream.argtypes = [ctypes.c_int32, P, ctypes.c_int64, ctypes.c_int64, P, P]
+    lib.moe_expert_ffn_packed.argtypes = [D, P, P, PK, P, P, sz, P]
+    lib.moe_forward_packed.argtypes = [D, P, P, P, P, PK, P, P, P, P, P, P, P, P, P, P, P, sz, P]
     lib.moe_backward_workspace_size.argtypes = [D, ctypes.POINTER(ctypes.c_size_t)]
     lib.moe_backward.argtypes = [D] + [P] * 14 + [ctypes.c_float, ctypes.c_float] + [P] * 7 + [sz, P]
     lib.moe_status_string.argtypes = [ctypes.c_int]
@@ -120,7 +135,7 @@ def load(build_if_missing: bool = True):
                "moe_expert_ffn", "moe_combine", "moe_forward", "moe_workspace_size_shared",
                "moe_shared_ffn", "moe_combine_shared", "moe_forward_shared", "moe_quantize_e4m3",
                "moe_expert_ffn_fp8", "moe_forward_fp8", "moe_backward_workspace_size", "moe_backward",
-               "moe_forward_noalloc"):
+               "moe_forward_noalloc", "moe_pack_stream", "moe_expert_ffn_packed", "moe_forward_packed"):
         getattr(lib, fn).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -415,6 +430,78 @@ def moe_forward_fp8(desc, fp8: MoeFp8Experts, x, W_r, bias, noise, y, ws, topk_i
         _ptr(stats, torch.float32, (2 * E + 2,), "stats", True),
         _ptr(ws, torch.uint8, None, "ws"), ws.numel(), _stream(stream))
     _check("moe_forward_fp8", rc)
+
+
+def moe_pack_stream(W, out, stream=None):
+    """W [..., cols] (bf16, or uint8 e4m3 codes) viewed as [rows][cols] ->
+    out (same dtype and shape) in the streaming tile layout."""
+    if W.dtype not in (torch.bfloat16, torch.uint8):
+        raise TypeError("W must be bf16 or uint8 (e4m3 codes)")
+    cols = int(W.shape[-1])
+    rows = W.numel() // cols if cols else 0
+    rc = load().moe_pack_stream(2 if W.dtype == torch.bfloat16 else 1, _ptr(W, None, None, "W"), rows, cols,
+                                _ptr(out, W.dtype, tuple(W.shape), "out"), _stream(stream))
+    _check("moe_pack_stream", rc)
+
+
+def pack_experts(W1, W3, W2, stream=None) -> dict:
+    """Packed copies p1, p3, p2 of expert weights or codes (W3 may be None)."""
+    out = {}
+    for name, W in (("1", W1), ("3", W3), ("2", W2)):
+        if W is None:
+            out["p" + name] = None
+            continue
+        pk = torch.empty_like(W)
+        moe_pack_stream(W, pk, stream)
+        out["p" + name] = pk
+    return out
+
+
+def make_packed(desc, fmt, p1, p3, p2, s1=None, s3=None, s2=None) -> MoePackedExperts:
+    """A moe_packed_experts over device tensors (they must outlive its use);
+    fmt "bf16" (no scales) or "e4m3" (codes with row scales)."""
+    d, d_ff, E = desc.d, desc.d_ff, desc.E
+    wt = torch.bfloat16 if fmt == "bf16" else torch.uint8
+    return MoePackedExperts(WEIGHTS[fmt],
+                            _ptr(p1, wt, (E, d_ff, d), "p1"),
+                            _ptr(p3, wt, (E, d_ff, d), "p3", True),
+                            _ptr(p2, wt, (E, d, d_ff), "p2"),
+                            _ptr(s1, torch.float32, (E, d_ff), "s1", True),
+                            _ptr(s3, torch.float32, (E, d_ff), "s3", True),
+                            _ptr(s2, torch.float32, (E, d), "s2", True))
+
+
+def moe_expert_ffn_packed(desc, x_perm, offsets, pk: MoePackedExperts, y_perm, ws, stream=None):
+    T, d, E, k = desc.T, desc.d, desc.E, desc.k
+    rc = load().moe_expert_ffn_packed(
+        ctypes.byref(desc), _ptr(x_perm, _act_dtype(desc), (T * k, d), "x_perm"),
+        _ptr(offsets, torch.int32, (E + 1,), "offsets"), ctypes.byref(pk),
+        _ptr(y_perm, torch.float32, (T * k, d), "y_perm"), _ptr(ws, torch.uint8, None, "ws"),
+        ws.numel(), _stream(stream))
+    _check("moe_expert_ffn_packed", rc)
+
+
+def moe_forward_packed(desc, pk: MoePackedExperts, x, W_r, bias, noise, y, ws, topk_idx=None,
+                       gates=None, routed_counts=None, kept_counts=None, offsets=None,
+                       row_of_slot=None, token_of_row=None, dropped=None, stats=None, stream=None):
+    T, d, E, k = desc.T, desc.d, desc.E, desc.k
+    dt = _act_dtype(desc)
+    rc = load().moe_forward_packed(
+        ctypes.byref(desc), _ptr(x, dt, (T, d), "x"), _ptr(W_r, torch.float32, (E, d), "W_r"),
+        _ptr(bias, torch.float32, (E,), "bias", True),
+        _ptr(noise, torch.float32, (T, E), "noise", True), ctypes.byref(pk),
+        _ptr(y, dt, (T, d), "y"),
+        _ptr(topk_idx, torch.int32, (T, k), "topk_idx", True),
+        _ptr(gates, torch.float32, (T, k), "gates", True),
+        _ptr(routed_counts, torch.int32, (E,), "routed_counts", True),
+        _ptr(kept_counts, torch.int32, (E,), "kept_counts", True),
+        _ptr(offsets, torch.int32, (E + 1,), "offsets", True),
+        _ptr(row_of_slot, torch.int32, (T, k), "row_of_slot", True),
+        _ptr(token_of_row, torch.int32, (T * k,), "token_of_row", True),
+        _ptr(dropped, torch.uint8, (T, k), "dropped", True),
+        _ptr(stats, torch.float32, (2 * E + 2,), "stats", True),
+        _ptr(ws, torch.uint8, None, "ws"), ws.numel(), _stream(stream))
+    _check("moe_forward_packed", rc)
 
 
 def moe_backward_workspace_size(desc: MoeDesc) -> int:

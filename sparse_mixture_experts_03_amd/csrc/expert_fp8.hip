@@ -109,7 +109,7 @@ __device__ __forceinline__ bf16x8_t e4m3x8_to_bf16(uint32_t w0, uint32_t w1) {
     return __builtin_bit_cast(bf16x8_t, o);
 }
 
-template <int MT, int NT, int PF, int KS, bool DUAL, int ACT, bool OUT_BF16>
+template <int MT, int NT, int PF, int KS, bool DUAL, int ACT, bool OUT_BF16, bool PACKED>
 __global__ __launch_bounds__(64 * KS) void gemm_fp8w_skinny_kernel(
     const uint16_t *__restrict__ A, const int32_t *__restrict__ a_rows,
     const int32_t *__restrict__ offsets, int E, const uint8_t *__restrict__ B1,
@@ -144,8 +144,11 @@ __global__ __launch_bounds__(64 * KS) void gemm_fp8w_skinny_kernel(
     for (int q = 0; q < NB; ++q)
 #pragma unroll
         for (int t = 0; t < NT; ++t)
-            b_row[q][t] = ((DUAL && q) ? B3 : B1) + ((int64_t)e * N + min(n0 + t * 16 + n, N - 1)) * K +
-                          (int64_t)cb * F8_KC + g * 32;
+            b_row[q][t] = PACKED ? ((DUAL && q) ? B3 : B1) + (int64_t)e * N * K +
+                                       ((int64_t)min(n0 / 16 + t, N / 16 - 1) * (K / F8_KC) + cb) * 2048 +
+                                       lane * 16
+                                 : ((DUAL && q) ? B3 : B1) + ((int64_t)e * N + min(n0 + t * 16 + n, N - 1)) * K +
+                                       (int64_t)cb * F8_KC + g * 32;
 
     f32x4_t acc[MT][NB][NT];
 #pragma unroll
@@ -165,7 +168,8 @@ __global__ __launch_bounds__(64 * KS) void gemm_fp8w_skinny_kernel(
             for (int t = 0; t < NT; ++t)
 #pragma unroll
                 for (int h = 0; h < 2; ++h)
-                    rb[slot][q][t][h] = *(const uint4 *)(b_row[q][t] + (int64_t)ch * F8_KC + h * 16);
+                    rb[slot][q][t][h] = *(const uint4 *)(b_row[q][t] + (PACKED ? (int64_t)ch * 2048 + h * 1024
+                                                                              : (int64_t)ch * F8_KC + h * 16));
     };
     auto load_a = [&](int slot, int ch) {
 #pragma unroll
@@ -261,7 +265,7 @@ __global__ __launch_bounds__(64 * KS) void gemm_fp8w_skinny_kernel(
 // the weight bytes.  Measured on the Mixtral decode layer against 1 or 2
 // tiles with an 8-chunk ring: up projection 180 against 196 us, down 91
 // against 100 us.
-template <int MT, int NT, bool DUAL, int ACT, bool OUT_BF16>
+template <int MT, int NT, bool DUAL, int ACT, bool OUT_BF16, bool PACKED>
 hipError_t launch_fp8(const Shape &s, const void *A, const int32_t *a_rows, const int32_t *offsets,
                       const uint8_t *B1, const uint8_t *B3, const float *S1, const float *S3, void *C,
                       int N, int K, hipStream_t st) {
@@ -270,10 +274,10 @@ hipError_t launch_fp8(const Shape &s, const void *A, const int32_t *a_rows, cons
     // split K over the waves of a block when there are too few column tiles
     // to keep enough weight bytes in flight and K is long
     if (blocks < 4096 && K / F8_KC >= 64)
-        launch_kernel((gemm_fp8w_skinny_kernel<MT, NT, PF, 4, DUAL, ACT, OUT_BF16>), dim3(blocks), dim3(256), 0,
+        launch_kernel((gemm_fp8w_skinny_kernel<MT, NT, PF, 4, DUAL, ACT, OUT_BF16, PACKED>), dim3(blocks), dim3(256), 0,
                       st, (const uint16_t *)A, a_rows, offsets, s.E, B1, B3, S1, S3, C, N, K);
     else
-        launch_kernel((gemm_fp8w_skinny_kernel<MT, NT, PF, 1, DUAL, ACT, OUT_BF16>), dim3(blocks), dim3(64), 0,
+        launch_kernel((gemm_fp8w_skinny_kernel<MT, NT, PF, 1, DUAL, ACT, OUT_BF16, PACKED>), dim3(blocks), dim3(64), 0,
                       st, (const uint16_t *)A, a_rows, offsets, s.E, B1, B3, S1, S3, C, N, K);
     return hipGetLastError();
 }
@@ -307,27 +311,44 @@ hipError_t launch_quantize_e4m3(int dtype, const void *W, int64_t rows, int64_t 
     return hipGetLastError();
 }
 
-hipError_t launch_expert_up_fp8(const Shape &s, const void *A, const int32_t *a_rows,
-                                const int32_t *offsets, const uint8_t *W1, const uint8_t *W3,
-                                const float *S1, const float *S3, void *H, hipStream_t st) {
+namespace {
+
+template <bool PACKED>
+hipError_t up_fp8(const Shape &s, const void *A, const int32_t *a_rows, const int32_t *offsets, const uint8_t *W1,
+                  const uint8_t *W3, const float *S1, const float *S3, void *H, hipStream_t st) {
     const int mt = fp8_tiles(s);
     const int N = s.d_ff, K = s.d;
     if (s.act == ACT_SWIGLU)
-        return mt == 2 ? launch_fp8<2, 4, true, ACT_SWIGLU, true>(s, A, a_rows, offsets, W1, W3, S1, S3, H, N, K, st)
-                       : launch_fp8<3, 4, true, ACT_SWIGLU, true>(s, A, a_rows, offsets, W1, W3, S1, S3, H, N, K, st);
+        return mt == 2 ? launch_fp8<2, 4, true, ACT_SWIGLU, true, PACKED>(s, A, a_rows, offsets, W1, W3, S1, S3, H, N, K, st)
+                       : launch_fp8<3, 4, true, ACT_SWIGLU, true, PACKED>(s, A, a_rows, offsets, W1, W3, S1, S3, H, N, K, st);
     if (s.act == ACT_GELU)
-        return mt == 2 ? launch_fp8<2, 8, false, ACT_GELU, true>(s, A, a_rows, offsets, W1, nullptr, S1, nullptr, H, N, K, st)
-                       : launch_fp8<3, 8, false, ACT_GELU, true>(s, A, a_rows, offsets, W1, nullptr, S1, nullptr, H, N, K, st);
-    return mt == 2 ? launch_fp8<2, 8, false, ACT_RELU, true>(s, A, a_rows, offsets, W1, nullptr, S1, nullptr, H, N, K, st)
-                   : launch_fp8<3, 8, false, ACT_RELU, true>(s, A, a_rows, offsets, W1, nullptr, S1, nullptr, H, N, K, st);
+        return mt == 2 ? launch_fp8<2, 8, false, ACT_GELU, true, PACKED>(s, A, a_rows, offsets, W1, nullptr, S1, nullptr, H, N, K, st)
+                       : launch_fp8<3, 8, false, ACT_GELU, true, PACKED>(s, A, a_rows, offsets, W1, nullptr, S1, nullptr, H, N, K, st);
+    return mt == 2 ? launch_fp8<2, 8, false, ACT_RELU, true, PACKED>(s, A, a_rows, offsets, W1, nullptr, S1, nullptr, H, N, K, st)
+                   : launch_fp8<3, 8, false, ACT_RELU, true, PACKED>(s, A, a_rows, offsets, W1, nullptr, S1, nullptr, H, N, K, st);
+}
+
+template <bool PACKED>
+hipError_t down_fp8(const Shape &s, const void *H, const int32_t *offsets, const uint8_t *W2, const float *S2,
+                    float *y_perm, hipStream_t st) {
+    const int mt = fp8_tiles(s);
+    const int N = s.d, K = s.d_ff;
+    return mt == 2 ? launch_fp8<2, 8, false, ACT_NONE, false, PACKED>(s, H, nullptr, offsets, W2, nullptr, S2, nullptr, y_perm, N, K, st)
+                   : launch_fp8<3, 8, false, ACT_NONE, false, PACKED>(s, H, nullptr, offsets, W2, nullptr, S2, nullptr, y_perm, N, K, st);
+}
+
+}  // namespace
+
+hipError_t launch_expert_up_fp8(const Shape &s, const void *A, const int32_t *a_rows,
+                                const int32_t *offsets, const uint8_t *W1, const uint8_t *W3,
+                                const float *S1, const float *S3, void *H, hipStream_t st, bool packed) {
+    return packed ? up_fp8<true>(s, A, a_rows, offsets, W1, W3, S1, S3, H, st)
+                  : up_fp8<false>(s, A, a_rows, offsets, W1, W3, S1, S3, H, st);
 }
 
 hipError_t launch_expert_down_fp8(const Shape &s, const void *H, const int32_t *offsets,
-                                  const uint8_t *W2, const float *S2, float *y_perm, hipStream_t st) {
-    const int mt = fp8_tiles(s);
-    const int N = s.d, K = s.d_ff;
-    return mt == 2 ? launch_fp8<2, 8, false, ACT_NONE, false>(s, H, nullptr, offsets, W2, nullptr, S2, nullptr, y_perm, N, K, st)
-                   : launch_fp8<3, 8, false, ACT_NONE, false>(s, H, nullptr, offsets, W2, nullptr, S2, nullptr, y_perm, N, K, st);
+                                  const uint8_t *W2, const float *S2, float *y_perm, hipStream_t st, bool packed) {
+    return packed ? down_fp8<true>(s, H, offsets, W2, S2, y_perm, st) : down_fp8<false>(s, H, offsets, W2, S2, y_perm, st);
 }
 
 }  // namespace moe

@@ -761,7 +761,7 @@ __global__ __launch_bounds__(256) void gemm_bf16_big_kernel(
 // Experts with no rows exit at once.
 constexpr int SK_KC = 128;
 
-template <int MT, int NT, int PF, int KS, bool DUAL, int ACT, bool OUT_BF16>
+template <int MT, int NT, int PF, int KS, bool DUAL, int ACT, bool OUT_BF16, bool PACKED>
 __global__ __launch_bounds__(64 * KS) void gemm_bf16_skinny_kernel(
     const uint16_t *__restrict__ A, const int32_t *__restrict__ a_rows,
     const int32_t *__restrict__ offsets, int E, const uint16_t *__restrict__ B1,
@@ -800,9 +800,12 @@ __global__ __launch_bounds__(64 * KS) void gemm_bf16_skinny_kernel(
     for (int q = 0; q < NB; ++q)
 #pragma unroll
         for (int t = 0; t < NT; ++t)
-            b_row[q][t] = ((DUAL && q) ? B3 : B1) +
-                          ((int64_t)e * N + min(n0 + t * 16 + n, N - 1)) * K +
-                          (int64_t)cb * SK_KC + g * 32;
+            b_row[q][t] = PACKED ? ((DUAL && q) ? B3 : B1) + (int64_t)e * N * K +
+                                       ((int64_t)min(n0 / 16 + t, N / 16 - 1) * (K / SK_KC) + cb) * 2048 +
+                                       lane * 8
+                                 : ((DUAL && q) ? B3 : B1) +
+                                       ((int64_t)e * N + min(n0 + t * 16 + n, N - 1)) * K +
+                                       (int64_t)cb * SK_KC + g * 32;
 
     f32x4_t acc[MT][NB][NT];
 #pragma unroll
@@ -822,7 +825,8 @@ __global__ __launch_bounds__(64 * KS) void gemm_bf16_skinny_kernel(
             for (int t = 0; t < NT; ++t)
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
-                    rb[slot][q][t][j] = *(const uint4 *)(b_row[q][t] + (int64_t)ch * SK_KC + j * 8);
+                    rb[slot][q][t][j] = *(const uint4 *)(b_row[q][t] + (PACKED ? (int64_t)ch * 2048 + j * 512
+                                                                              : (int64_t)ch * SK_KC + j * 8));
     };
     auto load_a = [&](int slot, int ch) {
 #pragma unroll
@@ -1053,7 +1057,7 @@ hipError_t launch_big(const Shape &s, const void *A, const int32_t *a_rows, cons
     return hipGetLastError();
 }
 
-template <int MT, int NT, int PF, bool DUAL, int ACT, bool OUT_BF16>
+template <int MT, int NT, int PF, bool DUAL, int ACT, bool OUT_BF16, bool PACKED>
 hipError_t launch_skinny(const Shape &s, const void *A, const int32_t *a_rows, const int32_t *offsets, const void *B1,
                          const void *B3, void *C, int N, int K, hipStream_t st) {
     const unsigned blocks = (unsigned)s.E * (unsigned)((N + 16 * NT - 1) / (16 * NT));
@@ -1062,11 +1066,11 @@ hipError_t launch_skinny(const Shape &s, const void *A, const int32_t *a_rows, c
     // >= 16 chunks)
     const int nch = K / SK_KC;
     if (blocks < 4096 && nch >= 64) {
-        launch_kernel((gemm_bf16_skinny_kernel<MT, NT, PF, 4, DUAL, ACT, OUT_BF16>),
+        launch_kernel((gemm_bf16_skinny_kernel<MT, NT, PF, 4, DUAL, ACT, OUT_BF16, PACKED>),
                            dim3(blocks), dim3(256), 0, st, (const uint16_t *)A, a_rows, offsets, s.E,
                            (const uint16_t *)B1, (const uint16_t *)B3, C, N, K);
     } else {
-        launch_kernel((gemm_bf16_skinny_kernel<MT, NT, PF, 1, DUAL, ACT, OUT_BF16>),
+        launch_kernel((gemm_bf16_skinny_kernel<MT, NT, PF, 1, DUAL, ACT, OUT_BF16, PACKED>),
                            dim3(blocks), dim3(64), 0, st, (const uint16_t *)A, a_rows, offsets, s.E,
                            (const uint16_t *)B1, (const uint16_t *)B3, C, N, K);
     }
@@ -1082,7 +1086,7 @@ inline int skinny_tiles(const Shape &s, int K) {
     return 0;
 }
 
-template <bool DUAL, int ACT, bool OUT_BF16>
+template <bool DUAL, int ACT, bool OUT_BF16, bool PACKED = false>
 hipError_t launch_skinny_any(const Shape &s, int mt, const void *A, const int32_t *a_rows, const int32_t *offsets,
                              const void *B1, const void *B3, void *C, int N, int K,
                              hipStream_t st) {
@@ -1095,11 +1099,14 @@ hipError_t launch_skinny_any(const Shape &s, int mt, const void *A, const int32_
     // per step, its down projection gaining; the split decode down
     // projection is no faster with them)
     if (!DUAL && !((int64_t)s.E * ((N + 63) / 64) < 4096 && K / SK_KC >= 64)) {
-        if (mt == 2) return launch_skinny<2, 8, 2, DUAL, ACT, OUT_BF16>(s, A, a_rows, offsets, B1, B3, C, N, K, st);
-        return launch_skinny<3, 8, 2, DUAL, ACT, OUT_BF16>(s, A, a_rows, offsets, B1, B3, C, N, K, st);
+        if (mt == 2) return launch_skinny<2, 8, 2, DUAL, ACT, OUT_BF16, PACKED>(s, A, a_rows, offsets, B1, B3, C, N, K, st);
+        return launch_skinny<3, 8, 2, DUAL, ACT, OUT_BF16, PACKED>(s, A, a_rows, offsets, B1, B3, C, N, K, st);
     }
-    if (mt == 2) return launch_skinny<2, DUAL ? 1 : 4, DUAL ? 4 : 2, DUAL, ACT, OUT_BF16>(s, A, a_rows, offsets, B1, B3, C, N, K, st);
-    return launch_skinny<3, DUAL ? 1 : 4, DUAL ? 4 : 2, DUAL, ACT, OUT_BF16>(s, A, a_rows, offsets, B1, B3, C, N, K, st);
+    if (mt == 2)
+        return launch_skinny<2, DUAL ? 1 : 4, DUAL ? 4 : 2, DUAL, ACT, OUT_BF16, PACKED>(s, A, a_rows, offsets, B1, B3,
+                                                                                       C, N, K, st);
+    return launch_skinny<3, DUAL ? 1 : 4, DUAL ? 4 : 2, DUAL, ACT, OUT_BF16, PACKED>(s, A, a_rows, offsets, B1, B3, C,
+                                                                                   N, K, st);
 }
 
 template <int ACT, bool DUAL>
@@ -1171,6 +1178,77 @@ hipError_t launch_expert_down(const Shape &s, const void *H, const int32_t *offs
     case 64:  return launch_gemm<64, 128, 2, 2, false, ACT_NONE, false>(s, H, nullptr, offsets, W2, nullptr, y_perm, s.d, s.d_ff, st);
     default:  return launch_gemm<32, 128, 1, 4, false, ACT_NONE, false>(s, H, nullptr, offsets, W2, nullptr, y_perm, s.d, s.d_ff, st);
     }
+}
+
+// Expert GEMMs of decode-sized batches on weights in the streaming tile
+// layout (pack_stream_kernel): the streaming kernel reads each 16-byte
+// unit of a chunk from where its lane needs it, so every load instruction
+// of a wave covers 1 KB of contiguous memory.  Same products in the same
+// order as on row-major weights, hence the same bits.
+hipError_t launch_expert_up_packed(const Shape &s, const void *x, const int32_t *a_rows, const int32_t *offsets,
+                                   const void *W1, const void *W3, void *H, hipStream_t st) {
+    const int mt = skinny_tiles(s, s.d);
+    if (mt == 0 || s.dtype != 1) return hipErrorInvalidValue;
+    switch (s.act) {
+    case ACT_SWIGLU:
+        return launch_skinny_any<true, ACT_SWIGLU, true, true>(s, mt, x, a_rows, offsets, W1, W3, H, s.d_ff, s.d, st);
+    case ACT_GELU:
+        return launch_skinny_any<false, ACT_GELU, true, true>(s, mt, x, a_rows, offsets, W1, nullptr, H, s.d_ff, s.d,
+                                                              st);
+    default:
+        return launch_skinny_any<false, ACT_RELU, true, true>(s, mt, x, a_rows, offsets, W1, nullptr, H, s.d_ff, s.d,
+                                                              st);
+    }
+}
+
+hipError_t launch_expert_down_packed(const Shape &s, const void *H, const int32_t *offsets, const void *W2,
+                                     float *y_perm, hipStream_t st) {
+    const int mt = skinny_tiles(s, s.d_ff);
+    if (mt == 0 || s.dtype != 1) return hipErrorInvalidValue;
+    return launch_skinny_any<false, ACT_NONE, false, true>(s, mt, H, nullptr, offsets, W2, nullptr, y_perm, s.d,
+                                                           s.d_ff, st);
+}
+
+namespace {
+
+// The streaming tile layout of a [rows][cols] matrix of esz-byte elements
+// (esz = 2: bf16, 1: e4m3 codes; rows % 16 == 0, cols % 128 == 0), in
+// units of 16 bytes (8 / esz ... 16 / esz elements): blocks of 16 rows x
+// 128 columns, block (rb, cb) at index rb * (cols / 128) + cb, each of
+// 128 * esz units.  In row n of a block, unit u covers columns
+// u * 16 / esz .. +16 / esz; with V = 2 * esz units per 32 columns, unit
+// u = V g + r (g = 0..3) is stored at unit position r * 64 + 16 g + n.
+// That is the streaming kernels' lane order: lane l = 16 g + n holds row n
+// and the columns 32 g .. 32 g + 31 of a 128-column chunk, loading unit
+// r of them in its r-th load, so load r of a wave reads positions
+// r * 64 .. r * 64 + 63 of the block.  One thread per output unit.
+__global__ __launch_bounds__(256) void pack_stream_kernel(const uint4 *__restrict__ W, int64_t rows,
+                                                          int64_t cols, int esz, uint4 *__restrict__ out) {
+    const int64_t upr = cols * esz / 16;     // units per row
+    const int64_t nbc = cols / 128;          // blocks across a row
+    const int ub = 128 * esz;                // units per block
+    const int V = 2 * esz;
+    const int64_t total = rows * upr;
+    for (int64_t o = (int64_t)blockIdx.x * 256 + threadIdx.x; o < total; o += (int64_t)gridDim.x * 256) {
+        const int64_t b = o / ub;
+        const int p = (int)(o - b * ub);
+        const int r = p >> 6, g = (p >> 4) & 3, n = p & 15;
+        const int64_t rb = b / nbc, cb = b - rb * nbc;
+        const int64_t i = rb * 16 + n;
+        out[o] = W[i * upr + cb * (8 * esz) + V * g + r];
+    }
+}
+
+}  // namespace
+
+hipError_t launch_pack_stream(int esz, const void *W, int64_t rows, int64_t cols, void *out, hipStream_t st) {
+    const int64_t units = rows * cols * esz / 16;
+    int64_t blocks = (units + 255) / 256;
+    if (blocks > 65536) blocks = 65536;
+    if (blocks < 1) return hipSuccess;
+    launch_kernel(pack_stream_kernel, dim3((unsigned)blocks), dim3(256), 0, st, (const uint4 *)W, rows, cols, esz,
+                  (uint4 *)out);
+    return hipGetLastError();
 }
 
 namespace {

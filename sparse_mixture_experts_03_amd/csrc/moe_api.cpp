@@ -402,11 +402,57 @@ int check_fp8(const Shape &s, const moe_fp8_experts *w) {
     return MOE_OK;
 }
 
-// moe_forward, moe_forward_shared and moe_forward_fp8: sh == nullptr and
-// f8 == nullptr is moe_forward (seven stages); with sh the shared experts
-// run as their own stage between expert-down and the combine, which adds
-// them and the residual; with f8 the expert GEMMs read E4M3 weights.
-int forward_impl(const moe_desc *desc, const moe_shared *sh, const moe_fp8_experts *f8,
+// Validates packed expert weights for this description (format, then shape
+// support, then the pointers).
+int check_packed(const Shape &s, const moe_packed_experts *w) {
+    if (!w) return MOE_ERR_INVALID_ARG;
+    if (w->format != MOE_WEIGHTS_BF16 && w->format != MOE_WEIGHTS_E4M3) return MOE_ERR_INVALID_ARG;
+    if (!moe::fp8_supported(s)) return MOE_ERR_UNSUPPORTED;
+    if (!w->W1 || !w->W2) return MOE_ERR_INVALID_ARG;
+    const bool swiglu = s.act == MOE_ACT_SWIGLU;
+    if (swiglu != (w->W3 != nullptr)) return MOE_ERR_INVALID_ARG;
+    if (w->format == MOE_WEIGHTS_E4M3) {
+        if (!w->s1 || !w->s2 || swiglu != (w->s3 != nullptr)) return MOE_ERR_INVALID_ARG;
+    } else if (w->s1 || w->s2 || w->s3) {
+        return MOE_ERR_INVALID_ARG;
+    }
+    return MOE_OK;
+}
+
+// Expert weights of the weight-streaming kernels: e4m3 codes (row-major or
+// packed) or packed bf16 values.
+struct StreamW {
+    bool e4m3, packed;
+    const void *W1, *W3, *W2;
+    const float *s1, *s3, *s2;
+};
+
+StreamW stream_w(const moe_fp8_experts *w) { return StreamW{true, false, w->W1, w->W3, w->W2, w->s1, w->s3, w->s2}; }
+StreamW stream_w(const moe_packed_experts *w) {
+    return StreamW{w->format == MOE_WEIGHTS_E4M3, true, w->W1, w->W3, w->W2, w->s1, w->s3, w->s2};
+}
+
+hipError_t stream_up(const Shape &s, const void *A, const int32_t *a_rows, const int32_t *offsets, const StreamW &w,
+                     void *H, hipStream_t st) {
+    if (w.e4m3)
+        return moe::launch_expert_up_fp8(s, A, a_rows, offsets, (const uint8_t *)w.W1, (const uint8_t *)w.W3, w.s1,
+                                         w.s3, H, st, w.packed);
+    return moe::launch_expert_up_packed(s, A, a_rows, offsets, w.W1, w.W3, H, st);
+}
+
+hipError_t stream_down(const Shape &s, const void *H, const int32_t *offsets, const StreamW &w, float *y_perm,
+                       hipStream_t st) {
+    if (w.e4m3) return moe::launch_expert_down_fp8(s, H, offsets, (const uint8_t *)w.W2, w.s2, y_perm, st, w.packed);
+    return moe::launch_expert_down_packed(s, H, offsets, w.W2, y_perm, st);
+}
+
+// moe_forward, moe_forward_shared, moe_forward_fp8 and moe_forward_packed:
+// sh == nullptr and f8 == nullptr is moe_forward (seven stages); with sh the
+// shared experts run as their own stage between expert-down and the
+// combine, which adds them and the residual; with f8 the expert GEMMs are
+// the weight-streaming kernels on E4M3 or packed weights (already
+// validated by the caller, after the description).
+int forward_impl(const moe_desc *desc, const moe_shared *sh, const StreamW *f8,
                  const void *x, const float *W_r, const float *bias, const float *noise,
                  const void *W1, const void *W3, const void *W2, void *y, int32_t *topk_idx,
                  float *gates, int32_t *routed_counts, int32_t *kept_counts, int32_t *offsets,
@@ -417,7 +463,6 @@ int forward_impl(const moe_desc *desc, const moe_shared *sh, const moe_fp8_exper
     if (rc != MOE_OK) return rc;
     if (f8) {
         if (!x || !W_r || !y) return MOE_ERR_INVALID_ARG;
-        if ((rc = check_fp8(s, f8)) != MOE_OK) return rc;
     } else {
         if (!x || !W_r || !W1 || !W2 || !y) return MOE_ERR_INVALID_ARG;
         if ((s.act == MOE_ACT_SWIGLU) != (W3 != nullptr)) return MOE_ERR_INVALID_ARG;
@@ -478,14 +523,14 @@ int forward_impl(const moe_desc *desc, const moe_shared *sh, const moe_fp8_exper
     // read from x through token_of_row, so x_perm is not materialised here
     ev.around_next_launch();  // events before and after expert-up
     const hipError_t up_err =
-        f8 ? moe::launch_expert_up_fp8(s, x, token_of_row, offsets, f8->W1, f8->W3, f8->s1, f8->s3, H, st)
+        f8 ? stream_up(s, x, token_of_row, offsets, *f8, H, st)
            : moe::launch_expert_up(s, x, token_of_row, offsets, W1, W3, H, st, tctr);
     moe::next_launch_events() = moe::LaunchEvents{nullptr, nullptr};
     MOE_TRY(up_err);
-    // the e4m3 path never splits K (streaming kernel only)
+    // the streaming path never splits K across blocks
     float *part2 = (!f8 && L.y_perm2) ? at<float>(ws, L.y_perm2) : nullptr;
     if (f8)
-        MOE_TRY(moe::launch_expert_down_fp8(s, H, offsets, f8->W2, f8->s2, y_perm, st));
+        MOE_TRY(stream_down(s, H, offsets, *f8, y_perm, st));
     else
         MOE_TRY(moe::launch_expert_down(s, H, offsets, W2, y_perm, part2, st, tctr ? tctr + CW : nullptr));
     if (!sh) {
@@ -632,7 +677,58 @@ int moe_forward_fp8(const moe_desc *desc, const void *x, const float *W_r, const
                     int32_t *row_of_slot, int32_t *token_of_row, uint8_t *dropped, float *stats,
                     void *ws, size_t ws_bytes, void *stream) {
     if (!w) return MOE_ERR_INVALID_ARG;
-    return forward_impl(desc, nullptr, w, x, W_r, bias, noise, nullptr, nullptr, nullptr, y,
+    Shape s;
+    int rc = check_desc(desc, &s);
+    if (rc != MOE_OK) return rc;
+    if (!x || !W_r || !y) return MOE_ERR_INVALID_ARG;
+    if ((rc = check_fp8(s, w)) != MOE_OK) return rc;
+    const StreamW sw = stream_w(w);
+    return forward_impl(desc, nullptr, &sw, x, W_r, bias, noise, nullptr, nullptr, nullptr, y,
+                        topk_idx, gates, routed_counts, kept_counts, offsets, row_of_slot,
+                        token_of_row, dropped, stats, ws, ws_bytes, stream);
+}
+
+int moe_pack_stream(int32_t elem_bytes, const void *W, int64_t rows, int64_t cols, void *W_packed,
+                    void *stream) {
+    if (elem_bytes != 1 && elem_bytes != 2) return MOE_ERR_INVALID_ARG;
+    if (rows < 0 || rows % 16 != 0 || cols < 128 || cols % 128 != 0) return MOE_ERR_INVALID_ARG;
+    if (rows == 0) return MOE_OK;
+    if (!W || !W_packed) return MOE_ERR_INVALID_ARG;
+    MOE_TRY(moe::launch_pack_stream(elem_bytes, W, rows, cols, W_packed, (hipStream_t)stream));
+    return MOE_OK;
+}
+
+int moe_expert_ffn_packed(const moe_desc *desc, const void *x_perm, const int32_t *offsets,
+                          const moe_packed_experts *w, float *y_perm, void *ws, size_t ws_bytes,
+                          void *stream) {
+    Shape s;
+    int rc = check_desc(desc, &s);
+    if (rc != MOE_OK) return rc;
+    if (!x_perm || !offsets || !y_perm) return MOE_ERR_INVALID_ARG;
+    if ((rc = check_packed(s, w)) != MOE_OK) return rc;
+    if ((rc = check_ws(s, ws, ws_bytes)) != MOE_OK) return rc;
+    const Layout L = layout(s);
+    hipStream_t st = (hipStream_t)stream;
+    void *H = at<char>(ws, L.H);
+    const StreamW sw = stream_w(w);
+    MOE_TRY(stream_up(s, x_perm, nullptr, offsets, sw, H, st));
+    MOE_TRY(stream_down(s, H, offsets, sw, y_perm, st));
+    return MOE_OK;
+}
+
+int moe_forward_packed(const moe_desc *desc, const void *x, const float *W_r, const float *bias,
+                       const float *noise, const moe_packed_experts *w, void *y, int32_t *topk_idx,
+                       float *gates, int32_t *routed_counts, int32_t *kept_counts, int32_t *offsets,
+                       int32_t *row_of_slot, int32_t *token_of_row, uint8_t *dropped, float *stats,
+                       void *ws, size_t ws_bytes, void *stream) {
+    if (!w) return MOE_ERR_INVALID_ARG;
+    Shape s;
+    int rc = check_desc(desc, &s);
+    if (rc != MOE_OK) return rc;
+    if (!x || !W_r || !y) return MOE_ERR_INVALID_ARG;
+    if ((rc = check_packed(s, w)) != MOE_OK) return rc;
+    const StreamW sw = stream_w(w);
+    return forward_impl(desc, nullptr, &sw, x, W_r, bias, noise, nullptr, nullptr, nullptr, y,
                         topk_idx, gates, routed_counts, kept_counts, offsets, row_of_slot,
                         token_of_row, dropped, stats, ws, ws_bytes, stream);
 }

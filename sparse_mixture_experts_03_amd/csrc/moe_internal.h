@@ -172,11 +172,26 @@ hipError_t launch_quantize_e4m3(int dtype, const void *W, int64_t rows, int64_t 
 // The e4m3-weight expert GEMMs exist for the weight-streaming shapes only:
 // bf16 activations, at most 48 rows per expert, d and d_ff multiples of 128.
 bool fp8_supported(const Shape &s);
+// packed: the codes are in the streaming tile layout (launch_pack_stream)
+// instead of row-major.
 hipError_t launch_expert_up_fp8(const Shape &s, const void *A, const int32_t *a_rows,
                                 const int32_t *offsets, const uint8_t *W1, const uint8_t *W3,
-                                const float *S1, const float *S3, void *H, hipStream_t st);
+                                const float *S1, const float *S3, void *H, hipStream_t st,
+                                bool packed = false);
 hipError_t launch_expert_down_fp8(const Shape &s, const void *H, const int32_t *offsets,
-                                  const uint8_t *W2, const float *S2, float *y_perm, hipStream_t st);
+                                  const uint8_t *W2, const float *S2, float *y_perm, hipStream_t st,
+                                  bool packed = false);
+
+// ---- weights in the streaming tile layout ------------------------------
+// [rows][cols] of esz-byte elements (2: bf16, 1: e4m3 codes) -> the
+// layout the weight-streaming kernels read with one contiguous KB per load
+// instruction (rows % 16 == 0, cols % 128 == 0; see pack_stream_kernel).
+hipError_t launch_pack_stream(int esz, const void *W, int64_t rows, int64_t cols, void *out, hipStream_t st);
+// bf16 expert GEMMs on packed weights, for the shapes fp8_supported() accepts
+hipError_t launch_expert_up_packed(const Shape &s, const void *x, const int32_t *a_rows, const int32_t *offsets,
+                                   const void *W1, const void *W3, void *H, hipStream_t st);
+hipError_t launch_expert_down_packed(const Shape &s, const void *H, const int32_t *offsets, const void *W2,
+                                     float *y_perm, hipStream_t st);
 
 // ---- backward (training gradients) --------------------------------------
 // batched transposes of the expert weights; with row offsets (may be

@@ -105,6 +105,74 @@ def run_forward_fp8(w, dw, dt, f8, stream=None):
     return {k: v.cpu() for k, v in out.items()}
 
 
+def device_packed(w, desc, dw, f8=None):
+    """Packed copies of the device expert weights (bf16, f8 None) or of the
+    e4m3 codes f8, and their moe_packed_experts (the tensors ride along)."""
+    if f8 is None:
+        pk = B.pack_experts(dw["W1"], dw.get("W3"), dw["W2"])
+        return pk, B.make_packed(desc, "bf16", pk["p1"], pk["p3"], pk["p2"])
+    pk = B.pack_experts(f8["q1"], f8["q3"], f8["q2"])
+    return pk, B.make_packed(desc, "e4m3", pk["p1"], pk["p3"], pk["p2"], f8["s1"], f8["s3"], f8["s2"])
+
+
+def run_forward_packed(w, dw, dt, f8=None, stream=None):
+    """moe_forward_packed on packed copies of the bf16 weights (f8 None) or
+    of the e4m3 codes f8."""
+    desc = B.desc_for(w)
+    out = B.alloc_outputs(desc)
+    ws = B.workspace(desc)
+    tensors, pk = device_packed(w, desc, dw, f8)
+    B.moe_forward_packed(desc, pk, dt["x"], dw["Wr"], dw["bias"], dt["noise"], out["y"], ws,
+                         topk_idx=out["topk_idx"], gates=out["gates"],
+                         routed_counts=out["routed_counts"], kept_counts=out["kept_counts"],
+                         offsets=out["offsets"], row_of_slot=out["row_of_slot"],
+                         token_of_row=out["token_of_row"], dropped=out["dropped"],
+                         stats=out["stats"], stream=stream)
+    torch.cuda.synchronize()
+    del tensors
+    return {k: v.cpu() for k, v in out.items()}
+
+
+def assert_outputs_identical(a, b):
+    """Every output of two forward calls (host tensors), bit for bit."""
+    assert a.keys() == b.keys()
+    for k in a:
+        x, y = a[k].contiguous().view(torch.uint8), b[k].contiguous().view(torch.uint8)
+        assert x.shape == y.shape, k
+        bad = int((x != y).sum())
+        assert bad == 0, f"{k}: {bad} bytes differ"
+
+
+# ---- the streaming tile layout of include/moe.h, for the packed tests ----
+
+def pack_loops(Wh):
+    """The streaming tile layout by its definition, element by element (small matrices)."""
+    rows, cols = Wh.shape
+    esz = Wh.dtype.itemsize
+    per_unit = 16 // esz
+    V = 2 * esz
+    out = np.zeros(rows * cols, Wh.dtype)
+    for i in range(rows):
+        rb, n = divmod(i, 16)
+        for j in range(cols):
+            cb, c = divmod(j, 128)
+            u, e = divmod(c, per_unit)
+            g, r = divmod(u, V)
+            block = rb * (cols // 128) + cb
+            pos = block * 128 * esz + r * 64 + 16 * g + n
+            out[pos * per_unit + e] = Wh[i, j]
+    return out.reshape(rows, cols)
+
+
+def pack_reshape(Wh):
+    """The same layout as one reshape / transpose: [rb][n][cb][g][r][e] ->
+    [rb][cb][r][g][n][e]."""
+    rows, cols = Wh.shape
+    esz = Wh.dtype.itemsize
+    u = Wh.reshape(rows // 16, 16, cols // 128, 4, 2 * esz, 16 // esz)
+    return np.ascontiguousarray(u.transpose(0, 2, 4, 3, 1, 5)).reshape(rows, cols)
+
+
 def shared_arg(w, desc, dw, dt):
     """moe_shared for the workload's shared experts and residual."""
     return B.make_shared(desc, dw.get("Ws1"), dw.get("Ws3"), dw.get("Ws2"),

@@ -216,6 +216,77 @@ def test_fp8_validation_before_launch(desc_kw, w, code):
                                None) == -1
 
 
+# ---- weights in the streaming tile layout ------------------------------------
+
+def test_pack_stream_validation():
+    lib = B.load()
+    assert lib.moe_pack_stream(3, FAKE, 16, 128, FAKE, None) == -1      # element size
+    assert lib.moe_pack_stream(2, FAKE, 24, 128, FAKE, None) == -1      # rows % 16
+    assert lib.moe_pack_stream(2, FAKE, 16, 192, FAKE, None) == -1      # cols % 128
+    assert lib.moe_pack_stream(1, FAKE, 16, 64, FAKE, None) == -1       # cols < 128
+    assert lib.moe_pack_stream(1, FAKE, -16, 128, FAKE, None) == -1
+    assert lib.moe_pack_stream(2, None, 16, 128, FAKE, None) == -1
+    assert lib.moe_pack_stream(2, FAKE, 16, 128, None, None) == -1
+    assert lib.moe_pack_stream(1, None, 0, 128, None, None) == 0        # nothing to do
+
+
+@pytest.mark.parametrize("esz", [2, 1], ids=["bf16", "e4m3"])
+def test_pack_layout_reshape_matches_definition(esz):
+    """The packed tests' two statements of the streaming tile layout agree:
+    element-wise loops over the header's definition, and one reshape."""
+    import numpy as np
+    import harness as H
+    rng = np.random.default_rng(3)
+    Wh = rng.integers(0, 1 << (8 * esz), size=(32, 256)).astype(np.uint16 if esz == 2 else np.uint8)
+    np.testing.assert_array_equal(H.pack_reshape(Wh), H.pack_loops(Wh))
+    # the definition is a permutation, and the block holding (i, j) is
+    # rb * cols / 128 + cb
+    assert sorted(H.pack_loops(Wh).ravel().tolist()) == sorted(Wh.ravel().tolist())
+    blk = H.pack_loops(Wh).reshape(-1)[: 128 * 16]
+    assert sorted(blk.tolist()) == sorted(Wh[:16, :128].ravel().tolist())
+
+
+def _pk(fmt=2, W3=FAKE, s1=FAKE, s3=FAKE, s2=FAKE):
+    return B.MoePackedExperts(fmt, FAKE, W3, FAKE, s1, s3, s2)
+
+
+@pytest.mark.parametrize("desc_kw,w,code", [
+    (dict(T=32, d=512, d_ff=768), _pk(), 0),                              # e4m3, SwiGLU
+    (dict(T=32, d=512, d_ff=768), _pk(fmt=1, s1=None, s3=None, s2=None), 0),   # bf16
+    (dict(T=32, d=512, d_ff=768), _pk(fmt=3), -1),                        # unknown format
+    (dict(T=32, d=512, d_ff=768), _pk(fmt=1), -1),                        # scales with bf16
+    (dict(T=32, d=512, d_ff=768), _pk(s2=None), -1),                      # an e4m3 scale missing
+    (dict(T=32, d=512, d_ff=768), _pk(W3=None), -1),                      # SwiGLU needs W3
+    (dict(T=32, d=512, d_ff=768, act="gelu"), _pk(s3=None), -1),          # W3 only for SwiGLU
+    (dict(T=32, d=512, d_ff=768, act="gelu"), _pk(W3=None, s3=None), 0),
+    (dict(T=100, d=512, d_ff=768), _pk(), -2),                            # > 48 rows per expert
+    (dict(T=4096, d=768, d_ff=3072, E=128, k=1, cf=1.25, act="gelu"),
+     _pk(fmt=1, W3=None, s1=None, s3=None, s2=None), 0),                  # Switch: 40 rows
+    (dict(T=32, d=576, d_ff=768), _pk(), -2),                             # d % 128
+    (dict(T=32, d=512, d_ff=768, dtype="f32"), _pk(), -2),                # bf16 activations only
+])
+def test_packed_validation_before_launch(desc_kw, w, code):
+    lib = B.load()
+    kw = dict(E=8, k=2)
+    kw.update(desc_kw)
+    desc = B.make_desc(kw.pop("T"), kw.pop("d"), kw.pop("d_ff"), kw.pop("E"), kw.pop("k"), **kw)
+    d = ctypes.byref(desc)
+    need = B.moe_workspace_size(desc)
+    if code == 0:
+        # valid: shown by reaching the workspace check (one byte short)
+        assert lib.moe_forward_packed(d, FAKE, FAKE, None, None, ctypes.byref(w), FAKE, *([None] * 9),
+                                      FAKE, need - 1, None) == -4
+        assert lib.moe_expert_ffn_packed(d, FAKE, FAKE, ctypes.byref(w), FAKE, FAKE, need - 1, None) == -4
+    else:
+        assert lib.moe_forward_packed(d, FAKE, FAKE, None, None, ctypes.byref(w), FAKE, *([None] * 9),
+                                      FAKE, need, None) == code
+        assert lib.moe_expert_ffn_packed(d, FAKE, FAKE, ctypes.byref(w), FAKE, FAKE, need, None) == code
+    assert lib.moe_forward_packed(d, FAKE, FAKE, None, None, None, FAKE, *([None] * 9), FAKE, need,
+                                  None) == -1
+    assert lib.moe_forward_packed(d, None, FAKE, None, None, ctypes.byref(w), FAKE, *([None] * 9), FAKE,
+                                  need, None) == -1
+
+
 def test_header_compiles_as_c_and_links(tmp_path):
     """include/moe.h is a C header: a C11 program compiled by gcc against it
     and linked to libmoe.so calls the host-only entry points."""
