@@ -1099,12 +1099,23 @@ hipError_t launch_skinny_any(const Shape &s, int mt, const void *A, const int32_
     // per step, its down projection gaining; the split decode down
     // projection is no faster with them)
     if (!DUAL && !((int64_t)s.E * ((N + 63) / 64) < 4096 && K / SK_KC >= 64)) {
+        // on packed weights with a short K (fewer than 16 chunks: the Switch
+        // layer's up projection) 64 rows per wave with a 4-chunk ring (up
+        // projection 150 against 146 us; its down projection, 24 chunks,
+        // keeps 128 rows: 126 against 141 us)
+        if (PACKED && K / SK_KC < 16) {
+            if (mt == 2) return launch_skinny<2, 4, 4, DUAL, ACT, OUT_BF16, PACKED>(s, A, a_rows, offsets, B1, B3, C, N, K, st);
+            return launch_skinny<3, 4, 4, DUAL, ACT, OUT_BF16, PACKED>(s, A, a_rows, offsets, B1, B3, C, N, K, st);
+        }
         if (mt == 2) return launch_skinny<2, 8, 2, DUAL, ACT, OUT_BF16, PACKED>(s, A, a_rows, offsets, B1, B3, C, N, K, st);
         return launch_skinny<3, 8, 2, DUAL, ACT, OUT_BF16, PACKED>(s, A, a_rows, offsets, B1, B3, C, N, K, st);
     }
+    // (on packed weights a one-matrix product with two A tiles takes 32
+    // weight rows per wave instead of 64: Mixtral decode down projection 162
+    // against 159 us)
     if (mt == 2)
-        return launch_skinny<2, DUAL ? 1 : 4, DUAL ? 4 : 2, DUAL, ACT, OUT_BF16, PACKED>(s, A, a_rows, offsets, B1, B3,
-                                                                                       C, N, K, st);
+        return launch_skinny<2, DUAL ? 1 : (PACKED ? 2 : 4), DUAL ? 4 : 2, DUAL, ACT, OUT_BF16, PACKED>(
+            s, A, a_rows, offsets, B1, B3, C, N, K, st);
     return launch_skinny<3, DUAL ? 1 : 4, DUAL ? 4 : 2, DUAL, ACT, OUT_BF16, PACKED>(s, A, a_rows, offsets, B1, B3, C,
                                                                                    N, K, st);
 }
