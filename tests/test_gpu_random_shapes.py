@@ -4,7 +4,9 @@ activation, capacity factor and dtype drawn within the supported ranges
 hand-picked cases (routing bit-exact, statistics, y within tolerance,
 fully dropped tokens exactly zero); likewise with 1-3 shared experts and
 the residual, with e4m3 expert weights (decode-sized batches, codes and
-scales bit-exact), and for the backward (every gradient within 2e-2 of
+scales bit-exact), with bf16 weights and e4m3 codes in the streaming tile
+layout (decode-sized batches, bit for bit equal to the row-major entry
+points), and for the backward (every gradient within 2e-2 of
 its largest reference value for bf16 layers, 1e-5 for fp32 ones).  The draws are fixed (seed 2024), so a
 failure names its case."""
 import numpy as np
@@ -94,6 +96,8 @@ def _draw_bwd_f32(i):
 
 SHARED_CASES = [_draw_shared(i) for i in range(8)]
 FP8_CASES = [_draw_fp8(i) for i in range(10)]
+# weight-streaming layers again (other draws), for packed weights
+PACKED_CASES = [_draw_fp8(i) for i in range(10, 20)]
 BWD_CASES = [_draw_bwd(i) for i in range(10)] + [_draw_bwd_f32(i) for i in range(6)]
 
 
@@ -127,6 +131,25 @@ def test_random_shape_fp8_matches_oracle(w):
     y = H.y_float(got["y"])
     H.assert_y_close(w, y, ref["y"])
     assert (y[(ref["row_of_slot"] < 0).all(axis=1)] == 0).all()
+
+
+@pytest.mark.parametrize("w", PACKED_CASES, ids=_ids)
+def test_random_shape_packed_matches_row_major_and_oracle(w):
+    """Packed bf16 weights give moe_forward's outputs bit for bit and packed
+    e4m3 codes moe_forward_fp8's; both match the oracle."""
+    print(f"[rand packed] {w}", flush=True)
+    wt, tk = H.prepare(w)
+    dw, dt = H.device_weights(w, wt), H.device_tokens(w, tk)
+    got = H.run_forward_packed(w, dw, dt)
+    H.assert_outputs_identical(got, H.run_forward(w, dw, dt))
+    ref = H.reference(w, wt, tk)
+    H.assert_routing_exact(w, got, ref)
+    H.assert_y_close(w, H.y_float(got["y"]), ref["y"])
+    f8 = H.device_fp8(dw)
+    got8 = H.run_forward_packed(w, dw, dt, f8)
+    H.assert_outputs_identical(got8, H.run_forward_fp8(w, dw, dt, f8))
+    qref = H.quantize_ref(wt)
+    H.assert_y_close(w, H.y_float(got8["y"]), H.reference_fp8(w, wt, tk, qref)["y"])
 
 
 @pytest.mark.parametrize("w", BWD_CASES, ids=_ids)
