@@ -49,8 +49,9 @@ Switch-style and fine-grained Zipf layers, HBM-bound, each timed over
 fill) before every step (median, minimum, 90th percentile), against 8 TB/s
 over their algorithmic bytes: the touched experts' weights (from the run's
 kept counts) + x + y + W_r (+ the noise input); plus their dominant
-kernel's event-timed rate.  "sclk" samples the shader clock (amdsmi) while
-prefill steps run back to back for about a second; "cpu_baseline_1thread"
+kernel's event-timed rate.  "sclk" samples the shader clock and socket
+power (amdsmi; each refresh of its metrics table counted once) while
+prefill steps run back to back for about three seconds; "cpu_baseline_1thread"
 times the oracle on one host thread for the tiny layer and the decode
 layer.
 
@@ -436,11 +437,15 @@ def hbm_layer_object(w, steps, warmup=5, packed=False):
     }
 
 
-def sample_sclk(step, seconds=1.0, period_s=0.002):
-    """The shader clock while ``step`` runs back to back for about
-    ``seconds``: amdsmi's GPU metrics polled from a second thread; returns
-    the median and range of the samples in MHz (None if amdsmi is not
-    usable here)."""
+def sample_sclk(step, seconds=2.0, period_s=0.002):
+    """The shader clock (and socket power) while ``step`` runs back to back
+    for about ``seconds``, from amdsmi's GPU metrics polled from a second
+    thread.  The firmware refreshes that table only every few hundred ms,
+    so consecutive polls mostly return the same snapshot: a snapshot counts
+    once (a new value of the accumulated gfx activity marks a refresh), and
+    the first one seen after the steps start is left out (it may predate
+    them).  Returns the median and range over those snapshots (None if
+    amdsmi is not usable here)."""
     import threading
 
     import torch
@@ -451,32 +456,42 @@ def sample_sclk(step, seconds=1.0, period_s=0.002):
     except Exception as e:  # noqa: BLE001 -- reported, never fatal
         return {"mhz": None, "reason": f"amdsmi unavailable: {e}"[:160]}
 
+    def num(v):
+        return float(v) if isinstance(v, (int, float)) else None
+
     def read():
         m = amdsmi.amdsmi_get_gpu_metrics_info(h)
+        clk = None
         v = m.get("current_gfxclks")
         if isinstance(v, (list, tuple)):
             v = [c for c in v if isinstance(c, (int, float)) and 0 < c < 10000]
             if v:
-                return float(np.mean(v))
-        v = m.get("current_gfxclk")
-        if isinstance(v, (int, float)) and 0 < v < 10000:
-            return float(v)
-        return None
+                clk = float(np.mean(v))
+        if clk is None:
+            c = num(m.get("current_gfxclk"))
+            clk = c if c is not None and 0 < c < 10000 else None
+        return clk, num(m.get("current_socket_power")), m.get("gfx_activity_acc")
 
-    samples, stop = [], threading.Event()
+    snaps, stop = [], threading.Event()
+    started = threading.Event()
 
     def poll():
+        last = None
         while not stop.is_set():
             try:
-                v = read()
+                clk, pw, acc = read()
             except Exception:  # noqa: BLE001
-                v = None
-            if v is not None:
-                samples.append(v)
+                clk, pw, acc = None, None, None
+            key = (acc, clk, pw)
+            if clk is not None and key != last:
+                snaps.append((started.is_set(), clk, pw))
+                last = key
             time.sleep(period_s)
 
     th = threading.Thread(target=poll, daemon=True)
     th.start()
+    time.sleep(0.01)
+    started.set()
     t0 = time.perf_counter()
     n = 0
     while time.perf_counter() - t0 < seconds:
@@ -490,15 +505,19 @@ def sample_sclk(step, seconds=1.0, period_s=0.002):
         amdsmi.amdsmi_shut_down()
     except Exception:  # noqa: BLE001
         pass
-    if not samples:
-        return {"mhz": None, "reason": "no clock samples from amdsmi"}
-    a = np.array(samples)
-    busy = a[a >= 500.0]          # samples at idle clocks (before the first step lands) left out
-    a = busy if len(busy) else a
-    return {"mhz": round(float(np.median(a)), 1), "min": round(float(a.min()), 1),
-            "max": round(float(a.max()), 1), "samples": len(a), "steps": n,
-            "source": "amdsmi gpu metrics (current_gfxclks, mean over XCDs), polled every 2 ms; "
-                      "samples below 500 MHz (idle) left out"}
+    # snapshots refreshed after the steps began, less the first of them
+    during = [(c, p) for after, c, p in snaps if after][1:]
+    if not during:
+        return {"mhz": None, "reason": "no refreshed clock snapshot from amdsmi during the steps"}
+    clk = np.array([c for c, _ in during])
+    pw = np.array([p for _, p in during if p is not None])
+    out = {"mhz": round(float(np.median(clk)), 1), "min": round(float(clk.min()), 1),
+           "max": round(float(clk.max()), 1), "snapshots": len(during), "steps": n,
+           "source": "amdsmi gpu metrics (current_gfxclks, mean over XCDs); each refresh of the table "
+                     "counted once, the first after the steps began left out"}
+    if len(pw):
+        out["socket_power_w"] = round(float(np.median(pw)), 1)
+    return out
 
 
 def cpu_one_thread(seed=0):
@@ -803,7 +822,7 @@ def main():
         print(json.dumps(line), flush=True)
         return
     res = run_workload(w, args.steps, args.warmup,
-                       sclk_seconds=1.0 if w.name == "mixtral_prefill" else 0.0, packed=args.packed)
+                       sclk_seconds=3.0 if w.name == "mixtral_prefill" else 0.0, packed=args.packed)
     ms_step = res["elapsed"] * 1e3 / res["steps"]
     tokens_s = w.T * res["steps"] / res["elapsed"]
     n_up = 2 if w.act == "swiglu" else 1
