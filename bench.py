@@ -24,6 +24,9 @@ before timing, into the streaming tile layout (moe_pack_stream; then
 moe_forward_packed), which gives the same results bit for bit as row-major
 weights; each of their objects carries the row-major entry point's
 (moe_forward, moe_forward_fp8) figures beside, under "row_major".
+"switch_fp8" is the Switch layer again with its expert weights quantised
+to e4m3 and packed before timing, against 8 TB/s over its bytes (1-byte
+codes plus a 4-byte scale per weight row).
 
 Roofline of the dominant kernel (the expert up-projection, a grouped GEMM
 on bf16 MFMA): algorithmic FLOPs per launch = N_kept * 2 * n_up * d * d_ff
@@ -351,7 +354,14 @@ def run_cold(w, steps, warmup, seed=0, flush_bytes=512 << 20, packed=False):
     desc = B.desc_for(w)
     ws = B.workspace(desc)
     out = B.alloc_outputs(desc)
-    pk = pack_weights(w, desc, dw, None)[0] if packed else None
+    f8 = None
+    if w.weights == "e4m3":
+        # post-training quantisation of the expert weights, before timing
+        f8 = B.quantize_experts(dw["W1"], dw["W3"], dw["W2"])
+        for key in ("W1", "W3", "W2"):
+            dw[key] = None
+    pk = pack_weights(w, desc, dw, f8)[0] if packed else None
+    fp8 = B.make_fp8(desc, f8["q1"], f8["q3"], f8["q2"], f8["s1"], f8["s3"], f8["s2"]) if f8 and not packed else None
     scratch = torch.empty(flush_bytes // 4, dtype=torch.float32, device="cuda")
     stream = torch.cuda.current_stream()
     times = []
@@ -361,6 +371,8 @@ def run_cold(w, steps, warmup, seed=0, flush_bytes=512 << 20, packed=False):
         a.record(stream)
         if pk is not None:
             B.moe_forward_packed(desc, pk, x, dw["Wr"], dw["bias"], noise, out["y"], ws, stream=stream)
+        elif fp8 is not None:
+            B.moe_forward_fp8(desc, fp8, x, dw["Wr"], dw["bias"], noise, out["y"], ws, stream=stream)
         else:
             B.moe_forward(desc, x, dw["Wr"], dw["bias"], noise, dw["W1"], dw["W3"], dw["W2"], out["y"], ws,
                           stream=stream)
@@ -383,7 +395,10 @@ def layer_bytes(w, n_kept, touched):
     noise input when the workload has one."""
     n_mat = 3 if w.act == "swiglu" else 2
     eb = 2 if w.dtype == "bf16" else 4
-    b = touched * n_mat * w.d * w.d_ff * eb + 2 * w.T * w.d * eb + w.E * w.d * 4
+    wb = 1 if w.weights == "e4m3" else eb      # e4m3: 1-byte codes, a 4-byte scale per weight row
+    b = touched * n_mat * w.d * w.d_ff * wb + 2 * w.T * w.d * eb + w.E * w.d * 4
+    if w.weights == "e4m3":
+        b += touched * ((n_mat - 1) * w.d_ff + w.d) * 4
     if w.noise_std > 0:
         b += w.T * w.E * 4
     if w.zipf_s > 0:
@@ -395,10 +410,12 @@ def kernel_bytes(w, stage, n_kept, touched):
     """Algorithmic bytes of one expert GEMM launch: its touched weights, the
     rows of A it reads and the rows it writes."""
     eb = 2 if w.dtype == "bf16" else 4
+    f8 = w.weights == "e4m3"
+    wb = 1 if f8 else eb
     if stage == "expert_up":
         n_up = 2 if w.act == "swiglu" else 1
-        return int(touched * n_up * w.d_ff * w.d * eb + n_kept * (w.d + w.d_ff) * eb)
-    return int(touched * w.d * w.d_ff * eb + n_kept * w.d_ff * eb + n_kept * w.d * 4)
+        return int(touched * n_up * w.d_ff * (w.d * wb + (4 if f8 else 0)) + n_kept * (w.d + w.d_ff) * eb)
+    return int(touched * w.d * (w.d_ff * wb + (4 if f8 else 0)) + n_kept * w.d_ff * eb + n_kept * w.d * 4)
 
 
 def hbm_layer_object(w, steps, warmup=5, packed=False):
@@ -421,6 +438,7 @@ def hbm_layer_object(w, steps, warmup=5, packed=False):
         "workload": w.name, "T": w.T, "d": w.d, "d_ff": w.d_ff, "E": w.E, "k": w.k,
         "gate": w.gate, "act": w.act, "capacity_factor": w.cf,
         "kept_rows": res["n_kept"], "touched_experts": res["touched"],
+        "weights": "e4m3" if w.weights == "e4m3" else "bf16",
         "weight_layout": LAYOUT_PACKED if packed else "row-major (moe_forward)",
         "value": round(w.T / (med * 1e-3), 1), "unit": "tokens/s", "steps": steps,
         "cache": "last-level cache flushed (512 MB device fill) before every timed step",
@@ -907,6 +925,12 @@ def main():
                     "frac": rr["roofline"]["frac"]}
             log(f"[bench] {name}: median {line[name]['ms_per_step_median_min_p90'][0]:.4f} ms/step "
                 f"(cold), {line[name]['roofline']['frac']:.3f} of HBM")
+        # the Switch layer with e4m3 expert weights (quantised and packed
+        # before timing), against 8 TB/s over its bytes (1-byte codes + scales)
+        log(f"[bench] switch_fp8: {args.layer_steps} warm + {args.layer_steps} cold steps ...")
+        line["switch_fp8"] = hbm_layer_object(synth.WORKLOADS["switch_fp8"], args.layer_steps, packed=True)
+        log(f"[bench] switch_fp8: median {line['switch_fp8']['ms_per_step_median_min_p90'][0]:.4f} ms/step "
+            f"(cold), {line['switch_fp8']['roofline']['frac']:.3f} of HBM")
     if res["sclk"] is not None:
         line["sclk"] = res["sclk"]
     if not args.no_cpu:

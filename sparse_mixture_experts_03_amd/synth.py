@@ -95,6 +95,10 @@ WORKLOADS = {
     # library's or the oracle's, not this module's).
     "mixtral_decode_fp8": Workload("mixtral_decode_fp8", 32, 4096, 14336, 8, 2, "renorm", 0.0,
                                    "swiglu", "bf16", x_rmsnorm=True, steps=100, weights="e4m3"),
+    # The Switch-shape layer with e4m3 expert weights (at most 40 rows per
+    # expert: the weight-streaming kernels).
+    "switch_fp8": Workload("switch_fp8", 4096, 768, 3072, 128, 1, "switch", 1.25, "gelu", "bf16",
+                           noise_std=1.0 / 128, weights="e4m3"),
 }
 
 
