@@ -816,7 +816,15 @@ __global__ __launch_bounds__(64 * KS) void gemm_bf16_skinny_kernel(
             for (int t = 0; t < NT; ++t) acc[m][q][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
     uint4 rb[PF][NB][NT][4];
-    uint4 ra[2][MT][4];
+    // A1: one buffer for the rows of A, refilled after the chunk's MFMAs, on
+    // packed weights with a 2-chunk ring and no K split.  The one-matrix
+    // 64-row waves then fit in 256 registers and two share a SIMD, each
+    // covering the other's start and epilogue (the Switch layer's up
+    // projection 147 -> 133 us with bf16 weights, 145 -> 110 us with e4m3
+    // codes); the e4m3 decode up projection, still one wave per SIMD, gains
+    // 170 -> 165 us; the rest are unchanged.
+    constexpr bool A1 = PACKED && PF == 2 && KS == 1;
+    uint4 ra[A1 ? 1 : 2][MT][4];
     const int nch = ce - cb;
     auto load_b = [&](int slot, int ch) {
 #pragma unroll
@@ -846,7 +854,7 @@ __global__ __launch_bounds__(64 * KS) void gemm_bf16_skinny_kernel(
             const int ch = c0 + sl;
             if (ch < nch) {
                 if (ch + PF - 1 < nch) load_b((sl + PF - 1) % PF, ch + PF - 1);
-                if (ch + 1 < nch) load_a((sl + 1) & 1, ch + 1);
+                if (!A1 && ch + 1 < nch) load_a((sl + 1) & 1, ch + 1);
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
 #pragma unroll
@@ -858,9 +866,10 @@ __global__ __launch_bounds__(64 * KS) void gemm_bf16_skinny_kernel(
                             for (int m = 0; m < MT; ++m)
                                 if (m < nm)
                                     acc[m][q][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                                        __builtin_bit_cast(bf16x8_t, ra[sl & 1][m][j]), b,
+                                        __builtin_bit_cast(bf16x8_t, ra[A1 ? 0 : (sl & 1)][m][j]), b,
                                         acc[m][q][t], 0, 0, 0);
                         }
+                if (A1 && ch + 1 < nch) load_a(0, ch + 1);
             }
         }
     }
@@ -1100,12 +1109,12 @@ hipError_t launch_skinny_any(const Shape &s, int mt, const void *A, const int32_
     // projection is no faster with them)
     if (!DUAL && !((int64_t)s.E * ((N + 63) / 64) < 4096 && K / SK_KC >= 64)) {
         // on packed weights with a short K (fewer than 16 chunks: the Switch
-        // layer's up projection) 64 rows per wave with a 4-chunk ring (up
-        // projection 150 against 146 us; its down projection, 24 chunks,
-        // keeps 128 rows: 126 against 141 us)
+        // layer's up projection) 64 rows per wave with a 2-chunk ring and one
+        // A buffer, two waves per SIMD (up projection 150 -> 133 us; its down
+        // projection, 24 chunks, keeps 128 rows: 126 against 141 us with 64)
         if (PACKED && K / SK_KC < 16) {
-            if (mt == 2) return launch_skinny<2, 4, 4, DUAL, ACT, OUT_BF16, PACKED>(s, A, a_rows, offsets, B1, B3, C, N, K, st);
-            return launch_skinny<3, 4, 4, DUAL, ACT, OUT_BF16, PACKED>(s, A, a_rows, offsets, B1, B3, C, N, K, st);
+            if (mt == 2) return launch_skinny<2, 4, 2, DUAL, ACT, OUT_BF16, PACKED>(s, A, a_rows, offsets, B1, B3, C, N, K, st);
+            return launch_skinny<3, 4, 2, DUAL, ACT, OUT_BF16, PACKED>(s, A, a_rows, offsets, B1, B3, C, N, K, st);
         }
         if (mt == 2) return launch_skinny<2, 8, 2, DUAL, ACT, OUT_BF16, PACKED>(s, A, a_rows, offsets, B1, B3, C, N, K, st);
         return launch_skinny<3, 8, 2, DUAL, ACT, OUT_BF16, PACKED>(s, A, a_rows, offsets, B1, B3, C, N, K, st);
