@@ -165,8 +165,9 @@ __global__ __launch_bounds__(64 * KS) void gemm_fp8w_skinny_kernel(
     // covering the other's start and epilogue (the Switch layer's up
     // projection 147 -> 133 us with bf16 weights, 145 -> 110 us with e4m3
     // codes); the e4m3 decode up projection, still one wave per SIMD, gains
-    // 170 -> 165 us; the rest are unchanged.
-    constexpr bool A1 = PACKED && PF == 2 && KS == 1;
+    // 170 -> 165 us; the rest are unchanged.  Row-major codes take the same
+    // 64-row short-K shape (Switch up projection 155 -> 119 us).
+    constexpr bool A1 = PF == 2 && KS == 1 && (PACKED || (!DUAL && NT == 4));
     uint4 ra[A1 ? 1 : 2][MT][4];
     const int nch = ce - cb;
     auto load_b = [&](int slot, int ch) {
@@ -331,9 +332,9 @@ hipError_t up_fp8(const Shape &s, const void *A, const int32_t *a_rows, const in
         return mt == 2 ? launch_fp8<2, 4, true, ACT_SWIGLU, true, PACKED>(s, A, a_rows, offsets, W1, W3, S1, S3, H, N, K, st)
                        : launch_fp8<3, 4, true, ACT_SWIGLU, true, PACKED>(s, A, a_rows, offsets, W1, W3, S1, S3, H, N, K, st);
     // one matrix with a short K (fewer than 16 chunks: the Switch layer's up
-    // projection) on packed codes: 64 rows per wave and one A buffer, two
-    // waves per SIMD (145 -> 110 us)
-    if (PACKED && s.act != ACT_SWIGLU && K / F8_KC < 16) {
+    // projection): 64 rows per wave and one A buffer, two waves per SIMD
+    // (packed codes 145 -> 110 us, row-major 155 -> 119 us)
+    if (s.act != ACT_SWIGLU && K / F8_KC < 16) {
         if (s.act == ACT_GELU)
             return mt == 2 ? launch_fp8<2, 4, false, ACT_GELU, true, PACKED>(s, A, a_rows, offsets, W1, nullptr, S1, nullptr, H, N, K, st)
                            : launch_fp8<3, 4, false, ACT_GELU, true, PACKED>(s, A, a_rows, offsets, W1, nullptr, S1, nullptr, H, N, K, st);
